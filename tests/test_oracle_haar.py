@@ -1,0 +1,139 @@
+"""Pins of the oracle's Haar pyramid (WaveFilter section 2.2, eq. 5).
+
+Each pin is independent of the oracle's own code: a direct-loop closed form,
+the textbook orthonormal Haar matrix built by its Kronecker recursion, a
+hand-worked example, and the invariants of an orthonormal transform.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import haar_pyramid, haar_reconstruct, analysis_step, synthesis_step
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "haar_worked_example.txt")
+
+
+def closed_form(x, j):
+    """A_j[n] = 2^{-j/2} sum_{t in [n 2^j, (n+1) 2^j)} x[t] and
+    D_j[n] = 2^{-j/2} (sum of the first half of that range - sum of the second half),
+    by explicit loops."""
+    n_out = x.shape[0] >> j
+    a = np.zeros((n_out,) + x.shape[1:])
+    dd = np.zeros_like(a)
+    w = 1 << j
+    for n in range(n_out):
+        for t in range(n * w, (n + 1) * w):
+            a[n] += x[t]
+            if j >= 1:
+                dd[n] += x[t] if t < n * w + w // 2 else -x[t]
+    return a / 2 ** (j / 2), dd / 2 ** (j / 2)
+
+
+def haar_matrix(n):
+    """Orthonormal Haar matrix by H_{2m} = [H_m (x) (1, 1); I_m (x) (1, -1)] / sqrt2."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        m = h.shape[0]
+        top = np.kron(h, np.array([[1.0, 1.0]]))
+        bot = np.kron(np.eye(m), np.array([[1.0, -1.0]]))
+        h = np.vstack([top, bot]) / math.sqrt(2.0)
+    return h
+
+
+@pytest.mark.parametrize("levels", [0, 1, 2, 3, 5, 6])
+def test_closed_form(levels):
+    rng = np.random.default_rng(1 + levels)
+    x = rng.standard_normal((64, 3))
+    approx, detail = haar_pyramid(x, levels)
+    for j in range(levels + 1):
+        a, dd = closed_form(x, j)
+        np.testing.assert_allclose(approx[j], a, rtol=0, atol=1e-13)
+        if j >= 1:
+            np.testing.assert_allclose(detail[j], dd, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64])
+def test_textbook_haar_matrix(n):
+    h = haar_matrix(n)
+    np.testing.assert_allclose(h @ h.T, np.eye(n), atol=1e-13)
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n)
+    levels = int(math.log2(n))
+    approx, detail = haar_pyramid(x, levels)
+    stacked = np.concatenate([approx[levels]] + [detail[j] for j in range(levels, 0, -1)])
+    np.testing.assert_allclose(stacked, h @ x, atol=1e-13)
+
+
+def _parse_golden():
+    vals = {}
+    r2 = math.sqrt(2.0)
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rhs = (s.strip() for s in line.split("=", 1))
+            vals[key] = np.array([eval(e, {"r2": r2}) for e in rhs.split(",")], dtype=float)
+    return vals
+
+
+def test_hand_worked_example():
+    g = _parse_golden()
+    approx, detail = haar_pyramid(g["x"], 3)
+    for j in (1, 2, 3):
+        np.testing.assert_allclose(approx[j], g[f"A{j}"], atol=1e-14)
+        np.testing.assert_allclose(detail[j], g[f"D{j}"], atol=1e-14)
+    energy = (approx[3] ** 2).sum() + sum((detail[j] ** 2).sum() for j in (1, 2, 3))
+    assert abs(energy - g["energy"][0]) < 1e-12
+
+
+@pytest.mark.parametrize("levels", [1, 3, 6, 10])
+def test_perfect_reconstruction(levels):
+    rng = np.random.default_rng(10 + levels)
+    x = rng.standard_normal((1024, 8)) * 3.0
+    approx, detail = haar_pyramid(x, levels)
+    y = haar_reconstruct(approx[levels], detail)
+    assert np.max(np.abs(y - x)) <= 1e-12 * np.max(np.abs(x))
+
+
+@pytest.mark.parametrize("levels", [1, 4, 7])
+def test_parseval(levels):
+    rng = np.random.default_rng(20 + levels)
+    x = rng.standard_t(4, size=(512, 5))
+    approx, detail = haar_pyramid(x, levels)
+    e_in = (x ** 2).sum(axis=0)
+    e_out = (approx[levels] ** 2).sum(axis=0) + sum((detail[j] ** 2).sum(axis=0) for j in range(1, levels + 1))
+    np.testing.assert_allclose(e_out, e_in, rtol=1e-12)
+
+
+def test_special_signals():
+    c = 1.75
+    approx, detail = haar_pyramid(np.full(64, c), 6)
+    for j in range(1, 7):
+        np.testing.assert_allclose(detail[j], 0.0, atol=1e-14)
+        np.testing.assert_allclose(approx[j], c * 2 ** (j / 2), rtol=1e-14)
+    alt = np.array([1.0, -1.0] * 32)
+    approx, detail = haar_pyramid(alt, 1)
+    np.testing.assert_allclose(approx[1], 0.0, atol=1e-15)
+    np.testing.assert_allclose(detail[1], math.sqrt(2.0), rtol=1e-15)
+    imp = np.zeros(64)
+    imp[13] = 1.0
+    approx, detail = haar_pyramid(imp, 6)
+    for j in range(1, 7):
+        nz = np.flatnonzero(approx[j])
+        assert list(nz) == [13 >> j]
+        assert abs(approx[j][13 >> j] - 2 ** (-j / 2)) < 1e-15
+
+
+def test_single_step_roundtrip_and_shape_errors():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, 2))
+    a, dd = analysis_step(x)
+    np.testing.assert_allclose(synthesis_step(a, dd), x, atol=1e-15)
+    with pytest.raises(ValueError):
+        analysis_step(np.zeros(5))
+    with pytest.raises(ValueError):
+        haar_pyramid(np.zeros((12, 2)), 3)

@@ -1,0 +1,184 @@
+"""Pins of the oracle's coarse-to-fine selection (WaveFilter Figure 2 (c)-(d)).
+
+Independent checks: scores by explicit loops over tokens (not through the
+pyramid), brute-force flat top-B when the coarse levels keep everything,
+the union-of-coarse-blocks special case, exhaustive subset search on tiny
+inputs, exact ties, and invariances.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import level_scores, top_k, select, haar_pyramid
+from workloads.configs import check_budgets
+
+
+def block_score_loop(q, k_prompt, j, c):
+    """max_i q_i . (2^{-j/2} sum_{t in block c} k_t) / sqrt(d), by explicit loops."""
+    n_q, d = q.shape
+    w = 1 << j
+    best = -math.inf
+    for i in range(n_q):
+        acc = 0.0
+        for t in range(c * w, (c + 1) * w):
+            acc += float(np.dot(q[i], k_prompt[t]))
+        best = max(best, acc * 2 ** (-j / 2) / math.sqrt(d))
+    return best
+
+
+def rank_key(score, idx):
+    return (-score, idx)
+
+
+def test_level_scores_loop():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((7, 6))
+    kp = rng.standard_normal((32, 6))
+    approx, _ = haar_pyramid(kp, 3)
+    for j in range(4):
+        s = level_scores(q, approx[j])
+        for c in range(32 >> j):
+            assert abs(s[c] - block_score_loop(q, kp, j, c)) < 1e-12
+
+
+def test_top_k_ties_and_gap():
+    cand = np.array([10, 3, 7, 5, 1])
+    sc = np.array([2.0, 5.0, 2.0, 2.0, -1.0])
+    chosen, gap = top_k(cand, sc, 2)
+    # best is 3 (5.0); then among the three 2.0 ties the lowest index, 5
+    assert list(chosen) == [3, 5]
+    assert gap == 0.0
+    chosen, gap = top_k(cand, sc, 4)
+    assert list(chosen) == [3, 5, 7, 10]
+    assert abs(gap - (2.0 - (-1.0)) / 2.0) < 1e-15
+    chosen, gap = top_k(cand, sc, 5)
+    assert gap == math.inf and list(chosen) == [1, 3, 5, 7, 10]
+    with pytest.raises(ValueError):
+        top_k(cand, sc, 6)
+
+
+@pytest.mark.parametrize("levels,n_p,B", [(1, 32, 5), (3, 64, 9), (4, 256, 37)])
+def test_flat_top_b_when_coarse_levels_keep_all(levels, n_p, B):
+    rng = np.random.default_rng(levels)
+    d = 8
+    q = rng.standard_normal((5, d))
+    kp = rng.standard_normal((n_p, d))
+    budgets = [n_p >> j for j in range(levels, 0, -1)] + [B]
+    res = select(q, kp, budgets, levels)
+    tok = [max(float(np.dot(q[i], kp[t])) for i in range(5)) / math.sqrt(d) for t in range(n_p)]
+    brute = sorted(range(n_p), key=lambda t: rank_key(tok[t], t))[:B]
+    assert list(res.sel[0]) == sorted(brute)
+
+
+def test_union_of_coarse_blocks_on_full_expansion():
+    rng = np.random.default_rng(7)
+    levels, n_p, d = 3, 256, 8
+    q = rng.standard_normal((4, d))
+    kp = rng.standard_normal((n_p, d))
+    k_top = 5
+    budgets = [k_top << i for i in range(levels + 1)]
+    res = select(q, kp, budgets, levels)
+    blocks = sorted(range(n_p >> levels),
+                    key=lambda c: rank_key(block_score_loop(q, kp, levels, c), c))[:k_top]
+    want = sorted(t for c in blocks for t in range(c << levels, (c + 1) << levels))
+    assert list(res.sel[0]) == want
+
+
+def brute_select(q, kp, budgets, levels):
+    """Level by level, the kept set is the k-subset of the candidates with the
+    largest score sum (exhaustive search over all subsets); candidates are
+    the children of the kept parents; scores by explicit loops."""
+    n_top = kp.shape[0] >> levels
+    cand = list(range(n_top))
+    out = {}
+    for j in range(levels, -1, -1):
+        if j < levels:
+            cand = sorted([2 * p for p in out[j + 1]] + [2 * p + 1 for p in out[j + 1]])
+        sc = {c: block_score_loop(q, kp, j, c) for c in cand}
+        k = budgets[levels - j]
+        best = max(itertools.combinations(cand, k), key=lambda sub: sum(sc[c] for c in sub))
+        out[j] = sorted(best)
+    return out
+
+
+def test_exhaustive_tiny():
+    rng = np.random.default_rng(11)
+    checked = 0
+    for levels, n_p in [(1, 8), (2, 16), (3, 16), (2, 32)]:
+        schedules = []
+        n_top = n_p >> levels
+
+        def grow(prefix):
+            if len(prefix) == levels + 1:
+                schedules.append(list(prefix))
+                return
+            j = levels - len(prefix)
+            for k in range(1, min(2 * prefix[-1], n_p >> j) + 1):
+                grow(prefix + [k])
+
+        for k_top in range(1, n_top + 1):
+            grow([k_top])
+        # keep the exhaustive search small: at most a few thousand subsets per level
+        schedules = [s for s in schedules
+                     if math.comb(n_top, s[0]) <= 3000
+                     and all(math.comb(2 * s[i - 1], s[i]) <= 3000 for i in range(1, len(s)))]
+        picks = rng.choice(len(schedules), size=min(12, len(schedules)), replace=False)
+        for p in picks:
+            budgets = schedules[p]
+            assert check_budgets(n_p, levels, budgets)
+            q = rng.standard_normal((3, 4))
+            kp = rng.standard_normal((n_p, 4))
+            res = select(q, kp, budgets, levels)
+            want = brute_select(q, kp, budgets, levels)
+            for j in range(levels + 1):
+                assert list(res.sel[j]) == want[j], (levels, n_p, budgets, j)
+            checked += 1
+    assert checked >= 30
+
+
+def test_full_budgets_select_everything():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 8))
+    kp = rng.standard_normal((128, 8))
+    budgets = [128 >> j for j in range(4, -1, -1)]
+    res = select(q, kp, budgets, 4)
+    assert list(res.sel[0]) == list(range(128))
+    assert all(res.gap[j] == math.inf for j in range(5))
+
+
+def test_exact_tie_goes_to_lower_index():
+    rng = np.random.default_rng(9)
+    d, levels = 8, 2
+    kp = rng.standard_normal((32, d)) * 0.01
+    q = rng.standard_normal((3, d))
+    big = rng.standard_normal((4, d))
+    kp[20:24] = big + 5 * q.mean(axis=0)   # block 5 at level 2
+    kp[8:12] = kp[20:24]                   # block 2: identical keys, exactly equal score
+    res = select(q, kp, [1, 2, 4], levels)
+    assert list(res.sel[2]) == [2]
+    assert res.gap[2] == 0.0
+
+
+def test_invariances():
+    rng = np.random.default_rng(4)
+    levels, n_p, d = 4, 512, 16
+    q = rng.standard_normal((6, d))
+    kp = rng.standard_normal((n_p, d))
+    budgets = [6, 10, 17, 30, 50]
+    base = select(q, kp, budgets, levels)
+    scaled = select(3.5 * q, kp, budgets, levels)
+    perm = select(q[rng.permutation(6)], kp, budgets, levels)
+    for j in range(levels + 1):
+        assert list(base.sel[j]) == list(scaled.sel[j]) == list(perm.sel[j])
+    # scaling one level-2 region's keys by c > 0 scales its level-2 score by c
+    c_reg, factor = 9, 0.37
+    kp2 = kp.copy()
+    kp2[c_reg * 4:(c_reg + 1) * 4] *= factor
+    a1, _ = haar_pyramid(kp, 2)
+    a2, _ = haar_pyramid(kp2, 2)
+    s1 = level_scores(q, a1[2][c_reg:c_reg + 1])[0]
+    s2 = level_scores(q, a2[2][c_reg:c_reg + 1])[0]
+    assert abs(s2 - factor * s1) < 1e-12
