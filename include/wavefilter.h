@@ -1,0 +1,189 @@
+/*
+ * wavefilter.h -- C ABI of the WaveFilter per-step sparse-attention path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: WaveFilter, "Enhancing the Long-Context Capability of Diffusion
+ * LLMs via Wavelet-Guided KV Cache Filtering" (arXiv 2606.00724).  Per layer
+ * and denoising step, the cached prompt keys are decomposed along the token
+ * axis by a discrete wavelet transform (section 2.2, equation 5; section 3.1),
+ * the step's query block is scored against the low-frequency keys and a
+ * Top-K keeps candidate regions (Figure 2 (c)), the regions are refined
+ * recursively across scales down to single tokens (Figure 2 (d)), and the
+ * queries attend over the kept prompt tokens plus the generated-position
+ * cache (section 2.1, equation 3, restricted to that set).
+ *
+ * Two calls carry the work:
+ *   wf_build_pyramid  -- once per cache refresh: orthonormal Haar
+ *                        approximation of the prompt keys;
+ *   wf_select_attend  -- once per denoising step: scoring, Top-K,
+ *                        refinement and the sparse attention.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device memory owned by the caller; the library
+ *     never allocates, frees or synchronises, and keeps no mutable global
+ *     state.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and completes asynchronously.
+ *   - Arguments are checked on the host before anything is enqueued; on an
+ *     error the call returns a negative status and enqueues nothing, and the
+ *     outputs are untouched.  A failed kernel launch returns WF_ERR_HIP.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Tensors are row-major and dense unless a stride argument says
+ *     otherwise.  Base pointers must be 16-byte aligned.
+ *   - Concurrent calls need distinct workspaces; calls on one workspace must
+ *     be ordered (same stream, or synchronised).
+ */
+#ifndef WAVEFILTER_H
+#define WAVEFILTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    WF_OK = 0,
+    WF_ERR_NULL = -1,      /* a required pointer is NULL */
+    WF_ERR_SHAPE = -2,     /* a size is out of range or inconsistent */
+    WF_ERR_DTYPE = -3,     /* unknown element type, or q/k/v types differ from the pyramid's */
+    WF_ERR_LEVELS = -4,    /* level count out of range or N_p not a multiple of 2^L */
+    WF_ERR_BUDGET = -5,    /* per-level keep counts infeasible or beyond the supported size */
+    WF_ERR_WORKSPACE = -6, /* workspace or pyramid buffer too small */
+    WF_ERR_ALIGN = -7,     /* a pointer or stride is not 16-byte aligned */
+    WF_ERR_HIP = -8,       /* a HIP launch failed */
+    WF_ERR_PYRAMID = -9    /* pyramid descriptor not built by wf_build_pyramid */
+};
+
+/* Element types of q, k and v. */
+enum { WF_F32 = 0, WF_BF16 = 1 };
+
+/* wf_build_pyramid flags. */
+#define WF_PYR_ALL_LEVELS 1u /* also store A_1..A_{L-1} and D_1..D_L (test/inspection) */
+
+/* Supported sizes. */
+#define WF_MAX_LEVELS 7      /* region of 2^L tokens, L <= 7 */
+#define WF_MAX_QUERIES 64    /* query-block rows n_q */
+
+/*
+ * Pyramid descriptor, filled by wf_build_pyramid.  `base` points to the
+ * caller's device buffer; the library reads it in wf_select_attend.
+ * Layout of the buffer (float32, row-major):
+ *   A_L  [batch, heads, N_p / 2^L, head_dim]                   at offset 0
+ * and with WF_PYR_ALL_LEVELS additionally, in this order,
+ *   D_1 .. D_L   then   A_1 .. A_{L-1},   each [batch, heads, N_p / 2^j, head_dim]
+ * (use wf_pyramid_offset for the byte offset of each band).
+ */
+typedef struct wf_pyramid {
+    int32_t batch;
+    int32_t heads;
+    int32_t n_prompt;
+    int32_t head_dim;
+    int32_t levels;
+    int32_t dtype;     /* element type of the keys it was built from */
+    uint32_t flags;
+    uint32_t magic;    /* set by wf_build_pyramid */
+    void* base;
+    uint64_t bytes;
+} wf_pyramid;
+
+/* Library version string (static storage). */
+const char* wf_version(void);
+
+/* Human-readable text of a status code (static storage). */
+const char* wf_status_string(int status);
+
+/*
+ * Bytes of device memory wf_build_pyramid needs for the given shape and
+ * flags, or 0 if the shape is invalid.
+ */
+uint64_t wf_pyramid_bytes(int32_t batch, int32_t heads, int32_t n_prompt, int32_t head_dim,
+                          int32_t levels, uint32_t flags);
+
+/*
+ * Byte offset inside the pyramid buffer of band `band` (0 = approximation A,
+ * 1 = detail D) at level `level`, or UINT64_MAX when that band is not stored.
+ */
+uint64_t wf_pyramid_offset(const wf_pyramid* pyr, int32_t band, int32_t level);
+
+/*
+ * Haar pyramid of the cached prompt keys along the token axis (WaveFilter
+ * section 2.2, equation 5, iterated on the approximation band; section 3.1:
+ * applied to the prompt positions only).  Orthonormal Haar filters; output
+ * coefficient n of level j is built from tokens [n 2^j, (n+1) 2^j):
+ *     A_j[n] = (A_{j-1}[2n] + A_{j-1}[2n+1]) / sqrt(2),  A_0 = K_prompt,
+ *     D_j[n] = (A_{j-1}[2n] - A_{j-1}[2n+1]) / sqrt(2).
+ * Float32 accumulation; the coefficients are stored as float32.
+ *
+ *   k_prompt     device, element type `dtype`; head (b, h) starts at
+ *                k_prompt + (b*heads + h) * head_stride elements and holds
+ *                n_prompt rows of head_dim contiguous elements
+ *   head_stride  elements between consecutive heads (>= n_prompt*head_dim,
+ *                a multiple of 16 bytes); e.g. N_tot*head_dim when the prompt
+ *                is the first n_prompt rows of a [B, H, N_tot, d] cache
+ *   head_dim     64 or 128
+ *   levels       0 <= L <= WF_MAX_LEVELS, n_prompt a multiple of 2^L
+ *   flags        0 or WF_PYR_ALL_LEVELS
+ *   pyr_mem      device buffer of pyr_bytes >= wf_pyramid_bytes(...)
+ *   out          host descriptor, filled on success
+ */
+int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, int32_t heads,
+                     int32_t n_prompt, int32_t head_dim, int32_t dtype, int32_t levels,
+                     uint32_t flags, void* pyr_mem, uint64_t pyr_bytes, wf_pyramid* out,
+                     void* stream);
+
+/*
+ * Bytes of workspace wf_select_attend needs, or 0 if the arguments are
+ * invalid.  `budgets` is the host array k_L, ..., k_0 (levels + 1 entries).
+ */
+uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen,
+                                          const int32_t* budgets);
+
+/*
+ * One denoising step of WaveFilter for every (sequence, head):
+ *   1. s_L[n] = max_i (q_i . A_L[n]) / sqrt(d) for every level-L region n,
+ *      and keep the k_L best (Figure 2 (c)).
+ *   2. For j = L-1 .. 0: the candidates are the two children of each region
+ *      kept at level j+1, scored as s_j[c] = max_i (q_i . A_j[c]) / sqrt(d),
+ *      and the k_j best are kept (Figure 2 (d)).  A_j is never stored: its
+ *      dot products are the 2^{-j/2}-scaled sums of the token dot products
+ *      q_i . k_t over the region (linearity of the transform).
+ *   3. O_i = softmax over T of (q_i . k_t / sqrt(d)) applied to v_t, with T
+ *      the kept prompt tokens followed by the generated positions gen_idx
+ *      (equation 3 restricted to T; no mask).
+ * "Best" means higher score, and on equal scores the lower index.  Scores
+ * and accumulation are float32.
+ *
+ *   q            device [batch, heads, n_q, head_dim], element type of the pyramid
+ *   pyr          built by wf_build_pyramid from k's prompt rows
+ *   k, v         device [batch, heads, n_tot, head_dim]; rows [0, N_p) are
+ *                the prompt, the rows named by gen_idx the generated positions
+ *   gen_idx      device int32 [n_gen], row indices in [0, n_tot) shared by all
+ *                heads (normally N_p .. n_tot-1); NULL allowed when n_gen == 0;
+ *                out-of-range entries are clamped, not reported
+ *   budgets      HOST int32 [levels + 1] = k_L, ..., k_0 with
+ *                1 <= k_L <= N_p/2^L and 1 <= k_j <= min(2 k_{j+1}, N_p/2^j)
+ *   n_q          1 .. WF_MAX_QUERIES
+ *   out          device float32 [batch, heads, n_q, head_dim]
+ *   sel_out      NULL, or device int32 [batch, heads, k_0]: kept prompt
+ *                tokens, ascending
+ *   sel_levels   NULL, or device int32 [batch, heads, k_L + ... + k_0]: the
+ *                kept region indices of level L, then L-1, ..., then 0, each
+ *                ascending (level-j region n covers tokens [n 2^j, (n+1) 2^j))
+ *   score_levels NULL, or device float32 of the same shape: each kept
+ *                region's score s_j
+ *   workspace    device buffer of ws_bytes >= wf_select_attend_workspace_bytes;
+ *                must be zero-filled before its first use; every call leaves
+ *                its synchronisation counters at zero again
+ */
+int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const void* v,
+                     int32_t n_tot, const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets,
+                     int32_t n_q, float* out, int32_t* sel_out, int32_t* sel_levels,
+                     float* score_levels, void* workspace, uint64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAVEFILTER_H */

@@ -1,0 +1,25 @@
+"""WaveFilter per-step sparse attention for AMD Instinct MI355X (gfx950).
+
+The work runs in ``libwavefilter.so`` (hand-written HIP, C ABI declared in
+``include/wavefilter.h``); this package only marshals arguments to it.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    MAX_LEVELS,
+    MAX_QUERIES,
+    WF_BF16,
+    WF_F32,
+    WF_PYR_ALL_LEVELS,
+    Pyramid,
+    WfError,
+    Workspace,
+    build_pyramid,
+    lib,
+    pyramid_bytes,
+    select_attend,
+    split_levels,
+    status_string,
+    version,
+    workspace_bytes,
+)

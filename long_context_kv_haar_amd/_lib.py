@@ -1,0 +1,234 @@
+"""ctypes binding of libwavefilter.so (argument marshalling only).
+
+Every step of the path runs inside the HIP library.  PyTorch provides device
+memory (tensors are passed by ``data_ptr``) and the stream
+(``torch.cuda.current_stream().cuda_stream``).  There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwavefilter.so")
+
+WF_OK = 0
+WF_F32 = 0
+WF_BF16 = 1
+WF_PYR_ALL_LEVELS = 1
+MAX_LEVELS = 7
+MAX_QUERIES = 64
+U64_MAX = (1 << 64) - 1
+
+STATUS_NAMES = {
+    0: "WF_OK", -1: "WF_ERR_NULL", -2: "WF_ERR_SHAPE", -3: "WF_ERR_DTYPE", -4: "WF_ERR_LEVELS",
+    -5: "WF_ERR_BUDGET", -6: "WF_ERR_WORKSPACE", -7: "WF_ERR_ALIGN", -8: "WF_ERR_HIP", -9: "WF_ERR_PYRAMID",
+}
+
+
+class WfPyramid(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("n_prompt", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("levels", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("magic", ctypes.c_uint32),
+        ("base", ctypes.c_void_p),
+        ("bytes", ctypes.c_uint64),
+    ]
+
+
+class WfError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: build it with long_context_kv_haar_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64
+        pyr_p = ctypes.POINTER(WfPyramid)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.wf_version.restype = ctypes.c_char_p
+        L.wf_version.argtypes = []
+        L.wf_status_string.restype = ctypes.c_char_p
+        L.wf_status_string.argtypes = [ctypes.c_int]
+        L.wf_pyramid_bytes.restype = u64
+        L.wf_pyramid_bytes.argtypes = [i32, i32, i32, i32, i32, u32]
+        L.wf_pyramid_offset.restype = u64
+        L.wf_pyramid_offset.argtypes = [pyr_p, i32, i32]
+        L.wf_build_pyramid.restype = ctypes.c_int
+        L.wf_build_pyramid.argtypes = [vp, i64, i32, i32, i32, i32, i32, i32, u32, vp, u64, pyr_p, vp]
+        L.wf_select_attend_workspace_bytes.restype = u64
+        L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p]
+        L.wf_select_attend.restype = ctypes.c_int
+        L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, vp, vp, vp, vp, vp, u64, vp]
+        _LIB = L
+    return _LIB
+
+
+def version():
+    return lib().wf_version().decode()
+
+
+def status_string(status):
+    return lib().wf_status_string(int(status)).decode()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return WF_BF16
+    if t.dtype == torch.float32:
+        return WF_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _budget_array(budgets):
+    arr = (ctypes.c_int32 * len(budgets))(*[int(b) for b in budgets])
+    return arr
+
+
+def pyramid_bytes(batch, heads, n_prompt, head_dim, levels, flags=0):
+    return int(lib().wf_pyramid_bytes(batch, heads, n_prompt, head_dim, levels, flags))
+
+
+class Pyramid:
+    """Device pyramid buffer plus its C descriptor."""
+
+    def __init__(self, buf, desc):
+        self.buf = buf
+        self.desc = desc
+
+    @property
+    def levels(self):
+        return self.desc.levels
+
+    def band(self, band, level):
+        """Float32 view ``[B, H, N_p / 2^level, d]`` of a stored band (0 = A, 1 = D)."""
+        off = int(lib().wf_pyramid_offset(ctypes.byref(self.desc), band, level))
+        if off == U64_MAX:
+            raise KeyError((band, level))
+        d = self.desc
+        n = (d.batch * d.heads * (d.n_prompt >> level) * d.head_dim)
+        flat = self.buf[off:off + 4 * n].view(torch.float32)
+        return flat.view(d.batch, d.heads, d.n_prompt >> level, d.head_dim)
+
+    @property
+    def top(self):
+        return self.band(0, self.desc.levels)
+
+
+def build_pyramid(k, n_prompt, levels, flags=0, buf=None):
+    """Haar pyramid of the prompt rows ``k[:, :, :n_prompt]`` of a ``[B, H, N, d]`` cache."""
+    if k.dim() != 4 or not k.is_cuda or not k.is_contiguous():
+        raise ValueError("k must be a contiguous [B, H, N, d] device tensor")
+    B, H, N, d = k.shape
+    need = pyramid_bytes(B, H, n_prompt, d, levels, flags)
+    if need == 0:
+        raise WfError(-2, "wf_pyramid_bytes")
+    if buf is None or buf.numel() < need:
+        buf = torch.empty(need, dtype=torch.uint8, device=k.device)
+    desc = WfPyramid()
+    st = lib().wf_build_pyramid(ctypes.c_void_p(k.data_ptr()), N * d, B, H, n_prompt, d, _dtype_code(k), levels,
+                                flags, ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.byref(desc),
+                                _stream_handle(k.device))
+    if st != WF_OK:
+        raise WfError(st, "wf_build_pyramid")
+    return Pyramid(buf, desc)
+
+
+def workspace_bytes(pyr, n_q, n_gen, budgets):
+    return int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, _budget_array(budgets)))
+
+
+class Workspace:
+    """Zero-filled device workspace, grown on demand and reused across calls."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=device)
+
+    def get(self, nbytes):
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_WORKSPACES = {}
+
+
+def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels_out=False, workspace=None):
+    """One step for every (sequence, head).
+
+    Returns a dict with ``out`` (float32 ``[B, H, n_q, d]``), ``sel``
+    (int32 ``[B, H, k_0]``) and, with ``levels_out``, ``sel_levels`` /
+    ``score_levels`` (``[B, H, sum k_j]``, level L first).
+    """
+    B, H, n_q, d = q.shape
+    n_tot = k.shape[2]
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if gen_idx is not None and (gen_idx.dtype != torch.int32 or not gen_idx.is_contiguous()):
+        raise ValueError("gen_idx must be a contiguous int32 device tensor")
+    if q.dtype != k.dtype or k.dtype != v.dtype or _dtype_code(q) != pyr.desc.dtype:
+        raise WfError(-3, "select_attend")
+    n_gen = 0 if gen_idx is None else gen_idx.numel()
+    budgets = [int(b) for b in budgets]
+    barr = _budget_array(budgets)
+    ws_need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, barr))
+    if ws_need == 0:
+        raise WfError(-5, "wf_select_attend_workspace_bytes")
+    if workspace is None:
+        workspace = _WORKSPACES.setdefault(q.device, Workspace(q.device))
+    ws = workspace.get(ws_need)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.float32, device=dev)
+    k0 = budgets[-1]
+    if sel_out is None:
+        sel_out = torch.empty((B, H, k0), dtype=torch.int32, device=dev)
+    sel_levels = score_levels = None
+    if levels_out:
+        sel_levels = torch.empty((B, H, sum(budgets)), dtype=torch.int32, device=dev)
+        score_levels = torch.empty((B, H, sum(budgets)), dtype=torch.float32, device=dev)
+
+    def ptr(t):
+        return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+    st = lib().wf_select_attend(ptr(q), ctypes.byref(pyr.desc), ptr(k), ptr(v), n_tot, ptr(gen_idx), n_gen, barr,
+                                n_q, ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels), ptr(ws),
+                                ws.numel(), _stream_handle(dev))
+    if st != WF_OK:
+        raise WfError(st, "wf_select_attend")
+    res = {"out": out, "sel": sel_out}
+    if levels_out:
+        res["sel_levels"] = sel_levels
+        res["score_levels"] = score_levels
+    return res
+
+
+def split_levels(flat, budgets):
+    """Split a ``[..., sum k_j]`` per-level tensor into {level j: [..., k_j]}."""
+    L = len(budgets) - 1
+    out, off = {}, 0
+    for i, kb in enumerate(budgets):
+        out[L - i] = flat[..., off:off + kb]
+        off += kb
+    return out

@@ -1,0 +1,243 @@
+// C ABI of the WaveFilter library: argument checks, buffer layout, launch.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/wavefilter.h"
+#include "wf_internal.h"
+
+namespace {
+
+constexpr uint32_t kPyramidMagic = 0x57465059u;  // "WFPY"
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+int elem_bytes(int dtype) { return dtype == WF_BF16 ? 2 : 4; }
+
+bool valid_pyramid_shape(int32_t batch, int32_t heads, int32_t n_prompt, int32_t head_dim, int32_t levels) {
+  if (batch < 1 || heads < 1 || n_prompt < 1) return false;
+  if ((int64_t)batch * heads > 65535) return false;
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (levels < 0 || levels > WF_MAX_LEVELS) return false;
+  if (n_prompt % (1 << levels) != 0) return false;
+  return true;
+}
+
+uint64_t band_bytes(int64_t heads_total, int32_t n_prompt, int32_t head_dim, int j) {
+  return align_up((uint64_t)heads_total * (uint64_t)(n_prompt >> j) * (uint64_t)head_dim * 4u);
+}
+
+// Offsets of every stored band; returns the total size.
+uint64_t pyramid_layout(int64_t heads_total, int32_t n_prompt, int32_t head_dim, int32_t levels, uint32_t flags,
+                        uint64_t* off_a, uint64_t* off_d) {
+  for (int j = 0; j <= WF_MAX_LEVELS; ++j) {
+    off_a[j] = UINT64_MAX;
+    off_d[j] = UINT64_MAX;
+  }
+  off_a[levels] = 0;
+  uint64_t off = band_bytes(heads_total, n_prompt, head_dim, levels);
+  if (flags & WF_PYR_ALL_LEVELS) {
+    for (int j = 1; j <= levels; ++j) {
+      off_d[j] = off;
+      off += band_bytes(heads_total, n_prompt, head_dim, j);
+    }
+    for (int j = 1; j < levels; ++j) {
+      off_a[j] = off;
+      off += band_bytes(heads_total, n_prompt, head_dim, j);
+    }
+  }
+  return off;
+}
+
+bool pyramid_ok(const wf_pyramid* p) {
+  return p && p->magic == kPyramidMagic && p->base &&
+         valid_pyramid_shape(p->batch, p->heads, p->n_prompt, p->head_dim, p->levels) &&
+         (p->dtype == WF_F32 || p->dtype == WF_BF16);
+}
+
+// Resolve budgets and the workspace layout; returns a status.
+int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* budgets, wf::SelectPlan* P) {
+  if (!pyramid_ok(pyr)) return pyr ? WF_ERR_PYRAMID : WF_ERR_NULL;
+  if (!budgets) return WF_ERR_NULL;
+  if (n_q < 1 || n_q > WF_MAX_QUERIES || n_gen < 0) return WF_ERR_SHAPE;
+  memset(P, 0, sizeof(*P));
+  const int L = pyr->levels;
+  P->heads_total = pyr->batch * pyr->heads;
+  P->n_q = n_q;
+  P->n_prompt = pyr->n_prompt;
+  P->n_top = pyr->n_prompt >> L;
+  P->head_dim = pyr->head_dim;
+  P->dtype = pyr->dtype;
+  P->levels = L;
+  P->n_gen = n_gen;
+  // budgets: 1 <= k_L <= n_L ; 1 <= k_j <= min(2 k_{j+1}, n_j)
+  int kmax = 0, nmax = 0;
+  int64_t sum_k = 0;
+  for (int i = 0; i <= L; ++i) {
+    const int j = L - i;
+    const int64_t k = budgets[i];
+    const int64_t n_j = pyr->n_prompt >> j;
+    const int64_t cap = (i == 0) ? n_j : (2 * (int64_t)budgets[i - 1] < n_j ? 2 * (int64_t)budgets[i - 1] : n_j);
+    if (k < 1 || k > cap) return WF_ERR_BUDGET;
+    P->budgets[i] = (int)k;
+    sum_k += k;
+    if (k > kmax) kmax = (int)k;
+    if (i < L && 2 * k > nmax) nmax = (int)(2 * k);
+  }
+  P->k_top = P->budgets[0];
+  P->k0 = P->budgets[L];
+  P->sum_k = (int)sum_k;
+  P->covered = (int64_t)P->k_top << L;
+  int64_t off = 0;
+  for (int j = 0; j < L; ++j) {
+    P->cov_off[j] = off;
+    off += P->covered >> j;
+  }
+  P->cov_len = off;
+  P->refine_lds = 4 * (nmax + 2 * kmax);
+  if (P->refine_lds > wf::kRefineLdsBytes) return WF_ERR_BUDGET;
+  // attention split: about one workgroup per compute unit in total
+  P->n_att = P->k0 + n_gen;
+  const int chunk = (pyr->dtype == WF_BF16) ? wf::kAttendChunkBf16 : wf::kAttendChunkF32;
+  P->n_chunks = (P->n_att + chunk - 1) / chunk;
+  int target = (256 + P->heads_total - 1) / P->heads_total;
+  if (target > wf::kMaxSplit) target = wf::kMaxSplit;
+  if (target < 1) target = 1;
+  P->chunks_per_split = (P->n_chunks + target - 1) / target;
+  P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
+  // workspace sections
+  const uint64_t H = (uint64_t)P->heads_total;
+  uint64_t w = 0;
+  P->off_counters = w; w += align_up(H * 4 * 4);
+  P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
+  P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
+  P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
+  P->off_sel0 = w;     w += align_up(H * (uint64_t)P->k0 * 4);
+  P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
+  P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * P->head_dim * 4);
+  P->total = w;
+  return WF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wf_version(void) { return "wavefilter-gfx950 0.1.0"; }
+
+const char* wf_status_string(int status) {
+  switch (status) {
+    case WF_OK: return "ok";
+    case WF_ERR_NULL: return "a required pointer is NULL";
+    case WF_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case WF_ERR_DTYPE: return "unsupported or mismatched element type";
+    case WF_ERR_LEVELS: return "level count out of range or prompt length not a multiple of 2^L";
+    case WF_ERR_BUDGET: return "per-level keep counts infeasible or beyond the supported size";
+    case WF_ERR_WORKSPACE: return "workspace or pyramid buffer too small";
+    case WF_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case WF_ERR_HIP: return "HIP launch failed";
+    case WF_ERR_PYRAMID: return "pyramid descriptor not built by wf_build_pyramid";
+    default: return "unknown status";
+  }
+}
+
+uint64_t wf_pyramid_bytes(int32_t batch, int32_t heads, int32_t n_prompt, int32_t head_dim, int32_t levels,
+                          uint32_t flags) {
+  if (!valid_pyramid_shape(batch, heads, n_prompt, head_dim, levels)) return 0;
+  if (flags & ~WF_PYR_ALL_LEVELS) return 0;
+  uint64_t off_a[WF_MAX_LEVELS + 1], off_d[WF_MAX_LEVELS + 1];
+  return pyramid_layout((int64_t)batch * heads, n_prompt, head_dim, levels, flags, off_a, off_d);
+}
+
+uint64_t wf_pyramid_offset(const wf_pyramid* pyr, int32_t band, int32_t level) {
+  if (!pyramid_ok(pyr) || level < 0 || level > pyr->levels || (band != 0 && band != 1)) return UINT64_MAX;
+  uint64_t off_a[WF_MAX_LEVELS + 1], off_d[WF_MAX_LEVELS + 1];
+  pyramid_layout((int64_t)pyr->batch * pyr->heads, pyr->n_prompt, pyr->head_dim, pyr->levels, pyr->flags, off_a,
+                 off_d);
+  return band == 0 ? off_a[level] : off_d[level];
+}
+
+int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, int32_t heads, int32_t n_prompt,
+                     int32_t head_dim, int32_t dtype, int32_t levels, uint32_t flags, void* pyr_mem,
+                     uint64_t pyr_bytes, wf_pyramid* out, void* stream) {
+  if (!k_prompt || !pyr_mem || !out) return WF_ERR_NULL;
+  if (dtype != WF_F32 && dtype != WF_BF16) return WF_ERR_DTYPE;
+  if (levels < 0 || levels > WF_MAX_LEVELS) return WF_ERR_LEVELS;
+  if (n_prompt >= 1 && n_prompt % (1 << levels) != 0) return WF_ERR_LEVELS;
+  if (!valid_pyramid_shape(batch, heads, n_prompt, head_dim, levels)) return WF_ERR_SHAPE;
+  if (flags & ~WF_PYR_ALL_LEVELS) return WF_ERR_SHAPE;
+  if (head_stride < (int64_t)n_prompt * head_dim) return WF_ERR_SHAPE;
+  if (!aligned16(k_prompt) || !aligned16(pyr_mem) || (head_stride * elem_bytes(dtype)) % 16 != 0)
+    return WF_ERR_ALIGN;
+  wf::PyramidLaunch a;
+  const int64_t heads_total = (int64_t)batch * heads;
+  const uint64_t need = pyramid_layout(heads_total, n_prompt, head_dim, levels, flags, a.band_off_a, a.band_off_d);
+  if (pyr_bytes < need) return WF_ERR_WORKSPACE;
+  a.k = k_prompt;
+  a.head_stride = head_stride;
+  a.heads_total = (int)heads_total;
+  a.n_prompt = n_prompt;
+  a.head_dim = head_dim;
+  a.dtype = dtype;
+  a.levels = levels;
+  a.flags = flags;
+  a.base = reinterpret_cast<float*>(pyr_mem);
+  if (wf::launch_pyramid(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  out->batch = batch;
+  out->heads = heads;
+  out->n_prompt = n_prompt;
+  out->head_dim = head_dim;
+  out->levels = levels;
+  out->dtype = dtype;
+  out->flags = flags;
+  out->magic = kPyramidMagic;
+  out->base = pyr_mem;
+  out->bytes = pyr_bytes;
+  return WF_OK;
+}
+
+uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen,
+                                          const int32_t* budgets) {
+  wf::SelectPlan P;
+  if (make_plan(pyr, n_q, n_gen, budgets, &P) != WF_OK) return 0;
+  return P.total;
+}
+
+int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const void* v, int32_t n_tot,
+                     const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets, int32_t n_q, float* out,
+                     int32_t* sel_out, int32_t* sel_levels, float* score_levels, void* workspace,
+                     uint64_t ws_bytes, void* stream) {
+  if (!q || !pyr || !k || !v || !out || !workspace || !budgets) return WF_ERR_NULL;
+  if (n_gen > 0 && !gen_idx) return WF_ERR_NULL;
+  wf::SelectPlan P;
+  const int st = make_plan(pyr, n_q, n_gen, budgets, &P);
+  if (st != WF_OK) return st;
+  if (n_tot < pyr->n_prompt || n_tot < 1) return WF_ERR_SHAPE;
+  P.n_tot = n_tot;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+      !aligned16(pyr->base))
+    return WF_ERR_ALIGN;
+  if ((gen_idx && !aligned4(gen_idx)) || (sel_out && !aligned4(sel_out)) || (sel_levels && !aligned4(sel_levels)) ||
+      (score_levels && !aligned4(score_levels)))
+    return WF_ERR_ALIGN;
+  if (ws_bytes < P.total) return WF_ERR_WORKSPACE;
+  wf::SelectLaunch a;
+  a.plan = P;
+  a.q = q;
+  a.a_top = reinterpret_cast<const float*>(pyr->base);
+  a.k = k;
+  a.v = v;
+  a.gen_idx = gen_idx;
+  a.out = out;
+  a.sel_out = sel_out;
+  a.sel_levels = sel_levels;
+  a.score_levels = score_levels;
+  a.ws = reinterpret_cast<uint8_t*>(workspace);
+  if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  return WF_OK;
+}
+
+}  // extern "C"

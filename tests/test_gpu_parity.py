@@ -1,0 +1,203 @@
+"""GPU parity of the HIP path against the float64 oracle (through the C ABI).
+
+Selected index sets must match the oracle exactly at every level whose
+boundary gap exceeds 1e-3 (margins are planted so that all do); attention
+outputs must match within 2e-3 (bfloat16 inputs) or 1e-5 (float32).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_kv_haar_amd as wf
+from oracle import haar_pyramid
+from workloads.configs import CONFIGS, Config
+from workloads.gen import make_layer, to_f64
+
+from _parity import TOL, check_head, check_structure, plant, say, torch_attend_all
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(inp):
+    inp.q, inp.k, inp.v, inp.gen_idx = (t.to(DEV) for t in (inp.q, inp.k, inp.v, inp.gen_idx))
+    return inp
+
+
+def run(inp, budgets=None, levels=None, flags=0):
+    cfg = inp.cfg
+    budgets = cfg.budgets if budgets is None else budgets
+    levels = cfg.levels if levels is None else levels
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, levels, flags)
+    res = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True)
+    torch.cuda.synchronize()
+    return pyr, res
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_pyramid_matches_oracle(cid):
+    say(f"[pyramid c{cid}]")
+    inp = to_dev(make_layer(cid, 0))
+    cfg = inp.cfg
+    for flags in (0, wf.WF_PYR_ALL_LEVELS):
+        pyr = wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels, flags)
+        torch.cuda.synchronize()
+        for h in range(cfg.heads):
+            approx, detail = haar_pyramid(to_f64(inp.k[0, h, :cfg.n_prompt]), cfg.levels)
+            top = pyr.top[0, h].cpu().numpy()
+            assert np.abs(top - approx[cfg.levels]).max() <= 1e-5 * (1 + np.abs(approx[cfg.levels]).max())
+            if flags:
+                for j in range(1, cfg.levels + 1):
+                    for band, ref in ((0, approx[j]), (1, detail[j])):
+                        got = pyr.band(band, j)[0, h].cpu().numpy()
+                        assert np.abs(got - ref).max() <= 1e-5 * (1 + np.abs(ref).max()), (band, j)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_select_attend_matches_oracle(cid):
+    say(f"[select_attend c{cid}]")
+    inp = make_layer(cid, 0)
+    cfg = inp.cfg
+    heads = [(0, h) for h in range(cfg.heads)]
+    ok = plant(inp, heads)
+    assert all(ok.values())
+    to_dev(inp)
+    _, res = run(inp)
+    check_structure(res, cfg.budgets, cfg.levels, cfg.n_prompt)
+    unpinned = sum(check_head(inp, res, b, h) for b, h in heads)
+    assert unpinned == 0
+
+
+def test_full_size_64k():
+    """The 64K-token workload at its full size, in the launch shape the benchmark times."""
+    say("[full size c4]")
+    inp = make_layer(4, 0, device=DEV)
+    cfg = inp.cfg
+    sampled = [(0, 0), (0, 13), (0, 31)]
+    ok = plant(inp, sampled)
+    assert all(ok.values())
+    pyr, res = run(inp)
+    check_structure(res, cfg.budgets, cfg.levels, cfg.n_prompt)
+    for b, h in sampled:
+        assert check_head(inp, res, b, h) == 0
+        approx, _ = haar_pyramid(to_f64(inp.k[b, h, :cfg.n_prompt]), cfg.levels)
+        top = pyr.top[b, h].cpu().numpy()
+        assert np.abs(top - approx[cfg.levels]).max() <= 1e-5 * (1 + np.abs(approx[cfg.levels]).max())
+    assert torch_attend_all(inp, res) <= TOL["bf16"]
+
+
+def test_full_size_128k_32_layers():
+    """32 layers x 2 sequences x 32 heads of a 128K-token prompt resident at once
+    (about 128 GiB of KV); every layer is built and stepped, sampled heads of
+    the first and last layers are compared with the oracle."""
+    cfg = CONFIGS[5]
+    layers = []
+    sampled = {0: [(0, 0), (1, 31)], cfg.layers - 1: [(1, 7)]}
+    try:
+        for layer in range(cfg.layers):
+            say(f"[full size c5] generate layer {layer}")
+            inp = make_layer(5, layer, device=DEV)
+            if layer in sampled:
+                assert all(plant(inp, sampled[layer]).values())
+            layers.append(inp)
+        pyrs = []
+        for layer, inp in enumerate(layers):
+            pyrs.append(wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels))
+        results = []
+        for layer, inp in enumerate(layers):
+            results.append(wf.select_attend(inp.q, pyrs[layer], inp.k, inp.v, inp.gen_idx, cfg.budgets,
+                                            levels_out=True))
+        torch.cuda.synchronize()
+        say("[full size c5] checking")
+        for layer in (0, cfg.layers // 2, cfg.layers - 1):
+            check_structure(results[layer], cfg.budgets, cfg.levels, cfg.n_prompt)
+        for layer, heads in sampled.items():
+            for b, h in heads:
+                assert check_head(layers[layer], results[layer], b, h) == 0
+        assert torch_attend_all(layers[cfg.layers - 1], results[cfg.layers - 1]) <= TOL["bf16"]
+    finally:
+        del layers
+        torch.cuda.empty_cache()
+
+
+def custom(base, **kw):
+    return dataclasses.replace(CONFIGS[base], **kw)
+
+
+EDGE = [
+    # name, config, budgets, levels
+    ("dense-L0-f32", custom(1, cid=90, n_prompt=512, n_gen=16, levels=0, n_spans=0), [512], 0),
+    ("dense-L0-bf16", custom(2, cid=91, heads=2, n_prompt=256, n_gen=0, levels=0, n_spans=0), [256], 0),
+    ("ragged-nq20-b2", custom(2, cid=92, batch=2, heads=3, n_q=20, n_prompt=2048, n_gen=7, levels=4), [5, 9, 17, 30, 50], 4),
+    ("nq1-full-budget", custom(2, cid=93, heads=2, n_q=1, n_prompt=512, n_gen=3, levels=3),
+     [64, 128, 256, 512], 3),
+    ("nq64-L7", custom(5, cid=94, layers=1, batch=1, heads=2, n_q=64, n_prompt=8192, n_gen=40, levels=7, n_spans=4),
+     [9, 17, 33, 60, 110, 200, 350, 600], 7),
+    ("f32-d128", custom(2, cid=95, dtype="f32", heads=2, n_q=48, n_prompt=2048, levels=5), [6, 11, 20, 36, 64, 100], 5),
+    ("bf16-d64", custom(2, cid=96, head_dim=64, heads=4, n_q=33, n_prompt=4096, n_gen=100, levels=6),
+     [3, 6, 12, 23, 40, 70, 120], 6),
+    ("L1", custom(1, cid=97, dtype="bf16", n_prompt=256, levels=1), [70, 101], 1),
+]
+
+
+@pytest.mark.parametrize("name,cfg,budgets,levels", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, cfg, budgets, levels):
+    say(f"[edge {name}]")
+    inp = make_layer(cfg, 0)
+    heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    assert all(plant(inp, heads, budgets, levels).values())
+    to_dev(inp)
+    if cfg.n_gen == 0:
+        inp.gen_idx = torch.zeros(0, dtype=torch.int32, device=DEV)
+    elif name.startswith("ragged"):
+        # generated positions in a scrambled order
+        inp.gen_idx = inp.gen_idx[torch.randperm(cfg.n_gen, generator=torch.Generator().manual_seed(1)).to(DEV)]
+    _, res = run(inp, budgets, levels)
+    check_structure(res, budgets, levels, cfg.n_prompt)
+    for b, h in heads:
+        assert check_head(inp, res, b, h, budgets, levels) == 0
+
+
+def test_exact_ties_take_the_lower_index():
+    say("[ties]")
+    cfg = custom(2, cid=98, heads=1, n_prompt=1024, n_gen=8, levels=4, n_spans=0)
+    inp = make_layer(cfg, 0)
+    # two identical 16-token regions far above the rest: regions 5 and 40
+    inp.k[0, 0, 40 * 16:41 * 16] = inp.k[0, 0, 5 * 16:6 * 16] = (2.5 * inp.q[0, 0].float().mean(0)).to(inp.k.dtype)
+    to_dev(inp)
+    budgets = [1, 2, 4, 8, 16]
+    _, res = run(inp, budgets, 4)
+    lv = res["sel_levels"][0, 0].cpu().numpy()
+    assert lv[0] == 5
+    assert list(res["sel"][0, 0].cpu().numpy()) == list(range(80, 96))
+
+
+def test_repeat_calls_are_bitwise_identical():
+    say("[determinism]")
+    inp = to_dev(make_layer(2, 0))
+    cfg = inp.cfg
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels)
+    outs = [wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, cfg.budgets, levels_out=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for key in ("out", "sel", "sel_levels", "score_levels"):
+            assert torch.equal(o[key], outs[0][key]), key
+
+
+def test_one_workspace_serves_different_shapes():
+    say("[workspace reuse]")
+    ws = wf.Workspace(DEV)
+    a = to_dev(make_layer(1, 0))
+    b = to_dev(make_layer(2, 0))
+    pa = wf.build_pyramid(a.k, a.cfg.n_prompt, a.cfg.levels)
+    pb = wf.build_pyramid(b.k, b.cfg.n_prompt, b.cfg.levels)
+    ra1 = wf.select_attend(a.q, pa, a.k, a.v, a.gen_idx, a.cfg.budgets, workspace=ws)
+    rb = wf.select_attend(b.q, pb, b.k, b.v, b.gen_idx, b.cfg.budgets, workspace=ws)
+    ra2 = wf.select_attend(a.q, pa, a.k, a.v, a.gen_idx, a.cfg.budgets, workspace=ws)
+    rb2 = wf.select_attend(b.q, pb, b.k, b.v, b.gen_idx, b.cfg.budgets)
+    torch.cuda.synchronize()
+    assert torch.equal(ra1["out"], ra2["out"]) and torch.equal(ra1["sel"], ra2["sel"])
+    assert torch.equal(rb["out"], rb2["out"])
