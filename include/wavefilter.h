@@ -65,6 +65,12 @@ enum { WF_F32 = 0, WF_BF16 = 1 };
 /* Supported sizes. */
 #define WF_MAX_LEVELS 7      /* region of 2^L tokens, L <= 7 */
 #define WF_MAX_QUERIES 64    /* query-block rows n_q */
+#define WF_MAX_HEADS 65535   /* batch * heads */
+
+/* wf_select_attend keeps its synchronisation counters in the first
+ * WF_WORKSPACE_COUNTER_BYTES of the workspace, at the same place for every
+ * shape, so one workspace can serve calls of different shapes. */
+#define WF_WORKSPACE_COUNTER_BYTES (2u * 4u * 65536u)
 
 /*
  * Pyramid descriptor, filled by wf_build_pyramid.  `base` points to the
@@ -174,8 +180,9 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  *   score_levels NULL, or device float32 of the same shape: each kept
  *                region's score s_j
  *   workspace    device buffer of ws_bytes >= wf_select_attend_workspace_bytes;
- *                must be zero-filled before its first use; every call leaves
- *                its synchronisation counters at zero again
+ *                its first WF_WORKSPACE_COUNTER_BYTES must be zero before the
+ *                first use (zero-fill it once); every call leaves them zero
+ *                again.  The rest is scratch and may hold anything.
  */
 int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const void* v,
                      int32_t n_tot, const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets,

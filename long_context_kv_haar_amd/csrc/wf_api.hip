@@ -19,7 +19,7 @@ int elem_bytes(int dtype) { return dtype == WF_BF16 ? 2 : 4; }
 
 bool valid_pyramid_shape(int32_t batch, int32_t heads, int32_t n_prompt, int32_t head_dim, int32_t levels) {
   if (batch < 1 || heads < 1 || n_prompt < 1) return false;
-  if ((int64_t)batch * heads > 65535) return false;
+  if ((int64_t)batch * heads > WF_MAX_HEADS) return false;
   if (head_dim != 64 && head_dim != 128) return false;
   if (levels < 0 || levels > WF_MAX_LEVELS) return false;
   if (n_prompt % (1 << levels) != 0) return false;
@@ -111,7 +111,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
-  P->off_counters = w; w += align_up(H * 4 * 4);
+  P->off_counters = w; w += WF_WORKSPACE_COUNTER_BYTES;  // same place and size for every shape
   P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);

@@ -188,7 +188,7 @@ struct StepArgs {
   int32_t* sel_out;
   int32_t* sel_levels;
   float* score_levels;
-  int32_t* counters;     // [heads_total][4]
+  int32_t* counters;     // [WF_MAX_HEADS + 1][2]: coarse, attend
   uint32_t* keys_top;    // [heads_total][n_top]
   int32_t* sel_top;      // [heads_total][k_top]
   float* cov;            // [heads_total][cov_len]
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
   if (g == 0 && valid) keys[n] = order_key(m * a.inv_sqrt_d);
 
-  if (!last_arrival(a.counters + head * 4 + 0, gridDim.x)) return;
+  if (!last_arrival(a.counters + head * 2 + 0, gridDim.x)) return;
   __shared__ TopKShared<256> sh;
   auto key = [&](int i) { return keys[i]; };
   const Threshold t = radix_select<256>(key, a.n_top, a.k_top, sh);
@@ -342,8 +342,8 @@ __global__ __launch_bounds__(256) void cover_kernel(StepArgs a) {
     const int64_t p = wave_base + 16 * t + l16;
     Frag<T, D> b;
     if (p < a.covered) {
-      int64_t tok = ((int64_t)sel[p >> L] << L) + (p & ((1 << L) - 1));
-      tok = tok < a.n_prompt ? tok : a.n_prompt - 1;
+      const int r = clampi(sel[p >> L], 0, a.n_top - 1);  // kept region (clamped: memory safety)
+      const int64_t tok = ((int64_t)r << L) + (p & ((1 << L) - 1));
       b.load(kh + tok * D, g);
     } else {
       b.zero();
@@ -437,8 +437,9 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(StepArgs a) {
   float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   for (int i = threadIdx.x; i < a.k_top; i += NT) {
     cur[i] = i;
-    if (dbg_sel) dbg_sel[i] = sel_top[i];
-    if (dbg_score) dbg_score[i] = key_to_f32(keys_top[sel_top[i]]);
+    const int r = clampi(sel_top[i], 0, a.n_top - 1);
+    if (dbg_sel) dbg_sel[i] = r;
+    if (dbg_score) dbg_score[i] = key_to_f32(keys_top[r]);
   }
   __syncthreads();
   int kprev = a.k_top, dbg_off = a.k_top;
@@ -446,19 +447,20 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(StepArgs a) {
     const int kj = a.budgets[L - j];
     const int n = 2 * kprev;
     const float* cj = a.cov + (int64_t)head * a.cov_len + a.cov_off[j];
-    for (int c = threadIdx.x; c < n; c += NT) keys[c] = order_key(cj[2 * cur[c >> 1] + (c & 1)]);
+    const int nj = (int)(a.covered >> j);  // level-j positions in the covered set
+    for (int c = threadIdx.x; c < n; c += NT) keys[c] = order_key(cj[clampi(2 * cur[c >> 1] + (c & 1), 0, nj - 1)]);
     __syncthreads();
     auto key = [&](int i) { return keys[i]; };
     const Threshold t = radix_select<NT>(key, n, kj, sh);
     topk_compact<NT>(key, n, t, sh, [&](int o, int i) {
-      if (o < kj) nxt[o] = 2 * cur[i >> 1] + (i & 1);
+      if (o < kj) nxt[o] = clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1);
     });
     __syncthreads();
     if (dbg_sel || dbg_score) {
       const int sh_l = L - j;
       for (int o = threadIdx.x; o < kj; o += NT) {
         const int p = nxt[o];
-        if (dbg_sel) dbg_sel[dbg_off + o] = (sel_top[p >> sh_l] << sh_l) + (p & ((1 << sh_l) - 1));
+        if (dbg_sel) dbg_sel[dbg_off + o] = (clampi(sel_top[p >> sh_l], 0, a.n_top - 1) << sh_l) + (p & ((1 << sh_l) - 1));
         if (dbg_score) dbg_score[dbg_off + o] = cj[p];
       }
     }
@@ -473,7 +475,7 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(StepArgs a) {
   int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
   for (int o = threadIdx.x; o < a.k0; o += NT) {
     const int p = cur[o];
-    const int tok = (sel_top[p >> L] << L) + (p & ((1 << L) - 1));
+    const int tok = (clampi(sel_top[clampi(p >> L, 0, a.k_top - 1)], 0, a.n_top - 1) << L) + (p & ((1 << L) - 1));
     s0[o] = tok;
     if (so) so[o] = tok;
   }
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(64 * NQT) void attend_kernel(StepArgs a) {
           make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
   }
 
-  if (!last_arrival(a.counters + head * 4 + 2, gridDim.x)) return;
+  if (!last_arrival(a.counters + head * 2 + 1, gridDim.x)) return;
   // merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
   __shared__ float wgt[kMaxSplit * 64];
   const float* ml = a.part_ml + (int64_t)head * a.n_split * 2 * a.n_q;

@@ -188,8 +188,14 @@ def test_repeat_calls_are_bitwise_identical():
 
 
 def test_one_workspace_serves_different_shapes():
+    """Calls of different head counts share one workspace (the counters keep
+    one fixed place, so a 1-head call cannot leave data where a 32-head call
+    keeps its counters)."""
     say("[workspace reuse]")
     ws = wf.Workspace(DEV)
+    one = to_dev(make_layer(dataclasses.replace(CONFIGS[2], cid=99, heads=1, n_prompt=1024, n_gen=8), 0))
+    p1 = wf.build_pyramid(one.k, 1024, 4)
+    r1 = wf.select_attend(one.q, p1, one.k, one.v, one.gen_idx, [4, 8, 16, 32, 64], workspace=ws)
     a = to_dev(make_layer(1, 0))
     b = to_dev(make_layer(2, 0))
     pa = wf.build_pyramid(a.k, a.cfg.n_prompt, a.cfg.levels)
@@ -198,6 +204,8 @@ def test_one_workspace_serves_different_shapes():
     rb = wf.select_attend(b.q, pb, b.k, b.v, b.gen_idx, b.cfg.budgets, workspace=ws)
     ra2 = wf.select_attend(a.q, pa, a.k, a.v, a.gen_idx, a.cfg.budgets, workspace=ws)
     rb2 = wf.select_attend(b.q, pb, b.k, b.v, b.gen_idx, b.cfg.budgets)
+    r1b = wf.select_attend(one.q, p1, one.k, one.v, one.gen_idx, [4, 8, 16, 32, 64], workspace=ws)
     torch.cuda.synchronize()
+    assert torch.equal(r1["out"], r1b["out"])
     assert torch.equal(ra1["out"], ra2["out"]) and torch.equal(ra1["sel"], ra2["sel"])
     assert torch.equal(rb["out"], rb2["out"])
