@@ -66,11 +66,7 @@ enum { WF_F32 = 0, WF_BF16 = 1 };
 #define WF_MAX_LEVELS 7      /* region of 2^L tokens, L <= 7 */
 #define WF_MAX_QUERIES 64    /* query-block rows n_q */
 #define WF_MAX_HEADS 65535   /* batch * heads */
-
-/* wf_select_attend keeps its synchronisation counters in the first
- * WF_WORKSPACE_COUNTER_BYTES of the workspace, at the same place for every
- * shape, so one workspace can serve calls of different shapes. */
-#define WF_WORKSPACE_COUNTER_BYTES (2u * 4u * 65536u)
+#define WF_MAX_KEEP_TOP 16384 /* k_L, the kept coarse regions */
 
 /*
  * Pyramid descriptor, filled by wf_build_pyramid.  `base` points to the
@@ -169,7 +165,9 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  *                heads (normally N_p .. n_tot-1); NULL allowed when n_gen == 0;
  *                out-of-range entries are clamped, not reported
  *   budgets      HOST int32 [levels + 1] = k_L, ..., k_0 with
- *                1 <= k_L <= N_p/2^L and 1 <= k_j <= min(2 k_{j+1}, N_p/2^j)
+ *                1 <= k_L <= min(N_p/2^L, WF_MAX_KEEP_TOP) and
+ *                1 <= k_j <= min(2 k_{j+1}, N_p/2^j); WF_ERR_BUDGET also when
+ *                the refinement state would not fit one workgroup's LDS
  *   n_q          1 .. WF_MAX_QUERIES
  *   out          device float32 [batch, heads, n_q, head_dim]
  *   sel_out      NULL, or device int32 [batch, heads, k_0]: kept prompt
@@ -180,9 +178,7 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  *   score_levels NULL, or device float32 of the same shape: each kept
  *                region's score s_j
  *   workspace    device buffer of ws_bytes >= wf_select_attend_workspace_bytes;
- *                its first WF_WORKSPACE_COUNTER_BYTES must be zero before the
- *                first use (zero-fill it once); every call leaves them zero
- *                again.  The rest is scratch and may hold anything.
+ *                scratch only: its contents on entry do not matter
  */
 int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const void* v,
                      int32_t n_tot, const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets,

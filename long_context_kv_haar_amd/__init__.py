@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     WF_F32,
     WF_PYR_ALL_LEVELS,
     Pyramid,
+    PreparedBuild,
+    PreparedStep,
     WfError,
     Workspace,
     build_pyramid,

@@ -232,3 +232,48 @@ def split_levels(flat, budgets):
         out[L - i] = flat[..., off:off + kb]
         off += kb
     return out
+
+
+class PreparedStep:
+    """A select-attend call with every argument marshalled once, for tight
+    loops (benchmarks, serving): calling it only crosses into the library."""
+
+    def __init__(self, q, pyr, k, v, gen_idx, budgets, out, sel_out, workspace, sel_levels=None, score_levels=None):
+        n_gen = 0 if gen_idx is None else gen_idx.numel()
+        self._keep = (q, pyr, k, v, gen_idx, out, sel_out, workspace, sel_levels, score_levels)
+        self._barr = _budget_array(budgets)
+        need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), q.shape[2], n_gen, self._barr))
+        if need == 0 or workspace.numel() < need:
+            raise WfError(-6, "PreparedStep")
+
+        def ptr(t):
+            return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+        self._args = (ptr(q), ctypes.byref(pyr.desc), ptr(k), ptr(v), k.shape[2], ptr(gen_idx), n_gen, self._barr,
+                      q.shape[2], ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels), ptr(workspace),
+                      workspace.numel(), _stream_handle(q.device))
+        self._fn = lib().wf_select_attend
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != WF_OK:
+            raise WfError(st, "wf_select_attend")
+
+
+class PreparedBuild:
+    """A pyramid build with its arguments marshalled once."""
+
+    def __init__(self, k, n_prompt, levels, buf, flags=0):
+        B, H, N, d = k.shape
+        self.desc = WfPyramid()
+        self._keep = (k, buf)
+        self._args = (ctypes.c_void_p(k.data_ptr()), N * d, B, H, n_prompt, d, _dtype_code(k), levels, flags,
+                      ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.byref(self.desc), _stream_handle(k.device))
+        self._fn = lib().wf_build_pyramid
+        self.pyramid = Pyramid(buf, self.desc)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != WF_OK:
+            raise WfError(st, "wf_build_pyramid")
+        return self.pyramid

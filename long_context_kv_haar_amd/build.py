@@ -5,7 +5,7 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("wf_api.hip", "wf_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("wf_api.hip", "wf_pyramid.hip", "wf_step.hip")]
 LIB_PATH = os.path.join(HERE, "libwavefilter.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -90,32 +90,45 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->k_top = P->budgets[0];
   P->k0 = P->budgets[L];
   P->sum_k = (int)sum_k;
+  if (P->k_top > wf::kMaxKeepTop) return WF_ERR_BUDGET;
   P->covered = (int64_t)P->k_top << L;
   int64_t off = 0;
-  for (int j = 0; j < L; ++j) {
+  for (int j = 0; j < L; ++j) {  // level arrays start on 16-byte boundaries
     P->cov_off[j] = off;
-    off += P->covered >> j;
+    off += ((P->covered >> j) + 3) / 4 * 4;
   }
   P->cov_len = off;
-  P->refine_lds = 4 * (nmax + 2 * kmax);
-  if (P->refine_lds > wf::kRefineLdsBytes) return WF_ERR_BUDGET;
-  // attention split: about one workgroup per compute unit in total
+  // cover kernel: kept coarse regions (+ the coarse keys when they fit) in LDS
+  P->coarse_keys_in_lds = P->n_top <= wf::kMaxCoarseLds;
+  P->cover_lds = 4 * (((P->k_top + 3) & ~3) + (P->coarse_keys_in_lds ? P->n_top : 0));
+  // attention: about one workgroup per compute unit in total
   P->n_att = P->k0 + n_gen;
-  const int chunk = (pyr->dtype == WF_BF16) ? wf::kAttendChunkBf16 : wf::kAttendChunkF32;
-  P->n_chunks = (P->n_att + chunk - 1) / chunk;
+  P->chunk = wf::attend_chunk(pyr->dtype, (n_q + 15) / 16);
+  P->n_chunks = (P->n_att + P->chunk - 1) / P->chunk;
   int target = (256 + P->heads_total - 1) / P->heads_total;
   if (target > wf::kMaxSplit) target = wf::kMaxSplit;
   if (target < 1) target = 1;
   P->chunks_per_split = (P->n_chunks + target - 1) / target;
   P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
+  // attention workgroup LDS: the attended-set list, then (aliased) the
+  // refinement state or the K/V chunk buffers
+  P->att_t_words = (P->n_att + 3) & ~3;
+  P->refine_nmax = (nmax + 3) / 4 * 4;
+  P->refine_kmax = (kmax + 3) / 4 * 4;
+  const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
+  const int64_t refine_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
+  if (refine_base > budget) return WF_ERR_BUDGET;
+  P->refine_cov_in_lds = (refine_base + 4 * P->cov_len) <= budget;
+  const int64_t refine_bytes = refine_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0);
+  const int64_t buf_bytes = wf::attend_buffer_bytes(pyr->dtype, pyr->head_dim, (n_q + 15) / 16);
+  if (buf_bytes > budget) return WF_ERR_BUDGET;
+  P->attend_lds = (int)(4 * (int64_t)P->att_t_words + (refine_bytes > buf_bytes ? refine_bytes : buf_bytes));
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
-  P->off_counters = w; w += WF_WORKSPACE_COUNTER_BYTES;  // same place and size for every shape
   P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
-  P->off_sel0 = w;     w += align_up(H * (uint64_t)P->k0 * 4);
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * P->head_dim * 4);
   P->total = w;

@@ -147,95 +147,207 @@ __device__ __forceinline__ float key_to_f32(uint32_t k) {
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup-wide Top-K by radix select on 32-bit keys (8-bit digits, most
-// significant first), followed by a stable compaction in index order.  The
-// kept set is: every key above the threshold, and of the keys equal to it,
-// the ones with the lowest indices.  NT = threads in the workgroup (a
-// multiple of 64).  All threads must call these functions together.
+// Workgroup-wide Top-K on 32-bit keys.
+//
+// select_threshold narrows the k-th largest key by range bisection: the keys
+// still in play lie in [lo, lo + range]; each pass counts them into at most
+// kTopKBins bins of width 2^s (bin = (key - lo) >> s) with LDS atomics, finds
+// the bin holding the k-th largest, and recurses into it.  Starting from the
+// actual [min, max] of the keys spreads them over the bins (scores of one
+// level share their leading bits, so fixed-digit radix passes would pile
+// every key into one bin and serialise the atomics); a pass ends the search
+// once every key of the chosen bin is kept, or the bin holds a single value.
+// The bin search is spread over the whole workgroup: thread t owns the
+// contiguous bins [t B, (t+1) B), B = kTopKBins / NT, read with 16-byte LDS
+// loads, and one workgroup scan of the per-thread totals locates the bin.
+//
+// The kept set is: every key > hi, and of the keys in [lo, hi] the `need`
+// ones with the lowest indices (when the search narrowed to one value,
+// lo == hi and these are ties, resolved toward lower indices).  topk_compact
+// emits the kept indices in ascending order with a single workgroup scan.
+// NT = threads of the workgroup (a multiple of 64, at most 1024); all threads
+// must call these functions together.
 // ---------------------------------------------------------------------------
+constexpr int kTopKBins = 4096;
+constexpr int floor_log2(int x) { return x <= 1 ? 0 : 1 + floor_log2(x / 2); }
+
 template <int NT> struct TopKShared {
-  int hist[256];
-  int wsum[NT / 64];
+  int hist[kTopKBins];
+  uint32_t wmin[NT / 64], wmax[NT / 64];
+  int wsum_a[NT / 64], wsum_b[NT / 64];
   int bcast[4];
 };
 
+struct Threshold {
+  uint32_t lo, hi;
+  int need;
+};
+
+// Wave-wide reductions and scans on DPP row operations plus readlane (a
+// few cycles each, no LDS round trip).  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_or0(int x) {  // x of the source lane, 0 where none
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = min(x, dpp_u<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = min(x, dpp_u<0x141>(x));  // row_half_mirror
+  x = min(x, dpp_u<0x140>(x));  // row_mirror: every lane holds its row's min
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u<0xB1>(x));
+  x = max(x, dpp_u<0x4E>(x));
+  x = max(x, dpp_u<0x141>(x));
+  x = max(x, dpp_u<0x140>(x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+// Inclusive prefix sum over the lanes of a wave; *total receives the sum.
+__device__ __forceinline__ int wave_incl_scan(int x, int* total) {
+  x += dpp_or0<0x111>(x);  // row_shr:1
+  x += dpp_or0<0x112>(x);  // row_shr:2
+  x += dpp_or0<0x114>(x);  // row_shr:4
+  x += dpp_or0<0x118>(x);  // row_shr:8 -> inclusive within each row of 16
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+  const int row = (threadIdx.x & 63) >> 4;
+  x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+  *total = r0 + r1 + r2 + r3;
+  return x;
+}
+
+// Inclusive scan of one int per thread across the workgroup (one barrier;
+// the caller must not touch `wsum` again before another barrier).
 template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+__device__ __forceinline__ int block_incl_scan(int a, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
+  int t;
+  const int x = wave_incl_scan(a, &t);
+  if (lane == 0) wsum[w] = t;
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) {
-    int s = wsum[i];
-    base += (i < w) ? s : 0;
-    tot += s;
+    const int v = wsum[i];
+    base += (i < w) ? v : 0;
+    tot += v;
   }
-  __syncthreads();
   *total = tot;
-  return base + x - v;
+  return base + x;
 }
 
-struct Threshold {
-  uint32_t prefix;  // kept: (key & mask) > prefix, or == prefix and among the first `need`
-  uint32_t mask;
-  int need;
-};
+// Exclusive scan of two ints per thread across the workgroup.
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* wa, int* wb, int& ea, int& eb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int ta, tb;
+  const int x = wave_incl_scan(a, &ta);
+  const int y = wave_incl_scan(b, &tb);
+  if (lane == 0) {
+    wa[w] = ta;
+    wb[w] = tb;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    if (i < w) {
+      ba += wa[i];
+      bb += wb[i];
+    }
+  }
+  __syncthreads();
+  ea = ba + x - a;
+  eb = bb + y - b;
+}
 
 template <int NT, class KeyFn>
-__device__ Threshold radix_select(KeyFn key, int n, int k, TopKShared<NT>& sh) {
-  Threshold t{0u, 0u, k};
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += NT) {
-      uint32_t x = key(i);
-      if ((x & t.mask) == t.prefix) atomicAdd(&sh.hist[(x >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      const int h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1];
-      const int h2 = sh.hist[4 * lane + 2], h3 = sh.hist[4 * lane + 3];
-      const int s = h0 + h1 + h2 + h3;
-      int x = s;  // inclusive suffix sum over lanes
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_down(x, o, 64);
-        if (lane + o < 64) x += y;
-      }
-      const int kk = t.need;
-      int a = x - s;  // keys in higher lanes' bins
-      int digit = -1, rem = 0, cnt = 0;
-      if (a < kk && kk <= a + h3) { digit = 4 * lane + 3; rem = kk - a; cnt = h3; }
-      a += h3;
-      if (digit < 0 && a < kk && kk <= a + h2) { digit = 4 * lane + 2; rem = kk - a; cnt = h2; }
-      a += h2;
-      if (digit < 0 && a < kk && kk <= a + h1) { digit = 4 * lane + 1; rem = kk - a; cnt = h1; }
-      a += h1;
-      if (digit < 0 && a < kk && kk <= a + h0) { digit = 4 * lane; rem = kk - a; cnt = h0; }
-      if (digit >= 0) {
-        sh.bcast[0] = digit;
-        sh.bcast[1] = rem;
-        sh.bcast[2] = cnt;
-      }
-    }
-    __syncthreads();
-    const int digit = sh.bcast[0];
-    t.need = sh.bcast[1];
-    const int cnt = sh.bcast[2];
-    t.prefix |= (uint32_t)digit << shift;
-    t.mask |= 255u << shift;
-    __syncthreads();
-    if (cnt == t.need) break;  // the whole bin is kept: no tie to resolve below
+__device__ Threshold select_threshold(KeyFn key, int n, int k, TopKShared<NT>& sh) {
+  constexpr int BPT = (kTopKBins / NT) & ~3;  // bins per thread in the bin search
+  constexpr int LOGB = floor_log2(NT * BPT);   // bins used per pass: 2^LOGB
+  static_assert(BPT >= 4, "too many threads for the bin search");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t x = key(i);
+    mn = min(mn, x);
+    mx = max(mx, x);
   }
-  return t;
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    sh.wmin[w] = mn;
+    sh.wmax[w] = mx;
+  }
+  int4* own = reinterpret_cast<int4*>(sh.hist + threadIdx.x * BPT);
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    mn = min(mn, sh.wmin[i]);
+    mx = max(mx, sh.wmax[i]);
+  }
+  uint32_t lo = mn, range = mx - mn;
+  int need = k;
+  while (range != 0) {
+    const int bits = 32 - __clz(range);
+    const int s = bits > LOGB ? bits - LOGB : 0;  // (key - lo) >> s < 2^LOGB
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint32_t d = key(i) - lo;  // wraps above range for keys below lo
+      if (d <= range) atomicAdd(&sh.hist[d >> s], 1);
+    }
+    __syncthreads();
+    // bin search: per-thread totals of its own bins, then a workgroup scan
+    int h[BPT];
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) {
+      const int4 v = own[i];
+      h[4 * i] = v.x;
+      h[4 * i + 1] = v.y;
+      h[4 * i + 2] = v.z;
+      h[4 * i + 3] = v.w;
+      tot += v.x + v.y + v.z + v.w;
+    }
+    int all;
+    const int incl = block_incl_scan<NT>(tot, sh.wsum_a, &all);
+    int above = all - incl;  // keys in bins owned by higher threads
+    if (above < need && need <= above + tot) {
+#pragma unroll
+      for (int i = BPT - 1; i >= 0; --i) {
+        if (above < need && need <= above + h[i]) {
+          sh.bcast[0] = threadIdx.x * BPT + i;
+          sh.bcast[1] = need - above;
+          sh.bcast[2] = h[i];
+        }
+        above += h[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    const int b = sh.bcast[0];
+    need = sh.bcast[1];
+    const int cnt = sh.bcast[2];
+    lo += (uint32_t)b << s;
+    const uint32_t rest = range - ((uint32_t)b << s);
+    range = s == 0 ? 0u : min(rest, (1u << s) - 1u);
+    if (cnt == need) break;
+    __syncthreads();  // bcast and wsum are rewritten by the next pass
+  }
+  return Threshold{lo, lo + range, need};
 }
 
 // Calls out(o, i) for the kept indices i in ascending order, o = 0..k-1.
@@ -243,25 +355,290 @@ template <int NT, class KeyFn, class OutFn>
 __device__ void topk_compact(KeyFn key, int n, Threshold t, TopKShared<NT>& sh, OutFn out) {
   const int seg = (n + NT - 1) / NT;
   const int i0 = min(n, (int)threadIdx.x * seg), i1 = min(n, i0 + seg);
-  int eq = 0;
-  for (int i = i0; i < i1; ++i) eq += ((key(i) & t.mask) == t.prefix);
-  int tot;
-  const int eq_before = block_exclusive_scan<NT>(eq, sh.wsum, &tot);
-  int r = eq_before, cnt = 0;
+  int g = 0, e = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t x = key(i) & t.mask;
-    const bool e = (x == t.prefix);
-    cnt += (x > t.prefix) || (e && r < t.need);
-    r += e;
+    const uint32_t x = key(i);
+    g += x > t.hi;
+    e += (x >= t.lo) & (x <= t.hi);
   }
-  int o = block_exclusive_scan<NT>(cnt, sh.wsum, &tot);
-  r = eq_before;
+  int G, E;
+  block_exclusive_scan2<NT>(g, e, sh.wsum_a, sh.wsum_b, G, E);
   for (int i = i0; i < i1; ++i) {
-    const uint32_t x = key(i) & t.mask;
-    const bool e = (x == t.prefix);
-    if ((x > t.prefix) || (e && r < t.need)) out(o++, i);
-    r += e;
+    const uint32_t x = key(i);
+    const bool gt = x > t.hi;
+    const bool eq = (x >= t.lo) & (x <= t.hi);
+    if (gt || (eq && E < t.need)) out(G + min(E, t.need), i);
+    G += gt;
+    E += eq;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Top-K in (usually) one histogram pass.  The kept set of "the k best by
+// (key descending, index ascending)" is exactly the set of indices i with
+// (key_i > tk) or (key_i == tk and i <= ti), where (tk, ti) is the k-th best
+// (key, index) pair.  One pass counts the keys into kTopKBins bins spanning
+// their [min, max]; the bin holding the k-th best is found by a workgroup
+// scan.  If every key of that bin is kept, (tk, ti) = (bin start, any).
+// Otherwise the bin's keys (a handful: the bins split the range finely) are
+// gathered with their indices and ranked exactly inside one wave.  A bin with
+// more than kGatherMax keys (heavy ties) falls back to select_threshold +
+// topk_compact.  Emits the kept indices in ascending order with one scan.
+// ---------------------------------------------------------------------------
+constexpr int kGatherMax = 64;
+
+template <int NT> struct TopKFastShared {
+  TopKShared<NT> base;
+  uint32_t gkey[kGatherMax];
+  int gidx[kGatherMax];
+  int gcount;
+  uint32_t tk;
+  int ti;
+};
+
+template <int NT, class KeyFn, class OutFn>
+__device__ void topk_fast(KeyFn key, int n, int k, TopKFastShared<NT>& fs, OutFn out) {
+  constexpr int BPT = (kTopKBins / NT) & ~3;
+  constexpr int LOGB = floor_log2(NT * BPT);
+  TopKShared<NT>& sh = fs.base;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t x = key(i);
+    mn = min(mn, x);
+    mx = max(mx, x);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    sh.wmin[w] = mn;
+    sh.wmax[w] = mx;
+  }
+  int4* own = reinterpret_cast<int4*>(sh.hist + threadIdx.x * BPT);
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
+  if (threadIdx.x == 0) fs.gcount = 0;
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    mn = min(mn, sh.wmin[i]);
+    mx = max(mx, sh.wmax[i]);
+  }
+  const uint32_t range = mx - mn;
+  uint32_t tk;
+  int ti;
+  bool general = false;
+  if (range == 0) {  // all keys equal: the k lowest indices
+    tk = mn;
+    ti = k - 1;
+  } else {
+    const int bits = 32 - __clz(range);
+    const int s = bits > LOGB ? bits - LOGB : 0;
+    for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sh.hist[(key(i) - mn) >> s], 1);
+    __syncthreads();
+    int h[BPT];
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) {
+      const int4 v = own[i];
+      h[4 * i] = v.x;
+      h[4 * i + 1] = v.y;
+      h[4 * i + 2] = v.z;
+      h[4 * i + 3] = v.w;
+      tot += v.x + v.y + v.z + v.w;
+    }
+    int all;
+    const int incl = block_incl_scan<NT>(tot, sh.wsum_a, &all);
+    int above = all - incl;
+    if (above < k && k <= above + tot) {  // exactly one thread
+      int bin = 0, rem = 0, c = 0;
+#pragma unroll
+      for (int i = BPT - 1; i >= 0; --i) {
+        const bool hit = (above < k) & (k <= above + h[i]);
+        bin = hit ? i : bin;
+        rem = hit ? k - above : rem;
+        c = hit ? h[i] : c;
+        above += h[i];
+      }
+      sh.bcast[0] = threadIdx.x * BPT + bin;
+      sh.bcast[1] = rem;
+      sh.bcast[2] = c;
+    }
+    __syncthreads();
+    const int b = sh.bcast[0], need = sh.bcast[1], cnt = sh.bcast[2];
+    const uint32_t blo = mn + ((uint32_t)b << s);
+    const uint32_t bhi = blo + (s == 0 ? 0u : min(range - ((uint32_t)b << s), (1u << s) - 1u));
+    if (cnt == need) {  // the whole bin is kept
+      tk = blo;
+      ti = 0x7FFFFFFF;
+    } else if (cnt <= kGatherMax) {
+      for (int i = threadIdx.x; i < n; i += NT) {
+        const uint32_t x = key(i);
+        if (x >= blo && x <= bhi) {
+          const int slot = atomicAdd(&fs.gcount, 1);
+          fs.gkey[slot] = x;
+          fs.gidx[slot] = i;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < 64) {  // rank the gathered keys; rank need-1 is the threshold
+        const bool act = lane < cnt;
+        const uint32_t x = act ? fs.gkey[lane] : 0u;
+        const int xi = act ? fs.gidx[lane] : 0;
+        int rank = 0;
+        for (int m = 0; m < cnt; ++m) {
+          const uint32_t y = fs.gkey[m];
+          const int yi = fs.gidx[m];
+          rank += (y > x) | ((y == x) & (yi < xi));
+        }
+        if (act && rank == need - 1) {
+          fs.tk = x;
+          fs.ti = xi;
+        }
+      }
+      __syncthreads();
+      tk = fs.tk;
+      ti = fs.ti;
+    } else {
+      general = true;
+    }
+  }
+  if (general) {  // heavily tied bin: multi-pass search
+    __syncthreads();
+    const Threshold t = select_threshold<NT>(key, n, k, sh);
+    topk_compact<NT>(key, n, t, sh, out);
+    return;
+  }
+  // compaction in index order
+  const int seg = (n + NT - 1) / NT;
+  const int i0 = min(n, (int)threadIdx.x * seg), i1 = min(n, i0 + seg);
+  int c = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = key(i);
+    c += (x > tk) | ((x == tk) & (i <= ti));
+  }
+  int all;
+  int o = block_incl_scan<NT>(c, sh.wsum_a, &all) - c;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = key(i);
+    if ((x > tk) | ((x == tk) & (i <= ti))) out(o++, i);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident Top-K for n <= NT * KPT keys: thread t holds keys
+// [t KPT, t KPT + KPT) (its contiguous segment, so the ascending output order
+// is the thread order) in registers for the whole selection, so every key is
+// read from memory once.  Same rule and result as select_threshold +
+// topk_compact; 2048 bins per pass, searched branch-free over the 2048 / NT
+// bins each thread owns.  out(o, i, j) receives the output slot o, the key
+// index i and the register slot j of the key.
+// ---------------------------------------------------------------------------
+template <int NT, int KPT, class OutFn>
+__device__ void topk_regs(const uint32_t (&key)[KPT], int n, int k, TopKShared<NT>& sh, OutFn out) {
+  constexpr int BPT = (2048 / NT) >= 4 ? ((2048 / NT) & ~3) : 4;  // bins per thread
+  constexpr int LOGB = floor_log2(NT * BPT);                      // bins used per pass: 2^LOGB
+  static_assert(NT * BPT <= kTopKBins, "bin search layout");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i0 = threadIdx.x * KPT;
+  const int cnt = max(0, min(KPT, n - i0));
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (j < cnt) {
+      mn = min(mn, key[j]);
+      mx = max(mx, key[j]);
+    }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    sh.wmin[w] = mn;
+    sh.wmax[w] = mx;
+  }
+  int4* own = reinterpret_cast<int4*>(sh.hist + threadIdx.x * BPT);
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    mn = min(mn, sh.wmin[i]);
+    mx = max(mx, sh.wmax[i]);
+  }
+  uint32_t lo = mn, range = mx - mn;
+  int need = k;
+  while (range != 0) {
+    const int bits = 32 - __clz(range);
+    const int s = bits > LOGB ? bits - LOGB : 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t d = key[j] - lo;  // wraps above range for keys below lo
+      if (j < cnt && d <= range) atomicAdd(&sh.hist[d >> s], 1);
+    }
+    __syncthreads();
+    int h[BPT];
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) {
+      const int4 v = own[i];
+      h[4 * i] = v.x;
+      h[4 * i + 1] = v.y;
+      h[4 * i + 2] = v.z;
+      h[4 * i + 3] = v.w;
+      tot += v.x + v.y + v.z + v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
+    int all;
+    const int incl = block_incl_scan<NT>(tot, sh.wsum_a, &all);
+    int above = all - incl;  // keys in bins owned by higher threads
+    if (above < need && need <= above + tot) {  // exactly one thread
+      int bin = 0, rem = 0, c = 0;
+#pragma unroll
+      for (int i = BPT - 1; i >= 0; --i) {
+        const bool hit = (above < need) & (need <= above + h[i]);
+        bin = hit ? i : bin;
+        rem = hit ? need - above : rem;
+        c = hit ? h[i] : c;
+        above += h[i];
+      }
+      sh.bcast[0] = threadIdx.x * BPT + bin;
+      sh.bcast[1] = rem;
+      sh.bcast[2] = c;
+    }
+    __syncthreads();
+    const int b = sh.bcast[0];
+    need = sh.bcast[1];
+    const int c = sh.bcast[2];
+    lo += (uint32_t)b << s;
+    const uint32_t rest = range - ((uint32_t)b << s);
+    range = s == 0 ? 0u : min(rest, (1u << s) - 1u);
+    if (c == need) break;
+    __syncthreads();  // bcast and wsum are rewritten by the next pass
+  }
+  const uint32_t hi = lo + range;
+  int g = 0, e = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (j < cnt) {
+      g += key[j] > hi;
+      e += (key[j] >= lo) & (key[j] <= hi);
+    }
+  int G, E;
+  block_exclusive_scan2<NT>(g, e, sh.wsum_a, sh.wsum_b, G, E);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (j < cnt) {
+      const bool gt = key[j] > hi;
+      const bool eq = (key[j] >= lo) & (key[j] <= hi);
+      if (gt || (eq && E < need)) out(G + min(E, need), i0 + j, j);
+      G += gt;
+      E += eq;
+    }
 }
 
 }  // namespace wf

@@ -9,12 +9,17 @@
 namespace wf {
 
 constexpr int kMaxLevels = WF_MAX_LEVELS;
-constexpr int kCoverTokensPerWave = 64;  // positions per wave in the coverage kernel
-constexpr int kAttendChunkBf16 = 64;     // tokens per attention chunk (bf16)
-constexpr int kAttendChunkF32 = 32;      // tokens per attention chunk (f32)
-constexpr int kMaxSplit = 16;            // attention splits per head
-constexpr int kRefineThreads = 512;
-constexpr int kRefineLdsBytes = 64 * 1024;
+constexpr int kAttendChunkF32 = 32;       // tokens per attention chunk (f32)
+constexpr int kMaxSplit = 16;             // attention splits per head
+constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to this count
+constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
+constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
+constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
+constexpr int kCoverThreads = 256;
+constexpr int kCoarseRegKeys = 4096;     // coarse Top-K held in registers up to this many keys
+constexpr int kRefineRegKeys = 5120;     // refinement Top-K held in registers up to this many candidates
+constexpr int kRefineRegMaxPerThread = 40;
+constexpr int kRegTopKMin = 2048;         // below this many keys the LDS-resident Top-K is faster
 
 struct PyramidLaunch {
   const void* k;
@@ -33,12 +38,19 @@ struct SelectPlan {
   int budgets[kMaxLevels + 1];  // k_L .. k_0
   int k_top, k0, sum_k;
   int64_t covered;              // k_L 2^L
-  int64_t cov_len;              // floats per head over levels 0..L-1
+  int64_t cov_len;              // floats per head over levels 0..L-1 (each level 16-byte aligned)
   int64_t cov_off[kMaxLevels];  // float offset of level j inside a head's slice
-  int n_att, n_chunks, n_split, chunks_per_split;
-  int refine_lds;               // dynamic LDS bytes of the refine kernel
+  // attention
+  int n_att, chunk, n_chunks, n_split, chunks_per_split;
+  // LDS plans (bytes)
+  int cover_lds;                // kept coarse regions (+ coarse keys when staged)
+  int coarse_keys_in_lds;
+  int refine_nmax, refine_kmax; // candidate / kept capacity (words, multiples of 4)
+  int refine_cov_in_lds;        // coverage scores staged in LDS
+  int att_t_words;              // words of the attended-set list (T) region
+  int attend_lds;               // T list + max(refinement state, K/V chunk buffers)
   // workspace sections (byte offsets)
-  uint64_t off_counters, off_keys, off_sel_top, off_cov, off_sel0, off_part_ml, off_part_o, total;
+  uint64_t off_keys, off_sel_top, off_cov, off_part_ml, off_part_o, total;
 };
 
 struct SelectLaunch {
@@ -57,5 +69,20 @@ struct SelectLaunch {
 
 hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s);
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
+
+// Tokens per attention chunk: 8 16-byte K and V vectors per thread and
+// chunk for bfloat16 (32 tokens per query tile, up to 128), 32 for float32.
+constexpr int attend_chunk(int dtype, int nqt) {
+  return dtype == WF_BF16 ? (nqt >= 3 ? 128 : 32 * nqt) : kAttendChunkF32;
+}
+
+// LDS bytes of the attention chunk buffers (K rows, transposed V).
+inline int attend_buffer_bytes(int dtype, int head_dim, int nqt) {
+  const bool bf = dtype == WF_BF16;
+  const int es = bf ? 2 : 4;
+  const int ch = attend_chunk(dtype, nqt);
+  const int kpad = bf ? 8 : 4, vpad = 4;
+  return ch * (head_dim + kpad) * es + head_dim * (ch + vpad) * es;
+}
 
 }  // namespace wf

@@ -1,0 +1,167 @@
+// WaveFilter pyramid kernels for gfx950 (MI355X), run once per cache refresh:
+//   pyramid_top_kernel    A_L of the prompt keys in one streaming pass
+//   pyramid_level_kernel  one analysis level, for the all-levels inspection mode
+//
+// Citations are to WaveFilter (arXiv 2606.00724).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "wf_device.h"
+#include "wf_internal.h"
+
+namespace wf {
+
+// ===========================================================================
+// Pyramid: A_L[n] = 2^{-L/2} sum_{t in [n 2^L, (n+1) 2^L)} k_t
+// (section 2.2, eq. 5 iterated L times with orthonormal Haar filters: the
+// pairwise sums telescope into one block sum).  One wave owns a run of
+// rows_per_item consecutive prompt rows; lane (r, col) streams 16-byte
+// vectors of rows r, r + RPP, ... at column block col, so each wave-wide
+// load reads 1 KiB of contiguous memory.  The keys are read once, so the
+// loads are non-temporal (they do not displace reusable cache lines; this
+// streams measurably faster).  Row groups of one block are reduced with
+// cross-lane shuffles.
+// ===========================================================================
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void add(const float* p, float* acc) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
+  }
+};
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void add(const bf16_t* p, float* acc) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += bf16_to_f32(x[i] & 0xFFFFu);
+      acc[2 * i + 1] += bf16_to_f32(x[i] >> 16);
+    }
+  }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pyramid_top_kernel(const T* __restrict__ k, int64_t head_stride,
+                                                          int heads_total, int n_prompt, int levels,
+                                                          int rows_per_item, int64_t items_per_head,
+                                                          float scale, float* __restrict__ a_top) {
+  constexpr int VE = Vec16<T>::N;
+  constexpr int V = D / VE;     // vectors per row
+  constexpr int RPP = 64 / V;   // rows per wave pass
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= items_per_head * heads_total) return;
+  const int64_t head = item / items_per_head;
+  const int64_t it = item - head * items_per_head;
+  const int col = lane % V, r = lane / V;
+  const int64_t row0 = it * rows_per_item + r;
+  const T* src = k + head * head_stride + row0 * D + col * VE;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  const int passes = rows_per_item / RPP;
+  if (row0 + (int64_t)(passes - 1) * RPP < n_prompt) {
+#pragma unroll 8
+    for (int p = 0; p < passes; ++p) Vec16<T>::add(src + (int64_t)p * RPP * D, acc);
+  } else {
+    for (int p = 0; p < passes; ++p)
+      if (row0 + (int64_t)p * RPP < n_prompt) Vec16<T>::add(src + (int64_t)p * RPP * D, acc);
+  }
+  const int block_rows = 1 << levels;
+  const int G = block_rows < RPP ? block_rows : RPP;  // row groups per block inside one pass
+  for (int o = V; o < V * G; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+  if ((r & (G - 1)) == 0 && row0 < n_prompt) {
+    const int n_top = n_prompt >> levels;
+    const int64_t out_row = head * n_top + (row0 >> levels);
+    float* dst = a_top + out_row * D + col * VE;
+#pragma unroll
+    for (int e = 0; e < VE; e += 4)
+      *reinterpret_cast<float4*>(dst + e) =
+          make_float4(acc[e] * scale, acc[e + 1] * scale, acc[e + 2] * scale, acc[e + 3] * scale);
+  }
+}
+
+// One analysis level (section 2.2, eq. 5): A_j[n] = (x[2n] + x[2n+1])/sqrt2,
+// D_j[n] = (x[2n] - x[2n+1])/sqrt2, with x = A_{j-1} (x = keys for j = 1).
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p);
+template <> __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void pyramid_level_kernel(const T* __restrict__ src, int64_t src_head_stride,
+                                                            int heads_total, int n_out, int d,
+                                                            float* __restrict__ a_out, float* __restrict__ d_out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_head = (int64_t)n_out * d;
+  if (idx >= per_head * heads_total) return;
+  const int64_t head = idx / per_head;
+  const int64_t rem = idx - head * per_head;
+  const int64_t n = rem / d, c = rem - n * d;
+  const T* base = src + head * src_head_stride;
+  const float x0 = load_elem<T>(base + (2 * n) * d + c);
+  const float x1 = load_elem<T>(base + (2 * n + 1) * d + c);
+  const float inv_sqrt2 = 0.70710678118654752440f;
+  a_out[idx] = (x0 + x1) * inv_sqrt2;
+  d_out[idx] = (x0 - x1) * inv_sqrt2;
+}
+
+hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
+  const int L = a.levels;
+  uint8_t* base = reinterpret_cast<uint8_t*>(a.base);
+  if (a.flags & WF_PYR_ALL_LEVELS) {
+    // level by level, each level reading the previous one
+    for (int j = 1; j <= L; ++j) {
+      const int n_out = a.n_prompt >> j;
+      const int64_t total = (int64_t)n_out * a.head_dim * a.heads_total;
+      const unsigned grid = (unsigned)((total + 255) / 256);
+      float* a_out = reinterpret_cast<float*>(base + a.band_off_a[j]);
+      float* d_out = reinterpret_cast<float*>(base + a.band_off_d[j]);
+      if (j == 1) {
+        if (a.dtype == WF_BF16)
+          hipLaunchKernelGGL(pyramid_level_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+                             reinterpret_cast<const bf16_t*>(a.k), a.head_stride, a.heads_total, n_out,
+                             a.head_dim, a_out, d_out);
+        else
+          hipLaunchKernelGGL(pyramid_level_kernel<float>, dim3(grid), dim3(256), 0, s,
+                             reinterpret_cast<const float*>(a.k), a.head_stride, a.heads_total, n_out,
+                             a.head_dim, a_out, d_out);
+      } else {
+        const float* prev = reinterpret_cast<const float*>(base + a.band_off_a[j - 1]);
+        hipLaunchKernelGGL(pyramid_level_kernel<float>, dim3(grid), dim3(256), 0, s, prev,
+                           (int64_t)(a.n_prompt >> (j - 1)) * a.head_dim, a.heads_total, n_out,
+                           a.head_dim, a_out, d_out);
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (L > 0) return hipSuccess;
+    // L == 0: A_0 is the keys themselves, converted below by the streaming kernel
+  }
+  const int vec_elems = (a.dtype == WF_BF16) ? 8 : 4;
+  const int rpp = 64 / (a.head_dim / vec_elems);
+  const int rows_per_item = (1 << L) > rpp ? (1 << L) : rpp;
+  const int64_t items_per_head = (a.n_prompt + rows_per_item - 1) / rows_per_item;
+  const int64_t items = items_per_head * a.heads_total;
+  const unsigned grid = (unsigned)((items + 3) / 4);
+  const float scale = (float)ldexp(1.0, -L / 2) * ((L & 1) ? 0.70710678118654752440f : 1.0f);
+#define WF_PYR(T, D)                                                                                   \
+  hipLaunchKernelGGL((pyramid_top_kernel<T, D>), dim3(grid), dim3(256), 0, s,                         \
+                     reinterpret_cast<const T*>(a.k), a.head_stride, a.heads_total, a.n_prompt, L,    \
+                     rows_per_item, items_per_head, scale, a.base)
+  if (a.dtype == WF_BF16) {
+    if (a.head_dim == 128) WF_PYR(bf16_t, 128); else WF_PYR(bf16_t, 64);
+  } else {
+    if (a.head_dim == 128) WF_PYR(float, 128); else WF_PYR(float, 64);
+  }
+#undef WF_PYR
+  return hipGetLastError();
+}
+
+}  // namespace wf

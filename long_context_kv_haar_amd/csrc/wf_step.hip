@@ -1,0 +1,794 @@
+// WaveFilter per-denoising-step kernels for gfx950 (MI355X).
+//
+//   coarse_kernel   s_L[n] = max_i q_i . A_L[n] / sqrt(d) on MFMA (Figure 2 (c))
+//   cover_kernel    the coarse Top-K (recomputed by every workgroup of the
+//                   head, so no cross-workgroup handoff is needed), then
+//                   q_i . k_t for every token the kept regions cover, on MFMA,
+//                   summed in registers into the scores of all their
+//                   sub-regions at levels 0 .. L-1 (Figure 2 (d), with A_j
+//                   taken by linearity from the token dot products)
+//   attend_kernel   the recursive refinement (again recomputed by every
+//                   workgroup of the head, from LDS), then split-K
+//                   online-softmax attention over the kept prompt tokens plus
+//                   the generated positions (eq. 3 restricted to that set)
+//   combine_kernel  log-sum-exp merge of the split partial results
+//
+// Citations are to WaveFilter (arXiv 2606.00724).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "wf_device.h"
+#include "wf_internal.h"
+
+namespace wf {
+
+struct StepArgs {
+  const void* q;
+  const float* a_top;
+  const void* k;
+  const void* v;
+  const int32_t* gen_idx;
+  float* out;
+  int32_t* sel_out;
+  int32_t* sel_levels;
+  float* score_levels;
+  uint32_t* keys_top;    // [heads_total][n_top]
+  int32_t* sel_top;      // [heads_total][k_top]
+  float* cov;            // [heads_total][cov_len]
+  float* part_ml;        // [heads_total][n_split][2][n_q]
+  float* part_o;         // [heads_total][n_split][n_q][d]
+  int n_q, n_top, n_prompt, n_tot, n_gen, levels;
+  int k_top, k0, sum_k;
+  int64_t covered, cov_len;
+  int64_t cov_off[kMaxLevels];
+  int budgets[kMaxLevels + 1];
+  int n_att, n_chunks, n_split, chunks_per_split;
+  int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, att_t_words;
+  float inv_sqrt_d;
+};
+
+// Max across the 16 lanes of a row; every lane of the row ends with it.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  return x;
+}
+
+// Query fragments as the B operand: lane (l16, g) supplies query row
+// 16 qt + l16, quarter g of the head dimension; zero beyond n_q.
+template <typename T, int D, int RT>
+__device__ __forceinline__ void load_query_frags(const T* qh, int n_q, int l16, int g, Frag<T, D> (&qf)[RT]) {
+#pragma unroll
+  for (int qt = 0; qt < RT; ++qt) {
+    const int row = 16 * qt + l16;
+    if (row < n_q) qf[qt].load(qh + (int64_t)row * D, g);
+    else qf[qt].zero();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Coarse scores.  Wave w of block x scores level-L regions
+// n = 64 x + 16 w + [0, 16): tile = A_L rows (A operand) x Q^T (B operand),
+// so lane (query 16 qt + l16, g) holds regions 16 w + 4 g + r.  For bfloat16
+// inputs the float32 coefficients are split into bf16 hi + lo parts, both
+// multiplied exactly, accumulated in float32.  Max over queries: in registers
+// over qt, then across the 16 lanes of a row.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
+  const int head = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
+  Frag<T, D> qf[RT];
+  load_query_frags<T, D, RT>(qh, a.n_q, l16, g, qf);
+
+  const int n = blockIdx.x * 64 + w * 16 + l16;  // region supplied by this lane (A operand)
+  const bool valid = n < a.n_top;
+  const float* arow = a.a_top + ((int64_t)head * a.n_top + (valid ? n : 0)) * D;
+  f32x4 acc[RT];
+#pragma unroll
+  for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+    constexpr int STEPS = D / 32;
+    const float4* p = reinterpret_cast<const float4*>(arow + g * (D / 4));
+    float4 x[2 * STEPS];
+#pragma unroll
+    for (int i = 0; i < 2 * STEPS; ++i) x[i] = valid ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float xs[4] = {x[2 * s + h].x, x[2 * s + h].y, x[2 * s + h].z, x[2 * s + h].w};
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hb[e] = f32_to_bf16(xs[e]);
+          lb[e] = f32_to_bf16(xs[e] - bf16_to_f32(hb[e]));
+        }
+        hi[2 * h] = pack_bf16(hb[0], hb[1]);
+        hi[2 * h + 1] = pack_bf16(hb[2], hb[3]);
+        lo[2 * h] = pack_bf16(lb[0], lb[1]);
+        lo[2 * h + 1] = pack_bf16(lb[2], lb[3]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) {
+        acc[qt] = mma_bf16(hi, qf[qt].v[s], acc[qt]);
+        acc[qt] = mma_bf16(lo, qf[qt].v[s], acc[qt]);
+      }
+    }
+  } else {
+    Frag<float, D> b;
+    if (valid) b.load(arow, g); else b.zero();
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(b, qf[qt], acc[qt]);
+  }
+  float m[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt)
+      if (16 * qt + l16 < a.n_q) x = fmaxf(x, acc[qt][r]);
+    m[r] = row_max16(x);
+  }
+  uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
+  const int n0 = blockIdx.x * 64 + w * 16 + 4 * g;  // first region of this row
+  if (l16 == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n0 + r < a.n_top) keys[n0 + r] = order_key(m[r] * a.inv_sqrt_d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cover: coarse Top-K, then coverage scores.
+//
+// The kept coarse regions, ascending, cover positions p = 0 .. k_L 2^L - 1;
+// position p is token sel_L[p >> L] 2^L + (p mod 2^L).  Wave w of block x
+// owns positions 256 x + 64 w + [0, 64) as four 16-token tiles t; tile = K
+// rows (A operand) x Q^T (B operand), so lane (query 16 qt + l16, g) holds
+// S[query][tokens 16 t + 4 g + r].  Sums along the token axis: levels 1 and
+// 2 in-lane (r), levels 3 and 4 across lane groups g (xor 16, xor 32),
+// levels 5 and 6 across tiles in registers.  The score of a block is the max
+// over queries: over qt in registers, then across the 16 lanes of a row.
+// Scores are written per level at the block's position p >> j.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
+  constexpr int NT = kCoverThreads;
+  extern __shared__ uint32_t lds[];
+  __shared__ TopKFastShared<NT> sh;
+  const int head = blockIdx.y;
+  const int L = a.levels;
+  int* sel_l = reinterpret_cast<int*>(lds);  // k_top kept regions, ascending
+  uint32_t* keys_l = lds + ((a.k_top + 3) & ~3);
+  const uint32_t* keys_g = a.keys_top + (int64_t)head * a.n_top;
+
+  // -- coarse Top-K of this head (every workgroup of the head computes the same set)
+  const bool first = blockIdx.x == 0;
+  int32_t* dbg_sel = (first && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = (first && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+  auto emit = [&](int o, int i) {
+    if (o < a.k_top) {
+      sel_l[o] = i;
+      if (first) sel_g[o] = i;
+      if (dbg_sel) dbg_sel[o] = i;
+      if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
+    }
+  };
+  if (a.coarse_keys_in_lds) {
+    for (int i = threadIdx.x; i < a.n_top; i += NT) keys_l[i] = keys_g[i];
+    __syncthreads();
+    topk_fast<NT>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, sh, emit);
+  } else {
+    topk_fast<NT>([&](int i) { return keys_g[i]; }, a.n_top, a.k_top, sh, emit);
+  }
+  __syncthreads();
+  if (L == 0) return;  // no finer level to score
+
+  // -- coverage scores
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t wave_base = (int64_t)blockIdx.x * 256 + w * 64;
+  if (wave_base >= a.covered) return;  // no workgroup barrier below
+  const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
+  Frag<T, D> qf[RT];
+  load_query_frags<T, D, RT>(qh, a.n_q, l16, g, qf);
+
+  const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
+  Frag<T, D> kf[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    int64_t p = wave_base + 16 * t + l16;
+    p = p < a.covered ? p : a.covered - 1;  // past the end: any covered row, never written out
+    const int r = clampi(sel_l[p >> L], 0, a.n_top - 1);
+    const int64_t tok = ((int64_t)r << L) + (p & ((1 << L) - 1));
+    kf[t].load(kh + tok * D, g);
+  }
+  f32x4 s[4][RT];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt) s[t][qt] = mma_tile<D>(kf[t], qf[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+  // rows of absent queries never win a max
+#pragma unroll
+  for (int qt = 0; qt < RT; ++qt)
+    if (16 * qt + l16 >= a.n_q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s[t][qt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+
+  float* cov = a.cov + (int64_t)head * a.cov_len;
+  const int jmax = L < 7 ? L : 7;  // levels 0 .. jmax-1 are scored here
+  const float isd = a.inv_sqrt_d;
+  const bool writer = (l16 == 0);
+  const int64_t tb = wave_base + 4 * g;  // first position of this row in tile 0
+  // level 0
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float m[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = s[t][0][r];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][r]);
+      m[r] = row_max16(x) * isd;
+    }
+    const int64_t p = tb + 16 * t;
+    if (writer && p < a.covered)
+      *reinterpret_cast<float4*>(cov + a.cov_off[0] + p) = make_float4(m[0], m[1], m[2], m[3]);
+  }
+  if (jmax <= 1) return;
+  // level 1: token pairs (r = 0,1 and 2,3), in place into s[t][qt][0] and [2]
+  {
+    const float sc = isd * 0.70710678118654752440f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) {
+        s[t][qt][0] += s[t][qt][1];
+        s[t][qt][2] += s[t][qt][3];
+      }
+      float m[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float x = s[t][0][2 * h];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][2 * h]);
+        m[h] = row_max16(x) * sc;
+      }
+      const int64_t p = tb + 16 * t;
+      if (writer && p < a.covered)
+        *reinterpret_cast<float2*>(cov + a.cov_off[1] + (p >> 1)) = make_float2(m[0], m[1]);
+    }
+  }
+  if (jmax <= 2) return;
+  // level 2: 4-token blocks (one per lane group), into s[t][qt][0]
+  {
+    const float sc = isd * 0.5f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += s[t][qt][2];
+      float x = s[t][0][0];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+      x = row_max16(x) * sc;
+      const int64_t p = tb + 16 * t;
+      if (writer && p < a.covered) cov[a.cov_off[2] + (p >> 2)] = x;
+    }
+  }
+  if (jmax <= 3) return;
+  // level 3: 8-token blocks = lane groups {0,1} and {2,3}
+  {
+    const float sc = isd * 0.35355339059327376220f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += __shfl_xor(s[t][qt][0], 16, 64);
+      float x = s[t][0][0];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+      x = row_max16(x) * sc;
+      const int64_t p = tb + 16 * t;
+      if (writer && (g & 1) == 0 && p < a.covered) cov[a.cov_off[3] + (p >> 3)] = x;
+    }
+  }
+  if (jmax <= 4) return;
+  // level 4: 16-token blocks = whole tiles
+  {
+    const float sc = isd * 0.25f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += __shfl_xor(s[t][qt][0], 32, 64);
+      float x = s[t][0][0];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+      x = row_max16(x) * sc;
+      const int64_t p = wave_base + 16 * t;
+      if (writer && g == 0 && p < a.covered) cov[a.cov_off[4] + (p >> 4)] = x;
+    }
+  }
+  if (jmax <= 5) return;
+  // level 5: tile pairs; level 6: the whole wave
+  {
+    float x01 = -INFINITY, x23 = -INFINITY, xall = -INFINITY;
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt) {
+      const float a01 = s[0][qt][0] + s[1][qt][0];
+      const float a23 = s[2][qt][0] + s[3][qt][0];
+      x01 = fmaxf(x01, a01);
+      x23 = fmaxf(x23, a23);
+      xall = fmaxf(xall, a01 + a23);
+    }
+    x01 = row_max16(x01) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
+    x23 = row_max16(x23) * (isd * 0.17677669529663688110f);
+    xall = row_max16(xall) * (isd * 0.125f);                 // 2^{-3}
+    if (lane == 0) {
+      if (wave_base < a.covered) cov[a.cov_off[5] + (wave_base >> 5)] = x01;
+      if (wave_base + 32 < a.covered) cov[a.cov_off[5] + (wave_base >> 5) + 1] = x23;
+      if (jmax > 6) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Recursive refinement (Figure 2 (d)) for one head, by one workgroup.
+// Positions at level j index the level-j blocks inside the covered set,
+// ascending; the block at position p has children 2p and 2p+1 and global
+// index sel_L[p >> (L-j)] 2^{L-j} + (p mod 2^{L-j}).  State lives in LDS:
+// keys[nmax] | cur[kmax] | nxt[kmax] | (coverage scores, when they fit).
+// Writes the kept tokens (ascending) to tsel[0 .. k0).  With `report`, also
+// writes sel_out and the per-level outputs of levels L-1 .. 0.
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ void refine_head(const StepArgs& a, int head, uint32_t* lds, TopKFastShared<NT>& sh, int* tsel,
+                            bool report) {
+  const int L = a.levels;
+  uint32_t* keys = lds;
+  int* cur = reinterpret_cast<int*>(lds + a.refine_nmax);
+  int* nxt = cur + a.refine_kmax;
+  float* cov_l = reinterpret_cast<float*>(nxt + a.refine_kmax);
+  const int32_t* sel_top = a.sel_top + (int64_t)head * a.k_top;
+  const float* cov_g = a.cov + (int64_t)head * a.cov_len;
+  const float* cov = a.refine_cov_in_lds ? cov_l : cov_g;
+  if (a.refine_cov_in_lds) {
+    const float4* src = reinterpret_cast<const float4*>(cov_g);
+    float4* dst = reinterpret_cast<float4*>(cov_l);
+    const int n4 = (int)(a.cov_len / 4);
+    for (int i = threadIdx.x; i < n4; i += NT) dst[i] = src[i];
+  }
+  int32_t* dbg_sel = (report && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = (report && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  for (int i = threadIdx.x; i < a.k_top; i += NT) cur[i] = i;
+  __syncthreads();
+  int kprev = a.k_top, dbg_off = a.k_top;
+  for (int j = L - 1; j >= 0; --j) {
+    const int kj = a.budgets[L - j];
+    const int n = 2 * kprev;
+    const int nj = (int)(a.covered >> j);  // level-j positions in the covered set
+    const float* cj = cov + a.cov_off[j];
+    for (int c = threadIdx.x; c < n; c += NT) keys[c] = order_key(cj[clampi(2 * cur[c >> 1] + (c & 1), 0, nj - 1)]);
+    __syncthreads();
+    topk_fast<NT>([&](int i) { return keys[i]; }, n, kj, sh, [&](int o, int i) {
+      if (o < kj) nxt[o] = clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1);
+    });
+    __syncthreads();
+    if (dbg_sel || dbg_score) {
+      const int sh_l = L - j;
+      for (int o = threadIdx.x; o < kj; o += NT) {
+        const int p = nxt[o];
+        if (dbg_sel)
+          dbg_sel[dbg_off + o] =
+              (clampi(sel_top[clampi(p >> sh_l, 0, a.k_top - 1)], 0, a.n_top - 1) << sh_l) + (p & ((1 << sh_l) - 1));
+        if (dbg_score) dbg_score[dbg_off + o] = cj[p];
+      }
+    }
+    int* tmp = cur;
+    cur = nxt;
+    nxt = tmp;
+    kprev = kj;
+    dbg_off += kj;
+  }
+  int32_t* so = (report && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  for (int o = threadIdx.x; o < a.k0; o += NT) {
+    const int p = cur[o];
+    const int tok = (clampi(sel_top[clampi(p >> L, 0, a.k_top - 1)], 0, a.n_top - 1) << L) + (p & ((1 << L) - 1));
+    tsel[o] = tok;
+    if (so) so[o] = tok;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Sparse attention (eq. 3 over T = kept prompt tokens, then gen_idx).
+// Workgroup (split, head) first runs the refinement, leaving T in LDS, then
+// walks chunks of CH tokens; wave w owns query tile w.  Per chunk: K rows ->
+// LDS (row-major, padded), V rows -> LDS transposed; S^T = K Q^T on MFMA
+// (lane (query l16, g) holds tokens 16 t + 4 g + r); online softmax per
+// query row in float32; O^T += V^T P^T on MFMA with P split into bf16 hi + lo
+// (float32 MFMA for float32 inputs).  The next chunk's rows are fetched into
+// registers while the current one computes.  Writes the split's partial
+// (m, l, O) to the workspace.
+// ---------------------------------------------------------------------------
+template <typename T> struct AttendTraits;
+template <> struct AttendTraits<bf16_t> { static constexpr int KPAD = 8, VPAD = 4, DT = WF_BF16; };
+template <> struct AttendTraits<float> { static constexpr int KPAD = 4, VPAD = 4, DT = WF_F32; };
+
+template <typename T, int D, int NQT>
+__global__ __launch_bounds__(64 * NQT) void attend_kernel(StepArgs a) {
+  constexpr int NT = 64 * NQT;
+  constexpr int CH = attend_chunk(AttendTraits<T>::DT, NQT);
+  constexpr int KS = D + AttendTraits<T>::KPAD;   // Ks row stride (elements)
+  constexpr int VS = CH + AttendTraits<T>::VPAD;  // Vt row stride (elements)
+  constexpr int VE = 16 / sizeof(T);              // elements per 16-byte vector
+  constexpr int NV = D / VE;                      // vectors per row
+  constexpr int PER = (CH * NV + NT - 1) / NT;    // vectors per thread per tensor
+  extern __shared__ uint32_t lds[];
+  __shared__ TopKFastShared<NT> sh;
+  int* tlist = reinterpret_cast<int*>(lds);        // T: kept prompt tokens, then gen_idx
+  uint32_t* scratch = lds + a.att_t_words;         // refinement state, then K/V buffers
+  T* Ks = reinterpret_cast<T*>(scratch);
+  T* Vt = Ks + CH * KS;
+
+  const int head = blockIdx.y, split = blockIdx.x;
+  refine_head<NT>(a, head, scratch, sh, tlist, split == 0);
+  for (int i = threadIdx.x; i < a.n_gen; i += NT) tlist[a.k0 + i] = clampi(a.gen_idx[i], 0, a.n_tot - 1);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int query = 16 * w + l16;
+  const bool qvalid = query < a.n_q;
+  const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
+  const T* vh = reinterpret_cast<const T*>(a.v) + (int64_t)head * a.n_tot * D;
+
+  Frag<T, D> qf;
+  const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
+  if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
+
+  const float sl2 = a.inv_sqrt_d * 1.44269504088896340736f;  // log2(e)/sqrt(d)
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int c_begin = split * a.chunks_per_split;
+  const int c_end = min(a.n_chunks, c_begin + a.chunks_per_split);
+
+  // K: vector e = (row, cv) of the chunk, row-major.  V (bfloat16): lane
+  // handles the token pair (2 p, 2 p + 1) at column block cv, so that each
+  // transposed LDS store writes one 32-bit word (two tokens) and a wave's
+  // store covers 64 consecutive words of one V^T row: no bank conflicts.
+  constexpr int NPAIR = CH / 2;                  // token pairs per chunk
+  constexpr int VPER = (NPAIR * NV + NT - 1) / NT;  // (pair, cv) items per thread
+  u32x4 kreg[PER], vreg[sizeof(T) == 2 ? 2 * VPER : PER];
+  auto fetch = [&](int chunk) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * NT;
+      const int row = e / NV, cv = e - row * NV;
+      const int pos = chunk * CH + row;
+      kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (e < CH * NV && pos < a.n_att) {
+        const int64_t tok = tlist[pos];
+        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + tok * D + cv * VE));
+      }
+      if constexpr (sizeof(T) != 2) {
+        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+        if (e < CH * NV && pos < a.n_att) {
+          const int64_t tok = tlist[pos];
+          vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE));
+        }
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < VPER; ++i) {
+        const int e = threadIdx.x + i * NT;  // e = cv * NPAIR + pair: lanes walk pairs
+        const int cv = e / NPAIR, pr = e - cv * NPAIR;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pos = chunk * CH + 2 * pr + h;
+          vreg[2 * i + h] = u32x4{0u, 0u, 0u, 0u};
+          if (e < NPAIR * NV && pos < a.n_att) {
+            const int64_t tok = tlist[pos];
+            vreg[2 * i + h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE));
+          }
+        }
+      }
+    }
+  };
+  if (c_begin < c_end) fetch(c_begin);
+  for (int chunk = c_begin; chunk < c_end; ++chunk) {
+    const int pos0 = chunk * CH;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * NT;
+      if (e < CH * NV) {
+        const int row = e / NV, cv = e - row * NV;
+        *reinterpret_cast<u32x4*>(Ks + row * KS + cv * VE) = kreg[i];
+        if constexpr (sizeof(T) != 2) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) Vt[(cv * VE + c) * VS + row] = __uint_as_float(vreg[i][c]);
+        }
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < VPER; ++i) {
+        const int e = threadIdx.x + i * NT;
+        if (e < NPAIR * NV) {
+          const int cv = e / NPAIR, pr = e - cv * NPAIR;
+          uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + (cv * VE) * VS + 2 * pr);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {  // elements 2c, 2c+1 of the 8-wide column block
+            const uint32_t a0 = vreg[2 * i][c], a1 = vreg[2 * i + 1][c];
+            dst[(2 * c) * (VS / 2)] = (a0 & 0xFFFFu) | (a1 << 16);
+            dst[(2 * c + 1) * (VS / 2)] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (chunk + 1 < c_end) fetch(chunk + 1);  // overlaps with the math below
+
+    f32x4 sv[CH / 16];
+#pragma unroll
+    for (int t = 0; t < CH / 16; ++t) {
+      Frag<T, D> kf;
+      kf.load(Ks + (16 * t + l16) * KS, g);
+      sv[t] = mma_tile<D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < CH / 16; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = pos0 + 16 * t + 4 * g + r;
+        const float x = (pos < a.n_att) ? sv[t][r] * sl2 : -INFINITY;
+        sv[t][r] = x;
+        cmax = fmaxf(cmax, x);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m, cmax);
+    const float alpha = exp2f(m - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < CH / 16; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2f(sv[t][r] - m_new);
+        sv[t][r] = p;
+        psum += p;
+      }
+    lsum = lsum * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int st = 0; st < CH / 32; ++st) {
+        u32x4 ph, pl;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = sv[2 * st + hh][r];
+            hb[r] = f32_to_bf16(p);
+            lb[r] = f32_to_bf16(p - bf16_to_f32(hb[r]));
+          }
+          ph[2 * hh] = pack_bf16(hb[0], hb[1]);
+          ph[2 * hh + 1] = pack_bf16(hb[2], hb[3]);
+          pl[2 * hh] = pack_bf16(lb[0], lb[1]);
+          pl[2 * hh + 1] = pack_bf16(lb[2], lb[3]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const T* vr = Vt + (16 * dt + l16) * VS + 32 * st + 4 * g;
+          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
+          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
+          const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
+          o[dt] = mma_bf16(vf, ph, o[dt]);
+          o[dt] = mma_bf16(vf, pl, o[dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < CH / 16; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const float vf = Vt[(16 * dt + l16) * VS + 16 * t + 4 * g + r];
+            o[dt] = mma_f32(vf, sv[t][r], o[dt]);
+          }
+    }
+    __syncthreads();
+  }
+
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  float* pml = a.part_ml + ((int64_t)head * a.n_split + split) * 2 * a.n_q;
+  float* po = a.part_o + ((int64_t)head * a.n_split + split) * a.n_q * D;
+  if (qvalid) {
+    if (g == 0) {
+      pml[query] = m;
+      pml[a.n_q + query] = lsum;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<float4*>(po + (int64_t)query * D + 16 * dt + 4 * g) =
+          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the split partials: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s,
+// M = max_s m_s (m in log2 units).  Block (x, head) merges 16 query rows.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
+  constexpr int FPT = (16 * D / 4 + 255) / 256;  // float4 outputs per thread
+  __shared__ float wgt[16][kMaxSplit];
+  const int head = blockIdx.y;
+  const int q0 = blockIdx.x * 16;
+  const int nq = min(16, a.n_q - q0);
+  const int ns = a.n_split;
+  const float* ml = a.part_ml + (int64_t)head * ns * 2 * a.n_q;
+  if (threadIdx.x < nq) {
+    const int qi = q0 + threadIdx.x;
+    float mv[kMaxSplit], lv[kMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {  // every load issued before any is used
+      mv[sp] = sp < ns ? ml[sp * 2 * a.n_q + qi] : -INFINITY;
+      lv[sp] = sp < ns ? ml[sp * 2 * a.n_q + a.n_q + qi] : 0.f;
+    }
+    float mm = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
+    float den = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      mv[sp] = sp < ns ? exp2f(mv[sp] - mm) : 0.f;
+      den += mv[sp] * lv[sp];
+    }
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) wgt[threadIdx.x][sp] = mv[sp] * inv;
+  }
+  const float* pob = a.part_o + (int64_t)head * ns * a.n_q * D;
+  float4 x[FPT][kMaxSplit];
+#pragma unroll
+  for (int f = 0; f < FPT; ++f) {
+    const int e = threadIdx.x + f * 256;
+    const int ql = e / (D / 4), c4 = e - ql * (D / 4);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp)
+      x[f][sp] = (sp < ns && ql < nq)
+                     ? *reinterpret_cast<const float4*>(pob + ((int64_t)sp * a.n_q + q0 + ql) * D + 4 * c4)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  float* outh = a.out + (int64_t)head * a.n_q * D;
+#pragma unroll
+  for (int f = 0; f < FPT; ++f) {
+    const int e = threadIdx.x + f * 256;
+    const int ql = e / (D / 4), c4 = e - ql * (D / 4);
+    if (ql >= nq) continue;
+    float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      const float wv = sp < ns ? wgt[ql][sp] : 0.f;
+      acc4.x += wv * x[f][sp].x;
+      acc4.y += wv * x[f][sp].y;
+      acc4.z += wv * x[f][sp].z;
+      acc4.w += wv * x[f][sp].w;
+    }
+    *reinterpret_cast<float4*>(outh + (int64_t)(q0 + ql) * D + 4 * c4) = acc4;
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <class K>
+static hipError_t allow_lds(K kernel, int bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             bytes);
+}
+
+hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
+  const SelectPlan& P = L.plan;
+  StepArgs a;
+  a.q = L.q;
+  a.a_top = L.a_top;
+  a.k = L.k;
+  a.v = L.v;
+  a.gen_idx = L.gen_idx;
+  a.out = L.out;
+  a.sel_out = L.sel_out;
+  a.sel_levels = L.sel_levels;
+  a.score_levels = L.score_levels;
+  a.keys_top = reinterpret_cast<uint32_t*>(L.ws + P.off_keys);
+  a.sel_top = reinterpret_cast<int32_t*>(L.ws + P.off_sel_top);
+  a.cov = reinterpret_cast<float*>(L.ws + P.off_cov);
+  a.part_ml = reinterpret_cast<float*>(L.ws + P.off_part_ml);
+  a.part_o = reinterpret_cast<float*>(L.ws + P.off_part_o);
+  a.n_q = P.n_q;
+  a.n_top = P.n_top;
+  a.n_prompt = P.n_prompt;
+  a.n_tot = P.n_tot;
+  a.n_gen = P.n_gen;
+  a.levels = P.levels;
+  a.k_top = P.k_top;
+  a.k0 = P.k0;
+  a.sum_k = P.sum_k;
+  a.covered = P.covered;
+  a.cov_len = P.cov_len;
+  for (int j = 0; j < kMaxLevels; ++j) a.cov_off[j] = P.cov_off[j];
+  for (int j = 0; j <= kMaxLevels; ++j) a.budgets[j] = P.budgets[j];
+  a.n_att = P.n_att;
+  a.n_chunks = P.n_chunks;
+  a.n_split = P.n_split;
+  a.chunks_per_split = P.chunks_per_split;
+  a.coarse_keys_in_lds = P.coarse_keys_in_lds;
+  a.refine_cov_in_lds = P.refine_cov_in_lds;
+  a.refine_nmax = P.refine_nmax;
+  a.refine_kmax = P.refine_kmax;
+  a.att_t_words = P.att_t_words;
+  a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
+
+  const int H = P.heads_total;
+  const int rt = (P.n_q + 15) / 16;
+  const bool bf = P.dtype == WF_BF16;
+  const bool d128 = P.head_dim == 128;
+  hipError_t e;
+
+#define WF_RT_SWITCH(MACRO, ...)                  \
+  switch (rt) {                                   \
+    case 1: MACRO(1, __VA_ARGS__); break;         \
+    case 2: MACRO(2, __VA_ARGS__); break;         \
+    case 3: MACRO(3, __VA_ARGS__); break;         \
+    default: MACRO(4, __VA_ARGS__); break;        \
+  }
+#define WF_LAUNCH(RTV, KERNEL, GRID, BLOCK, LDS)                                                           \
+  do {                                                                                                     \
+    if (bf && d128) {                                                                                      \
+      if ((e = allow_lds(KERNEL<bf16_t, 128, RTV>, LDS)) != hipSuccess) return e;                          \
+      hipLaunchKernelGGL((KERNEL<bf16_t, 128, RTV>), GRID, BLOCK, LDS, s, a);                              \
+    } else if (bf) {                                                                                       \
+      if ((e = allow_lds(KERNEL<bf16_t, 64, RTV>, LDS)) != hipSuccess) return e;                           \
+      hipLaunchKernelGGL((KERNEL<bf16_t, 64, RTV>), GRID, BLOCK, LDS, s, a);                               \
+    } else if (d128) {                                                                                     \
+      if ((e = allow_lds(KERNEL<float, 128, RTV>, LDS)) != hipSuccess) return e;                           \
+      hipLaunchKernelGGL((KERNEL<float, 128, RTV>), GRID, BLOCK, LDS, s, a);                               \
+    } else {                                                                                               \
+      if ((e = allow_lds(KERNEL<float, 64, RTV>, LDS)) != hipSuccess) return e;                            \
+      hipLaunchKernelGGL((KERNEL<float, 64, RTV>), GRID, BLOCK, LDS, s, a);                                \
+    }                                                                                                      \
+  } while (0)
+
+  WF_RT_SWITCH(WF_LAUNCH, coarse_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
+  WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt), P.attend_lds);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rt, H), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(combine_kernel<64>, dim3(rt, H), dim3(256), 0, s, a);
+  return hipGetLastError();
+#undef WF_RT_SWITCH
+#undef WF_LAUNCH
+}
+
+}  // namespace wf

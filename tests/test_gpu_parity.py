@@ -140,6 +140,13 @@ EDGE = [
     ("bf16-d64", custom(2, cid=96, head_dim=64, heads=4, n_q=33, n_prompt=4096, n_gen=100, levels=6),
      [3, 6, 12, 23, 40, 70, 120], 6),
     ("L1", custom(1, cid=97, dtype="bf16", n_prompt=256, levels=1), [70, 101], 1),
+    # selections too large for the register-resident Top-K take the general path
+    ("coarse-8192-keys", custom(2, cid=86, heads=2, n_prompt=16384, n_gen=16, levels=1, n_spans=4),
+     [300, 500], 1),
+    ("coarse-20480-keys-global", custom(2, cid=87, head_dim=64, heads=1, n_prompt=20480, n_gen=8, levels=0,
+                                        n_spans=2), [1000], 0),
+    ("refine-6000-candidates", custom(4, cid=88, heads=2, n_prompt=32768, n_gen=32, levels=2, n_spans=4,
+                                      key_law="normal"), [2000, 3000, 5600], 2),
 ]
 
 
