@@ -103,7 +103,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->cover_lds = 4 * (((P->k_top + 3) & ~3) + (P->coarse_keys_in_lds ? P->n_top : 0));
   // attention: about one workgroup per compute unit in total
   P->n_att = P->k0 + n_gen;
-  P->chunk = wf::attend_chunk(pyr->dtype, (n_q + 15) / 16);
+  P->chunk = wf::attend_chunk(pyr->dtype);
   P->n_chunks = (P->n_att + P->chunk - 1) / P->chunk;
   int target = (256 + P->heads_total - 1) / P->heads_total;
   if (target > wf::kMaxSplit) target = wf::kMaxSplit;

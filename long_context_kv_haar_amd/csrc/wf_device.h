@@ -35,9 +35,11 @@ __device__ __forceinline__ uint32_t pack_bf16(uint32_t lo, uint32_t hi) { return
 // MFMA 16x16 tiles.  D[i][j] += sum_k A[i][k] B[k][j]; lane l supplies row
 // i = l % 16 of A and column j = l % 16 of B, with k-slots chosen by
 // g = l / 16; the accumulator holds D[4g + r][l % 16], r = 0..3.  Only the
-// pairing of A's and B's k-slots matters for a dot product, so every kernel
-// assigns lane group g the contiguous quarter [g d/4, (g+1) d/4) of the
-// contraction axis, read as one run of contiguous bytes.
+// pairing of A's and B's k-slots matters for a dot product, so the kernels
+// choose the permutation of the contraction axis that suits the loads:
+//   bfloat16: step s of lane group g takes elements [32 s + 8 g, 32 s + 8 g + 8),
+//     so the four lane groups of a row read 64 contiguous bytes per step;
+//   float32:  lane group g takes the contiguous quarter [g d/4, (g+1) d/4).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -56,11 +58,11 @@ template <typename T, int D> struct Frag;
 template <int D> struct Frag<bf16_t, D> {
   static constexpr int STEPS = D / 32;
   u32x4 v[STEPS];
-  // Row `row` of a row-major [*, D] bfloat16 matrix, quarter g.
+  // Row `row` of a row-major [*, D] bfloat16 matrix, lane group g.
   __device__ __forceinline__ void load(const bf16_t* row, int g) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(row + g * (D / 4));
+    const u32x4* p = reinterpret_cast<const u32x4*>(row + 8 * g);
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) v[s] = p[s];
+    for (int s = 0; s < STEPS; ++s) v[s] = p[4 * s];
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -151,15 +153,15 @@ __device__ __forceinline__ float key_to_f32(uint32_t k) {
 //
 // select_threshold narrows the k-th largest key by range bisection: the keys
 // still in play lie in [lo, lo + range]; each pass counts them into at most
-// kTopKBins bins of width 2^s (bin = (key - lo) >> s) with LDS atomics, finds
+// 4 NT bins of width 2^s (bin = (key - lo) >> s) with LDS atomics, finds
 // the bin holding the k-th largest, and recurses into it.  Starting from the
 // actual [min, max] of the keys spreads them over the bins (scores of one
 // level share their leading bits, so fixed-digit radix passes would pile
 // every key into one bin and serialise the atomics); a pass ends the search
 // once every key of the chosen bin is kept, or the bin holds a single value.
-// The bin search is spread over the whole workgroup: thread t owns the
-// contiguous bins [t B, (t+1) B), B = kTopKBins / NT, read with 16-byte LDS
-// loads, and one workgroup scan of the per-thread totals locates the bin.
+// The bin search is spread over the whole workgroup: thread t owns the four
+// contiguous bins [4 t, 4 t + 4), read with one 16-byte LDS load, and one
+// workgroup scan of the per-thread totals locates the bin.
 //
 // The kept set is: every key > hi, and of the keys in [lo, hi] the `need`
 // ones with the lowest indices (when the search narrowed to one value,
@@ -168,11 +170,11 @@ __device__ __forceinline__ float key_to_f32(uint32_t k) {
 // NT = threads of the workgroup (a multiple of 64, at most 1024); all threads
 // must call these functions together.
 // ---------------------------------------------------------------------------
-constexpr int kTopKBins = 4096;
+constexpr int kTopKBinsPerThread = 4;  // histogram bins owned by each thread in the bin search
 constexpr int floor_log2(int x) { return x <= 1 ? 0 : 1 + floor_log2(x / 2); }
 
 template <int NT> struct TopKShared {
-  int hist[kTopKBins];
+  int hist[kTopKBinsPerThread * NT];
   uint32_t wmin[NT / 64], wmax[NT / 64];
   int wsum_a[NT / 64], wsum_b[NT / 64];
   int bcast[4];
@@ -271,10 +273,9 @@ __device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* wa, int
 }
 
 template <int NT, class KeyFn>
-__device__ Threshold select_threshold(KeyFn key, int n, int k, TopKShared<NT>& sh) {
-  constexpr int BPT = (kTopKBins / NT) & ~3;  // bins per thread in the bin search
+__device__ __forceinline__ Threshold select_threshold(KeyFn key, int n, int k, TopKShared<NT>& sh) {
+  constexpr int BPT = kTopKBinsPerThread;     // bins per thread in the bin search
   constexpr int LOGB = floor_log2(NT * BPT);   // bins used per pass: 2^LOGB
-  static_assert(BPT >= 4, "too many threads for the bin search");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = threadIdx.x; i < n; i += NT) {
@@ -352,7 +353,7 @@ __device__ Threshold select_threshold(KeyFn key, int n, int k, TopKShared<NT>& s
 
 // Calls out(o, i) for the kept indices i in ascending order, o = 0..k-1.
 template <int NT, class KeyFn, class OutFn>
-__device__ void topk_compact(KeyFn key, int n, Threshold t, TopKShared<NT>& sh, OutFn out) {
+__device__ __forceinline__ void topk_compact(KeyFn key, int n, Threshold t, TopKShared<NT>& sh, OutFn out) {
   const int seg = (n + NT - 1) / NT;
   const int i0 = min(n, (int)threadIdx.x * seg), i1 = min(n, i0 + seg);
   int g = 0, e = 0;
@@ -376,11 +377,15 @@ __device__ void topk_compact(KeyFn key, int n, Threshold t, TopKShared<NT>& sh, 
 // ---------------------------------------------------------------------------
 // Top-K in (usually) one histogram pass.  The kept set of "the k best by
 // (key descending, index ascending)" is exactly the set of indices i with
-// (key_i > tk) or (key_i == tk and i <= ti), where (tk, ti) is the k-th best
-// (key, index) pair.  One pass counts the keys into kTopKBins bins spanning
-// their [min, max]; the bin holding the k-th best is found by a workgroup
-// scan.  If every key of that bin is kept, (tk, ti) = (bin start, any).
-// Otherwise the bin's keys (a handful: the bins split the range finely) are
+// bin(key_i) > b, or bin(key_i) == b and (key_i > tk or (key_i == tk and
+// i <= ti)), for any bin function that is monotone in the key, where b is the
+// bin of the k-th best (key, index) pair and (tk, ti) that pair.  The bins
+// split the scores' value range [min, max] linearly (bin = (x - min) * scale,
+// a composition of monotone float operations, so it never inverts an order);
+// linear bins spread clustered scores far better than bins of the key bits,
+// which give each binade only a handful of bins.  One pass counts the keys
+// into 4 NT bins and a workgroup scan finds b.  If every key of bin b is
+// kept, (tk, ti) are not needed; otherwise the bin's keys (a handful) are
 // gathered with their indices and ranked exactly inside one wave.  A bin with
 // more than kGatherMax keys (heavy ties) falls back to select_threshold +
 // topk_compact.  Emits the kept indices in ascending order with one scan.
@@ -396,9 +401,22 @@ template <int NT> struct TopKFastShared {
   int ti;
 };
 
+// Bin of a key: linear in the float value when the range allows it, else by
+// the key bits (range shift s).  Monotone non-decreasing in the key.
+struct BinFn {
+  float fmin, scale;
+  uint32_t kmin;
+  int shift, nb;
+  bool linear;
+  __device__ __forceinline__ int operator()(uint32_t x) const {
+    if (linear) return min(nb - 1, (int)((key_to_f32(x) - fmin) * scale));
+    return (int)((x - kmin) >> shift);
+  }
+};
+
 template <int NT, class KeyFn, class OutFn>
-__device__ void topk_fast(KeyFn key, int n, int k, TopKFastShared<NT>& fs, OutFn out) {
-  constexpr int BPT = (kTopKBins / NT) & ~3;
+__device__ __forceinline__ void topk_fast(KeyFn key, int n, int k, TopKFastShared<NT>& fs, OutFn out) {
+  constexpr int BPT = kTopKBinsPerThread;
   constexpr int LOGB = floor_log2(NT * BPT);
   TopKShared<NT>& sh = fs.base;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -427,16 +445,25 @@ __device__ void topk_fast(KeyFn key, int n, int k, TopKFastShared<NT>& fs, OutFn
     mx = max(mx, sh.wmax[i]);
   }
   const uint32_t range = mx - mn;
-  uint32_t tk;
-  int ti;
+  uint32_t tk = 0u;
+  int ti = 0x7FFFFFFF;
+  int b = -1;  // bins above b are kept whole; -1: no bins (all keys equal)
+  BinFn bin;
   bool general = false;
   if (range == 0) {  // all keys equal: the k lowest indices
     tk = mn;
     ti = k - 1;
   } else {
+    const float fmin = key_to_f32(mn), span = key_to_f32(mx) - fmin;
+    const float scale = (float)(1 << LOGB) / span;
     const int bits = 32 - __clz(range);
-    const int s = bits > LOGB ? bits - LOGB : 0;
-    for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sh.hist[(key(i) - mn) >> s], 1);
+    bin.fmin = fmin;
+    bin.scale = scale;
+    bin.kmin = mn;
+    bin.shift = bits > LOGB ? bits - LOGB : 0;
+    bin.nb = 1 << LOGB;
+    bin.linear = span > 0.f && span < 3.0e38f && scale < 3.0e38f;  // finite, non-degenerate range
+    for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&sh.hist[bin(key(i))], 1);
     __syncthreads();
     int h[BPT];
     int tot = 0;
@@ -453,30 +480,27 @@ __device__ void topk_fast(KeyFn key, int n, int k, TopKFastShared<NT>& fs, OutFn
     const int incl = block_incl_scan<NT>(tot, sh.wsum_a, &all);
     int above = all - incl;
     if (above < k && k <= above + tot) {  // exactly one thread
-      int bin = 0, rem = 0, c = 0;
+      int bn = 0, rem = 0, c = 0;
 #pragma unroll
       for (int i = BPT - 1; i >= 0; --i) {
         const bool hit = (above < k) & (k <= above + h[i]);
-        bin = hit ? i : bin;
+        bn = hit ? i : bn;
         rem = hit ? k - above : rem;
         c = hit ? h[i] : c;
         above += h[i];
       }
-      sh.bcast[0] = threadIdx.x * BPT + bin;
+      sh.bcast[0] = threadIdx.x * BPT + bn;
       sh.bcast[1] = rem;
       sh.bcast[2] = c;
     }
     __syncthreads();
-    const int b = sh.bcast[0], need = sh.bcast[1], cnt = sh.bcast[2];
-    const uint32_t blo = mn + ((uint32_t)b << s);
-    const uint32_t bhi = blo + (s == 0 ? 0u : min(range - ((uint32_t)b << s), (1u << s) - 1u));
-    if (cnt == need) {  // the whole bin is kept
-      tk = blo;
-      ti = 0x7FFFFFFF;
+    b = sh.bcast[0];
+    const int need = sh.bcast[1], cnt = sh.bcast[2];
+    if (cnt == need) {  // the whole bin is kept: any key passes (tk, ti) = (0, max)
     } else if (cnt <= kGatherMax) {
       for (int i = threadIdx.x; i < n; i += NT) {
         const uint32_t x = key(i);
-        if (x >= blo && x <= bhi) {
+        if (bin(x) == b) {
           const int slot = atomicAdd(&fs.gcount, 1);
           fs.gkey[slot] = x;
           fs.gidx[slot] = i;
@@ -512,36 +536,38 @@ __device__ void topk_fast(KeyFn key, int n, int k, TopKFastShared<NT>& fs, OutFn
     return;
   }
   // compaction in index order
+  auto kept = [&](uint32_t x, int i) {
+    if (b < 0) return (x > tk) | ((x == tk) & (i <= ti));
+    const int bx = bin(x);
+    return (bx > b) | ((bx == b) & ((x > tk) | ((x == tk) & (i <= ti))));
+  };
   const int seg = (n + NT - 1) / NT;
   const int i0 = min(n, (int)threadIdx.x * seg), i1 = min(n, i0 + seg);
   int c = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t x = key(i);
-    c += (x > tk) | ((x == tk) & (i <= ti));
-  }
+  for (int i = i0; i < i1; ++i) c += kept(key(i), i);
   int all;
   int o = block_incl_scan<NT>(c, sh.wsum_a, &all) - c;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t x = key(i);
-    if ((x > tk) | ((x == tk) & (i <= ti))) out(o++, i);
-  }
+  for (int i = i0; i < i1; ++i)
+    if (kept(key(i), i)) out(o++, i);
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// Register-resident Top-K for n <= NT * KPT keys: thread t holds keys
-// [t KPT, t KPT + KPT) (its contiguous segment, so the ascending output order
-// is the thread order) in registers for the whole selection, so every key is
-// read from memory once.  Same rule and result as select_threshold +
-// topk_compact; 2048 bins per pass, searched branch-free over the 2048 / NT
-// bins each thread owns.  out(o, i, j) receives the output slot o, the key
-// index i and the register slot j of the key.
+// Register-resident Top-K, same rule and output as topk_fast, for
+// n <= NT * KPT keys.  Thread t holds the keys of indices [t KPT, t KPT + KPT)
+// in registers (a contiguous segment, so thread order is index order) and
+// every pass works on them, with no per-key LDS round trip.  key_at(i) reads
+// key i again, for the rare heavily tied bin that needs the multi-pass
+// search; out_reg(o, j) receives the output slot o of register slot j (a
+// compile-time constant in the unrolled loops), out_idx(o, i) the output
+// slot of index i on that fallback path.
 // ---------------------------------------------------------------------------
-template <int NT, int KPT, class OutFn>
-__device__ void topk_regs(const uint32_t (&key)[KPT], int n, int k, TopKShared<NT>& sh, OutFn out) {
-  constexpr int BPT = (2048 / NT) >= 4 ? ((2048 / NT) & ~3) : 4;  // bins per thread
-  constexpr int LOGB = floor_log2(NT * BPT);                      // bins used per pass: 2^LOGB
-  static_assert(NT * BPT <= kTopKBins, "bin search layout");
+template <int NT, int KPT, class KeyFn, class OutReg, class OutIdx>
+__device__ __forceinline__ void topk_block(const uint32_t (&key)[KPT], int n, int k, TopKFastShared<NT>& fs, KeyFn key_at,
+                           OutReg out_reg, OutIdx out_idx) {
+  constexpr int BPT = kTopKBinsPerThread;
+  constexpr int LOGB = floor_log2(NT * BPT);
+  TopKShared<NT>& sh = fs.base;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i0 = threadIdx.x * KPT;
   const int cnt = max(0, min(KPT, n - i0));
@@ -561,6 +587,7 @@ __device__ void topk_regs(const uint32_t (&key)[KPT], int n, int k, TopKShared<N
   int4* own = reinterpret_cast<int4*>(sh.hist + threadIdx.x * BPT);
 #pragma unroll
   for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
+  if (threadIdx.x == 0) fs.gcount = 0;
   __syncthreads();
   mn = 0xFFFFFFFFu;
   mx = 0u;
@@ -569,15 +596,30 @@ __device__ void topk_regs(const uint32_t (&key)[KPT], int n, int k, TopKShared<N
     mn = min(mn, sh.wmin[i]);
     mx = max(mx, sh.wmax[i]);
   }
-  uint32_t lo = mn, range = mx - mn;
-  int need = k;
-  while (range != 0) {
-    const int bits = 32 - __clz(range);
-    const int s = bits > LOGB ? bits - LOGB : 0;
+  int bn[KPT];
+  int b = 0;
+  uint32_t tk;
+  int ti;
+  if (mx == mn) {  // all keys equal: the k lowest indices
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) bn[j] = 0;
+    tk = mn;
+    ti = k - 1;
+  } else {
+    BinFn bin;
+    const float fmin = key_to_f32(mn), span = key_to_f32(mx) - fmin;
+    const float scale = (float)(1 << LOGB) / span;
+    const int bits = 32 - __clz(mx - mn);
+    bin.fmin = fmin;
+    bin.scale = scale;
+    bin.kmin = mn;
+    bin.shift = bits > LOGB ? bits - LOGB : 0;
+    bin.nb = 1 << LOGB;
+    bin.linear = span > 0.f && span < 3.0e38f && scale < 3.0e38f;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint32_t d = key[j] - lo;  // wraps above range for keys below lo
-      if (j < cnt && d <= range) atomicAdd(&sh.hist[d >> s], 1);
+      bn[j] = bin(key[j]);
+      if (j < cnt) atomicAdd(&sh.hist[bn[j]], 1);
     }
     __syncthreads();
     int h[BPT];
@@ -591,54 +633,78 @@ __device__ void topk_regs(const uint32_t (&key)[KPT], int n, int k, TopKShared<N
       h[4 * i + 3] = v.w;
       tot += v.x + v.y + v.z + v.w;
     }
-#pragma unroll
-    for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
     int all;
     const int incl = block_incl_scan<NT>(tot, sh.wsum_a, &all);
-    int above = all - incl;  // keys in bins owned by higher threads
-    if (above < need && need <= above + tot) {  // exactly one thread
-      int bin = 0, rem = 0, c = 0;
+    int above = all - incl;
+    if (above < k && k <= above + tot) {  // exactly one thread
+      int bb = 0, rem = 0, c = 0;
 #pragma unroll
       for (int i = BPT - 1; i >= 0; --i) {
-        const bool hit = (above < need) & (need <= above + h[i]);
-        bin = hit ? i : bin;
-        rem = hit ? need - above : rem;
+        const bool hit = (above < k) & (k <= above + h[i]);
+        bb = hit ? i : bb;
+        rem = hit ? k - above : rem;
         c = hit ? h[i] : c;
         above += h[i];
       }
-      sh.bcast[0] = threadIdx.x * BPT + bin;
+      sh.bcast[0] = threadIdx.x * BPT + bb;
       sh.bcast[1] = rem;
       sh.bcast[2] = c;
     }
     __syncthreads();
-    const int b = sh.bcast[0];
-    need = sh.bcast[1];
-    const int c = sh.bcast[2];
-    lo += (uint32_t)b << s;
-    const uint32_t rest = range - ((uint32_t)b << s);
-    range = s == 0 ? 0u : min(rest, (1u << s) - 1u);
-    if (c == need) break;
-    __syncthreads();  // bcast and wsum are rewritten by the next pass
+    b = sh.bcast[0];
+    const int need = sh.bcast[1], bc = sh.bcast[2];
+    tk = 0u;
+    ti = 0x7FFFFFFF;
+    if (bc != need) {
+      if (bc > kGatherMax) {  // heavily tied bin: multi-pass search over key_at
+        __syncthreads();
+        const Threshold t = select_threshold<NT>(key_at, n, k, sh);
+        topk_compact<NT>(key_at, n, t, sh, out_idx);
+        __syncthreads();
+        return;
+      }
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (j < cnt && bn[j] == b) {
+          const int slot = atomicAdd(&fs.gcount, 1);
+          fs.gkey[slot] = key[j];
+          fs.gidx[slot] = i0 + j;
+        }
+      __syncthreads();
+      if (threadIdx.x < 64) {  // rank the gathered keys; rank need-1 is the threshold
+        const bool act = lane < bc;
+        const uint32_t x = act ? fs.gkey[lane] : 0u;
+        const int xi = act ? fs.gidx[lane] : 0;
+        int rank = 0;
+        for (int m = 0; m < bc; ++m) {
+          const uint32_t y = fs.gkey[m];
+          const int yi = fs.gidx[m];
+          rank += (y > x) | ((y == x) & (yi < xi));
+        }
+        if (act && rank == need - 1) {
+          fs.tk = x;
+          fs.ti = xi;
+        }
+      }
+      __syncthreads();
+      tk = fs.tk;
+      ti = fs.ti;
+    }
   }
-  const uint32_t hi = lo + range;
-  int g = 0, e = 0;
+  bool kept[KPT];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t x = key[j];
+    kept[j] = (j < cnt) & ((bn[j] > b) | ((bn[j] == b) & ((x > tk) | ((x == tk) & (i0 + j <= ti)))));
+    c += kept[j];
+  }
+  int all;
+  int o = block_incl_scan<NT>(c, sh.wsum_a, &all) - c;
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
-    if (j < cnt) {
-      g += key[j] > hi;
-      e += (key[j] >= lo) & (key[j] <= hi);
-    }
-  int G, E;
-  block_exclusive_scan2<NT>(g, e, sh.wsum_a, sh.wsum_b, G, E);
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (j < cnt) {
-      const bool gt = key[j] > hi;
-      const bool eq = (key[j] >= lo) & (key[j] <= hi);
-      if (gt || (eq && E < need)) out(G + min(E, need), i0 + j, j);
-      G += gt;
-      E += eq;
-    }
+    if (kept[j]) out_reg(o++, j);
+  __syncthreads();
 }
 
 }  // namespace wf

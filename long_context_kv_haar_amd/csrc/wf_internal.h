@@ -9,17 +9,13 @@
 namespace wf {
 
 constexpr int kMaxLevels = WF_MAX_LEVELS;
-constexpr int kAttendChunkF32 = 32;       // tokens per attention chunk (f32)
+constexpr int kAttendGroups = 4;          // waves per query tile in the attention workgroup
 constexpr int kMaxSplit = 16;             // attention splits per head
 constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to this count
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
 constexpr int kCoverThreads = 256;
-constexpr int kCoarseRegKeys = 4096;     // coarse Top-K held in registers up to this many keys
-constexpr int kRefineRegKeys = 5120;     // refinement Top-K held in registers up to this many candidates
-constexpr int kRefineRegMaxPerThread = 40;
-constexpr int kRegTopKMin = 2048;         // below this many keys the LDS-resident Top-K is faster
 
 struct PyramidLaunch {
   const void* k;
@@ -70,19 +66,20 @@ struct SelectLaunch {
 hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s);
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
 
-// Tokens per attention chunk: 8 16-byte K and V vectors per thread and
-// chunk for bfloat16 (32 tokens per query tile, up to 128), 32 for float32.
-constexpr int attend_chunk(int dtype, int nqt) {
-  return dtype == WF_BF16 ? (nqt >= 3 ? 128 : 32 * nqt) : kAttendChunkF32;
-}
+// Tokens per attention chunk (32 per wave for bfloat16, 16 for float32).
+constexpr int attend_chunk(int dtype) { return dtype == WF_BF16 ? 32 * kAttendGroups : 16 * kAttendGroups; }
 
-// LDS bytes of the attention chunk buffers (K rows, transposed V).
+// LDS bytes after the attended-set list: the chunk buffers (K rows,
+// transposed V), aliased at the end by the merge slots of the wave states
+// (kAttendGroups / 2 slots per query tile).
 inline int attend_buffer_bytes(int dtype, int head_dim, int nqt) {
   const bool bf = dtype == WF_BF16;
   const int es = bf ? 2 : 4;
-  const int ch = attend_chunk(dtype, nqt);
-  const int kpad = bf ? 8 : 4, vpad = 4;
-  return ch * (head_dim + kpad) * es + head_dim * (ch + vpad) * es;
+  const int ch = attend_chunk(dtype);
+  const int kpad = bf ? 8 : 4, vpad = bf ? 16 : 4;
+  const int kv = ch * (head_dim + kpad) * es + head_dim * (ch + vpad) * es;
+  const int merge = (kAttendGroups / 2) * nqt * 64 * (head_dim / 4 + 2) * 4;
+  return kv > merge ? kv : merge;
 }
 
 }  // namespace wf

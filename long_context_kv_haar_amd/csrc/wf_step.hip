@@ -94,10 +94,12 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (sizeof(T) == 2) {
     constexpr int STEPS = D / 32;
-    const float4* p = reinterpret_cast<const float4*>(arow + g * (D / 4));
+    // step s of lane group g: coefficients [32 s + 8 g, 32 s + 8 g + 8), as Frag<bf16_t>
+    const float4* p = reinterpret_cast<const float4*>(arow);
     float4 x[2 * STEPS];
 #pragma unroll
-    for (int i = 0; i < 2 * STEPS; ++i) x[i] = valid ? p[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < 2 * STEPS; ++i)
+      x[i] = valid ? p[8 * (i >> 1) + 2 * g + (i & 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       u32x4 hi, lo;
@@ -145,6 +147,19 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   }
 }
 
+// Coarse Top-K with the keys in registers (n <= NT * KPT); emit(o, i) gets
+// output slot o of region i.
+template <int NT, int KPT, class Emit>
+__device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, int k, TopKFastShared<NT>& sh,
+                                                 Emit emit) {
+  const int i0 = threadIdx.x * KPT;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = (i0 + j < n) ? keys_g[i0 + j] : 0u;
+  topk_block<NT, KPT>(key, n, k, sh, [&](int i) { return keys_g[i]; }, [&](int o, int j) { emit(o, i0 + j); },
+                      emit);
+}
+
 // ---------------------------------------------------------------------------
 // Cover: coarse Top-K, then coverage scores.
 //
@@ -182,7 +197,15 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
     }
   };
-  if (a.coarse_keys_in_lds) {
+  if (a.n_top <= NT * 4) {
+    coarse_topk_regs<NT, 4>(keys_g, a.n_top, a.k_top, sh, emit);
+  } else if (a.n_top <= NT * 8) {
+    coarse_topk_regs<NT, 8>(keys_g, a.n_top, a.k_top, sh, emit);
+  } else if (a.n_top <= NT * 16) {
+    coarse_topk_regs<NT, 16>(keys_g, a.n_top, a.k_top, sh, emit);
+  } else if (a.n_top <= NT * 32) {
+    coarse_topk_regs<NT, 32>(keys_g, a.n_top, a.k_top, sh, emit);
+  } else if (a.coarse_keys_in_lds) {
     for (int i = threadIdx.x; i < a.n_top; i += NT) keys_l[i] = keys_g[i];
     __syncthreads();
     topk_fast<NT>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, sh, emit);
@@ -338,6 +361,35 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   }
 }
 
+// One refinement level with the candidates in registers (n <= NT * KPT):
+// thread t takes candidates [t KPT, t KPT + KPT), the children of kept
+// parents [t KPT / 2, (t + 1) KPT / 2), and writes the kept ones to nxt.
+template <int NT, int KPT>
+__device__ __forceinline__ void refine_level(const float* cj, int nj, const int* cur, int* nxt, int n, int kj,
+                                             TopKFastShared<NT>& sh) {
+  static_assert(KPT % 2 == 0, "children come in pairs");
+  const int i0 = threadIdx.x * KPT;
+  int pos[KPT];
+  uint32_t key[KPT];
+#pragma unroll
+  for (int m = 0; m < KPT / 2; ++m) {
+    const int par = (i0 + 2 * m < n) ? cur[i0 / 2 + m] : 0;
+    pos[2 * m] = clampi(2 * par, 0, nj - 1);
+    pos[2 * m + 1] = clampi(2 * par + 1, 0, nj - 1);
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = (i0 + j < n) ? order_key(cj[pos[j]]) : 0u;
+  auto pos_of = [&](int i) { return clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1); };
+  topk_block<NT, KPT>(
+      key, n, kj, sh, [&](int i) { return order_key(cj[pos_of(i)]); },
+      [&](int o, int j) {
+        if (o < kj) nxt[o] = pos[j];
+      },
+      [&](int o, int i) {
+        if (o < kj) nxt[o] = pos_of(i);
+      });
+}
+
 // ---------------------------------------------------------------------------
 // Recursive refinement (Figure 2 (d)) for one head, by one workgroup.
 // Positions at level j index the level-j blocks inside the covered set,
@@ -348,7 +400,7 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
 // writes sel_out and the per-level outputs of levels L-1 .. 0.
 // ---------------------------------------------------------------------------
 template <int NT>
-__device__ void refine_head(const StepArgs& a, int head, uint32_t* lds, TopKFastShared<NT>& sh, int* tsel,
+__device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, TopKFastShared<NT>& sh, int* tsel,
                             bool report) {
   const int L = a.levels;
   uint32_t* keys = lds;
@@ -374,11 +426,22 @@ __device__ void refine_head(const StepArgs& a, int head, uint32_t* lds, TopKFast
     const int n = 2 * kprev;
     const int nj = (int)(a.covered >> j);  // level-j positions in the covered set
     const float* cj = cov + a.cov_off[j];
-    for (int c = threadIdx.x; c < n; c += NT) keys[c] = order_key(cj[clampi(2 * cur[c >> 1] + (c & 1), 0, nj - 1)]);
-    __syncthreads();
-    topk_fast<NT>([&](int i) { return keys[i]; }, n, kj, sh, [&](int o, int i) {
-      if (o < kj) nxt[o] = clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1);
-    });
+    // register-resident candidates up to 8 per thread (16 for small
+    // workgroups); beyond that the keys stay in LDS
+    constexpr int KMAX = NT >= 512 ? 8 : 16;
+    if (n <= NT * 4) {
+      refine_level<NT, 4>(cj, nj, cur, nxt, n, kj, sh);
+    } else if (n <= NT * 8) {
+      refine_level<NT, 8>(cj, nj, cur, nxt, n, kj, sh);
+    } else if (KMAX >= 16 && n <= NT * 16) {
+      refine_level<NT, KMAX>(cj, nj, cur, nxt, n, kj, sh);
+    } else {
+      for (int c = threadIdx.x; c < n; c += NT) keys[c] = order_key(cj[clampi(2 * cur[c >> 1] + (c & 1), 0, nj - 1)]);
+      __syncthreads();
+      topk_fast<NT>([&](int i) { return keys[i]; }, n, kj, sh, [&](int o, int i) {
+        if (o < kj) nxt[o] = clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1);
+      });
+    }
     __syncthreads();
     if (dbg_sel || dbg_score) {
       const int sh_l = L - j;
@@ -408,32 +471,58 @@ __device__ void refine_head(const StepArgs& a, int head, uint32_t* lds, TopKFast
 
 // ---------------------------------------------------------------------------
 // Sparse attention (eq. 3 over T = kept prompt tokens, then gen_idx).
-// Workgroup (split, head) first runs the refinement, leaving T in LDS, then
-// walks chunks of CH tokens; wave w owns query tile w.  Per chunk: K rows ->
-// LDS (row-major, padded), V rows -> LDS transposed; S^T = K Q^T on MFMA
-// (lane (query l16, g) holds tokens 16 t + 4 g + r); online softmax per
-// query row in float32; O^T += V^T P^T on MFMA with P split into bf16 hi + lo
-// (float32 MFMA for float32 inputs).  The next chunk's rows are fetched into
-// registers while the current one computes.  Writes the split's partial
-// (m, l, O) to the workspace.
+// Workgroup (split, head) first runs the refinement with all its threads,
+// leaving T in LDS, then walks chunks of CH tokens.  Wave w owns query tile
+// qt = w / TG and token group tg = w % TG: the CW = CH / TG tokens
+// [tg CW, tg CW + CW) of every chunk, with an online-softmax state of its
+// own; the TG states of a query tile are merged through LDS at the end, so
+// there are TG waves per query tile to hide one another's latencies.  Per
+// chunk: K rows -> LDS (row-major, padded), V -> LDS transposed (V^T);
+// S^T = K Q^T on MFMA (lane (query l16, g) holds tokens 16 t + 4 g + r);
+// online softmax per query row in float32; O^T += V^T P^T on MFMA with P
+// split into bf16 hi + lo (float32 MFMA for float32 inputs).  The next
+// chunk's rows are fetched into registers while the current one computes.
+// Writes the split's partial (m, l, O) to the workspace.
 // ---------------------------------------------------------------------------
 template <typename T> struct AttendTraits;
-template <> struct AttendTraits<bf16_t> { static constexpr int KPAD = 8, VPAD = 4, DT = WF_BF16; };
+template <> struct AttendTraits<bf16_t> { static constexpr int KPAD = 8, VPAD = 16, DT = WF_BF16; };
 template <> struct AttendTraits<float> { static constexpr int KPAD = 4, VPAD = 4, DT = WF_F32; };
 
+// Online-softmax state of one wave: lane (query l16, g) holds m and l of its
+// query row and O^T[16 dt + 4 g + r][query].
+template <int D> struct SoftmaxState {
+  float m, l;
+  f32x4 o[D / 16];
+};
+
+// Merge `b` into `a` (m in log2 units; an empty state has m = -inf, l = 0, O = 0).
+template <int D>
+__device__ __forceinline__ void merge_state(SoftmaxState<D>& a, float mb, float lb, const f32x4* ob) {
+  const float mm = fmaxf(a.m, mb);
+  const float sa = (a.m == -INFINITY) ? 0.f : exp2f(a.m - mm);
+  const float sb = (mb == -INFINITY) ? 0.f : exp2f(mb - mm);
+  a.m = mm;
+  a.l = a.l * sa + lb * sb;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) a.o[dt] = a.o[dt] * sa + ob[dt] * sb;
+}
+
 template <typename T, int D, int NQT>
-__global__ __launch_bounds__(64 * NQT) void attend_kernel(StepArgs a) {
-  constexpr int NT = 64 * NQT;
-  constexpr int CH = attend_chunk(AttendTraits<T>::DT, NQT);
+__global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepArgs a) {
+  constexpr int TG = kAttendGroups;
+  constexpr int NT = 64 * NQT * TG;
+  constexpr int CH = attend_chunk(AttendTraits<T>::DT);
+  constexpr int CW = CH / TG;                     // tokens of one wave per chunk
   constexpr int KS = D + AttendTraits<T>::KPAD;   // Ks row stride (elements)
   constexpr int VS = CH + AttendTraits<T>::VPAD;  // Vt row stride (elements)
   constexpr int VE = 16 / sizeof(T);              // elements per 16-byte vector
   constexpr int NV = D / VE;                      // vectors per row
   constexpr int PER = (CH * NV + NT - 1) / NT;    // vectors per thread per tensor
+  static_assert(CW % 16 == 0 && (sizeof(T) != 2 || CW % 32 == 0), "whole MFMA tiles per wave");
   extern __shared__ uint32_t lds[];
   __shared__ TopKFastShared<NT> sh;
   int* tlist = reinterpret_cast<int*>(lds);        // T: kept prompt tokens, then gen_idx
-  uint32_t* scratch = lds + a.att_t_words;         // refinement state, then K/V buffers
+  uint32_t* scratch = lds + a.att_t_words;         // refinement state, K/V buffers, merge slots
   T* Ks = reinterpret_cast<T*>(scratch);
   T* Vt = Ks + CH * KS;
 
@@ -443,8 +532,9 @@ __global__ __launch_bounds__(64 * NQT) void attend_kernel(StepArgs a) {
   __syncthreads();
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int qt = w / TG, tg = w - qt * TG;
   const int g = lane >> 4, l16 = lane & 15;
-  const int query = 16 * w + l16;
+  const int query = 16 * qt + l16;
   const bool qvalid = query < a.n_q;
   const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
   const T* vh = reinterpret_cast<const T*>(a.v) + (int64_t)head * a.n_tot * D;
@@ -454,21 +544,30 @@ __global__ __launch_bounds__(64 * NQT) void attend_kernel(StepArgs a) {
   if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
 
   const float sl2 = a.inv_sqrt_d * 1.44269504088896340736f;  // log2(e)/sqrt(d)
-  float m = -INFINITY, lsum = 0.f;
-  f32x4 o[D / 16];
+  SoftmaxState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int c_begin = split * a.chunks_per_split;
   const int c_end = min(a.n_chunks, c_begin + a.chunks_per_split);
 
-  // K: vector e = (row, cv) of the chunk, row-major.  V (bfloat16): lane
-  // handles the token pair (2 p, 2 p + 1) at column block cv, so that each
-  // transposed LDS store writes one 32-bit word (two tokens) and a wave's
-  // store covers 64 consecutive words of one V^T row: no bank conflicts.
-  constexpr int NPAIR = CH / 2;                  // token pairs per chunk
-  constexpr int VPER = (NPAIR * NV + NT - 1) / NT;  // (pair, cv) items per thread
-  u32x4 kreg[PER], vreg[sizeof(T) == 2 ? 2 * VPER : PER];
+  // K and V: vector e = (row, cv) of the chunk, row-major, so each wave-wide
+  // load reads whole rows.  K rows go to LDS as they are.  bfloat16 V goes to
+  // LDS transposed (V^T, d-major) as 32-bit words holding one element of two
+  // consecutive tokens: the lanes holding rows 2p and 2p + 1 at the same
+  // column block (lanes l and l ^ NV) swap half their vector, then each writes
+  // four words.  V^T word column p of d-row d is stored at p ^ vswz(d), an XOR
+  // swizzle that keeps these stores and the 8-byte fragment reads below free
+  // of bank conflicts.  Vectors e >= CH * NV (when NT does not divide the
+  // chunk) are idle; pair partners e and e ^ NV are both idle or both not, and
+  // every lane takes part in the swap.
+  static_assert(NV <= 32 && NT % (2 * NV) == 0, "pair partners within one wave");
+  constexpr int VW = VS / 2;               // V^T words per d-row (bfloat16)
+  constexpr int VSWM = (CH / 2 - 1) & ~1;  // swizzle keeps columns inside [0, CH/2)
+  auto vswz = [](int d) { return ((d >> 2) * 2) & VSWM; };
+  u32x4 kreg[PER], vreg[PER];
   auto fetch = [&](int chunk) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -476,159 +575,165 @@ __global__ __launch_bounds__(64 * NQT) void attend_kernel(StepArgs a) {
       const int row = e / NV, cv = e - row * NV;
       const int pos = chunk * CH + row;
       kreg[i] = u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = u32x4{0u, 0u, 0u, 0u};
       if (e < CH * NV && pos < a.n_att) {
         const int64_t tok = tlist[pos];
         kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + tok * D + cv * VE));
-      }
-      if constexpr (sizeof(T) != 2) {
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-        if (e < CH * NV && pos < a.n_att) {
-          const int64_t tok = tlist[pos];
-          vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE));
-        }
-      }
-    }
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int i = 0; i < VPER; ++i) {
-        const int e = threadIdx.x + i * NT;  // e = cv * NPAIR + pair: lanes walk pairs
-        const int cv = e / NPAIR, pr = e - cv * NPAIR;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int pos = chunk * CH + 2 * pr + h;
-          vreg[2 * i + h] = u32x4{0u, 0u, 0u, 0u};
-          if (e < NPAIR * NV && pos < a.n_att) {
-            const int64_t tok = tlist[pos];
-            vreg[2 * i + h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE));
-          }
-        }
+        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE));
       }
     }
   };
   if (c_begin < c_end) fetch(c_begin);
   for (int chunk = c_begin; chunk < c_end; ++chunk) {
-    const int pos0 = chunk * CH;
+    const int pos0 = chunk * CH + tg * CW;  // first token of this wave's slice
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = threadIdx.x + i * NT;
-      if (e < CH * NV) {
-        const int row = e / NV, cv = e - row * NV;
-        *reinterpret_cast<u32x4*>(Ks + row * KS + cv * VE) = kreg[i];
-        if constexpr (sizeof(T) != 2) {
+      const int row = e / NV, cv = e - row * NV;
+      const bool act = e < CH * NV;
+      if (act) *reinterpret_cast<u32x4*>(Ks + row * KS + cv * VE) = kreg[i];
+      if constexpr (sizeof(T) != 2) {
+        if (act)
 #pragma unroll
           for (int c = 0; c < 4; ++c) Vt[(cv * VE + c) * VS + row] = __uint_as_float(vreg[i][c]);
-        }
-      }
-    }
-    if constexpr (sizeof(T) == 2) {
+      } else {
+        const u32x4 x = vreg[i];
+        const bool odd = row & 1;  // odd rows write elements 4..7 of the pair, even rows 0..3
+        const uint32_t r0 = __shfl_xor(odd ? x[0] : x[2], NV, 64);
+        const uint32_t r1 = __shfl_xor(odd ? x[1] : x[3], NV, 64);
+        const uint32_t lo0 = odd ? r0 : x[0], hi0 = odd ? x[2] : r0;  // element pairs (row 2p, row 2p + 1)
+        const uint32_t lo1 = odd ? r1 : x[1], hi1 = odd ? x[3] : r1;
+        const uint32_t w4[4] = {(lo0 & 0xFFFFu) | (hi0 << 16), (lo0 >> 16) | (hi0 & 0xFFFF0000u),
+                                (lo1 & 0xFFFFu) | (hi1 << 16), (lo1 >> 16) | (hi1 & 0xFFFF0000u)};
+        uint32_t* vw = reinterpret_cast<uint32_t*>(Vt);
+        const int pcol = row >> 1, d0 = cv * VE + (odd ? 4 : 0);
+        if (act)
 #pragma unroll
-      for (int i = 0; i < VPER; ++i) {
-        const int e = threadIdx.x + i * NT;
-        if (e < NPAIR * NV) {
-          const int cv = e / NPAIR, pr = e - cv * NPAIR;
-          uint32_t* dst = reinterpret_cast<uint32_t*>(Vt + (cv * VE) * VS + 2 * pr);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {  // elements 2c, 2c+1 of the 8-wide column block
-            const uint32_t a0 = vreg[2 * i][c], a1 = vreg[2 * i + 1][c];
-            dst[(2 * c) * (VS / 2)] = (a0 & 0xFFFFu) | (a1 << 16);
-            dst[(2 * c + 1) * (VS / 2)] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-          }
-        }
+          for (int c = 0; c < 4; ++c) vw[(d0 + c) * VW + (pcol ^ vswz(d0 + c))] = w4[c];
       }
     }
     __syncthreads();
     if (chunk + 1 < c_end) fetch(chunk + 1);  // overlaps with the math below
 
-    f32x4 sv[CH / 16];
+    if (pos0 < a.n_att) {  // wave-uniform: a slice wholly past the end has no work
+      f32x4 sv[CW / 16];
 #pragma unroll
-    for (int t = 0; t < CH / 16; ++t) {
-      Frag<T, D> kf;
-      kf.load(Ks + (16 * t + l16) * KS, g);
-      sv[t] = mma_tile<D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    float cmax = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < CH / 16; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = pos0 + 16 * t + 4 * g + r;
-        const float x = (pos < a.n_att) ? sv[t][r] * sl2 : -INFINITY;
-        sv[t][r] = x;
-        cmax = fmaxf(cmax, x);
+      for (int t = 0; t < CW / 16; ++t) {
+        Frag<T, D> kf;
+        kf.load(Ks + (tg * CW + 16 * t + l16) * KS, g);
+        sv[t] = mma_tile<D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m, cmax);
-    const float alpha = exp2f(m - m_new);
-    float psum = 0.f;
+      float cmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < CH / 16; ++t)
+      for (int t = 0; t < CW / 16; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(sv[t][r] - m_new);
-        sv[t][r] = p;
-        psum += p;
-      }
-    lsum = lsum * alpha + psum;
-    m = m_new;
+        for (int r = 0; r < 4; ++r) {
+          const int pos = pos0 + 16 * t + 4 * g + r;
+          const float x = (pos < a.n_att) ? sv[t][r] * sl2 : -INFINITY;
+          sv[t][r] = x;
+          cmax = fmaxf(cmax, x);
+        }
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(st.m, cmax);  // finite: the slice holds a valid token
+      const float alpha = exp2f(st.m - m_new);
+      float psum = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+      for (int t = 0; t < CW / 16; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(sv[t][r] - m_new);
+          sv[t][r] = p;
+          psum += p;
+        }
+      st.l = st.l * alpha + psum;
+      st.m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) st.o[dt] *= alpha;
 
-    if constexpr (sizeof(T) == 2) {
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int st = 0; st < CH / 32; ++st) {
-        u32x4 ph, pl;
+        for (int s2 = 0; s2 < CW / 32; ++s2) {
+          u32x4 ph, pl;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t hb[4], lb[4];
+          for (int hh = 0; hh < 2; ++hh) {
+            uint32_t hb[4], lb[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = sv[2 * st + hh][r];
-            hb[r] = f32_to_bf16(p);
-            lb[r] = f32_to_bf16(p - bf16_to_f32(hb[r]));
+            for (int r = 0; r < 4; ++r) {
+              const float p = sv[2 * s2 + hh][r];
+              hb[r] = f32_to_bf16(p);
+              lb[r] = f32_to_bf16(p - bf16_to_f32(hb[r]));
+            }
+            ph[2 * hh] = pack_bf16(hb[0], hb[1]);
+            ph[2 * hh + 1] = pack_bf16(hb[2], hb[3]);
+            pl[2 * hh] = pack_bf16(lb[0], lb[1]);
+            pl[2 * hh + 1] = pack_bf16(lb[2], lb[3]);
           }
-          ph[2 * hh] = pack_bf16(hb[0], hb[1]);
-          ph[2 * hh + 1] = pack_bf16(hb[2], hb[3]);
-          pl[2 * hh] = pack_bf16(lb[0], lb[1]);
-          pl[2 * hh + 1] = pack_bf16(lb[2], lb[3]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const T* vr = Vt + (16 * dt + l16) * VS + 32 * st + 4 * g;
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
-          const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
-          o[dt] = mma_bf16(vf, ph, o[dt]);
-          o[dt] = mma_bf16(vf, pl, o[dt]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < CH / 16; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
+          // V^T rows d, tokens tg CW + 32 s2 + 4 g + [0,4) and + 16 (word columns c0, c0 + 8)
+          const int c0 = (tg * CW) / 2 + 16 * s2 + 2 * g;
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) {
-            const float vf = Vt[(16 * dt + l16) * VS + 16 * t + 4 * g + r];
-            o[dt] = mma_f32(vf, sv[t][r], o[dt]);
+            const int d = 16 * dt + l16;
+            const uint32_t* vr = reinterpret_cast<const uint32_t*>(Vt) + d * VW;
+            const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr + (c0 ^ vswz(d)));
+            const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + ((c0 + 8) ^ vswz(d)));
+            const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
+            st.o[dt] = mma_bf16(vf, ph, st.o[dt]);
+            st.o[dt] = mma_bf16(vf, pl, st.o[dt]);
           }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < CW / 16; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+              const float vf = Vt[(16 * dt + l16) * VS + tg * CW + 16 * t + 4 * g + r];
+              st.o[dt] = mma_f32(vf, sv[t][r], st.o[dt]);
+            }
+      }
     }
     __syncthreads();
   }
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  // Row sums over the four lane groups, then a tree merge of the TG states of
+  // each query tile through LDS (slots alias the K/V buffers).
+  st.l += __shfl_xor(st.l, 16, 64);
+  st.l += __shfl_xor(st.l, 32, 64);
+  constexpr int SLOT = 64 * (D / 4 + 2);  // floats per merge slot
+  float* slots = reinterpret_cast<float*>(scratch);
+#pragma unroll
+  for (int half = TG / 2; half >= 1; half /= 2) {
+    if (tg >= half && tg < 2 * half) {
+      float* sl = slots + (qt * (TG / 2) + (tg - half)) * SLOT;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) reinterpret_cast<f32x4*>(sl)[dt * 64 + lane] = st.o[dt];
+      reinterpret_cast<float2*>(sl + 64 * (D / 4))[lane] = make_float2(st.m, st.l);
+    }
+    __syncthreads();
+    if (tg < half) {
+      const float* sl = slots + (qt * (TG / 2) + tg) * SLOT;
+      f32x4 ob[D / 16];
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) ob[dt] = reinterpret_cast<const f32x4*>(sl)[dt * 64 + lane];
+      const float2 ml = reinterpret_cast<const float2*>(sl + 64 * (D / 4))[lane];
+      merge_state<D>(st, ml.x, ml.y, ob);
+    }
+    __syncthreads();
+  }
+  if (tg != 0) return;
   float* pml = a.part_ml + ((int64_t)head * a.n_split + split) * 2 * a.n_q;
   float* po = a.part_o + ((int64_t)head * a.n_split + split) * a.n_q * D;
   if (qvalid) {
     if (g == 0) {
-      pml[query] = m;
-      pml[a.n_q + query] = lsum;
+      pml[query] = st.m;
+      pml[a.n_q + query] = st.l;
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
       *reinterpret_cast<float4*>(po + (int64_t)query * D + 16 * dt + 4 * g) =
-          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+          make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
   }
 }
 
@@ -782,7 +887,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
   WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt), P.attend_lds);
+  WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt * kAttendGroups), P.attend_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rt, H), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(combine_kernel<64>, dim3(rt, H), dim3(256), 0, s, a);
