@@ -194,9 +194,9 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
   a.heads_total = (int)heads_total;
   a.n_prompt = n_prompt;
   a.head_dim = head_dim;
-  a.dtype = dtype;
+  a.bf16 = dtype == WF_BF16;
   a.levels = levels;
-  a.flags = flags;
+  a.all_levels = (flags & WF_PYR_ALL_LEVELS) != 0;
   a.base = reinterpret_cast<float*>(pyr_mem);
   if (wf::launch_pyramid(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
   out->batch = batch;

@@ -10,15 +10,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wf_types.h"
+
 namespace wf {
-
-typedef uint16_t bf16_t;  // bfloat16 storage
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // Round-to-nearest-even float32 -> bfloat16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {

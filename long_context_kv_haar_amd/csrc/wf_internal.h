@@ -5,10 +5,12 @@
 #include <stdint.h>
 
 #include "../../include/wavefilter.h"
+#include "wf_pyramid.h"
 
 namespace wf {
 
 constexpr int kMaxLevels = WF_MAX_LEVELS;
+static_assert(kMaxLevels == kPyrMaxLevels, "one level limit");
 constexpr int kAttendGroups = 4;          // waves per query tile in the attention workgroup
 constexpr int kMaxSplit = 16;             // attention splits per head
 constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to this count
@@ -16,17 +18,6 @@ constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
 constexpr int kCoverThreads = 256;
-
-struct PyramidLaunch {
-  const void* k;
-  int64_t head_stride;  // elements
-  int heads_total;      // batch * heads
-  int n_prompt, head_dim, dtype, levels;
-  uint32_t flags;
-  float* base;          // pyramid buffer
-  uint64_t band_off_a[kMaxLevels + 1];  // byte offsets, A_j (j = L at 0)
-  uint64_t band_off_d[kMaxLevels + 1];  // byte offsets, D_j
-};
 
 // Byte layout of the per-call workspace, and the resolved launch shape.
 struct SelectPlan {
@@ -63,7 +54,6 @@ struct SelectLaunch {
   uint8_t* ws;
 };
 
-hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s);
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
 
 // Tokens per attention chunk (32 per wave for bfloat16, 16 for float32).

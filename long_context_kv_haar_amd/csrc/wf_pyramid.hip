@@ -7,8 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "wf_device.h"
-#include "wf_internal.h"
+#include "wf_pyramid.h"
+#include "wf_types.h"
 
 namespace wf {
 
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void pyramid_level_kernel(const T* __restrict_
 hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
   const int L = a.levels;
   uint8_t* base = reinterpret_cast<uint8_t*>(a.base);
-  if (a.flags & WF_PYR_ALL_LEVELS) {
+  if (a.all_levels) {
     // level by level, each level reading the previous one
     for (int j = 1; j <= L; ++j) {
       const int n_out = a.n_prompt >> j;
@@ -124,7 +124,7 @@ hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
       float* a_out = reinterpret_cast<float*>(base + a.band_off_a[j]);
       float* d_out = reinterpret_cast<float*>(base + a.band_off_d[j]);
       if (j == 1) {
-        if (a.dtype == WF_BF16)
+        if (a.bf16)
           hipLaunchKernelGGL(pyramid_level_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
                              reinterpret_cast<const bf16_t*>(a.k), a.head_stride, a.heads_total, n_out,
                              a.head_dim, a_out, d_out);
@@ -144,23 +144,23 @@ hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
     if (L > 0) return hipSuccess;
     // L == 0: A_0 is the keys themselves, converted below by the streaming kernel
   }
-  const int vec_elems = (a.dtype == WF_BF16) ? 8 : 4;
+  const int vec_elems = a.bf16 ? 8 : 4;
   const int rpp = 64 / (a.head_dim / vec_elems);
   const int rows_per_item = (1 << L) > rpp ? (1 << L) : rpp;
   const int64_t items_per_head = (a.n_prompt + rows_per_item - 1) / rows_per_item;
   const int64_t items = items_per_head * a.heads_total;
   const unsigned grid = (unsigned)((items + 3) / 4);
   const float scale = (float)ldexp(1.0, -L / 2) * ((L & 1) ? 0.70710678118654752440f : 1.0f);
-#define WF_PYR(T, D)                                                                                   \
+#define PYR_LAUNCH(T, D)                                                                                   \
   hipLaunchKernelGGL((pyramid_top_kernel<T, D>), dim3(grid), dim3(256), 0, s,                         \
                      reinterpret_cast<const T*>(a.k), a.head_stride, a.heads_total, a.n_prompt, L,    \
                      rows_per_item, items_per_head, scale, a.base)
-  if (a.dtype == WF_BF16) {
-    if (a.head_dim == 128) WF_PYR(bf16_t, 128); else WF_PYR(bf16_t, 64);
+  if (a.bf16) {
+    if (a.head_dim == 128) PYR_LAUNCH(bf16_t, 128); else PYR_LAUNCH(bf16_t, 64);
   } else {
-    if (a.head_dim == 128) WF_PYR(float, 128); else WF_PYR(float, 64);
+    if (a.head_dim == 128) PYR_LAUNCH(float, 128); else PYR_LAUNCH(float, 64);
   }
-#undef WF_PYR
+#undef PYR_LAUNCH
   return hipGetLastError();
 }
 
