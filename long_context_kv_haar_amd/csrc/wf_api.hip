@@ -114,7 +114,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // refinement state or the K/V chunk buffers
   P->att_t_words = (P->n_att + 3) & ~3;
   P->refine_nmax = (nmax + 3) / 4 * 4;
-  P->refine_kmax = (kmax + 3) / 4 * 4;
+  P->refine_kmax = (kmax + 1 + 3) / 4 * 4;  // + a spare slot for rejected candidates
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
   const int64_t refine_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
   if (refine_base > budget) return WF_ERR_BUDGET;

@@ -547,158 +547,279 @@ __device__ __forceinline__ void topk_fast(KeyFn key, int n, int k, TopKFastShare
 }
 
 // ---------------------------------------------------------------------------
-// Register-resident Top-K, same rule and output as topk_fast, for
-// n <= NT * KPT keys.  Thread t holds the keys of indices [t KPT, t KPT + KPT)
-// in registers (a contiguous segment, so thread order is index order) and
-// every pass works on them, with no per-key LDS round trip.  key_at(i) reads
-// key i again, for the rare heavily tied bin that needs the multi-pass
-// search; out_reg(o, j) receives the output slot o of register slot j (a
-// compile-time constant in the unrolled loops), out_idx(o, i) the output
-// slot of index i on that fallback path.
+// Strided Top-K for n <= ACT * MAXS keys, same rule and output as topk_fast.
+// Key i lives in register slot i / ACT of thread i mod ACT, so every active
+// thread holds ceil(n / ACT) slots (balanced), and only the first ACT threads
+// (ACT / 64 waves, ideally one per SIMD) do any work: the others just meet
+// the barriers.  No per-key branches: keys that must not be counted go to a trash bin of
+// their lane (distinct LDS words, so those atomics never queue on one word).
+//  1. min and max of the keys;
+//  2. one histogram pass with bins linear in the score value over [min, max]
+//     (monotone, so a key in a higher bin is strictly greater than every key
+//     in a lower one); a scan finds bin b holding the k-th best;
+//  3. the exact key range [lo, hi] of bin b is taken: every key above hi is
+//     kept; unless bin b is kept whole, histogram passes over [lo, hi] in key
+//     space narrow the boundary until the boundary range is kept whole or
+//     holds a single key value (ties: the lowest indices win);
+//  4. compaction in index order (slot-major, thread-minor): per-slot wave
+//     ballots plus one prefix over (slot, wave) totals computed by wave 0.
+// Slots are processed in straight-line groups of four (one uniform branch
+// per group), so their LDS reads are in flight together.  load(i, j) returns
+// key i for register slot j (i < n; slots past the end get i = n - 1 and are
+// ignored) and may keep data of its own in slot j; out(o, kept, i, j) is
+// called for every slot of the used groups with its output slot o, which is
+// meaningful only when kept (the caller writes the others to a spare slot,
+// with no branch).  All NT threads must call it.
 // ---------------------------------------------------------------------------
-template <int NT, int KPT, class KeyFn, class OutReg, class OutIdx>
-__device__ __forceinline__ void topk_block(const uint32_t (&key)[KPT], int n, int k, TopKFastShared<NT>& fs, KeyFn key_at,
-                           OutReg out_reg, OutIdx out_idx) {
-  constexpr int BPT = kTopKBinsPerThread;
-  constexpr int LOGB = floor_log2(NT * BPT);
-  TopKShared<NT>& sh = fs.base;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i0 = threadIdx.x * KPT;
-  const int cnt = max(0, min(KPT, n - i0));
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (j < cnt) {
-      mn = min(mn, key[j]);
-      mx = max(mx, key[j]);
+template <int ACT, int MAXS> struct TopKSel {
+  static constexpr int W = ACT / 64;
+  static constexpr int NB = 4 * ACT;
+  int hist[NB + 64];         // NB bins, then one trash bin per lane (never read)
+  uint32_t wmn[W], wmx[W];
+  int wtot[W];
+  int cnt[MAXS * W];         // compaction: per (slot, wave) packed counts (16 + 16 bits), then prefixes
+  int bc[4];
+};
+
+template <int NT, int ACT, int MAXS, class Load, class Out>
+__device__ __forceinline__ void topk_strided(int n, int k, TopKSel<ACT, MAXS>& sh, Load load, Out out) {
+  constexpr int W = ACT / 64;
+  constexpr int NB = 4 * ACT;
+  constexpr int LOGNB = floor_log2(NB);
+  static_assert((NB & (NB - 1)) == 0 && ACT <= NT && MAXS * W <= 128, "Top-K layout");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const bool act = t < ACT;  // wave-uniform
+  const int ns = (n + ACT - 1) / ACT;
+  int4* hist4 = reinterpret_cast<int4*>(sh.hist);
+
+  // bin search: thread t < ACT owns bins [4t, 4t+4) (read and cleared here);
+  // the thread holding the want-th best key writes (bin, need in bin, count)
+  auto search = [&](int want) {
+    int4 h = make_int4(0, 0, 0, 0);
+    int incl = 0, tot = 0;
+    if (act) {
+      h = hist4[t];
+      hist4[t] = make_int4(0, 0, 0, 0);
+      tot = h.x + h.y + h.z + h.w;
+      int wt;
+      incl = wave_incl_scan(tot, &wt);
+      if (lane == 63) sh.wtot[w] = wt;
     }
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if (lane == 0) {
-    sh.wmin[w] = mn;
-    sh.wmax[w] = mx;
-  }
-  int4* own = reinterpret_cast<int4*>(sh.hist + threadIdx.x * BPT);
+    __syncthreads();
+    if (act) {
+      int base = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < BPT / 4; ++i) own[i] = make_int4(0, 0, 0, 0);
-  if (threadIdx.x == 0) fs.gcount = 0;
+      for (int i = 0; i < W; ++i) {
+        const int v = sh.wtot[i];
+        base += (i < w) ? v : 0;
+        all += v;
+      }
+      int above = all - (base + incl);  // keys in bins of higher threads
+      if (above < want && want <= above + tot) {
+        const int hv[4] = {h.x, h.y, h.z, h.w};
+        int bb = 0, rem = 0, c = 0;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const bool hit = (above < want) & (want <= above + hv[i]);
+          bb = hit ? i : bb;
+          rem = hit ? want - above : rem;
+          c = hit ? hv[i] : c;
+          above += hv[i];
+        }
+        sh.bc[0] = 4 * t + bb;
+        sh.bc[1] = rem;
+        sh.bc[2] = c;
+      }
+    }
+  };
+
+  // 1. load, min and max; clear the histogram
+  static_assert(MAXS % 4 == 0, "slot groups of four");
+  uint32_t key[MAXS];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  if (act) {
+#pragma unroll
+    for (int j0 = 0; j0 < MAXS; j0 += 4) {
+#pragma unroll
+      for (int j = j0; j < j0 + 4; ++j) key[j] = 0u;
+      if (j0 < ns) {
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) {
+          const int i = j * ACT + t;
+          const bool valid = i < n;
+          const uint32_t x = load(valid ? i : n - 1, j);
+          key[j] = valid ? x : 0u;
+          mn = min(mn, valid ? x : 0xFFFFFFFFu);
+          mx = max(mx, key[j]);
+        }
+      }
+    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+      sh.wmn[w] = mn;
+      sh.wmx[w] = mx;
+    }
+    hist4[t] = make_int4(0, 0, 0, 0);
+  }
   __syncthreads();
   mn = 0xFFFFFFFFu;
   mx = 0u;
 #pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    mn = min(mn, sh.wmin[i]);
-    mx = max(mx, sh.wmax[i]);
+  for (int i = 0; i < W; ++i) {
+    mn = min(mn, sh.wmn[i]);
+    mx = max(mx, sh.wmx[i]);
   }
-  int bn[KPT];
-  int b = 0;
-  uint32_t tk;
-  int ti;
-  if (mx == mn) {  // all keys equal: the k lowest indices
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) bn[j] = 0;
-    tk = mn;
-    ti = k - 1;
-  } else {
-    BinFn bin;
+
+  // 2./3. the boundary: keep every key > hi and `need` keys of [lo, hi]
+  int bn[MAXS];
+  uint32_t lo = mn, hi = mn;
+  int need = k;
+  if (mx != mn) {
     const float fmin = key_to_f32(mn), span = key_to_f32(mx) - fmin;
-    const float scale = (float)(1 << LOGB) / span;
+    const float scale = (float)NB / span;
+    const bool linear = span > 0.f && span < 3.0e38f && scale < 3.0e38f;
     const int bits = 32 - __clz(mx - mn);
-    bin.fmin = fmin;
-    bin.scale = scale;
-    bin.kmin = mn;
-    bin.shift = bits > LOGB ? bits - LOGB : 0;
-    bin.nb = 1 << LOGB;
-    bin.linear = span > 0.f && span < 3.0e38f && scale < 3.0e38f;
+    const int shift = bits > LOGNB ? bits - LOGNB : 0;
+    // the bin function is chosen once, outside the slot loops
+    auto pass1 = [&](auto bin_of) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      bn[j] = bin(key[j]);
-      if (j < cnt) atomicAdd(&sh.hist[bn[j]], 1);
+      for (int j0 = 0; j0 < MAXS; j0 += 4) {
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) bn[j] = -1;
+        if (j0 < ns) {
+#pragma unroll
+          for (int j = j0; j < j0 + 4; ++j) {
+            const bool valid = j * ACT + t < n;
+            const int bj = bin_of(key[j]);
+            bn[j] = valid ? bj : -1;
+            atomicAdd(&sh.hist[valid ? bj : NB + lane], 1);
+          }
+        }
+      }
+    };
+    if (act) {
+      if (linear)
+        pass1([&](uint32_t x) { return min(NB - 1, (int)((key_to_f32(x) - fmin) * scale)); });
+      else
+        pass1([&](uint32_t x) { return (int)((x - mn) >> shift); });
     }
     __syncthreads();
-    int h[BPT];
-    int tot = 0;
-#pragma unroll
-    for (int i = 0; i < BPT / 4; ++i) {
-      const int4 v = own[i];
-      h[4 * i] = v.x;
-      h[4 * i + 1] = v.y;
-      h[4 * i + 2] = v.z;
-      h[4 * i + 3] = v.w;
-      tot += v.x + v.y + v.z + v.w;
-    }
-    int all;
-    const int incl = block_incl_scan<NT>(tot, sh.wsum_a, &all);
-    int above = all - incl;
-    if (above < k && k <= above + tot) {  // exactly one thread
-      int bb = 0, rem = 0, c = 0;
-#pragma unroll
-      for (int i = BPT - 1; i >= 0; --i) {
-        const bool hit = (above < k) & (k <= above + h[i]);
-        bb = hit ? i : bb;
-        rem = hit ? k - above : rem;
-        c = hit ? h[i] : c;
-        above += h[i];
-      }
-      sh.bcast[0] = threadIdx.x * BPT + bb;
-      sh.bcast[1] = rem;
-      sh.bcast[2] = c;
-    }
+    search(k);
     __syncthreads();
-    b = sh.bcast[0];
-    const int need = sh.bcast[1], bc = sh.bcast[2];
-    tk = 0u;
-    ti = 0x7FFFFFFF;
-    if (bc != need) {
-      if (bc > kGatherMax) {  // heavily tied bin: multi-pass search over key_at
-        __syncthreads();
-        const Threshold t = select_threshold<NT>(key_at, n, k, sh);
-        topk_compact<NT>(key_at, n, t, sh, out_idx);
-        __syncthreads();
-        return;
-      }
+    const int b = sh.bc[0];
+    const int nb_need = sh.bc[1], nb_cnt = sh.bc[2];
+    {
+      // exact key range of bin b
+      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+      if (act) {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (j < cnt && bn[j] == b) {
-          const int slot = atomicAdd(&fs.gcount, 1);
-          fs.gkey[slot] = key[j];
-          fs.gidx[slot] = i0 + j;
+        for (int j = 0; j < MAXS; ++j) {  // slots past the end have bn = -1
+          const bool in = bn[j] == b;
+          kmn = min(kmn, in ? key[j] : 0xFFFFFFFFu);
+          kmx = max(kmx, in ? key[j] : 0u);
         }
-      __syncthreads();
-      if (threadIdx.x < 64) {  // rank the gathered keys; rank need-1 is the threshold
-        const bool act = lane < bc;
-        const uint32_t x = act ? fs.gkey[lane] : 0u;
-        const int xi = act ? fs.gidx[lane] : 0;
-        int rank = 0;
-        for (int m = 0; m < bc; ++m) {
-          const uint32_t y = fs.gkey[m];
-          const int yi = fs.gidx[m];
-          rank += (y > x) | ((y == x) & (yi < xi));
-        }
-        if (act && rank == need - 1) {
-          fs.tk = x;
-          fs.ti = xi;
+        kmn = wave_min_u32(kmn);
+        kmx = wave_max_u32(kmx);
+        if (lane == 0) {
+          sh.wmn[w] = kmn;
+          sh.wmx[w] = kmx;
         }
       }
       __syncthreads();
-      tk = fs.tk;
-      ti = fs.ti;
+      lo = 0xFFFFFFFFu;
+      hi = 0u;
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        lo = min(lo, sh.wmn[i]);
+        hi = max(hi, sh.wmx[i]);
+      }
+      need = nb_need;
+      // narrow [lo, hi] in key space unless bin b is kept whole; the
+      // histogram was cleared by search()
+      while (nb_cnt != nb_need && lo != hi) {
+        const uint32_t range = hi - lo;
+        const int rb = 32 - __clz(range);
+        const int s = rb > LOGNB ? rb - LOGNB : 0;
+        if (act) {
+#pragma unroll
+          for (int j0 = 0; j0 < MAXS; j0 += 4)
+            if (j0 < ns) {
+#pragma unroll
+              for (int j = j0; j < j0 + 4; ++j) {
+                const uint32_t d = key[j] - lo;  // wraps above range below lo
+                const bool in = (j * ACT + t < n) & (d <= range);
+                atomicAdd(&sh.hist[in ? (int)(d >> s) : NB + lane], 1);
+              }
+            }
+        }
+        __syncthreads();
+        search(need);
+        __syncthreads();
+        const int bb = sh.bc[0], need2 = sh.bc[1], cnt2 = sh.bc[2];
+        __syncthreads();  // every thread has read bc before the next pass rewrites it
+        lo += (uint32_t)bb << s;
+        hi = lo + (s == 0 ? 0u : min(range - ((uint32_t)bb << s), (1u << s) - 1u));
+        need = need2;
+        if (cnt2 == need2) break;  // the boundary range is kept whole
+      }
     }
   }
-  bool kept[KPT];
-  int c = 0;
+
+  // 4. compaction in index order: g = strictly above the boundary, e = in the
+  // boundary range [lo, hi] (kept while fewer than `need` precede it)
+  auto classify = [&](int j, bool& g, bool& e) {
+    const bool valid = j * ACT + t < n;
+    g = valid & (key[j] > hi);
+    e = valid & (key[j] >= lo) & (key[j] <= hi);
+  };
+  if (act) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t x = key[j];
-    kept[j] = (j < cnt) & ((bn[j] > b) | ((bn[j] == b) & ((x > tk) | ((x == tk) & (i0 + j <= ti)))));
-    c += kept[j];
+    for (int j0 = 0; j0 < MAXS; j0 += 4)
+      if (j0 < ns) {
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) {
+          bool g, e;
+          classify(j, g, e);
+          const int cg = __popcll(__ballot(g)), ce = __popcll(__ballot(e));
+          if (lane == 0) sh.cnt[j * W + w] = cg | (ce << 16);
+        }
+      }
   }
-  int all;
-  int o = block_incl_scan<NT>(c, sh.wsum_a, &all) - c;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (kept[j]) out_reg(o++, j);
   __syncthreads();
+  if (w == 0) {  // exclusive prefix over (slot, wave) in index order
+    int run = 0;
+    const int used = ((ns + 3) & ~3) * W;  // every slot of the used groups
+#pragma unroll
+    for (int base = 0; base < MAXS * W; base += 64) {
+      const int idx = base + lane;
+      const bool in = idx < used;
+      const int v = in ? sh.cnt[idx] : 0;
+      int tot;
+      const int incl = wave_incl_scan(v, &tot);
+      if (in) sh.cnt[idx] = run + incl - v;
+      run += tot;
+    }
+  }
+  __syncthreads();
+  if (act) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j0 = 0; j0 < MAXS; j0 += 4)
+      if (j0 < ns) {
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) {
+          bool g, e;
+          classify(j, g, e);  // false past the end
+          const uint64_t gm = __ballot(g), em = __ballot(e);
+          const int pre = sh.cnt[j * W + w];
+          const int G = (pre & 0xFFFF) + __popcll(gm & below);
+          const int E = (pre >> 16) + __popcll(em & below);
+          const int i = j * ACT + t;
+          out(G + min(E, need), g | (e & (E < need)), i < n ? i : n - 1, j);
+        }
+      }
+  }
 }
 
 }  // namespace wf

@@ -11,7 +11,7 @@ namespace wf {
 
 constexpr int kMaxLevels = WF_MAX_LEVELS;
 static_assert(kMaxLevels == kPyrMaxLevels, "one level limit");
-constexpr int kAttendGroups = 4;          // waves per query tile in the attention workgroup
+constexpr int kAttendGroups = 2;          // waves per query tile in the attention workgroup
 constexpr int kMaxSplit = 16;             // attention splits per head
 constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to this count
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
@@ -56,8 +56,9 @@ struct SelectLaunch {
 
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
 
-// Tokens per attention chunk (32 per wave for bfloat16, 16 for float32).
-constexpr int attend_chunk(int dtype) { return dtype == WF_BF16 ? 32 * kAttendGroups : 16 * kAttendGroups; }
+// Tokens per attention chunk; each of the kAttendGroups waves of a query
+// tile takes an equal slice.
+constexpr int attend_chunk(int dtype) { return dtype == WF_BF16 ? 128 : 64; }
 
 // LDS bytes after the attended-set list: the chunk buffers (K rows,
 // transposed V), aliased at the end by the merge slots of the wave states

@@ -147,17 +147,28 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   }
 }
 
-// Coarse Top-K with the keys in registers (n <= NT * KPT); emit(o, i) gets
-// output slot o of region i.
-template <int NT, int KPT, class Emit>
-__device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, int k, TopKFastShared<NT>& sh,
+// LDS scratch shared by every Top-K variant a workgroup of NT threads uses:
+// the strided register Top-K on min(NT, 256) threads (up to 32 slots), on
+// 512 threads (16 slots) for large workgroups, and the LDS-resident fallback.
+constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+template <int NT> struct TopKRaw {
+  static constexpr int ACT0 = NT < 256 ? NT : 256;
+  static constexpr size_t BYTES =
+      cmax(sizeof(TopKFastShared<NT>),
+           cmax(sizeof(TopKSel<ACT0, 32>), NT >= 512 ? sizeof(TopKSel<512, 16>) : size_t(0)));
+};
+
+// Coarse Top-K with the keys in registers (n <= ACT * MAXS); emit(o, i)
+// gets output slot o of region i.
+template <int NT, int ACT, int MAXS, class Emit>
+__device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, int k, unsigned char* raw,
                                                  Emit emit) {
-  const int i0 = threadIdx.x * KPT;
-  uint32_t key[KPT];
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = (i0 + j < n) ? keys_g[i0 + j] : 0u;
-  topk_block<NT, KPT>(key, n, k, sh, [&](int i) { return keys_g[i]; }, [&](int o, int j) { emit(o, i0 + j); },
-                      emit);
+  auto& sh = *reinterpret_cast<TopKSel<ACT, MAXS>*>(raw);
+  topk_strided<NT, ACT, MAXS>(
+      n, k, sh, [&](int i, int) { return keys_g[i]; },
+      [&](int o, bool kept, int i, int) {
+        if (kept) emit(o, i);
+      });
 }
 
 // ---------------------------------------------------------------------------
@@ -177,7 +188,8 @@ template <typename T, int D, int RT>
 __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   constexpr int NT = kCoverThreads;
   extern __shared__ uint32_t lds[];
-  __shared__ TopKFastShared<NT> sh;
+  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
+  auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
   const int head = blockIdx.y;
   const int L = a.levels;
   int* sel_l = reinterpret_cast<int*>(lds);  // k_top kept regions, ascending
@@ -197,14 +209,15 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
     }
   };
+  static_assert(NT == 256, "coarse Top-K layout");
   if (a.n_top <= NT * 4) {
-    coarse_topk_regs<NT, 4>(keys_g, a.n_top, a.k_top, sh, emit);
+    coarse_topk_regs<NT, NT, 4>(keys_g, a.n_top, a.k_top, tk_raw, emit);
   } else if (a.n_top <= NT * 8) {
-    coarse_topk_regs<NT, 8>(keys_g, a.n_top, a.k_top, sh, emit);
+    coarse_topk_regs<NT, NT, 8>(keys_g, a.n_top, a.k_top, tk_raw, emit);
   } else if (a.n_top <= NT * 16) {
-    coarse_topk_regs<NT, 16>(keys_g, a.n_top, a.k_top, sh, emit);
+    coarse_topk_regs<NT, NT, 16>(keys_g, a.n_top, a.k_top, tk_raw, emit);
   } else if (a.n_top <= NT * 32) {
-    coarse_topk_regs<NT, 32>(keys_g, a.n_top, a.k_top, sh, emit);
+    coarse_topk_regs<NT, NT, 32>(keys_g, a.n_top, a.k_top, tk_raw, emit);
   } else if (a.coarse_keys_in_lds) {
     for (int i = threadIdx.x; i < a.n_top; i += NT) keys_l[i] = keys_g[i];
     __syncthreads();
@@ -361,33 +374,22 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   }
 }
 
-// One refinement level with the candidates in registers (n <= NT * KPT):
-// thread t takes candidates [t KPT, t KPT + KPT), the children of kept
-// parents [t KPT / 2, (t + 1) KPT / 2), and writes the kept ones to nxt.
-template <int NT, int KPT>
+// One refinement level with the candidates in registers (n <= ACT * MAXS):
+// candidate i is child (i & 1) of kept parent cur[i >> 1]; the kept ones go
+// to nxt in ascending order, the others to its spare slot nxt[kj].
+template <int NT, int ACT, int MAXS>
 __device__ __forceinline__ void refine_level(const float* cj, int nj, const int* cur, int* nxt, int n, int kj,
-                                             TopKFastShared<NT>& sh) {
-  static_assert(KPT % 2 == 0, "children come in pairs");
-  const int i0 = threadIdx.x * KPT;
-  int pos[KPT];
-  uint32_t key[KPT];
-#pragma unroll
-  for (int m = 0; m < KPT / 2; ++m) {
-    const int par = (i0 + 2 * m < n) ? cur[i0 / 2 + m] : 0;
-    pos[2 * m] = clampi(2 * par, 0, nj - 1);
-    pos[2 * m + 1] = clampi(2 * par + 1, 0, nj - 1);
-  }
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = (i0 + j < n) ? order_key(cj[pos[j]]) : 0u;
-  auto pos_of = [&](int i) { return clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1); };
-  topk_block<NT, KPT>(
-      key, n, kj, sh, [&](int i) { return order_key(cj[pos_of(i)]); },
-      [&](int o, int j) {
-        if (o < kj) nxt[o] = pos[j];
+                                             unsigned char* raw) {
+  auto& sh = *reinterpret_cast<TopKSel<ACT, MAXS>*>(raw);
+  int pos[MAXS];
+  topk_strided<NT, ACT, MAXS>(
+      n, kj, sh,
+      [&](int i, int j) {
+        const int p = clampi(2 * cur[i >> 1] + (i & 1), 0, nj - 1);
+        pos[j] = p;
+        return order_key(cj[p]);
       },
-      [&](int o, int i) {
-        if (o < kj) nxt[o] = pos_of(i);
-      });
+      [&](int o, bool kept, int, int j) { nxt[kept ? o : kj] = pos[j]; });
 }
 
 // ---------------------------------------------------------------------------
@@ -400,8 +402,8 @@ __device__ __forceinline__ void refine_level(const float* cj, int nj, const int*
 // writes sel_out and the per-level outputs of levels L-1 .. 0.
 // ---------------------------------------------------------------------------
 template <int NT>
-__device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, TopKFastShared<NT>& sh, int* tsel,
-                            bool report) {
+__device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
+                                            int* tsel, bool report) {
   const int L = a.levels;
   uint32_t* keys = lds;
   int* cur = reinterpret_cast<int*>(lds + a.refine_nmax);
@@ -426,16 +428,21 @@ __device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_
     const int n = 2 * kprev;
     const int nj = (int)(a.covered >> j);  // level-j positions in the covered set
     const float* cj = cov + a.cov_off[j];
-    // register-resident candidates up to 8 per thread (16 for small
-    // workgroups); beyond that the keys stay in LDS
-    constexpr int KMAX = NT >= 512 ? 8 : 16;
-    if (n <= NT * 4) {
-      refine_level<NT, 4>(cj, nj, cur, nxt, n, kj, sh);
-    } else if (n <= NT * 8) {
-      refine_level<NT, 8>(cj, nj, cur, nxt, n, kj, sh);
-    } else if (KMAX >= 16 && n <= NT * 16) {
-      refine_level<NT, KMAX>(cj, nj, cur, nxt, n, kj, sh);
+    // candidates in registers on one wave per SIMD where they fit (on all
+    // threads for large sets); beyond that the keys stay in LDS
+    constexpr int A0 = TopKRaw<NT>::ACT0;
+    if (n <= A0 * 4) {
+      refine_level<NT, A0, 4>(cj, nj, cur, nxt, n, kj, tk_raw);
+    } else if (n <= A0 * 8) {
+      refine_level<NT, A0, 8>(cj, nj, cur, nxt, n, kj, tk_raw);
+    } else if (n <= A0 * 16) {
+      refine_level<NT, A0, 16>(cj, nj, cur, nxt, n, kj, tk_raw);
+    } else if (NT >= 512 && n <= 512 * 16) {
+      refine_level<NT, (NT >= 512 ? 512 : A0), 16>(cj, nj, cur, nxt, n, kj, tk_raw);
+    } else if (n <= A0 * 32) {
+      refine_level<NT, A0, 32>(cj, nj, cur, nxt, n, kj, tk_raw);
     } else {
+      auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
       for (int c = threadIdx.x; c < n; c += NT) keys[c] = order_key(cj[clampi(2 * cur[c >> 1] + (c & 1), 0, nj - 1)]);
       __syncthreads();
       topk_fast<NT>([&](int i) { return keys[i]; }, n, kj, sh, [&](int o, int i) {
@@ -520,14 +527,14 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   constexpr int PER = (CH * NV + NT - 1) / NT;    // vectors per thread per tensor
   static_assert(CW % 16 == 0 && (sizeof(T) != 2 || CW % 32 == 0), "whole MFMA tiles per wave");
   extern __shared__ uint32_t lds[];
-  __shared__ TopKFastShared<NT> sh;
+  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
   int* tlist = reinterpret_cast<int*>(lds);        // T: kept prompt tokens, then gen_idx
   uint32_t* scratch = lds + a.att_t_words;         // refinement state, K/V buffers, merge slots
   T* Ks = reinterpret_cast<T*>(scratch);
   T* Vt = Ks + CH * KS;
 
   const int head = blockIdx.y, split = blockIdx.x;
-  refine_head<NT>(a, head, scratch, sh, tlist, split == 0);
+  refine_head<NT>(a, head, scratch, tk_raw, tlist, split == 0);
   for (int i = threadIdx.x; i < a.n_gen; i += NT) tlist[a.k0 + i] = clampi(a.gen_idx[i], 0, a.n_tot - 1);
   __syncthreads();
 
@@ -576,10 +583,10 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
       const int pos = chunk * CH + row;
       kreg[i] = u32x4{0u, 0u, 0u, 0u};
       vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (e < CH * NV && pos < a.n_att) {
+      if (e < CH * NV && pos < a.n_att) {  // plain loads: the non-temporal hint slows scattered row gathers
         const int64_t tok = tlist[pos];
-        kreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + tok * D + cv * VE));
-        vreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE));
+        kreg[i] = *reinterpret_cast<const u32x4*>(kh + tok * D + cv * VE);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE);
       }
     }
   };
