@@ -116,7 +116,13 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->refine_nmax = (nmax + 3) / 4 * 4;
   P->refine_kmax = (kmax + 1 + 3) / 4 * 4;  // + a spare slot for rejected candidates
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
-  const int64_t refine_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
+  // bitmask refinement: 2 masks over the covered positions (whole groups of
+  // kMaskGroup positions), the kept coarse regions and per-level key ranges
+  P->refine_mask_words = (int)((P->covered + wf::kMaskGroup - 1) / wf::kMaskGroup * (wf::kMaskGroup / 32));
+  const int64_t mask_base = 4 * (((int64_t)P->k_top + 3) / 4 * 4 + 2 * (int64_t)P->refine_mask_words +
+                                 2 * wf::kMaxLevels * 16);
+  const int64_t list_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
+  const int64_t refine_base = list_base > mask_base ? list_base : mask_base;
   if (refine_base > budget) return WF_ERR_BUDGET;
   P->refine_cov_in_lds = (refine_base + 4 * P->cov_len) <= budget;
   const int64_t refine_bytes = refine_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0);

@@ -17,6 +17,7 @@ constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to thi
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
+constexpr int kMaskGroup = 2048;          // positions per group of four Top-K slots of up to 512 positions
 constexpr int kCoverThreads = 256;
 
 // Byte layout of the per-call workspace, and the resolved launch shape.
@@ -33,6 +34,7 @@ struct SelectPlan {
   int cover_lds;                // kept coarse regions (+ coarse keys when staged)
   int coarse_keys_in_lds;
   int refine_nmax, refine_kmax; // candidate / kept capacity (words, multiples of 4)
+  int refine_mask_words;        // words of one bitmask over the covered positions
   int refine_cov_in_lds;        // coverage scores staged in LDS
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + max(refinement state, K/V chunk buffers)

@@ -38,13 +38,13 @@ struct StepArgs {
   float* cov;            // [heads_total][cov_len]
   float* part_ml;        // [heads_total][n_split][2][n_q]
   float* part_o;         // [heads_total][n_split][n_q][d]
-  int n_q, n_top, n_prompt, n_tot, n_gen, levels;
+  int heads_total, n_q, n_top, n_prompt, n_tot, n_gen, levels;
   int k_top, k0, sum_k;
   int64_t covered, cov_len;
   int64_t cov_off[kMaxLevels];
   int budgets[kMaxLevels + 1];
   int n_att, n_chunks, n_split, chunks_per_split;
-  int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, att_t_words;
+  int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, refine_mask_words, att_t_words;
   float inv_sqrt_d;
 };
 
@@ -57,14 +57,31 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
-// Query fragments as the B operand: lane (l16, g) supplies query row
-// 16 qt + l16, quarter g of the head dimension; zero beyond n_q.
+// The query block of one head staged once per workgroup in LDS (rows padded
+// like the attention's K rows, so fragment reads are free of bank conflicts),
+// instead of every wave reading all of Q from memory.
+template <typename T> struct QueryLds;
+template <> struct QueryLds<bf16_t> { static constexpr int PAD = 8; };
+template <> struct QueryLds<float> { static constexpr int PAD = 4; };
+
+template <typename T, int D, int NT>
+__device__ __forceinline__ void stage_query(const T* qh, int n_q, T* qs) {
+  constexpr int VE = 16 / sizeof(T), NV = D / VE, QS = D + QueryLds<T>::PAD;
+  for (int e = threadIdx.x; e < n_q * NV; e += NT) {
+    const int row = e / NV, cv = e - row * NV;
+    *reinterpret_cast<u32x4*>(qs + row * QS + cv * VE) = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * D + cv * VE);
+  }
+}
+
+// Query fragments as the B operand from the staged rows: lane (l16, g)
+// supplies query row 16 qt + l16; zero beyond n_q.
 template <typename T, int D, int RT>
-__device__ __forceinline__ void load_query_frags(const T* qh, int n_q, int l16, int g, Frag<T, D> (&qf)[RT]) {
+__device__ __forceinline__ void load_query_frags(const T* qs, int n_q, int l16, int g, Frag<T, D> (&qf)[RT]) {
+  constexpr int QS = D + QueryLds<T>::PAD;
 #pragma unroll
   for (int qt = 0; qt < RT; ++qt) {
     const int row = 16 * qt + l16;
-    if (row < n_q) qf[qt].load(qh + (int64_t)row * D, g);
+    if (row < n_q) qf[qt].load(qs + row * QS, g);
     else qf[qt].zero();
   }
 }
@@ -79,12 +96,10 @@ __device__ __forceinline__ void load_query_frags(const T* qh, int n_q, int l16, 
 // ---------------------------------------------------------------------------
 template <typename T, int D, int RT>
 __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
+  __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   const int head = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
-  const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
-  Frag<T, D> qf[RT];
-  load_query_frags<T, D, RT>(qh, a.n_q, l16, g, qf);
 
   const int n = blockIdx.x * 64 + w * 16 + l16;  // region supplied by this lane (A operand)
   const bool valid = n < a.n_top;
@@ -100,6 +115,11 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
 #pragma unroll
     for (int i = 0; i < 2 * STEPS; ++i)
       x[i] = valid ? p[8 * (i >> 1) + 2 * g + (i & 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
+    // Q staged while the coefficient rows are in flight
+    stage_query<T, D, 256>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+    __syncthreads();
+    Frag<T, D> qf[RT];
+    load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       u32x4 hi, lo;
@@ -126,6 +146,10 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   } else {
     Frag<float, D> b;
     if (valid) b.load(arow, g); else b.zero();
+    stage_query<T, D, 256>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+    __syncthreads();
+    Frag<T, D> qf[RT];
+    load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
 #pragma unroll
     for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(b, qf[qt], acc[qt]);
   }
@@ -153,8 +177,10 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
 constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
 template <int NT> struct TopKRaw {
   static constexpr int ACT0 = NT < 256 ? NT : 256;
+  static constexpr int MACT = 1 << floor_log2(NT);     // mask Top-K threads (a power of two)
+  static constexpr int MMAX = MACT >= 512 ? 16 : 32;   // and its slots per thread
   static constexpr size_t BYTES =
-      cmax(sizeof(TopKFastShared<NT>),
+      cmax(cmax(sizeof(TopKFastShared<NT>), sizeof(TopKMaskShared<MACT, MMAX>)),
            cmax(sizeof(TopKSel<ACT0, 32>), NT >= 512 ? sizeof(TopKSel<512, 16>) : size_t(0)));
 };
 
@@ -189,7 +215,10 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   constexpr int NT = kCoverThreads;
   extern __shared__ uint32_t lds[];
   __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
+  __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
+  // the query block, staged now and read after the Top-K's barriers
+  if (a.levels > 0) stage_query<T, D, NT>(reinterpret_cast<const T*>(a.q) + (int64_t)blockIdx.y * a.n_q * D, a.n_q, qs);
   const int head = blockIdx.y;
   const int L = a.levels;
   int* sel_l = reinterpret_cast<int*>(lds);  // k_top kept regions, ascending
@@ -233,9 +262,8 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t wave_base = (int64_t)blockIdx.x * 256 + w * 64;
   if (wave_base >= a.covered) return;  // no workgroup barrier below
-  const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
   Frag<T, D> qf[RT];
-  load_query_frags<T, D, RT>(qh, a.n_q, l16, g, qf);
+  load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
 
   const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
   Frag<T, D> kf[4];
@@ -402,8 +430,8 @@ __device__ __forceinline__ void refine_level(const float* cj, int nj, const int*
 // writes sel_out and the per-level outputs of levels L-1 .. 0.
 // ---------------------------------------------------------------------------
 template <int NT>
-__device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
-                                            int* tsel, bool report) {
+__device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
+                                                  int* tsel, bool report) {
   const int L = a.levels;
   uint32_t* keys = lds;
   int* cur = reinterpret_cast<int*>(lds + a.refine_nmax);
@@ -474,6 +502,166 @@ __device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_
     if (so) so[o] = tok;
   }
   __syncthreads();
+}
+
+// Emits the set bits of mask[0 .. nbits) in ascending order: emit(o, p) for
+// the o-th set bit p.  Thread t takes bytes [t B, t B + B) of the mask, one
+// workgroup scan gives its output offset.  Ends with a workgroup barrier.
+template <int NT, class Emit>
+__device__ __forceinline__ void mask_compact(const uint32_t* mask, int nbits, int* wsum, Emit emit) {
+  const int nbytes = (nbits + 7) >> 3;
+  const int per = (nbytes + NT - 1) / NT;
+  const int b0 = min(nbytes, (int)threadIdx.x * per), b1 = min(nbytes, b0 + per);
+  const uint8_t* mb = reinterpret_cast<const uint8_t*>(mask);
+  int c = 0;
+  for (int i = b0; i < b1; ++i) c += __popc(mb[i]);
+  int all;
+  int o = block_incl_scan<NT>(c, wsum, &all) - c;
+  for (int i = b0; i < b1; ++i) {
+    uint32_t x = mb[i];
+    while (x) {
+      const int bit = __ffs(x) - 1;
+      x &= x - 1;
+      emit(o++, 8 * i + bit);
+    }
+  }
+  __syncthreads();
+}
+
+// One refinement level with the kept set as a bitmask: candidates are the
+// level-j positions whose parent (p >> 1) is set in `prev`; the kept ones are
+// set in `next`.
+template <int NT, int MAXS>
+__device__ __forceinline__ void refine_level_mask(const float* cj, int n, int kj, uint32_t kmin, uint32_t kmax,
+                                                  const uint32_t* prev, uint32_t* next, unsigned char* raw) {
+  // the bins sit at the same offset for every MAXS (they depend on ACT only)
+  constexpr int ACT = TopKRaw<NT>::MACT;
+  auto& shm = *reinterpret_cast<TopKMaskShared<ACT, MAXS>*>(raw);
+  topk_mask<NT, ACT, MAXS>(
+      n, kj, kmin, kmax, shm, [&](int p, int) { return order_key(cj[p]); },
+      [&](int p) {
+        const int q = p >> 1;  // the parent at level j + 1
+        return ((prev[q >> 5] >> (q & 31)) & 1u) != 0u;
+      },
+      next);
+}
+
+// Recursive refinement with bitmask kept sets (covered <= MACT * MMAX).
+// LDS: [coverage scores] | sel_L | mask A | mask B | per-level key range.
+template <int NT>
+__device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
+                                                 int* tsel, bool report) {
+  constexpr int W = NT / 64;
+  const int L = a.levels;
+  const int covered = (int)a.covered;
+  float* cov_l = reinterpret_cast<float*>(lds);
+  int* sel_l = reinterpret_cast<int*>(lds + (a.refine_cov_in_lds ? a.cov_len : 0));
+  uint32_t* mask_a = reinterpret_cast<uint32_t*>(sel_l + ((a.k_top + 3) & ~3));
+  uint32_t* mask_b = mask_a + a.refine_mask_words;
+  uint32_t* lvmn = mask_b + a.refine_mask_words;  // [kMaxLevels][W]
+  uint32_t* lvmx = lvmn + kMaxLevels * W;
+  const float* cov_g = a.cov + (int64_t)head * a.cov_len;
+  const float* cov = a.refine_cov_in_lds ? cov_l : cov_g;
+  const int32_t* sel_top = a.sel_top + (int64_t)head * a.k_top;
+  auto& shm = *reinterpret_cast<TopKMaskShared<TopKRaw<NT>::MACT, TopKRaw<NT>::MMAX>*>(tk_raw);
+  if (a.refine_cov_in_lds) {
+    const float4* src = reinterpret_cast<const float4*>(cov_g);
+    float4* dst = reinterpret_cast<float4*>(cov_l);
+    const int n4 = (int)(a.cov_len / 4);
+    for (int i = threadIdx.x; i < n4; i += NT) dst[i] = src[i];
+  }
+  for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_top[i], 0, a.n_top - 1);
+  for (int i = threadIdx.x; i < a.refine_mask_words; i += NT)  // level L: every kept coarse region
+    mask_a[i] = (32 * i + 32 <= a.k_top) ? 0xFFFFFFFFu : (32 * i < a.k_top ? (1u << (a.k_top - 32 * i)) - 1u : 0u);
+  topk_mask_init<NT, TopKRaw<NT>::MACT, TopKRaw<NT>::MMAX>(shm);
+  __syncthreads();
+  // per-level key range over every covered position of the level
+  {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < kMaxLevels; ++j)
+      if (j < L) {
+        const float* cj = cov + a.cov_off[j];
+        const int nj = covered >> j;
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+        for (int p0 = threadIdx.x; p0 < nj; p0 += 4 * NT) {  // four reads in flight
+          float x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = cj[min(p0 + u * NT, nj - 1)];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t kx = order_key(x[u]);
+            mn = min(mn, kx);
+            mx = max(mx, kx);
+          }
+        }
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+        if (lane == 0) {
+          lvmn[j * W + w] = mn;
+          lvmx[j * W + w] = mx;
+        }
+      }
+  }
+  __syncthreads();
+  int32_t* dbg_sel = (report && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = (report && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  uint32_t* prev = mask_a;
+  uint32_t* next = mask_b;
+  int dbg_off = a.k_top;
+  for (int j = L - 1; j >= 0; --j) {
+    const int kj = a.budgets[L - j];
+    const int nj = covered >> j;
+    const float* cj = cov + a.cov_off[j];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      kmin = min(kmin, lvmn[j * W + i]);
+      kmax = max(kmax, lvmx[j * W + i]);
+    }
+    constexpr int MM = TopKRaw<NT>::MMAX, MA = TopKRaw<NT>::MACT;
+    if (nj <= MA * 4) {
+      refine_level_mask<NT, 4>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+    } else if (nj <= MA * 8) {
+      refine_level_mask<NT, 8>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+    } else if (MM <= 16 || nj <= MA * 16) {
+      refine_level_mask<NT, 16>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+    } else {
+      refine_level_mask<NT, MM>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+    }
+    if (dbg_sel || dbg_score) {
+      const int sh_l = L - j;
+      mask_compact<NT>(next, nj, shm.cnt, [&](int o, int p) {
+        if (o < kj) {
+          if (dbg_sel) dbg_sel[dbg_off + o] = (sel_l[clampi(p >> sh_l, 0, a.k_top - 1)] << sh_l) + (p & ((1 << sh_l) - 1));
+          if (dbg_score) dbg_score[dbg_off + o] = cj[p];
+        }
+      });
+    }
+    uint32_t* tmp = prev;
+    prev = next;
+    next = tmp;
+    dbg_off += kj;
+  }
+  int32_t* so = (report && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  mask_compact<NT>(prev, covered, shm.cnt, [&](int o, int p) {
+    if (o < a.k0) {
+      const int tok = (sel_l[clampi(p >> L, 0, a.k_top - 1)] << L) + (p & ((1 << L) - 1));
+      tsel[o] = tok;
+      if (so) so[o] = tok;
+    }
+  });
+}
+
+// Recursive refinement (Figure 2 (d)) for one head: bitmask kept sets when
+// the covered set fits the register Top-K, else sorted index lists in LDS.
+template <int NT>
+__device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
+                                            int* tsel, bool report) {
+  if (a.covered <= (int64_t)TopKRaw<NT>::MACT * TopKRaw<NT>::MMAX && a.levels > 0)
+    refine_head_mask<NT>(a, head, lds, tk_raw, tsel, report);
+  else
+    refine_head_lists<NT>(a, head, lds, tk_raw, tsel, report);
 }
 
 // ---------------------------------------------------------------------------
@@ -746,68 +934,48 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
 
 // ---------------------------------------------------------------------------
 // Merge of the split partials: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s,
-// M = max_s m_s (m in log2 units).  Block (x, head) merges 16 query rows.
+// M = max_s m_s (m in log2 units; an empty split has m = -inf, l = 0).
+// Thread = one float4 of the output (head, query, 4 columns), so the whole
+// merge is one round of independent loads spread over the chip.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
-  constexpr int FPT = (16 * D / 4 + 255) / 256;  // float4 outputs per thread
-  __shared__ float wgt[16][kMaxSplit];
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * 16;
-  const int nq = min(16, a.n_q - q0);
+  constexpr int C4 = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_head = (int64_t)a.n_q * C4;
+  if (idx >= per_head * a.heads_total) return;
+  const int head = (int)(idx / per_head);
+  const int rem = (int)(idx - head * per_head);
+  const int query = rem / C4, c4 = rem - query * C4;
   const int ns = a.n_split;
   const float* ml = a.part_ml + (int64_t)head * ns * 2 * a.n_q;
-  if (threadIdx.x < nq) {
-    const int qi = q0 + threadIdx.x;
-    float mv[kMaxSplit], lv[kMaxSplit];
+  const float* po = a.part_o + ((int64_t)head * ns * a.n_q + query) * D + 4 * c4;
+  float mv[kMaxSplit], lv[kMaxSplit];
+  float4 ov[kMaxSplit];
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {  // every load issued before any is used
-      mv[sp] = sp < ns ? ml[sp * 2 * a.n_q + qi] : -INFINITY;
-      lv[sp] = sp < ns ? ml[sp * 2 * a.n_q + a.n_q + qi] : 0.f;
-    }
-    float mm = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
-    float den = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {
-      mv[sp] = sp < ns ? exp2f(mv[sp] - mm) : 0.f;
-      den += mv[sp] * lv[sp];
-    }
-    const float inv = 1.0f / den;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) wgt[threadIdx.x][sp] = mv[sp] * inv;
+  for (int sp = 0; sp < kMaxSplit; ++sp) {  // every load issued before any is used
+    const bool in = sp < ns;
+    mv[sp] = in ? ml[sp * 2 * a.n_q + query] : -INFINITY;
+    lv[sp] = in ? ml[sp * 2 * a.n_q + a.n_q + query] : 0.f;
+    ov[sp] = in ? *reinterpret_cast<const float4*>(po + (int64_t)sp * a.n_q * D) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float* pob = a.part_o + (int64_t)head * ns * a.n_q * D;
-  float4 x[FPT][kMaxSplit];
+  float mm = -INFINITY;
 #pragma unroll
-  for (int f = 0; f < FPT; ++f) {
-    const int e = threadIdx.x + f * 256;
-    const int ql = e / (D / 4), c4 = e - ql * (D / 4);
+  for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
+  float den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp)
-      x[f][sp] = (sp < ns && ql < nq)
-                     ? *reinterpret_cast<const float4*>(pob + ((int64_t)sp * a.n_q + q0 + ql) * D + 4 * c4)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    const float wv = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - mm);
+    den += wv * lv[sp];
+    acc.x += wv * ov[sp].x;
+    acc.y += wv * ov[sp].y;
+    acc.z += wv * ov[sp].z;
+    acc.w += wv * ov[sp].w;
   }
-  __syncthreads();
-  float* outh = a.out + (int64_t)head * a.n_q * D;
-#pragma unroll
-  for (int f = 0; f < FPT; ++f) {
-    const int e = threadIdx.x + f * 256;
-    const int ql = e / (D / 4), c4 = e - ql * (D / 4);
-    if (ql >= nq) continue;
-    float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {
-      const float wv = sp < ns ? wgt[ql][sp] : 0.f;
-      acc4.x += wv * x[f][sp].x;
-      acc4.y += wv * x[f][sp].y;
-      acc4.z += wv * x[f][sp].z;
-      acc4.w += wv * x[f][sp].w;
-    }
-    *reinterpret_cast<float4*>(outh + (int64_t)(q0 + ql) * D + 4 * c4) = acc4;
-  }
+  const float inv = 1.0f / den;
+  *reinterpret_cast<float4*>(a.out + ((int64_t)head * a.n_q + query) * D + 4 * c4) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -835,6 +1003,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.cov = reinterpret_cast<float*>(L.ws + P.off_cov);
   a.part_ml = reinterpret_cast<float*>(L.ws + P.off_part_ml);
   a.part_o = reinterpret_cast<float*>(L.ws + P.off_part_o);
+  a.heads_total = P.heads_total;
   a.n_q = P.n_q;
   a.n_top = P.n_top;
   a.n_prompt = P.n_prompt;
@@ -856,6 +1025,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.refine_cov_in_lds = P.refine_cov_in_lds;
   a.refine_nmax = P.refine_nmax;
   a.refine_kmax = P.refine_kmax;
+  a.refine_mask_words = P.refine_mask_words;
   a.att_t_words = P.att_t_words;
   a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
 
@@ -896,8 +1066,9 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt * kAttendGroups), P.attend_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(rt, H), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(combine_kernel<64>, dim3(rt, H), dim3(256), 0, s, a);
+  const unsigned comb_blocks = (unsigned)(((int64_t)H * P.n_q * (P.head_dim / 4) + 255) / 256);
+  if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 #undef WF_RT_SWITCH
 #undef WF_LAUNCH
