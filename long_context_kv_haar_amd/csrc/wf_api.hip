@@ -120,7 +120,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // kMaskGroup positions), the kept coarse regions and per-level key ranges
   P->refine_mask_words = (int)((P->covered + wf::kMaskGroup - 1) / wf::kMaskGroup * (wf::kMaskGroup / 32));
   const int64_t mask_base = 4 * (((int64_t)P->k_top + 3) / 4 * 4 + 2 * (int64_t)P->refine_mask_words +
-                                 2 * wf::kMaxLevels * 16);
+                                 2 * wf::kMaxLevels);
   const int64_t list_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
   const int64_t refine_base = list_base > mask_base ? list_base : mask_base;
   if (refine_base > budget) return WF_ERR_BUDGET;
@@ -135,6 +135,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
+  P->off_lvl = w;      w += align_up(H * (uint64_t)((P->covered + 63) / 64) * wf::kMaxLevels * 2 * 4);
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * P->head_dim * 4);
   P->total = w;

@@ -858,9 +858,9 @@ __device__ __forceinline__ void topk_mask_init(TopKMaskShared<ACT, MAXS>& sh) {
   for (int i = threadIdx.x; i < 4 * ACT; i += NT) sh.hist[i] = 0;
 }
 
-template <int NT, int ACT, int MAXS, class KeyFn, class ValidFn>
-__device__ __forceinline__ void topk_mask(int n, int k, uint32_t kmin, uint32_t kmax, TopKMaskShared<ACT, MAXS>& sh,
-                                          KeyFn key_of, ValidFn valid_of, uint32_t* mask_out) {
+template <int NT, int ACT, int MAXS, class ScoreFn, class ValidFn>
+__device__ __forceinline__ void topk_mask(int n, int k, float smin, float smax, TopKMaskShared<ACT, MAXS>& sh,
+                                          ScoreFn score_of, ValidFn valid_of, uint32_t* mask_out) {
   constexpr int W = ACT / 64;
   constexpr int NB = 4 * ACT;
   constexpr int LOGNB = floor_log2(NB);
@@ -872,58 +872,61 @@ __device__ __forceinline__ void topk_mask(int n, int k, uint32_t kmin, uint32_t 
   const int ns = (n + ACT - 1) / ACT;
 
   // wave 0 finds the bin of the want-th best, publishes (bin, need, count),
-  // clears the bins; ends with a barrier
+  // clears the bins; ends with a barrier.  Two wave scans, no serial walk:
+  // the first over the lanes' totals (lane l owns bins [BPL l, BPL l + BPL))
+  // finds the owner lane T of the boundary, the second spreads T's bins over
+  // lanes and finds the bin.
   auto search = [&](int want) {
     if (w == 0) {
       int4* h4 = reinterpret_cast<int4*>(sh.hist + BPL * lane);
-      int hv[BPL];
       int tot = 0;
 #pragma unroll
       for (int q = 0; q < BPL / 4; ++q) {
         const int4 v = h4[q];
-        hv[4 * q] = v.x;
-        hv[4 * q + 1] = v.y;
-        hv[4 * q + 2] = v.z;
-        hv[4 * q + 3] = v.w;
         tot += v.x + v.y + v.z + v.w;
-        h4[q] = make_int4(0, 0, 0, 0);
       }
       int all;
       const int incl = wave_incl_scan(tot, &all);
-      int above = all - incl;  // keys in bins of higher lanes
-      if (above < want && want <= above + tot) {
-        int bb = 0, rem = 0, c = 0;
-#pragma unroll
-        for (int i = BPL - 1; i >= 0; --i) {
-          const bool hit = (above < want) & (want <= above + hv[i]);
-          bb = hit ? i : bb;
-          rem = hit ? want - above : rem;
-          c = hit ? hv[i] : c;
-          above += hv[i];
-        }
-        sh.bc[0] = BPL * lane + bb;
-        sh.bc[1] = rem;
+      const int above = all - incl;  // keys in bins of higher lanes
+      const uint64_t hitm = __ballot((above < want) & (want <= above + tot));
+      const int owner = (int)__ffsll((unsigned long long)hitm) - 1;  // exactly one lane
+      const int above_t = __shfl(above, owner, 64);
+      // bins of the owner: lane l < BPL takes bin BPL * owner + l
+      const int c = (lane < BPL) ? sh.hist[BPL * owner + lane] : 0;
+      int all2;
+      const int incl2 = wave_incl_scan(c, &all2);
+      const int hi_cnt = above_t + (all2 - incl2);  // keys in higher bins of the owner and above
+      const bool hit = (lane < BPL) & (hi_cnt < want) & (want <= hi_cnt + c);
+      const uint64_t hm = __ballot(hit);
+      if (hit) {
+        sh.bc[0] = BPL * owner + lane;
+        sh.bc[1] = want - hi_cnt;
         sh.bc[2] = c;
       }
+      (void)hm;
+#pragma unroll
+      for (int q = 0; q < BPL / 4; ++q) h4[q] = make_int4(0, 0, 0, 0);
     }
     __syncthreads();
   };
 
-  // 1. keys, validity, bins
-  uint32_t key[MAXS];
+  // 1. scores, validity, bins (linear in the value over [smin, smax], or, for
+  // a degenerate span, in the order-preserving integer key)
+  float sc[MAXS];
   bool valid[MAXS];
   int bn[MAXS];
-  const float fmin = key_to_f32(kmin), span = key_to_f32(kmax) - fmin;
+  const float span = smax - smin;
   const float scale = (float)NB / span;
   const bool linear = span > 0.f && span < 3.0e38f && scale < 3.0e38f;
-  const uint32_t krange = kmax - kmin;
+  const uint32_t kmin = order_key(smin);
+  const uint32_t krange = order_key(smax) - kmin;
   const int kshift = (32 - __clz(krange)) > LOGNB ? (32 - __clz(krange)) - LOGNB : 0;
   if (act) {
 #pragma unroll
     for (int j0 = 0; j0 < MAXS; j0 += 4) {
 #pragma unroll
       for (int j = j0; j < j0 + 4; ++j) {
-        key[j] = 0u;
+        sc[j] = 0.f;
         valid[j] = false;
         bn[j] = -1;
       }
@@ -932,18 +935,17 @@ __device__ __forceinline__ void topk_mask(int n, int k, uint32_t kmin, uint32_t 
         for (int j = j0; j < j0 + 4; ++j) {
           const int p = j * ACT + t;
           const int pc = p < n ? p : n - 1;
-          const bool v = (p < n) && valid_of(pc);
-          const uint32_t x = key_of(pc, j);
-          key[j] = x;
-          valid[j] = v;
+          valid[j] = (p < n) && valid_of(pc);
+          sc[j] = score_of(pc, j);
         }
         if (linear) {
 #pragma unroll
           for (int j = j0; j < j0 + 4; ++j)
-            bn[j] = valid[j] ? min(NB - 1, max(0, (int)((key_to_f32(key[j]) - fmin) * scale))) : -1;
+            bn[j] = valid[j] ? min(NB - 1, max(0, (int)((sc[j] - smin) * scale))) : -1;
         } else {
 #pragma unroll
-          for (int j = j0; j < j0 + 4; ++j) bn[j] = valid[j] ? (int)(min(key[j] - kmin, krange) >> kshift) : -1;
+          for (int j = j0; j < j0 + 4; ++j)
+            bn[j] = valid[j] ? (int)(min(order_key(sc[j]) - kmin, krange) >> kshift) : -1;
         }
 #pragma unroll
         for (int j = j0; j < j0 + 4; ++j)
@@ -971,7 +973,7 @@ __device__ __forceinline__ void topk_mask(int n, int k, uint32_t kmin, uint32_t 
         if (j0 < ns) {
 #pragma unroll
           for (int j = j0; j < j0 + 4; ++j) {
-            const float fr = (key_to_f32(key[j]) - fmin) * scale - (float)b;
+            const float fr = (sc[j] - smin) * scale - (float)b;
             sub[j] = min(NB - 1, max(0, (int)(fr * (float)NB)));
             if (bn[j] == b) atomicAdd(&sh.hist[sub[j]], 1);
           }
@@ -990,7 +992,10 @@ __device__ __forceinline__ void topk_mask(int n, int k, uint32_t kmin, uint32_t 
   // 3. exact key range of the boundary class, then key-space narrowing
   uint32_t lo = 0u, hi = 0u;
   bool tie = false;
+  uint32_t key[MAXS];  // order-preserving keys, for the exact path only
   if (mode == 3) {
+#pragma unroll
+    for (int j = 0; j < MAXS; ++j) key[j] = order_key(sc[j]);
     const bool two = linear;  // the class is (bin b, sub-bin sb) after step 2, else bin b
     auto in_class = [&](int j) { return (bn[j] == b) & (!two | (sub[j] == sb)); };
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;

@@ -39,7 +39,7 @@ struct SelectPlan {
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + max(refinement state, K/V chunk buffers)
   // workspace sections (byte offsets)
-  uint64_t off_keys, off_sel_top, off_cov, off_part_ml, off_part_o, total;
+  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_part_ml, off_part_o, total;
 };
 
 struct SelectLaunch {

@@ -36,6 +36,8 @@ struct StepArgs {
   uint32_t* keys_top;    // [heads_total][n_top]
   int32_t* sel_top;      // [heads_total][k_top]
   float* cov;            // [heads_total][cov_len]
+  uint32_t* lvl_mm;      // [heads_total][cover waves][kMaxLevels][2]: order keys of each level's least and
+                         // greatest score over the positions of one coverage wave
   float* part_ml;        // [heads_total][n_split][2][n_q]
   float* part_o;         // [heads_total][n_split][n_q][d]
   int heads_total, n_q, n_top, n_prompt, n_tot, n_gen, levels;
@@ -292,7 +294,26 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   const float isd = a.inv_sqrt_d;
   const bool writer = (l16 == 0);
   const int64_t tb = wave_base + 4 * g;  // first position of this row in tile 0
+  // each level's least and greatest score over the wave, one slot per wave
+  const int nwav = (int)((a.covered + 63) >> 6);
+  uint32_t* lvl = a.lvl_mm + ((int64_t)head * nwav + (wave_base >> 6)) * 2 * kMaxLevels;
+  uint32_t rmn, rmx;
+  auto track = [&](bool in, float v) {
+    const uint32_t k = order_key(v);
+    rmn = in ? min(rmn, k) : rmn;
+    rmx = in ? max(rmx, k) : rmx;
+  };
+  auto publish = [&](int j) {
+    rmn = wave_min_u32(rmn);
+    rmx = wave_max_u32(rmx);
+    if (lane == 0) {
+      lvl[2 * j] = rmn;
+      lvl[2 * j + 1] = rmx;
+    }
+  };
   // level 0
+  rmn = 0xFFFFFFFFu;
+  rmx = 0u;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     float m[4];
@@ -306,9 +327,14 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
     const int64_t p = tb + 16 * t;
     if (writer && p < a.covered)
       *reinterpret_cast<float4*>(cov + a.cov_off[0] + p) = make_float4(m[0], m[1], m[2], m[3]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) track(writer && p + r < a.covered, m[r]);
   }
+  publish(0);
   if (jmax <= 1) return;
   // level 1: token pairs (r = 0,1 and 2,3), in place into s[t][qt][0] and [2]
+  rmn = 0xFFFFFFFFu;
+  rmx = 0u;
   {
     const float sc = isd * 0.70710678118654752440f;
 #pragma unroll
@@ -329,10 +355,15 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       const int64_t p = tb + 16 * t;
       if (writer && p < a.covered)
         *reinterpret_cast<float2*>(cov + a.cov_off[1] + (p >> 1)) = make_float2(m[0], m[1]);
+      track(writer && p < a.covered, m[0]);
+      track(writer && p + 2 < a.covered, m[1]);
     }
   }
+  publish(1);
   if (jmax <= 2) return;
   // level 2: 4-token blocks (one per lane group), into s[t][qt][0]
+  rmn = 0xFFFFFFFFu;
+  rmx = 0u;
   {
     const float sc = isd * 0.5f;
 #pragma unroll
@@ -345,10 +376,14 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       x = row_max16(x) * sc;
       const int64_t p = tb + 16 * t;
       if (writer && p < a.covered) cov[a.cov_off[2] + (p >> 2)] = x;
+      track(writer && p < a.covered, x);
     }
   }
+  publish(2);
   if (jmax <= 3) return;
   // level 3: 8-token blocks = lane groups {0,1} and {2,3}
+  rmn = 0xFFFFFFFFu;
+  rmx = 0u;
   {
     const float sc = isd * 0.35355339059327376220f;
 #pragma unroll
@@ -361,10 +396,14 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       x = row_max16(x) * sc;
       const int64_t p = tb + 16 * t;
       if (writer && (g & 1) == 0 && p < a.covered) cov[a.cov_off[3] + (p >> 3)] = x;
+      track(writer && (g & 1) == 0 && p < a.covered, x);
     }
   }
+  publish(3);
   if (jmax <= 4) return;
   // level 4: 16-token blocks = whole tiles
+  rmn = 0xFFFFFFFFu;
+  rmx = 0u;
   {
     const float sc = isd * 0.25f;
 #pragma unroll
@@ -377,8 +416,10 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       x = row_max16(x) * sc;
       const int64_t p = wave_base + 16 * t;
       if (writer && g == 0 && p < a.covered) cov[a.cov_off[4] + (p >> 4)] = x;
+      track(writer && g == 0 && p < a.covered, x);
     }
   }
+  publish(4);
   if (jmax <= 5) return;
   // level 5: tile pairs; level 6: the whole wave
   {
@@ -398,6 +439,17 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       if (wave_base < a.covered) cov[a.cov_off[5] + (wave_base >> 5)] = x01;
       if (wave_base + 32 < a.covered) cov[a.cov_off[5] + (wave_base >> 5) + 1] = x23;
       if (jmax > 6) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
+    }
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(lane == 0 && wave_base < a.covered, x01);
+    track(lane == 0 && wave_base + 32 < a.covered, x23);
+    publish(5);
+    if (jmax > 6) {
+      rmn = 0xFFFFFFFFu;
+      rmx = 0u;
+      track(lane == 0, xall);
+      publish(6);
     }
   }
 }
@@ -532,13 +584,13 @@ __device__ __forceinline__ void mask_compact(const uint32_t* mask, int nbits, in
 // level-j positions whose parent (p >> 1) is set in `prev`; the kept ones are
 // set in `next`.
 template <int NT, int MAXS>
-__device__ __forceinline__ void refine_level_mask(const float* cj, int n, int kj, uint32_t kmin, uint32_t kmax,
+__device__ __forceinline__ void refine_level_mask(const float* cj, int n, int kj, float smin, float smax,
                                                   const uint32_t* prev, uint32_t* next, unsigned char* raw) {
   // the bins sit at the same offset for every MAXS (they depend on ACT only)
   constexpr int ACT = TopKRaw<NT>::MACT;
   auto& shm = *reinterpret_cast<TopKMaskShared<ACT, MAXS>*>(raw);
   topk_mask<NT, ACT, MAXS>(
-      n, kj, kmin, kmax, shm, [&](int p, int) { return order_key(cj[p]); },
+      n, kj, smin, smax, shm, [&](int p, int) { return cj[p]; },
       [&](int p) {
         const int q = p >> 1;  // the parent at level j + 1
         return ((prev[q >> 5] >> (q & 31)) & 1u) != 0u;
@@ -551,15 +603,13 @@ __device__ __forceinline__ void refine_level_mask(const float* cj, int n, int kj
 template <int NT>
 __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
                                                  int* tsel, bool report) {
-  constexpr int W = NT / 64;
   const int L = a.levels;
   const int covered = (int)a.covered;
   float* cov_l = reinterpret_cast<float*>(lds);
   int* sel_l = reinterpret_cast<int*>(lds + (a.refine_cov_in_lds ? a.cov_len : 0));
   uint32_t* mask_a = reinterpret_cast<uint32_t*>(sel_l + ((a.k_top + 3) & ~3));
   uint32_t* mask_b = mask_a + a.refine_mask_words;
-  uint32_t* lvmn = mask_b + a.refine_mask_words;  // [kMaxLevels][W]
-  uint32_t* lvmx = lvmn + kMaxLevels * W;
+  uint32_t* lvm = mask_b + a.refine_mask_words;  // [kMaxLevels][2]: each level's score range (order keys)
   const float* cov_g = a.cov + (int64_t)head * a.cov_len;
   const float* cov = a.refine_cov_in_lds ? cov_l : cov_g;
   const int32_t* sel_top = a.sel_top + (int64_t)head * a.k_top;
@@ -571,38 +621,27 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
     for (int i = threadIdx.x; i < n4; i += NT) dst[i] = src[i];
   }
   for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_top[i], 0, a.n_top - 1);
+  {  // each level's score range: wave j reduces the coverage waves' slots of level j
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nwav = (int)((a.covered + 63) >> 6);
+    const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
+    for (int j = w; j < L; j += NT / 64) {
+      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+      for (int v = lane; v < nwav; v += 64) {
+        mn = min(mn, lm[(int64_t)v * 2 * kMaxLevels + 2 * j]);
+        mx = max(mx, lm[(int64_t)v * 2 * kMaxLevels + 2 * j + 1]);
+      }
+      mn = wave_min_u32(mn);
+      mx = wave_max_u32(mx);
+      if (lane == 0) {
+        lvm[2 * j] = mn;
+        lvm[2 * j + 1] = mx;
+      }
+    }
+  }
   for (int i = threadIdx.x; i < a.refine_mask_words; i += NT)  // level L: every kept coarse region
     mask_a[i] = (32 * i + 32 <= a.k_top) ? 0xFFFFFFFFu : (32 * i < a.k_top ? (1u << (a.k_top - 32 * i)) - 1u : 0u);
   topk_mask_init<NT, TopKRaw<NT>::MACT, TopKRaw<NT>::MMAX>(shm);
-  __syncthreads();
-  // per-level key range over every covered position of the level
-  {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int j = 0; j < kMaxLevels; ++j)
-      if (j < L) {
-        const float* cj = cov + a.cov_off[j];
-        const int nj = covered >> j;
-        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-        for (int p0 = threadIdx.x; p0 < nj; p0 += 4 * NT) {  // four reads in flight
-          float x[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) x[u] = cj[min(p0 + u * NT, nj - 1)];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t kx = order_key(x[u]);
-            mn = min(mn, kx);
-            mx = max(mx, kx);
-          }
-        }
-        mn = wave_min_u32(mn);
-        mx = wave_max_u32(mx);
-        if (lane == 0) {
-          lvmn[j * W + w] = mn;
-          lvmx[j * W + w] = mx;
-        }
-      }
-  }
   __syncthreads();
   int32_t* dbg_sel = (report && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
   float* dbg_score = (report && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
@@ -613,21 +652,16 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
     const int kj = a.budgets[L - j];
     const int nj = covered >> j;
     const float* cj = cov + a.cov_off[j];
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      kmin = min(kmin, lvmn[j * W + i]);
-      kmax = max(kmax, lvmx[j * W + i]);
-    }
+    const float smin = key_to_f32(lvm[2 * j]), smax = key_to_f32(lvm[2 * j + 1]);
     constexpr int MM = TopKRaw<NT>::MMAX, MA = TopKRaw<NT>::MACT;
     if (nj <= MA * 4) {
-      refine_level_mask<NT, 4>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+      refine_level_mask<NT, 4>(cj, nj, kj, smin, smax, prev, next, tk_raw);
     } else if (nj <= MA * 8) {
-      refine_level_mask<NT, 8>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+      refine_level_mask<NT, 8>(cj, nj, kj, smin, smax, prev, next, tk_raw);
     } else if (MM <= 16 || nj <= MA * 16) {
-      refine_level_mask<NT, 16>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+      refine_level_mask<NT, 16>(cj, nj, kj, smin, smax, prev, next, tk_raw);
     } else {
-      refine_level_mask<NT, MM>(cj, nj, kj, kmin, kmax, prev, next, tk_raw);
+      refine_level_mask<NT, MM>(cj, nj, kj, smin, smax, prev, next, tk_raw);
     }
     if (dbg_sel || dbg_score) {
       const int sh_l = L - j;
@@ -1001,6 +1035,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.keys_top = reinterpret_cast<uint32_t*>(L.ws + P.off_keys);
   a.sel_top = reinterpret_cast<int32_t*>(L.ws + P.off_sel_top);
   a.cov = reinterpret_cast<float*>(L.ws + P.off_cov);
+  a.lvl_mm = reinterpret_cast<uint32_t*>(L.ws + P.off_lvl);
   a.part_ml = reinterpret_cast<float*>(L.ws + P.off_part_ml);
   a.part_o = reinterpret_cast<float*>(L.ws + P.off_part_o);
   a.heads_total = P.heads_total;
