@@ -185,6 +185,41 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
                      int32_t n_q, float* out, int32_t* sel_out, int32_t* sel_levels,
                      float* score_levels, void* workspace, uint64_t ws_bytes, void* stream);
 
+/*
+ * Bytes of workspace wf_attend_selected needs, or 0 if the arguments are
+ * invalid.
+ */
+uint64_t wf_attend_selected_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype,
+                                            int32_t n_q, int32_t k0, int32_t n_gen);
+
+/*
+ * Attention only, over a selection made earlier: step 3 of wf_select_attend
+ * with the kept prompt tokens handed in (equation 3 restricted to T = sel
+ * followed by gen_idx; no mask; float32 accumulation).  This serves the
+ * reading of WaveFilter section 1 and section 3.1 in which the key tokens
+ * located at one denoising step are kept for the following steps: select
+ * with wf_select_attend (its sel_out), then call this on the next steps with
+ * their queries.
+ *
+ *   q            device [batch, heads, n_q, head_dim], element type `dtype`
+ *   k, v         device [batch, heads, n_tot, head_dim]
+ *   sel          device int32 [batch, heads, k0]: prompt rows per head (any
+ *                order; ascending as wf_select_attend returns them); NULL
+ *                allowed when k0 == 0; out-of-range entries are clamped
+ *   gen_idx      device int32 [n_gen], shared by all heads; NULL allowed when
+ *                n_gen == 0; out-of-range entries are clamped
+ *   k0 + n_gen   >= 1
+ *   out          device float32 [batch, heads, n_q, head_dim]
+ *   workspace    device buffer of ws_bytes >= wf_attend_selected_workspace_bytes;
+ *                scratch only
+ * Returns WF_ERR_SHAPE / WF_ERR_DTYPE / WF_ERR_NULL / WF_ERR_ALIGN /
+ * WF_ERR_WORKSPACE / WF_ERR_BUDGET (T too long for one workgroup's list) on
+ * invalid arguments, before anything is enqueued.
+ */
+int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batch, int32_t heads, int32_t n_tot,
+                       int32_t head_dim, int32_t dtype, const int32_t* sel, int32_t k0, const int32_t* gen_idx,
+                       int32_t n_gen, int32_t n_q, float* out, void* workspace, uint64_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,10 +12,13 @@ from ._lib import (  # noqa: F401
     WF_F32,
     WF_PYR_ALL_LEVELS,
     Pyramid,
+    PreparedAttend,
     PreparedBuild,
     PreparedStep,
     WfError,
     Workspace,
+    attend_selected,
+    attend_selected_workspace_bytes,
     build_pyramid,
     lib,
     pyramid_bytes,

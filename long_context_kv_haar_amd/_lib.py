@@ -75,6 +75,10 @@ def lib():
         L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p]
         L.wf_select_attend.restype = ctypes.c_int
         L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, vp, vp, vp, vp, vp, u64, vp]
+        L.wf_attend_selected_workspace_bytes.restype = u64
+        L.wf_attend_selected_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.wf_attend_selected.restype = ctypes.c_int
+        L.wf_attend_selected.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, i32, i32, vp, vp, u64, vp]
         _LIB = L
     return _LIB
 
@@ -222,6 +226,66 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
         res["sel_levels"] = sel_levels
         res["score_levels"] = score_levels
     return res
+
+
+def attend_selected_workspace_bytes(batch, heads, head_dim, dtype_code, n_q, k0, n_gen):
+    return int(lib().wf_attend_selected_workspace_bytes(batch, heads, head_dim, dtype_code, n_q, k0, n_gen))
+
+
+def _attend_selected_args(q, k, v, sel, gen_idx, out, ws):
+    B, H, n_q, d = q.shape
+    k0 = 0 if sel is None else sel.shape[-1]
+    n_gen = 0 if gen_idx is None else gen_idx.numel()
+
+    def ptr(t):
+        return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+    return (ptr(q), ptr(k), ptr(v), B, H, k.shape[2], d, _dtype_code(q), ptr(sel), k0, ptr(gen_idx), n_gen, n_q,
+            ptr(out), ptr(ws), ws.numel(), _stream_handle(q.device))
+
+
+def attend_selected(q, k, v, sel, gen_idx, out=None, workspace=None):
+    """Attention only over a selection made earlier (``sel``: int32
+    ``[B, H, k0]`` prompt rows, e.g. ``select_attend(...)["sel"]``) plus the
+    generated rows ``gen_idx``.  Returns float32 ``[B, H, n_q, d]``."""
+    B, H, n_q, d = q.shape
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if q.dtype != k.dtype or k.dtype != v.dtype:
+        raise WfError(-3, "attend_selected")
+    if sel is not None and (sel.dtype != torch.int32 or not sel.is_contiguous() or tuple(sel.shape[:2]) != (B, H)):
+        raise ValueError("sel must be a contiguous int32 [B, H, k0] device tensor")
+    if gen_idx is not None and (gen_idx.dtype != torch.int32 or not gen_idx.is_contiguous()):
+        raise ValueError("gen_idx must be a contiguous int32 device tensor")
+    k0 = 0 if sel is None else sel.shape[-1]
+    n_gen = 0 if gen_idx is None else gen_idx.numel()
+    need = attend_selected_workspace_bytes(B, H, d, _dtype_code(q), n_q, k0, n_gen)
+    if need == 0:
+        raise WfError(-2, "wf_attend_selected_workspace_bytes")
+    if workspace is None:
+        workspace = _WORKSPACES.setdefault(q.device, Workspace(q.device))
+    ws = workspace.get(need)
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.float32, device=q.device)
+    st = lib().wf_attend_selected(*_attend_selected_args(q, k, v, sel, gen_idx, out, ws))
+    if st != WF_OK:
+        raise WfError(st, "wf_attend_selected")
+    return out
+
+
+class PreparedAttend:
+    """An attend_selected call with its arguments marshalled once."""
+
+    def __init__(self, q, k, v, sel, gen_idx, out, workspace):
+        self._keep = (q, k, v, sel, gen_idx, out, workspace)
+        self._args = _attend_selected_args(q, k, v, sel, gen_idx, out, workspace)
+        self._fn = lib().wf_attend_selected
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != WF_OK:
+            raise WfError(st, "wf_attend_selected")
 
 
 def split_levels(flat, budgets):

@@ -142,6 +142,43 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   return WF_OK;
 }
 
+// Attention-only plan (a selection handed in): the chunking, split and LDS
+// layout of the attention stage and the workspace sections it uses.
+int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, int32_t n_q, int32_t k0,
+                     int32_t n_gen, wf::SelectPlan* P) {
+  if (batch < 1 || heads < 1 || (int64_t)batch * heads > WF_MAX_HEADS) return WF_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return WF_ERR_SHAPE;
+  if (dtype != WF_F32 && dtype != WF_BF16) return WF_ERR_DTYPE;
+  if (n_q < 1 || n_q > WF_MAX_QUERIES || k0 < 0 || n_gen < 0 || (int64_t)k0 + n_gen < 1) return WF_ERR_SHAPE;
+  if ((int64_t)k0 + n_gen > (1 << 24)) return WF_ERR_SHAPE;
+  memset(P, 0, sizeof(*P));
+  P->heads_total = batch * heads;
+  P->n_q = n_q;
+  P->head_dim = head_dim;
+  P->dtype = dtype;
+  P->k0 = k0;
+  P->n_gen = n_gen;
+  P->n_att = k0 + n_gen;
+  P->chunk = wf::attend_chunk(dtype);
+  P->n_chunks = (P->n_att + P->chunk - 1) / P->chunk;
+  int target = (256 + P->heads_total - 1) / P->heads_total;
+  if (target > wf::kMaxSplit) target = wf::kMaxSplit;
+  if (target < 1) target = 1;
+  P->chunks_per_split = (P->n_chunks + target - 1) / target;
+  P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
+  P->att_t_words = (P->n_att + 3) & ~3;
+  const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
+  const int64_t buf_bytes = wf::attend_buffer_bytes(dtype, head_dim, (n_q + 15) / 16);
+  if (buf_bytes > budget) return WF_ERR_BUDGET;
+  P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
+  const uint64_t H = (uint64_t)P->heads_total;
+  uint64_t w = 0;
+  P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
+  P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * head_dim * 4);
+  P->total = w;
+  return WF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,10 +288,50 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
   a.k = k;
   a.v = v;
   a.gen_idx = gen_idx;
+  a.sel_in = nullptr;
+  a.attend_only = 0;
   a.out = out;
   a.sel_out = sel_out;
   a.sel_levels = sel_levels;
   a.score_levels = score_levels;
+  a.ws = reinterpret_cast<uint8_t*>(workspace);
+  if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  return WF_OK;
+}
+
+uint64_t wf_attend_selected_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype,
+                                            int32_t n_q, int32_t k0, int32_t n_gen) {
+  wf::SelectPlan P;
+  if (make_attend_plan(batch, heads, head_dim, dtype, n_q, k0, n_gen, &P) != WF_OK) return 0;
+  return P.total;
+}
+
+int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batch, int32_t heads, int32_t n_tot,
+                       int32_t head_dim, int32_t dtype, const int32_t* sel, int32_t k0, const int32_t* gen_idx,
+                       int32_t n_gen, int32_t n_q, float* out, void* workspace, uint64_t ws_bytes, void* stream) {
+  if (!q || !k || !v || !out || !workspace) return WF_ERR_NULL;
+  if ((k0 > 0 && !sel) || (n_gen > 0 && !gen_idx)) return WF_ERR_NULL;
+  wf::SelectPlan P;
+  const int st = make_attend_plan(batch, heads, head_dim, dtype, n_q, k0, n_gen, &P);
+  if (st != WF_OK) return st;
+  if (n_tot < 1) return WF_ERR_SHAPE;
+  P.n_tot = n_tot;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace)) return WF_ERR_ALIGN;
+  if ((sel && !aligned4(sel)) || (gen_idx && !aligned4(gen_idx))) return WF_ERR_ALIGN;
+  if (ws_bytes < P.total) return WF_ERR_WORKSPACE;
+  wf::SelectLaunch a;
+  a.plan = P;
+  a.q = q;
+  a.a_top = nullptr;
+  a.k = k;
+  a.v = v;
+  a.gen_idx = gen_idx;
+  a.sel_in = sel;  // NULL when k0 == 0
+  a.attend_only = 1;
+  a.out = out;
+  a.sel_out = nullptr;
+  a.sel_levels = nullptr;
+  a.score_levels = nullptr;
   a.ws = reinterpret_cast<uint8_t*>(workspace);
   if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;

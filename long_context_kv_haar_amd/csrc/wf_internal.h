@@ -49,6 +49,8 @@ struct SelectLaunch {
   const void* k;
   const void* v;
   const int32_t* gen_idx;
+  const int32_t* sel_in;  // attention only: the kept prompt tokens [heads_total][k0] (NULL if k0 == 0)
+  int attend_only;        // 1: skip selection, attend over sel_in and gen_idx
   float* out;
   int32_t* sel_out;
   int32_t* sel_levels;

@@ -29,6 +29,8 @@ struct StepArgs {
   const void* k;
   const void* v;
   const int32_t* gen_idx;
+  const int32_t* sel_in;  // attention only: the kept prompt tokens [heads_total][k0] (NULL if k0 == 0)
+  int attend_only;        // 1: skip selection, attend over sel_in and gen_idx
   float* out;
   int32_t* sel_out;
   int32_t* sel_levels;
@@ -756,7 +758,11 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   T* Vt = Ks + CH * KS;
 
   const int head = blockIdx.y, split = blockIdx.x;
-  refine_head<NT>(a, head, scratch, tk_raw, tlist, split == 0);
+  if (a.attend_only) {  // a selection made earlier: attention only
+    for (int i = threadIdx.x; i < a.k0; i += NT) tlist[i] = clampi(a.sel_in[(int64_t)head * a.k0 + i], 0, a.n_tot - 1);
+  } else {
+    refine_head<NT>(a, head, scratch, tk_raw, tlist, split == 0);
+  }
   for (int i = threadIdx.x; i < a.n_gen; i += NT) tlist[a.k0 + i] = clampi(a.gen_idx[i], 0, a.n_tot - 1);
   __syncthreads();
 
@@ -1028,6 +1034,8 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.k = L.k;
   a.v = L.v;
   a.gen_idx = L.gen_idx;
+  a.sel_in = L.sel_in;
+  a.attend_only = L.attend_only;
   a.out = L.out;
   a.sel_out = L.sel_out;
   a.sel_levels = L.sel_levels;
@@ -1094,11 +1102,13 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
     }                                                                                                      \
   } while (0)
 
-  WF_RT_SWITCH(WF_LAUNCH, coarse_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
-  WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!L.attend_only) {  // selection stages (skipped when the caller hands in a selection)
+    WF_RT_SWITCH(WF_LAUNCH, coarse_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
+    WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt * kAttendGroups), P.attend_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned comb_blocks = (unsigned)(((int64_t)H * P.n_q * (P.head_dim / 4) + 255) / 256);

@@ -24,5 +24,6 @@ from .wavefilter import (  # noqa: F401
     select,
     attend,
     select_attend,
+    attend_selected,
     SelectResult,
 )

@@ -235,3 +235,20 @@ def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels):
     rows = np.concatenate([res.sel[0], np.asarray(gen_idx, dtype=np.int64)])
     out = attend(q, k_all[rows], v_all[rows])
     return out, res
+
+
+def attend_selected(q, k_all, v_all, sel, gen_idx):
+    """Attention of a later step over a selection made earlier (one head).
+
+    The pages say the DWT is taken at the initial time step to locate the
+    key tokens (section 1, section 3.1); one reading is that the selection
+    itself is then kept for the following denoising steps, so a later step
+    only attends.  This is eq. 3 restricted to the given prompt tokens
+    ``sel`` followed by the generated positions ``gen_idx``, with the
+    current queries ``q``: exactly the attention stage of ``select_attend``
+    with the selection handed in.
+    """
+    k_all = np.asarray(k_all, dtype=np.float64)
+    v_all = np.asarray(v_all, dtype=np.float64)
+    rows = np.concatenate([np.asarray(sel, dtype=np.int64), np.asarray(gen_idx, dtype=np.int64)])
+    return attend(q, k_all[rows], v_all[rows])

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -112,3 +112,30 @@ def test_select_attend_rejects_bad_arguments():
     assert select(q=MISALIGNED) == -7
     assert select(sel=FAKE + 2) == -7
     assert select(ws_bytes=64) == -6
+
+
+def attend_sel(q=FAKE, k=FAKE, v=FAKE, B=1, H=2, n_tot=1100, d=64, dt=wf.WF_BF16, sel=FAKE, k0=64, gen=FAKE, n_gen=8,
+               n_q=32, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib().wf_attend_selected(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), B, H, n_tot, d, dt,
+                                    ctypes.c_void_p(sel), k0, ctypes.c_void_p(gen), n_gen, n_q, ctypes.c_void_p(out),
+                                    ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_attend_selected_rejects_bad_arguments():
+    need = lib().wf_attend_selected_workspace_bytes(1, 2, 64, wf.WF_BF16, 32, 64, 8)
+    assert need > 0
+    assert lib().wf_attend_selected_workspace_bytes(1, 2, 96, wf.WF_BF16, 32, 64, 8) == 0   # head dim
+    assert lib().wf_attend_selected_workspace_bytes(1, 2, 64, wf.WF_BF16, 65, 64, 8) == 0   # too many queries
+    assert lib().wf_attend_selected_workspace_bytes(1, 2, 64, wf.WF_BF16, 32, 0, 0) == 0    # empty set
+    assert attend_sel(q=0) == -1
+    assert attend_sel(sel=0) == -1                 # a selection is needed when k0 > 0
+    assert attend_sel(gen=0) == -1                 # generated rows are needed when n_gen > 0
+    assert attend_sel(dt=5) == -3
+    assert attend_sel(d=96) == -2
+    assert attend_sel(k0=-1) == -2
+    assert attend_sel(n_q=0) == -2
+    assert attend_sel(n_tot=0) == -2
+    assert attend_sel(q=MISALIGNED) == -7
+    assert attend_sel(sel=FAKE + 2) == -7
+    assert attend_sel(ws_bytes=need - 1) == -6
+

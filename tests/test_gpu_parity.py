@@ -216,3 +216,63 @@ def test_one_workspace_serves_different_shapes():
     assert torch.equal(r1["out"], r1b["out"])
     assert torch.equal(ra1["out"], ra2["out"]) and torch.equal(ra1["sel"], ra2["sel"])
     assert torch.equal(rb["out"], rb2["out"])
+
+
+def oracle_attend_selected_head(q, inp, sel_bh, gen, b, h):
+    from oracle import attend_selected
+    return attend_selected(to_f64(q[b, h]), to_f64(inp.k[b, h]), to_f64(inp.v[b, h]), sel_bh, gen)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_attend_selected_reuses_a_selection(cid):
+    """Attention over a selection made by an earlier call: with the same
+    queries it reproduces that call's output bit for bit; with the queries of
+    a later step it matches the oracle's attention over the same rows."""
+    say(f"[attend_selected c{cid}]")
+    inp = to_dev(make_layer(cid, 0))
+    cfg = inp.cfg
+    _, res = run(inp)
+    again = wf.attend_selected(inp.q, inp.k, inp.v, res["sel"], inp.gen_idx)
+    torch.cuda.synchronize()
+    assert torch.equal(again, res["out"])
+    q2 = make_layer(cid, 1).q.to(DEV)          # the queries of another step, same shape
+    out2 = wf.attend_selected(q2, inp.k, inp.v, res["sel"], inp.gen_idx)
+    torch.cuda.synchronize()
+    gen = inp.gen_idx.cpu().numpy().astype(np.int64)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            ref = oracle_attend_selected_head(q2, inp, res["sel"][b, h].cpu().numpy(), gen, b, h)
+            err = np.abs(out2[b, h].cpu().numpy() - ref).max()
+            assert err <= TOL[cfg.dtype], (b, h, err)
+
+
+ATTEND_EDGE = [
+    # name, config, k0 (kept prompt rows per head), generated rows
+    ("gen-only", custom(2, cid=80, heads=2, n_prompt=1024, n_gen=40), 0, 40),
+    ("prompt-only", custom(2, cid=81, heads=3, n_prompt=2048, n_gen=8), 300, 0),
+    ("ragged-b2-nq20", custom(2, cid=82, batch=2, heads=3, n_q=20, n_prompt=4096, n_gen=7), 777, 7),
+    ("f32-d64-nq64", custom(1, cid=83, head_dim=64, heads=2, n_q=64, n_prompt=2048, n_gen=16), 513, 16),
+    ("one-row", custom(2, cid=84, heads=1, n_q=1, n_prompt=256, n_gen=0), 1, 0),
+    ("many-splits", custom(2, cid=85, heads=1, n_q=16, n_prompt=32768, n_gen=64), 9000, 64),
+]
+
+
+@pytest.mark.parametrize("name,cfg,k0,n_gen", ATTEND_EDGE, ids=[e[0] for e in ATTEND_EDGE])
+def test_attend_selected_edge_cases(name, cfg, k0, n_gen):
+    say(f"[attend_selected edge {name}]")
+    inp = make_layer(cfg, 0)
+    gsel = torch.Generator().manual_seed(cfg.cid)
+    # any rows, in any order, repeats allowed: a random draw over the prompt
+    sel = torch.randint(0, cfg.n_prompt, (cfg.batch, cfg.heads, k0), generator=gsel, dtype=torch.int32)
+    gen = inp.gen_idx[:n_gen]
+    to_dev(inp)
+    sel_d = sel.to(DEV) if k0 else None
+    gen_d = gen.to(DEV) if n_gen else None
+    out = wf.attend_selected(inp.q, inp.k, inp.v, sel_d, gen_d)
+    torch.cuda.synchronize()
+    g = gen.numpy().astype(np.int64)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            ref = oracle_attend_selected_head(inp.q, inp, sel[b, h].numpy(), g, b, h)
+            err = np.abs(out[b, h].cpu().numpy() - ref).max()
+            assert err <= TOL[cfg.dtype], (b, h, err)

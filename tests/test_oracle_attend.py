@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attend, select_attend
+from oracle import attend, attend_selected, select_attend
 
 
 @pytest.mark.parametrize("n_p,n_g,d", [(64, 8, 16), (256, 0, 32), (128, 32, 64)])
@@ -64,3 +64,29 @@ def test_restricted_set_is_selected_plus_generated():
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q)[None], torch.from_numpy(k[rows])[None], torch.from_numpy(v[rows])[None])[0].numpy()
     np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+def test_reused_selection_matches_select_attend_and_library():
+    """A selection made at one step, attended with the same queries, gives
+    select_attend's output; with the next step's queries it is eq. 3 over the
+    same rows (checked against torch's float64 attention)."""
+    rng = np.random.default_rng(9)
+    n_p, n_g, d = 256, 12, 16
+    q0 = rng.standard_normal((8, d))
+    q1 = rng.standard_normal((8, d))
+    k = rng.standard_normal((n_p + n_g, d))
+    v = rng.standard_normal((n_p + n_g, d))
+    gen = np.arange(n_p, n_p + n_g)
+    out0, res = select_attend(q0, k, v, n_p, gen, [6, 12, 24, 40], 3)
+    np.testing.assert_array_equal(attend_selected(q0, k, v, res.sel[0], gen), out0)
+    rows = list(res.sel[0]) + list(gen)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q1)[None], torch.from_numpy(k[rows])[None], torch.from_numpy(v[rows])[None])[0].numpy()
+    np.testing.assert_allclose(attend_selected(q1, k, v, res.sel[0], gen), ref, atol=1e-12)
+    # only generated positions, and only prompt tokens
+    ref_g = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q1)[None], torch.from_numpy(k[gen])[None], torch.from_numpy(v[gen])[None])[0].numpy()
+    np.testing.assert_allclose(attend_selected(q1, k, v, np.zeros(0, dtype=np.int64), gen), ref_g, atol=1e-12)
+    np.testing.assert_allclose(attend_selected(q1, k, v, np.arange(n_p), np.zeros(0, dtype=np.int64)),
+                               attend(q1, k[:n_p], v[:n_p]), atol=1e-14)
+
