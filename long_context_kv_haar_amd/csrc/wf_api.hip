@@ -110,25 +110,29 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   if (target < 1) target = 1;
   P->chunks_per_split = (P->n_chunks + target - 1) / target;
   P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
-  // attention workgroup LDS: the attended-set list, then (aliased) the
-  // refinement state or the K/V chunk buffers
-  P->att_t_words = (P->n_att + 3) & ~3;
+  // refinement workgroup LDS (one per head): the kept sets and candidate
+  // lists, plus the coverage scores when they fit
   P->refine_nmax = (nmax + 3) / 4 * 4;
   P->refine_kmax = (kmax + 1 + 3) / 4 * 4;  // + a spare slot for rejected candidates
-  const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
-  // bitmask refinement: 2 masks over the covered positions (whole groups of
-  // kMaskGroup positions), the kept coarse regions and per-level key ranges
-  P->refine_mask_words = (int)((P->covered + wf::kMaskGroup - 1) / wf::kMaskGroup * (wf::kMaskGroup / 32));
-  const int64_t mask_base = 4 * (((int64_t)P->k_top + 3) / 4 * 4 + 2 * (int64_t)P->refine_mask_words +
-                                 2 * wf::kMaxLevels);
+  const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve;
+  // bitmask refinement: the kept coarse regions and 2 masks, each over at
+  // least 2 x the covered positions (a level's slots span up to the next
+  // power of two of its positions) and at least kMaskGroup positions
+  {
+    const int64_t bits = 2 * P->covered > wf::kMaskGroup ? 2 * P->covered : wf::kMaskGroup;
+    P->refine_mask_words = (int)((bits + 2047) / 2048 * 64);
+  }
+  const int64_t mask_base = 4 * (((int64_t)P->k_top + 3) / 4 * 4 + 2 * (int64_t)P->refine_mask_words);
   const int64_t list_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
   const int64_t refine_base = list_base > mask_base ? list_base : mask_base;
   if (refine_base > budget) return WF_ERR_BUDGET;
   P->refine_cov_in_lds = (refine_base + 4 * P->cov_len) <= budget;
-  const int64_t refine_bytes = refine_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0);
+  P->refine_lds = (int)(refine_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0));
+  // attention workgroup LDS: the attended-set list, then the K/V chunk buffers
+  P->att_t_words = (P->chunks_per_split * P->chunk + 3) & ~3;  // one split's part of T
   const int64_t buf_bytes = wf::attend_buffer_bytes(pyr->dtype, pyr->head_dim, (n_q + 15) / 16);
-  if (buf_bytes > budget) return WF_ERR_BUDGET;
-  P->attend_lds = (int)(4 * (int64_t)P->att_t_words + (refine_bytes > buf_bytes ? refine_bytes : buf_bytes));
+  if (buf_bytes > wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words) return WF_ERR_BUDGET;
+  P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
@@ -136,6 +140,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
   P->off_lvl = w;      w += align_up(H * (uint64_t)((P->covered + 63) / 64) * wf::kMaxLevels * 2 * 4);
+  P->off_sel = w;      w += align_up(H * (uint64_t)(P->k0 > 0 ? P->k0 : 1) * 4);
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * P->head_dim * 4);
   P->total = w;
@@ -166,7 +171,7 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
   if (target < 1) target = 1;
   P->chunks_per_split = (P->n_chunks + target - 1) / target;
   P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
-  P->att_t_words = (P->n_att + 3) & ~3;
+  P->att_t_words = (P->chunks_per_split * P->chunk + 3) & ~3;  // one split's part of T
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
   const int64_t buf_bytes = wf::attend_buffer_bytes(dtype, head_dim, (n_q + 15) / 16);
   if (buf_bytes > budget) return WF_ERR_BUDGET;

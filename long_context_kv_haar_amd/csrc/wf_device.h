@@ -822,294 +822,4 @@ __device__ __forceinline__ void topk_strided(int n, int k, TopKSel<ACT, MAXS>& s
   }
 }
 
-// ---------------------------------------------------------------------------
-// Top-K over a position set given as a validity predicate, with the result
-// written as a bitmask (bit p set for a kept position p < n).  Same rule as
-// above: the k best valid positions by (key descending, position ascending).
-// The caller supplies the keys' overall [kmin, kmax] (any range containing
-// every valid key), so no reduction pass is needed.  Position p lives in
-// slot p / ACT of thread p mod ACT; only the first ACT threads work.
-//  1. one count per valid key into 4 ACT bins linear in the value over
-//     [kmin, kmax]; wave 0 finds the bin b holding the k-th best;
-//  2. unless bin b is kept whole, its keys alone are counted into sub-bins
-//     linear in the value across bin b, and wave 0 finds the sub-bin sb;
-//  3. unless (b, sb) is kept whole (rare), the exact key range of its keys
-//     is reduced and narrowed in key space until it is kept whole or holds a
-//     single value (a tie: the lowest positions win, by ballots and a prefix
-//     over (slot, wave));
-//  4. one ballot per slot writes 64 bits of the mask.
-// Bins are monotone in the key, so a key in a higher bin (or sub-bin) beats
-// every key in a lower one.  key(p, j) and valid(p) are evaluated for p < n
-// only.  mask_out must hold ceil(n / (4 ACT)) * 4 ACT / 32 words.  All NT
-// threads must call it; it ends with a workgroup barrier.
-// ---------------------------------------------------------------------------
-template <int ACT, int MAXS> struct TopKMaskShared {
-  static constexpr int W = ACT / 64;
-  static constexpr int NB = 4 * ACT;
-  int hist[NB];             // bins (cleared by the search that reads them)
-  int cnt[MAXS * W];        // tie path: per (slot, wave) counts, then prefixes
-  uint32_t wmn[W], wmx[W];  // exact range of the boundary bin (rare path)
-  int bc[4];                // broadcast: bin, need, count
-};
-
-// Clears the bins before the first use (all NT threads; no barrier inside).
-template <int NT, int ACT, int MAXS>
-__device__ __forceinline__ void topk_mask_init(TopKMaskShared<ACT, MAXS>& sh) {
-  for (int i = threadIdx.x; i < 4 * ACT; i += NT) sh.hist[i] = 0;
-}
-
-template <int NT, int ACT, int MAXS, class ScoreFn, class ValidFn>
-__device__ __forceinline__ void topk_mask(int n, int k, float smin, float smax, TopKMaskShared<ACT, MAXS>& sh,
-                                          ScoreFn score_of, ValidFn valid_of, uint32_t* mask_out) {
-  constexpr int W = ACT / 64;
-  constexpr int NB = 4 * ACT;
-  constexpr int LOGNB = floor_log2(NB);
-  constexpr int BPL = NB / 64;  // bins per lane of wave 0
-  static_assert((NB & (NB - 1)) == 0 && BPL % 4 == 0 && ACT <= NT && MAXS % 4 == 0 && MAXS * W <= 128,
-                "Top-K layout");
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const bool act = t < ACT;  // wave-uniform
-  const int ns = (n + ACT - 1) / ACT;
-
-  // wave 0 finds the bin of the want-th best, publishes (bin, need, count),
-  // clears the bins; ends with a barrier.  Two wave scans, no serial walk:
-  // the first over the lanes' totals (lane l owns bins [BPL l, BPL l + BPL))
-  // finds the owner lane T of the boundary, the second spreads T's bins over
-  // lanes and finds the bin.
-  auto search = [&](int want) {
-    if (w == 0) {
-      int4* h4 = reinterpret_cast<int4*>(sh.hist + BPL * lane);
-      int tot = 0;
-#pragma unroll
-      for (int q = 0; q < BPL / 4; ++q) {
-        const int4 v = h4[q];
-        tot += v.x + v.y + v.z + v.w;
-      }
-      int all;
-      const int incl = wave_incl_scan(tot, &all);
-      const int above = all - incl;  // keys in bins of higher lanes
-      const uint64_t hitm = __ballot((above < want) & (want <= above + tot));
-      const int owner = (int)__ffsll((unsigned long long)hitm) - 1;  // exactly one lane
-      const int above_t = __shfl(above, owner, 64);
-      // bins of the owner: lane l < BPL takes bin BPL * owner + l
-      const int c = (lane < BPL) ? sh.hist[BPL * owner + lane] : 0;
-      int all2;
-      const int incl2 = wave_incl_scan(c, &all2);
-      const int hi_cnt = above_t + (all2 - incl2);  // keys in higher bins of the owner and above
-      const bool hit = (lane < BPL) & (hi_cnt < want) & (want <= hi_cnt + c);
-      const uint64_t hm = __ballot(hit);
-      if (hit) {
-        sh.bc[0] = BPL * owner + lane;
-        sh.bc[1] = want - hi_cnt;
-        sh.bc[2] = c;
-      }
-      (void)hm;
-#pragma unroll
-      for (int q = 0; q < BPL / 4; ++q) h4[q] = make_int4(0, 0, 0, 0);
-    }
-    __syncthreads();
-  };
-
-  // 1. scores, validity, bins (linear in the value over [smin, smax], or, for
-  // a degenerate span, in the order-preserving integer key)
-  float sc[MAXS];
-  bool valid[MAXS];
-  int bn[MAXS];
-  const float span = smax - smin;
-  const float scale = (float)NB / span;
-  const bool linear = span > 0.f && span < 3.0e38f && scale < 3.0e38f;
-  const uint32_t kmin = order_key(smin);
-  const uint32_t krange = order_key(smax) - kmin;
-  const int kshift = (32 - __clz(krange)) > LOGNB ? (32 - __clz(krange)) - LOGNB : 0;
-  if (act) {
-#pragma unroll
-    for (int j0 = 0; j0 < MAXS; j0 += 4) {
-#pragma unroll
-      for (int j = j0; j < j0 + 4; ++j) {
-        sc[j] = 0.f;
-        valid[j] = false;
-        bn[j] = -1;
-      }
-      if (j0 < ns) {
-#pragma unroll
-        for (int j = j0; j < j0 + 4; ++j) {
-          const int p = j * ACT + t;
-          const int pc = p < n ? p : n - 1;
-          valid[j] = (p < n) && valid_of(pc);
-          sc[j] = score_of(pc, j);
-        }
-        if (linear) {
-#pragma unroll
-          for (int j = j0; j < j0 + 4; ++j)
-            bn[j] = valid[j] ? min(NB - 1, max(0, (int)((sc[j] - smin) * scale))) : -1;
-        } else {
-#pragma unroll
-          for (int j = j0; j < j0 + 4; ++j)
-            bn[j] = valid[j] ? (int)(min(order_key(sc[j]) - kmin, krange) >> kshift) : -1;
-        }
-#pragma unroll
-        for (int j = j0; j < j0 + 4; ++j)
-          if (valid[j]) atomicAdd(&sh.hist[bn[j]], 1);
-      }
-    }
-  }
-  __syncthreads();
-  search(k);
-  const int b = sh.bc[0];
-  int need = sh.bc[1], cnt = sh.bc[2];
-  __syncthreads();  // bc is rewritten below
-
-  // 2. sub-bins across bin b (linear mode; in key mode the bins are exact
-  // key ranges already and step 3 takes over)
-  int mode = (cnt == need) ? 1 : (linear ? 2 : 3);
-  int sb = 0;
-  int sub[MAXS];
-#pragma unroll
-  for (int j = 0; j < MAXS; ++j) sub[j] = 0;
-  if (mode == 2) {
-    if (act) {
-#pragma unroll
-      for (int j0 = 0; j0 < MAXS; j0 += 4)
-        if (j0 < ns) {
-#pragma unroll
-          for (int j = j0; j < j0 + 4; ++j) {
-            const float fr = (sc[j] - smin) * scale - (float)b;
-            sub[j] = min(NB - 1, max(0, (int)(fr * (float)NB)));
-            if (bn[j] == b) atomicAdd(&sh.hist[sub[j]], 1);
-          }
-        }
-    }
-    __syncthreads();
-    search(need);
-    sb = sh.bc[0];
-    const int need2 = sh.bc[1], cnt2 = sh.bc[2];
-    __syncthreads();
-    need = need2;
-    cnt = cnt2;
-    if (cnt2 != need2) mode = 3;
-  }
-
-  // 3. exact key range of the boundary class, then key-space narrowing
-  uint32_t lo = 0u, hi = 0u;
-  bool tie = false;
-  uint32_t key[MAXS];  // order-preserving keys, for the exact path only
-  if (mode == 3) {
-#pragma unroll
-    for (int j = 0; j < MAXS; ++j) key[j] = order_key(sc[j]);
-    const bool two = linear;  // the class is (bin b, sub-bin sb) after step 2, else bin b
-    auto in_class = [&](int j) { return (bn[j] == b) & (!two | (sub[j] == sb)); };
-    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
-    if (act) {
-#pragma unroll
-      for (int j = 0; j < MAXS; ++j) {
-        const bool in = in_class(j);
-        kmn = min(kmn, in ? key[j] : 0xFFFFFFFFu);
-        kmx = max(kmx, in ? key[j] : 0u);
-      }
-      kmn = wave_min_u32(kmn);
-      kmx = wave_max_u32(kmx);
-      if (lane == 0) {
-        sh.wmn[w] = kmn;
-        sh.wmx[w] = kmx;
-      }
-    }
-    __syncthreads();
-    lo = 0xFFFFFFFFu;
-    hi = 0u;
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      lo = min(lo, sh.wmn[i]);
-      hi = max(hi, sh.wmx[i]);
-    }
-    // keys above the class (higher bin or sub-bin) are > hi, below are < lo
-    while (cnt != need && lo != hi) {
-      const uint32_t range = hi - lo;
-      const int rb = 32 - __clz(range);
-      const int sft = rb > LOGNB ? rb - LOGNB : 0;
-      if (act) {
-#pragma unroll
-        for (int j0 = 0; j0 < MAXS; j0 += 4)
-          if (j0 < ns) {
-#pragma unroll
-            for (int j = j0; j < j0 + 4; ++j) {
-              const uint32_t d = key[j] - lo;  // wraps above range below lo
-              if (valid[j] & (d <= range)) atomicAdd(&sh.hist[d >> sft], 1);
-            }
-          }
-      }
-      __syncthreads();
-      search(need);
-      const int bb = sh.bc[0];
-      need = sh.bc[1];
-      cnt = sh.bc[2];
-      __syncthreads();
-      lo += (uint32_t)bb << sft;
-      hi = lo + (sft == 0 ? 0u : min(range - ((uint32_t)bb << sft), (1u << sft) - 1u));
-    }
-    tie = cnt != need;  // then lo == hi: keep the lowest positions
-    if (tie) {
-      if (act) {
-#pragma unroll
-        for (int j0 = 0; j0 < MAXS; j0 += 4)
-          if (j0 < ns) {
-#pragma unroll
-            for (int j = j0; j < j0 + 4; ++j) {
-              const int ce = __popcll(__ballot(valid[j] & (key[j] == lo)));
-              if (lane == 0) sh.cnt[j * W + w] = ce;
-            }
-          }
-      }
-      __syncthreads();
-      if (w == 0) {
-        int run = 0;
-#pragma unroll
-        for (int base = 0; base < MAXS * W; base += 64) {
-          const int idx = base + lane;
-          const bool in = idx < ((ns + 3) & ~3) * W;
-          const int v = in ? sh.cnt[idx] : 0;
-          int tot;
-          const int incl = wave_incl_scan(v, &tot);
-          if (in) sh.cnt[idx] = run + incl - v;
-          run += tot;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // 4. the kept set as a bitmask, one loop per rule
-  auto write_mask = [&](auto keep) {
-    if (act) {
-#pragma unroll
-      for (int j0 = 0; j0 < MAXS; j0 += 4)
-        if (j0 < ns) {
-#pragma unroll
-          for (int j = j0; j < j0 + 4; ++j) {
-            const uint64_t km = __ballot(valid[j] & keep(j));
-            if (lane == 0) {
-              const int word = (j * ACT + 64 * w) >> 5;
-              mask_out[word] = (uint32_t)km;
-              mask_out[word + 1] = (uint32_t)(km >> 32);
-            }
-          }
-        }
-    }
-  };
-  if (mode == 1) {
-    write_mask([&](int j) { return bn[j] >= b; });
-  } else if (mode == 2) {
-    write_mask([&](int j) { return (bn[j] > b) | ((bn[j] == b) & (sub[j] >= sb)); });
-  } else if (!tie) {
-    write_mask([&](int j) { return key[j] >= lo; });  // the class above lo is kept whole
-  } else {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    write_mask([&](int j) {
-      const bool e = valid[j] & (key[j] == lo);
-      const int E = sh.cnt[j * W + w] + __popcll(__ballot(e) & below);
-      return (key[j] > lo) | (e & (E < need));
-    });
-  }
-  __syncthreads();
-}
-
 }  // namespace wf

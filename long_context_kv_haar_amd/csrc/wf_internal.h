@@ -17,7 +17,8 @@ constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to thi
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
-constexpr int kMaskGroup = 2048;          // positions per group of four Top-K slots of up to 512 positions
+constexpr int kRefineThreads = 512;       // one refinement workgroup per head
+constexpr int kMaskGroup = 2048;          // least positions a refinement mask spans
 constexpr int kCoverThreads = 256;
 
 // Byte layout of the per-call workspace, and the resolved launch shape.
@@ -36,10 +37,11 @@ struct SelectPlan {
   int refine_nmax, refine_kmax; // candidate / kept capacity (words, multiples of 4)
   int refine_mask_words;        // words of one bitmask over the covered positions
   int refine_cov_in_lds;        // coverage scores staged in LDS
+  int refine_lds;               // refinement workgroup: its state (kept sets, candidate lists)
   int att_t_words;              // words of the attended-set list (T) region
-  int attend_lds;               // T list + max(refinement state, K/V chunk buffers)
+  int attend_lds;               // T list + K/V chunk buffers
   // workspace sections (byte offsets)
-  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_part_ml, off_part_o, total;
+  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, total;
 };
 
 struct SelectLaunch {

@@ -7,10 +7,12 @@
 //                   summed in registers into the scores of all their
 //                   sub-regions at levels 0 .. L-1 (Figure 2 (d), with A_j
 //                   taken by linearity from the token dot products)
-//   attend_kernel   the recursive refinement (again recomputed by every
-//                   workgroup of the head, from LDS), then split-K
-//                   online-softmax attention over the kept prompt tokens plus
-//                   the generated positions (eq. 3 restricted to that set)
+//   refine_kernel   the recursive refinement, one workgroup per head, with
+//                   the coverage scores in registers and the kept sets as
+//                   bitmasks in LDS; writes the kept prompt tokens
+//   attend_kernel   split-K online-softmax attention over the kept prompt
+//                   tokens plus the generated positions (eq. 3 restricted to
+//                   that set); also serves a selection handed in by the caller
 //   combine_kernel  log-sum-exp merge of the split partial results
 //
 // Citations are to WaveFilter (arXiv 2606.00724).
@@ -29,8 +31,8 @@ struct StepArgs {
   const void* k;
   const void* v;
   const int32_t* gen_idx;
-  const int32_t* sel_in;  // attention only: the kept prompt tokens [heads_total][k0] (NULL if k0 == 0)
-  int attend_only;        // 1: skip selection, attend over sel_in and gen_idx
+  const int32_t* sel_in;  // the kept prompt tokens [heads_total][k0] the attention reads (NULL if k0 == 0)
+  int32_t* sel_ws;        // where the refinement writes them [heads_total][k0]
   float* out;
   int32_t* sel_out;
   int32_t* sel_levels;
@@ -175,6 +177,17 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   }
 }
 
+// State of the fast refinement level (see refine_level_fast).
+struct RefineShared {
+  static constexpr int NB = 1024;   // histogram bins (a power of two, 16 per lane of a wave)
+  static constexpr int LMAX = 256;  // boundary-bin list capacity
+  int hist[NB];
+  uint64_t list[LMAX];
+  int list_n[2];  // list lengths, by level parity (the other one is cleared for the next level)
+  int pad[2];
+};
+constexpr size_t kRefineFastBytes = sizeof(RefineShared);
+
 // LDS scratch shared by every Top-K variant a workgroup of NT threads uses:
 // the strided register Top-K on min(NT, 256) threads (up to 32 slots), on
 // 512 threads (16 slots) for large workgroups, and the LDS-resident fallback.
@@ -182,9 +195,9 @@ constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
 template <int NT> struct TopKRaw {
   static constexpr int ACT0 = NT < 256 ? NT : 256;
   static constexpr int MACT = 1 << floor_log2(NT);     // mask Top-K threads (a power of two)
-  static constexpr int MMAX = MACT >= 512 ? 16 : 32;   // and its slots per thread
+  static constexpr int MMAX = NT > 256 ? 16 : 32;      // and its slots per thread (registers)
   static constexpr size_t BYTES =
-      cmax(cmax(sizeof(TopKFastShared<NT>), sizeof(TopKMaskShared<MACT, MMAX>)),
+      cmax(cmax(sizeof(TopKFastShared<NT>), kRefineFastBytes),
            cmax(sizeof(TopKSel<ACT0, 32>), NT >= 512 ? sizeof(TopKSel<512, 16>) : size_t(0)));
 };
 
@@ -558,117 +571,334 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
   __syncthreads();
 }
 
-// Emits the set bits of mask[0 .. nbits) in ascending order: emit(o, p) for
-// the o-th set bit p.  Thread t takes bytes [t B, t B + B) of the mask, one
-// workgroup scan gives its output offset.  Ends with a workgroup barrier.
-template <int NT, class Emit>
-__device__ __forceinline__ void mask_compact(const uint32_t* mask, int nbits, int* wsum, Emit emit) {
-  const int nbytes = (nbits + 7) >> 3;
-  const int per = (nbytes + NT - 1) / NT;
-  const int b0 = min(nbytes, (int)threadIdx.x * per), b1 = min(nbytes, b0 + per);
-  const uint8_t* mb = reinterpret_cast<const uint8_t*>(mask);
-  int c = 0;
-  for (int i = b0; i < b1; ++i) c += __popc(mb[i]);
-  int all;
-  int o = block_incl_scan<NT>(c, wsum, &all) - c;
-  for (int i = b0; i < b1; ++i) {
-    uint32_t x = mb[i];
-    while (x) {
-      const int bit = __ffs(x) - 1;
-      x &= x - 1;
-      emit(o++, 8 * i + bit);
+// ---------------------------------------------------------------------------
+// Recursive refinement with bitmask kept sets (covered <= MACT * MMAX).
+//
+// Level-j position p (p < n_j = covered >> j) lives in slot s = p / ACT of
+// thread t = p mod ACT, so a wave's 64 positions of one slot form one 64-bit
+// word of a level mask and their parents (p >> 1) one 32-bit word of the
+// parent mask.  Every level's coverage scores are loaded into registers at
+// the start (coarsest level first), so the loads of all levels overlap the
+// work of the first ones.  One level (the k_j best candidates, candidates =
+// children of the kept parents):
+//   A. each valid candidate adds one count to a histogram of NB bins linear
+//      in the score over the level's [min, max] (published by the cover
+//      kernel);                                                   barrier B
+//   S. every wave finds by itself the bin b holding the k_j-th best, the
+//      count `need` still to take from it and its size `cnt` (two wave scans
+//      over the bins), so no broadcast round is needed;
+//   M. candidates in bins above b (and b itself when need == cnt) are written
+//      to the level mask with one ballot per slot; the candidates of bin b go
+//      to a short list as (order key, ~position);                barrier C
+//   R. each list entry counts the entries ranked above it (greater score, or
+//      equal score and lower position) and, within `need`, sets its bit;
+//      the histogram is cleared for the next level;              barrier D
+// Bins are monotone in the score, so bin order plus the exact in-bin rank is
+// the (score descending, position ascending) order.  When a level's score
+// range is degenerate, or its boundary bin holds more than LMAX candidates,
+// the head is refined again from the top by the list-based refinement.
+// ---------------------------------------------------------------------------
+
+template <int J> struct IntC { static constexpr int value = J; };
+template <int MMAX, int J> struct LevelSlots { static constexpr int N = (MMAX >> J) > 0 ? (MMAX >> J) : 1; };
+
+// Coverage scores of levels 0 .. kMaxLevels-1 in registers, compile-time indexed.
+template <int MMAX> struct LevelScores {
+  float s0[LevelSlots<MMAX, 0>::N], s1[LevelSlots<MMAX, 1>::N], s2[LevelSlots<MMAX, 2>::N];
+  float s3[LevelSlots<MMAX, 3>::N], s4[LevelSlots<MMAX, 4>::N], s5[LevelSlots<MMAX, 5>::N];
+  float s6[LevelSlots<MMAX, 6>::N];
+  template <int J> __device__ __forceinline__ auto& get() {
+    if constexpr (J == 0) return s0;
+    else if constexpr (J == 1) return s1;
+    else if constexpr (J == 2) return s2;
+    else if constexpr (J == 3) return s3;
+    else if constexpr (J == 4) return s4;
+    else if constexpr (J == 5) return s5;
+    else return s6;
+  }
+};
+static_assert(kMaxLevels == 7, "LevelScores holds seven levels");
+
+template <int J, class F>
+__device__ __forceinline__ void for_levels_desc(F&& f) {
+  f(IntC<J>{});
+  if constexpr (J > 0) for_levels_desc<J - 1>(f);
+}
+
+// Number of set bits of the 64-bit mask m in lanes below this one.
+__device__ __forceinline__ int mask_rank(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t lds_mask64(const uint32_t* mask, int word64) {
+  const uint2 v = *reinterpret_cast<const uint2*>(mask + 2 * word64);
+  return ((uint64_t)v.y << 32) | v.x;
+}
+
+// Emits the set bits of a level mask over positions [0, nbits) in ascending
+// order: emit(o, p, set) is called for every position p < 64 ceil(nbits/64)
+// of threads t < ACT in the slot layout above, with set = bit p and o its
+// rank among the set bits when set (reads the caller makes in emit outside
+// a branch on `set` are issued together).  Each active wave scans the words' bit counts itself (one
+// wave scan per 64 words), so no barrier is needed; the caller synchronises
+// before the output is read.
+template <int ACT, int S, class Emit>
+__device__ __forceinline__ void emit_mask(const uint32_t* mask, int nbits, Emit emit) {
+  constexpr int W = ACT / 64;
+  constexpr int R = (S * W + 63) / 64;  // rounds of 64 words
+  static_assert(R <= 2, "at most 128 mask words");
+  if ((int)threadIdx.x >= ACT) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nw = (nbits + 63) >> 6;
+  int excl[R];
+  int off = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = 64 * r + lane;
+    const int c = idx < nw ? __popcll(lds_mask64(mask, idx)) : 0;
+    int tot;
+    const int incl = wave_incl_scan(c, &tot);
+    excl[r] = off + incl - c;
+    off += tot;
+  }
+  uint64_t m[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) m[s] = lds_mask64(mask, min(s * W + w, nw - 1));  // reads first, then the work
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int idx = s * W + w;  // wave-uniform
+    if (idx < nw) {
+      const int e = (R == 1 || idx < 64) ? excl[0] : excl[R - 1];
+      const int base = __builtin_amdgcn_readlane(e, idx & 63);
+      emit(base + mask_rank(m[s]), 64 * idx + lane, ((m[s] >> lane) & 1ull) != 0ull);
     }
   }
-  __syncthreads();
 }
 
-// One refinement level with the kept set as a bitmask: candidates are the
-// level-j positions whose parent (p >> 1) is set in `prev`; the kept ones are
-// set in `next`.
-template <int NT, int MAXS>
-__device__ __forceinline__ void refine_level_mask(const float* cj, int n, int kj, float smin, float smax,
-                                                  const uint32_t* prev, uint32_t* next, unsigned char* raw) {
-  // the bins sit at the same offset for every MAXS (they depend on ACT only)
-  constexpr int ACT = TopKRaw<NT>::MACT;
-  auto& shm = *reinterpret_cast<TopKMaskShared<ACT, MAXS>*>(raw);
-  topk_mask<NT, ACT, MAXS>(
-      n, kj, smin, smax, shm, [&](int p, int) { return cj[p]; },
-      [&](int p) {
-        const int q = p >> 1;  // the parent at level j + 1
-        return ((prev[q >> 5] >> (q & 31)) & 1u) != 0u;
-      },
-      next);
+// One level of the fast refinement (steps A, S, M, R above).  Returns true
+// (uniformly, with every wave past its reads of the shared state) when the
+// level cannot be resolved this way.  All NT threads call it.  The code is
+// written for few vector instructions per slot: the slot bounds are scalar
+// (the wave index is uniform), the bins are computed once, the mask words of
+// a wave's slots are gathered into one lane each and stored together.
+template <int NT, int ACT, int S>
+__device__ __forceinline__ bool refine_level_fast(const float (&sj)[S], int nj, int kj, float smin, float smax,
+                                                  int par, const uint32_t* prev, uint32_t* next, RefineShared& sh) {
+  constexpr int NB = RefineShared::NB, BPL = NB / 64;
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  if (t == 0) sh.list_n[par ^ 1] = 0;  // the next level's list (last read before the previous barrier)
+  const float span = smax - smin;
+  const float scale = __fdividef((float)NB, span);  // any positive scale keeps the bins monotone
+  if (!(span > 0.f && span < 3.0e38f && scale > 0.f && scale < 3.0e38f)) return true;  // uniform
+  const float boff = -smin * scale;  // bin = floor(score * scale + boff), monotone in the score
+  const bool act = w < ACT / 64;     // uniform
+  const int pbase = 64 * w + lane;
+
+  // A. validity (parent kept), bins (-1: not a candidate), histogram.  Every
+  // slot is processed without branches; positions past n_j are invalid.
+  int bn[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) bn[s] = -1;
+  if (act) {
+    const int pmax = (nj - 1) >> 6;
+    uint32_t pw[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) pw[s] = prev[min((s * ACT + 64 * w) >> 6, pmax)];
+    const int half = lane >> 1;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const bool v = (s * ACT + pbase < nj) & (__builtin_amdgcn_ubfe(pw[s], half, 1) != 0u);
+      const int bi = min(NB - 1, max(0, (int)fmaf(sj[s], scale, boff)));
+      bn[s] = v ? bi : -1;
+      if (v) atomicAdd(&sh.hist[bi], 1);
+    }
+  }
+  __syncthreads();  // B
+  // S. the boundary bin, by every wave
+  int b, need, cnt;
+  {
+    // lane l owns bins [BPL l, BPL l + BPL); its 16-byte reads are rotated
+    // by l so that the lanes of one read fall in different LDS banks
+    const int4* h4 = reinterpret_cast<const int4*>(sh.hist + BPL * lane);
+    int tot = 0;
+#pragma unroll
+    for (int q = 0; q < BPL / 4; ++q) {
+      const int4 v = h4[(q + lane) & (BPL / 4 - 1)];
+      tot += v.x + v.y + v.z + v.w;
+    }
+    int all;
+    const int incl = wave_incl_scan(tot, &all);
+    const int above = all - incl;  // candidates in the bins of higher lanes
+    const uint64_t om = __ballot((above < kj) & (kj <= above + tot));
+    const int owner = om ? (int)__ffsll((unsigned long long)om) - 1 : 0;  // wave-uniform
+    const int above_t = __builtin_amdgcn_readlane(above, owner);
+    const int c = (lane < BPL) ? sh.hist[BPL * owner + lane] : 0;
+    int all2;
+    const int incl2 = wave_incl_scan(c, &all2);
+    const int hi_cnt = above_t + (all2 - incl2);
+    const uint64_t hm = __ballot((lane < BPL) & (hi_cnt < kj) & (kj <= hi_cnt + c));
+    const int bl = hm ? (int)__ffsll((unsigned long long)hm) - 1 : 0;
+    b = BPL * owner + bl;
+    need = kj - __builtin_amdgcn_readlane(hi_cnt, bl);
+    cnt = __builtin_amdgcn_readlane(c, bl);
+  }
+  const bool whole = cnt == need;
+  if (!whole && cnt > RefineShared::LMAX) {  // uniform: too many in the boundary bin
+    __syncthreads();                          // every wave has read the bins
+    return true;
+  }
+  // M. the mask of the candidates above the boundary (lane s gathers slot s's
+  // word pair); the boundary bin's candidates to the list, one reservation
+  // per wave
+  if (act) {
+    uint32_t col_lo = 0u, col_hi = 0u;
+    int nbd = 0;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint64_t eq = __ballot(bn[s] == b);
+      const uint64_t km = __ballot(bn[s] > b) | (whole ? eq : 0ull);
+      col_lo = (lane == s) ? (uint32_t)km : col_lo;
+      col_hi = (lane == s) ? (uint32_t)(km >> 32) : col_hi;
+      nbd += __popcll(eq);
+    }
+    if (lane < S) *reinterpret_cast<uint2*>(next + ((lane * ACT + 64 * w) >> 5)) = make_uint2(col_lo, col_hi);
+    if (!whole && nbd > 0) {  // uniform
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sh.list_n[par], nbd);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint64_t eq = __ballot(bn[s] == b);
+        if (bn[s] == b)
+          sh.list[base + mask_rank(eq)] =
+              ((uint64_t)order_key(sj[s]) << 32) | (uint64_t)(~(uint32_t)(s * ACT + pbase));
+        base += __popcll(eq);
+      }
+    }
+  }
+  __syncthreads();  // C
+  // R. exact ranks inside the boundary bin: P lanes per entry (P <= 16, a
+  // power of two, one DPP row) each count a strided share of the list
+  if (!whole) {
+    const int nl = sh.list_n[par];
+    int lg = 0;
+    while (lg < 4 && (2 << lg) * nl <= NT) ++lg;  // uniform
+    const int P = 1 << lg;
+    const int part = t & (P - 1);
+    for (int i0 = 0; i0 < nl; i0 += NT >> lg) {  // uniform trip count (the DPP sums need whole waves)
+      const int i = i0 + (t >> lg);
+      const uint64_t me = (i < nl) ? sh.list[i] : ~0ull;
+      int rank = 0;
+      for (int e = part; e < nl; e += P) rank += (sh.list[e] > me) ? 1 : 0;
+      if (lg >= 1) rank += dpp_or0<0xB1>(rank);   // quad_perm [1,0,3,2]
+      if (lg >= 2) rank += dpp_or0<0x4E>(rank);   // quad_perm [2,3,0,1]
+      if (lg >= 3) rank += dpp_or0<0x141>(rank);  // row_half_mirror
+      if (lg >= 4) rank += dpp_or0<0x140>(rank);  // row_mirror
+      if (part == 0 && i < nl && rank < need) {
+        const uint32_t p = ~(uint32_t)me;
+        atomicOr(&next[p >> 5], 1u << (p & 31));
+      }
+    }
+  }
+  for (int i = t; i < NB / 4; i += NT) reinterpret_cast<int4*>(sh.hist)[i] = make_int4(0, 0, 0, 0);
+  __syncthreads();  // D
+  return false;
 }
 
-// Recursive refinement with bitmask kept sets (covered <= MACT * MMAX).
-// LDS: [coverage scores] | sel_L | mask A | mask B | per-level key range.
-template <int NT>
+// LDS: sel_L | mask A | mask B; RefineShared in the Top-K scratch.
+template <int NT, int MMAX>
 __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
                                                  int* tsel, bool report) {
+  constexpr int ACT = TopKRaw<NT>::MACT;
+  static_assert(ACT * MMAX <= 128 * 64, "at most 128 coverage waves per head on this path");
   const int L = a.levels;
   const int covered = (int)a.covered;
-  float* cov_l = reinterpret_cast<float*>(lds);
-  int* sel_l = reinterpret_cast<int*>(lds + (a.refine_cov_in_lds ? a.cov_len : 0));
+  const int t = threadIdx.x, lane = t & 63;
+  const bool act = t < ACT;
+  int* sel_l = reinterpret_cast<int*>(lds);
   uint32_t* mask_a = reinterpret_cast<uint32_t*>(sel_l + ((a.k_top + 3) & ~3));
   uint32_t* mask_b = mask_a + a.refine_mask_words;
-  uint32_t* lvm = mask_b + a.refine_mask_words;  // [kMaxLevels][2]: each level's score range (order keys)
   const float* cov_g = a.cov + (int64_t)head * a.cov_len;
-  const float* cov = a.refine_cov_in_lds ? cov_l : cov_g;
   const int32_t* sel_top = a.sel_top + (int64_t)head * a.k_top;
-  auto& shm = *reinterpret_cast<TopKMaskShared<TopKRaw<NT>::MACT, TopKRaw<NT>::MMAX>*>(tk_raw);
-  if (a.refine_cov_in_lds) {
-    const float4* src = reinterpret_cast<const float4*>(cov_g);
-    float4* dst = reinterpret_cast<float4*>(cov_l);
-    const int n4 = (int)(a.cov_len / 4);
-    for (int i = threadIdx.x; i < n4; i += NT) dst[i] = src[i];
-  }
-  for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_top[i], 0, a.n_top - 1);
-  {  // each level's score range: wave j reduces the coverage waves' slots of level j
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int nwav = (int)((a.covered + 63) >> 6);
-    const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
-    for (int j = w; j < L; j += NT / 64) {
-      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-      for (int v = lane; v < nwav; v += 64) {
-        mn = min(mn, lm[(int64_t)v * 2 * kMaxLevels + 2 * j]);
-        mx = max(mx, lm[(int64_t)v * 2 * kMaxLevels + 2 * j + 1]);
-      }
-      mn = wave_min_u32(mn);
-      mx = wave_max_u32(mx);
-      if (lane == 0) {
-        lvm[2 * j] = mn;
-        lvm[2 * j + 1] = mx;
+  auto& sh = *reinterpret_cast<RefineShared*>(tk_raw);
+
+  // each level's score range: the coverage waves' slots (at most 128 per
+  // head here), all loaded before the scores so their wait is short
+  const int nwav = (covered + 63) >> 6;
+  const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
+  uint2 rr[kMaxLevels][2];
+#pragma unroll
+  for (int j = 0; j < kMaxLevels; ++j)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int v = lane + 64 * r;
+      rr[j][r] = (j < L && v < nwav) ? *reinterpret_cast<const uint2*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j)
+                                     : make_uint2(0xFFFFFFFFu, 0u);
+    }
+  // every level's scores into registers, coarsest level first
+  LevelScores<MMAX> sc;
+  for_levels_desc<kMaxLevels - 1>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int SJ = LevelSlots<MMAX, J>::N;
+    auto& sj = sc.template get<J>();
+    if (J < L) {
+      const int nj = covered >> J;
+      const float* src = cov_g + a.cov_off[J];
+#pragma unroll
+      for (int s = 0; s < SJ; ++s) {
+        const int p = s * ACT + t;
+        sj[s] = (act && p < nj) ? src[p] : 0.f;
       }
     }
+  });
+  // the ranges, reduced by every wave; the budgets, read once
+  uint32_t rmn[kMaxLevels], rmx[kMaxLevels];
+  int kb[kMaxLevels];  // kb[j]: the budget of level j
+#pragma unroll
+  for (int j = 0; j < kMaxLevels; ++j) {
+    rmn[j] = wave_min_u32(min(rr[j][0].x, rr[j][1].x));
+    rmx[j] = wave_max_u32(max(rr[j][0].y, rr[j][1].y));
+    kb[j] = (j < L) ? a.budgets[L - j] : 0;
   }
-  for (int i = threadIdx.x; i < a.refine_mask_words; i += NT)  // level L: every kept coarse region
+  for (int i = t; i < a.k_top; i += NT) sel_l[i] = clampi(sel_top[i], 0, a.n_top - 1);
+  for (int i = t; i < a.refine_mask_words; i += NT)  // level L: every kept coarse region
     mask_a[i] = (32 * i + 32 <= a.k_top) ? 0xFFFFFFFFu : (32 * i < a.k_top ? (1u << (a.k_top - 32 * i)) - 1u : 0u);
-  topk_mask_init<NT, TopKRaw<NT>::MACT, TopKRaw<NT>::MMAX>(shm);
+  for (int i = t; i < RefineShared::NB / 4; i += NT) reinterpret_cast<int4*>(sh.hist)[i] = make_int4(0, 0, 0, 0);
+  if (t < 2) sh.list_n[t] = 0;
   __syncthreads();
+
   int32_t* dbg_sel = (report && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
   float* dbg_score = (report && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   uint32_t* prev = mask_a;
   uint32_t* next = mask_b;
   int dbg_off = a.k_top;
+  bool general = false;
   for (int j = L - 1; j >= 0; --j) {
-    const int kj = a.budgets[L - j];
     const int nj = covered >> j;
-    const float* cj = cov + a.cov_off[j];
-    const float smin = key_to_f32(lvm[2 * j]), smax = key_to_f32(lvm[2 * j + 1]);
-    constexpr int MM = TopKRaw<NT>::MMAX, MA = TopKRaw<NT>::MACT;
-    if (nj <= MA * 4) {
-      refine_level_mask<NT, 4>(cj, nj, kj, smin, smax, prev, next, tk_raw);
-    } else if (nj <= MA * 8) {
-      refine_level_mask<NT, 8>(cj, nj, kj, smin, smax, prev, next, tk_raw);
-    } else if (MM <= 16 || nj <= MA * 16) {
-      refine_level_mask<NT, 16>(cj, nj, kj, smin, smax, prev, next, tk_raw);
-    } else {
-      refine_level_mask<NT, MM>(cj, nj, kj, smin, smax, prev, next, tk_raw);
-    }
+    uint32_t kmn = rmn[0], kmx = rmx[0];
+    int kj = kb[0];
+#pragma unroll
+    for (int i = 1; i < kMaxLevels; ++i)
+      if (i == j) {
+        kmn = rmn[i];
+        kmx = rmx[i];
+        kj = kb[i];
+      }
+    const float smin = key_to_f32(kmn), smax = key_to_f32(kmx);
+    for_levels_desc<kMaxLevels - 1>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      if (J == j)
+        general = refine_level_fast<NT, ACT, LevelSlots<MMAX, J>::N>(sc.template get<J>(), nj, kj, smin, smax, j & 1,
+                                                                      prev, next, sh);
+    });
+    if (general) break;
     if (dbg_sel || dbg_score) {
       const int sh_l = L - j;
-      mask_compact<NT>(next, nj, shm.cnt, [&](int o, int p) {
-        if (o < kj) {
+      const float* cj = cov_g + a.cov_off[j];
+      emit_mask<ACT, MMAX>(next, nj, [&](int o, int p, bool set) {
+        if (set && o < kj) {
           if (dbg_sel) dbg_sel[dbg_off + o] = (sel_l[clampi(p >> sh_l, 0, a.k_top - 1)] << sh_l) + (p & ((1 << sh_l) - 1));
           if (dbg_score) dbg_score[dbg_off + o] = cj[p];
         }
@@ -679,10 +909,15 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
     next = tmp;
     dbg_off += kj;
   }
+  if (general) {  // uniform
+    __syncthreads();  // no wave still reads the masks the list path overwrites
+    refine_head_lists<NT>(a, head, lds, tk_raw, tsel, report);
+    return;
+  }
   int32_t* so = (report && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
-  mask_compact<NT>(prev, covered, shm.cnt, [&](int o, int p) {
-    if (o < a.k0) {
-      const int tok = (sel_l[clampi(p >> L, 0, a.k_top - 1)] << L) + (p & ((1 << L) - 1));
+  emit_mask<ACT, MMAX>(prev, covered, [&](int o, int p, bool set) {
+    const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & ((1 << L) - 1));
+    if (set && o < a.k0) {
       tsel[o] = tok;
       if (so) so[o] = tok;
     }
@@ -690,14 +925,36 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
 }
 
 // Recursive refinement (Figure 2 (d)) for one head: bitmask kept sets when
-// the covered set fits the register Top-K, else sorted index lists in LDS.
+// the covered set fits the register Top-K (with level-0 slots per thread
+// fitted to it: 4, 8, 16 or 32), else sorted index lists in LDS.
 template <int NT>
 __device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
                                             int* tsel, bool report) {
-  if (a.covered <= (int64_t)TopKRaw<NT>::MACT * TopKRaw<NT>::MMAX && a.levels > 0)
-    refine_head_mask<NT>(a, head, lds, tk_raw, tsel, report);
-  else
+  constexpr int64_t ACT = TopKRaw<NT>::MACT, MMAX = TopKRaw<NT>::MMAX;
+  const int64_t cv = a.covered;
+  if (a.levels == 0 || cv > ACT * MMAX)
     refine_head_lists<NT>(a, head, lds, tk_raw, tsel, report);
+  else if (cv <= ACT * 4)
+    refine_head_mask<NT, 4>(a, head, lds, tk_raw, tsel, report);
+  else if (cv <= ACT * 8)
+    refine_head_mask<NT, 8>(a, head, lds, tk_raw, tsel, report);
+  else if (MMAX == 16 || cv <= ACT * 16)
+    refine_head_mask<NT, 16>(a, head, lds, tk_raw, tsel, report);
+  else
+    refine_head_mask<NT, (MMAX > 16 ? MMAX : 16)>(a, head, lds, tk_raw, tsel, report);
+}
+
+// ---------------------------------------------------------------------------
+// Refinement, one workgroup per head: the kept prompt tokens of the head,
+// ascending, to the workspace (the attention reads them from there), and to
+// sel_out and the per-level outputs when those are requested.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRefineThreads) void refine_kernel(StepArgs a) {
+  extern __shared__ uint32_t lds[];
+  static_assert(TopKRaw<kRefineThreads>::BYTES <= (size_t)kTopKSharedReserve, "static LDS beyond its reserve");
+  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<kRefineThreads>::BYTES];
+  const int head = blockIdx.x;
+  refine_head<kRefineThreads>(a, head, lds, tk_raw, a.sel_ws + (int64_t)head * a.k0, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -751,21 +1008,12 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   constexpr int PER = (CH * NV + NT - 1) / NT;    // vectors per thread per tensor
   static_assert(CW % 16 == 0 && (sizeof(T) != 2 || CW % 32 == 0), "whole MFMA tiles per wave");
   extern __shared__ uint32_t lds[];
-  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
-  int* tlist = reinterpret_cast<int*>(lds);        // T: kept prompt tokens, then gen_idx
-  uint32_t* scratch = lds + a.att_t_words;         // refinement state, K/V buffers, merge slots
+  int* tlist = reinterpret_cast<int*>(lds);        // this split's part of T (kept prompt tokens, then gen_idx)
+  uint32_t* scratch = lds + a.att_t_words;         // K/V buffers, merge slots
   T* Ks = reinterpret_cast<T*>(scratch);
   T* Vt = Ks + CH * KS;
 
   const int head = blockIdx.y, split = blockIdx.x;
-  if (a.attend_only) {  // a selection made earlier: attention only
-    for (int i = threadIdx.x; i < a.k0; i += NT) tlist[i] = clampi(a.sel_in[(int64_t)head * a.k0 + i], 0, a.n_tot - 1);
-  } else {
-    refine_head<NT>(a, head, scratch, tk_raw, tlist, split == 0);
-  }
-  for (int i = threadIdx.x; i < a.n_gen; i += NT) tlist[a.k0 + i] = clampi(a.gen_idx[i], 0, a.n_tot - 1);
-  __syncthreads();
-
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qt = w / TG, tg = w - qt * TG;
   const int g = lane >> 4, l16 = lane & 15;
@@ -774,9 +1022,21 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
   const T* vh = reinterpret_cast<const T*>(a.v) + (int64_t)head * a.n_tot * D;
 
+  // this wave's query fragment, in flight while the token list arrives
   Frag<T, D> qf;
   const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
   if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
+
+  // the attended tokens of this split's chunks: T positions [t0, t0 + tcount)
+  const int c_begin = split * a.chunks_per_split;
+  const int c_end = min(a.n_chunks, c_begin + a.chunks_per_split);
+  const int t0 = c_begin * CH;
+  const int tcount = max(0, min(a.n_att, c_end * CH) - t0);
+  for (int i = threadIdx.x; i < tcount; i += NT) {
+    const int gi = t0 + i;
+    tlist[i] = clampi(gi < a.k0 ? a.sel_in[(int64_t)head * a.k0 + gi] : a.gen_idx[gi - a.k0], 0, a.n_tot - 1);
+  }
+  __syncthreads();
 
   const float sl2 = a.inv_sqrt_d * 1.44269504088896340736f;  // log2(e)/sqrt(d)
   SoftmaxState<D> st;
@@ -784,9 +1044,6 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int c_begin = split * a.chunks_per_split;
-  const int c_end = min(a.n_chunks, c_begin + a.chunks_per_split);
 
   // K and V: vector e = (row, cv) of the chunk, row-major, so each wave-wide
   // load reads whole rows.  K rows go to LDS as they are.  bfloat16 V goes to
@@ -812,7 +1069,7 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
       kreg[i] = u32x4{0u, 0u, 0u, 0u};
       vreg[i] = u32x4{0u, 0u, 0u, 0u};
       if (e < CH * NV && pos < a.n_att) {  // plain loads: the non-temporal hint slows scattered row gathers
-        const int64_t tok = tlist[pos];
+        const int64_t tok = tlist[pos - t0];
         kreg[i] = *reinterpret_cast<const u32x4*>(kh + tok * D + cv * VE);
         vreg[i] = *reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE);
       }
@@ -1034,8 +1291,8 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.k = L.k;
   a.v = L.v;
   a.gen_idx = L.gen_idx;
-  a.sel_in = L.sel_in;
-  a.attend_only = L.attend_only;
+  a.sel_ws = reinterpret_cast<int32_t*>(L.ws + P.off_sel);
+  a.sel_in = L.attend_only ? L.sel_in : a.sel_ws;
   a.out = L.out;
   a.sel_out = L.sel_out;
   a.sel_levels = L.sel_levels;
@@ -1107,6 +1364,9 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
     WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = allow_lds(refine_kernel, P.refine_lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(refine_kernel, dim3(H), dim3(kRefineThreads), P.refine_lds, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt * kAttendGroups), P.attend_lds);

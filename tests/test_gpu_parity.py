@@ -276,3 +276,32 @@ def test_attend_selected_edge_cases(name, cfg, k0, n_gen):
             ref = oracle_attend_selected_head(inp.q, inp, sel[b, h].numpy(), g, b, h)
             err = np.abs(out[b, h].cpu().numpy() - ref).max()
             assert err <= TOL[cfg.dtype], (b, h, err)
+
+
+@pytest.mark.parametrize("spike", [False, True], ids=["flat", "crowded"])
+def test_tied_levels_match_the_oracle_exactly(spike):
+    """Prompt keys that are all one row give every candidate of a level the
+    same score (no score range to bin); with a block of rows three times
+    larger on top, most candidates of a level tie inside one bin, more than
+    the in-bin ranking takes at level 0.  Both take the general path where
+    needed; ties go to the lower index, at every level."""
+    say(f"[tied levels {'crowded' if spike else 'flat'}]")
+    from _parity import oracle_head, split_levels_np
+    cfg = custom(2, cid=79, heads=2, n_prompt=4096, n_gen=8, levels=4, n_spans=0)
+    budgets = [32, 60, 110, 200, 350]
+    inp = make_layer(cfg, 0)
+    for h in range(cfg.heads):
+        row = (0.5 * inp.q[0, h].float().mean(0)).to(inp.k.dtype)
+        inp.k[0, h, :cfg.n_prompt] = row
+        if spike:
+            inp.k[0, h, 1000:1100] = (3.0 * row.float()).to(inp.k.dtype)
+    to_dev(inp)
+    _, res = run(inp, budgets, 4)
+    check_structure(res, budgets, 4, cfg.n_prompt)
+    for h in range(cfg.heads):
+        out_ora, ora = oracle_head(inp, 0, h, budgets, 4)
+        lv = split_levels_np(res["sel_levels"][0, h].cpu().numpy(), budgets)
+        for j in range(4, -1, -1):
+            np.testing.assert_array_equal(lv[j], ora.sel[j], err_msg=f"level {j} head {h}")
+        np.testing.assert_array_equal(res["sel"][0, h].cpu().numpy(), ora.sel[0])
+        assert np.abs(res["out"][0, h].cpu().numpy() - out_ora).max() <= TOL["bf16"]
