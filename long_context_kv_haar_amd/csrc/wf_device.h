@@ -117,17 +117,38 @@ __device__ __forceinline__ float group_sum_step(float x, int lvl) {
   }
 }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+// Exchanges across 16-lane rows with the gfx950 lane permutes, which stay in
+// the VALU (a shuffle through ds_bpermute is an LDS round trip).
+// permlane16_swap(x, x) returns (x of rows 0,0,2,2 ; x of rows 1,1,3,3) and
+// permlane32_swap(x, x) returns (x of halves lo,lo ; x of halves hi,hi), so
+// the two results hold each lane's value and its partner's.
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t x) {  // x of lane l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {  // x of lane l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float wave_sum_xor_16_32(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
+__device__ __forceinline__ float wave_max_xor_16_32(float x) { return max_xor32(max_xor16(x)); }
+__device__ __forceinline__ float wave_sum_xor_16_32(float x) { return sum_xor32(sum_xor16(x)); }
 
 // ---------------------------------------------------------------------------
 // Order-preserving keys: key(a) > key(b)  <=>  a > b for finite floats;

@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += __shfl_xor(s[t][qt][0], 16, 64);
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor16(s[t][qt][0]);
       float x = s[t][0][0];
 #pragma unroll
       for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += __shfl_xor(s[t][qt][0], 32, 64);
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor32(s[t][qt][0]);
       float x = s[t][0][0];
 #pragma unroll
       for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
@@ -972,6 +972,14 @@ __global__ __launch_bounds__(kRefineThreads) void refine_kernel(StepArgs a) {
 // chunk's rows are fetched into registers while the current one computes.
 // Writes the split's partial (m, l, O) to the workspace.
 // ---------------------------------------------------------------------------
+// x of lane l ^ NV: a DPP row rotation by 8 for NV = 8, a lane permute for 16.
+template <int NV>
+__device__ __forceinline__ uint32_t lane_xor_nv(uint32_t x) {
+  static_assert(NV == 8 || NV == 16, "pair partners NV lanes apart");
+  if constexpr (NV == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  else return lane_xor16(x);
+}
+
 template <typename T> struct AttendTraits;
 template <> struct AttendTraits<bf16_t> { static constexpr int KPAD = 8, VPAD = 16, DT = WF_BF16; };
 template <> struct AttendTraits<float> { static constexpr int KPAD = 4, VPAD = 4, DT = WF_F32; };
@@ -1091,8 +1099,8 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
       } else {
         const u32x4 x = vreg[i];
         const bool odd = row & 1;  // odd rows write elements 4..7 of the pair, even rows 0..3
-        const uint32_t r0 = __shfl_xor(odd ? x[0] : x[2], NV, 64);
-        const uint32_t r1 = __shfl_xor(odd ? x[1] : x[3], NV, 64);
+        const uint32_t r0 = lane_xor_nv<NV>(odd ? x[0] : x[2]);
+        const uint32_t r1 = lane_xor_nv<NV>(odd ? x[1] : x[3]);
         const uint32_t lo0 = odd ? r0 : x[0], hi0 = odd ? x[2] : r0;  // element pairs (row 2p, row 2p + 1)
         const uint32_t lo1 = odd ? r1 : x[1], hi1 = odd ? x[3] : r1;
         const uint32_t w4[4] = {(lo0 & 0xFFFFu) | (hi0 << 16), (lo0 >> 16) | (hi0 & 0xFFFF0000u),
@@ -1125,8 +1133,7 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
           sv[t][r] = x;
           cmax = fmaxf(cmax, x);
         }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      cmax = wave_max_xor_16_32(cmax);
       const float m_new = fmaxf(st.m, cmax);  // finite: the slice holds a valid token
       const float alpha = exp2f(st.m - m_new);
       float psum = 0.f;
@@ -1191,8 +1198,7 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
 
   // Row sums over the four lane groups, then a tree merge of the TG states of
   // each query tile through LDS (slots alias the K/V buffers).
-  st.l += __shfl_xor(st.l, 16, 64);
-  st.l += __shfl_xor(st.l, 32, 64);
+  st.l = wave_sum_xor_16_32(st.l);
   constexpr int SLOT = 64 * (D / 4 + 2);  // floats per merge slot
   float* slots = reinterpret_cast<float*>(scratch);
 #pragma unroll
