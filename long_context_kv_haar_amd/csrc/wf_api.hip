@@ -101,15 +101,9 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // cover kernel: kept coarse regions (+ the coarse keys when they fit) in LDS
   P->coarse_keys_in_lds = P->n_top <= wf::kMaxCoarseLds;
   P->cover_lds = 4 * (((P->k_top + 3) & ~3) + (P->coarse_keys_in_lds ? P->n_top : 0));
-  // attention: about one workgroup per compute unit in total
-  P->n_att = P->k0 + n_gen;
+  // attention splits
   P->chunk = wf::attend_chunk(pyr->dtype);
-  P->n_chunks = (P->n_att + P->chunk - 1) / P->chunk;
-  int target = (256 + P->heads_total - 1) / P->heads_total;
-  if (target > wf::kMaxSplit) target = wf::kMaxSplit;
-  if (target < 1) target = 1;
-  P->chunks_per_split = (P->n_chunks + target - 1) / target;
-  P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
+  wf::plan_attention_splits(P, true);
   // refinement workgroup LDS (one per head): the kept sets and candidate
   // lists, plus the coverage scores when they fit
   P->refine_nmax = (nmax + 3) / 4 * 4;
@@ -128,8 +122,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   if (refine_base > budget) return WF_ERR_BUDGET;
   P->refine_cov_in_lds = (refine_base + 4 * P->cov_len) <= budget;
   P->refine_lds = (int)(refine_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0));
-  // attention workgroup LDS: the attended-set list, then the K/V chunk buffers
-  P->att_t_words = (P->chunks_per_split * P->chunk + 3) & ~3;  // one split's part of T
+  // attention workgroup LDS: the split's part of T, then the K/V chunk buffers
   const int64_t buf_bytes = wf::attend_buffer_bytes(pyr->dtype, pyr->head_dim, (n_q + 15) / 16);
   if (buf_bytes > wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words) return WF_ERR_BUDGET;
   P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
@@ -163,15 +156,8 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
   P->dtype = dtype;
   P->k0 = k0;
   P->n_gen = n_gen;
-  P->n_att = k0 + n_gen;
   P->chunk = wf::attend_chunk(dtype);
-  P->n_chunks = (P->n_att + P->chunk - 1) / P->chunk;
-  int target = (256 + P->heads_total - 1) / P->heads_total;
-  if (target > wf::kMaxSplit) target = wf::kMaxSplit;
-  if (target < 1) target = 1;
-  P->chunks_per_split = (P->n_chunks + target - 1) / target;
-  P->n_split = (P->n_chunks + P->chunks_per_split - 1) / P->chunks_per_split;
-  P->att_t_words = (P->chunks_per_split * P->chunk + 3) & ~3;  // one split's part of T
+  wf::plan_attention_splits(P, false);
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
   const int64_t buf_bytes = wf::attend_buffer_bytes(dtype, head_dim, (n_q + 15) / 16);
   if (buf_bytes > budget) return WF_ERR_BUDGET;

@@ -17,7 +17,6 @@ constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to thi
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
-constexpr int kRefineThreads = 512;       // one refinement workgroup per head
 constexpr int kMaskGroup = 2048;          // least positions a refinement mask spans
 constexpr int kCoverThreads = 256;
 
@@ -29,8 +28,11 @@ struct SelectPlan {
   int64_t covered;              // k_L 2^L
   int64_t cov_len;              // floats per head over levels 0..L-1 (each level 16-byte aligned)
   int64_t cov_off[kMaxLevels];  // float offset of level j inside a head's slice
-  // attention
-  int n_att, chunk, n_chunks, n_split, chunks_per_split;
+  // attention: T = kept prompt tokens [0, k0) then generated positions
+  // [k0, k0 + n_gen), each part cut into chunks of `chunk` tokens on its own;
+  // splits 0 .. n_split_p - 1 take cps_p prompt chunks each, the remaining
+  // n_split - n_split_p take cps_g generated chunks each
+  int n_att, chunk, n_split, n_split_p, cps_p, cps_g;
   // LDS plans (bytes)
   int cover_lds;                // kept coarse regions (+ coarse keys when staged)
   int coarse_keys_in_lds;
@@ -61,6 +63,40 @@ struct SelectLaunch {
 };
 
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
+
+// Split plan of the attention over T (fills n_att .. cps_g from k0, n_gen,
+// chunk and heads_total), about one workgroup per compute unit over all heads.
+// gen_apart: the generated part's splits run in another launch (beside the
+// refinement), so the prompt part alone fills the chip and the generated part
+// takes up to 4 splits of its own; otherwise both parts share one count of
+// chunks per split.  At most kMaxSplit splits in all.
+inline void plan_attention_splits(SelectPlan* P, bool gen_apart) {
+  const int ch = P->chunk;
+  P->n_att = P->k0 + P->n_gen;
+  const int nc_p = (P->k0 + ch - 1) / ch, nc_g = (P->n_gen + ch - 1) / ch;
+  int target = (256 + P->heads_total - 1) / P->heads_total;
+  if (target > kMaxSplit) target = kMaxSplit;
+  if (gen_apart) {
+    const int sg = nc_g < 4 ? nc_g : 4;
+    P->cps_g = sg > 0 ? (nc_g + sg - 1) / sg : 1;
+    const int n_split_g = sg > 0 ? (nc_g + P->cps_g - 1) / P->cps_g : 0;
+    if (target > kMaxSplit - n_split_g) target = kMaxSplit - n_split_g;
+    if (target < 1) target = 1;
+    P->cps_p = nc_p > 0 ? (nc_p + target - 1) / target : 1;
+    P->n_split_p = nc_p > 0 ? (nc_p + P->cps_p - 1) / P->cps_p : 0;
+    P->n_split = P->n_split_p + n_split_g;
+  } else {
+    if (target < 2) target = 2;  // room for a prompt and a generated split
+    int cps = (nc_p + nc_g + target - 1) / target;
+    if (cps < 1) cps = 1;
+    while ((nc_p + cps - 1) / cps + (nc_g + cps - 1) / cps > target) ++cps;
+    P->cps_p = P->cps_g = cps;
+    P->n_split_p = (nc_p + cps - 1) / cps;
+    P->n_split = P->n_split_p + (nc_g + cps - 1) / cps;
+  }
+  const int cps = P->cps_p > P->cps_g ? P->cps_p : P->cps_g;
+  P->att_t_words = (cps * ch + 3) & ~3;  // one split's part of T
+}
 
 // Tokens per attention chunk; each of the kAttendGroups waves of a query
 // tile takes an equal slice.

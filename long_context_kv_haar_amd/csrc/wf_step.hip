@@ -9,7 +9,9 @@
 //                   taken by linearity from the token dot products)
 //   refine_kernel   the recursive refinement, one workgroup per head, with
 //                   the coverage scores in registers and the kept sets as
-//                   bitmasks in LDS; writes the kept prompt tokens
+//                   bitmasks in LDS; writes the kept prompt tokens.  Its
+//                   other workgroups attend over the generated positions
+//                   (independent of the selection) meanwhile
 //   attend_kernel   split-K online-softmax attention over the kept prompt
 //                   tokens plus the generated positions (eq. 3 restricted to
 //                   that set); also serves a selection handed in by the caller
@@ -49,7 +51,7 @@ struct StepArgs {
   int64_t covered, cov_len;
   int64_t cov_off[kMaxLevels];
   int budgets[kMaxLevels + 1];
-  int n_att, n_chunks, n_split, chunks_per_split;
+  int n_att, n_split, n_split_p, cps_p, cps_g;
   int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, refine_mask_words, att_t_words;
   float inv_sqrt_d;
 };
@@ -230,7 +232,7 @@ __device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, 
 template <typename T, int D, int RT>
 __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   constexpr int NT = kCoverThreads;
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __align__(16) uint32_t lds[];
   __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
@@ -945,19 +947,6 @@ __device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Refinement, one workgroup per head: the kept prompt tokens of the head,
-// ascending, to the workspace (the attention reads them from there), and to
-// sel_out and the per-level outputs when those are requested.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRefineThreads) void refine_kernel(StepArgs a) {
-  extern __shared__ uint32_t lds[];
-  static_assert(TopKRaw<kRefineThreads>::BYTES <= (size_t)kTopKSharedReserve, "static LDS beyond its reserve");
-  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<kRefineThreads>::BYTES];
-  const int head = blockIdx.x;
-  refine_head<kRefineThreads>(a, head, lds, tk_raw, a.sel_ws + (int64_t)head * a.k0, true);
-}
-
-// ---------------------------------------------------------------------------
 // Sparse attention (eq. 3 over T = kept prompt tokens, then gen_idx).
 // Workgroup (split, head) first runs the refinement with all its threads,
 // leaving T in LDS, then walks chunks of CH tokens.  Wave w owns query tile
@@ -1004,7 +993,7 @@ __device__ __forceinline__ void merge_state(SoftmaxState<D>& a, float mb, float 
 }
 
 template <typename T, int D, int NQT>
-__global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepArgs a) {
+__device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, int head, int split) {
   constexpr int TG = kAttendGroups;
   constexpr int NT = 64 * NQT * TG;
   constexpr int CH = attend_chunk(AttendTraits<T>::DT);
@@ -1015,13 +1004,11 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   constexpr int NV = D / VE;                      // vectors per row
   constexpr int PER = (CH * NV + NT - 1) / NT;    // vectors per thread per tensor
   static_assert(CW % 16 == 0 && (sizeof(T) != 2 || CW % 32 == 0), "whole MFMA tiles per wave");
-  extern __shared__ uint32_t lds[];
   int* tlist = reinterpret_cast<int*>(lds);        // this split's part of T (kept prompt tokens, then gen_idx)
   uint32_t* scratch = lds + a.att_t_words;         // K/V buffers, merge slots
   T* Ks = reinterpret_cast<T*>(scratch);
   T* Vt = Ks + CH * KS;
 
-  const int head = blockIdx.y, split = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int qt = w / TG, tg = w - qt * TG;
   const int g = lane >> 4, l16 = lane & 15;
@@ -1035,11 +1022,14 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
   if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
 
-  // the attended tokens of this split's chunks: T positions [t0, t0 + tcount)
-  const int c_begin = split * a.chunks_per_split;
-  const int c_end = min(a.n_chunks, c_begin + a.chunks_per_split);
-  const int t0 = c_begin * CH;
-  const int tcount = max(0, min(a.n_att, c_end * CH) - t0);
+  // the attended tokens of this split: T positions [t0, t_end), in nck chunks
+  // (prompt splits first, then the generated positions' splits)
+  const bool gen_part = split >= a.n_split_p;
+  const int cps = gen_part ? a.cps_g : a.cps_p;
+  const int t0 = gen_part ? a.k0 + (split - a.n_split_p) * cps * CH : split * cps * CH;
+  const int t_end = min(gen_part ? a.n_att : a.k0, t0 + cps * CH);
+  const int tcount = max(0, t_end - t0);
+  const int nck = (tcount + CH - 1) / CH;
   for (int i = threadIdx.x; i < tcount; i += NT) {
     const int gi = t0 + i;
     tlist[i] = clampi(gi < a.k0 ? a.sel_in[(int64_t)head * a.k0 + gi] : a.gen_idx[gi - a.k0], 0, a.n_tot - 1);
@@ -1073,19 +1063,19 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
     for (int i = 0; i < PER; ++i) {
       const int e = threadIdx.x + i * NT;
       const int row = e / NV, cv = e - row * NV;
-      const int pos = chunk * CH + row;
+      const int pos = t0 + chunk * CH + row;
       kreg[i] = u32x4{0u, 0u, 0u, 0u};
       vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (e < CH * NV && pos < a.n_att) {  // plain loads: the non-temporal hint slows scattered row gathers
+      if (e < CH * NV && pos < t_end) {  // plain loads: the non-temporal hint slows scattered row gathers
         const int64_t tok = tlist[pos - t0];
         kreg[i] = *reinterpret_cast<const u32x4*>(kh + tok * D + cv * VE);
         vreg[i] = *reinterpret_cast<const u32x4*>(vh + tok * D + cv * VE);
       }
     }
   };
-  if (c_begin < c_end) fetch(c_begin);
-  for (int chunk = c_begin; chunk < c_end; ++chunk) {
-    const int pos0 = chunk * CH + tg * CW;  // first token of this wave's slice
+  if (nck > 0) fetch(0);
+  for (int chunk = 0; chunk < nck; ++chunk) {  // chunk: index within this split
+    const int pos0 = t0 + chunk * CH + tg * CW;  // first token of this wave's slice
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = threadIdx.x + i * NT;
@@ -1113,9 +1103,9 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
       }
     }
     __syncthreads();
-    if (chunk + 1 < c_end) fetch(chunk + 1);  // overlaps with the math below
+    if (chunk + 1 < nck) fetch(chunk + 1);  // overlaps with the math below
 
-    if (pos0 < a.n_att) {  // wave-uniform: a slice wholly past the end has no work
+    if (pos0 < t_end) {  // wave-uniform: a slice wholly past the end has no work
       f32x4 sv[CW / 16];
 #pragma unroll
       for (int t = 0; t < CW / 16; ++t) {
@@ -1129,7 +1119,7 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int pos = pos0 + 16 * t + 4 * g + r;
-          const float x = (pos < a.n_att) ? sv[t][r] * sl2 : -INFINITY;
+          const float x = (pos < t_end) ? sv[t][r] * sl2 : -INFINITY;
           sv[t][r] = x;
           cmax = fmaxf(cmax, x);
         }
@@ -1235,6 +1225,36 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepAr
   }
 }
 
+template <typename T, int D, int NQT>
+__global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// Refinement, one workgroup per head (workgroups 0 .. heads_total - 1): the
+// kept prompt tokens of the head, ascending, to the workspace (the attention
+// reads them from there), and to sel_out and the per-level outputs when those
+// are requested.  The workgroups after them take the attention splits of the
+// generated positions, which do not depend on the selection, so they run
+// while the refinement does.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NQT>
+__global__ __launch_bounds__(64 * NQT * kAttendGroups) void refine_kernel(StepArgs a) {
+  constexpr int NT = 64 * NQT * kAttendGroups;
+  extern __shared__ __align__(16) uint32_t lds[];
+  static_assert(TopKRaw<NT>::BYTES <= (size_t)kTopKSharedReserve, "static LDS beyond its reserve");
+  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
+  if ((int)blockIdx.x < a.heads_total) {
+    const int head = blockIdx.x;
+    refine_head<NT>(a, head, lds, tk_raw, a.sel_ws + (int64_t)head * a.k0, true);
+  } else {
+    const int gsplits = a.n_split - a.n_split_p;
+    const int idx = blockIdx.x - a.heads_total;
+    attend_split<T, D, NQT>(a, lds, idx / gsplits, a.n_split_p + idx % gsplits);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Merge of the split partials: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s,
 // M = max_s m_s (m in log2 units; an empty split has m = -inf, l = 0).
@@ -1324,9 +1344,10 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   for (int j = 0; j < kMaxLevels; ++j) a.cov_off[j] = P.cov_off[j];
   for (int j = 0; j <= kMaxLevels; ++j) a.budgets[j] = P.budgets[j];
   a.n_att = P.n_att;
-  a.n_chunks = P.n_chunks;
   a.n_split = P.n_split;
-  a.chunks_per_split = P.chunks_per_split;
+  a.n_split_p = P.n_split_p;
+  a.cps_p = P.cps_p;
+  a.cps_g = P.cps_g;
   a.coarse_keys_in_lds = P.coarse_keys_in_lds;
   a.refine_cov_in_lds = P.refine_cov_in_lds;
   a.refine_nmax = P.refine_nmax;
@@ -1371,11 +1392,16 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
     const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
     WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = allow_lds(refine_kernel, P.refine_lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(refine_kernel, dim3(H), dim3(kRefineThreads), P.refine_lds, s, a);
+    // one refinement workgroup per head, then the generated positions' attention splits
+    const int lds_r = P.refine_lds > P.attend_lds ? P.refine_lds : P.attend_lds;
+    const unsigned refine_blocks = (unsigned)(H + H * (P.n_split - P.n_split_p));
+    WF_RT_SWITCH(WF_LAUNCH, refine_kernel, dim3(refine_blocks), dim3(64 * rt * kAttendGroups), lds_r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(P.n_split, H), dim3(64 * rt * kAttendGroups), P.attend_lds);
+  // the prompt splits (and, for a handed-in selection, the generated ones too)
+  const unsigned att_splits = (unsigned)(L.attend_only ? P.n_split : P.n_split_p);
+  if (att_splits > 0)
+    WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(att_splits, H), dim3(64 * rt * kAttendGroups), P.attend_lds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned comb_blocks = (unsigned)(((int64_t)H * P.n_q * (P.head_dim / 4) + 255) / 256);
   if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, a);
