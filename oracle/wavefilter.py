@@ -25,7 +25,8 @@ Readings where the pages are silent (each is also listed in the design
 notes): orthonormal Haar filters; the pair (x[2n], x[2n+1]) forms coefficient
 n, so level-j coefficient n covers tokens [n 2^j, (n+1) 2^j) and has exactly
 the children 2n, 2n+1; the score of a region is the maximum over the query
-rows of the scaled dot product with its approximation coefficient; only the
+rows of the scaled dot product with its approximation coefficient (or, as
+the variant "mean", its average over the rows); only the
 two children of a selected region become candidates at the next finer level;
 ties go to the lower index; the generated positions are always attended and
 never scored; no mask.
@@ -108,21 +109,27 @@ def haar_reconstruct(a_top, details):
     return x
 
 
-def level_scores(q, coeff_rows):
-    """Score of each region: max over query rows of the scaled dot product.
+AGGREGATIONS = ("max", "mean")
+
+
+def level_scores(q, coeff_rows, agg="max"):
+    """Score of each region: the query rows' scaled dot products, aggregated.
 
     ``q`` is ``[n_q, d]``, ``coeff_rows`` is ``[m, d]`` (the approximation
     coefficients of the m candidate regions).  Returns ``[m]`` with
-    ``s[c] = max_i (q_i . a_c) / sqrt(d)``.  The dot product against the
-    low-frequency keys is the "correlation" of Figure 2 (c); the 1/sqrt(d)
-    factor is the one of eq. 3; the maximum over the query block is the
-    aggregation reading adopted where the pages say nothing.
+    ``s[c] = max_i (q_i . a_c) / sqrt(d)`` for ``agg="max"`` and the mean
+    over i for ``agg="mean"``.  The dot product against the low-frequency
+    keys is the "correlation" of Figure 2 (c); the 1/sqrt(d) factor is the
+    one of eq. 3; how the query block is combined is not stated on the
+    pages: the maximum is the main reading, the mean a variant.
     """
+    if agg not in AGGREGATIONS:
+        raise ValueError("unknown aggregation")
     q = np.asarray(q, dtype=np.float64)
     coeff_rows = np.asarray(coeff_rows, dtype=np.float64)
     d = q.shape[1]
     logits = q @ coeff_rows.T / math.sqrt(d)
-    return logits.max(axis=0)
+    return logits.max(axis=0) if agg == "max" else logits.mean(axis=0)
 
 
 def top_k(candidates, scores, k):
@@ -169,7 +176,7 @@ class SelectResult:
     detail: list = None
 
 
-def select(q, k_prompt, budgets, levels):
+def select(q, k_prompt, budgets, levels, agg="max"):
     """Coarse-to-fine token selection for one head.
 
     Steps (WaveFilter section 3.1 and Figure 2 (b)-(d)):
@@ -181,7 +188,8 @@ def select(q, k_prompt, budgets, levels):
        region kept at level j+1; score them with A_j and keep the top
        ``budgets[L-j]``.
 
-    ``budgets`` lists k_L, k_{L-1}, ..., k_0.  Returns a ``SelectResult``.
+    ``budgets`` lists k_L, k_{L-1}, ..., k_0; ``agg`` is the aggregation of
+    ``level_scores``.  Returns a ``SelectResult``.
     """
     q = np.asarray(q, dtype=np.float64)
     if len(budgets) != levels + 1:
@@ -194,7 +202,7 @@ def select(q, k_prompt, budgets, levels):
         if j < levels:
             parents = res.sel[j + 1]
             cand = np.sort(np.concatenate([2 * parents, 2 * parents + 1]))
-        s = level_scores(q, approx[j][cand])
+        s = level_scores(q, approx[j][cand], agg)
         chosen, gap = top_k(cand, s, budgets[levels - j])
         res.cand[j] = cand
         res.scores[j] = s
@@ -220,7 +228,7 @@ def attend(q, keys, values):
     return w @ values
 
 
-def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels):
+def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels, agg="max"):
     """One per-step call for one head: select prompt tokens, then attend.
 
     ``k_all``/``v_all`` are the cached rows ``[N_tot, d]`` with the prompt at
@@ -231,7 +239,7 @@ def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels):
     """
     k_all = np.asarray(k_all, dtype=np.float64)
     v_all = np.asarray(v_all, dtype=np.float64)
-    res = select(q, k_all[:n_prompt], budgets, levels)
+    res = select(q, k_all[:n_prompt], budgets, levels, agg)
     rows = np.concatenate([res.sel[0], np.asarray(gen_idx, dtype=np.int64)])
     out = attend(q, k_all[rows], v_all[rows])
     return out, res

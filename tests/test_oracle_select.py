@@ -182,3 +182,60 @@ def test_invariances():
     s1 = level_scores(q, a1[2][c_reg:c_reg + 1])[0]
     s2 = level_scores(q, a2[2][c_reg:c_reg + 1])[0]
     assert abs(s2 - factor * s1) < 1e-12
+
+
+# -- the "mean" aggregation variant (the query rows' scores averaged) --------
+
+def test_mean_scores_are_the_mean_query_loop():
+    """Mean aggregation, written out as a double loop over rows and columns."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((5, 8))
+    a = rng.standard_normal((7, 8))
+    got = level_scores(q, a, "mean")
+    for c in range(7):
+        acc = 0.0
+        for i in range(5):
+            acc += sum(q[i, t] * a[c, t] for t in range(8))
+        assert abs(got[c] - acc / 5 / math.sqrt(8)) < 1e-12
+
+
+def test_mean_selection_is_the_averaged_query_selection():
+    """By linearity the mean of the rows' scores is the score of the mean
+    query row, and with one row every aggregation agrees: the mean selection
+    of a block equals the selection of its single averaged row, at every level."""
+    rng = np.random.default_rng(22)
+    for levels, n_p, budgets in [(3, 256, [5, 9, 16, 30]), (4, 512, [6, 10, 17, 30, 50]), (0, 64, [20])]:
+        q = rng.standard_normal((6, 16))
+        kp = rng.standard_normal((n_p, 16))
+        mean = select(q, kp, budgets, levels, "mean")
+        single = select(q.mean(axis=0, keepdims=True), kp, budgets, levels, "max")
+        for j in range(levels + 1):
+            assert list(mean.sel[j]) == list(single.sel[j])
+
+
+def test_max_and_mean_pick_different_tokens():
+    """Hand-worked: rows (1, 0) and (0, 1); token 0 = (3, -3) scores 3/sqrt2
+    for one row and -3/sqrt2 for the other, token 1 = (1, 1) scores 1/sqrt2
+    for both.  The maximum keeps token 0 (3/sqrt2 > 1/sqrt2), the mean keeps
+    token 1 (0 < 1/sqrt2)."""
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    kp = np.array([[3.0, -3.0], [1.0, 1.0]])
+    s_max = level_scores(q, kp, "max")
+    s_mean = level_scores(q, kp, "mean")
+    assert np.allclose(s_max, [3 / math.sqrt(2), 1 / math.sqrt(2)])
+    assert np.allclose(s_mean, [0.0, 1 / math.sqrt(2)])
+    assert list(select(q, kp, [1], 0, "max").sel[0]) == [0]
+    assert list(select(q, kp, [1], 0, "mean").sel[0]) == [1]
+
+
+def test_duplicated_row_moves_the_mean_not_the_max():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((4, 8))
+    a = rng.standard_normal((9, 8))
+    q_dup = np.concatenate([q, q[1:2]])
+    assert np.array_equal(level_scores(q_dup, a, "max"), level_scores(q, a, "max"))
+    per_row = q @ a.T / math.sqrt(8)
+    want = (per_row.sum(axis=0) + per_row[1]) / 5
+    assert np.allclose(level_scores(q_dup, a, "mean"), want, atol=1e-12)
+    with pytest.raises(ValueError):
+        level_scores(q, a, "median")
