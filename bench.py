@@ -210,6 +210,21 @@ def main():
     torch.cuda.synchronize()
     sel_only_ms = s0.elapsed_time(s1) / K
 
+    # -- select-attend with the query rows averaged instead of maximised (same bytes)
+    steps_mean = []
+    for c, pb, (out, sel) in zip(copies, builds, outs):
+        steps_mean.append(wf.PreparedStep(c.q, pb.pyramid, c.k, c.v, c.gen_idx, budgets, torch.empty_like(out),
+                                          torch.empty_like(sel), ws, agg="mean"))
+    for i in range(args.warmup):
+        steps_mean[i % R]()
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for i in range(K):
+        steps_mean[i % R]()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    mean_ms = s0.elapsed_time(s1) / K
+
     # -- attention over the selection each copy's last call made (a later step reusing it)
     reuse = [wf.PreparedAttend(c.q, c.k, c.v, sel, c.gen_idx, torch.empty_like(out), ws)
              for c, (out, sel) in zip(copies, outs)]
@@ -266,6 +281,11 @@ def main():
             "algorithmic_bytes": sel_bytes,
             "achieved_GBps": round(sel_gbs, 1),
             "frac_of_hbm_peak": round(sel_gbs / HBM_PEAK_GBS, 4),
+        },
+        "select_attend_mean_rows": {
+            "calls_per_s": 1e3 / mean_ms,
+            "us_per_call": round(mean_ms * 1e3, 2),
+            "achieved_GBps": round(sel_bytes / (mean_ms * 1e-3) / 1e9, 1),
         },
         "attend_selected": {
             "calls_per_s": 1e3 / reuse_ms,

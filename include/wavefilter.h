@@ -53,8 +53,15 @@ enum {
     WF_ERR_WORKSPACE = -6, /* workspace or pyramid buffer too small */
     WF_ERR_ALIGN = -7,     /* a pointer or stride is not 16-byte aligned */
     WF_ERR_HIP = -8,       /* a HIP launch failed */
-    WF_ERR_PYRAMID = -9    /* pyramid descriptor not built by wf_build_pyramid */
+    WF_ERR_PYRAMID = -9,   /* pyramid descriptor not built by wf_build_pyramid */
+    WF_ERR_OPTION = -10    /* an option argument has no defined meaning */
 };
+
+/* How the n_q query rows combine into one region score (Figure 2 (c) scores
+ * regions by the queries' correlation with the low-frequency keys and leaves
+ * the combination of the rows open): the maximum over the rows, or their
+ * mean (which equals the score of the averaged query row). */
+enum { WF_AGG_MAX = 0, WF_AGG_MEAN = 1 };
 
 /* Element types of q, k and v. */
 enum { WF_F32 = 0, WF_BF16 = 1 };
@@ -144,11 +151,11 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
 
 /*
  * One denoising step of WaveFilter for every (sequence, head):
- *   1. s_L[n] = max_i (q_i . A_L[n]) / sqrt(d) for every level-L region n,
- *      and keep the k_L best (Figure 2 (c)).
+ *   1. s_L[n] = max_i (q_i . A_L[n]) / sqrt(d) for every level-L region n
+ *      (mean_i with WF_AGG_MEAN), and keep the k_L best (Figure 2 (c)).
  *   2. For j = L-1 .. 0: the candidates are the two children of each region
- *      kept at level j+1, scored as s_j[c] = max_i (q_i . A_j[c]) / sqrt(d),
- *      and the k_j best are kept (Figure 2 (d)).  A_j is never stored: its
+ *      kept at level j+1, scored as s_j[c] = max_i (q_i . A_j[c]) / sqrt(d)
+ *      (mean_i with WF_AGG_MEAN), and the k_j best are kept (Figure 2 (d)).  A_j is never stored: its
  *      dot products are the 2^{-j/2}-scaled sums of the token dot products
  *      q_i . k_t over the region (linearity of the transform).
  *   3. O_i = softmax over T of (q_i . k_t / sqrt(d)) applied to v_t, with T
@@ -169,6 +176,8 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  *                1 <= k_j <= min(2 k_{j+1}, N_p/2^j); WF_ERR_BUDGET also when
  *                the refinement state would not fit one workgroup's LDS
  *   n_q          1 .. WF_MAX_QUERIES
+ *   aggregation  WF_AGG_MAX or WF_AGG_MEAN (else WF_ERR_OPTION): how the
+ *                query rows combine into the scores s_j at every level
  *   out          device float32 [batch, heads, n_q, head_dim]
  *   sel_out      NULL, or device int32 [batch, heads, k_0]: kept prompt
  *                tokens, ascending
@@ -182,8 +191,9 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  */
 int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const void* v,
                      int32_t n_tot, const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets,
-                     int32_t n_q, float* out, int32_t* sel_out, int32_t* sel_levels,
-                     float* score_levels, void* workspace, uint64_t ws_bytes, void* stream);
+                     int32_t n_q, int32_t aggregation, float* out, int32_t* sel_out,
+                     int32_t* sel_levels, float* score_levels, void* workspace, uint64_t ws_bytes,
+                     void* stream);
 
 /*
  * Bytes of workspace wf_attend_selected needs, or 0 if the arguments are

@@ -8,6 +8,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MAX_LEVELS,
     MAX_QUERIES,
+    WF_AGG_MAX,
+    WF_AGG_MEAN,
     WF_BF16,
     WF_F32,
     WF_PYR_ALL_LEVELS,

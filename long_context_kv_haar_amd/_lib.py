@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwavefilt
 WF_OK = 0
 WF_F32 = 0
 WF_BF16 = 1
+WF_AGG_MAX = 0
+WF_AGG_MEAN = 1
+AGGREGATIONS = {"max": WF_AGG_MAX, "mean": WF_AGG_MEAN}
 WF_PYR_ALL_LEVELS = 1
 MAX_LEVELS = 7
 MAX_QUERIES = 64
@@ -74,7 +77,7 @@ def lib():
         L.wf_select_attend_workspace_bytes.restype = u64
         L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p]
         L.wf_select_attend.restype = ctypes.c_int
-        L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, vp, vp, vp, vp, vp, u64, vp]
+        L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp, u64, vp]
         L.wf_attend_selected_workspace_bytes.restype = u64
         L.wf_attend_selected_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.wf_attend_selected.restype = ctypes.c_int
@@ -177,13 +180,22 @@ class Workspace:
 _WORKSPACES = {}
 
 
-def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels_out=False, workspace=None):
+def _agg_code(agg):
+    if agg not in AGGREGATIONS:
+        raise ValueError("agg must be 'max' or 'mean'")
+    return AGGREGATIONS[agg]
+
+
+def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels_out=False, workspace=None,
+                  agg="max"):
     """One step for every (sequence, head).
 
+    ``agg`` combines the query rows into region scores: "max" or "mean".
     Returns a dict with ``out`` (float32 ``[B, H, n_q, d]``), ``sel``
     (int32 ``[B, H, k_0]``) and, with ``levels_out``, ``sel_levels`` /
     ``score_levels`` (``[B, H, sum k_j]``, level L first).
     """
+    agg_code = _agg_code(agg)
     B, H, n_q, d = q.shape
     n_tot = k.shape[2]
     for t in (q, k, v):
@@ -217,7 +229,7 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
         return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
     st = lib().wf_select_attend(ptr(q), ctypes.byref(pyr.desc), ptr(k), ptr(v), n_tot, ptr(gen_idx), n_gen, barr,
-                                n_q, ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels), ptr(ws),
+                                n_q, agg_code, ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels), ptr(ws),
                                 ws.numel(), _stream_handle(dev))
     if st != WF_OK:
         raise WfError(st, "wf_select_attend")
@@ -302,7 +314,8 @@ class PreparedStep:
     """A select-attend call with every argument marshalled once, for tight
     loops (benchmarks, serving): calling it only crosses into the library."""
 
-    def __init__(self, q, pyr, k, v, gen_idx, budgets, out, sel_out, workspace, sel_levels=None, score_levels=None):
+    def __init__(self, q, pyr, k, v, gen_idx, budgets, out, sel_out, workspace, sel_levels=None, score_levels=None,
+                 agg="max"):
         n_gen = 0 if gen_idx is None else gen_idx.numel()
         self._keep = (q, pyr, k, v, gen_idx, out, sel_out, workspace, sel_levels, score_levels)
         self._barr = _budget_array(budgets)
@@ -314,8 +327,8 @@ class PreparedStep:
             return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
         self._args = (ptr(q), ctypes.byref(pyr.desc), ptr(k), ptr(v), k.shape[2], ptr(gen_idx), n_gen, self._barr,
-                      q.shape[2], ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels), ptr(workspace),
-                      workspace.numel(), _stream_handle(q.device))
+                      q.shape[2], _agg_code(agg), ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels),
+                      ptr(workspace), workspace.numel(), _stream_handle(q.device))
         self._fn = lib().wf_select_attend
 
     def __call__(self):

@@ -188,6 +188,7 @@ const char* wf_status_string(int status) {
     case WF_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case WF_ERR_HIP: return "HIP launch failed";
     case WF_ERR_PYRAMID: return "pyramid descriptor not built by wf_build_pyramid";
+    case WF_ERR_OPTION: return "an option argument has no defined meaning";
     default: return "unknown status";
   }
 }
@@ -255,11 +256,12 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
 }
 
 int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const void* v, int32_t n_tot,
-                     const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets, int32_t n_q, float* out,
-                     int32_t* sel_out, int32_t* sel_levels, float* score_levels, void* workspace,
-                     uint64_t ws_bytes, void* stream) {
+                     const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets, int32_t n_q,
+                     int32_t aggregation, float* out, int32_t* sel_out, int32_t* sel_levels, float* score_levels,
+                     void* workspace, uint64_t ws_bytes, void* stream) {
   if (!q || !pyr || !k || !v || !out || !workspace || !budgets) return WF_ERR_NULL;
   if (n_gen > 0 && !gen_idx) return WF_ERR_NULL;
+  if (aggregation != WF_AGG_MAX && aggregation != WF_AGG_MEAN) return WF_ERR_OPTION;
   wf::SelectPlan P;
   const int st = make_plan(pyr, n_q, n_gen, budgets, &P);
   if (st != WF_OK) return st;
@@ -281,6 +283,7 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
   a.gen_idx = gen_idx;
   a.sel_in = nullptr;
   a.attend_only = 0;
+  a.agg_mean = aggregation == WF_AGG_MEAN;
   a.out = out;
   a.sel_out = sel_out;
   a.sel_levels = sel_levels;
@@ -319,6 +322,7 @@ int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batc
   a.gen_idx = gen_idx;
   a.sel_in = sel;  // NULL when k0 == 0
   a.attend_only = 1;
+  a.agg_mean = 0;
   a.out = out;
   a.sel_out = nullptr;
   a.sel_levels = nullptr;

@@ -55,6 +55,7 @@ struct SelectLaunch {
   const int32_t* gen_idx;
   const int32_t* sel_in;  // attention only: the kept prompt tokens [heads_total][k0] (NULL if k0 == 0)
   int attend_only;        // 1: skip selection, attend over sel_in and gen_idx
+  int agg_mean;           // 1: region scores average the query rows (else their maximum)
   float* out;
   int32_t* sel_out;
   int32_t* sel_levels;

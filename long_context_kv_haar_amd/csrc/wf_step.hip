@@ -54,6 +54,7 @@ struct StepArgs {
   int n_att, n_split, n_split_p, cps_p, cps_g;
   int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, refine_mask_words, att_t_words;
   float inv_sqrt_d;
+  float inv_nq;  // 1 / n_q, for the mean over query rows
 };
 
 // Max across the 16 lanes of a row; every lane of the row ends with it.
@@ -64,6 +65,24 @@ __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
   return x;
 }
+
+// How the query rows of a block combine into a region score: the maximum
+// (rows past n_q are set to -inf) or the mean (rows past n_q hold 0, the sum
+// is scaled by 1/n_q).  comb() folds two rows a lane holds, row() the 16 rows
+// spread over the lanes of a 16-lane row.
+template <bool MEAN> struct QueryAgg;
+template <> struct QueryAgg<false> {
+  __device__ __forceinline__ static float comb(float x, float y) { return fmaxf(x, y); }
+  __device__ __forceinline__ static float row(float x) { return row_max16(x); }
+};
+template <> struct QueryAgg<true> {
+  __device__ __forceinline__ static float comb(float x, float y) { return x + y; }
+  __device__ __forceinline__ static float row(float x) {
+#pragma unroll
+    for (int lvl = 1; lvl <= 4; ++lvl) x = group_sum_step(x, lvl);
+    return x;
+  }
+};
 
 // The query block of one head staged once per workgroup in LDS (rows padded
 // like the attention's K rows, so fragment reads are free of bank conflicts),
@@ -102,8 +121,9 @@ __device__ __forceinline__ void load_query_frags(const T* qs, int n_q, int l16, 
 // multiplied exactly, accumulated in float32.  Max over queries: in registers
 // over qt, then across the 16 lanes of a row.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
+template <typename T, int D, int RT, bool MEAN>
+__device__ __forceinline__ void coarse_scores(const StepArgs& a) {
+  using AG = QueryAgg<MEAN>;
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   const int head = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -164,20 +184,27 @@ __global__ __launch_bounds__(256) void coarse_kernel(StepArgs a) {
   float m[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float x = -INFINITY;
+    float x = acc[0][r];  // query tile 0 always holds a valid row
 #pragma unroll
-    for (int qt = 0; qt < RT; ++qt)
-      if (16 * qt + l16 < a.n_q) x = fmaxf(x, acc[qt][r]);
-    m[r] = row_max16(x);
+    for (int qt = 1; qt < RT; ++qt)
+      if (MEAN || 16 * qt + l16 < a.n_q) x = AG::comb(x, acc[qt][r]);  // absent rows: 0 from zero query rows
+    if (!MEAN && l16 >= a.n_q) x = -INFINITY;
+    m[r] = AG::row(x);
   }
+  const float sc = MEAN ? a.inv_sqrt_d * a.inv_nq : a.inv_sqrt_d;
   uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
   const int n0 = blockIdx.x * 64 + w * 16 + 4 * g;  // first region of this row
   if (l16 == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (n0 + r < a.n_top) keys[n0 + r] = order_key(m[r] * a.inv_sqrt_d);
+      if (n0 + r < a.n_top) keys[n0 + r] = order_key(m[r] * sc);
   }
 }
+
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(256) void coarse_max_kernel(StepArgs a) { coarse_scores<T, D, RT, false>(a); }
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(256) void coarse_mean_kernel(StepArgs a) { coarse_scores<T, D, RT, true>(a); }
 
 // State of the fast refinement level (see refine_level_fast).
 struct RefineShared {
@@ -229,8 +256,9 @@ __device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, 
 // over queries: over qt in registers, then across the 16 lanes of a row.
 // Scores are written per level at the block's position p >> j.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
+template <typename T, int D, int RT, bool MEAN>
+__device__ __forceinline__ void cover_scores(const StepArgs& a) {
+  using AG = QueryAgg<MEAN>;
   constexpr int NT = kCoverThreads;
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
@@ -299,16 +327,18 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int qt = 0; qt < RT; ++qt) s[t][qt] = mma_tile<D>(kf[t], qf[qt], f32x4{0.f, 0.f, 0.f, 0.f});
-  // rows of absent queries never win a max
+  // rows of absent queries never win a max (for the mean they hold 0, from
+  // zero query rows)
+  if (!MEAN)
 #pragma unroll
-  for (int qt = 0; qt < RT; ++qt)
-    if (16 * qt + l16 >= a.n_q)
+    for (int qt = 0; qt < RT; ++qt)
+      if (16 * qt + l16 >= a.n_q)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s[t][qt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int t = 0; t < 4; ++t) s[t][qt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
   float* cov = a.cov + (int64_t)head * a.cov_len;
   const int jmax = L < 7 ? L : 7;  // levels 0 .. jmax-1 are scored here
-  const float isd = a.inv_sqrt_d;
+  const float isd = MEAN ? a.inv_sqrt_d * a.inv_nq : a.inv_sqrt_d;
   const bool writer = (l16 == 0);
   const int64_t tb = wave_base + 4 * g;  // first position of this row in tile 0
   // each level's least and greatest score over the wave, one slot per wave
@@ -338,8 +368,8 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
     for (int r = 0; r < 4; ++r) {
       float x = s[t][0][r];
 #pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][r]);
-      m[r] = row_max16(x) * isd;
+      for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][r]);
+      m[r] = AG::row(x) * isd;
     }
     const int64_t p = tb + 16 * t;
     if (writer && p < a.covered)
@@ -366,8 +396,8 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       for (int h = 0; h < 2; ++h) {
         float x = s[t][0][2 * h];
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][2 * h]);
-        m[h] = row_max16(x) * sc;
+        for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][2 * h]);
+        m[h] = AG::row(x) * sc;
       }
       const int64_t p = tb + 16 * t;
       if (writer && p < a.covered)
@@ -389,8 +419,8 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += s[t][qt][2];
       float x = s[t][0][0];
 #pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
-      x = row_max16(x) * sc;
+      for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
+      x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
       if (writer && p < a.covered) cov[a.cov_off[2] + (p >> 2)] = x;
       track(writer && p < a.covered, x);
@@ -409,8 +439,8 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor16(s[t][qt][0]);
       float x = s[t][0][0];
 #pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
-      x = row_max16(x) * sc;
+      for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
+      x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
       if (writer && (g & 1) == 0 && p < a.covered) cov[a.cov_off[3] + (p >> 3)] = x;
       track(writer && (g & 1) == 0 && p < a.covered, x);
@@ -429,8 +459,8 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
       for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor32(s[t][qt][0]);
       float x = s[t][0][0];
 #pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
-      x = row_max16(x) * sc;
+      for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
+      x = AG::row(x) * sc;
       const int64_t p = wave_base + 16 * t;
       if (writer && g == 0 && p < a.covered) cov[a.cov_off[4] + (p >> 4)] = x;
       track(writer && g == 0 && p < a.covered, x);
@@ -440,18 +470,19 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
   if (jmax <= 5) return;
   // level 5: tile pairs; level 6: the whole wave
   {
-    float x01 = -INFINITY, x23 = -INFINITY, xall = -INFINITY;
+    float x01 = s[0][0][0] + s[1][0][0], x23 = s[2][0][0] + s[3][0][0];
+    float xall = x01 + x23;
 #pragma unroll
-    for (int qt = 0; qt < RT; ++qt) {
+    for (int qt = 1; qt < RT; ++qt) {
       const float a01 = s[0][qt][0] + s[1][qt][0];
       const float a23 = s[2][qt][0] + s[3][qt][0];
-      x01 = fmaxf(x01, a01);
-      x23 = fmaxf(x23, a23);
-      xall = fmaxf(xall, a01 + a23);
+      x01 = AG::comb(x01, a01);
+      x23 = AG::comb(x23, a23);
+      xall = AG::comb(xall, a01 + a23);
     }
-    x01 = row_max16(x01) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
-    x23 = row_max16(x23) * (isd * 0.17677669529663688110f);
-    xall = row_max16(xall) * (isd * 0.125f);                 // 2^{-3}
+    x01 = AG::row(x01) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
+    x23 = AG::row(x23) * (isd * 0.17677669529663688110f);
+    xall = AG::row(xall) * (isd * 0.125f);                 // 2^{-3}
     if (lane == 0) {
       if (wave_base < a.covered) cov[a.cov_off[5] + (wave_base >> 5)] = x01;
       if (wave_base + 32 < a.covered) cov[a.cov_off[5] + (wave_base >> 5) + 1] = x23;
@@ -470,6 +501,11 @@ __global__ __launch_bounds__(kCoverThreads) void cover_kernel(StepArgs a) {
     }
   }
 }
+
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(kCoverThreads) void cover_max_kernel(StepArgs a) { cover_scores<T, D, RT, false>(a); }
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(kCoverThreads) void cover_mean_kernel(StepArgs a) { cover_scores<T, D, RT, true>(a); }
 
 // One refinement level with the candidates in registers (n <= ACT * MAXS):
 // candidate i is child (i & 1) of kept parent cur[i >> 1]; the kept ones go
@@ -1355,6 +1391,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.refine_mask_words = P.refine_mask_words;
   a.att_t_words = P.att_t_words;
   a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
+  a.inv_nq = 1.0f / (float)P.n_q;
 
   const int H = P.heads_total;
   const int rt = (P.n_q + 15) / 16;
@@ -1387,10 +1424,18 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   } while (0)
 
   if (!L.attend_only) {  // selection stages (skipped when the caller hands in a selection)
-    WF_RT_SWITCH(WF_LAUNCH, coarse_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
+    if (L.agg_mean) {
+      WF_RT_SWITCH(WF_LAUNCH, coarse_mean_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
+    } else {
+      WF_RT_SWITCH(WF_LAUNCH, coarse_max_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
-    WF_RT_SWITCH(WF_LAUNCH, cover_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
+    if (L.agg_mean) {
+      WF_RT_SWITCH(WF_LAUNCH, cover_mean_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
+    } else {
+      WF_RT_SWITCH(WF_LAUNCH, cover_max_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // one refinement workgroup per head, then the generated positions' attention splits
     const int lds_r = P.refine_lds > P.attend_lds ? P.refine_lds : P.attend_lds;

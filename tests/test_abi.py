@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert wf.version().startswith("wavefilter-gfx950")
-    for st in range(-9, 1):
+    for st in range(-10, 1):
         assert wf.status_string(st) != "unknown status"
 
 
@@ -91,10 +91,10 @@ def test_workspace_query_and_budget_checks():
 
 
 def select(pyr=None, q=FAKE, k=FAKE, v=FAKE, n_tot=1056, gen=FAKE, n_gen=32, b=(8, 16, 32, 64), n_q=32, out=FAKE,
-           ws=FAKE, ws_bytes=1 << 30, sel=None):
+           ws=FAKE, ws_bytes=1 << 30, sel=None, agg=wf.WF_AGG_MAX):
     p = fake_pyramid() if pyr is None else pyr
     return lib().wf_select_attend(ctypes.c_void_p(q), ctypes.byref(p), ctypes.c_void_p(k), ctypes.c_void_p(v),
-                                  n_tot, ctypes.c_void_p(gen), n_gen, budgets_arr(list(b)), n_q,
+                                  n_tot, ctypes.c_void_p(gen), n_gen, budgets_arr(list(b)), n_q, agg,
                                   ctypes.c_void_p(out), ctypes.c_void_p(sel), None, None, ctypes.c_void_p(ws),
                                   ws_bytes, None)
 
@@ -112,6 +112,8 @@ def test_select_attend_rejects_bad_arguments():
     assert select(q=MISALIGNED) == -7
     assert select(sel=FAKE + 2) == -7
     assert select(ws_bytes=64) == -6
+    assert select(agg=2) == -10
+    assert select(agg=-1) == -10
 
 
 def attend_sel(q=FAKE, k=FAKE, v=FAKE, B=1, H=2, n_tot=1100, d=64, dt=wf.WF_BF16, sel=FAKE, k0=64, gen=FAKE, n_gen=8,

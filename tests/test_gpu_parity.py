@@ -305,3 +305,45 @@ def test_tied_levels_match_the_oracle_exactly(spike):
             np.testing.assert_array_equal(lv[j], ora.sel[j], err_msg=f"level {j} head {h}")
         np.testing.assert_array_equal(res["sel"][0, h].cpu().numpy(), ora.sel[0])
         assert np.abs(res["out"][0, h].cpu().numpy() - out_ora).max() <= TOL["bf16"]
+
+
+MEAN_CASES = [
+    ("1k-f32", CONFIGS[1], None, None),
+    ("4k-bf16", CONFIGS[2], None, None),
+    ("ragged-nq20-b2", custom(2, cid=78, batch=2, heads=2, n_q=20, n_prompt=2048, n_gen=7, levels=4),
+     [5, 9, 17, 30, 50], 4),
+    ("bf16-d64-nq48", custom(2, cid=77, head_dim=64, heads=3, n_q=48, n_prompt=4096, n_gen=40, levels=5),
+     [6, 11, 20, 36, 64, 100], 5),
+]
+
+
+@pytest.mark.parametrize("name,cfg,budgets,levels", MEAN_CASES, ids=[c[0] for c in MEAN_CASES])
+def test_mean_aggregation_matches_oracle(name, cfg, budgets, levels):
+    """The region scores average the query rows (WF_AGG_MEAN); rows past
+    n_q in the last query tile must count as absent, not as zero scores."""
+    say(f"[mean {name}]")
+    inp = make_layer(cfg, 0)
+    budgets = cfg.budgets if budgets is None else budgets
+    levels = cfg.levels if levels is None else levels
+    heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    assert all(plant(inp, heads, budgets, levels, agg="mean").values())
+    to_dev(inp)
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, levels)
+    res = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True, agg="mean")
+    torch.cuda.synchronize()
+    check_structure(res, budgets, levels, cfg.n_prompt)
+    for b, h in heads:
+        assert check_head(inp, res, b, h, budgets, levels, agg="mean") == 0
+
+
+def test_one_query_row_mean_equals_max():
+    say("[mean n_q=1]")
+    cfg = custom(2, cid=76, heads=2, n_q=1, n_prompt=2048, n_gen=8, levels=4)
+    inp = to_dev(make_layer(cfg, 0))
+    budgets = [8, 15, 28, 50, 90]
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, 4)
+    a = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True, agg="max")
+    m = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True, agg="mean")
+    torch.cuda.synchronize()
+    assert torch.equal(a["sel_levels"], m["sel_levels"])
+    assert torch.equal(a["out"], m["out"])
