@@ -25,5 +25,6 @@ from .wavefilter import (  # noqa: F401
     attend,
     select_attend,
     attend_selected,
+    refresh_top,
     SelectResult,
 )

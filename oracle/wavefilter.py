@@ -112,6 +112,22 @@ def haar_reconstruct(a_top, details):
 AGGREGATIONS = ("max", "mean")
 
 
+def refresh_top(a_top, k_prompt_new, blocks, levels):
+    """Incremental refresh of the level-L approximation of a head's pyramid.
+
+    The cached prompt keys change on the cache's own schedule (section 2.1,
+    eq. 4, for the positions a step recomputes); the low-frequency keys of
+    section 3.1 are the DWT of the current cache.  Rows ``blocks`` of the
+    old ``a_top`` (``[n_L, d]``) are recomputed from the new keys by the
+    pyramid itself (eq. 5 iterated); every other row is kept as it was.
+    """
+    out = np.array(a_top, dtype=np.float64, copy=True)
+    approx, _ = haar_pyramid(k_prompt_new, levels)
+    for b in set(int(x) for x in blocks):
+        out[b] = approx[levels][b]
+    return out
+
+
 def level_scores(q, coeff_rows, agg="max"):
     """Score of each region: the query rows' scaled dot products, aggregated.
 

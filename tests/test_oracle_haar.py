@@ -137,3 +137,29 @@ def test_single_step_roundtrip_and_shape_errors():
         analysis_step(np.zeros(5))
     with pytest.raises(ValueError):
         haar_pyramid(np.zeros((12, 2)), 3)
+
+
+def test_refresh_recomputes_only_the_listed_blocks():
+    """Incremental refresh: listed level-L blocks equal the block-sum closed
+    form on the new keys (a direct loop), unlisted blocks keep their old
+    rows even when their keys changed; an empty list and repeated entries
+    change nothing more."""
+    from oracle import refresh_top
+    rng = np.random.default_rng(31)
+    levels, n_p, d = 3, 64, 5
+    k_old = rng.standard_normal((n_p, d))
+    a_old, _ = haar_pyramid(k_old, levels)
+    k_new = k_old.copy()
+    k_new[8:10] += 1.0      # block 1
+    k_new[40] -= 2.0        # block 5
+    k_new[60:64] *= 3.0     # block 7, left out of the list below
+    got = refresh_top(a_old[levels], k_new, [1, 5, 5], levels)
+    for b in range(n_p >> levels):
+        if b in (1, 5):
+            want = [sum(k_new[t, c] for t in range(b * 8, b * 8 + 8)) * 2.0 ** (-levels / 2) for c in range(d)]
+            assert np.allclose(got[b], want, atol=1e-12)
+        else:
+            assert np.array_equal(got[b], a_old[levels][b])
+    assert np.array_equal(refresh_top(a_old[levels], k_new, [], levels), a_old[levels])
+    full = refresh_top(a_old[levels], k_new, range(n_p >> levels), levels)
+    assert np.allclose(full, haar_pyramid(k_new, levels)[0][levels], atol=1e-12)
