@@ -225,6 +225,30 @@ def main():
     torch.cuda.synchronize()
     mean_ms = s0.elapsed_time(s1) / K
 
+    # -- incremental refresh: every copy (standing in for a layer) rebuilds 64 of its
+    #    1024 level-L blocks, all copies in one call
+    n_top = cfg.n_prompt >> L
+    gref = torch.Generator().manual_seed(7)
+    ref_items = [(c.k, pb.pyramid, torch.randperm(n_top, generator=gref)[:64].to(torch.int32).to(dev))
+                 for c, pb in zip(copies, builds)]
+    refresh = wf.PreparedRefresh(ref_items)
+    for _ in range(args.warmup):
+        refresh()
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for _ in range(K):
+        refresh()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    refresh_ms = s0.elapsed_time(s1) / K
+    es = 2 if cfg.dtype == "bf16" else 4
+    refresh_units = R * cfg.batch * cfg.heads * 64
+    refresh_bytes = refresh_units * ((1 << L) * cfg.head_dim * es + cfg.head_dim * 4)
+    # restore every copy's pyramid for what follows
+    for pb in builds:
+        pb()
+    torch.cuda.synchronize()
+
     # -- attention over the selection each copy's last call made (a later step reusing it)
     reuse = [wf.PreparedAttend(c.q, c.k, c.v, sel, c.gen_idx, torch.empty_like(out), ws)
              for c, (out, sel) in zip(copies, outs)]
@@ -286,6 +310,14 @@ def main():
             "calls_per_s": 1e3 / mean_ms,
             "us_per_call": round(mean_ms * 1e3, 2),
             "achieved_GBps": round(sel_bytes / (mean_ms * 1e-3) / 1e9, 1),
+        },
+        "refresh_pyramids": {
+            "layers": R,
+            "blocks_per_layer": 64,
+            "us_per_call": round(refresh_ms * 1e3, 2),
+            "algorithmic_bytes": refresh_bytes,
+            "achieved_GBps": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "attend_selected": {
             "calls_per_s": 1e3 / reuse_ms,

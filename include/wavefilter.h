@@ -143,6 +143,41 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
                      void* stream);
 
 /*
+ * Incremental pyramid refresh, batched over layers (or any pyramids that share
+ * dtype and head_dim).  The cached prompt keys change on the cache's own
+ * schedule (section 2.1, eq. 4 updates cache rows between steps); the
+ * low-frequency keys of section 3.1 must follow.  For every item and every
+ * (sequence, head) of its pyramid, each listed level-L block n is recomputed
+ * from the item's current prompt keys, rows [n 2^L, (n+1) 2^L):
+ * A_L[n] = 2^{-L/2} * sum of those rows (equation 5 iterated L times, as in
+ * wf_build_pyramid, and bit for bit what a full rebuild writes).  Rows not
+ * listed are left as they are.  One kernel launch for the whole batch.
+ *
+ *   items[i].k_prompt    device keys of the layer, laid out as for
+ *                        wf_build_pyramid (its head_stride)
+ *   items[i].pyr         host descriptor from wf_build_pyramid, without
+ *                        WF_PYR_ALL_LEVELS (else WF_ERR_OPTION: the
+ *                        inspection bands are not refreshed)
+ *   items[i].blocks      device int32 [n_blocks]: level-L block indices shared
+ *                        by all heads of the layer; entries outside
+ *                        [0, N_p / 2^L) are skipped; repeats are harmless
+ *   items[i].n_blocks    >= 0 (0: nothing to do for this item)
+ *   n_items              1 .. WF_MAX_REFRESH_ITEMS
+ * Errors: WF_ERR_NULL, WF_ERR_SHAPE, WF_ERR_PYRAMID, WF_ERR_OPTION,
+ * WF_ERR_DTYPE (items differ in dtype or head_dim), WF_ERR_ALIGN, WF_ERR_HIP.
+ */
+#define WF_MAX_REFRESH_ITEMS 32
+typedef struct {
+    const void* k_prompt;
+    int64_t head_stride;
+    const wf_pyramid* pyr;
+    const int32_t* blocks;
+    int32_t n_blocks;
+} wf_refresh_item;
+
+int wf_refresh_pyramids(const wf_refresh_item* items, int32_t n_items, void* stream);
+
+/*
  * Bytes of workspace wf_select_attend needs, or 0 if the arguments are
  * invalid.  `budgets` is the host array k_L, ..., k_0 (levels + 1 entries).
  */

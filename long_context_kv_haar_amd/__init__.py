@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     Pyramid,
     PreparedAttend,
     PreparedBuild,
+    PreparedRefresh,
     PreparedStep,
     WfError,
     Workspace,
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     build_pyramid,
     lib,
     pyramid_bytes,
+    refresh_pyramids,
     select_attend,
     split_levels,
     status_string,

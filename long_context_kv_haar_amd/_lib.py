@@ -27,7 +27,9 @@ U64_MAX = (1 << 64) - 1
 STATUS_NAMES = {
     0: "WF_OK", -1: "WF_ERR_NULL", -2: "WF_ERR_SHAPE", -3: "WF_ERR_DTYPE", -4: "WF_ERR_LEVELS",
     -5: "WF_ERR_BUDGET", -6: "WF_ERR_WORKSPACE", -7: "WF_ERR_ALIGN", -8: "WF_ERR_HIP", -9: "WF_ERR_PYRAMID",
+    -10: "WF_ERR_OPTION",
 }
+MAX_REFRESH_ITEMS = 32
 
 
 class WfPyramid(ctypes.Structure):
@@ -42,6 +44,16 @@ class WfPyramid(ctypes.Structure):
         ("magic", ctypes.c_uint32),
         ("base", ctypes.c_void_p),
         ("bytes", ctypes.c_uint64),
+    ]
+
+
+class WfRefreshItem(ctypes.Structure):
+    _fields_ = [
+        ("k_prompt", ctypes.c_void_p),
+        ("head_stride", ctypes.c_int64),
+        ("pyr", ctypes.POINTER(WfPyramid)),
+        ("blocks", ctypes.c_void_p),
+        ("n_blocks", ctypes.c_int32),
     ]
 
 
@@ -78,6 +90,8 @@ def lib():
         L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p]
         L.wf_select_attend.restype = ctypes.c_int
         L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp, u64, vp]
+        L.wf_refresh_pyramids.restype = ctypes.c_int
+        L.wf_refresh_pyramids.argtypes = [ctypes.POINTER(WfRefreshItem), i32, vp]
         L.wf_attend_selected_workspace_bytes.restype = u64
         L.wf_attend_selected_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.wf_attend_selected.restype = ctypes.c_int
@@ -158,6 +172,53 @@ def build_pyramid(k, n_prompt, levels, flags=0, buf=None):
     if st != WF_OK:
         raise WfError(st, "wf_build_pyramid")
     return Pyramid(buf, desc)
+
+
+def _refresh_array(items):
+    if not 1 <= len(items) <= MAX_REFRESH_ITEMS:
+        raise ValueError(f"1 .. {MAX_REFRESH_ITEMS} items per call")
+    arr = (WfRefreshItem * len(items))()
+    keep = []
+    for slot, (k, pyr, blocks) in zip(arr, items):
+        if k.dim() != 4 or not k.is_cuda or not k.is_contiguous():
+            raise ValueError("k must be a contiguous [B, H, N, d] device tensor")
+        if blocks is not None and (blocks.dtype != torch.int32 or not blocks.is_contiguous() or not blocks.is_cuda):
+            raise ValueError("blocks must be a contiguous int32 device tensor")
+        slot.k_prompt = k.data_ptr()
+        slot.head_stride = k.shape[2] * k.shape[3]
+        slot.pyr = ctypes.pointer(pyr.desc)
+        slot.blocks = 0 if blocks is None else blocks.data_ptr()
+        slot.n_blocks = 0 if blocks is None else blocks.numel()
+        keep.append((k, pyr, blocks))
+    return arr, keep
+
+
+def refresh_pyramids(items):
+    """Recompute the listed level-L blocks of several pyramids in one launch.
+
+    ``items`` is a list of ``(k, pyr, blocks)``: the layer's current
+    ``[B, H, N, d]`` cache (prompt rows first, as built), its ``Pyramid`` and
+    an int32 device tensor of level-L block indices shared by all heads.
+    """
+    arr, _ = _refresh_array(items)
+    st = lib().wf_refresh_pyramids(arr, len(items), _stream_handle(items[0][0].device))
+    if st != WF_OK:
+        raise WfError(st, "wf_refresh_pyramids")
+
+
+class PreparedRefresh:
+    """A refresh call with its item array marshalled once."""
+
+    def __init__(self, items):
+        self._arr, self._keep = _refresh_array(items)
+        self._n = len(items)
+        self._stream = _stream_handle(items[0][0].device)
+        self._fn = lib().wf_refresh_pyramids
+
+    def __call__(self):
+        st = self._fn(self._arr, self._n, self._stream)
+        if st != WF_OK:
+            raise WfError(st, "wf_refresh_pyramids")
 
 
 def workspace_bytes(pyr, n_q, n_gen, budgets):

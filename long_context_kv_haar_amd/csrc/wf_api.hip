@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <math.h>
 #include <string.h>
 
 #include "../../include/wavefilter.h"
@@ -245,6 +246,47 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
   out->magic = kPyramidMagic;
   out->base = pyr_mem;
   out->bytes = pyr_bytes;
+  return WF_OK;
+}
+
+int wf_refresh_pyramids(const wf_refresh_item* items, int32_t n_items, void* stream) {
+  if (!items) return WF_ERR_NULL;
+  if (n_items < 1 || n_items > WF_MAX_REFRESH_ITEMS) return WF_ERR_SHAPE;
+  static_assert(WF_MAX_REFRESH_ITEMS == wf::kMaxRefreshItems, "refresh item capacity");
+  wf::RefreshLaunch r;
+  memset(&r, 0, sizeof(r));
+  int64_t units = 0;
+  for (int i = 0; i < n_items; ++i) {
+    const wf_refresh_item& it = items[i];
+    if (!it.k_prompt || !it.pyr) return WF_ERR_NULL;
+    if (!pyramid_ok(it.pyr)) return WF_ERR_PYRAMID;
+    if (it.pyr->flags & WF_PYR_ALL_LEVELS) return WF_ERR_OPTION;  // the inspection bands are not refreshed
+    if (i > 0 && (it.pyr->dtype != items[0].pyr->dtype || it.pyr->head_dim != items[0].pyr->head_dim))
+      return WF_ERR_DTYPE;
+    if (it.n_blocks < 0) return WF_ERR_SHAPE;
+    if (it.n_blocks > 0 && !it.blocks) return WF_ERR_NULL;
+    if (it.head_stride < (int64_t)it.pyr->n_prompt * it.pyr->head_dim) return WF_ERR_SHAPE;
+    if (!aligned16(it.k_prompt) || (it.head_stride * elem_bytes(it.pyr->dtype)) % 16 != 0 ||
+        (it.blocks && !aligned4(it.blocks)))
+      return WF_ERR_ALIGN;
+    wf::RefreshItem& d = r.items[i];
+    d.k = it.k_prompt;
+    d.head_stride = it.head_stride;
+    d.a_top = reinterpret_cast<float*>(it.pyr->base);  // A_L sits at offset 0 of the pyramid buffer
+    d.blocks = it.blocks;
+    d.unit_begin = units;
+    d.n_blocks = it.n_blocks;
+    d.n_top = it.pyr->n_prompt >> it.pyr->levels;
+    d.levels = it.pyr->levels;
+    const int L = it.pyr->levels;
+    d.scale = (float)ldexp(1.0, -L / 2) * ((L & 1) ? 0.70710678118654752440f : 1.0f);
+    units += (int64_t)it.n_blocks * it.pyr->batch * it.pyr->heads;
+  }
+  r.n_items = n_items;
+  r.head_dim = items[0].pyr->head_dim;
+  r.bf16 = items[0].pyr->dtype == WF_BF16;
+  r.units_total = units;
+  if (wf::launch_refresh(r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;
 }
 

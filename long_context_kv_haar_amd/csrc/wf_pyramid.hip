@@ -112,6 +112,71 @@ __global__ __launch_bounds__(256) void pyramid_level_kernel(const T* __restrict_
   d_out[idx] = (x0 - x1) * inv_sqrt2;
 }
 
+// ===========================================================================
+// Incremental refresh (the cached prompt keys change on the cache's schedule,
+// section 2.1 eq. 4; the low-frequency keys of section 3.1 follow them): one
+// wave per (item, head, listed block) recomputes A_L[block] from the block's
+// 2^L rows.  Lane layout, pass order and the cross-lane reduction tree are
+// those of pyramid_top_kernel, so a refreshed row is bit for bit the row a
+// full rebuild on the same keys writes.
+// ===========================================================================
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pyramid_refresh_kernel(RefreshLaunch r) {
+  constexpr int VE = Vec16<T>::N;
+  constexpr int V = D / VE;     // vectors per row
+  constexpr int RPP = 64 / V;   // rows per wave pass
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= r.units_total) return;
+  int it = 0;  // wave-uniform: the item holding this unit
+  for (int i = 1; i < r.n_items; ++i)
+    if (unit >= r.items[i].unit_begin) it = i;
+  const RefreshItem& I = r.items[it];
+  const int64_t u = unit - I.unit_begin;
+  const int64_t head = u / I.n_blocks;
+  const int block = I.blocks[u - head * I.n_blocks];
+  if (block < 0 || block >= I.n_top) return;  // wave-uniform
+  const int rows = 1 << I.levels;
+  const int col = lane % V, rr = lane / V;
+  const T* src = reinterpret_cast<const T*>(I.k) + head * I.head_stride + ((int64_t)block * rows + rr) * D + col * VE;
+  float acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+  const int passes = (rows + RPP - 1) / RPP;
+  for (int p = 0; p < passes; ++p)
+    if (rr + p * RPP < rows) Vec16<T>::add(src + (int64_t)p * RPP * D, acc);
+  const int G = rows < RPP ? rows : RPP;  // row groups holding this block's rows
+  for (int o = V; o < V * G; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  }
+  if (rr == 0) {
+    const float scale = I.scale;
+    float* dst = I.a_top + (head * I.n_top + block) * D + col * VE;
+#pragma unroll
+    for (int e = 0; e < VE; e += 4)
+      *reinterpret_cast<float4*>(dst + e) =
+          make_float4(acc[e] * scale, acc[e + 1] * scale, acc[e + 2] * scale, acc[e + 3] * scale);
+  }
+}
+
+hipError_t launch_refresh(const RefreshLaunch& r, hipStream_t s) {
+  if (r.units_total <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((r.units_total + 3) / 4);
+  if (r.bf16) {
+    if (r.head_dim == 128)
+      hipLaunchKernelGGL((pyramid_refresh_kernel<bf16_t, 128>), dim3(grid), dim3(256), 0, s, r);
+    else
+      hipLaunchKernelGGL((pyramid_refresh_kernel<bf16_t, 64>), dim3(grid), dim3(256), 0, s, r);
+  } else {
+    if (r.head_dim == 128)
+      hipLaunchKernelGGL((pyramid_refresh_kernel<float, 128>), dim3(grid), dim3(256), 0, s, r);
+    else
+      hipLaunchKernelGGL((pyramid_refresh_kernel<float, 64>), dim3(grid), dim3(256), 0, s, r);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
   const int L = a.levels;
   uint8_t* base = reinterpret_cast<uint8_t*>(a.base);

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -140,4 +140,39 @@ def test_attend_selected_rejects_bad_arguments():
     assert attend_sel(q=MISALIGNED) == -7
     assert attend_sel(sel=FAKE + 2) == -7
     assert attend_sel(ws_bytes=need - 1) == -6
+
+
+def refresh(items, n=None):
+    arr = (wf._lib.WfRefreshItem * max(1, len(items)))()
+    keep = []
+    for slot, (k, pyr, blocks, n_blocks, stride) in zip(arr, items):
+        slot.k_prompt = k
+        slot.head_stride = stride
+        slot.pyr = ctypes.pointer(pyr) if pyr is not None else None
+        slot.blocks = blocks
+        slot.n_blocks = n_blocks
+        keep.append(pyr)
+    return lib().wf_refresh_pyramids(arr, len(items) if n is None else n, None)
+
+
+def test_refresh_rejects_bad_arguments():
+    def one(k=FAKE, pyr=None, blocks=FAKE, n_blocks=8, stride=1024 * 64):
+        return refresh([(k, fake_pyramid() if pyr is None else pyr, blocks, n_blocks, stride)])
+
+    assert lib().wf_refresh_pyramids(None, 1, None) == -1
+    assert refresh([(FAKE, fake_pyramid(), FAKE, 8, 1024 * 64)], n=0) == -2
+    assert refresh([(FAKE, fake_pyramid(), FAKE, 8, 1024 * 64)], n=33) == -2
+    assert one(k=0) == -1
+    assert one(blocks=0) == -1
+    assert one(blocks=0, n_blocks=0) != -1      # nothing to refresh needs no list
+    assert one(n_blocks=-1) == -2
+    assert one(pyr=fake_pyramid(magic=7)) == -9
+    p_all = fake_pyramid()
+    p_all.flags = wf.WF_PYR_ALL_LEVELS
+    assert one(pyr=p_all) == -10
+    assert one(stride=1000) == -2
+    assert one(k=MISALIGNED) == -7
+    assert one(blocks=FAKE + 2) == -7
+    mixed = [(FAKE, fake_pyramid(), FAKE, 8, 1024 * 64), (FAKE, fake_pyramid(dt=wf.WF_F32), FAKE, 8, 1024 * 64)]
+    assert refresh(mixed) == -3
 

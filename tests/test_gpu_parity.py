@@ -347,3 +347,86 @@ def test_one_query_row_mean_equals_max():
     torch.cuda.synchronize()
     assert torch.equal(a["sel_levels"], m["sel_levels"])
     assert torch.equal(a["out"], m["out"])
+
+
+def _modify_blocks(k, n_prompt, L, blocks, gen):
+    """Change the prompt keys of the given level-L blocks (some rows of each)."""
+    rows = 1 << L
+    for b in blocks:
+        r0 = b * rows + int(torch.randint(0, rows, (1,), generator=gen))
+        r1 = min((b + 1) * rows, r0 + max(1, rows // 2))
+        k[:, :, r0:r1] = (k[:, :, r0:r1].float() * 1.5 + 0.25).to(k.dtype)
+
+
+REFRESH_CASES = [
+    ("1k-f32-L3", custom(1, cid=70), 3),
+    ("4k-bf16-L4", custom(2, cid=71, heads=4), 4),
+    ("bf16-d64-L6", custom(2, cid=72, head_dim=64, heads=3, n_prompt=8192, levels=6), 6),
+    ("bf16-L0", custom(2, cid=73, heads=2, n_prompt=512, levels=0), 0),
+    ("bf16-L1", custom(2, cid=74, heads=2, n_prompt=1024, levels=1), 1),
+]
+
+
+@pytest.mark.parametrize("name,cfg,L", REFRESH_CASES, ids=[c[0] for c in REFRESH_CASES])
+def test_refresh_equals_a_rebuild(name, cfg, L):
+    """Listed blocks after a refresh are bit for bit what a full rebuild on the
+    changed keys writes (and match the oracle); unlisted blocks keep their old
+    rows, even those whose keys changed."""
+    say(f"[refresh {name}]")
+    inp = to_dev(make_layer(cfg, 0))
+    n_top = cfg.n_prompt >> L
+    old = wf.build_pyramid(inp.k, cfg.n_prompt, L)
+    torch.cuda.synchronize()
+    a_old = old.top.clone()
+    gen = torch.Generator().manual_seed(cfg.cid)
+    perm = torch.randperm(n_top, generator=gen)
+    listed = sorted(perm[: max(1, n_top // 8)].tolist())
+    stale = sorted(perm[n_top // 8: n_top // 8 + max(1, n_top // 16)].tolist())  # changed but not listed
+    _modify_blocks(inp.k, cfg.n_prompt, L, listed + stale, gen)
+    blocks = torch.tensor(listed + [listed[0]], dtype=torch.int32, device=DEV)  # a repeat is harmless
+    wf.refresh_pyramids([(inp.k, old, blocks)])
+    full = wf.build_pyramid(inp.k, cfg.n_prompt, L)
+    torch.cuda.synchronize()
+    got, ref = old.top, full.top
+    lst = torch.tensor(listed, device=DEV)
+    keep = torch.ones(n_top, dtype=torch.bool, device=DEV)
+    keep[lst] = False
+    assert torch.equal(got[:, :, lst], ref[:, :, lst])
+    assert torch.equal(got[:, :, keep], a_old[:, :, keep])
+    from oracle import refresh_top
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            want = refresh_top(a_old[b, h].cpu().numpy(), to_f64(inp.k[b, h, :cfg.n_prompt]), listed, L)
+            err = np.abs(got[b, h].cpu().numpy() - want)[listed].max()
+            assert err <= 1e-5 * (1 + np.abs(want).max()), (b, h, err)
+
+
+def test_refresh_batched_over_layers():
+    """One call refreshes three pyramids of different shapes; an entry past
+    the last block is skipped."""
+    say("[refresh batch]")
+    cfgs = [custom(2, cid=60, heads=2, n_prompt=2048, levels=4), custom(2, cid=61, heads=3, n_prompt=4096, levels=5),
+            custom(2, cid=62, heads=1, n_prompt=1024, levels=2)]
+    layers, items, olds = [], [], []
+    gen = torch.Generator().manual_seed(5)
+    for cfg in cfgs:
+        inp = to_dev(make_layer(cfg, 0))
+        pyr = wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels)
+        torch.cuda.synchronize()
+        olds.append(pyr.top.clone())
+        n_top = cfg.n_prompt >> cfg.levels
+        listed = sorted(torch.randperm(n_top, generator=gen)[: n_top // 4].tolist())
+        _modify_blocks(inp.k, cfg.n_prompt, cfg.levels, listed, gen)
+        blocks = torch.tensor(listed + [n_top + 3], dtype=torch.int32, device=DEV)
+        layers.append((inp, cfg, listed))
+        items.append((inp.k, pyr, blocks))
+    wf.refresh_pyramids(items)
+    torch.cuda.synchronize()
+    for (inp, cfg, listed), (_, pyr, _), a_old in zip(layers, items, olds):
+        full = wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels)
+        torch.cuda.synchronize()
+        lst = torch.tensor(listed, device=DEV)
+        keep = torch.ones(cfg.n_prompt >> cfg.levels, dtype=torch.bool, device=DEV)
+        keep[lst] = False
+        assert torch.equal(pyr.top[:, :, lst], full.top[:, :, lst])
+        assert torch.equal(pyr.top[:, :, keep], a_old[:, :, keep])
