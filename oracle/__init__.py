@@ -15,6 +15,10 @@ arrays that hold exactly the (already rounded) input values.
 from .wavefilter import (  # noqa: F401
     HAAR_G,
     HAAR_H,
+    DB2_G,
+    DB2_H,
+    analysis_step_periodic,
+    dwt_pyramid,
     analysis_step,
     synthesis_step,
     haar_pyramid,

@@ -21,7 +21,7 @@ import numpy as np
 from .wavefilter import select
 
 
-def plant_margins(q, k_prompt, budgets, levels, min_gap=2e-3, band=3e-3, max_iter=64, agg="max"):
+def plant_margins(q, k_prompt, budgets, levels, min_gap=2e-3, band=3e-3, max_iter=64, agg="max", wavelet="haar"):
     """Scale near-boundary losing regions until every level's gap exceeds ``min_gap``.
 
     Works from the coarsest level whose gap is too small: every candidate
@@ -36,7 +36,7 @@ def plant_margins(q, k_prompt, budgets, levels, min_gap=2e-3, band=3e-3, max_ite
     k = np.array(k_prompt, dtype=np.float64, copy=True)
     ops = []
     for _ in range(max_iter):
-        res = select(q, k, budgets, levels, agg)
+        res = select(q, k, budgets, levels, agg, wavelet)
         low = [j for j in range(levels, -1, -1) if res.gap[j] <= min_gap]
         if not low:
             return k, ops, True
@@ -58,6 +58,6 @@ def plant_margins(q, k_prompt, budgets, levels, min_gap=2e-3, band=3e-3, max_ite
             changed = True
         if not changed:
             break
-    res = select(q, k, budgets, levels, agg)
+    res = select(q, k, budgets, levels, agg, wavelet)
     ok = all(res.gap[j] > min_gap for j in range(levels + 1))
     return k, ops, ok

@@ -42,6 +42,15 @@ import numpy as np
 HAAR_G = np.array([1.0, 1.0]) / math.sqrt(2.0)
 HAAR_H = np.array([1.0, -1.0]) / math.sqrt(2.0)
 
+# Daubechies' orthonormal four-tap filters (two vanishing moments), from their
+# closed form (1 + s, 3 + s, 3 - s, 1 - s) / (4 sqrt2) with s = sqrt3; the
+# high-pass filter is the quadrature mirror h[m] = (-1)^m g[3 - m].  A longer
+# basis psi than Haar, for the variant of section 3.1's generic wavelet.
+_S3 = math.sqrt(3.0)
+DB2_G = np.array([1.0 + _S3, 3.0 + _S3, 3.0 - _S3, 1.0 - _S3]) / (4.0 * math.sqrt(2.0))
+DB2_H = np.array([DB2_G[3], -DB2_G[2], DB2_G[1], -DB2_G[0]])
+WAVELETS = ("haar", "db2")
+
 
 def analysis_step(x, g=HAAR_G, h=HAAR_H):
     """One level of the two-channel analysis filter bank (section 2.2, eq. 5).
@@ -66,6 +75,48 @@ def analysis_step(x, g=HAAR_G, h=HAAR_H):
         a += g[m] * phase
         dd += h[m] * phase
     return a, dd
+
+
+def analysis_step_periodic(x, g, h):
+    """One analysis level (eq. 5) with the signal extended periodically.
+
+    ``A[n] = sum_m g[m] x[(2n + m) mod N]`` and likewise D with h: the same
+    alignment as ``analysis_step`` (output n starts at input 2n), with the
+    filter wrapping around the end of the signal.  For two-tap filters it
+    equals ``analysis_step``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n_in = x.shape[0]
+    if n_in % 2 != 0:
+        raise ValueError("signal length must be even")
+    n_out = n_in // 2
+    a = np.zeros((n_out,) + x.shape[1:], dtype=np.float64)
+    dd = np.zeros_like(a)
+    for n in range(n_out):
+        for m in range(len(g)):
+            a[n] += g[m] * x[(2 * n + m) % n_in]
+            dd[n] += h[m] * x[(2 * n + m) % n_in]
+    return a, dd
+
+
+def dwt_pyramid(x, levels, wavelet="haar"):
+    """L-level pyramid with the named basis: "haar" (``haar_pyramid``) or
+    "db2" (Daubechies' four-tap filters, periodic extension at every level).
+    Same return convention as ``haar_pyramid``."""
+    if wavelet == "haar":
+        return haar_pyramid(x, levels)
+    if wavelet != "db2":
+        raise ValueError("unknown wavelet")
+    x = np.asarray(x, dtype=np.float64)
+    if levels < 0 or x.shape[0] % (1 << levels) != 0:
+        raise ValueError("token count must be a multiple of 2**levels")
+    approx = [x]
+    detail = [None]
+    for _ in range(levels):
+        a, dd = analysis_step_periodic(approx[-1], DB2_G, DB2_H)
+        approx.append(a)
+        detail.append(dd)
+    return approx, detail
 
 
 def synthesis_step(a, dd):
@@ -192,7 +243,7 @@ class SelectResult:
     detail: list = None
 
 
-def select(q, k_prompt, budgets, levels, agg="max"):
+def select(q, k_prompt, budgets, levels, agg="max", wavelet="haar"):
     """Coarse-to-fine token selection for one head.
 
     Steps (WaveFilter section 3.1 and Figure 2 (b)-(d)):
@@ -205,12 +256,16 @@ def select(q, k_prompt, budgets, levels, agg="max"):
        ``budgets[L-j]``.
 
     ``budgets`` lists k_L, k_{L-1}, ..., k_0; ``agg`` is the aggregation of
-    ``level_scores``.  Returns a ``SelectResult``.
+    ``level_scores``; ``wavelet`` the basis of ``dwt_pyramid``.  With a
+    longer basis a coefficient's support reaches past its block of 2^j
+    tokens, but the refinement tree is the same: the children of level-(j+1)
+    coefficient n are level-j coefficients 2n and 2n+1.  Returns a
+    ``SelectResult``.
     """
     q = np.asarray(q, dtype=np.float64)
     if len(budgets) != levels + 1:
         raise ValueError("need one budget per level L..0")
-    approx, detail = haar_pyramid(k_prompt, levels)
+    approx, detail = dwt_pyramid(k_prompt, levels, wavelet)
     res = SelectResult(levels=levels, approx=approx, detail=detail)
     n_top = approx[levels].shape[0]
     cand = np.arange(n_top)
@@ -244,7 +299,7 @@ def attend(q, keys, values):
     return w @ values
 
 
-def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels, agg="max"):
+def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels, agg="max", wavelet="haar"):
     """One per-step call for one head: select prompt tokens, then attend.
 
     ``k_all``/``v_all`` are the cached rows ``[N_tot, d]`` with the prompt at
@@ -255,7 +310,7 @@ def select_attend(q, k_all, v_all, n_prompt, gen_idx, budgets, levels, agg="max"
     """
     k_all = np.asarray(k_all, dtype=np.float64)
     v_all = np.asarray(v_all, dtype=np.float64)
-    res = select(q, k_all[:n_prompt], budgets, levels, agg)
+    res = select(q, k_all[:n_prompt], budgets, levels, agg, wavelet)
     rows = np.concatenate([res.sel[0], np.asarray(gen_idx, dtype=np.int64)])
     out = attend(q, k_all[rows], v_all[rows])
     return out, res

@@ -11,7 +11,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import haar_pyramid, haar_reconstruct, analysis_step, synthesis_step
+from oracle import HAAR_G as HAAR_G_, HAAR_H as HAAR_H_, haar_pyramid, haar_reconstruct, analysis_step, synthesis_step
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "haar_worked_example.txt")
 
@@ -163,3 +163,74 @@ def test_refresh_recomputes_only_the_listed_blocks():
     assert np.array_equal(refresh_top(a_old[levels], k_new, [], levels), a_old[levels])
     full = refresh_top(a_old[levels], k_new, range(n_p >> levels), levels)
     assert np.allclose(full, haar_pyramid(k_new, levels)[0][levels], atol=1e-12)
+
+
+# -- Daubechies' four-tap basis (the longer-wavelet variant) -----------------
+
+def test_db2_filter_identities():
+    """The defining identities of an orthonormal four-tap pair with two
+    vanishing moments: sum g = sqrt2, unit energy, orthogonal to its even
+    shifts, h a quadrature mirror with zero sum and zero first moment."""
+    from oracle import DB2_G as g, DB2_H as h
+    assert abs(g.sum() - math.sqrt(2.0)) < 1e-14
+    assert abs((g * g).sum() - 1.0) < 1e-14
+    assert abs(g[0] * g[2] + g[1] * g[3]) < 1e-14
+    assert abs(h.sum()) < 1e-14 and abs((np.arange(4) * h).sum()) < 1e-14
+    assert abs((g * h).sum()) < 1e-14 and abs(g[0] * h[2] + g[1] * h[3]) < 1e-14
+
+
+def test_db2_periodic_level_is_orthogonal():
+    """The periodic analysis level as a matrix (applied to unit vectors) is
+    orthogonal: Parseval holds and its transpose reconstructs."""
+    from oracle import DB2_G, DB2_H, analysis_step_periodic
+    n = 16
+    w = np.zeros((n, n))
+    for i in range(n):
+        e = np.zeros(n)
+        e[i] = 1.0
+        a, dd = analysis_step_periodic(e, DB2_G, DB2_H)
+        w[:, i] = np.concatenate([a, dd])
+    assert np.allclose(w @ w.T, np.eye(n), atol=1e-13)
+    x = np.random.default_rng(41).standard_normal(n)
+    a, dd = analysis_step_periodic(x, DB2_G, DB2_H)
+    assert abs((a * a).sum() + (dd * dd).sum() - (x * x).sum()) < 1e-12
+
+
+def test_db2_annihilates_lines_away_from_the_wrap():
+    """Two vanishing moments: a linear signal has zero detail wherever the
+    filter does not wrap around the end; a constant gives sqrt2 x c."""
+    from oracle import DB2_G, DB2_H, analysis_step_periodic
+    x = 0.3 + 0.7 * np.arange(32.0)
+    _, dd = analysis_step_periodic(x, DB2_G, DB2_H)
+    assert np.abs(dd[:15]).max() < 1e-12 and abs(dd[15]) > 1.0
+    a, dd = analysis_step_periodic(np.full(8, 2.5), DB2_G, DB2_H)
+    assert np.allclose(a, 2.5 * math.sqrt(2.0)) and np.abs(dd).max() < 1e-12
+
+
+def test_periodic_step_with_haar_is_the_plain_step():
+    from oracle import analysis_step_periodic, dwt_pyramid
+    x = np.random.default_rng(42).standard_normal((16, 3))
+    a1, d1 = analysis_step_periodic(x, HAAR_G_, HAAR_H_)
+    a2, d2 = analysis_step(x)
+    assert np.allclose(a1, a2, atol=1e-15) and np.allclose(d1, d2, atol=1e-15)
+    ap, _ = dwt_pyramid(x, 3, "haar")
+    hp, _ = haar_pyramid(x, 3)
+    assert all(np.array_equal(ap[j], hp[j]) for j in range(4))
+
+
+def test_db2_selection_tree_and_scores():
+    """With the db2 basis the selection still refines children 2n, 2n+1, and
+    each level's candidate scores are the query block's dot products with
+    the level's db2 coefficients (checked against a direct cascade loop)."""
+    from oracle import DB2_G, select
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((3, 4))
+    kp = rng.standard_normal((32, 4))
+    res = select(q, kp, [2, 3, 5, 9], 3, wavelet="db2")
+    for j in range(2, -1, -1):
+        assert set(res.cand[j]) == set(2 * c for c in res.sel[j + 1]) | set(2 * c + 1 for c in res.sel[j + 1])
+    # level-2 coefficients by an explicit two-step loop with wrap-around
+    lv1 = np.array([[sum(DB2_G[m] * kp[(2 * n + m) % 32, c] for m in range(4)) for c in range(4)] for n in range(16)])
+    lv2 = np.array([[sum(DB2_G[m] * lv1[(2 * n + m) % 16, c] for m in range(4)) for c in range(4)] for n in range(8)])
+    s_want = (q @ lv2[res.cand[2]].T / 2.0).max(axis=0)
+    assert np.allclose(res.scores[2], s_want, atol=1e-12)
