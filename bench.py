@@ -249,6 +249,32 @@ def main():
         pb()
     torch.cuda.synchronize()
 
+    # -- the Daubechies four-tap basis: its build stores every band (about 2 GB for this
+    #    layer), so one copy is used; finer levels are scored from the stored bands
+    db2_bytes = wf.pyramid_bytes(cfg.batch, cfg.heads, cfg.n_prompt, cfg.head_dim, L, wf.WF_PYR_DB2)
+    db2_build = wf.PreparedBuild(base.k, cfg.n_prompt, L, torch.empty(db2_bytes, dtype=torch.uint8, device=dev),
+                                 flags=wf.WF_PYR_DB2)
+    db2_build()
+    db2_out = torch.empty_like(outs[0][0])
+    db2_sel = torch.empty_like(outs[0][1])
+    db2_step = wf.PreparedStep(base.q, db2_build.pyramid, base.k, base.v, base.gen_idx, budgets, db2_out, db2_sel, ws)
+    for _ in range(args.warmup):
+        db2_step()
+    torch.cuda.synchronize()
+    s0.record(stream)
+    for _ in range(K):
+        db2_step()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    db2_ms = s0.elapsed_time(s1) / K
+    s0.record(stream)
+    db2_build()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    db2_build_ms = s0.elapsed_time(s1)
+    del db2_build, db2_step
+    torch.cuda.empty_cache()
+
     # -- attention over the selection each copy's last call made (a later step reusing it)
     reuse = [wf.PreparedAttend(c.q, c.k, c.v, sel, c.gen_idx, torch.empty_like(out), ws)
              for c, (out, sel) in zip(copies, outs)]
@@ -318,6 +344,11 @@ def main():
             "algorithmic_bytes": refresh_bytes,
             "achieved_GBps": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "select_attend_db2": {
+            "us_per_call": round(db2_ms * 1e3, 2),
+            "pyramid_build_us": round(db2_build_ms * 1e3, 1),
+            "note": "one copy (the stored bands take about 2 GB), so its inputs may sit in the MALL",
         },
         "attend_selected": {
             "calls_per_s": 1e3 / reuse_ms,

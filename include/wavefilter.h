@@ -68,6 +68,13 @@ enum { WF_F32 = 0, WF_BF16 = 1 };
 
 /* wf_build_pyramid flags. */
 #define WF_PYR_ALL_LEVELS 1u /* also store A_1..A_{L-1} and D_1..D_L (test/inspection) */
+#define WF_PYR_DB2 2u        /* Daubechies' four-tap basis instead of Haar (section 3.1 leaves
+                                the basis psi open): A_j[n] = sum_m g[m] A_{j-1}[(2n + m) mod N_j-1],
+                                g = (1+r3, 3+r3, 3-r3, 1-r3) / (4 r2), D_j likewise with
+                                h[m] = (-1)^m g[3-m] (the signal is extended periodically); every
+                                band is stored as with WF_PYR_ALL_LEVELS, and wf_select_attend
+                                scores the finer levels from the stored A_j (a coefficient is no
+                                longer the scaled sum of its own 2^j tokens) */
 
 /* Supported sizes. */
 #define WF_MAX_LEVELS 7      /* region of 2^L tokens, L <= 7 */
@@ -80,7 +87,7 @@ enum { WF_F32 = 0, WF_BF16 = 1 };
  * caller's device buffer; the library reads it in wf_select_attend.
  * Layout of the buffer (float32, row-major):
  *   A_L  [batch, heads, N_p / 2^L, head_dim]                   at offset 0
- * and with WF_PYR_ALL_LEVELS additionally, in this order,
+ * and with WF_PYR_ALL_LEVELS or WF_PYR_DB2 additionally, in this order,
  *   D_1 .. D_L   then   A_1 .. A_{L-1},   each [batch, heads, N_p / 2^j, head_dim]
  * (use wf_pyramid_offset for the byte offset of each band).
  */
@@ -133,7 +140,7 @@ uint64_t wf_pyramid_offset(const wf_pyramid* pyr, int32_t band, int32_t level);
  *                is the first n_prompt rows of a [B, H, N_tot, d] cache
  *   head_dim     64 or 128
  *   levels       0 <= L <= WF_MAX_LEVELS, n_prompt a multiple of 2^L
- *   flags        0 or WF_PYR_ALL_LEVELS
+ *   flags        0, WF_PYR_ALL_LEVELS, WF_PYR_DB2 or both
  *   pyr_mem      device buffer of pyr_bytes >= wf_pyramid_bytes(...)
  *   out          host descriptor, filled on success
  */
@@ -156,8 +163,8 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
  *   items[i].k_prompt    device keys of the layer, laid out as for
  *                        wf_build_pyramid (its head_stride)
  *   items[i].pyr         host descriptor from wf_build_pyramid, without
- *                        WF_PYR_ALL_LEVELS (else WF_ERR_OPTION: the
- *                        inspection bands are not refreshed)
+ *                        WF_PYR_ALL_LEVELS or WF_PYR_DB2 (else
+ *                        WF_ERR_OPTION: stored finer bands are not refreshed)
  *   items[i].blocks      device int32 [n_blocks]: level-L block indices shared
  *                        by all heads of the layer; entries outside
  *                        [0, N_p / 2^L) are skipped; repeats are harmless

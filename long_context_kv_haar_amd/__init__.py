@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     WF_BF16,
     WF_F32,
     WF_PYR_ALL_LEVELS,
+    WF_PYR_DB2,
     Pyramid,
     PreparedAttend,
     PreparedBuild,

@@ -20,6 +20,7 @@ WF_AGG_MAX = 0
 WF_AGG_MEAN = 1
 AGGREGATIONS = {"max": WF_AGG_MAX, "mean": WF_AGG_MEAN}
 WF_PYR_ALL_LEVELS = 1
+WF_PYR_DB2 = 2
 MAX_LEVELS = 7
 MAX_QUERIES = 64
 U64_MAX = (1 << 64) - 1

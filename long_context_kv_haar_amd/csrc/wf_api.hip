@@ -40,7 +40,7 @@ uint64_t pyramid_layout(int64_t heads_total, int32_t n_prompt, int32_t head_dim,
   }
   off_a[levels] = 0;
   uint64_t off = band_bytes(heads_total, n_prompt, head_dim, levels);
-  if (flags & WF_PYR_ALL_LEVELS) {
+  if (flags & (WF_PYR_ALL_LEVELS | WF_PYR_DB2)) {
     for (int j = 1; j <= levels; ++j) {
       off_d[j] = off;
       off += band_bytes(heads_total, n_prompt, head_dim, j);
@@ -102,6 +102,14 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // cover kernel: kept coarse regions (+ the coarse keys when they fit) in LDS
   P->coarse_keys_in_lds = P->n_top <= wf::kMaxCoarseLds;
   P->cover_lds = 4 * (((P->k_top + 3) & ~3) + (P->coarse_keys_in_lds ? P->n_top : 0));
+  // a longer basis: its finer approximation bands are read from the pyramid
+  P->stored_bands = (pyr->flags & WF_PYR_DB2) != 0;
+  if (P->stored_bands) {
+    uint64_t off_a[WF_MAX_LEVELS + 1], off_d[WF_MAX_LEVELS + 1];
+    pyramid_layout((int64_t)pyr->batch * pyr->heads, pyr->n_prompt, pyr->head_dim, pyr->levels, pyr->flags, off_a,
+                   off_d);
+    for (int j = 1; j < pyr->levels; ++j) P->band_off[j] = off_a[j];
+  }
   // attention splits
   P->chunk = wf::attend_chunk(pyr->dtype);
   wf::plan_attention_splits(P, true);
@@ -197,7 +205,7 @@ const char* wf_status_string(int status) {
 uint64_t wf_pyramid_bytes(int32_t batch, int32_t heads, int32_t n_prompt, int32_t head_dim, int32_t levels,
                           uint32_t flags) {
   if (!valid_pyramid_shape(batch, heads, n_prompt, head_dim, levels)) return 0;
-  if (flags & ~WF_PYR_ALL_LEVELS) return 0;
+  if (flags & ~(WF_PYR_ALL_LEVELS | WF_PYR_DB2)) return 0;
   uint64_t off_a[WF_MAX_LEVELS + 1], off_d[WF_MAX_LEVELS + 1];
   return pyramid_layout((int64_t)batch * heads, n_prompt, head_dim, levels, flags, off_a, off_d);
 }
@@ -218,7 +226,7 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
   if (levels < 0 || levels > WF_MAX_LEVELS) return WF_ERR_LEVELS;
   if (n_prompt >= 1 && n_prompt % (1 << levels) != 0) return WF_ERR_LEVELS;
   if (!valid_pyramid_shape(batch, heads, n_prompt, head_dim, levels)) return WF_ERR_SHAPE;
-  if (flags & ~WF_PYR_ALL_LEVELS) return WF_ERR_SHAPE;
+  if (flags & ~(WF_PYR_ALL_LEVELS | WF_PYR_DB2)) return WF_ERR_OPTION;
   if (head_stride < (int64_t)n_prompt * head_dim) return WF_ERR_SHAPE;
   if (!aligned16(k_prompt) || !aligned16(pyr_mem) || (head_stride * elem_bytes(dtype)) % 16 != 0)
     return WF_ERR_ALIGN;
@@ -233,7 +241,8 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
   a.head_dim = head_dim;
   a.bf16 = dtype == WF_BF16;
   a.levels = levels;
-  a.all_levels = (flags & WF_PYR_ALL_LEVELS) != 0;
+  a.all_levels = (flags & (WF_PYR_ALL_LEVELS | WF_PYR_DB2)) != 0;
+  a.db2 = (flags & WF_PYR_DB2) != 0;
   a.base = reinterpret_cast<float*>(pyr_mem);
   if (wf::launch_pyramid(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
   out->batch = batch;
@@ -260,7 +269,7 @@ int wf_refresh_pyramids(const wf_refresh_item* items, int32_t n_items, void* str
     const wf_refresh_item& it = items[i];
     if (!it.k_prompt || !it.pyr) return WF_ERR_NULL;
     if (!pyramid_ok(it.pyr)) return WF_ERR_PYRAMID;
-    if (it.pyr->flags & WF_PYR_ALL_LEVELS) return WF_ERR_OPTION;  // the inspection bands are not refreshed
+    if (it.pyr->flags & (WF_PYR_ALL_LEVELS | WF_PYR_DB2)) return WF_ERR_OPTION;  // stored finer bands are not refreshed
     if (i > 0 && (it.pyr->dtype != items[0].pyr->dtype || it.pyr->head_dim != items[0].pyr->head_dim))
       return WF_ERR_DTYPE;
     if (it.n_blocks < 0) return WF_ERR_SHAPE;

@@ -40,6 +40,8 @@ struct SelectPlan {
   int refine_mask_words;        // words of one bitmask over the covered positions
   int refine_cov_in_lds;        // coverage scores staged in LDS
   int refine_lds;               // refinement workgroup: its state (kept sets, candidate lists)
+  int stored_bands;             // levels 1 .. L-1 scored from stored A_j (longer bases)
+  uint64_t band_off[kMaxLevels];  // byte offset of A_j inside the pyramid buffer, when stored
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + K/V chunk buffers
   // workspace sections (byte offsets)

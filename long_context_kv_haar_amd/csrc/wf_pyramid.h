@@ -15,6 +15,7 @@ struct PyramidLaunch {
   int n_prompt, head_dim, levels;
   bool bf16;            // element type of k: bfloat16, else float32
   bool all_levels;      // also store A_1..A_{L-1} and D_1..D_L
+  bool db2;             // Daubechies four-tap filters with periodic extension (implies all_levels)
   float* base;          // pyramid buffer
   uint64_t band_off_a[kPyrMaxLevels + 1];  // byte offsets, A_j (j = L at 0)
   uint64_t band_off_d[kPyrMaxLevels + 1];  // byte offsets, D_j

@@ -160,6 +160,37 @@ __global__ __launch_bounds__(256) void pyramid_refresh_kernel(RefreshLaunch r) {
   }
 }
 
+// One analysis level with Daubechies' four-tap filters and periodic
+// extension (the longer-basis variant of section 3.1's wavelet psi):
+// A[n] = sum_m g[m] x[(2n + m) mod n_in], D[n] likewise with h, in the same
+// alignment as the Haar level above (output n starts at input 2n).
+struct Db2Filters {
+  float g[4], h[4];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void pyramid_level_db2_kernel(const T* __restrict__ src, int64_t src_head_stride,
+                                                                int heads_total, int n_in, int d, Db2Filters f,
+                                                                float* __restrict__ a_out, float* __restrict__ d_out) {
+  const int n_out = n_in >> 1;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_head = (int64_t)n_out * d;
+  if (idx >= per_head * heads_total) return;
+  const int64_t head = idx / per_head;
+  const int64_t rem = idx - head * per_head;
+  const int64_t n = rem / d, c = rem - n * d;
+  const T* base = src + head * src_head_stride;
+  float a = 0.f, dd = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float x = load_elem<T>(base + ((2 * n + m) % n_in) * d + c);
+    a += f.g[m] * x;
+    dd += f.h[m] * x;
+  }
+  a_out[idx] = a;
+  d_out[idx] = dd;
+}
+
 hipError_t launch_refresh(const RefreshLaunch& r, hipStream_t s) {
   if (r.units_total <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((r.units_total + 3) / 4);
@@ -180,7 +211,38 @@ hipError_t launch_refresh(const RefreshLaunch& r, hipStream_t s) {
 hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
   const int L = a.levels;
   uint8_t* base = reinterpret_cast<uint8_t*>(a.base);
-  if (a.all_levels) {
+  if (a.db2) {
+    Db2Filters f;
+    const double s3 = sqrt(3.0), den = 4.0 * sqrt(2.0);
+    const double g[4] = {(1.0 + s3) / den, (3.0 + s3) / den, (3.0 - s3) / den, (1.0 - s3) / den};
+    for (int m = 0; m < 4; ++m) {
+      f.g[m] = (float)g[m];
+      f.h[m] = (float)((m & 1) ? -g[3 - m] : g[3 - m]);
+    }
+    for (int j = 1; j <= L; ++j) {
+      const int n_in = a.n_prompt >> (j - 1);
+      const int64_t total = (int64_t)(n_in >> 1) * a.head_dim * a.heads_total;
+      const unsigned grid = (unsigned)((total + 255) / 256);
+      float* a_out = reinterpret_cast<float*>(base + a.band_off_a[j]);
+      float* d_out = reinterpret_cast<float*>(base + a.band_off_d[j]);
+      if (j == 1 && a.bf16)
+        hipLaunchKernelGGL(pyramid_level_db2_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+                           reinterpret_cast<const bf16_t*>(a.k), a.head_stride, a.heads_total, n_in, a.head_dim, f,
+                           a_out, d_out);
+      else if (j == 1)
+        hipLaunchKernelGGL(pyramid_level_db2_kernel<float>, dim3(grid), dim3(256), 0, s,
+                           reinterpret_cast<const float*>(a.k), a.head_stride, a.heads_total, n_in, a.head_dim, f,
+                           a_out, d_out);
+      else
+        hipLaunchKernelGGL(pyramid_level_db2_kernel<float>, dim3(grid), dim3(256), 0, s,
+                           reinterpret_cast<const float*>(base + a.band_off_a[j - 1]), (int64_t)n_in * a.head_dim,
+                           a.heads_total, n_in, a.head_dim, f, a_out, d_out);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (L > 0) return hipSuccess;
+    // L == 0: A_0 is the keys themselves, converted below by the streaming kernel
+  } else if (a.all_levels) {
     // level by level, each level reading the previous one
     for (int j = 1; j <= L; ++j) {
       const int n_out = a.n_prompt >> j;

@@ -55,6 +55,8 @@ struct StepArgs {
   int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, refine_mask_words, att_t_words;
   float inv_sqrt_d;
   float inv_nq;  // 1 / n_q, for the mean over query rows
+  int stored_bands;                    // score levels 1 .. L-1 from stored A_j (longer bases)
+  const float* band_a[kMaxLevels];     // A_j [heads_total][n_prompt >> j][d], when stored
 };
 
 // Max across the 16 lanes of a row; every lane of the row ends with it.
@@ -243,6 +245,110 @@ __device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, 
       });
 }
 
+// One 16-row tile of float32 coefficient rows (A operand; lane row l16,
+// k-slice g) against the staged query tiles (B operands): bfloat16 queries
+// take the rows as exact hi + lo bf16 parts, float32 queries the fp32 MFMA.
+template <typename T, int D, int RT>
+__device__ __forceinline__ void f32_rows_tile(const float* arow, bool valid, int g, const Frag<T, D> (&qf)[RT],
+                                              f32x4 (&acc)[RT]) {
+#pragma unroll
+  for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+    constexpr int STEPS = D / 32;
+    const float4* p = reinterpret_cast<const float4*>(arow);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      u32x4 hi, lo;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4 x = valid ? p[8 * s + 2 * g + h] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hb[e] = f32_to_bf16(xs[e]);
+          lb[e] = f32_to_bf16(xs[e] - bf16_to_f32(hb[e]));
+        }
+        hi[2 * h] = pack_bf16(hb[0], hb[1]);
+        hi[2 * h + 1] = pack_bf16(hb[2], hb[3]);
+        lo[2 * h] = pack_bf16(lb[0], lb[1]);
+        lo[2 * h + 1] = pack_bf16(lb[2], lb[3]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) {
+        acc[qt] = mma_bf16(hi, qf[qt].v[s], acc[qt]);
+        acc[qt] = mma_bf16(lo, qf[qt].v[s], acc[qt]);
+      }
+    }
+  } else {
+    Frag<float, D> b;
+    if (valid) b.load(arow, g); else b.zero();
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(b, qf[qt], acc[qt]);
+  }
+}
+
+// Coverage scores from stored approximation bands, for a longer basis whose
+// level-j coefficient is not the scaled sum of its own 2^j tokens: wave
+// `wave_base / 64` scores positions [wave_base, wave_base + 64) of every
+// level j < L (level 0 from the key rows, the others from A_j) against the
+// query block, writes them, and publishes each level's score range of its
+// positions (a neutral range where it has none).
+template <typename T, int D, int RT, bool MEAN>
+__device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, const int* sel_l, const Frag<T, D> (&qf)[RT],
+                                                 int64_t wave_base, int lane, int g, int l16) {
+  using AG = QueryAgg<MEAN>;
+  const int L = a.levels;
+  const float sc = MEAN ? a.inv_sqrt_d * a.inv_nq : a.inv_sqrt_d;
+  float* cov = a.cov + (int64_t)head * a.cov_len;
+  const int nwav = (int)((a.covered + 63) >> 6);
+  uint32_t* lvl = a.lvl_mm + ((int64_t)head * nwav + (wave_base >> 6)) * 2 * kMaxLevels;
+  const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
+  for (int j = 0; j < L; ++j) {
+    const int64_t nj = a.covered >> j;
+    const int sh = L - j;
+    uint32_t rmn = 0xFFFFFFFFu, rmx = 0u;
+    for (int t = 0; t < 4; ++t) {
+      const int64_t p0 = wave_base + 16 * t;
+      if (p0 >= nj) break;  // wave-uniform
+      int64_t p = p0 + l16;  // the A-operand row of this lane
+      const bool valid = p < nj;
+      p = valid ? p : nj - 1;
+      const int64_t idx = ((int64_t)clampi(sel_l[p >> sh], 0, a.n_top - 1) << sh) + (p & ((1 << sh) - 1));
+      f32x4 acc[RT];
+      if (j == 0) {
+        Frag<T, D> kf;
+        kf.load(kh + idx * D, g);
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(kf, qf[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+      } else {
+        f32_rows_tile<T, D, RT>(a.band_a[j] + ((int64_t)head * (a.n_prompt >> j) + idx) * D, valid, g, qf, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = acc[0][r];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt)
+          if (MEAN || 16 * qt + l16 < a.n_q) x = AG::comb(x, acc[qt][r]);
+        if (!MEAN && l16 >= a.n_q) x = -INFINITY;
+        const float m = AG::row(x) * sc;
+        const int64_t pr = p0 + 4 * g + r;
+        const bool in = (l16 == 0) && pr < nj;
+        if (in) cov[a.cov_off[j] + pr] = m;
+        const uint32_t k = order_key(m);
+        rmn = in ? min(rmn, k) : rmn;
+        rmx = in ? max(rmx, k) : rmx;
+      }
+    }
+    rmn = wave_min_u32(rmn);
+    rmx = wave_max_u32(rmx);
+    if (lane == 0) {
+      lvl[2 * j] = rmn;
+      lvl[2 * j + 1] = rmx;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cover: coarse Top-K, then coverage scores.
 //
@@ -311,6 +417,10 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
   if (wave_base >= a.covered) return;  // no workgroup barrier below
   Frag<T, D> qf[RT];
   load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
+  if (a.stored_bands) {  // uniform: a longer basis, scored from its stored bands
+    cover_from_bands<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
+    return;
+  }
 
   const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
   Frag<T, D> kf[4];
@@ -1392,6 +1502,11 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.att_t_words = P.att_t_words;
   a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
   a.inv_nq = 1.0f / (float)P.n_q;
+  a.stored_bands = P.stored_bands;
+  for (int j = 0; j < kMaxLevels; ++j)
+    a.band_a[j] = P.stored_bands && j > 0 && j < P.levels
+                      ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top) + P.band_off[j])
+                      : nullptr;
 
   const int H = P.heads_total;
   const int rt = (P.n_q + 15) / 16;

@@ -19,7 +19,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def plant(inp, heads, budgets=None, levels=None, agg="max"):
+def plant(inp, heads, budgets=None, levels=None, agg="max", wavelet="haar"):
     """Plant margins on the listed (b, h) heads, editing ``inp.k`` in place
     (scales by powers of two are exact in the stored dtype)."""
     cfg = inp.cfg
@@ -29,14 +29,14 @@ def plant(inp, heads, budgets=None, levels=None, agg="max"):
     for b, h in heads:
         q = to_f64(inp.q[b, h])
         kp = to_f64(inp.k[b, h, :cfg.n_prompt])
-        _, ops, conv = plant_margins(q, kp, budgets, levels, agg=agg)
+        _, ops, conv = plant_margins(q, kp, budgets, levels, agg=agg, wavelet=wavelet)
         for r0, r1, f in ops:
             inp.k[b, h, r0:r1] *= f
         ok[(b, h)] = conv
     return ok
 
 
-def oracle_head(inp, b, h, budgets=None, levels=None, agg="max"):
+def oracle_head(inp, b, h, budgets=None, levels=None, agg="max", wavelet="haar"):
     cfg = inp.cfg
     budgets = cfg.budgets if budgets is None else budgets
     levels = cfg.levels if levels is None else levels
@@ -44,7 +44,7 @@ def oracle_head(inp, b, h, budgets=None, levels=None, agg="max"):
     k = to_f64(inp.k[b, h])
     v = to_f64(inp.v[b, h])
     gen = inp.gen_idx.cpu().numpy().astype(np.int64) if inp.gen_idx is not None else np.zeros(0, np.int64)
-    return oracle_select_attend(q, k, v, cfg.n_prompt, gen, budgets, levels, agg)
+    return oracle_select_attend(q, k, v, cfg.n_prompt, gen, budgets, levels, agg, wavelet)
 
 
 def split_levels_np(flat, budgets):
@@ -56,14 +56,14 @@ def split_levels_np(flat, budgets):
     return out
 
 
-def check_head(inp, gpu, b, h, budgets=None, levels=None, tol=None, agg="max"):
+def check_head(inp, gpu, b, h, budgets=None, levels=None, tol=None, agg="max", wavelet="haar"):
     """Compare one head with the oracle under the margin rule.  Returns the
     number of unpinned levels (0 when every level was compared exactly)."""
     cfg = inp.cfg
     budgets = cfg.budgets if budgets is None else budgets
     levels = cfg.levels if levels is None else levels
     tol = TOL[cfg.dtype] if tol is None else tol
-    out_ora, res = oracle_head(inp, b, h, budgets, levels, agg)
+    out_ora, res = oracle_head(inp, b, h, budgets, levels, agg, wavelet)
     lv = split_levels_np(gpu["sel_levels"][b, h].cpu().numpy(), budgets)
     sc = split_levels_np(gpu["score_levels"][b, h].cpu().numpy(), budgets)
     pinned = True

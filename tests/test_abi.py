@@ -41,7 +41,9 @@ def test_pyramid_bytes():
     assert wf.pyramid_bytes(1, 2, 1004, 64, 3) == 0     # N_p not a multiple of 2^L
     assert wf.pyramid_bytes(1, 2, 1024, 96, 3) == 0     # unsupported head dim
     assert wf.pyramid_bytes(1, 2, 1024, 64, 8) == 0     # too many levels
-    assert wf.pyramid_bytes(1, 2, 1024, 64, 3, 2) == 0  # unknown flag
+    assert wf.pyramid_bytes(1, 2, 1024, 64, 3, 4) == 0  # unknown flag
+    # the Daubechies basis stores every band, like the inspection layout
+    assert wf.pyramid_bytes(1, 2, 1024, 64, 3, wf.WF_PYR_DB2) == want
 
 
 def build(k=FAKE, stride=1024 * 64, B=1, H=2, n=1024, d=64, dt=wf.WF_BF16, L=3, flags=0, mem=FAKE, nbytes=1 << 30,
@@ -59,7 +61,7 @@ def test_build_pyramid_rejects_bad_arguments():
     assert build(L=8) == -4
     assert build(n=1004) == -4
     assert build(d=96) == -2
-    assert build(flags=4) == -2
+    assert build(flags=4) == -10
     assert build(stride=100) == -2
     assert build(k=MISALIGNED) == -7
     assert build(mem=MISALIGNED) == -7

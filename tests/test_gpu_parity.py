@@ -430,3 +430,43 @@ def test_refresh_batched_over_layers():
         keep[lst] = False
         assert torch.equal(pyr.top[:, :, lst], full.top[:, :, lst])
         assert torch.equal(pyr.top[:, :, keep], a_old[:, :, keep])
+
+
+def test_db2_pyramid_matches_oracle():
+    """Every band of the Daubechies four-tap pyramid (periodic extension)."""
+    say("[db2 pyramid]")
+    from oracle import dwt_pyramid
+    for cfg in (custom(1, cid=50), custom(2, cid=51, heads=3, n_prompt=2048, levels=5)):
+        inp = to_dev(make_layer(cfg, 0))
+        pyr = wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels, wf.WF_PYR_DB2)
+        torch.cuda.synchronize()
+        for h in range(cfg.heads):
+            approx, detail = dwt_pyramid(to_f64(inp.k[0, h, :cfg.n_prompt]), cfg.levels, "db2")
+            for j in range(1, cfg.levels + 1):
+                for band, ref in ((0, approx[j]), (1, detail[j])):
+                    got = pyr.band(band, j)[0, h].cpu().numpy()
+                    assert np.abs(got - ref).max() <= 1e-5 * (1 + np.abs(ref).max()), (band, j)
+
+
+DB2_CASES = [
+    ("1k-f32", custom(1, cid=52), "max"),
+    ("4k-bf16-4h", custom(2, cid=53, heads=4), "max"),
+    ("bf16-d64-nq20-mean", custom(2, cid=54, head_dim=64, heads=3, n_q=20, n_prompt=2048, n_gen=12, levels=4), "mean"),
+]
+
+
+@pytest.mark.parametrize("name,cfg,agg", DB2_CASES, ids=[c[0] for c in DB2_CASES])
+def test_db2_select_attend_matches_oracle(name, cfg, agg):
+    """Selection on the Daubechies pyramid: the finer levels are scored from
+    the stored bands, the refinement tree is the dyadic one."""
+    say(f"[db2 select {name}]")
+    inp = make_layer(cfg, 0)
+    heads = [(0, h) for h in range(cfg.heads)]
+    assert all(plant(inp, heads, agg=agg, wavelet="db2").values())
+    to_dev(inp)
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels, wf.WF_PYR_DB2)
+    res = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, cfg.budgets, levels_out=True, agg=agg)
+    torch.cuda.synchronize()
+    check_structure(res, cfg.budgets, cfg.levels, cfg.n_prompt)
+    for b, h in heads:
+        assert check_head(inp, res, b, h, agg=agg, wavelet="db2") == 0
