@@ -1448,11 +1448,78 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Launches.  This file is compiled once per (input type, head dimension,
+// query tiles) with WF_STEP_T, WF_STEP_D and WF_STEP_RT set, each unit
+// instantiating that combination's kernels (so the units build in
+// parallel), and once without them for the dispatcher and the merge kernel.
+// ---------------------------------------------------------------------------
 template <class K>
 static hipError_t allow_lds(K kernel, int bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                              bytes);
+}
+
+template <class K>
+static hipError_t launch_one(K kernel, dim3 grid, dim3 block, int lds, hipStream_t s, const StepArgs& a) {
+  hipError_t e = allow_lds(kernel, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+// Every stage before the merge, for one (T, D, RT).
+template <typename T, int D, int RT>
+hipError_t launch_stages(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  const SelectPlan& P = L.plan;
+  const int H = P.heads_total;
+  const dim3 att_block(64 * RT * kAttendGroups);
+  hipError_t e;
+  if (!L.attend_only) {  // selection stages (skipped when the caller hands in a selection)
+    const dim3 coarse_grid((P.n_top + 63) / 64, H);
+    e = L.agg_mean ? launch_one(coarse_mean_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a)
+                   : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
+    if (e != hipSuccess) return e;
+    const dim3 cover_grid(P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u, H);
+    e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
+                   : launch_one(cover_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+    if (e != hipSuccess) return e;
+    // one refinement workgroup per head, then the generated positions' attention splits
+    const int lds_r = P.refine_lds > P.attend_lds ? P.refine_lds : P.attend_lds;
+    const unsigned refine_blocks = (unsigned)(H + H * (P.n_split - P.n_split_p));
+    if ((e = launch_one(refine_kernel<T, D, RT>, dim3(refine_blocks), att_block, lds_r, s, a)) != hipSuccess)
+      return e;
+  }
+  // the prompt splits (and, for a handed-in selection, the generated ones too)
+  const unsigned att_splits = (unsigned)(L.attend_only ? P.n_split : P.n_split_p);
+  if (att_splits > 0)
+    return launch_one(attend_kernel<T, D, RT>, dim3(att_splits, H), att_block, P.attend_lds, s, a);
+  return hipSuccess;
+}
+
+#if defined(WF_STEP_T)
+template hipError_t launch_stages<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&,
+                                                                    hipStream_t);
+#else
+#define WF_EXTERN_STAGES(T, D)                                                               \
+  extern template hipError_t launch_stages<T, D, 1>(const StepArgs&, const SelectLaunch&, hipStream_t); \
+  extern template hipError_t launch_stages<T, D, 2>(const StepArgs&, const SelectLaunch&, hipStream_t); \
+  extern template hipError_t launch_stages<T, D, 3>(const StepArgs&, const SelectLaunch&, hipStream_t); \
+  extern template hipError_t launch_stages<T, D, 4>(const StepArgs&, const SelectLaunch&, hipStream_t);
+WF_EXTERN_STAGES(bf16_t, 128)
+WF_EXTERN_STAGES(bf16_t, 64)
+WF_EXTERN_STAGES(float, 128)
+WF_EXTERN_STAGES(float, 64)
+#undef WF_EXTERN_STAGES
+
+template <typename T, int D>
+static hipError_t launch_stages_rt(int rt, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  switch (rt) {
+    case 1: return launch_stages<T, D, 1>(a, L, s);
+    case 2: return launch_stages<T, D, 2>(a, L, s);
+    case 3: return launch_stages<T, D, 3>(a, L, s);
+    default: return launch_stages<T, D, 4>(a, L, s);
+  }
 }
 
 hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
@@ -1508,67 +1575,17 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
                       ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top) + P.band_off[j])
                       : nullptr;
 
-  const int H = P.heads_total;
   const int rt = (P.n_q + 15) / 16;
   const bool bf = P.dtype == WF_BF16;
   const bool d128 = P.head_dim == 128;
-  hipError_t e;
-
-#define WF_RT_SWITCH(MACRO, ...)                  \
-  switch (rt) {                                   \
-    case 1: MACRO(1, __VA_ARGS__); break;         \
-    case 2: MACRO(2, __VA_ARGS__); break;         \
-    case 3: MACRO(3, __VA_ARGS__); break;         \
-    default: MACRO(4, __VA_ARGS__); break;        \
-  }
-#define WF_LAUNCH(RTV, KERNEL, GRID, BLOCK, LDS)                                                           \
-  do {                                                                                                     \
-    if (bf && d128) {                                                                                      \
-      if ((e = allow_lds(KERNEL<bf16_t, 128, RTV>, LDS)) != hipSuccess) return e;                          \
-      hipLaunchKernelGGL((KERNEL<bf16_t, 128, RTV>), GRID, BLOCK, LDS, s, a);                              \
-    } else if (bf) {                                                                                       \
-      if ((e = allow_lds(KERNEL<bf16_t, 64, RTV>, LDS)) != hipSuccess) return e;                           \
-      hipLaunchKernelGGL((KERNEL<bf16_t, 64, RTV>), GRID, BLOCK, LDS, s, a);                               \
-    } else if (d128) {                                                                                     \
-      if ((e = allow_lds(KERNEL<float, 128, RTV>, LDS)) != hipSuccess) return e;                           \
-      hipLaunchKernelGGL((KERNEL<float, 128, RTV>), GRID, BLOCK, LDS, s, a);                               \
-    } else {                                                                                               \
-      if ((e = allow_lds(KERNEL<float, 64, RTV>, LDS)) != hipSuccess) return e;                            \
-      hipLaunchKernelGGL((KERNEL<float, 64, RTV>), GRID, BLOCK, LDS, s, a);                                \
-    }                                                                                                      \
-  } while (0)
-
-  if (!L.attend_only) {  // selection stages (skipped when the caller hands in a selection)
-    if (L.agg_mean) {
-      WF_RT_SWITCH(WF_LAUNCH, coarse_mean_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
-    } else {
-      WF_RT_SWITCH(WF_LAUNCH, coarse_max_kernel, dim3((P.n_top + 63) / 64, H), dim3(256), 0);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned cover_blocks = P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u;
-    if (L.agg_mean) {
-      WF_RT_SWITCH(WF_LAUNCH, cover_mean_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
-    } else {
-      WF_RT_SWITCH(WF_LAUNCH, cover_max_kernel, dim3(cover_blocks, H), dim3(kCoverThreads), P.cover_lds);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // one refinement workgroup per head, then the generated positions' attention splits
-    const int lds_r = P.refine_lds > P.attend_lds ? P.refine_lds : P.attend_lds;
-    const unsigned refine_blocks = (unsigned)(H + H * (P.n_split - P.n_split_p));
-    WF_RT_SWITCH(WF_LAUNCH, refine_kernel, dim3(refine_blocks), dim3(64 * rt * kAttendGroups), lds_r);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  // the prompt splits (and, for a handed-in selection, the generated ones too)
-  const unsigned att_splits = (unsigned)(L.attend_only ? P.n_split : P.n_split_p);
-  if (att_splits > 0)
-    WF_RT_SWITCH(WF_LAUNCH, attend_kernel, dim3(att_splits, H), dim3(64 * rt * kAttendGroups), P.attend_lds);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned comb_blocks = (unsigned)(((int64_t)H * P.n_q * (P.head_dim / 4) + 255) / 256);
+  hipError_t e = bf ? (d128 ? launch_stages_rt<bf16_t, 128>(rt, a, L, s) : launch_stages_rt<bf16_t, 64>(rt, a, L, s))
+                    : (d128 ? launch_stages_rt<float, 128>(rt, a, L, s) : launch_stages_rt<float, 64>(rt, a, L, s));
+  if (e != hipSuccess) return e;
+  const unsigned comb_blocks = (unsigned)(((int64_t)P.heads_total * P.n_q * (P.head_dim / 4) + 255) / 256);
   if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, a);
   return hipGetLastError();
-#undef WF_RT_SWITCH
-#undef WF_LAUNCH
 }
+#endif
 
 }  // namespace wf
