@@ -87,6 +87,74 @@ def read_pmc_traffic():
     return float(m_b.group(1))
 
 
+def time_workload(cfg, dev, launches, warmup):
+    """Per-layer timings of one workload: wf_build_pyramid and wf_select_attend
+    each launched back to back over R device copies of one synthetic layer
+    (R sized so the copies exceed the 256 MB last-level cache where they can),
+    between one pair of HIP events on the launch stream."""
+    import math
+
+    import torch
+
+    import long_context_kv_haar_amd as wf
+    from workloads.gen import make_layer
+
+    es = 2 if cfg.dtype == "bf16" else 4
+    BH, d, L, budgets = cfg.batch * cfg.heads, cfg.head_dim, cfg.levels, cfg.budgets
+    per_copy = BH * (2 * cfg.n_tot + cfg.n_q) * d * es
+    R = min(16, max(2, math.ceil((2 << 30) / per_copy)))
+    base = make_layer(cfg, 0, device=dev)
+    copies = [base] + [type(base)(cfg, 0, base.q.clone(), base.k.clone(), base.v.clone(), base.gen_idx.clone(),
+                                  base.spans) for _ in range(R - 1)]
+    pbytes = wf.pyramid_bytes(cfg.batch, cfg.heads, cfg.n_prompt, d, L)
+    builds, steps, ws = [], [], None
+    for c in copies:
+        pb = wf.PreparedBuild(c.k, cfg.n_prompt, L, torch.empty(pbytes, dtype=torch.uint8, device=dev))
+        pyr = pb()
+        if ws is None:
+            ws = torch.zeros(wf.workspace_bytes(pyr, cfg.n_q, cfg.n_gen, budgets), dtype=torch.uint8, device=dev)
+        out = torch.empty((cfg.batch, cfg.heads, cfg.n_q, d), dtype=torch.float32, device=dev)
+        sel = torch.empty((cfg.batch, cfg.heads, budgets[-1]), dtype=torch.int32, device=dev)
+        builds.append(pb)
+        steps.append(wf.PreparedStep(c.q, pyr, c.k, c.v, c.gen_idx, budgets, out, sel, ws))
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fns):
+        for i in range(warmup):
+            fns[i % R]()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(launches):
+            fns[i % R]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches * 1e3  # us
+
+    build_us = timed(builds)
+    sel_us = timed(steps)
+    pyr_b, sel_b = algorithmic_bytes(cfg)
+    rec = {
+        "layers_x_batch_x_heads": f"{cfg.layers}x{cfg.batch}x{cfg.heads}",
+        "dtype": cfg.dtype, "n_prompt": cfg.n_prompt, "n_q": cfg.n_q, "levels": L,
+        "budgets": ",".join(map(str, budgets)),
+        "rotating_copies": R,
+        "inputs_fit_in_last_level_cache": R * per_copy < (512 << 20),
+        "build_us": round(build_us, 2),
+        "build_GBps": round(pyr_b / (build_us * 1e-6) / 1e9, 1),
+        "select_attend_us": round(sel_us, 2),
+        "select_attend_calls_per_s": round(1e6 / sel_us, 1),
+        "select_attend_GBps": round(sel_b / (sel_us * 1e-6) / 1e9, 1),
+        "select_attend_frac_of_hbm_peak": round(sel_b / (sel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    if cfg.layers > 1:  # every layer has the same shape: the step of all layers
+        rec["all_layers_select_attend_ms"] = round(cfg.layers * sel_us * 1e-3, 3)
+        rec["all_layers_build_ms"] = round(cfg.layers * build_us * 1e-3, 3)
+    del builds, steps, copies, base, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 def cpu_baseline(inp, heads, min_seconds):
     """The float64 oracle, unchanged, on `heads` heads of one step (one thread),
     repeated over those heads until at least `min_seconds` of oracle time."""
@@ -125,6 +193,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=16, help="device copies of the layer rotated over")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the CPU-baseline sample (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time of the CPU-baseline sample")
+    ap.add_argument("--workloads", type=int, default=1,
+                    help="also time every workload's build and select-attend per layer (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -373,6 +443,13 @@ def main():
         },
         "kernel_source_sha256_12": kernel_source_hash(),
     }
+    if args.workloads:
+        # the other workloads (the 1K, 4K, 16K and 128K-sweep layers are parity cases; their
+        # timings are reported here, not as bench lines)
+        del steps, builds, steps_mean, reuse, refresh, ref_items, copies, ws, outs
+        torch.cuda.empty_cache()
+        rec["workloads"] = {CONFIGS[c].name: time_workload(CONFIGS[c], dev, 100 if c < 5 else 40, 10)
+                            for c in sorted(CONFIGS)}
     if args.cpu_heads > 0:
         rec["cpu_baseline"] = cpu_baseline(base, list(range(min(args.cpu_heads, cfg.heads))), args.cpu_seconds)
     print(json.dumps(rec), flush=True)
