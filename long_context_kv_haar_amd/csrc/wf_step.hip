@@ -432,6 +432,10 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
     const int64_t tok = ((int64_t)r << L) + (p & ((1 << L) - 1));
     kf[t].load(kh + tok * D, g);
   }
+  // all 16 row loads stay ahead of the math: left to itself the scheduler
+  // interleaves them with the MFMAs, three or four in flight at a time, and
+  // the gather runs as several serial round trips
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 s[4][RT];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -973,7 +977,10 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
   auto& sh = *reinterpret_cast<RefineShared*>(tk_raw);
 
   // each level's score range: the coverage waves' slots (at most 128 per
-  // head here), all loaded before the scores so their wait is short
+  // head here), all loaded before the scores so their wait is short.  The
+  // loads are unconditional, from clamped in-bounds slots, and the values
+  // are selected afterwards: a load under a condition becomes a branch that
+  // waits for it, and the loads would run as serial round trips.
   const int nwav = (covered + 63) >> 6;
   const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
   uint2 rr[kMaxLevels][2];
@@ -982,24 +989,28 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int v = lane + 64 * r;
-      rr[j][r] = (j < L && v < nwav) ? *reinterpret_cast<const uint2*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j)
-                                     : make_uint2(0xFFFFFFFFu, 0u);
+      const uint2 x = *reinterpret_cast<const uint2*>(lm + (int64_t)min(v, nwav - 1) * 2 * kMaxLevels + 2 * j);
+      // slots past nwav take the neutral range (least = ~0, greatest = 0), by
+      // an all-ones mask rather than a select (which the compiler turns into
+      // a branch around the load); levels past L are never used
+      const uint32_t off = (uint32_t)((nwav - 1 - v) >> 31);
+      rr[j][r] = make_uint2(x.x | off, x.y & ~off);
     }
-  // every level's scores into registers, coarsest level first
+  // every level's scores into registers, coarsest level first (unconditional
+  // loads of clamped positions, as above)
   LevelScores<MMAX> sc;
   for_levels_desc<kMaxLevels - 1>([&](auto jc) {
     constexpr int J = decltype(jc)::value;
     constexpr int SJ = LevelSlots<MMAX, J>::N;
     auto& sj = sc.template get<J>();
-    if (J < L) {
-      const int nj = covered >> J;
-      const float* src = cov_g + a.cov_off[J];
+    // levels past L read level 0's slice (never used: the loop below stops at
+    // L); slots past n_j hold the last score (never used: a level's validity
+    // test excludes them)
+    const bool live = J < L;
+    const int nj = live ? covered >> J : covered;
+    const float* src = cov_g + a.cov_off[live ? J : 0];
 #pragma unroll
-      for (int s = 0; s < SJ; ++s) {
-        const int p = s * ACT + t;
-        sj[s] = (act && p < nj) ? src[p] : 0.f;
-      }
-    }
+    for (int s = 0; s < SJ; ++s) sj[s] = src[min(s * ACT + t, nj - 1)];
   });
   // the ranges, reduced by every wave; the budgets, read once
   uint32_t rmn[kMaxLevels], rmx[kMaxLevels];
