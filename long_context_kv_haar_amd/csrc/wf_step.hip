@@ -248,21 +248,33 @@ __device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, 
 // One 16-row tile of float32 coefficient rows (A operand; lane row l16,
 // k-slice g) against the staged query tiles (B operands): bfloat16 queries
 // take the rows as exact hi + lo bf16 parts, float32 queries the fp32 MFMA.
+// f32_row_load fetches a lane's part of its row (D/16 float4 either way);
+// f32_rows_mma multiplies it, so a caller can put several tiles' loads in
+// flight before the first multiply.
+template <typename T, int D>
+__device__ __forceinline__ void f32_row_load(const float* arow, int g, float4 (&x)[D / 16]) {
+  const float4* p = reinterpret_cast<const float4*>(arow);
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    if constexpr (sizeof(T) == 2) x[i] = p[8 * (i >> 1) + 2 * g + (i & 1)];  // step i/2, half i%2: [32 s + 8 g, +8)
+    else x[i] = p[g * (D / 16) + i];                                         // the quarter [g D/4, (g+1) D/4)
+  }
+}
+
 template <typename T, int D, int RT>
-__device__ __forceinline__ void f32_rows_tile(const float* arow, bool valid, int g, const Frag<T, D> (&qf)[RT],
-                                              f32x4 (&acc)[RT]) {
+__device__ __forceinline__ void f32_rows_mma(const float4 (&x)[D / 16], const Frag<T, D> (&qf)[RT],
+                                             f32x4 (&acc)[RT]) {
 #pragma unroll
   for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (sizeof(T) == 2) {
     constexpr int STEPS = D / 32;
-    const float4* p = reinterpret_cast<const float4*>(arow);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       u32x4 hi, lo;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float4 x = valid ? p[8 * s + 2 * g + h] : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
+        const float4 v = x[2 * s + h];
+        const float xs[4] = {v.x, v.y, v.z, v.w};
         uint32_t hb[4], lb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -282,7 +294,13 @@ __device__ __forceinline__ void f32_rows_tile(const float* arow, bool valid, int
     }
   } else {
     Frag<float, D> b;
-    if (valid) b.load(arow, g); else b.zero();
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      b.v[4 * i] = x[i].x;
+      b.v[4 * i + 1] = x[i].y;
+      b.v[4 * i + 2] = x[i].z;
+      b.v[4 * i + 3] = x[i].w;
+    }
 #pragma unroll
     for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(b, qf[qt], acc[qt]);
   }
@@ -293,7 +311,10 @@ __device__ __forceinline__ void f32_rows_tile(const float* arow, bool valid, int
 // `wave_base / 64` scores positions [wave_base, wave_base + 64) of every
 // level j < L (level 0 from the key rows, the others from A_j) against the
 // query block, writes them, and publishes each level's score range of its
-// positions (a neutral range where it has none).
+// positions (a neutral range where it has none).  The level's four 16-row
+// tiles go in pairs, both tiles' rows requested before either is multiplied;
+// rows past the level's end repeat its last row (in bounds) and are never
+// written.
 template <typename T, int D, int RT, bool MEAN>
 __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, const int* sel_l, const Frag<T, D> (&qf)[RT],
                                                  int64_t wave_base, int lane, int g, int l16) {
@@ -308,36 +329,54 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
     const int64_t nj = a.covered >> j;
     const int sh = L - j;
     uint32_t rmn = 0xFFFFFFFFu, rmx = 0u;
-    for (int t = 0; t < 4; ++t) {
-      const int64_t p0 = wave_base + 16 * t;
-      if (p0 >= nj) break;  // wave-uniform
-      int64_t p = p0 + l16;  // the A-operand row of this lane
-      const bool valid = p < nj;
-      p = valid ? p : nj - 1;
-      const int64_t idx = ((int64_t)clampi(sel_l[p >> sh], 0, a.n_top - 1) << sh) + (p & ((1 << sh) - 1));
-      f32x4 acc[RT];
-      if (j == 0) {
-        Frag<T, D> kf;
-        kf.load(kh + idx * D, g);
+    if (wave_base < nj) {  // wave-uniform: this wave has positions at level j
 #pragma unroll
-        for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(kf, qf[qt], f32x4{0.f, 0.f, 0.f, 0.f});
-      } else {
-        f32_rows_tile<T, D, RT>(a.band_a[j] + ((int64_t)head * (a.n_prompt >> j) + idx) * D, valid, g, qf, acc);
-      }
+      for (int tp = 0; tp < 2; ++tp) {  // tile pairs: both tiles' rows in flight together
+        int64_t idx[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = acc[0][r];
+        for (int u = 0; u < 2; ++u) {
+          int64_t p = wave_base + 16 * (2 * tp + u) + l16;  // the A-operand row of this lane
+          p = p < nj ? p : nj - 1;
+          idx[u] = ((int64_t)clampi(sel_l[p >> sh], 0, a.n_top - 1) << sh) + (p & ((1 << sh) - 1));
+        }
+        f32x4 acc[2][RT];
+        if (j == 0) {
+          Frag<T, D> kf[2];
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt)
-          if (MEAN || 16 * qt + l16 < a.n_q) x = AG::comb(x, acc[qt][r]);
-        if (!MEAN && l16 >= a.n_q) x = -INFINITY;
-        const float m = AG::row(x) * sc;
-        const int64_t pr = p0 + 4 * g + r;
-        const bool in = (l16 == 0) && pr < nj;
-        if (in) cov[a.cov_off[j] + pr] = m;
-        const uint32_t k = order_key(m);
-        rmn = in ? min(rmn, k) : rmn;
-        rmx = in ? max(rmx, k) : rmx;
+          for (int u = 0; u < 2; ++u) kf[u].load(kh + idx[u] * D, g);
+          __builtin_amdgcn_sched_barrier(0);  // both row loads ahead of the math
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int qt = 0; qt < RT; ++qt) acc[u][qt] = mma_tile<D>(kf[u], qf[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+        } else {
+          const float* band = a.band_a[j] + (int64_t)head * (a.n_prompt >> j) * D;
+          float4 xr[2][D / 16];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) f32_row_load<T, D>(band + idx[u] * D, g, xr[u]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) f32_rows_mma<T, D, RT>(xr[u], qf, acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t p0 = wave_base + 16 * (2 * tp + u);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = acc[u][0][r];
+#pragma unroll
+            for (int qt = 1; qt < RT; ++qt)
+              if (MEAN || 16 * qt + l16 < a.n_q) x = AG::comb(x, acc[u][qt][r]);
+            if (!MEAN && l16 >= a.n_q) x = -INFINITY;
+            const float m = AG::row(x) * sc;
+            const int64_t pr = p0 + 4 * g + r;
+            const bool in = (l16 == 0) && pr < nj;
+            if (in) cov[a.cov_off[j] + pr] = m;
+            const uint32_t k = order_key(m);
+            rmn = in ? min(rmn, k) : rmn;
+            rmx = in ? max(rmx, k) : rmx;
+          }
+        }
       }
     }
     rmn = wave_min_u32(rmn);
@@ -362,7 +401,7 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
 // over queries: over qt in registers, then across the 16 lanes of a row.
 // Scores are written per level at the block's position p >> j.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int RT, bool MEAN>
+template <typename T, int D, int RT, bool MEAN, bool BANDS>
 __device__ __forceinline__ void cover_scores(const StepArgs& a) {
   using AG = QueryAgg<MEAN>;
   constexpr int NT = kCoverThreads;
@@ -417,10 +456,10 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
   if (wave_base >= a.covered) return;  // no workgroup barrier below
   Frag<T, D> qf[RT];
   load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
-  if (a.stored_bands) {  // uniform: a longer basis, scored from its stored bands
+  if constexpr (BANDS) {  // a longer basis, scored from its stored bands (its own kernel: more registers)
     cover_from_bands<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
     return;
-  }
+  } else {
 
   const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
   Frag<T, D> kf[4];
@@ -614,12 +653,17 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       publish(6);
     }
   }
+  }  // Haar
 }
 
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_max_kernel(StepArgs a) { cover_scores<T, D, RT, false>(a); }
+__global__ __launch_bounds__(kCoverThreads) void cover_max_kernel(StepArgs a) { cover_scores<T, D, RT, false, false>(a); }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_mean_kernel(StepArgs a) { cover_scores<T, D, RT, true>(a); }
+__global__ __launch_bounds__(kCoverThreads) void cover_mean_kernel(StepArgs a) { cover_scores<T, D, RT, true, false>(a); }
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(kCoverThreads) void cover_bands_max_kernel(StepArgs a) { cover_scores<T, D, RT, false, true>(a); }
+template <typename T, int D, int RT>
+__global__ __launch_bounds__(kCoverThreads) void cover_bands_mean_kernel(StepArgs a) { cover_scores<T, D, RT, true, true>(a); }
 
 // One refinement level with the candidates in registers (n <= ACT * MAXS):
 // candidate i is child (i & 1) of kept parent cur[i >> 1]; the kept ones go
@@ -1492,8 +1536,12 @@ hipError_t launch_stages(const StepArgs& a, const SelectLaunch& L, hipStream_t s
                    : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
     if (e != hipSuccess) return e;
     const dim3 cover_grid(P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u, H);
-    e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
-                   : launch_one(cover_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+    if (P.stored_bands)
+      e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
+                     : launch_one(cover_bands_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+    else
+      e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
+                     : launch_one(cover_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
     if (e != hipSuccess) return e;
     // one refinement workgroup per head, then the generated positions' attention splits
     const int lds_r = P.refine_lds > P.attend_lds ? P.refine_lds : P.attend_lds;
