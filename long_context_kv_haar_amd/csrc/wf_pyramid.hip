@@ -170,27 +170,47 @@ struct Db2Filters {
   float g[4], h[4];
 };
 
+// Four consecutive columns of one input row as float32.
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&x)[4]);
+template <> __device__ __forceinline__ void load4<float>(const float* p, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <> __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&x)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  x[0] = bf16_to_f32(v.x & 0xFFFFu); x[1] = bf16_to_f32(v.x >> 16);
+  x[2] = bf16_to_f32(v.y & 0xFFFFu); x[3] = bf16_to_f32(v.y >> 16);
+}
+
+// Thread = four consecutive columns of one output row (one float4 of A and
+// of D); the four input rows are all requested before the arithmetic.
 template <typename T>
 __global__ __launch_bounds__(256) void pyramid_level_db2_kernel(const T* __restrict__ src, int64_t src_head_stride,
                                                                 int heads_total, int n_in, int d, Db2Filters f,
                                                                 float* __restrict__ a_out, float* __restrict__ d_out) {
   const int n_out = n_in >> 1;
+  const int d4 = d >> 2;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_head = (int64_t)n_out * d;
+  const int64_t per_head = (int64_t)n_out * d4;
   if (idx >= per_head * heads_total) return;
   const int64_t head = idx / per_head;
   const int64_t rem = idx - head * per_head;
-  const int64_t n = rem / d, c = rem - n * d;
+  const int64_t n = rem / d4, c = (rem - n * d4) * 4;
   const T* base = src + head * src_head_stride;
-  float a = 0.f, dd = 0.f;
+  float x[4][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float x = load_elem<T>(base + ((2 * n + m) % n_in) * d + c);
-    a += f.g[m] * x;
-    dd += f.h[m] * x;
-  }
-  a_out[idx] = a;
-  d_out[idx] = dd;
+  for (int m = 0; m < 4; ++m) load4<T>(base + ((2 * n + m) % n_in) * d + c, x[m]);
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] += f.g[m] * x[m][e];
+      dd[e] += f.h[m] * x[m][e];
+    }
+  *reinterpret_cast<float4*>(a_out + 4 * idx) = make_float4(a[0], a[1], a[2], a[3]);
+  *reinterpret_cast<float4*>(d_out + 4 * idx) = make_float4(dd[0], dd[1], dd[2], dd[3]);
 }
 
 hipError_t launch_refresh(const RefreshLaunch& r, hipStream_t s) {
@@ -223,7 +243,7 @@ hipError_t launch_pyramid(const PyramidLaunch& a, hipStream_t s) {
     }
     for (int j = 1; j <= L; ++j) {
       const int n_in = a.n_prompt >> (j - 1);
-      const int64_t total = (int64_t)(n_in >> 1) * a.head_dim * a.heads_total;
+      const int64_t total = (int64_t)(n_in >> 1) * (a.head_dim / 4) * a.heads_total;  // one thread per float4
       const unsigned grid = (unsigned)((total + 255) / 256);
       float* a_out = reinterpret_cast<float*>(base + a.band_off_a[j]);
       float* d_out = reinterpret_cast<float*>(base + a.band_off_d[j]);
