@@ -21,22 +21,28 @@ namespace wf {
 // load reads 1 KiB of contiguous memory.  The keys are read once, so the
 // loads are non-temporal (they do not displace reusable cache lines; this
 // streams measurably faster).  Row groups of one block are reduced with
-// cross-lane shuffles.  A workgroup is one wave, with up to 16 loads in
-// flight (faster than 4-wave workgroups or fewer loads in flight, measured
-// at 64K tokens: 6.27 against 6.06 TB/s).
+// cross-lane shuffles.  A workgroup is one wave, with its 16 loads in
+// flight together (measured at 64K tokens: 6.38 TB/s, against 6.28 with one
+// load in flight per wave and 6.06 with 4-wave workgroups).
 // ===========================================================================
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
   static constexpr int N = 4;
-  __device__ __forceinline__ static void add(const float* p, float* acc) {
-    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  typedef f32x4 Raw;
+  __device__ __forceinline__ static Raw load(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  }
+  __device__ __forceinline__ static void add(const Raw& x, float* acc) {
     acc[0] += x[0]; acc[1] += x[1]; acc[2] += x[2]; acc[3] += x[3];
   }
 };
 template <> struct Vec16<bf16_t> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void add(const bf16_t* p, float* acc) {
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  typedef u32x4 Raw;
+  __device__ __forceinline__ static Raw load(const bf16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  __device__ __forceinline__ static void add(const Raw& x, float* acc) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += bf16_to_f32(x[i] & 0xFFFFu);
@@ -44,6 +50,26 @@ template <> struct Vec16<bf16_t> {
     }
   }
 };
+
+// acc += the vectors at src + p * stride for p = 0 .. npass - 1, added in
+// that order.  Each group of 16 passes is requested before any of it is
+// added (passes past the end load the last one again, in bounds, and are
+// not added), so a wave keeps up to 16 loads in flight; left to itself the
+// compiler adds each vector as it arrives, one load at a time.  The build
+// and the refresh both sum through here, so their rows agree bit for bit.
+template <typename T>
+__device__ __forceinline__ void sum_passes(const T* src, int64_t stride, int npass, float* acc) {
+  constexpr int G = 16;
+  for (int g0 = 0; g0 < npass; g0 += G) {
+    typename Vec16<T>::Raw x[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) x[i] = Vec16<T>::load(src + (int64_t)min(g0 + i, npass - 1) * stride);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (g0 + i < npass) Vec16<T>::add(x[i], acc);
+  }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void pyramid_top_kernel(const T* __restrict__ k, int64_t head_stride,
@@ -66,11 +92,10 @@ __global__ __launch_bounds__(64) void pyramid_top_kernel(const T* __restrict__ k
   for (int e = 0; e < VE; ++e) acc[e] = 0.f;
   const int passes = rows_per_item / RPP;
   if (row0 + (int64_t)(passes - 1) * RPP < n_prompt) {
-#pragma unroll 16
-    for (int p = 0; p < passes; ++p) Vec16<T>::add(src + (int64_t)p * RPP * D, acc);
-  } else {
+    sum_passes<T>(src, (int64_t)RPP * D, passes, acc);
+  } else {  // the last rows of a prompt that is not a whole number of items
     for (int p = 0; p < passes; ++p)
-      if (row0 + (int64_t)p * RPP < n_prompt) Vec16<T>::add(src + (int64_t)p * RPP * D, acc);
+      if (row0 + (int64_t)p * RPP < n_prompt) Vec16<T>::add(Vec16<T>::load(src + (int64_t)p * RPP * D), acc);
   }
   const int block_rows = 1 << levels;
   const int G = block_rows < RPP ? block_rows : RPP;  // row groups per block inside one pass
@@ -123,19 +148,21 @@ __global__ __launch_bounds__(256) void pyramid_level_kernel(const T* __restrict_
 // full rebuild on the same keys writes.
 // ===========================================================================
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pyramid_refresh_kernel(RefreshLaunch r) {
+__global__ __launch_bounds__(64) void pyramid_refresh_kernel(RefreshLaunch r) {
   constexpr int VE = Vec16<T>::N;
   constexpr int V = D / VE;     // vectors per row
   constexpr int RPP = 64 / V;   // rows per wave pass
   const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // one wave per workgroup, so the unit and everything derived from it are
+  // scalar: the item descriptor comes through scalar loads
+  const int64_t unit = blockIdx.x;
   if (unit >= r.units_total) return;
-  int it = 0;  // wave-uniform: the item holding this unit
+  int it = 0;  // the item holding this unit
   for (int i = 1; i < r.n_items; ++i)
     if (unit >= r.items[i].unit_begin) it = i;
   const RefreshItem& I = r.items[it];
   const int64_t u = unit - I.unit_begin;
-  const int64_t head = u / I.n_blocks;
+  const int64_t head = (u <= 0x7FFFFFFF) ? (int64_t)((uint32_t)u / (uint32_t)I.n_blocks) : u / I.n_blocks;
   const int block = I.blocks[u - head * I.n_blocks];
   if (block < 0 || block >= I.n_top) return;  // wave-uniform
   const int rows = 1 << I.levels;
@@ -144,9 +171,11 @@ __global__ __launch_bounds__(256) void pyramid_refresh_kernel(RefreshLaunch r) {
   float acc[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-  const int passes = (rows + RPP - 1) / RPP;
-  for (int p = 0; p < passes; ++p)
-    if (rr + p * RPP < rows) Vec16<T>::add(src + (int64_t)p * RPP * D, acc);
+  if (rows >= RPP) {  // whole passes (rows is a power of two), summed as the build sums them
+    sum_passes<T>(src, (int64_t)RPP * D, rows / RPP, acc);
+  } else if (rr < rows) {  // a block smaller than one pass
+    Vec16<T>::add(Vec16<T>::load(src), acc);
+  }
   const int G = rows < RPP ? rows : RPP;  // row groups holding this block's rows
   for (int o = V; o < V * G; o <<= 1) {
 #pragma unroll
@@ -215,17 +244,18 @@ __global__ __launch_bounds__(256) void pyramid_level_db2_kernel(const T* __restr
 
 hipError_t launch_refresh(const RefreshLaunch& r, hipStream_t s) {
   if (r.units_total <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)((r.units_total + 3) / 4);
+  if (r.units_total > 0x7FFFFFFF) return hipErrorInvalidValue;  // one workgroup per unit
+  const unsigned grid = (unsigned)r.units_total;
   if (r.bf16) {
     if (r.head_dim == 128)
-      hipLaunchKernelGGL((pyramid_refresh_kernel<bf16_t, 128>), dim3(grid), dim3(256), 0, s, r);
+      hipLaunchKernelGGL((pyramid_refresh_kernel<bf16_t, 128>), dim3(grid), dim3(64), 0, s, r);
     else
-      hipLaunchKernelGGL((pyramid_refresh_kernel<bf16_t, 64>), dim3(grid), dim3(256), 0, s, r);
+      hipLaunchKernelGGL((pyramid_refresh_kernel<bf16_t, 64>), dim3(grid), dim3(64), 0, s, r);
   } else {
     if (r.head_dim == 128)
-      hipLaunchKernelGGL((pyramid_refresh_kernel<float, 128>), dim3(grid), dim3(256), 0, s, r);
+      hipLaunchKernelGGL((pyramid_refresh_kernel<float, 128>), dim3(grid), dim3(64), 0, s, r);
     else
-      hipLaunchKernelGGL((pyramid_refresh_kernel<float, 64>), dim3(grid), dim3(256), 0, s, r);
+      hipLaunchKernelGGL((pyramid_refresh_kernel<float, 64>), dim3(grid), dim3(64), 0, s, r);
   }
   return hipGetLastError();
 }
