@@ -170,6 +170,8 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
  *                        [0, N_p / 2^L) are skipped; repeats are harmless
  *   items[i].n_blocks    >= 0 (0: nothing to do for this item)
  *   n_items              1 .. WF_MAX_REFRESH_ITEMS
+ * The sum over items of n_blocks * batch * heads is at most 2^31 - 1 (one
+ * workgroup each), else WF_ERR_SHAPE.
  * Errors: WF_ERR_NULL, WF_ERR_SHAPE, WF_ERR_PYRAMID, WF_ERR_OPTION,
  * WF_ERR_DTYPE (items differ in dtype or head_dim), WF_ERR_ALIGN, WF_ERR_HIP.
  */

@@ -295,6 +295,7 @@ int wf_refresh_pyramids(const wf_refresh_item* items, int32_t n_items, void* str
   r.head_dim = items[0].pyr->head_dim;
   r.bf16 = items[0].pyr->dtype == WF_BF16;
   r.units_total = units;
+  if (units > 0x7FFFFFFF) return WF_ERR_SHAPE;  // one workgroup per (item, head, listed block)
   if (wf::launch_refresh(r, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;
 }
