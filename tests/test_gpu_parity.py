@@ -364,6 +364,9 @@ REFRESH_CASES = [
     ("bf16-d64-L6", custom(2, cid=72, head_dim=64, heads=3, n_prompt=8192, levels=6), 6),
     ("bf16-L0", custom(2, cid=73, heads=2, n_prompt=512, levels=0), 0),
     ("bf16-L1", custom(2, cid=74, heads=2, n_prompt=1024, levels=1), 1),
+    # blocks of more than 16 passes of one wave-wide load (summed in groups of 16 loads)
+    ("bf16-L7", custom(2, cid=75, heads=2, n_prompt=16384, levels=7), 7),
+    ("f32-d128-L7", custom(2, cid=76, dtype="f32", heads=2, n_prompt=8192, levels=7), 7),
 ]
 
 
