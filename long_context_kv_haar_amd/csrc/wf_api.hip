@@ -102,6 +102,13 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // cover kernel: kept coarse regions (+ the coarse keys when they fit) in LDS
   P->coarse_keys_in_lds = P->n_top <= wf::kMaxCoarseLds;
   P->cover_lds = 4 * (((P->k_top + 3) & ~3) + (P->coarse_keys_in_lds ? P->n_top : 0));
+  // Above 1 024 cover workgroups (several rounds of them on the chip), one
+  // Top-K workgroup per head beats every cover workgroup repeating it
+  // (measured on 128K-token layers, 2 048 workgroups: 128.7 -> 126.4 us per
+  // call); below, the extra launch costs more than it saves (64K, 512
+  // workgroups: 66.5 -> 69.4 us).
+  P->topk_apart = P->levels > 0 && (P->covered + 255) / 256 * (int64_t)P->heads_total > 1024;
+  P->topk_lds = P->coarse_keys_in_lds ? 4 * P->n_top : 0;
   // a longer basis: its finer approximation bands are read from the pyramid
   P->stored_bands = (pyr->flags & WF_PYR_DB2) != 0;
   if (P->stored_bands) {

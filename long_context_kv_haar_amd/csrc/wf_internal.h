@@ -36,6 +36,8 @@ struct SelectPlan {
   // LDS plans (bytes)
   int cover_lds;                // kept coarse regions (+ coarse keys when staged)
   int coarse_keys_in_lds;
+  int topk_apart;               // the coarse Top-K runs in a launch of its own (large cover launches)
+  int topk_lds;                 // that launch's LDS: the coarse keys, when staged
   int refine_nmax, refine_kmax; // candidate / kept capacity (words, multiples of 4)
   int refine_mask_words;        // words of one bitmask over the covered positions
   int refine_cov_in_lds;        // coverage scores staged in LDS

@@ -56,6 +56,7 @@ struct StepArgs {
   float inv_sqrt_d;
   float inv_nq;  // 1 / n_q, for the mean over query rows
   int stored_bands;                    // score levels 1 .. L-1 from stored A_j (longer bases)
+  int topk_apart;                      // the coarse Top-K ran in a launch of its own (sel_top holds it)
   const float* band_a[kMaxLevels];     // A_j [heads_total][n_prompt >> j][d], when stored
 };
 
@@ -388,6 +389,32 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
   }
 }
 
+// Coarse Top-K (Figure 2 (c)) of one head: the k_L best regions, ascending,
+// from the order keys of s_L, handed to emit(o, i).  All NT threads call it;
+// keys_l is LDS for n_L keys when they are staged.
+template <int NT, class Emit>
+__device__ __forceinline__ void coarse_topk_head(const StepArgs& a, int head, uint32_t* keys_l, unsigned char* tk_raw,
+                                                 Emit emit) {
+  auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
+  const uint32_t* keys_g = a.keys_top + (int64_t)head * a.n_top;
+  static_assert(NT == 256, "coarse Top-K layout");
+  if (a.n_top <= NT * 4) {
+    coarse_topk_regs<NT, NT, 4>(keys_g, a.n_top, a.k_top, tk_raw, emit);
+  } else if (a.n_top <= NT * 8) {
+    coarse_topk_regs<NT, NT, 8>(keys_g, a.n_top, a.k_top, tk_raw, emit);
+  } else if (a.n_top <= NT * 16) {
+    coarse_topk_regs<NT, NT, 16>(keys_g, a.n_top, a.k_top, tk_raw, emit);
+  } else if (a.n_top <= NT * 32) {
+    coarse_topk_regs<NT, NT, 32>(keys_g, a.n_top, a.k_top, tk_raw, emit);
+  } else if (a.coarse_keys_in_lds) {
+    for (int i = threadIdx.x; i < a.n_top; i += NT) keys_l[i] = keys_g[i];
+    __syncthreads();
+    topk_fast<NT>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, sh, emit);
+  } else {
+    topk_fast<NT>([&](int i) { return keys_g[i]; }, a.n_top, a.k_top, sh, emit);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cover: coarse Top-K, then coverage scores.
 //
@@ -408,7 +435,6 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
   extern __shared__ __align__(16) uint32_t lds[];
   __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
-  auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
   // the query block, staged now and read after the Top-K's barriers
   if (a.levels > 0) stage_query<T, D, NT>(reinterpret_cast<const T*>(a.q) + (int64_t)blockIdx.y * a.n_q * D, a.n_q, qs);
   const int head = blockIdx.y;
@@ -430,21 +456,10 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
     }
   };
-  static_assert(NT == 256, "coarse Top-K layout");
-  if (a.n_top <= NT * 4) {
-    coarse_topk_regs<NT, NT, 4>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.n_top <= NT * 8) {
-    coarse_topk_regs<NT, NT, 8>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.n_top <= NT * 16) {
-    coarse_topk_regs<NT, NT, 16>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.n_top <= NT * 32) {
-    coarse_topk_regs<NT, NT, 32>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.coarse_keys_in_lds) {
-    for (int i = threadIdx.x; i < a.n_top; i += NT) keys_l[i] = keys_g[i];
-    __syncthreads();
-    topk_fast<NT>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, sh, emit);
-  } else {
-    topk_fast<NT>([&](int i) { return keys_g[i]; }, a.n_top, a.k_top, sh, emit);
+  if (!a.topk_apart) {  // uniform
+    coarse_topk_head<NT>(a, head, keys_l, tk_raw, emit);
+  } else {  // large launches: the Top-K kernel has written the head's kept regions
+    for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   }
   __syncthreads();
   if (L == 0) return;  // no finer level to score
@@ -1012,7 +1027,6 @@ __device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, ui
   const int L = a.levels;
   const int covered = (int)a.covered;
   const int t = threadIdx.x, lane = t & 63;
-  const bool act = t < ACT;
   int* sel_l = reinterpret_cast<int*>(lds);
   uint32_t* mask_a = reinterpret_cast<uint32_t*>(sel_l + ((a.k_top + 3) & ~3));
   uint32_t* mask_b = mask_a + a.refine_mask_words;
@@ -1523,7 +1537,17 @@ static hipError_t launch_one(K kernel, dim3 grid, dim3 block, int lds, hipStream
   return hipGetLastError();
 }
 
-// Every stage before the merge, for one (T, D, RT).
+// The coarse scores, for one (T, D, RT).
+template <typename T, int D, int RT>
+hipError_t launch_coarse(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  const SelectPlan& P = L.plan;
+  const dim3 coarse_grid((P.n_top + 63) / 64, P.heads_total);
+  return L.agg_mean ? launch_one(coarse_mean_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a)
+                    : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
+}
+
+// Every stage after the coarse scores (and the coarse Top-K, when it runs
+// apart) and before the merge, for one (T, D, RT).
 template <typename T, int D, int RT>
 hipError_t launch_stages(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
   const SelectPlan& P = L.plan;
@@ -1531,10 +1555,6 @@ hipError_t launch_stages(const StepArgs& a, const SelectLaunch& L, hipStream_t s
   const dim3 att_block(64 * RT * kAttendGroups);
   hipError_t e;
   if (!L.attend_only) {  // selection stages (skipped when the caller hands in a selection)
-    const dim3 coarse_grid((P.n_top + 63) / 64, H);
-    e = L.agg_mean ? launch_one(coarse_mean_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a)
-                   : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
-    if (e != hipSuccess) return e;
     const dim3 cover_grid(P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u, H);
     if (P.stored_bands)
       e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
@@ -1557,22 +1577,61 @@ hipError_t launch_stages(const StepArgs& a, const SelectLaunch& L, hipStream_t s
 }
 
 #if defined(WF_STEP_T)
+template hipError_t launch_coarse<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&,
+                                                                    hipStream_t);
 template hipError_t launch_stages<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&,
                                                                     hipStream_t);
 #else
-#define WF_EXTERN_STAGES(T, D)                                                               \
-  extern template hipError_t launch_stages<T, D, 1>(const StepArgs&, const SelectLaunch&, hipStream_t); \
-  extern template hipError_t launch_stages<T, D, 2>(const StepArgs&, const SelectLaunch&, hipStream_t); \
-  extern template hipError_t launch_stages<T, D, 3>(const StepArgs&, const SelectLaunch&, hipStream_t); \
-  extern template hipError_t launch_stages<T, D, 4>(const StepArgs&, const SelectLaunch&, hipStream_t);
+#define WF_EXTERN_RT(F, T, D, RT) \
+  extern template hipError_t F<T, D, RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
+#define WF_EXTERN_STAGES(T, D)                                                              \
+  WF_EXTERN_RT(launch_coarse, T, D, 1) WF_EXTERN_RT(launch_coarse, T, D, 2)                 \
+  WF_EXTERN_RT(launch_coarse, T, D, 3) WF_EXTERN_RT(launch_coarse, T, D, 4)                 \
+  WF_EXTERN_RT(launch_stages, T, D, 1) WF_EXTERN_RT(launch_stages, T, D, 2)                 \
+  WF_EXTERN_RT(launch_stages, T, D, 3) WF_EXTERN_RT(launch_stages, T, D, 4)
 WF_EXTERN_STAGES(bf16_t, 128)
 WF_EXTERN_STAGES(bf16_t, 64)
 WF_EXTERN_STAGES(float, 128)
 WF_EXTERN_STAGES(float, 64)
 #undef WF_EXTERN_STAGES
+#undef WF_EXTERN_RT
+
+// The coarse Top-K as a launch of its own, one workgroup per head: used when
+// the cover launch takes several rounds of workgroups, each of which would
+// otherwise repeat it.
+__global__ __launch_bounds__(kCoverThreads) void coarse_topk_kernel(StepArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<kCoverThreads>::BYTES];
+  const int head = blockIdx.x;
+  const uint32_t* keys_g = a.keys_top + (int64_t)head * a.n_top;
+  int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  coarse_topk_head<kCoverThreads>(a, head, lds, tk_raw, [&](int o, int i) {
+    if (o < a.k_top) {
+      sel_g[o] = i;
+      if (dbg_sel) dbg_sel[o] = i;
+      if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
+    }
+  });
+}
 
 template <typename T, int D>
 static hipError_t launch_stages_rt(int rt, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  if (!L.attend_only) {
+    hipError_t e;
+    switch (rt) {
+      case 1: e = launch_coarse<T, D, 1>(a, L, s); break;
+      case 2: e = launch_coarse<T, D, 2>(a, L, s); break;
+      case 3: e = launch_coarse<T, D, 3>(a, L, s); break;
+      default: e = launch_coarse<T, D, 4>(a, L, s); break;
+    }
+    if (e != hipSuccess) return e;
+    if (L.plan.topk_apart &&
+        (e = launch_one(coarse_topk_kernel, dim3(L.plan.heads_total), dim3(kCoverThreads), L.plan.topk_lds, s, a)) !=
+            hipSuccess)
+      return e;
+  }
   switch (rt) {
     case 1: return launch_stages<T, D, 1>(a, L, s);
     case 2: return launch_stages<T, D, 2>(a, L, s);
@@ -1629,6 +1688,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
   a.inv_nq = 1.0f / (float)P.n_q;
   a.stored_bands = P.stored_bands;
+  a.topk_apart = P.topk_apart;
   for (int j = 0; j < kMaxLevels; ++j)
     a.band_a[j] = P.stored_bands && j > 0 && j < P.levels
                       ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top) + P.band_off[j])
