@@ -145,6 +145,9 @@ EDGE = [
      [300, 500], 1),
     ("coarse-20480-keys-global", custom(2, cid=87, head_dim=64, heads=1, n_prompt=20480, n_gen=8, levels=0,
                                         n_spans=2), [1000], 0),
+    # more than 1 024 cover workgroups (64 heads x 17): the coarse Top-K runs in a launch of its own
+    ("topk-apart-b2", custom(2, cid=89, batch=2, n_prompt=8192, n_gen=16, levels=3, n_spans=2),
+     [520, 1000, 1900, 3000], 3),
     ("refine-6000-candidates", custom(4, cid=88, heads=2, n_prompt=32768, n_gen=32, levels=2, n_spans=4,
                                       key_law="normal"), [2000, 3000, 5600], 2),
 ]
