@@ -69,8 +69,14 @@ struct SelectLaunch {
 
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
 
+// Waves per SIMD the attention kernel is compiled for: with two query tiles
+// its 256-thread workgroup fits 256 registers without spilling, so two
+// workgroups share a compute unit; larger workgroups take one each.
+constexpr int attend_waves_per_simd(int nqt) { return nqt == 2 ? 2 : 1; }
+
 // Split plan of the attention over T (fills n_att .. cps_g from k0, n_gen,
-// chunk and heads_total), about one workgroup per compute unit over all heads.
+// chunk, n_q and heads_total): about as many splits over all heads as
+// attention workgroups fit the chip at once.
 // gen_apart: the generated part's splits run in another launch (beside the
 // refinement), so the prompt part alone fills the chip and the generated part
 // takes up to 4 splits of its own; otherwise both parts share one count of
@@ -79,7 +85,8 @@ inline void plan_attention_splits(SelectPlan* P, bool gen_apart) {
   const int ch = P->chunk;
   P->n_att = P->k0 + P->n_gen;
   const int nc_p = (P->k0 + ch - 1) / ch, nc_g = (P->n_gen + ch - 1) / ch;
-  int target = (256 + P->heads_total - 1) / P->heads_total;
+  const int per_cu = attend_waves_per_simd((P->n_q + 15) / 16);  // attention workgroups per compute unit
+  int target = (256 * per_cu + P->heads_total - 1) / P->heads_total;
   if (target > kMaxSplit) target = kMaxSplit;
   if (gen_apart) {
     const int sg = nc_g < 4 ? nc_g : 4;

@@ -1441,7 +1441,7 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
 }
 
 template <typename T, int D, int NQT>
-__global__ __launch_bounds__(64 * NQT * kAttendGroups) void attend_kernel(StepArgs a) {
+__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
   attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
 }
