@@ -671,10 +671,20 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
   }  // Haar
 }
 
+// With one or two query tiles (and bfloat16 rows, or head dim 64) the Haar
+// cover kernel fits 128 registers without spilling: four workgroups per
+// compute unit, so large launches take fewer rounds; otherwise it keeps the
+// registers its loads in flight need.
+template <typename T, int D>
+constexpr int cover_waves_per_simd(int rt) { return (sizeof(T) == 2 || D == 64) && rt <= 2 ? 4 : 1; }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_max_kernel(StepArgs a) { cover_scores<T, D, RT, false, false>(a); }
+__global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_max_kernel(StepArgs a) {
+  cover_scores<T, D, RT, false, false>(a);
+}
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_mean_kernel(StepArgs a) { cover_scores<T, D, RT, true, false>(a); }
+__global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_mean_kernel(StepArgs a) {
+  cover_scores<T, D, RT, true, false>(a);
+}
 template <typename T, int D, int RT>
 __global__ __launch_bounds__(kCoverThreads) void cover_bands_max_kernel(StepArgs a) { cover_scores<T, D, RT, false, true>(a); }
 template <typename T, int D, int RT>
