@@ -1,12 +1,18 @@
 // WaveFilter per-denoising-step kernels for gfx950 (MI355X).
 //
-//   coarse_kernel   s_L[n] = max_i q_i . A_L[n] / sqrt(d) on MFMA (Figure 2 (c))
-//   cover_kernel    the coarse Top-K (recomputed by every workgroup of the
-//                   head, so no cross-workgroup handoff is needed), then
+//   coarse_max_kernel / coarse_mean_kernel
+//                   s_L[n] = max_i (or mean_i) q_i . A_L[n] / sqrt(d) on MFMA
+//                   (Figure 2 (c))
+//   cover_max_kernel / cover_mean_kernel
+//                   the coarse Top-K (recomputed by every workgroup of the
+//                   head, so no cross-workgroup handoff is needed, or read
+//                   from coarse_topk_kernel for large launches), then
 //                   q_i . k_t for every token the kept regions cover, on MFMA,
 //                   summed in registers into the scores of all their
 //                   sub-regions at levels 0 .. L-1 (Figure 2 (d), with A_j
 //                   taken by linearity from the token dot products)
+//   cover_bands_max_kernel / cover_bands_mean_kernel
+//                   the same on a Daubechies pyramid, from its stored bands
 //   refine_kernel   the recursive refinement, one workgroup per head, with
 //                   the coverage scores in registers and the kept sets as
 //                   bitmasks in LDS; writes the kept prompt tokens.  Its
@@ -1173,8 +1179,9 @@ __device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_
 
 // ---------------------------------------------------------------------------
 // Sparse attention (eq. 3 over T = kept prompt tokens, then gen_idx).
-// Workgroup (split, head) first runs the refinement with all its threads,
-// leaving T in LDS, then walks chunks of CH tokens.  Wave w owns query tile
+// Workgroup (split, head) loads its split's part of T (kept prompt tokens
+// from the refinement or the caller, then generated positions) into LDS,
+// then walks chunks of CH tokens.  Wave w owns query tile
 // qt = w / TG and token group tg = w % TG: the CW = CH / TG tokens
 // [tg CW, tg CW + CW) of every chunk, with an online-softmax state of its
 // own; the TG states of a query tile are merged through LDS at the end, so
