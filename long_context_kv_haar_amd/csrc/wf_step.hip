@@ -109,6 +109,29 @@ __device__ __forceinline__ void stage_query(const T* qh, int n_q, T* qs) {
   }
 }
 
+// The same with every load of a thread issued (clamped in bounds) before the
+// first LDS store: one round trip for the block instead of one per vector
+// (the coarse kernel, where nothing else overlaps the staging).
+template <typename T, int D, int NT, int RT>
+__device__ __forceinline__ void stage_query_batched(const T* qh, int n_q, T* qs) {
+  constexpr int VE = 16 / sizeof(T), NV = D / VE, QS = D + QueryLds<T>::PAD;
+  constexpr int IT = (16 * RT * NV + NT - 1) / NT;  // n_q <= 16 RT
+  const int total = n_q * NV;
+  u32x4 v[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = min((int)threadIdx.x + i * NT, total - 1);
+    const int row = e / NV, cv = e - row * NV;
+    v[i] = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * D + cv * VE);
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = (int)threadIdx.x + i * NT;
+    const int row = e / NV, cv = e - row * NV;
+    if (e < total) *reinterpret_cast<u32x4*>(qs + row * QS + cv * VE) = v[i];
+  }
+}
+
 // Query fragments as the B operand from the staged rows: lane (l16, g)
 // supplies query row 16 qt + l16; zero beyond n_q.
 template <typename T, int D, int RT>
@@ -153,7 +176,7 @@ __device__ __forceinline__ void coarse_scores(const StepArgs& a) {
     for (int i = 0; i < 2 * STEPS; ++i)
       x[i] = valid ? p[8 * (i >> 1) + 2 * g + (i & 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
     // Q staged while the coefficient rows are in flight
-    stage_query<T, D, 256>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
@@ -183,7 +206,7 @@ __device__ __forceinline__ void coarse_scores(const StepArgs& a) {
   } else {
     Frag<float, D> b;
     if (valid) b.load(arow, g); else b.zero();
-    stage_query<T, D, 256>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
