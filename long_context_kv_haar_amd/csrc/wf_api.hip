@@ -235,6 +235,12 @@ int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, i
   if (!valid_pyramid_shape(batch, heads, n_prompt, head_dim, levels)) return WF_ERR_SHAPE;
   if (flags & ~(WF_PYR_ALL_LEVELS | WF_PYR_DB2)) return WF_ERR_OPTION;
   if (head_stride < (int64_t)n_prompt * head_dim) return WF_ERR_SHAPE;
+  {
+    // one workgroup per run of max(2^L, rows one wave-wide load covers) rows of a head
+    const int64_t rpp = 64 / (head_dim / (dtype == WF_BF16 ? 8 : 4));
+    const int64_t run = (1 << levels) > rpp ? (1 << levels) : rpp;
+    if ((int64_t)batch * heads * ((n_prompt + run - 1) / run) > 0x7FFFFFFF) return WF_ERR_SHAPE;
+  }
   if (!aligned16(k_prompt) || !aligned16(pyr_mem) || (head_stride * elem_bytes(dtype)) % 16 != 0)
     return WF_ERR_ALIGN;
   wf::PyramidLaunch a;
