@@ -143,7 +143,7 @@ uint64_t wf_pyramid_offset(const wf_pyramid* pyr, int32_t band, int32_t level);
  *   flags        0, WF_PYR_ALL_LEVELS, WF_PYR_DB2 or both
  *   pyr_mem      device buffer of pyr_bytes >= wf_pyramid_bytes(...)
  *   out          host descriptor, filled on success
- * The streaming pass runs one workgroup per run of max(2^L, 4 or 8) rows of
+ * The streaming pass runs one workgroup per run of max(2^L, 2 to 8) rows of
  * a head; more than 2^31 - 1 such runs over all heads is WF_ERR_SHAPE.
  */
 int wf_build_pyramid(const void* k_prompt, int64_t head_stride, int32_t batch, int32_t heads,
