@@ -183,8 +183,13 @@ def _refresh_array(items):
     for slot, (k, pyr, blocks) in zip(arr, items):
         if k.dim() != 4 or not k.is_cuda or not k.is_contiguous():
             raise ValueError("k must be a contiguous [B, H, N, d] device tensor")
-        if blocks is not None and (blocks.dtype != torch.int32 or not blocks.is_contiguous() or not blocks.is_cuda):
-            raise ValueError("blocks must be a contiguous int32 device tensor")
+        d = pyr.desc
+        _need(tuple(k.shape[:2]) == (d.batch, d.heads) and k.shape[3] == d.head_dim and k.shape[2] >= d.n_prompt,
+              "k must be [B, H, N >= N_p, d] of the pyramid's shape")
+        _need(_dtype_code(k) == d.dtype, "k must have the dtype the pyramid was built from")
+        if blocks is not None:
+            _check_tensor(blocks, "blocks", k.device, dtype=torch.int32)
+            _need(blocks.dim() == 1, "blocks must be 1-d")
         slot.k_prompt = k.data_ptr()
         slot.head_stride = k.shape[2] * k.shape[3]
         slot.pyr = ctypes.pointer(pyr.desc)
@@ -222,6 +227,79 @@ class PreparedRefresh:
             raise WfError(st, "wf_refresh_pyramids")
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name, device, dtype=None, shape=None):
+    """``t`` lives on ``device``, is contiguous, and has the given dtype and shape."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.device == device, f"{name} must be on {device} (got {t.device})")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None:
+        _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _check_qkv(q, k, v, batch, heads, head_dim):
+    """q ``[B, H, n_q, d]`` and k, v ``[B, H, N_tot, d]`` of one dtype on q's device."""
+    dev = q.device
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-d [B, H, rows, d] tensors")
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share one dtype")
+    _dtype_code(q)
+    _check_tensor(q, "q", dev, shape=(batch, heads, q.shape[2], head_dim))
+    _check_tensor(k, "k", dev, shape=(batch, heads, k.shape[2], head_dim))
+    _check_tensor(v, "v", dev, shape=tuple(k.shape))
+    _need(1 <= q.shape[2] <= MAX_QUERIES, f"n_q must be 1 .. {MAX_QUERIES}")
+
+
+def _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out, sel_levels=None, score_levels=None):
+    """Host-side checks of a select-attend call: the tensors must match the
+    pyramid descriptor and each other, so no kernel reads or writes past a
+    buffer.  Raises ValueError (or WfError for a dtype mismatch with the
+    pyramid); launches nothing."""
+    d = pyr.desc
+    _check_qkv(q, k, v, d.batch, d.heads, d.head_dim)
+    _need(_dtype_code(q) == d.dtype, "q, k, v must have the dtype the pyramid was built from")
+    _need(k.shape[2] >= d.n_prompt, f"k, v must hold at least the {d.n_prompt} prompt rows")
+    _need(len(budgets) == d.levels + 1, f"need {d.levels + 1} budgets (k_L .. k_0)")
+    dev = q.device
+    if gen_idx is not None:
+        _check_tensor(gen_idx, "gen_idx", dev, dtype=torch.int32)
+        _need(gen_idx.dim() == 1, "gen_idx must be 1-d")
+    B, H, n_q, hd = q.shape
+    _check_tensor(out, "out", dev, dtype=torch.float32, shape=(B, H, n_q, hd))
+    if sel_out is not None:
+        _check_tensor(sel_out, "sel_out", dev, dtype=torch.int32, shape=(B, H, int(budgets[-1])))
+    total = sum(int(b) for b in budgets)
+    if sel_levels is not None:
+        _check_tensor(sel_levels, "sel_levels", dev, dtype=torch.int32, shape=(B, H, total))
+    if score_levels is not None:
+        _check_tensor(score_levels, "score_levels", dev, dtype=torch.float32, shape=(B, H, total))
+
+
+def _check_attend_args(q, k, v, sel, gen_idx, out):
+    """Host-side checks of an attend-selected call (see _check_select_args)."""
+    _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
+    B, H, n_q, hd = q.shape
+    _check_qkv(q, k, v, B, H, hd)
+    dev = q.device
+    if sel is not None:
+        _check_tensor(sel, "sel", dev, dtype=torch.int32)
+        _need(sel.dim() == 3 and tuple(sel.shape[:2]) == (B, H), "sel must be int32 [B, H, k0]")
+    if gen_idx is not None:
+        _check_tensor(gen_idx, "gen_idx", dev, dtype=torch.int32)
+        _need(gen_idx.dim() == 1, "gen_idx must be 1-d")
+    _check_tensor(out, "out", dev, dtype=torch.float32, shape=(B, H, n_q, hd))
+
+
+def _check_workspace(ws, dev, need):
+    _check_tensor(ws, "workspace", dev, dtype=torch.uint8)
+    _need(ws.numel() >= need, f"workspace holds {ws.numel()} bytes, the call needs {need}")
+
+
 def workspace_bytes(pyr, n_q, n_gen, budgets):
     return int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, _budget_array(budgets)))
 
@@ -242,6 +320,18 @@ class Workspace:
 _WORKSPACES = {}
 
 
+def default_workspace(device):
+    """The workspace calls without an explicit one use: one per (device,
+    current stream), so calls on different streams never share scratch
+    memory (concurrent calls on one workspace would race)."""
+    device = torch.device(device)
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = _WORKSPACES[key] = Workspace(device)
+    return ws
+
+
 def _agg_code(agg):
     if agg not in AGGREGATIONS:
         raise ValueError("agg must be 'max' or 'mean'")
@@ -258,25 +348,13 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
     ``score_levels`` (``[B, H, sum k_j]``, level L first).
     """
     agg_code = _agg_code(agg)
+    _need(isinstance(q, torch.Tensor) and q.is_cuda, "q must be a device tensor")
+    _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
     B, H, n_q, d = q.shape
     n_tot = k.shape[2]
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
-    if gen_idx is not None and (gen_idx.dtype != torch.int32 or not gen_idx.is_contiguous()):
-        raise ValueError("gen_idx must be a contiguous int32 device tensor")
-    if q.dtype != k.dtype or k.dtype != v.dtype or _dtype_code(q) != pyr.desc.dtype:
-        raise WfError(-3, "select_attend")
+    dev = q.device
     n_gen = 0 if gen_idx is None else gen_idx.numel()
     budgets = [int(b) for b in budgets]
-    barr = _budget_array(budgets)
-    ws_need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, barr))
-    if ws_need == 0:
-        raise WfError(-5, "wf_select_attend_workspace_bytes")
-    if workspace is None:
-        workspace = _WORKSPACES.setdefault(q.device, Workspace(q.device))
-    ws = workspace.get(ws_need)
-    dev = q.device
     if out is None:
         out = torch.empty((B, H, n_q, d), dtype=torch.float32, device=dev)
     k0 = budgets[-1]
@@ -286,6 +364,14 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
     if levels_out:
         sel_levels = torch.empty((B, H, sum(budgets)), dtype=torch.int32, device=dev)
         score_levels = torch.empty((B, H, sum(budgets)), dtype=torch.float32, device=dev)
+    _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out, sel_levels, score_levels)
+    barr = _budget_array(budgets)
+    ws_need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, barr))
+    if ws_need == 0:
+        raise WfError(-5, "wf_select_attend_workspace_bytes")
+    if workspace is None:
+        workspace = default_workspace(dev)
+    ws = workspace.get(ws_need)
 
     def ptr(t):
         return ctypes.c_void_p(0 if t is None else t.data_ptr())
@@ -322,26 +408,20 @@ def attend_selected(q, k, v, sel, gen_idx, out=None, workspace=None):
     """Attention only over a selection made earlier (``sel``: int32
     ``[B, H, k0]`` prompt rows, e.g. ``select_attend(...)["sel"]``) plus the
     generated rows ``gen_idx``.  Returns float32 ``[B, H, n_q, d]``."""
+    _need(isinstance(q, torch.Tensor) and q.is_cuda, "q must be a device tensor")
+    _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
     B, H, n_q, d = q.shape
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
-    if q.dtype != k.dtype or k.dtype != v.dtype:
-        raise WfError(-3, "attend_selected")
-    if sel is not None and (sel.dtype != torch.int32 or not sel.is_contiguous() or tuple(sel.shape[:2]) != (B, H)):
-        raise ValueError("sel must be a contiguous int32 [B, H, k0] device tensor")
-    if gen_idx is not None and (gen_idx.dtype != torch.int32 or not gen_idx.is_contiguous()):
-        raise ValueError("gen_idx must be a contiguous int32 device tensor")
+    if out is None:
+        out = torch.empty((B, H, n_q, d), dtype=torch.float32, device=q.device)
+    _check_attend_args(q, k, v, sel, gen_idx, out)
     k0 = 0 if sel is None else sel.shape[-1]
     n_gen = 0 if gen_idx is None else gen_idx.numel()
     need = attend_selected_workspace_bytes(B, H, d, _dtype_code(q), n_q, k0, n_gen)
     if need == 0:
         raise WfError(-2, "wf_attend_selected_workspace_bytes")
     if workspace is None:
-        workspace = _WORKSPACES.setdefault(q.device, Workspace(q.device))
+        workspace = default_workspace(q.device)
     ws = workspace.get(need)
-    if out is None:
-        out = torch.empty((B, H, n_q, d), dtype=torch.float32, device=q.device)
     st = lib().wf_attend_selected(*_attend_selected_args(q, k, v, sel, gen_idx, out, ws))
     if st != WF_OK:
         raise WfError(st, "wf_attend_selected")
@@ -352,6 +432,14 @@ class PreparedAttend:
     """An attend_selected call with its arguments marshalled once."""
 
     def __init__(self, q, k, v, sel, gen_idx, out, workspace):
+        _need(isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 4, "q must be a 4-d device tensor")
+        _check_attend_args(q, k, v, sel, gen_idx, out)
+        B, H, n_q, d = q.shape
+        need = attend_selected_workspace_bytes(B, H, d, _dtype_code(q), n_q, 0 if sel is None else sel.shape[-1],
+                                               0 if gen_idx is None else gen_idx.numel())
+        if need == 0:
+            raise WfError(-2, "PreparedAttend")
+        _check_workspace(workspace, q.device, need)
         self._keep = (q, k, v, sel, gen_idx, out, workspace)
         self._args = _attend_selected_args(q, k, v, sel, gen_idx, out, workspace)
         self._fn = lib().wf_attend_selected
@@ -379,11 +467,15 @@ class PreparedStep:
     def __init__(self, q, pyr, k, v, gen_idx, budgets, out, sel_out, workspace, sel_levels=None, score_levels=None,
                  agg="max"):
         n_gen = 0 if gen_idx is None else gen_idx.numel()
+        _need(isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 4, "q must be a 4-d device tensor")
+        budgets = [int(b) for b in budgets]
+        _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out, sel_levels, score_levels)
         self._keep = (q, pyr, k, v, gen_idx, out, sel_out, workspace, sel_levels, score_levels)
         self._barr = _budget_array(budgets)
         need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), q.shape[2], n_gen, self._barr))
-        if need == 0 or workspace.numel() < need:
-            raise WfError(-6, "PreparedStep")
+        if need == 0:
+            raise WfError(-5, "PreparedStep")
+        _check_workspace(workspace, q.device, need)
 
         def ptr(t):
             return ctypes.c_void_p(0 if t is None else t.data_ptr())

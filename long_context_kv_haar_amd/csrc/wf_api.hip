@@ -92,6 +92,9 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->k0 = P->budgets[L];
   P->sum_k = (int)sum_k;
   if (P->k_top > wf::kMaxKeepTop) return WF_ERR_BUDGET;
+  // the attended set T (kept tokens + generated positions) is indexed in int
+  // and chunked per split: same bound as the attention-only plan
+  if ((int64_t)P->k0 + n_gen > (1 << 24)) return WF_ERR_SHAPE;
   P->covered = (int64_t)P->k_top << L;
   int64_t off = 0;
   for (int j = 0; j < L; ++j) {  // level arrays start on 16-byte boundaries

@@ -178,3 +178,112 @@ def test_refresh_rejects_bad_arguments():
     mixed = [(FAKE, fake_pyramid(), FAKE, 8, 1024 * 64), (FAKE, fake_pyramid(dt=wf.WF_F32), FAKE, 8, 1024 * 64)]
     assert refresh(mixed) == -3
 
+
+
+def test_select_plan_rejects_an_attended_set_beyond_int_range():
+    """The kept tokens plus the generated positions must stay within the
+    attention's 2^24-entry bound, as for the attention-only call."""
+    p = fake_pyramid()
+    q = lib().wf_select_attend_workspace_bytes
+    assert q(ctypes.byref(p), 32, 5000, budgets_arr([8, 16, 32, 64])) > 0
+    assert q(ctypes.byref(p), 32, (1 << 24) - 63, budgets_arr([8, 16, 32, 64])) == 0
+    assert q(ctypes.byref(p), 32, 0x7FFFFFF0, budgets_arr([8, 16, 32, 64])) == 0
+    assert select(n_gen=0x7FFFFFF0) == -2
+
+
+class _FakePyr:
+    """A Python-side pyramid over a fake descriptor (never passed to a kernel)."""
+
+    def __init__(self, **kw):
+        self.desc = fake_pyramid(**kw)
+
+
+def _select_case(**over):
+    """Consistent CPU tensors of a select-attend call on the fake pyramid
+    (B=1, H=2, N_p=1024, d=64, bf16, L=3), with some replaced."""
+    import torch
+    bf = torch.bfloat16
+    args = dict(q=torch.zeros(1, 2, 32, 64, dtype=bf), k=torch.zeros(1, 2, 1056, 64, dtype=bf),
+                v=torch.zeros(1, 2, 1056, 64, dtype=bf), gen_idx=torch.arange(1024, 1056, dtype=torch.int32),
+                budgets=[8, 16, 32, 64], out=torch.zeros(1, 2, 32, 64), sel_out=torch.zeros(1, 2, 64, dtype=torch.int32))
+    args.update(over)
+    return args
+
+
+@pytest.mark.parametrize("bad", [
+    dict(q=None),                                                    # q of fewer heads
+    dict(v="short"),                                                 # v shorter than k
+    dict(k="few_rows"),                                              # fewer rows than the prompt
+    dict(k="d32"),                                                   # head dim differs from the pyramid's
+    dict(gen_idx="int64"),
+    dict(gen_idx="2d"),
+    dict(out="bf16"),
+    dict(out="shape"),
+    dict(sel_out="shape"),
+    dict(budgets=[8, 16, 64]),                                       # one budget per level
+    dict(q="f32"),                                                   # dtype differs from the pyramid's
+])
+def test_select_args_are_checked_on_the_host(bad):
+    """Mismatched tensors raise before any library call (so no kernel can
+    read or write past a buffer)."""
+    import torch
+    from long_context_kv_haar_amd._lib import _check_select_args
+    a = _select_case()
+    key, val = next(iter(bad.items()))
+    if key == "q" and val is None:
+        a["q"] = torch.zeros(1, 1, 32, 64, dtype=torch.bfloat16)
+    elif val == "short":
+        a["v"] = a["v"][:, :, :1000].contiguous()
+    elif val == "few_rows":
+        a["k"] = a["k"][:, :, :1000].contiguous()
+        a["v"] = a["v"][:, :, :1000].contiguous()
+    elif val == "d32":
+        a["k"] = torch.zeros(1, 2, 1056, 32, dtype=torch.bfloat16)
+        a["v"] = torch.zeros(1, 2, 1056, 32, dtype=torch.bfloat16)
+    elif val == "int64":
+        a["gen_idx"] = a["gen_idx"].long()
+    elif val == "2d":
+        a["gen_idx"] = a["gen_idx"].view(2, 16)
+    elif val == "bf16":
+        a["out"] = a["out"].bfloat16()
+    elif key == "out":
+        a["out"] = torch.zeros(1, 2, 31, 64)
+    elif key == "sel_out":
+        a["sel_out"] = torch.zeros(1, 2, 63, dtype=torch.int32)
+    elif key == "budgets":
+        a["budgets"] = val
+    elif val == "f32":
+        a["q"], a["k"], a["v"] = (a[n].float() for n in ("q", "k", "v"))
+    with pytest.raises((ValueError, TypeError)):
+        _check_select_args(a["q"], _FakePyr(), a["k"], a["v"], a["gen_idx"], a["budgets"], a["out"], a["sel_out"])
+
+
+def test_consistent_select_args_pass_the_host_checks():
+    from long_context_kv_haar_amd._lib import _check_select_args
+    a = _select_case()
+    _check_select_args(a["q"], _FakePyr(), a["k"], a["v"], a["gen_idx"], a["budgets"], a["out"], a["sel_out"])
+
+
+def test_attend_args_are_checked_on_the_host():
+    import torch
+    from long_context_kv_haar_amd._lib import _check_attend_args
+    bf = torch.bfloat16
+    q, k = torch.zeros(1, 2, 16, 64, dtype=bf), torch.zeros(1, 2, 300, 64, dtype=bf)
+    v, out = torch.zeros(1, 2, 300, 64, dtype=bf), torch.zeros(1, 2, 16, 64)
+    sel, gen = torch.zeros(1, 2, 10, dtype=torch.int32), torch.zeros(5, dtype=torch.int32)
+    _check_attend_args(q, k, v, sel, gen, out)
+    for bad in (dict(v=v[:, :, :10].contiguous()), dict(sel=sel.long()), dict(sel=torch.zeros(1, 3, 10, dtype=torch.int32)),
+                dict(gen=gen.view(1, 5)), dict(out=out[:, :1].contiguous()), dict(k=k.float())):
+        args = dict(q=q, k=k, v=v, sel=sel, gen=gen, out=out)
+        args.update(bad)
+        with pytest.raises((ValueError, TypeError)):
+            _check_attend_args(args["q"], args["k"], args["v"], args["sel"], args["gen"], args["out"])
+
+
+def test_public_calls_reject_host_tensors_before_the_library():
+    import torch
+    a = _select_case()
+    with pytest.raises(ValueError):
+        wf.select_attend(a["q"], _FakePyr(), a["k"], a["v"], a["gen_idx"], a["budgets"])
+    with pytest.raises(ValueError):
+        wf.attend_selected(a["q"], a["k"], a["v"], None, a["gen_idx"])
