@@ -16,6 +16,11 @@ constexpr uint64_t kAlign = 256;
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
 int elem_bytes(int dtype) { return dtype == WF_BF16 ? 2 : 4; }
 
 bool valid_pyramid_shape(int32_t batch, int32_t heads, int32_t n_prompt, int32_t head_dim, int32_t levels) {
@@ -102,16 +107,21 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
     off += ((P->covered >> j) + 3) / 4 * 4;
   }
   P->cov_len = off;
-  // cover kernel: kept coarse regions (+ the coarse keys when they fit) in LDS
-  P->coarse_keys_in_lds = P->n_top <= wf::kMaxCoarseLds;
-  P->cover_lds = 4 * (((P->k_top + 3) & ~3) + (P->coarse_keys_in_lds ? P->n_top : 0));
-  // Above 1 024 cover workgroups (several rounds of them on the chip), one
-  // Top-K workgroup per head beats every cover workgroup repeating it
-  // (measured on 128K-token layers, 2 048 workgroups: 128.7 -> 126.4 us per
-  // call); below, the extra launch costs more than it saves (64K, 512
-  // workgroups: 66.5 -> 69.4 us).
-  P->topk_apart = P->levels > 0 && (P->covered + 255) / 256 * (int64_t)P->heads_total > 1024;
-  P->topk_lds = P->coarse_keys_in_lds ? 4 * P->n_top : 0;
+  // coarse launch: 64 regions per workgroup; the head's last workgroup takes
+  // the Top-K in registers (up to 8 192 regions), else with the keys in LDS
+  // or read from memory
+  P->coarse_wg = (P->n_top + 63) / 64;
+  P->topk_s = P->n_top <= wf::kRegSelMax ? pow2_at_least((P->n_top + wf::kCoverThreads - 1) / wf::kCoverThreads) : 0;
+  P->coarse_keys_in_lds = P->topk_s == 0 && P->n_top <= wf::kMaxCoarseLds;
+  P->coarse_lds = P->coarse_keys_in_lds ? 4 * P->n_top : 0;
+  // cover launch: 256 covered positions per workgroup, the kept coarse
+  // regions in LDS.  The refinement holds 16 level-0 positions per thread in
+  // the head's last cover workgroup (covered sets up to 4 096), 32 in a
+  // launch of its own (up to 8 192), else runs list-based in a launch of its
+  // own
+  P->cover_wg = L > 0 ? (int)((P->covered + wf::kCoverThreads - 1) / wf::kCoverThreads) : 0;
+  P->cover_lds = 4 * ((P->k_top + 3) & ~3);
+  P->refine_s0 = L == 0 ? 0 : P->covered <= 16 * wf::kCoverThreads ? 16 : P->covered <= wf::kRegSelMax ? 32 : 0;
   // a longer basis: its finer approximation bands are read from the pyramid
   P->stored_bands = (pyr->flags & WF_PYR_DB2) != 0;
   if (P->stored_bands) {
@@ -122,25 +132,18 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   }
   // attention splits
   P->chunk = wf::attend_chunk(pyr->dtype);
-  wf::plan_attention_splits(P, true);
-  // refinement workgroup LDS (one per head): the kept sets and candidate
-  // lists, plus the coverage scores when they fit
-  P->refine_nmax = (nmax + 3) / 4 * 4;
-  P->refine_kmax = (kmax + 1 + 3) / 4 * 4;  // + a spare slot for rejected candidates
+  wf::plan_attention_splits(P);
+  // list-based refinement (one workgroup per head): the kept sets and
+  // candidate lists, plus the coverage scores when they fit
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve;
-  // bitmask refinement: the kept coarse regions and 2 masks, each over at
-  // least 2 x the covered positions (a level's slots span up to the next
-  // power of two of its positions) and at least kMaskGroup positions
-  {
-    const int64_t bits = 2 * P->covered > wf::kMaskGroup ? 2 * P->covered : wf::kMaskGroup;
-    P->refine_mask_words = (int)((bits + 2047) / 2048 * 64);
+  if (L > 0 && P->refine_s0 == 0) {
+    P->refine_nmax = (nmax + 3) / 4 * 4;
+    P->refine_kmax = (kmax + 1 + 3) / 4 * 4;  // + a spare slot for rejected candidates
+    const int64_t list_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
+    if (list_base > budget) return WF_ERR_BUDGET;
+    P->refine_cov_in_lds = (list_base + 4 * P->cov_len) <= budget;
+    P->refine_lds = (int)(list_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0));
   }
-  const int64_t mask_base = 4 * (((int64_t)P->k_top + 3) / 4 * 4 + 2 * (int64_t)P->refine_mask_words);
-  const int64_t list_base = 4 * ((int64_t)P->refine_nmax + 2 * (int64_t)P->refine_kmax);
-  const int64_t refine_base = list_base > mask_base ? list_base : mask_base;
-  if (refine_base > budget) return WF_ERR_BUDGET;
-  P->refine_cov_in_lds = (refine_base + 4 * P->cov_len) <= budget;
-  P->refine_lds = (int)(refine_base + (P->refine_cov_in_lds ? 4 * P->cov_len : 0));
   // attention workgroup LDS: the split's part of T, then the K/V chunk buffers
   const int64_t buf_bytes = wf::attend_buffer_bytes(pyr->dtype, pyr->head_dim, (n_q + 15) / 16);
   if (buf_bytes > wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words) return WF_ERR_BUDGET;
@@ -148,6 +151,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
+  P->off_counters = w; w += align_up(wf::kCounterBytes);
   P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
@@ -176,13 +180,14 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
   P->k0 = k0;
   P->n_gen = n_gen;
   P->chunk = wf::attend_chunk(dtype);
-  wf::plan_attention_splits(P, false);
+  wf::plan_attention_splits(P);
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
   const int64_t buf_bytes = wf::attend_buffer_bytes(dtype, head_dim, (n_q + 15) / 16);
   if (buf_bytes > budget) return WF_ERR_BUDGET;
   P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
+  P->off_counters = w; w += align_up(wf::kCounterBytes);
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * head_dim * 4);
   P->total = w;

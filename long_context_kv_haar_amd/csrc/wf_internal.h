@@ -13,12 +13,16 @@ constexpr int kMaxLevels = WF_MAX_LEVELS;
 static_assert(kMaxLevels == kPyrMaxLevels, "one level limit");
 constexpr int kAttendGroups = 2;          // waves per query tile in the attention workgroup
 constexpr int kMaxSplit = 16;             // attention splits per head
-constexpr int kMaxCoarseLds = 16384;      // coarse keys staged in LDS up to this count
+constexpr int kMaxCoarseLds = 16384;      // general coarse Top-K: keys staged in LDS up to this count
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
-constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the Top-K scratch and friends
-constexpr int kMaskGroup = 2048;          // least positions a refinement mask spans
+constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the selection scratch and friends
 constexpr int kCoverThreads = 256;
+constexpr int kRegSelMax = 256 * 32;      // positions one workgroup's in-register selection holds
+// Arrival counters, one per (sequence, head), at the start of every
+// workspace: a fixed place, so calls of different shapes that share a
+// workspace never find data where another call expects its zero counters.
+constexpr uint64_t kCounterBytes = 4ull * (WF_MAX_HEADS + 1);
 
 // Byte layout of the per-call workspace, and the resolved launch shape.
 struct SelectPlan {
@@ -33,21 +37,22 @@ struct SelectPlan {
   // splits 0 .. n_split_p - 1 take cps_p prompt chunks each, the remaining
   // n_split - n_split_p take cps_g generated chunks each
   int n_att, chunk, n_split, n_split_p, cps_p, cps_g;
-  // LDS plans (bytes)
-  int cover_lds;                // kept coarse regions (+ coarse keys when staged)
-  int coarse_keys_in_lds;
-  int topk_apart;               // the coarse Top-K runs in a launch of its own (large cover launches)
-  int topk_lds;                 // that launch's LDS: the coarse keys, when staged
-  int refine_nmax, refine_kmax; // candidate / kept capacity (words, multiples of 4)
-  int refine_mask_words;        // words of one bitmask over the covered positions
-  int refine_cov_in_lds;        // coverage scores staged in LDS
-  int refine_lds;               // refinement workgroup: its state (kept sets, candidate lists)
+  // launch shapes and LDS plans (bytes)
+  int coarse_wg, cover_wg;      // workgroups per head of the coarse and cover launches
+  int topk_s;                   // coarse keys per thread of the in-register coarse Top-K (0: general path)
+  int coarse_keys_in_lds;       // general coarse Top-K: keys staged in LDS
+  int coarse_lds;               // coarse launch: the staged keys
+  int cover_lds;                // cover launch: the kept coarse regions
+  int refine_s0;                // level-0 positions per thread of the in-register refinement (0: list-based)
+  int refine_nmax, refine_kmax; // list-based refinement: candidate / kept capacity (words, multiples of 4)
+  int refine_cov_in_lds;        // list-based refinement: coverage scores staged in LDS
+  int refine_lds;               // list-based refinement workgroup: its state
   int stored_bands;             // levels 1 .. L-1 scored from stored A_j (longer bases)
   uint64_t band_off[kMaxLevels];  // byte offset of A_j inside the pyramid buffer, when stored
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + K/V chunk buffers
   // workspace sections (byte offsets)
-  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, total;
+  uint64_t off_counters, off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, total;
 };
 
 struct SelectLaunch {
@@ -76,37 +81,24 @@ constexpr int attend_waves_per_simd(int nqt) { return nqt == 2 ? 2 : 1; }
 
 // Split plan of the attention over T (fills n_att .. cps_g from k0, n_gen,
 // chunk, n_q and heads_total): about as many splits over all heads as
-// attention workgroups fit the chip at once.
-// gen_apart: the generated part's splits run in another launch (beside the
-// refinement), so the prompt part alone fills the chip and the generated part
-// takes up to 4 splits of its own; otherwise both parts share one count of
-// chunks per split.  At most kMaxSplit splits in all.
-inline void plan_attention_splits(SelectPlan* P, bool gen_apart) {
+// attention workgroups fit the chip at once, at most kMaxSplit per head; the
+// prompt and the generated part share one count of chunks per split.  The
+// selecting call and the attention-only call use this same plan, so over the
+// same T they compute the same thing in the same order.
+inline void plan_attention_splits(SelectPlan* P) {
   const int ch = P->chunk;
   P->n_att = P->k0 + P->n_gen;
   const int nc_p = (P->k0 + ch - 1) / ch, nc_g = (P->n_gen + ch - 1) / ch;
   const int per_cu = attend_waves_per_simd((P->n_q + 15) / 16);  // attention workgroups per compute unit
   int target = (256 * per_cu + P->heads_total - 1) / P->heads_total;
   if (target > kMaxSplit) target = kMaxSplit;
-  if (gen_apart) {
-    const int sg = nc_g < 4 ? nc_g : 4;
-    P->cps_g = sg > 0 ? (nc_g + sg - 1) / sg : 1;
-    const int n_split_g = sg > 0 ? (nc_g + P->cps_g - 1) / P->cps_g : 0;
-    if (target > kMaxSplit - n_split_g) target = kMaxSplit - n_split_g;
-    if (target < 1) target = 1;
-    P->cps_p = nc_p > 0 ? (nc_p + target - 1) / target : 1;
-    P->n_split_p = nc_p > 0 ? (nc_p + P->cps_p - 1) / P->cps_p : 0;
-    P->n_split = P->n_split_p + n_split_g;
-  } else {
-    if (target < 2) target = 2;  // room for a prompt and a generated split
-    int cps = (nc_p + nc_g + target - 1) / target;
-    if (cps < 1) cps = 1;
-    while ((nc_p + cps - 1) / cps + (nc_g + cps - 1) / cps > target) ++cps;
-    P->cps_p = P->cps_g = cps;
-    P->n_split_p = (nc_p + cps - 1) / cps;
-    P->n_split = P->n_split_p + (nc_g + cps - 1) / cps;
-  }
-  const int cps = P->cps_p > P->cps_g ? P->cps_p : P->cps_g;
+  if (target < 2) target = 2;  // room for a prompt and a generated split
+  int cps = (nc_p + nc_g + target - 1) / target;
+  if (cps < 1) cps = 1;
+  while ((nc_p + cps - 1) / cps + (nc_g + cps - 1) / cps > target) ++cps;
+  P->cps_p = P->cps_g = cps;
+  P->n_split_p = (nc_p + cps - 1) / cps;
+  P->n_split = P->n_split_p + (nc_g + cps - 1) / cps;
   P->att_t_words = (cps * ch + 3) & ~3;  // one split's part of T
 }
 

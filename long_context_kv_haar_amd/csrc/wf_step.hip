@@ -1,27 +1,26 @@
-// WaveFilter per-denoising-step kernels for gfx950 (MI355X).
+// WaveFilter per-denoising-step kernels for gfx950 (MI355X).  One call is
+// three launches; in each, the workgroups of a head count their arrival and
+// the last one to arrive finishes the head's stage (see wf_select.h for the
+// agent-scope hand-over this relies on):
 //
-//   coarse_max_kernel / coarse_mean_kernel
-//                   s_L[n] = max_i (or mean_i) q_i . A_L[n] / sqrt(d) on MFMA
-//                   (Figure 2 (c))
-//   cover_max_kernel / cover_mean_kernel
-//                   the coarse Top-K (recomputed by every workgroup of the
-//                   head, so no cross-workgroup handoff is needed, or read
-//                   from coarse_topk_kernel for large launches), then
-//                   q_i . k_t for every token the kept regions cover, on MFMA,
-//                   summed in registers into the scores of all their
-//                   sub-regions at levels 0 .. L-1 (Figure 2 (d), with A_j
-//                   taken by linearity from the token dot products)
-//   cover_bands_max_kernel / cover_bands_mean_kernel
-//                   the same on a Daubechies pyramid, from its stored bands
-//   refine_kernel   the recursive refinement, one workgroup per head, with
-//                   the coverage scores in registers and the kept sets as
-//                   bitmasks in LDS; writes the kept prompt tokens.  Its
-//                   other workgroups attend over the generated positions
-//                   (independent of the selection) meanwhile
-//   attend_kernel   split-K online-softmax attention over the kept prompt
-//                   tokens plus the generated positions (eq. 3 restricted to
-//                   that set); also serves a selection handed in by the caller
-//   combine_kernel  log-sum-exp merge of the split partial results
+//   coarse_*_kernel  s_L[n] = max_i (or mean_i) q_i . A_L[n] / sqrt(d) on
+//                    MFMA; the head's last workgroup takes the coarse Top-K
+//                    (Figure 2 (c))
+//   cover_*_kernel   q_i . k_t for every token the kept regions cover, on
+//                    MFMA, summed in registers into the scores of all their
+//                    sub-regions at levels 0 .. L-1 (A_j by linearity from
+//                    the token dot products; from the stored bands for a
+//                    longer basis); the head's last workgroup runs the
+//                    recursive refinement (Figure 2 (d)) and writes the kept
+//                    prompt tokens
+//   attend_kernel    split-K online-softmax attention over the kept prompt
+//                    tokens plus the generated positions (eq. 3 restricted
+//                    to that set); the head's last workgroup merges the
+//                    splits into O.  It also serves a selection handed in.
+//   refine_lists_kernel
+//                    the refinement for covered sets beyond the in-register
+//                    capacity, one workgroup per head, in a launch between
+//                    the cover and the attention launches
 //
 // Citations are to WaveFilter (arXiv 2606.00724).
 #include <hip/hip_runtime.h>
@@ -30,6 +29,7 @@
 
 #include "wf_device.h"
 #include "wf_internal.h"
+#include "wf_select.h"
 
 namespace wf {
 
@@ -40,29 +40,32 @@ struct StepArgs {
   const void* v;
   const int32_t* gen_idx;
   const int32_t* sel_in;  // the kept prompt tokens [heads_total][k0] the attention reads (NULL if k0 == 0)
-  int32_t* sel_ws;        // where the refinement writes them [heads_total][k0]
+  int32_t* sel_ws;        // where the selection writes them [heads_total][k0]
   float* out;
   int32_t* sel_out;
   int32_t* sel_levels;
   float* score_levels;
+  uint32_t* counters;    // [heads_total] arrival counters, zero between launches
   uint32_t* keys_top;    // [heads_total][n_top]
   int32_t* sel_top;      // [heads_total][k_top]
   float* cov;            // [heads_total][cov_len]
   uint32_t* lvl_mm;      // [heads_total][cover waves][kMaxLevels][2]: order keys of each level's least and
                          // greatest score over the positions of one coverage wave
-  float* part_ml;        // [heads_total][n_split][2][n_q]
+  float* part_ml;        // [heads_total][n_split][n_q][2]: (m, l) of each split's partial state
   float* part_o;         // [heads_total][n_split][n_q][d]
   int heads_total, n_q, n_top, n_prompt, n_tot, n_gen, levels;
   int k_top, k0, sum_k;
   int64_t covered, cov_len;
   int64_t cov_off[kMaxLevels];
   int budgets[kMaxLevels + 1];
-  int n_att, n_split, n_split_p, cps_p, cps_g;
-  int coarse_keys_in_lds, refine_cov_in_lds, refine_nmax, refine_kmax, refine_mask_words, att_t_words;
+  int n_att, n_split, n_split_p, cps_p, cps_g, att_t_words;
+  int topk_s;             // coarse keys per thread of the in-register coarse Top-K (0: the general path)
+  int coarse_keys_in_lds; // general path: keys staged in LDS
+  int refine_s0;          // level-0 positions per thread of the in-register refinement (0: refine_lists_kernel)
+  int refine_cov_in_lds, refine_nmax, refine_kmax;  // refine_lists_kernel
   float inv_sqrt_d;
   float inv_nq;  // 1 / n_q, for the mean over query rows
   int stored_bands;                    // score levels 1 .. L-1 from stored A_j (longer bases)
-  int topk_apart;                      // the coarse Top-K ran in a launch of its own (sel_top holds it)
   const float* band_a[kMaxLevels];     // A_j [heads_total][n_prompt >> j][d], when stored
 };
 
@@ -145,18 +148,147 @@ __device__ __forceinline__ void load_query_frags(const T* qs, int n_q, int l16, 
   }
 }
 
+// LDS scratch shared by the general Top-K variants a workgroup of NT threads
+// uses (large coarse sets and the list-based refinement): the strided
+// register Top-K on min(NT, 256) threads (up to 32 slots) and the
+// LDS-resident one.
+constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+template <int NT> struct TopKRaw {
+  static constexpr int ACT0 = NT < 256 ? NT : 256;
+  static constexpr size_t BYTES = cmax(sizeof(TopKFastShared<NT>), sizeof(TopKSel<ACT0, 32>));
+};
+
+// ---------------------------------------------------------------------------
+// Coarse Top-K (Figure 2 (c)) by the head's last coarse workgroup: the k_L
+// best regions from the order keys of s_L (written by every coarse
+// workgroup of the head with agent-scope stores), handed to emit(o, i, s)
+// in ascending order.  In registers for n_L <= 256 x 32 (S keys per
+// thread), else by the general Top-K with the keys in LDS (up to
+// kMaxCoarseLds) or read from memory.
+// ---------------------------------------------------------------------------
+template <int S, class Emit>
+__device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int k, SelShared& sh, Emit emit) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int pos0 = t * S;
+  float sc[S];
+  uint32_t valid = 0u, mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int p = pos0 + i;
+    const bool in = p < n;
+    const uint32_t key = load_agent(keys + min(p, n - 1));
+    sc[i] = key_to_f32(key);
+    valid |= in ? (1u << i) : 0u;
+    mn = in ? min(mn, key) : mn;
+    mx = in ? max(mx, key) : mx;
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    sh.wmn[w] = mn;
+    sh.wmx[w] = mx;
+  }
+  sel_init(sh);
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    mn = min(mn, sh.wmn[i]);
+    mx = max(mx, sh.wmx[i]);
+  }
+  SelCursor cur;
+  const uint32_t kept = select_level<S>(sc, valid, valid, pos0, k, key_to_f32(mn), key_to_f32(mx), sh, cur);
+  int o = block_excl_scan(__popc(kept), sh, 1);
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    if ((kept >> i) & 1u) {
+      if (o < k) emit(o, pos0 + i, sc[i]);  // exactly k are kept; the bound guards the buffers
+      ++o;
+    }
+}
+
+// The in-register coarse Top-K with S keys per thread for S in SLIST, else
+// (topk_s = 0) the general Top-K.
+template <bool LARGE, class Emit>
+__device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, unsigned char* raw, uint32_t* keys_l,
+                                                Emit emit) {
+  const uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
+  SelShared& sh = *reinterpret_cast<SelShared*>(raw);
+  if constexpr (!LARGE) {
+    switch (a.topk_s) {
+      case 1: coarse_topk_sel<1>(keys, a.n_top, a.k_top, sh, emit); return;
+      case 2: coarse_topk_sel<2>(keys, a.n_top, a.k_top, sh, emit); return;
+      default: coarse_topk_sel<4>(keys, a.n_top, a.k_top, sh, emit); return;
+    }
+  } else {
+    switch (a.topk_s) {
+      case 8: coarse_topk_sel<8>(keys, a.n_top, a.k_top, sh, emit); return;
+      case 16: coarse_topk_sel<16>(keys, a.n_top, a.k_top, sh, emit); return;
+      case 32: coarse_topk_sel<32>(keys, a.n_top, a.k_top, sh, emit); return;
+      default: break;
+    }
+    auto& fs = *reinterpret_cast<TopKFastShared<kSelThreads>*>(raw);
+    auto out = [&](int o, int i) {
+      if (o < a.k_top) emit(o, i, key_to_f32(load_agent(keys + i)));
+    };
+    if (a.coarse_keys_in_lds) {
+      for (int i = threadIdx.x; i < a.n_top; i += kSelThreads) keys_l[i] = load_agent(keys + i);
+      __syncthreads();
+      topk_fast<kSelThreads>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, fs, out);
+    } else {
+      topk_fast<kSelThreads>([&](int i) { return load_agent(keys + i); }, a.n_top, a.k_top, fs, out);
+    }
+  }
+}
+
+// The coarse Top-K of one head and its outputs: the kept regions (the cover
+// launch reads them), the level-L sinks, and for L = 0 the kept tokens.
+template <bool LARGE>
+__device__ __forceinline__ void coarse_topk_head(const StepArgs& a, int head, unsigned char* raw, uint32_t* keys_l) {
+  const bool report = a.sel_levels || a.score_levels;
+  int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  // with L = 0 the coarse level is the tokens themselves: these are the kept tokens
+  int32_t* tsel = a.levels == 0 ? a.sel_ws + (int64_t)head * a.k0 : nullptr;
+  int32_t* tout = (a.levels == 0 && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  coarse_topk_run<LARGE>(a, head, raw, keys_l, [&](int o, int i, float sc) {
+    sel_g[o] = i;
+    if (report) {
+      if (dbg_sel) dbg_sel[o] = i;
+      if (dbg_score) dbg_score[o] = sc;
+    }
+    if (tsel) {
+      tsel[o] = i;
+      if (tout) tout[o] = i;
+    }
+  });
+}
+
+// The coarse Top-K runs in the coarse launch's last workgroup of a head for
+// up to 4 keys per thread (n_L <= 1 024), else in a launch of its own.
+__device__ __forceinline__ bool topk_in_coarse(const StepArgs& a) { return a.topk_s >= 1 && a.topk_s <= 4; }
+
+// Selection scratch of the coarse and cover workgroups: the in-register
+// selection state, or the general Top-K's.
+constexpr size_t kSelRawBytes = cmax(sizeof(SelShared), TopKRaw<kSelThreads>::BYTES);
+
 // ---------------------------------------------------------------------------
 // Coarse scores.  Wave w of block x scores level-L regions
 // n = 64 x + 16 w + [0, 16): tile = A_L rows (A operand) x Q^T (B operand),
 // so lane (query 16 qt + l16, g) holds regions 16 w + 4 g + r.  For bfloat16
 // inputs the float32 coefficients are split into bf16 hi + lo parts, both
 // multiplied exactly, accumulated in float32.  Max over queries: in registers
-// over qt, then across the 16 lanes of a row.
+// over qt, then across the 16 lanes of a row.  The head's last workgroup
+// then takes the coarse Top-K and writes the kept regions (for L = 0, the
+// kept tokens).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int RT, bool MEAN>
-__device__ __forceinline__ void coarse_scores(const StepArgs& a) {
+__device__ __forceinline__ void coarse_stage(const StepArgs& a) {
   using AG = QueryAgg<MEAN>;
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
+  __shared__ __align__(16) unsigned char raw[sizeof(SelShared)];
   const int head = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -229,51 +361,20 @@ __device__ __forceinline__ void coarse_scores(const StepArgs& a) {
   if (l16 == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (n0 + r < a.n_top) keys[n0 + r] = order_key(m[r] * sc);
+      if (n0 + r < a.n_top) store_agent(keys + n0 + r, order_key(m[r] * sc));
   }
+
+  // -- the head's last workgroup: the coarse Top-K
+  if (!topk_in_coarse(a)) return;  // uniform: coarse_topk_kernel takes it
+  SelShared& sh = *reinterpret_cast<SelShared*>(raw);
+  if (!arrive_last(a.counters + head, gridDim.x, &sh.last)) return;
+  coarse_topk_head<false>(a, head, raw, nullptr);
 }
 
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void coarse_max_kernel(StepArgs a) { coarse_scores<T, D, RT, false>(a); }
+__global__ __launch_bounds__(256) void coarse_max_kernel(StepArgs a) { coarse_stage<T, D, RT, false>(a); }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void coarse_mean_kernel(StepArgs a) { coarse_scores<T, D, RT, true>(a); }
-
-// State of the fast refinement level (see refine_level_fast).
-struct RefineShared {
-  static constexpr int NB = 1024;   // histogram bins (a power of two, 16 per lane of a wave)
-  static constexpr int LMAX = 256;  // boundary-bin list capacity
-  int hist[NB];
-  uint64_t list[LMAX];
-  int list_n[2];  // list lengths, by level parity (the other one is cleared for the next level)
-  int pad[2];
-};
-constexpr size_t kRefineFastBytes = sizeof(RefineShared);
-
-// LDS scratch shared by every Top-K variant a workgroup of NT threads uses:
-// the strided register Top-K on min(NT, 256) threads (up to 32 slots), on
-// 512 threads (16 slots) for large workgroups, and the LDS-resident fallback.
-constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-template <int NT> struct TopKRaw {
-  static constexpr int ACT0 = NT < 256 ? NT : 256;
-  static constexpr int MACT = 1 << floor_log2(NT);     // mask Top-K threads (a power of two)
-  static constexpr int MMAX = NT > 256 ? 16 : 32;      // and its slots per thread (registers)
-  static constexpr size_t BYTES =
-      cmax(cmax(sizeof(TopKFastShared<NT>), kRefineFastBytes),
-           cmax(sizeof(TopKSel<ACT0, 32>), NT >= 512 ? sizeof(TopKSel<512, 16>) : size_t(0)));
-};
-
-// Coarse Top-K with the keys in registers (n <= ACT * MAXS); emit(o, i)
-// gets output slot o of region i.
-template <int NT, int ACT, int MAXS, class Emit>
-__device__ __forceinline__ void coarse_topk_regs(const uint32_t* keys_g, int n, int k, unsigned char* raw,
-                                                 Emit emit) {
-  auto& sh = *reinterpret_cast<TopKSel<ACT, MAXS>*>(raw);
-  topk_strided<NT, ACT, MAXS>(
-      n, k, sh, [&](int i, int) { return keys_g[i]; },
-      [&](int o, bool kept, int i, int) {
-        if (kept) emit(o, i);
-      });
-}
+__global__ __launch_bounds__(256) void coarse_mean_kernel(StepArgs a) { coarse_stage<T, D, RT, true>(a); }
 
 // One 16-row tile of float32 coefficient rows (A operand; lane row l16,
 // k-slice g) against the staged query tiles (B operands): bfloat16 queries
@@ -344,7 +445,7 @@ __device__ __forceinline__ void f32_rows_mma(const float4 (&x)[D / 16], const Fr
 // positions (a neutral range where it has none).  The level's four 16-row
 // tiles go in pairs, both tiles' rows requested before either is multiplied;
 // rows past the level's end repeat its last row (in bounds) and are never
-// written.
+// written.  Writes are agent-scope: the head's last workgroup reads them.
 template <typename T, int D, int RT, bool MEAN>
 __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, const int* sel_l, const Frag<T, D> (&qf)[RT],
                                                  int64_t wave_base, int lane, int g, int l16) {
@@ -401,7 +502,7 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
             const float m = AG::row(x) * sc;
             const int64_t pr = p0 + 4 * g + r;
             const bool in = (l16 == 0) && pr < nj;
-            if (in) cov[a.cov_off[j] + pr] = m;
+            if (in) store_agent(cov + a.cov_off[j] + pr, m);
             const uint32_t k = order_key(m);
             rmn = in ? min(rmn, k) : rmn;
             rmx = in ? max(rmx, k) : rmx;
@@ -412,99 +513,30 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
     rmn = wave_min_u32(rmn);
     rmx = wave_max_u32(rmx);
     if (lane == 0) {
-      lvl[2 * j] = rmn;
-      lvl[2 * j + 1] = rmx;
+      store_agent(lvl + 2 * j, rmn);
+      store_agent(lvl + 2 * j + 1, rmx);
     }
   }
 }
 
-// Coarse Top-K (Figure 2 (c)) of one head: the k_L best regions, ascending,
-// from the order keys of s_L, handed to emit(o, i).  All NT threads call it;
-// keys_l is LDS for n_L keys when they are staged.
-template <int NT, class Emit>
-__device__ __forceinline__ void coarse_topk_head(const StepArgs& a, int head, uint32_t* keys_l, unsigned char* tk_raw,
-                                                 Emit emit) {
-  auto& sh = *reinterpret_cast<TopKFastShared<NT>*>(tk_raw);
-  const uint32_t* keys_g = a.keys_top + (int64_t)head * a.n_top;
-  static_assert(NT == 256, "coarse Top-K layout");
-  if (a.n_top <= NT * 4) {
-    coarse_topk_regs<NT, NT, 4>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.n_top <= NT * 8) {
-    coarse_topk_regs<NT, NT, 8>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.n_top <= NT * 16) {
-    coarse_topk_regs<NT, NT, 16>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.n_top <= NT * 32) {
-    coarse_topk_regs<NT, NT, 32>(keys_g, a.n_top, a.k_top, tk_raw, emit);
-  } else if (a.coarse_keys_in_lds) {
-    for (int i = threadIdx.x; i < a.n_top; i += NT) keys_l[i] = keys_g[i];
-    __syncthreads();
-    topk_fast<NT>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, sh, emit);
-  } else {
-    topk_fast<NT>([&](int i) { return keys_g[i]; }, a.n_top, a.k_top, sh, emit);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Cover: coarse Top-K, then coverage scores.
-//
-// The kept coarse regions, ascending, cover positions p = 0 .. k_L 2^L - 1;
-// position p is token sel_L[p >> L] 2^L + (p mod 2^L).  Wave w of block x
-// owns positions 256 x + 64 w + [0, 64) as four 16-token tiles t; tile = K
-// rows (A operand) x Q^T (B operand), so lane (query 16 qt + l16, g) holds
+// Haar coverage scores of one wave.  The kept coarse regions, ascending,
+// cover positions p = 0 .. k_L 2^L - 1; position p is token
+// sel_L[p >> L] 2^L + (p mod 2^L).  The wave owns positions
+// wave_base + [0, 64) as four 16-token tiles t; tile = K rows (A operand) x
+// Q^T (B operand), so lane (query 16 qt + l16, g) holds
 // S[query][tokens 16 t + 4 g + r].  Sums along the token axis: levels 1 and
 // 2 in-lane (r), levels 3 and 4 across lane groups g (xor 16, xor 32),
 // levels 5 and 6 across tiles in registers.  The score of a block is the max
 // over queries: over qt in registers, then across the 16 lanes of a row.
-// Scores are written per level at the block's position p >> j.
+// Scores are written per level at the block's position p >> j, with
+// agent-scope stores, and so is each level's score range over the wave.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int RT, bool MEAN, bool BANDS>
-__device__ __forceinline__ void cover_scores(const StepArgs& a) {
+template <typename T, int D, int RT, bool MEAN>
+__device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const int* sel_l, const Frag<T, D> (&qf)[RT],
+                                           int64_t wave_base, int lane, int g, int l16) {
   using AG = QueryAgg<MEAN>;
-  constexpr int NT = kCoverThreads;
-  extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
-  __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
-  // the query block, staged now and read after the Top-K's barriers
-  if (a.levels > 0) stage_query<T, D, NT>(reinterpret_cast<const T*>(a.q) + (int64_t)blockIdx.y * a.n_q * D, a.n_q, qs);
-  const int head = blockIdx.y;
   const int L = a.levels;
-  int* sel_l = reinterpret_cast<int*>(lds);  // k_top kept regions, ascending
-  uint32_t* keys_l = lds + ((a.k_top + 3) & ~3);
-  const uint32_t* keys_g = a.keys_top + (int64_t)head * a.n_top;
-
-  // -- coarse Top-K of this head (every workgroup of the head computes the same set)
-  const bool first = blockIdx.x == 0;
-  int32_t* dbg_sel = (first && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-  float* dbg_score = (first && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
-  int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-  auto emit = [&](int o, int i) {
-    if (o < a.k_top) {
-      sel_l[o] = i;
-      if (first) sel_g[o] = i;
-      if (dbg_sel) dbg_sel[o] = i;
-      if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
-    }
-  };
-  if (!a.topk_apart) {  // uniform
-    coarse_topk_head<NT>(a, head, keys_l, tk_raw, emit);
-  } else {  // large launches: the Top-K kernel has written the head's kept regions
-    for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
-  }
-  __syncthreads();
-  if (L == 0) return;  // no finer level to score
-
-  // -- coverage scores
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
-  const int64_t wave_base = (int64_t)blockIdx.x * 256 + w * 64;
-  if (wave_base >= a.covered) return;  // no workgroup barrier below
-  Frag<T, D> qf[RT];
-  load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
-  if constexpr (BANDS) {  // a longer basis, scored from its stored bands (its own kernel: more registers)
-    cover_from_bands<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
-    return;
-  } else {
-
   const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
   Frag<T, D> kf[4];
 #pragma unroll
@@ -551,8 +583,8 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
     rmn = wave_min_u32(rmn);
     rmx = wave_max_u32(rmx);
     if (lane == 0) {
-      lvl[2 * j] = rmn;
-      lvl[2 * j + 1] = rmx;
+      store_agent(lvl + 2 * j, rmn);
+      store_agent(lvl + 2 * j + 1, rmx);
     }
   };
   // level 0
@@ -569,8 +601,11 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       m[r] = AG::row(x) * isd;
     }
     const int64_t p = tb + 16 * t;
-    if (writer && p < a.covered)
-      *reinterpret_cast<float4*>(cov + a.cov_off[0] + p) = make_float4(m[0], m[1], m[2], m[3]);
+    if (writer && p < a.covered) {  // covered is a multiple of 4 when L >= 2; at L = 1 of 2
+      float* dst = cov + a.cov_off[0] + p;
+      store_agent2(dst, m[0], m[1]);
+      if (p + 2 < a.covered) store_agent2(dst + 2, m[2], m[3]);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) track(writer && p + r < a.covered, m[r]);
   }
@@ -597,8 +632,7 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
         m[h] = AG::row(x) * sc;
       }
       const int64_t p = tb + 16 * t;
-      if (writer && p < a.covered)
-        *reinterpret_cast<float2*>(cov + a.cov_off[1] + (p >> 1)) = make_float2(m[0], m[1]);
+      if (writer && p < a.covered) store_agent2(cov + a.cov_off[1] + (p >> 1), m[0], m[1]);
       track(writer && p < a.covered, m[0]);
       track(writer && p + 2 < a.covered, m[1]);
     }
@@ -619,7 +653,7 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
       x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
-      if (writer && p < a.covered) cov[a.cov_off[2] + (p >> 2)] = x;
+      if (writer && p < a.covered) store_agent(cov + a.cov_off[2] + (p >> 2), x);
       track(writer && p < a.covered, x);
     }
   }
@@ -639,7 +673,7 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
       x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
-      if (writer && (g & 1) == 0 && p < a.covered) cov[a.cov_off[3] + (p >> 3)] = x;
+      if (writer && (g & 1) == 0 && p < a.covered) store_agent(cov + a.cov_off[3] + (p >> 3), x);
       track(writer && (g & 1) == 0 && p < a.covered, x);
     }
   }
@@ -659,7 +693,7 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
       x = AG::row(x) * sc;
       const int64_t p = wave_base + 16 * t;
-      if (writer && g == 0 && p < a.covered) cov[a.cov_off[4] + (p >> 4)] = x;
+      if (writer && g == 0 && p < a.covered) store_agent(cov + a.cov_off[4] + (p >> 4), x);
       track(writer && g == 0 && p < a.covered, x);
     }
   }
@@ -681,9 +715,9 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
     x23 = AG::row(x23) * (isd * 0.17677669529663688110f);
     xall = AG::row(xall) * (isd * 0.125f);                 // 2^{-3}
     if (lane == 0) {
-      if (wave_base < a.covered) cov[a.cov_off[5] + (wave_base >> 5)] = x01;
-      if (wave_base + 32 < a.covered) cov[a.cov_off[5] + (wave_base >> 5) + 1] = x23;
-      if (jmax > 6) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
+      if (wave_base < a.covered) store_agent(cov + a.cov_off[5] + (wave_base >> 5), x01);
+      if (wave_base + 32 < a.covered) store_agent(cov + a.cov_off[5] + (wave_base >> 5) + 1, x23);
+      if (jmax > 6) store_agent(cov + a.cov_off[6] + (wave_base >> 6), xall);
     }
     rmn = 0xFFFFFFFFu;
     rmx = 0u;
@@ -697,27 +731,235 @@ __device__ __forceinline__ void cover_scores(const StepArgs& a) {
       publish(6);
     }
   }
-  }  // Haar
+}
+
+// ---------------------------------------------------------------------------
+// Recursive refinement (Figure 2 (d)) of one head in registers, by the
+// head's last cover workgroup: thread t holds the level-0 positions
+// [t S0, t S0 + S0) and their ancestors (see wf_select.h).  Every level's
+// coverage scores and score range are loaded at the start (agent-scope
+// loads: other workgroups of the launch wrote them), then each level keeps
+// the k_j best children of the kept parents.  Writes the kept tokens
+// ascending, and with the per-level sinks every level's kept regions.
+// ---------------------------------------------------------------------------
+template <int J> struct IntC { static constexpr int value = J; };
+template <int J, class F>
+__device__ __forceinline__ void for_levels_desc(F&& f) {
+  f(IntC<J>{});
+  if constexpr (J > 0) for_levels_desc<J - 1>(f);
+}
+static_assert(kMaxLevels == 7, "the refinement holds seven levels");
+
+template <int S0, int J> struct Held { static constexpr int N = (S0 >> J) > 0 ? (S0 >> J) : 1; };
+template <int S0> struct HeldScores {
+  float s0[Held<S0, 0>::N], s1[Held<S0, 1>::N], s2[Held<S0, 2>::N], s3[Held<S0, 3>::N];
+  float s4[Held<S0, 4>::N], s5[Held<S0, 5>::N], s6[Held<S0, 6>::N];
+  template <int J> __device__ __forceinline__ auto& get() {
+    if constexpr (J == 0) return s0;
+    else if constexpr (J == 1) return s1;
+    else if constexpr (J == 2) return s2;
+    else if constexpr (J == 3) return s3;
+    else if constexpr (J == 4) return s4;
+    else if constexpr (J == 5) return s5;
+    else return s6;
+  }
+};
+
+template <int S0>
+__device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const int* sel_l, SelShared& sh) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int L = a.levels;
+  const int covered = (int)a.covered;
+  const float* cov = a.cov + (int64_t)head * a.cov_len;
+  // each level's score range: the cover waves' slots (at most 128 per head
+  // here, lanes l and l + 64 of every wave), reduced by every wave.  Loads
+  // are unconditional, from clamped slots; slots past the last wave take the
+  // neutral range by an all-ones mask.
+  const int nwav = (covered + 63) >> 6;
+  const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
+  uint32_t rmn[kMaxLevels], rmx[kMaxLevels];
+  {
+    uint32_t x[2][kMaxLevels][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int v = min(lane + 64 * r, nwav - 1);
+#pragma unroll
+      for (int j = 0; j < kMaxLevels; ++j) {
+        const float2 p = load_agent2(reinterpret_cast<const float*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j));
+        x[r][j][0] = __float_as_uint(p.x);
+        x[r][j][1] = __float_as_uint(p.y);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxLevels; ++j) {
+      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t off = (uint32_t)((nwav - 1 - (lane + 64 * r)) >> 31);  // ~0u past the last wave
+        mn = min(mn, x[r][j][0] | off);
+        mx = max(mx, x[r][j][1] & ~off);
+      }
+      rmn[j] = wave_min_u32(mn);
+      rmx[j] = wave_max_u32(mx);
+    }
+  }
+  // every live level's scores into registers (clamped positions; slots past
+  // a level's end are never valid)
+  HeldScores<S0> hs;
+  for_levels_desc<kMaxLevels - 1>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int PJ = Held<S0, J>::N;
+    auto& s = hs.template get<J>();
+    if (J < L) {
+      const int nj = covered >> J;
+      const float* src = cov + a.cov_off[J];
+      const int p0 = (t * S0) >> J;
+      if constexpr (PJ >= 2) {
+#pragma unroll
+        for (int i = 0; i < PJ; i += 2) {
+          const float2 v = load_agent2(src + min(p0 + i, nj - 2));
+          s[i] = v.x;
+          s[i + 1] = v.y;
+        }
+      } else {
+        s[0] = load_agent(src + min(p0, nj - 1));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PJ; ++i) s[i] = 0.f;
+    }
+  });
+  sel_init(sh);
+  __syncthreads();
+
+  // level L: every kept coarse region (positions [0, k_L))
+  uint32_t keptp = 0u;
+  {
+    const int pl0 = (t * S0) >> L;
+    const int pl = (S0 >> L) > 0 ? (S0 >> L) : 1;
+    for (int m = 0; m < pl; ++m) keptp |= (pl0 + m < a.k_top) ? (1u << m) : 0u;
+  }
+  uint32_t kmask[kMaxLevels], omask[kMaxLevels];
+  SelCursor cur;
+  for_levels_desc<kMaxLevels - 1>([&](auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int PJ = Held<S0, J>::N;
+    kmask[J] = 0u;
+    omask[J] = 0u;
+    if (J < L) {
+      const int p0 = (t * S0) >> J, nj = covered >> J;
+      const bool own = PJ > 1 || ((t * S0) & ((1 << J) - 1)) == 0;
+      uint32_t valid = 0u;
+#pragma unroll
+      for (int i = 0; i < PJ; ++i) valid |= ((p0 + i < nj) && ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
+      const uint32_t owned = own ? valid : 0u;
+      const uint32_t kept = select_level<PJ>(hs.template get<J>(), valid, owned, p0, a.budgets[L - J],
+                                             key_to_f32(rmn[J]), key_to_f32(rmx[J]), sh, cur);
+      kmask[J] = kept;
+      omask[J] = own ? kept : 0u;
+      keptp = kept;
+    }
+  });
+
+  // the kept tokens, ascending
+  {
+    const uint32_t k0m = kmask[0];
+    int o = block_excl_scan(__popc(k0m), sh, 1);
+    int32_t* tsel = a.sel_ws + (int64_t)head * a.k0;
+    int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+    const int mask = (1 << L) - 1;
+#pragma unroll
+    for (int i = 0; i < S0; ++i)
+      if ((k0m >> i) & 1u) {
+        const int p = t * S0 + i;
+        const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & mask);
+        if (o < a.k0) {  // exactly k_0 are kept; the bound guards the buffers
+          tsel[o] = tok;
+          if (so) so[o] = tok;
+        }
+        ++o;
+      }
+  }
+  // the kept regions of levels L-1 .. 0 and their scores
+  if (a.sel_levels || a.score_levels) {
+    int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+    float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+    int off = a.k_top;
+    for_levels_desc<kMaxLevels - 1>([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int PJ = Held<S0, J>::N;
+      if (J < L) {
+        const int kj = a.budgets[L - J];
+        int o = block_excl_scan(__popc(omask[J]), sh, 2 + (J & 1));
+        const int shl = L - J, p0 = (t * S0) >> J;
+#pragma unroll
+        for (int i = 0; i < PJ; ++i)
+          if ((omask[J] >> i) & 1u) {
+            const int p = p0 + i;
+            if (o < kj) {
+              if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
+              if (dbg_score) dbg_score[off + o] = hs.template get<J>()[i];
+            }
+            ++o;
+          }
+        off += kj;
+      }
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cover stage: the kept coarse regions from the coarse launch, the coverage
+// scores of this workgroup's 256 covered positions, then (last workgroup of
+// the head, when the refinement fits in registers) the refinement.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int RT, bool MEAN, bool BANDS>
+__device__ __forceinline__ void cover_stage(const StepArgs& a) {
+  constexpr int NT = kCoverThreads;
+  static_assert(NT == kSelThreads, "the refinement runs on the cover workgroup");
+  extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L], ascending
+  __shared__ __align__(16) unsigned char raw[sizeof(SelShared)];
+  __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
+  const int head = blockIdx.y;
+  int* sel_l = reinterpret_cast<int*>(lds);
+  stage_query<T, D, NT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+  {
+    const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+    for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t wave_base = (int64_t)blockIdx.x * 256 + w * 64;
+  if (wave_base < a.covered) {  // wave-uniform
+    Frag<T, D> qf[RT];
+    load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
+    if constexpr (BANDS) cover_from_bands<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
+    else cover_haar<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
+  }
+  if (a.refine_s0 != 16) return;  // uniform: refined in a launch of its own
+  SelShared& sh = *reinterpret_cast<SelShared*>(raw);
+  if (!arrive_last(a.counters + head, gridDim.x, &sh.last)) return;
+  refine_sel<16>(a, head, sel_l, sh);
 }
 
 // With one or two query tiles (and bfloat16 rows, or head dim 64) the Haar
-// cover kernel fits 128 registers without spilling: four workgroups per
-// compute unit, so large launches take fewer rounds; otherwise it keeps the
-// registers its loads in flight need.
+// cover kernel fits 128 registers: four workgroups per compute unit;
+// otherwise it keeps the registers its loads in flight need.
 template <typename T, int D>
 constexpr int cover_waves_per_simd(int rt) { return (sizeof(T) == 2 || D == 64) && rt <= 2 ? 4 : 1; }
 template <typename T, int D, int RT>
 __global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_max_kernel(StepArgs a) {
-  cover_scores<T, D, RT, false, false>(a);
+  cover_stage<T, D, RT, false, false>(a);
 }
 template <typename T, int D, int RT>
 __global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_mean_kernel(StepArgs a) {
-  cover_scores<T, D, RT, true, false>(a);
+  cover_stage<T, D, RT, true, false>(a);
 }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_bands_max_kernel(StepArgs a) { cover_scores<T, D, RT, false, true>(a); }
+__global__ __launch_bounds__(kCoverThreads) void cover_bands_max_kernel(StepArgs a) { cover_stage<T, D, RT, false, true>(a); }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_bands_mean_kernel(StepArgs a) { cover_scores<T, D, RT, true, true>(a); }
+__global__ __launch_bounds__(kCoverThreads) void cover_bands_mean_kernel(StepArgs a) { cover_stage<T, D, RT, true, true>(a); }
 
 // One refinement level with the candidates in registers (n <= ACT * MAXS):
 // candidate i is child (i & 1) of kept parent cur[i >> 1]; the kept ones go
@@ -738,17 +980,19 @@ __device__ __forceinline__ void refine_level(const float* cj, int nj, const int*
 }
 
 // ---------------------------------------------------------------------------
-// Recursive refinement (Figure 2 (d)) for one head, by one workgroup.
-// Positions at level j index the level-j blocks inside the covered set,
-// ascending; the block at position p has children 2p and 2p+1 and global
-// index sel_L[p >> (L-j)] 2^{L-j} + (p mod 2^{L-j}).  State lives in LDS:
+// Recursive refinement (Figure 2 (d)) for one head with sorted index lists,
+// for covered sets beyond the in-register refinement: one workgroup per
+// head, in a launch of its own after the cover launch.  Positions at level j
+// index the level-j blocks inside the covered set, ascending; the block at
+// position p has children 2p and 2p+1 and global index
+// sel_L[p >> (L-j)] 2^{L-j} + (p mod 2^{L-j}).  State lives in LDS:
 // keys[nmax] | cur[kmax] | nxt[kmax] | (coverage scores, when they fit).
-// Writes the kept tokens (ascending) to tsel[0 .. k0).  With `report`, also
-// writes sel_out and the per-level outputs of levels L-1 .. 0.
+// Writes the kept tokens (ascending) to tsel[0 .. k0), sel_out and the
+// per-level outputs of levels L-1 .. 0.
 // ---------------------------------------------------------------------------
 template <int NT>
 __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
-                                                  int* tsel, bool report) {
+                                                  int* tsel) {
   const int L = a.levels;
   uint32_t* keys = lds;
   int* cur = reinterpret_cast<int*>(lds + a.refine_nmax);
@@ -763,8 +1007,8 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
     const int n4 = (int)(a.cov_len / 4);
     for (int i = threadIdx.x; i < n4; i += NT) dst[i] = src[i];
   }
-  int32_t* dbg_sel = (report && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-  float* dbg_score = (report && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   for (int i = threadIdx.x; i < a.k_top; i += NT) cur[i] = i;
   __syncthreads();
   int kprev = a.k_top, dbg_off = a.k_top;
@@ -773,8 +1017,6 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
     const int n = 2 * kprev;
     const int nj = (int)(a.covered >> j);  // level-j positions in the covered set
     const float* cj = cov + a.cov_off[j];
-    // candidates in registers on one wave per SIMD where they fit (on all
-    // threads for large sets); beyond that the keys stay in LDS
     constexpr int A0 = TopKRaw<NT>::ACT0;
     if (n <= A0 * 4) {
       refine_level<NT, A0, 4>(cj, nj, cur, nxt, n, kj, tk_raw);
@@ -782,8 +1024,6 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
       refine_level<NT, A0, 8>(cj, nj, cur, nxt, n, kj, tk_raw);
     } else if (n <= A0 * 16) {
       refine_level<NT, A0, 16>(cj, nj, cur, nxt, n, kj, tk_raw);
-    } else if (NT >= 512 && n <= 512 * 16) {
-      refine_level<NT, (NT >= 512 ? 512 : A0), 16>(cj, nj, cur, nxt, n, kj, tk_raw);
     } else if (n <= A0 * 32) {
       refine_level<NT, A0, 32>(cj, nj, cur, nxt, n, kj, tk_raw);
     } else {
@@ -811,394 +1051,43 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
     kprev = kj;
     dbg_off += kj;
   }
-  int32_t* so = (report && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
   for (int o = threadIdx.x; o < a.k0; o += NT) {
     const int p = cur[o];
     const int tok = (clampi(sel_top[clampi(p >> L, 0, a.k_top - 1)], 0, a.n_top - 1) << L) + (p & ((1 << L) - 1));
     tsel[o] = tok;
     if (so) so[o] = tok;
   }
-  __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// Recursive refinement with bitmask kept sets (covered <= MACT * MMAX).
-//
-// Level-j position p (p < n_j = covered >> j) lives in slot s = p / ACT of
-// thread t = p mod ACT, so a wave's 64 positions of one slot form one 64-bit
-// word of a level mask and their parents (p >> 1) one 32-bit word of the
-// parent mask.  Every level's coverage scores are loaded into registers at
-// the start (coarsest level first), so the loads of all levels overlap the
-// work of the first ones.  One level (the k_j best candidates, candidates =
-// children of the kept parents):
-//   A. each valid candidate adds one count to a histogram of NB bins linear
-//      in the score over the level's [min, max] (published by the cover
-//      kernel);                                                   barrier B
-//   S. every wave finds by itself the bin b holding the k_j-th best, the
-//      count `need` still to take from it and its size `cnt` (two wave scans
-//      over the bins), so no broadcast round is needed;
-//   M. candidates in bins above b (and b itself when need == cnt) are written
-//      to the level mask with one ballot per slot; the candidates of bin b go
-//      to a short list as (order key, ~position);                barrier C
-//   R. each list entry counts the entries ranked above it (greater score, or
-//      equal score and lower position) and, within `need`, sets its bit;
-//      the histogram is cleared for the next level;              barrier D
-// Bins are monotone in the score, so bin order plus the exact in-bin rank is
-// the (score descending, position ascending) order.  When a level's score
-// range is degenerate, or its boundary bin holds more than LMAX candidates,
-// the head is refined again from the top by the list-based refinement.
-// ---------------------------------------------------------------------------
-
-template <int J> struct IntC { static constexpr int value = J; };
-template <int MMAX, int J> struct LevelSlots { static constexpr int N = (MMAX >> J) > 0 ? (MMAX >> J) : 1; };
-
-// Coverage scores of levels 0 .. kMaxLevels-1 in registers, compile-time indexed.
-template <int MMAX> struct LevelScores {
-  float s0[LevelSlots<MMAX, 0>::N], s1[LevelSlots<MMAX, 1>::N], s2[LevelSlots<MMAX, 2>::N];
-  float s3[LevelSlots<MMAX, 3>::N], s4[LevelSlots<MMAX, 4>::N], s5[LevelSlots<MMAX, 5>::N];
-  float s6[LevelSlots<MMAX, 6>::N];
-  template <int J> __device__ __forceinline__ auto& get() {
-    if constexpr (J == 0) return s0;
-    else if constexpr (J == 1) return s1;
-    else if constexpr (J == 2) return s2;
-    else if constexpr (J == 3) return s3;
-    else if constexpr (J == 4) return s4;
-    else if constexpr (J == 5) return s5;
-    else return s6;
-  }
-};
-static_assert(kMaxLevels == 7, "LevelScores holds seven levels");
-
-template <int J, class F>
-__device__ __forceinline__ void for_levels_desc(F&& f) {
-  f(IntC<J>{});
-  if constexpr (J > 0) for_levels_desc<J - 1>(f);
+#if !defined(WF_STEP_T)  // one compile unit holds these
+// The coarse Top-K for n_L > 1 024, one workgroup per head.
+__global__ __launch_bounds__(kSelThreads) void coarse_topk_kernel(StepArgs a) {
+  extern __shared__ __align__(16) uint32_t keys_l[];  // general path: the keys, when staged
+  __shared__ __align__(16) unsigned char raw[kSelRawBytes];
+  coarse_topk_head<true>(a, blockIdx.x, raw, keys_l);
 }
 
-// Number of set bits of the 64-bit mask m in lanes below this one.
-__device__ __forceinline__ int mask_rank(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-__device__ __forceinline__ uint64_t lds_mask64(const uint32_t* mask, int word64) {
-  const uint2 v = *reinterpret_cast<const uint2*>(mask + 2 * word64);
-  return ((uint64_t)v.y << 32) | v.x;
-}
-
-// Emits the set bits of a level mask over positions [0, nbits) in ascending
-// order: emit(o, p, set) is called for every position p < 64 ceil(nbits/64)
-// of threads t < ACT in the slot layout above, with set = bit p and o its
-// rank among the set bits when set (reads the caller makes in emit outside
-// a branch on `set` are issued together).  Each active wave scans the words' bit counts itself (one
-// wave scan per 64 words), so no barrier is needed; the caller synchronises
-// before the output is read.
-template <int ACT, int S, class Emit>
-__device__ __forceinline__ void emit_mask(const uint32_t* mask, int nbits, Emit emit) {
-  constexpr int W = ACT / 64;
-  constexpr int R = (S * W + 63) / 64;  // rounds of 64 words
-  static_assert(R <= 2, "at most 128 mask words");
-  if ((int)threadIdx.x >= ACT) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int nw = (nbits + 63) >> 6;
-  int excl[R];
-  int off = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int idx = 64 * r + lane;
-    const int c = idx < nw ? __popcll(lds_mask64(mask, idx)) : 0;
-    int tot;
-    const int incl = wave_incl_scan(c, &tot);
-    excl[r] = off + incl - c;
-    off += tot;
-  }
-  uint64_t m[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) m[s] = lds_mask64(mask, min(s * W + w, nw - 1));  // reads first, then the work
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int idx = s * W + w;  // wave-uniform
-    if (idx < nw) {
-      const int e = (R == 1 || idx < 64) ? excl[0] : excl[R - 1];
-      const int base = __builtin_amdgcn_readlane(e, idx & 63);
-      emit(base + mask_rank(m[s]), 64 * idx + lane, ((m[s] >> lane) & 1ull) != 0ull);
-    }
-  }
-}
-
-// One level of the fast refinement (steps A, S, M, R above).  Returns true
-// (uniformly, with every wave past its reads of the shared state) when the
-// level cannot be resolved this way.  All NT threads call it.  The code is
-// written for few vector instructions per slot: the slot bounds are scalar
-// (the wave index is uniform), the bins are computed once, the mask words of
-// a wave's slots are gathered into one lane each and stored together.
-template <int NT, int ACT, int S>
-__device__ __forceinline__ bool refine_level_fast(const float (&sj)[S], int nj, int kj, float smin, float smax,
-                                                  int par, const uint32_t* prev, uint32_t* next, RefineShared& sh) {
-  constexpr int NB = RefineShared::NB, BPL = NB / 64;
-  const int t = threadIdx.x, lane = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  if (t == 0) sh.list_n[par ^ 1] = 0;  // the next level's list (last read before the previous barrier)
-  const float span = smax - smin;
-  const float scale = __fdividef((float)NB, span);  // any positive scale keeps the bins monotone
-  if (!(span > 0.f && span < 3.0e38f && scale > 0.f && scale < 3.0e38f)) return true;  // uniform
-  const float boff = -smin * scale;  // bin = floor(score * scale + boff), monotone in the score
-  const bool act = w < ACT / 64;     // uniform
-  const int pbase = 64 * w + lane;
-
-  // A. validity (parent kept), bins (-1: not a candidate), histogram.  Every
-  // slot is processed without branches; positions past n_j are invalid.
-  int bn[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) bn[s] = -1;
-  if (act) {
-    const int pmax = (nj - 1) >> 6;
-    uint32_t pw[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) pw[s] = prev[min((s * ACT + 64 * w) >> 6, pmax)];
-    const int half = lane >> 1;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const bool v = (s * ACT + pbase < nj) & (__builtin_amdgcn_ubfe(pw[s], half, 1) != 0u);
-      const int bi = min(NB - 1, max(0, (int)fmaf(sj[s], scale, boff)));
-      bn[s] = v ? bi : -1;
-      if (v) atomicAdd(&sh.hist[bi], 1);
-    }
-  }
-  __syncthreads();  // B
-  // S. the boundary bin, by every wave
-  int b, need, cnt;
-  {
-    // lane l owns bins [BPL l, BPL l + BPL); its 16-byte reads are rotated
-    // by l so that the lanes of one read fall in different LDS banks
-    const int4* h4 = reinterpret_cast<const int4*>(sh.hist + BPL * lane);
-    int tot = 0;
-#pragma unroll
-    for (int q = 0; q < BPL / 4; ++q) {
-      const int4 v = h4[(q + lane) & (BPL / 4 - 1)];
-      tot += v.x + v.y + v.z + v.w;
-    }
-    int all;
-    const int incl = wave_incl_scan(tot, &all);
-    const int above = all - incl;  // candidates in the bins of higher lanes
-    const uint64_t om = __ballot((above < kj) & (kj <= above + tot));
-    const int owner = om ? (int)__ffsll((unsigned long long)om) - 1 : 0;  // wave-uniform
-    const int above_t = __builtin_amdgcn_readlane(above, owner);
-    const int c = (lane < BPL) ? sh.hist[BPL * owner + lane] : 0;
-    int all2;
-    const int incl2 = wave_incl_scan(c, &all2);
-    const int hi_cnt = above_t + (all2 - incl2);
-    const uint64_t hm = __ballot((lane < BPL) & (hi_cnt < kj) & (kj <= hi_cnt + c));
-    const int bl = hm ? (int)__ffsll((unsigned long long)hm) - 1 : 0;
-    b = BPL * owner + bl;
-    need = kj - __builtin_amdgcn_readlane(hi_cnt, bl);
-    cnt = __builtin_amdgcn_readlane(c, bl);
-  }
-  const bool whole = cnt == need;
-  if (!whole && cnt > RefineShared::LMAX) {  // uniform: too many in the boundary bin
-    __syncthreads();                          // every wave has read the bins
-    return true;
-  }
-  // M. the mask of the candidates above the boundary (lane s gathers slot s's
-  // word pair); the boundary bin's candidates to the list, one reservation
-  // per wave
-  if (act) {
-    uint32_t col_lo = 0u, col_hi = 0u;
-    int nbd = 0;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint64_t eq = __ballot(bn[s] == b);
-      const uint64_t km = __ballot(bn[s] > b) | (whole ? eq : 0ull);
-      col_lo = (lane == s) ? (uint32_t)km : col_lo;
-      col_hi = (lane == s) ? (uint32_t)(km >> 32) : col_hi;
-      nbd += __popcll(eq);
-    }
-    if (lane < S) *reinterpret_cast<uint2*>(next + ((lane * ACT + 64 * w) >> 5)) = make_uint2(col_lo, col_hi);
-    if (!whole && nbd > 0) {  // uniform
-      int base = 0;
-      if (lane == 0) base = atomicAdd(&sh.list_n[par], nbd);
-      base = __builtin_amdgcn_readfirstlane(base);
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const uint64_t eq = __ballot(bn[s] == b);
-        if (bn[s] == b)
-          sh.list[base + mask_rank(eq)] =
-              ((uint64_t)order_key(sj[s]) << 32) | (uint64_t)(~(uint32_t)(s * ACT + pbase));
-        base += __popcll(eq);
-      }
-    }
-  }
-  __syncthreads();  // C
-  // R. exact ranks inside the boundary bin: P lanes per entry (P <= 16, a
-  // power of two, one DPP row) each count a strided share of the list
-  if (!whole) {
-    const int nl = sh.list_n[par];
-    int lg = 0;
-    while (lg < 4 && (2 << lg) * nl <= NT) ++lg;  // uniform
-    const int P = 1 << lg;
-    const int part = t & (P - 1);
-    for (int i0 = 0; i0 < nl; i0 += NT >> lg) {  // uniform trip count (the DPP sums need whole waves)
-      const int i = i0 + (t >> lg);
-      const uint64_t me = (i < nl) ? sh.list[i] : ~0ull;
-      int rank = 0;
-      for (int e = part; e < nl; e += P) rank += (sh.list[e] > me) ? 1 : 0;
-      if (lg >= 1) rank += dpp_or0<0xB1>(rank);   // quad_perm [1,0,3,2]
-      if (lg >= 2) rank += dpp_or0<0x4E>(rank);   // quad_perm [2,3,0,1]
-      if (lg >= 3) rank += dpp_or0<0x141>(rank);  // row_half_mirror
-      if (lg >= 4) rank += dpp_or0<0x140>(rank);  // row_mirror
-      if (part == 0 && i < nl && rank < need) {
-        const uint32_t p = ~(uint32_t)me;
-        atomicOr(&next[p >> 5], 1u << (p & 31));
-      }
-    }
-  }
-  for (int i = t; i < NB / 4; i += NT) reinterpret_cast<int4*>(sh.hist)[i] = make_int4(0, 0, 0, 0);
-  __syncthreads();  // D
-  return false;
-}
-
-// LDS: sel_L | mask A | mask B; RefineShared in the Top-K scratch.
-template <int NT, int MMAX>
-__device__ __forceinline__ void refine_head_mask(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
-                                                 int* tsel, bool report) {
-  constexpr int ACT = TopKRaw<NT>::MACT;
-  static_assert(ACT * MMAX <= 128 * 64, "at most 128 coverage waves per head on this path");
-  const int L = a.levels;
-  const int covered = (int)a.covered;
-  const int t = threadIdx.x, lane = t & 63;
+// The in-register refinement with 32 level-0 positions per thread (covered
+// sets of 4 097 .. 8 192 positions), one workgroup per head.
+__global__ __launch_bounds__(kSelThreads) void refine_sel_kernel(StepArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L]
+  __shared__ __align__(16) SelShared sh;
+  const int head = blockIdx.x;
   int* sel_l = reinterpret_cast<int*>(lds);
-  uint32_t* mask_a = reinterpret_cast<uint32_t*>(sel_l + ((a.k_top + 3) & ~3));
-  uint32_t* mask_b = mask_a + a.refine_mask_words;
-  const float* cov_g = a.cov + (int64_t)head * a.cov_len;
-  const int32_t* sel_top = a.sel_top + (int64_t)head * a.k_top;
-  auto& sh = *reinterpret_cast<RefineShared*>(tk_raw);
-
-  // each level's score range: the coverage waves' slots (at most 128 per
-  // head here), all loaded before the scores so their wait is short.  The
-  // loads are unconditional, from clamped in-bounds slots, and the values
-  // are selected afterwards: a load under a condition becomes a branch that
-  // waits for it, and the loads would run as serial round trips.
-  const int nwav = (covered + 63) >> 6;
-  const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
-  uint2 rr[kMaxLevels][2];
-#pragma unroll
-  for (int j = 0; j < kMaxLevels; ++j)
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int v = lane + 64 * r;
-      const uint2 x = *reinterpret_cast<const uint2*>(lm + (int64_t)min(v, nwav - 1) * 2 * kMaxLevels + 2 * j);
-      // slots past nwav take the neutral range (least = ~0, greatest = 0), by
-      // an all-ones mask rather than a select (which the compiler turns into
-      // a branch around the load); levels past L are never used
-      const uint32_t off = (uint32_t)((nwav - 1 - v) >> 31);
-      rr[j][r] = make_uint2(x.x | off, x.y & ~off);
-    }
-  // every level's scores into registers, coarsest level first (unconditional
-  // loads of clamped positions, as above)
-  LevelScores<MMAX> sc;
-  for_levels_desc<kMaxLevels - 1>([&](auto jc) {
-    constexpr int J = decltype(jc)::value;
-    constexpr int SJ = LevelSlots<MMAX, J>::N;
-    auto& sj = sc.template get<J>();
-    // levels past L read level 0's slice (never used: the loop below stops at
-    // L); slots past n_j hold the last score (never used: a level's validity
-    // test excludes them)
-    const bool live = J < L;
-    const int nj = live ? covered >> J : covered;
-    const float* src = cov_g + a.cov_off[live ? J : 0];
-#pragma unroll
-    for (int s = 0; s < SJ; ++s) sj[s] = src[min(s * ACT + t, nj - 1)];
-  });
-  // the ranges, reduced by every wave; the budgets, read once
-  uint32_t rmn[kMaxLevels], rmx[kMaxLevels];
-  int kb[kMaxLevels];  // kb[j]: the budget of level j
-#pragma unroll
-  for (int j = 0; j < kMaxLevels; ++j) {
-    rmn[j] = wave_min_u32(min(rr[j][0].x, rr[j][1].x));
-    rmx[j] = wave_max_u32(max(rr[j][0].y, rr[j][1].y));
-    kb[j] = (j < L) ? a.budgets[L - j] : 0;
-  }
-  for (int i = t; i < a.k_top; i += NT) sel_l[i] = clampi(sel_top[i], 0, a.n_top - 1);
-  for (int i = t; i < a.refine_mask_words; i += NT)  // level L: every kept coarse region
-    mask_a[i] = (32 * i + 32 <= a.k_top) ? 0xFFFFFFFFu : (32 * i < a.k_top ? (1u << (a.k_top - 32 * i)) - 1u : 0u);
-  for (int i = t; i < RefineShared::NB / 4; i += NT) reinterpret_cast<int4*>(sh.hist)[i] = make_int4(0, 0, 0, 0);
-  if (t < 2) sh.list_n[t] = 0;
+  const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+  for (int i = threadIdx.x; i < a.k_top; i += kSelThreads) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   __syncthreads();
-
-  int32_t* dbg_sel = (report && a.sel_levels) ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-  float* dbg_score = (report && a.score_levels) ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
-  uint32_t* prev = mask_a;
-  uint32_t* next = mask_b;
-  int dbg_off = a.k_top;
-  bool general = false;
-  for (int j = L - 1; j >= 0; --j) {
-    const int nj = covered >> j;
-    uint32_t kmn = rmn[0], kmx = rmx[0];
-    int kj = kb[0];
-#pragma unroll
-    for (int i = 1; i < kMaxLevels; ++i)
-      if (i == j) {
-        kmn = rmn[i];
-        kmx = rmx[i];
-        kj = kb[i];
-      }
-    const float smin = key_to_f32(kmn), smax = key_to_f32(kmx);
-    for_levels_desc<kMaxLevels - 1>([&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      if (J == j)
-        general = refine_level_fast<NT, ACT, LevelSlots<MMAX, J>::N>(sc.template get<J>(), nj, kj, smin, smax, j & 1,
-                                                                      prev, next, sh);
-    });
-    if (general) break;
-    if (dbg_sel || dbg_score) {
-      const int sh_l = L - j;
-      const float* cj = cov_g + a.cov_off[j];
-      emit_mask<ACT, MMAX>(next, nj, [&](int o, int p, bool set) {
-        if (set && o < kj) {
-          if (dbg_sel) dbg_sel[dbg_off + o] = (sel_l[clampi(p >> sh_l, 0, a.k_top - 1)] << sh_l) + (p & ((1 << sh_l) - 1));
-          if (dbg_score) dbg_score[dbg_off + o] = cj[p];
-        }
-      });
-    }
-    uint32_t* tmp = prev;
-    prev = next;
-    next = tmp;
-    dbg_off += kj;
-  }
-  if (general) {  // uniform
-    __syncthreads();  // no wave still reads the masks the list path overwrites
-    refine_head_lists<NT>(a, head, lds, tk_raw, tsel, report);
-    return;
-  }
-  int32_t* so = (report && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
-  emit_mask<ACT, MMAX>(prev, covered, [&](int o, int p, bool set) {
-    const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & ((1 << L) - 1));
-    if (set && o < a.k0) {
-      tsel[o] = tok;
-      if (so) so[o] = tok;
-    }
-  });
+  refine_sel<32>(a, head, sel_l, sh);
 }
 
-// Recursive refinement (Figure 2 (d)) for one head: bitmask kept sets when
-// the covered set fits the register Top-K (with level-0 slots per thread
-// fitted to it: 4, 8, 16 or 32), else sorted index lists in LDS.
-template <int NT>
-__device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_t* lds, unsigned char* tk_raw,
-                                            int* tsel, bool report) {
-  constexpr int64_t ACT = TopKRaw<NT>::MACT, MMAX = TopKRaw<NT>::MMAX;
-  const int64_t cv = a.covered;
-  if (a.levels == 0 || cv > ACT * MMAX)
-    refine_head_lists<NT>(a, head, lds, tk_raw, tsel, report);
-  else if (cv <= ACT * 4)
-    refine_head_mask<NT, 4>(a, head, lds, tk_raw, tsel, report);
-  else if (cv <= ACT * 8)
-    refine_head_mask<NT, 8>(a, head, lds, tk_raw, tsel, report);
-  else if (MMAX == 16 || cv <= ACT * 16)
-    refine_head_mask<NT, 16>(a, head, lds, tk_raw, tsel, report);
-  else
-    refine_head_mask<NT, (MMAX > 16 ? MMAX : 16)>(a, head, lds, tk_raw, tsel, report);
+__global__ __launch_bounds__(kSelThreads) void refine_lists_kernel(StepArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<kSelThreads>::BYTES];
+  const int head = blockIdx.x;
+  refine_head_lists<kSelThreads>(a, head, lds, tk_raw, a.sel_ws + (int64_t)head * a.k0);
 }
+#endif
 
 // ---------------------------------------------------------------------------
 // Sparse attention (eq. 3 over T = kept prompt tokens, then gen_idx).
@@ -1214,7 +1103,8 @@ __device__ __forceinline__ void refine_head(const StepArgs& a, int head, uint32_
 // online softmax per query row in float32; O^T += V^T P^T on MFMA with P
 // split into bf16 hi + lo (float32 MFMA for float32 inputs).  The next
 // chunk's rows are fetched into registers while the current one computes.
-// Writes the split's partial (m, l, O) to the workspace.
+// Writes the split's partial (m, l, O) with agent-scope stores; the head's
+// last split workgroup merges them.
 // ---------------------------------------------------------------------------
 // x of lane l ^ NV: a DPP row rotation by 8 for NV = 8, a lane permute for 16.
 template <int NV>
@@ -1465,102 +1355,87 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
     }
     __syncthreads();
   }
-  if (tg != 0) return;
-  float* pml = a.part_ml + ((int64_t)head * a.n_split + split) * 2 * a.n_q;
-  float* po = a.part_o + ((int64_t)head * a.n_split + split) * a.n_q * D;
-  if (qvalid) {
-    if (g == 0) {
-      pml[query] = st.m;
-      pml[a.n_q + query] = st.l;
-    }
+  if (tg == 0 && qvalid) {
+    float* pml = a.part_ml + (((int64_t)head * a.n_split + split) * a.n_q + query) * 2;
+    float* po = a.part_o + ((int64_t)head * a.n_split + split) * a.n_q * D + (int64_t)query * D;
+    if (g == 0) store_agent2(pml, st.m, st.l);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<float4*>(po + (int64_t)query * D + 16 * dt + 4 * g) =
-          make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+    for (int dt = 0; dt < D / 16; ++dt) {
+      store_agent2(po + 16 * dt + 4 * g, st.o[dt][0], st.o[dt][1]);
+      store_agent2(po + 16 * dt + 4 * g + 2, st.o[dt][2], st.o[dt][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of a head's split partials, by its last attention workgroup:
+// O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s, M = max_s m_s (m in
+// log2 units; an empty split has m = -inf, l = 0).  Thread = one float4 of
+// the output at a time; every split's loads are issued before any is used.
+// The splits are folded in index order, so the result does not depend on
+// which workgroup merges.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__device__ __forceinline__ void merge_splits(const StepArgs& a, int head) {
+  constexpr int C4 = D / 4;
+  const int ns = a.n_split, nq = a.n_q;
+  const float* ml = a.part_ml + (int64_t)head * ns * nq * 2;
+  const float* po = a.part_o + (int64_t)head * ns * nq * D;
+  float* out = a.out + (int64_t)head * nq * D;
+  for (int e = threadIdx.x; e < nq * C4; e += NT) {
+    const int query = e / C4, c4 = e - query * C4;
+    float mv[kMaxSplit], lv[kMaxSplit];
+    float4 ov[kMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      mv[sp] = -INFINITY;
+      lv[sp] = 0.f;
+      ov[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sp < ns) {  // uniform
+        const float2 m2 = load_agent2(ml + ((int64_t)sp * nq + query) * 2);
+        const float* p = po + ((int64_t)sp * nq + query) * D + 4 * c4;
+        const float2 x = load_agent2(p), y = load_agent2(p + 2);
+        mv[sp] = m2.x;
+        lv[sp] = m2.y;
+        ov[sp] = make_float4(x.x, x.y, y.x, y.y);
+      }
+    }
+    float mm = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
+    float den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      const float wv = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - mm);
+      den += wv * lv[sp];
+      acc.x += wv * ov[sp].x;
+      acc.y += wv * ov[sp].y;
+      acc.z += wv * ov[sp].z;
+      acc.w += wv * ov[sp].w;
+    }
+    const float inv = 1.0f / den;
+    *reinterpret_cast<float4*>(out + (int64_t)query * D + 4 * c4) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
 template <typename T, int D, int NQT>
 __global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
-}
-
-// ---------------------------------------------------------------------------
-// Refinement, one workgroup per head (workgroups 0 .. heads_total - 1): the
-// kept prompt tokens of the head, ascending, to the workspace (the attention
-// reads them from there), and to sel_out and the per-level outputs when those
-// are requested.  The workgroups after them take the attention splits of the
-// generated positions, which do not depend on the selection, so they run
-// while the refinement does.
-// ---------------------------------------------------------------------------
-template <typename T, int D, int NQT>
-__global__ __launch_bounds__(64 * NQT * kAttendGroups) void refine_kernel(StepArgs a) {
-  constexpr int NT = 64 * NQT * kAttendGroups;
-  extern __shared__ __align__(16) uint32_t lds[];
-  static_assert(TopKRaw<NT>::BYTES <= (size_t)kTopKSharedReserve, "static LDS beyond its reserve");
-  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<NT>::BYTES];
-  if ((int)blockIdx.x < a.heads_total) {
-    const int head = blockIdx.x;
-    refine_head<NT>(a, head, lds, tk_raw, a.sel_ws + (int64_t)head * a.k0, true);
-  } else {
-    const int gsplits = a.n_split - a.n_split_p;
-    const int idx = blockIdx.x - a.heads_total;
-    attend_split<T, D, NQT>(a, lds, idx / gsplits, a.n_split_p + idx % gsplits);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Merge of the split partials: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s,
-// M = max_s m_s (m in log2 units; an empty split has m = -inf, l = 0).
-// Thread = one float4 of the output (head, query, 4 columns), so the whole
-// merge is one round of independent loads spread over the chip.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
-  constexpr int C4 = D / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_head = (int64_t)a.n_q * C4;
-  if (idx >= per_head * a.heads_total) return;
-  const int head = (int)(idx / per_head);
-  const int rem = (int)(idx - head * per_head);
-  const int query = rem / C4, c4 = rem - query * C4;
-  const int ns = a.n_split;
-  const float* ml = a.part_ml + (int64_t)head * ns * 2 * a.n_q;
-  const float* po = a.part_o + ((int64_t)head * ns * a.n_q + query) * D + 4 * c4;
-  float mv[kMaxSplit], lv[kMaxSplit];
-  float4 ov[kMaxSplit];
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp) {  // every load issued before any is used
-    const bool in = sp < ns;
-    mv[sp] = in ? ml[sp * 2 * a.n_q + query] : -INFINITY;
-    lv[sp] = in ? ml[sp * 2 * a.n_q + a.n_q + query] : 0.f;
-    ov[sp] = in ? *reinterpret_cast<const float4*>(po + (int64_t)sp * a.n_q * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float mm = -INFINITY;
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
-  float den = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int sp = 0; sp < kMaxSplit; ++sp) {
-    const float wv = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - mm);
-    den += wv * lv[sp];
-    acc.x += wv * ov[sp].x;
-    acc.y += wv * ov[sp].y;
-    acc.z += wv * ov[sp].z;
-    acc.w += wv * ov[sp].w;
-  }
-  const float inv = 1.0f / den;
-  *reinterpret_cast<float4*>(a.out + ((int64_t)head * a.n_q + query) * D + 4 * c4) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  __shared__ int last;
+  const int head = blockIdx.y;
+  attend_split<T, D, NQT>(a, lds, head, blockIdx.x);
+  if (!arrive_last(a.counters + head, a.n_split, &last)) return;
+  merge_splits<D, 64 * NQT * kAttendGroups>(a, head);
 }
 
 // ---------------------------------------------------------------------------
 // Launches.  This file is compiled once per (input type, head dimension,
 // query tiles) with WF_STEP_T, WF_STEP_D and WF_STEP_RT set, each unit
 // instantiating that combination's kernels (so the units build in
-// parallel), and once without them for the dispatcher and the merge kernel.
+// parallel), and once without them for the dispatcher and the list-based
+// refinement.
 // ---------------------------------------------------------------------------
 template <class K>
 static hipError_t allow_lds(K kernel, int bytes) {
@@ -1577,106 +1452,90 @@ static hipError_t launch_one(K kernel, dim3 grid, dim3 block, int lds, hipStream
   return hipGetLastError();
 }
 
-// The coarse scores, for one (T, D, RT).
+// The coarse and cover stages, for one (T, D, RT).
 template <typename T, int D, int RT>
-hipError_t launch_coarse(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
-  const SelectPlan& P = L.plan;
-  const dim3 coarse_grid((P.n_top + 63) / 64, P.heads_total);
-  return L.agg_mean ? launch_one(coarse_mean_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a)
-                    : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
-}
-
-// Every stage after the coarse scores (and the coarse Top-K, when it runs
-// apart) and before the merge, for one (T, D, RT).
-template <typename T, int D, int RT>
-hipError_t launch_stages(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+hipError_t launch_select(const StepArgs& a, const SelectLaunch& L, int stage, hipStream_t s) {
   const SelectPlan& P = L.plan;
   const int H = P.heads_total;
-  const dim3 att_block(64 * RT * kAttendGroups);
-  hipError_t e;
-  if (!L.attend_only) {  // selection stages (skipped when the caller hands in a selection)
-    const dim3 cover_grid(P.levels > 0 ? (unsigned)((P.covered + 255) / 256) : 1u, H);
-    if (P.stored_bands)
-      e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
-                     : launch_one(cover_bands_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
-    else
-      e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
-                     : launch_one(cover_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
-    if (e != hipSuccess) return e;
-    // one refinement workgroup per head, then the generated positions' attention splits
-    const int lds_r = P.refine_lds > P.attend_lds ? P.refine_lds : P.attend_lds;
-    const unsigned refine_blocks = (unsigned)(H + H * (P.n_split - P.n_split_p));
-    if ((e = launch_one(refine_kernel<T, D, RT>, dim3(refine_blocks), att_block, lds_r, s, a)) != hipSuccess)
-      return e;
+  if (stage == 0) {
+    const dim3 coarse_grid(P.coarse_wg, H);
+    return L.agg_mean ? launch_one(coarse_mean_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a)
+                      : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
   }
-  // the prompt splits (and, for a handed-in selection, the generated ones too)
-  const unsigned att_splits = (unsigned)(L.attend_only ? P.n_split : P.n_split_p);
-  if (att_splits > 0)
-    return launch_one(attend_kernel<T, D, RT>, dim3(att_splits, H), att_block, P.attend_lds, s, a);
-  return hipSuccess;
+  hipError_t e;
+  const dim3 cover_grid(P.cover_wg, H);
+  if (P.stored_bands)
+    e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
+                   : launch_one(cover_bands_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+  else
+    e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
+                   : launch_one(cover_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+  return e;
+}
+
+// The attention stage, for one (T, D, RT).
+template <typename T, int D, int RT>
+hipError_t launch_attend(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  const SelectPlan& P = L.plan;
+  return launch_one(attend_kernel<T, D, RT>, dim3(P.n_split, P.heads_total), dim3(64 * RT * kAttendGroups),
+                    P.attend_lds, s, a);
 }
 
 #if defined(WF_STEP_T)
-template hipError_t launch_coarse<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&,
+template hipError_t launch_select<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&, int,
                                                                     hipStream_t);
-template hipError_t launch_stages<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&,
-                                                                    hipStream_t);
+template hipError_t launch_attend<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
 #else
-#define WF_EXTERN_RT(F, T, D, RT) \
-  extern template hipError_t F<T, D, RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
+#define WF_EXTERN_SEL(T, D, RT) \
+  extern template hipError_t launch_select<T, D, RT>(const StepArgs&, const SelectLaunch&, int, hipStream_t);
+#define WF_EXTERN_ATT(T, D, RT) \
+  extern template hipError_t launch_attend<T, D, RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
 #define WF_EXTERN_STAGES(T, D)                                                              \
-  WF_EXTERN_RT(launch_coarse, T, D, 1) WF_EXTERN_RT(launch_coarse, T, D, 2)                 \
-  WF_EXTERN_RT(launch_coarse, T, D, 3) WF_EXTERN_RT(launch_coarse, T, D, 4)                 \
-  WF_EXTERN_RT(launch_stages, T, D, 1) WF_EXTERN_RT(launch_stages, T, D, 2)                 \
-  WF_EXTERN_RT(launch_stages, T, D, 3) WF_EXTERN_RT(launch_stages, T, D, 4)
+  WF_EXTERN_SEL(T, D, 1) WF_EXTERN_SEL(T, D, 2) WF_EXTERN_SEL(T, D, 3) WF_EXTERN_SEL(T, D, 4) \
+  WF_EXTERN_ATT(T, D, 1) WF_EXTERN_ATT(T, D, 2) WF_EXTERN_ATT(T, D, 3) WF_EXTERN_ATT(T, D, 4)
 WF_EXTERN_STAGES(bf16_t, 128)
 WF_EXTERN_STAGES(bf16_t, 64)
 WF_EXTERN_STAGES(float, 128)
 WF_EXTERN_STAGES(float, 64)
 #undef WF_EXTERN_STAGES
-#undef WF_EXTERN_RT
+#undef WF_EXTERN_SEL
+#undef WF_EXTERN_ATT
 
-// The coarse Top-K as a launch of its own, one workgroup per head: used when
-// the cover launch takes several rounds of workgroups, each of which would
-// otherwise repeat it.
-__global__ __launch_bounds__(kCoverThreads) void coarse_topk_kernel(StepArgs a) {
-  extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ __align__(16) unsigned char tk_raw[TopKRaw<kCoverThreads>::BYTES];
-  const int head = blockIdx.x;
-  const uint32_t* keys_g = a.keys_top + (int64_t)head * a.n_top;
-  int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
-  coarse_topk_head<kCoverThreads>(a, head, lds, tk_raw, [&](int o, int i) {
-    if (o < a.k_top) {
-      sel_g[o] = i;
-      if (dbg_sel) dbg_sel[o] = i;
-      if (dbg_score) dbg_score[o] = key_to_f32(keys_g[i]);
+template <typename T, int D>
+static hipError_t launch_rt_select(int rt, int stage, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  {
+    switch (rt) {
+      case 1: e = launch_select<T, D, 1>(a, L, stage, s); break;
+      case 2: e = launch_select<T, D, 2>(a, L, stage, s); break;
+      case 3: e = launch_select<T, D, 3>(a, L, stage, s); break;
+      default: e = launch_select<T, D, 4>(a, L, stage, s); break;
     }
-  });
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The selection launches after the coarse one that some shapes need.
+static hipError_t launch_apart(const StepArgs& a, const SelectLaunch& L, int stage, hipStream_t s) {
+  const SelectPlan& P = L.plan;
+  const dim3 grid(P.heads_total), block(kSelThreads);
+  if (stage == 0) {  // between the coarse and the cover launches
+    if (P.topk_s >= 1 && P.topk_s <= 4) return hipSuccess;
+    return launch_one(coarse_topk_kernel, grid, block, P.coarse_lds, s, a);
+  }
+  if (P.levels == 0 || P.refine_s0 == 16) return hipSuccess;  // between the cover and the attention launches
+  if (P.refine_s0 == 32) return launch_one(refine_sel_kernel, grid, block, P.cover_lds, s, a);
+  return launch_one(refine_lists_kernel, grid, block, P.refine_lds, s, a);
 }
 
 template <typename T, int D>
-static hipError_t launch_stages_rt(int rt, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
-  if (!L.attend_only) {
-    hipError_t e;
-    switch (rt) {
-      case 1: e = launch_coarse<T, D, 1>(a, L, s); break;
-      case 2: e = launch_coarse<T, D, 2>(a, L, s); break;
-      case 3: e = launch_coarse<T, D, 3>(a, L, s); break;
-      default: e = launch_coarse<T, D, 4>(a, L, s); break;
-    }
-    if (e != hipSuccess) return e;
-    if (L.plan.topk_apart &&
-        (e = launch_one(coarse_topk_kernel, dim3(L.plan.heads_total), dim3(kCoverThreads), L.plan.topk_lds, s, a)) !=
-            hipSuccess)
-      return e;
-  }
+static hipError_t launch_rt_attend(int rt, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
   switch (rt) {
-    case 1: return launch_stages<T, D, 1>(a, L, s);
-    case 2: return launch_stages<T, D, 2>(a, L, s);
-    case 3: return launch_stages<T, D, 3>(a, L, s);
-    default: return launch_stages<T, D, 4>(a, L, s);
+    case 1: return launch_attend<T, D, 1>(a, L, s);
+    case 2: return launch_attend<T, D, 2>(a, L, s);
+    case 3: return launch_attend<T, D, 3>(a, L, s);
+    default: return launch_attend<T, D, 4>(a, L, s);
   }
 }
 
@@ -1694,6 +1553,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.sel_out = L.sel_out;
   a.sel_levels = L.sel_levels;
   a.score_levels = L.score_levels;
+  a.counters = reinterpret_cast<uint32_t*>(L.ws + P.off_counters);
   a.keys_top = reinterpret_cast<uint32_t*>(L.ws + P.off_keys);
   a.sel_top = reinterpret_cast<int32_t*>(L.ws + P.off_sel_top);
   a.cov = reinterpret_cast<float*>(L.ws + P.off_cov);
@@ -1719,16 +1579,16 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.n_split_p = P.n_split_p;
   a.cps_p = P.cps_p;
   a.cps_g = P.cps_g;
+  a.att_t_words = P.att_t_words;
+  a.topk_s = P.topk_s;
   a.coarse_keys_in_lds = P.coarse_keys_in_lds;
+  a.refine_s0 = P.refine_s0;
   a.refine_cov_in_lds = P.refine_cov_in_lds;
   a.refine_nmax = P.refine_nmax;
   a.refine_kmax = P.refine_kmax;
-  a.refine_mask_words = P.refine_mask_words;
-  a.att_t_words = P.att_t_words;
   a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
   a.inv_nq = 1.0f / (float)P.n_q;
   a.stored_bands = P.stored_bands;
-  a.topk_apart = P.topk_apart;
   for (int j = 0; j < kMaxLevels; ++j)
     a.band_a[j] = P.stored_bands && j > 0 && j < P.levels
                       ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top) + P.band_off[j])
@@ -1737,13 +1597,18 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   const int rt = (P.n_q + 15) / 16;
   const bool bf = P.dtype == WF_BF16;
   const bool d128 = P.head_dim == 128;
-  hipError_t e = bf ? (d128 ? launch_stages_rt<bf16_t, 128>(rt, a, L, s) : launch_stages_rt<bf16_t, 64>(rt, a, L, s))
-                    : (d128 ? launch_stages_rt<float, 128>(rt, a, L, s) : launch_stages_rt<float, 64>(rt, a, L, s));
-  if (e != hipSuccess) return e;
-  const unsigned comb_blocks = (unsigned)(((int64_t)P.heads_total * P.n_q * (P.head_dim / 4) + 255) / 256);
-  if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  hipError_t e;
+  if (!L.attend_only) {
+    for (int stage = 0; stage < 2; ++stage) {
+      if (stage == 1 && P.levels == 0) break;
+      e = bf ? (d128 ? launch_rt_select<bf16_t, 128>(rt, stage, a, L, s) : launch_rt_select<bf16_t, 64>(rt, stage, a, L, s))
+             : (d128 ? launch_rt_select<float, 128>(rt, stage, a, L, s) : launch_rt_select<float, 64>(rt, stage, a, L, s));
+      if (e != hipSuccess) return e;
+      if ((e = launch_apart(a, L, stage, s)) != hipSuccess) return e;
+    }
+  }
+  return bf ? (d128 ? launch_rt_attend<bf16_t, 128>(rt, a, L, s) : launch_rt_attend<bf16_t, 64>(rt, a, L, s))
+            : (d128 ? launch_rt_attend<float, 128>(rt, a, L, s) : launch_rt_attend<float, 64>(rt, a, L, s));
 }
 #endif
 
