@@ -115,13 +115,14 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->coarse_keys_in_lds = P->topk_s == 0 && P->n_top <= wf::kMaxCoarseLds;
   P->coarse_lds = P->coarse_keys_in_lds ? 4 * P->n_top : 0;
   // cover launch: 256 covered positions per workgroup, the kept coarse
-  // regions in LDS.  The refinement holds 16 level-0 positions per thread in
-  // the head's last cover workgroup (covered sets up to 4 096), 32 in a
-  // launch of its own (up to 8 192), else runs list-based in a launch of its
-  // own
+  // regions in LDS.  The refinement runs in a launch of its own, one
+  // workgroup of 1 024 threads per head holding 1 .. 8 level-0 positions
+  // each (covered sets up to 8 192), else list-based
   P->cover_wg = L > 0 ? (int)((P->covered + wf::kCoverThreads - 1) / wf::kCoverThreads) : 0;
   P->cover_lds = 4 * ((P->k_top + 3) & ~3);
-  P->refine_s0 = L == 0 ? 0 : P->covered <= 16 * wf::kCoverThreads ? 16 : P->covered <= wf::kRegSelMax ? 32 : 0;
+  P->refine_s0 = (L > 0 && P->covered <= 8 * wf::kRefineThreadsHost)
+                     ? pow2_at_least((int)((P->covered + wf::kRefineThreadsHost - 1) / wf::kRefineThreadsHost))
+                     : 0;
   // a longer basis: its finer approximation bands are read from the pyramid
   P->stored_bands = (pyr->flags & WF_PYR_DB2) != 0;
   if (P->stored_bands) {
@@ -151,7 +152,6 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
-  P->off_counters = w; w += align_up(wf::kCounterBytes);
   P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
@@ -187,7 +187,6 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
   P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = 0;
-  P->off_counters = w; w += align_up(wf::kCounterBytes);
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * head_dim * 4);
   P->total = w;

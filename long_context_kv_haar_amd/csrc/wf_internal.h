@@ -18,11 +18,8 @@ constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
 constexpr int kTopKSharedReserve = 20 * 1024;  // static LDS of the selection scratch and friends
 constexpr int kCoverThreads = 256;
-constexpr int kRegSelMax = 256 * 32;      // positions one workgroup's in-register selection holds
-// Arrival counters, one per (sequence, head), at the start of every
-// workspace: a fixed place, so calls of different shapes that share a
-// workspace never find data where another call expects its zero counters.
-constexpr uint64_t kCounterBytes = 4ull * (WF_MAX_HEADS + 1);
+constexpr int kRegSelMax = 256 * 32;      // coarse regions the in-register coarse Top-K holds
+constexpr int kRefineThreadsHost = 1024;  // threads of the refinement workgroup
 
 // Byte layout of the per-call workspace, and the resolved launch shape.
 struct SelectPlan {
@@ -52,7 +49,7 @@ struct SelectPlan {
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + K/V chunk buffers
   // workspace sections (byte offsets)
-  uint64_t off_counters, off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, total;
+  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, total;
 };
 
 struct SelectLaunch {

@@ -1,11 +1,10 @@
 // Workgroup-level selection machinery of the coarse Top-K and the recursive
-// refinement (WaveFilter, Figure 2 (c)-(d)), and the hand-over of data
-// between the workgroups of one launch.
+// refinement (WaveFilter, Figure 2 (c)-(d)).
 //
 // Selection rule everywhere: keep the k best candidates, higher score first
 // and on equal scores the lower position; kept sets are reported ascending.
 //
-// Layout.  A workgroup of kSelThreads threads holds one level's positions
+// Layout.  A workgroup of NT threads holds one level's positions
 // in contiguous runs: thread t holds the S positions [t S, t S + S) (S a
 // power of two).  The refinement descends a binary tree, so with S0
 // level-0 positions per thread, thread t holds level-j positions
@@ -18,23 +17,27 @@
 // shared state only).
 //
 // One level (select_level), all threads:
-//   A. every valid owned candidate adds one to a histogram of kSelBins bins
+//   1. every valid owned candidate adds one to a histogram of kSelBins bins
 //      linear in the score over [smin, smax] (monotone in the score, so a
-//      higher bin holds only greater scores);                   barrier B
-//   S. every wave finds by itself the bin b of the k-th best, the count
-//      still needed from it and its size (a wave scan over the bins);
-//   W. if bin b is kept whole, the decision is bin >= b: no more barriers;
-//   L. else the owned candidates of bin b are listed as (order key, ~pos)
-//      pairs;                                                    barrier C
-//      every holder ranks its bin-b candidates against the list (greater
-//      key, or equal key and lower position, ranks higher) and keeps those
-//      ranked below the count needed;
-//   D. a bin with more candidates than the list holds (heavy ties) is
+//      higher bin holds only greater scores);                   barrier
+//      every wave finds by itself the bin b of the k-th best, the count
+//      still needed from it and its size (one wave scan over the bins);
+//      if bin b is kept whole, the decision is bin >= b;
+//   2. else the owned candidates of bin b add one to a histogram of kSelBins
+//      sub-bins linear in the score over bin b's range;        barrier
+//      every wave finds the sub-bin b2 of the still-needed best; with a few
+//      dozen candidates in bin b it is almost always kept whole;
+//   3. else the owned candidates of that cell are listed as (order key,
+//      ~pos) pairs (greater pair = higher score, or equal score and lower
+//      position);                                                barrier
+//      the pair ranked at the count still needed is the threshold: a holder
+//      keeps its cell candidates whose pair is at or above it;
+//   4. a cell with more candidates than the list holds (heavy ties) is
 //      narrowed by histogram passes over the key bits, and ties on one key
 //      value go to the lowest positions (a workgroup scan in position order).
-// Histograms are triple-buffered and lists double-buffered, each cleared
-// one level after its last read, so a level costs barrier B, plus C when
-// its boundary bin is not kept whole.
+// Pass-1 histograms are triple-buffered, pass-2 histograms and lists
+// double-buffered, each cleared one level after its last read, so a level
+// costs one barrier, two when bin b is not kept whole.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,70 +47,25 @@
 
 namespace wf {
 
-constexpr int kSelThreads = 256;                // threads of a selecting workgroup
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelBins = 512;                   // linear histogram bins: 8 per lane of a wave
+constexpr int kSelThreads = 256;                // threads of a cover workgroup (coarse Top-K)
+constexpr int kRefineThreads = 1024;            // threads of a refinement workgroup
+constexpr int kSelBins = 256;                   // linear histogram bins: 4 per lane of a wave
 constexpr int kSelList = 256;                   // boundary-bin list capacity
-constexpr int kSelMaxSlots = 32;                // positions per thread held in registers
 
 // ---------------------------------------------------------------------------
-// Hand-over between the workgroups of one launch.  The L2 of an XCD is not
-// coherent with the other XCDs' L2, so data that another workgroup of the
-// same launch reads is written with agent-scope stores (written through to
-// memory) and read with agent-scope loads (never served from a stale line of
-// the reader's L2).  A workgroup counts its arrival only after its own
-// stores have completed; the last one to arrive sees every other's data.
+// Selection state in LDS, for a workgroup of NT threads.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_agent2(float* p, float x, float y) {  // p 8-byte aligned
-  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p)),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 load_agent2(const float* p) {  // p 8-byte aligned
-  const uint64_t v = __hip_atomic_load(const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p)), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
-// Arrival of this workgroup at a counter shared by the n workgroups of one
-// item; true, uniformly, in the last one to arrive.  The counter wraps back
-// to zero on the last arrival (the atomic increment with bound n - 1), so it
-// is ready for the next launch.  Every thread must call it; each wave's
-// agent-scope stores complete before the barrier.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n, int* flag_lds) {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are visible at agent scope
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *flag_lds = __builtin_amdgcn_atomic_inc32(counter, n - 1u, __ATOMIC_RELAXED, "agent") == n - 1u;
-  __syncthreads();
-  return *flag_lds != 0;
-}
-
-// ---------------------------------------------------------------------------
-// Selection state in LDS.
-// ---------------------------------------------------------------------------
-struct SelShared {
-  int hist[3][kSelBins];          // triple-buffered histograms (zero between uses)
+template <int NT> struct SelShared {
+  static constexpr int NW = NT / 64;
+  int hist[3][kSelBins + 64];     // triple-buffered pass-1 histograms (zero between uses), then a trash bin per lane
+  int hist2[2][kSelBins + 64];    // double-buffered pass-2 histograms
   uint64_t list[2][kSelList];     // boundary lists by level parity
   int list_n[2];
-  int last;                       // arrive_last flag
-  int pad;
-  uint32_t wmn[kSelWaves], wmx[kSelWaves];
-  int wsum[8][kSelWaves];         // per-wave totals of the workgroup scans
+  uint32_t wmn[NW], wmx[NW];
+  int wsum[8][NW];                // per-wave totals of the workgroup scans
+  uint32_t rmn[8], rmx[8];        // the refinement: each level's score range (order keys)
+  int bc[4];                      // a level's boundary bin, broadcast by wave 0
+  uint64_t tau;                   // a level's threshold pair, broadcast by wave 0
 };
 
 struct SelCursor {
@@ -115,8 +73,10 @@ struct SelCursor {
 };
 
 // Zero the selection state; the caller synchronises before the first level.
-__device__ __forceinline__ void sel_init(SelShared& sh) {
-  for (int i = threadIdx.x; i < 3 * kSelBins; i += kSelThreads) (&sh.hist[0][0])[i] = 0;
+template <int NT>
+__device__ __forceinline__ void sel_init(SelShared<NT>& sh) {
+  for (int i = threadIdx.x; i < 3 * (kSelBins + 64); i += NT) (&sh.hist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 2 * (kSelBins + 64); i += NT) (&sh.hist2[0][0])[i] = 0;
   if (threadIdx.x < 2) sh.list_n[threadIdx.x] = 0;
 }
 
@@ -135,6 +95,16 @@ struct LinBins {
   __device__ __forceinline__ int operator()(float s) const {
     return ok ? min(kSelBins - 1, max(0, (int)fmaf(s, scale, off))) : 0;
   }
+  // kSelBins sub-bins over bin b's range: another monotone map of the score
+  // (it orders only the candidates of bin b, so it need not match the bin
+  // edges exactly)
+  __device__ __forceinline__ LinBins sub(int b) const {
+    LinBins r = *this;
+    r.scale = scale * (float)kSelBins;
+    r.off = (off - (float)b) * (float)kSelBins;
+    r.ok = ok && r.scale < 3.0e38f;
+    return r;
+  }
 };
 
 // Ranking key of a candidate: greater is better (higher score, then lower position).
@@ -146,38 +116,31 @@ __device__ __forceinline__ uint64_t rank_key(uint32_t okey, int pos) {
 // a kSelBins-bin histogram: its index, the count still needed from it and
 // its size.  Each wave computes it on its own; want <= total is required.
 __device__ __forceinline__ void find_bin(const int* hist, int want, int& b, int& need, int& cnt) {
+  static_assert(kSelBins == 256, "four bins per lane");
   const int lane = threadIdx.x & 63;
-  const int4* h4 = reinterpret_cast<const int4*>(hist + 8 * lane);
-  const int r = lane & 1;  // read order alternates between lanes (spreads the LDS banks)
-  const int4 x = h4[r], y = h4[r ^ 1];
-  const int4 lo = r ? y : x, hi = r ? x : y;
-  const int c[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  int tot = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) tot += c[i];
+  const int4 x = reinterpret_cast<const int4*>(hist)[lane];
+  const int c[4] = {x.x, x.y, x.z, x.w};
+  const int tot = c[0] + c[1] + c[2] + c[3];
   int all;
   const int incl = wave_incl_scan(tot, &all);
   const int above = all - incl;  // entries in the bins of higher lanes
   const uint64_t om = __ballot((above < want) & (want <= above + tot));
   const int owner = om ? (int)__ffsll((unsigned long long)om) - 1 : 0;
-  int ab = above, bb = 0, nd = 0, ct = 0;
-#pragma unroll
-  for (int i = 7; i >= 0; --i) {
-    const bool hit = (ab < want) & (want <= ab + c[i]);
-    bb = hit ? i : bb;
-    nd = hit ? want - ab : nd;
-    ct = hit ? c[i] : ct;
-    ab += c[i];
-  }
-  b = 8 * owner + __builtin_amdgcn_readlane(bb, owner);
-  need = __builtin_amdgcn_readlane(nd, owner);
+  // the owner's bins, highest first: suffix counts within the lane
+  const int a3 = above, a2 = a3 + c[3], a1 = a2 + c[2], a0 = a1 + c[1];
+  const int bb = (want <= a2) ? 3 : (want <= a1) ? 2 : (want <= a0) ? 1 : 0;
+  const int ab = bb == 3 ? a3 : bb == 2 ? a2 : bb == 1 ? a1 : a0;
+  const int ct = bb == 3 ? c[3] : bb == 2 ? c[2] : bb == 1 ? c[1] : c[0];
+  b = 4 * owner + __builtin_amdgcn_readlane(bb, owner);
+  need = want - __builtin_amdgcn_readlane(ab, owner);
   cnt = __builtin_amdgcn_readlane(ct, owner);
 }
 
 // Exclusive prefix over the workgroup of one int per thread, in thread
 // order; row r of sh.wsum holds the wave totals (one barrier; the caller
 // must not reuse row r before another barrier).
-__device__ __forceinline__ int block_excl_scan(int x, SelShared& sh, int r, int* total = nullptr) {
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int x, SelShared<NT>& sh, int r, int* total = nullptr) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int wt;
   const int incl = wave_incl_scan(x, &wt);
@@ -185,7 +148,7 @@ __device__ __forceinline__ int block_excl_scan(int x, SelShared& sh, int r, int*
   __syncthreads();
   int base = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const int v = sh.wsum[r][i];
     base += (i < w) ? v : 0;
     all += v;
@@ -201,132 +164,179 @@ __device__ __forceinline__ int block_excl_scan(int x, SelShared& sh, int r, int*
 //          position whose first holder is another thread)
 //   k      how many to keep (at most the number of valid candidates)
 //   smin, smax  a range holding every candidate's score (any finite range
-//          keeps the result exact; a tight one keeps the lists short)
+//          keeps the result exact; a tight one keeps the boundary bins small)
 // All threads of the workgroup call it with the same k, smin, smax.
-template <int S>
+template <int NT, int S>
 __device__ __forceinline__ uint32_t select_level(const float (&sc)[S], uint32_t valid, uint32_t owned, int pos0, int k,
-                                                 float smin, float smax, SelShared& sh, SelCursor& cur) {
-  const int t = threadIdx.x;
+                                                 float smin, float smax, SelShared<NT>& sh, SelCursor& cur) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int trash = kSelBins + lane;  // this lane's bin for slots that do not count
   const LinBins bin(smin, smax);
   int* hist = sh.hist[cur.hb];
-  // A. histogram of the owned candidates
+  // 1. histogram of the owned candidates (no branch per slot)
 #pragma unroll
-  for (int i = 0; i < S; ++i)
-    if ((owned >> i) & 1u) atomicAdd(&hist[bin(sc[i])], 1);
-  __syncthreads();  // B
-  // the previous level's histogram and list are read no more: clear them
+  for (int i = 0; i < S; ++i) atomicAdd(&hist[((owned >> i) & 1u) ? bin(sc[i]) : trash], 1);
+  __syncthreads();
+  // the previous level's histograms and list are read no more: clear them
   // for the levels after this one
   {
     int* old = sh.hist[(cur.hb + 2) % 3];
-    for (int i = t; i < kSelBins; i += kSelThreads) old[i] = 0;
+    int* old2 = sh.hist2[cur.lb ^ 1];
+    for (int i = t; i < kSelBins; i += NT) {
+      old[i] = 0;
+      old2[i] = 0;
+    }
     if (t == 0) sh.list_n[cur.lb ^ 1] = 0;
   }
   int b, need, cnt;
   find_bin(hist, k, b, need, cnt);
-  uint32_t kept = 0u;
-  if (cnt == need) {  // W. bin b is kept whole (uniform)
+  uint32_t above = 0u, cell = 0u;  // candidates above the boundary cell, and in it
 #pragma unroll
-    for (int i = 0; i < S; ++i) kept |= (((valid >> i) & 1u) && bin(sc[i]) >= b) ? (1u << i) : 0u;
-  } else if (cnt <= kSelList) {  // L. exact ranks inside bin b (uniform)
-    uint64_t* list = sh.list[cur.lb];
-    uint32_t inb = 0u;
+  for (int i = 0; i < S; ++i) {
+    const int bi = bin(sc[i]);
+    const bool v = (valid >> i) & 1u;
+    above |= (v && bi > b) ? (1u << i) : 0u;
+    cell |= (v && bi == b) ? (1u << i) : 0u;
+  }
+  uint32_t kept;
+  if (cnt == need) {  // bin b is kept whole (uniform)
+    kept = above | cell;
+  } else {
+    // 2. sub-bins of bin b
+    const LinBins sub = bin.sub(b);
+    int* h2 = sh.hist2[cur.lb];
 #pragma unroll
-    for (int i = 0; i < S; ++i) inb |= (((valid >> i) & 1u) && bin(sc[i]) == b) ? (1u << i) : 0u;
-    const uint32_t mine = inb & owned;
-    {
-      const int n = __popc(mine);
-      int wt;
-      const int incl = wave_incl_scan(n, &wt);
-      int base = 0;
-      if ((threadIdx.x & 63) == 63 && wt > 0) base = atomicAdd(&sh.list_n[cur.lb], wt);
-      base = __builtin_amdgcn_readlane(base, 63) + incl - n;
+    for (int i = 0; i < S; ++i) atomicAdd(&h2[(((owned & cell) >> i) & 1u) ? sub(sc[i]) : trash], 1);
+    __syncthreads();
+    int b2, need2, cnt2;
+    find_bin(h2, need, b2, need2, cnt2);
+    uint32_t cell2 = 0u;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int si = sub(sc[i]);
+      const bool c = (cell >> i) & 1u;
+      above |= (c && si > b2) ? (1u << i) : 0u;
+      cell2 |= (c && si == b2) ? (1u << i) : 0u;
+    }
+    cell = cell2;
+    need = need2;
+    if (cnt2 == need2) {  // the sub-bin is kept whole (uniform)
+      kept = above | cell;
+    } else if (cnt2 <= kSelList) {  // 3. exact ranks inside the cell (uniform)
+      uint64_t* list = sh.list[cur.lb];
+      const uint32_t mine = cell & owned;
+      {
+        const int n = __popc(mine);
+        int wt;
+        const int incl = wave_incl_scan(n, &wt);
+        int base = 0;
+        if (lane == 63 && wt > 0) base = atomicAdd(&sh.list_n[cur.lb], wt);
+        base = __builtin_amdgcn_readlane(base, 63) + incl - n;
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+          if ((mine >> i) & 1u) list[base++] = rank_key(order_key(sc[i]), pos0 + i);
+      }
+      __syncthreads();
+      // the need-th best entry of the list, tau: lane l ranks entries l,
+      // l + 64, ... against the whole list (its ranks are 0 .. nl-1, the keys
+      // being distinct), and the entry of rank need - 1 is broadcast
+      const int nl = sh.list_n[cur.lb];
+      uint32_t tau_hi = 0u, tau_lo = 0u;
+      for (int e0 = 0; e0 < nl; e0 += 64) {  // uniform
+        const int e = e0 + lane;
+        const uint64_t me = e < nl ? list[e] : 0ull;
+        int rank = 0;
+        int f = 0;
+        for (; f + 4 <= nl; f += 4) {  // four reads in flight per step
+          const uint64_t x0 = list[f], x1 = list[f + 1], x2 = list[f + 2], x3 = list[f + 3];
+          rank += (x0 > me ? 1 : 0) + (x1 > me ? 1 : 0) + (x2 > me ? 1 : 0) + (x3 > me ? 1 : 0);
+        }
+        for (; f < nl; ++f) rank += list[f] > me ? 1 : 0;
+        const uint64_t hit = __ballot((e < nl) & (rank == need - 1));
+        if (hit) {  // uniform
+          const int src = (int)__ffsll((unsigned long long)hit) - 1;
+          tau_hi = __builtin_amdgcn_readlane((uint32_t)(me >> 32), src);
+          tau_lo = __builtin_amdgcn_readlane((uint32_t)me, src);
+        }
+      }
+      const uint64_t tau = ((uint64_t)tau_hi << 32) | tau_lo;
+      // kept: above the cell, and in it the entries ranked at or above tau
+      // (exactly `need` of them; a copy held by a non-owner decides the same)
+      kept = above;
 #pragma unroll
       for (int i = 0; i < S; ++i)
-        if ((mine >> i) & 1u) list[base++] = rank_key(order_key(sc[i]), pos0 + i);
-    }
-    __syncthreads();  // C
-    const int nl = sh.list_n[cur.lb];
+        kept |= (((cell >> i) & 1u) && rank_key(order_key(sc[i]), pos0 + i) >= tau) ? (1u << i) : 0u;
+    } else {  // 4. heavy ties: narrow the cell by the key bits (uniform)
+      const int w = t >> 6;
+      uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      if ((inb >> i) & 1u) {
-        const uint64_t me = rank_key(order_key(sc[i]), pos0 + i);
-        int rank = 0;
-        for (int e = 0; e < nl; ++e) rank += list[e] > me ? 1 : 0;
-        kept |= rank < need ? (1u << i) : 0u;
+      for (int i = 0; i < S; ++i) {
+        const bool in = (cell >> i) & 1u;
+        const uint32_t key = order_key(sc[i]);
+        kmn = in ? min(kmn, key) : kmn;
+        kmx = in ? max(kmx, key) : kmx;
       }
-      kept |= (((valid >> i) & 1u) && bin(sc[i]) > b) ? (1u << i) : 0u;
-    }
-  } else {  // D. heavy ties: narrow bin b by the key bits
-    const int lane = t & 63, w = t >> 6;
-    uint32_t inb = 0u;
-    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+      kmn = wave_min_u32(kmn);
+      kmx = wave_max_u32(kmx);
+      if (lane == 0) {
+        sh.wmn[w] = kmn;
+        sh.wmx[w] = kmx;
+      }
+      __syncthreads();
+      uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const bool in = ((valid >> i) & 1u) && bin(sc[i]) == b;
-      inb |= in ? (1u << i) : 0u;
-      const uint32_t key = order_key(sc[i]);
-      kmn = in ? min(kmn, key) : kmn;
-      kmx = in ? max(kmx, key) : kmx;
-    }
-    kmn = wave_min_u32(kmn);
-    kmx = wave_max_u32(kmx);
-    if (lane == 0) {
-      sh.wmn[w] = kmn;
-      sh.wmx[w] = kmx;
-    }
-    __syncthreads();
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+      for (int i = 0; i < NT / 64; ++i) {
+        lo = min(lo, sh.wmn[i]);
+        hi = max(hi, sh.wmx[i]);
+      }
+      int nd = need;
+      bool whole = false;
+      int* h3 = sh.hist[(cur.hb + 1) % 3];  // the next level's pass-1 histogram: zero now, zero again on exit
+      while (!whole && lo != hi) {          // uniform
+        const uint32_t range = hi - lo;
+        const int rb = 32 - __clz(range);
+        const int s8 = rb > 8 ? rb - 8 : 0;  // (range >> s8) < kSelBins
 #pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) {
-      lo = min(lo, sh.wmn[i]);
-      hi = max(hi, sh.wmx[i]);
-    }
-    int nd = need;
-    bool whole = false;
-    int* h2 = sh.hist[(cur.hb + 1) % 3];  // the next level's histogram: zero now, zero again on exit
-    while (!whole && lo != hi) {          // uniform
-      const uint32_t range = hi - lo;
-      const int rb = 32 - __clz(range);
-      const int s = rb > 9 ? rb - 9 : 0;  // (range >> s) < kSelBins
+        for (int i = 0; i < S; ++i) {
+          const uint32_t key = order_key(sc[i]);
+          if (((cell & owned) >> i) & 1u && key >= lo && key <= hi) atomicAdd(&h3[(key - lo) >> s8], 1);
+        }
+        __syncthreads();
+        int b3, nd3, cnt3;
+        find_bin(h3, nd, b3, nd3, cnt3);
+        __syncthreads();  // every wave has read h3
+        for (int i = t; i < kSelBins; i += NT) h3[i] = 0;
+        __syncthreads();
+        const uint32_t nlo = lo + ((uint32_t)b3 << s8);
+        hi = (s8 == 0) ? nlo : min(hi, nlo + ((1u << s8) - 1u));
+        lo = nlo;
+        nd = nd3;
+        whole = cnt3 == nd3;
+      }
+      // above the narrowed range: kept; inside: all (whole) or the nd lowest positions (ties)
+      uint32_t tie = 0u;
+      kept = above;
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const uint32_t key = order_key(sc[i]);
-        if (((inb & owned) >> i) & 1u && key >= lo && key <= hi) atomicAdd(&h2[(key - lo) >> s], 1);
+        const bool in = (cell >> i) & 1u;
+        kept |= (in && key > hi) ? (1u << i) : 0u;
+        tie |= (in && key >= lo && key <= hi) ? (1u << i) : 0u;
       }
-      __syncthreads();
-      int b2, nd2, cnt2;
-      find_bin(h2, nd, b2, nd2, cnt2);
-      __syncthreads();  // every wave has read h2
-      for (int i = t; i < kSelBins; i += kSelThreads) h2[i] = 0;
-      __syncthreads();
-      const uint32_t nlo = lo + ((uint32_t)b2 << s);
-      hi = (s == 0) ? nlo : min(hi, nlo + ((1u << s) - 1u));
-      lo = nlo;
-      nd = nd2;
-      whole = cnt2 == nd2;
-    }
-    // above the narrowed range: kept; inside: all (whole) or the nd lowest positions (ties)
-    uint32_t tie = 0u;
+      if (whole) {
+        kept |= tie;
+      } else {
+        const int before = block_excl_scan(__popc(tie & owned), sh, 0);
+        // a copy held by a non-owner was counted by its owner, an earlier thread
+        int r = before - ((tie & ~owned) ? 1 : 0);
 #pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const uint32_t key = order_key(sc[i]);
-      const bool ib = (inb >> i) & 1u;
-      kept |= ((((valid >> i) & 1u) && bin(sc[i]) > b) || (ib && key > hi)) ? (1u << i) : 0u;
-      tie |= (ib && key >= lo && key <= hi) ? (1u << i) : 0u;
-    }
-    if (whole) {
-      kept |= tie;
-    } else {
-      const int before = block_excl_scan(__popc(tie & owned), sh, 0);
-      // a copy held by a non-owner was counted by its owner, an earlier thread
-      int r = before - ((tie & ~owned) ? 1 : 0);
-#pragma unroll
-      for (int i = 0; i < S; ++i)
-        if ((tie >> i) & 1u) {
-          kept |= (r < nd) ? (1u << i) : 0u;
-          r += ((owned >> i) & 1u) ? 1 : 0;
-        }
-      __syncthreads();  // the scan row is free again
+        for (int i = 0; i < S; ++i)
+          if ((tie >> i) & 1u) {
+            kept |= (r < nd) ? (1u << i) : 0u;
+            r += ((owned >> i) & 1u) ? 1 : 0;
+          }
+        __syncthreads();  // the scan row is free again
+      }
     }
   }
   cur.hb = (cur.hb + 1) % 3;

@@ -1,26 +1,25 @@
-// WaveFilter per-denoising-step kernels for gfx950 (MI355X).  One call is
-// three launches; in each, the workgroups of a head count their arrival and
-// the last one to arrive finishes the head's stage (see wf_select.h for the
-// agent-scope hand-over this relies on):
+// WaveFilter per-denoising-step kernels for gfx950 (MI355X).  One call is a
+// chain of launches on the caller's stream:
 //
-//   coarse_*_kernel  s_L[n] = max_i (or mean_i) q_i . A_L[n] / sqrt(d) on
-//                    MFMA; the head's last workgroup takes the coarse Top-K
-//                    (Figure 2 (c))
-//   cover_*_kernel   q_i . k_t for every token the kept regions cover, on
-//                    MFMA, summed in registers into the scores of all their
-//                    sub-regions at levels 0 .. L-1 (A_j by linearity from
-//                    the token dot products; from the stored bands for a
-//                    longer basis); the head's last workgroup runs the
-//                    recursive refinement (Figure 2 (d)) and writes the kept
-//                    prompt tokens
-//   attend_kernel    split-K online-softmax attention over the kept prompt
-//                    tokens plus the generated positions (eq. 3 restricted
-//                    to that set); the head's last workgroup merges the
-//                    splits into O.  It also serves a selection handed in.
-//   refine_lists_kernel
-//                    the refinement for covered sets beyond the in-register
-//                    capacity, one workgroup per head, in a launch between
-//                    the cover and the attention launches
+//   coarse_*_kernel   s_L[n] = max_i (or mean_i) q_i . A_L[n] / sqrt(d) on
+//                     MFMA (Figure 2 (c))
+//   coarse_topk_kernel
+//                     the coarse Top-K, one workgroup per head, for large
+//                     coarse levels (n_L > 1 024) or L = 0; otherwise every
+//                     cover workgroup computes it for itself
+//   cover_*_kernel    the coarse Top-K (Figure 2 (c)), then q_i . k_t for
+//                     every token the kept regions cover, on MFMA, summed in
+//                     registers into the scores of all their sub-regions at
+//                     levels 0 .. L-1 (A_j by linearity from the token dot
+//                     products; from the stored bands for a longer basis)
+//   refine_sel_kernel the recursive refinement (Figure 2 (d)), one workgroup
+//                     of 1 024 threads per head, the coverage scores in
+//                     registers (refine_lists_kernel beyond 8 192 covered
+//                     positions); writes the kept prompt tokens
+//   attend_kernel     split-K online-softmax attention over the kept prompt
+//                     tokens plus the generated positions (eq. 3 restricted
+//                     to that set); also serves a selection handed in
+//   combine_kernel    log-sum-exp merge of the split partials into O
 //
 // Citations are to WaveFilter (arXiv 2606.00724).
 #include <hip/hip_runtime.h>
@@ -30,6 +29,8 @@
 #include "wf_device.h"
 #include "wf_internal.h"
 #include "wf_select.h"
+
+static_assert(wf::kRefineThreads == wf::kRefineThreadsHost, "one refinement workgroup size");
 
 namespace wf {
 
@@ -45,7 +46,6 @@ struct StepArgs {
   int32_t* sel_out;
   int32_t* sel_levels;
   float* score_levels;
-  uint32_t* counters;    // [heads_total] arrival counters, zero between launches
   uint32_t* keys_top;    // [heads_total][n_top]
   int32_t* sel_top;      // [heads_total][k_top]
   float* cov;            // [heads_total][cov_len]
@@ -159,15 +159,14 @@ template <int NT> struct TopKRaw {
 };
 
 // ---------------------------------------------------------------------------
-// Coarse Top-K (Figure 2 (c)) by the head's last coarse workgroup: the k_L
-// best regions from the order keys of s_L (written by every coarse
-// workgroup of the head with agent-scope stores), handed to emit(o, i, s)
-// in ascending order.  In registers for n_L <= 256 x 32 (S keys per
-// thread), else by the general Top-K with the keys in LDS (up to
-// kMaxCoarseLds) or read from memory.
+// Coarse Top-K (Figure 2 (c)) of one head: the k_L best regions from the
+// order keys of s_L, handed to emit(o, i, s) in ascending order.  In
+// registers with S keys per thread (n_L <= 256 S), else by the general
+// Top-K with the keys in LDS (up to kMaxCoarseLds) or read from memory.
 // ---------------------------------------------------------------------------
 template <int S, class Emit>
-__device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int k, SelShared& sh, Emit emit) {
+__device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int k, SelShared<kSelThreads>& sh,
+                                                Emit emit) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int pos0 = t * S;
   float sc[S];
@@ -176,7 +175,7 @@ __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int
   for (int i = 0; i < S; ++i) {
     const int p = pos0 + i;
     const bool in = p < n;
-    const uint32_t key = load_agent(keys + min(p, n - 1));
+    const uint32_t key = keys[min(p, n - 1)];
     sc[i] = key_to_f32(key);
     valid |= in ? (1u << i) : 0u;
     mn = in ? min(mn, key) : mn;
@@ -193,12 +192,12 @@ __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int
   mn = 0xFFFFFFFFu;
   mx = 0u;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < kSelThreads / 64; ++i) {
     mn = min(mn, sh.wmn[i]);
     mx = max(mx, sh.wmx[i]);
   }
   SelCursor cur;
-  const uint32_t kept = select_level<S>(sc, valid, valid, pos0, k, key_to_f32(mn), key_to_f32(mx), sh, cur);
+  const uint32_t kept = select_level<kSelThreads, S>(sc, valid, valid, pos0, k, key_to_f32(mn), key_to_f32(mx), sh, cur);
   int o = block_excl_scan(__popc(kept), sh, 1);
 #pragma unroll
   for (int i = 0; i < S; ++i)
@@ -208,20 +207,21 @@ __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int
     }
 }
 
-// The in-register coarse Top-K with S keys per thread for S in SLIST, else
-// (topk_s = 0) the general Top-K.
+// The in-register coarse Top-K for topk_s in {1, 2, 4} (what a cover
+// workgroup runs), or with LARGE also {8, 16, 32} and the general path (the
+// Top-K's own launch).
 template <bool LARGE, class Emit>
 __device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, unsigned char* raw, uint32_t* keys_l,
                                                 Emit emit) {
   const uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
-  SelShared& sh = *reinterpret_cast<SelShared*>(raw);
-  if constexpr (!LARGE) {
-    switch (a.topk_s) {
-      case 1: coarse_topk_sel<1>(keys, a.n_top, a.k_top, sh, emit); return;
-      case 2: coarse_topk_sel<2>(keys, a.n_top, a.k_top, sh, emit); return;
-      default: coarse_topk_sel<4>(keys, a.n_top, a.k_top, sh, emit); return;
-    }
-  } else {
+  SelShared<kSelThreads>& sh = *reinterpret_cast<SelShared<kSelThreads>*>(raw);
+  switch (a.topk_s) {
+    case 1: coarse_topk_sel<1>(keys, a.n_top, a.k_top, sh, emit); return;
+    case 2: coarse_topk_sel<2>(keys, a.n_top, a.k_top, sh, emit); return;
+    case 4: coarse_topk_sel<4>(keys, a.n_top, a.k_top, sh, emit); return;
+    default: break;
+  }
+  if constexpr (LARGE) {
     switch (a.topk_s) {
       case 8: coarse_topk_sel<8>(keys, a.n_top, a.k_top, sh, emit); return;
       case 16: coarse_topk_sel<16>(keys, a.n_top, a.k_top, sh, emit); return;
@@ -230,49 +230,49 @@ __device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, uns
     }
     auto& fs = *reinterpret_cast<TopKFastShared<kSelThreads>*>(raw);
     auto out = [&](int o, int i) {
-      if (o < a.k_top) emit(o, i, key_to_f32(load_agent(keys + i)));
+      if (o < a.k_top) emit(o, i, key_to_f32(keys[i]));
     };
     if (a.coarse_keys_in_lds) {
-      for (int i = threadIdx.x; i < a.n_top; i += kSelThreads) keys_l[i] = load_agent(keys + i);
+      for (int i = threadIdx.x; i < a.n_top; i += kSelThreads) keys_l[i] = keys[i];
       __syncthreads();
       topk_fast<kSelThreads>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, fs, out);
     } else {
-      topk_fast<kSelThreads>([&](int i) { return load_agent(keys + i); }, a.n_top, a.k_top, fs, out);
+      topk_fast<kSelThreads>([&](int i) { return keys[i]; }, a.n_top, a.k_top, fs, out);
     }
   }
 }
 
-// The coarse Top-K of one head and its outputs: the kept regions (the cover
-// launch reads them), the level-L sinks, and for L = 0 the kept tokens.
-template <bool LARGE>
-__device__ __forceinline__ void coarse_topk_head(const StepArgs& a, int head, unsigned char* raw, uint32_t* keys_l) {
-  const bool report = a.sel_levels || a.score_levels;
-  int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+// Where the coarse Top-K runs: in every cover workgroup of the head (each
+// computes the same set; n_L <= 1 024 and L > 0), else in a launch of its
+// own, one workgroup per head.
+__device__ __forceinline__ bool topk_in_cover(const StepArgs& a) { return a.topk_s >= 1 && a.topk_s <= 4 && a.levels > 0; }
+
+// The coarse Top-K's outputs beside emit_sel(o, i): the kept regions
+// (workgroup `writer` of the head only), the level-L sinks, and for L = 0
+// the kept tokens.
+template <class F>
+__device__ __forceinline__ auto coarse_emitter(const StepArgs& a, int head, bool writer, F emit_sel) {
+  const bool report = writer && (a.sel_levels || a.score_levels);
+  int32_t* sel_g = writer ? a.sel_top + (int64_t)head * a.k_top : nullptr;
+  int32_t* dbg_sel = report && a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = report && a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   // with L = 0 the coarse level is the tokens themselves: these are the kept tokens
-  int32_t* tsel = a.levels == 0 ? a.sel_ws + (int64_t)head * a.k0 : nullptr;
-  int32_t* tout = (a.levels == 0 && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
-  coarse_topk_run<LARGE>(a, head, raw, keys_l, [&](int o, int i, float sc) {
-    sel_g[o] = i;
-    if (report) {
-      if (dbg_sel) dbg_sel[o] = i;
-      if (dbg_score) dbg_score[o] = sc;
-    }
+  int32_t* tsel = (writer && a.levels == 0) ? a.sel_ws + (int64_t)head * a.k0 : nullptr;
+  int32_t* tout = (writer && a.levels == 0 && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  return [=](int o, int i, float sc) {
+    emit_sel(o, i);
+    if (sel_g) sel_g[o] = i;
+    if (dbg_sel) dbg_sel[o] = i;
+    if (dbg_score) dbg_score[o] = sc;
     if (tsel) {
       tsel[o] = i;
       if (tout) tout[o] = i;
     }
-  });
+  };
 }
 
-// The coarse Top-K runs in the coarse launch's last workgroup of a head for
-// up to 4 keys per thread (n_L <= 1 024), else in a launch of its own.
-__device__ __forceinline__ bool topk_in_coarse(const StepArgs& a) { return a.topk_s >= 1 && a.topk_s <= 4; }
-
-// Selection scratch of the coarse and cover workgroups: the in-register
-// selection state, or the general Top-K's.
-constexpr size_t kSelRawBytes = cmax(sizeof(SelShared), TopKRaw<kSelThreads>::BYTES);
+// Selection scratch of a workgroup that runs the general coarse Top-K.
+constexpr size_t kSelRawBytes = cmax(sizeof(SelShared<kSelThreads>), TopKRaw<kSelThreads>::BYTES);
 
 // ---------------------------------------------------------------------------
 // Coarse scores.  Wave w of block x scores level-L regions
@@ -280,15 +280,12 @@ constexpr size_t kSelRawBytes = cmax(sizeof(SelShared), TopKRaw<kSelThreads>::BY
 // so lane (query 16 qt + l16, g) holds regions 16 w + 4 g + r.  For bfloat16
 // inputs the float32 coefficients are split into bf16 hi + lo parts, both
 // multiplied exactly, accumulated in float32.  Max over queries: in registers
-// over qt, then across the 16 lanes of a row.  The head's last workgroup
-// then takes the coarse Top-K and writes the kept regions (for L = 0, the
-// kept tokens).
+// over qt, then across the 16 lanes of a row.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int RT, bool MEAN>
 __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
   using AG = QueryAgg<MEAN>;
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
-  __shared__ __align__(16) unsigned char raw[sizeof(SelShared)];
   const int head = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -361,14 +358,8 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
   if (l16 == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (n0 + r < a.n_top) store_agent(keys + n0 + r, order_key(m[r] * sc));
+      if (n0 + r < a.n_top) keys[n0 + r] = order_key(m[r] * sc);
   }
-
-  // -- the head's last workgroup: the coarse Top-K
-  if (!topk_in_coarse(a)) return;  // uniform: coarse_topk_kernel takes it
-  SelShared& sh = *reinterpret_cast<SelShared*>(raw);
-  if (!arrive_last(a.counters + head, gridDim.x, &sh.last)) return;
-  coarse_topk_head<false>(a, head, raw, nullptr);
 }
 
 template <typename T, int D, int RT>
@@ -445,7 +436,7 @@ __device__ __forceinline__ void f32_rows_mma(const float4 (&x)[D / 16], const Fr
 // positions (a neutral range where it has none).  The level's four 16-row
 // tiles go in pairs, both tiles' rows requested before either is multiplied;
 // rows past the level's end repeat its last row (in bounds) and are never
-// written.  Writes are agent-scope: the head's last workgroup reads them.
+// written.
 template <typename T, int D, int RT, bool MEAN>
 __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, const int* sel_l, const Frag<T, D> (&qf)[RT],
                                                  int64_t wave_base, int lane, int g, int l16) {
@@ -502,7 +493,7 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
             const float m = AG::row(x) * sc;
             const int64_t pr = p0 + 4 * g + r;
             const bool in = (l16 == 0) && pr < nj;
-            if (in) store_agent(cov + a.cov_off[j] + pr, m);
+            if (in) cov[a.cov_off[j] + pr] = m;
             const uint32_t k = order_key(m);
             rmn = in ? min(rmn, k) : rmn;
             rmx = in ? max(rmx, k) : rmx;
@@ -513,8 +504,8 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
     rmn = wave_min_u32(rmn);
     rmx = wave_max_u32(rmx);
     if (lane == 0) {
-      store_agent(lvl + 2 * j, rmn);
-      store_agent(lvl + 2 * j + 1, rmx);
+      lvl[2 * j] = rmn;
+      lvl[2 * j + 1] = rmx;
     }
   }
 }
@@ -529,8 +520,8 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
 // 2 in-lane (r), levels 3 and 4 across lane groups g (xor 16, xor 32),
 // levels 5 and 6 across tiles in registers.  The score of a block is the max
 // over queries: over qt in registers, then across the 16 lanes of a row.
-// Scores are written per level at the block's position p >> j, with
-// agent-scope stores, and so is each level's score range over the wave.
+// Scores are written per level at the block's position p >> j, and so is
+// each level's score range over the wave.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int RT, bool MEAN>
 __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const int* sel_l, const Frag<T, D> (&qf)[RT],
@@ -583,8 +574,8 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
     rmn = wave_min_u32(rmn);
     rmx = wave_max_u32(rmx);
     if (lane == 0) {
-      store_agent(lvl + 2 * j, rmn);
-      store_agent(lvl + 2 * j + 1, rmx);
+      lvl[2 * j] = rmn;
+      lvl[2 * j + 1] = rmx;
     }
   };
   // level 0
@@ -601,11 +592,8 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       m[r] = AG::row(x) * isd;
     }
     const int64_t p = tb + 16 * t;
-    if (writer && p < a.covered) {  // covered is a multiple of 4 when L >= 2; at L = 1 of 2
-      float* dst = cov + a.cov_off[0] + p;
-      store_agent2(dst, m[0], m[1]);
-      if (p + 2 < a.covered) store_agent2(dst + 2, m[2], m[3]);
-    }
+    if (writer && p < a.covered)  // (level arrays are padded to multiples of four)
+      *reinterpret_cast<float4*>(cov + a.cov_off[0] + p) = make_float4(m[0], m[1], m[2], m[3]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) track(writer && p + r < a.covered, m[r]);
   }
@@ -632,7 +620,7 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
         m[h] = AG::row(x) * sc;
       }
       const int64_t p = tb + 16 * t;
-      if (writer && p < a.covered) store_agent2(cov + a.cov_off[1] + (p >> 1), m[0], m[1]);
+      if (writer && p < a.covered) *reinterpret_cast<float2*>(cov + a.cov_off[1] + (p >> 1)) = make_float2(m[0], m[1]);
       track(writer && p < a.covered, m[0]);
       track(writer && p + 2 < a.covered, m[1]);
     }
@@ -653,7 +641,7 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
       x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
-      if (writer && p < a.covered) store_agent(cov + a.cov_off[2] + (p >> 2), x);
+      if (writer && p < a.covered) cov[a.cov_off[2] + (p >> 2)] = x;
       track(writer && p < a.covered, x);
     }
   }
@@ -673,7 +661,7 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
       x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
-      if (writer && (g & 1) == 0 && p < a.covered) store_agent(cov + a.cov_off[3] + (p >> 3), x);
+      if (writer && (g & 1) == 0 && p < a.covered) cov[a.cov_off[3] + (p >> 3)] = x;
       track(writer && (g & 1) == 0 && p < a.covered, x);
     }
   }
@@ -693,7 +681,7 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       for (int qt = 1; qt < RT; ++qt) x = AG::comb(x, s[t][qt][0]);
       x = AG::row(x) * sc;
       const int64_t p = wave_base + 16 * t;
-      if (writer && g == 0 && p < a.covered) store_agent(cov + a.cov_off[4] + (p >> 4), x);
+      if (writer && g == 0 && p < a.covered) cov[a.cov_off[4] + (p >> 4)] = x;
       track(writer && g == 0 && p < a.covered, x);
     }
   }
@@ -715,9 +703,9 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
     x23 = AG::row(x23) * (isd * 0.17677669529663688110f);
     xall = AG::row(xall) * (isd * 0.125f);                 // 2^{-3}
     if (lane == 0) {
-      if (wave_base < a.covered) store_agent(cov + a.cov_off[5] + (wave_base >> 5), x01);
-      if (wave_base + 32 < a.covered) store_agent(cov + a.cov_off[5] + (wave_base >> 5) + 1, x23);
-      if (jmax > 6) store_agent(cov + a.cov_off[6] + (wave_base >> 6), xall);
+      if (wave_base < a.covered) cov[a.cov_off[5] + (wave_base >> 5)] = x01;
+      if (wave_base + 32 < a.covered) cov[a.cov_off[5] + (wave_base >> 5) + 1] = x23;
+      if (jmax > 6) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
     }
     rmn = 0xFFFFFFFFu;
     rmx = 0u;
@@ -734,22 +722,15 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
 }
 
 // ---------------------------------------------------------------------------
-// Recursive refinement (Figure 2 (d)) of one head in registers, by the
-// head's last cover workgroup: thread t holds the level-0 positions
+// Recursive refinement (Figure 2 (d)) of one head in registers, by one
+// workgroup of NT threads: thread t holds the level-0 positions
 // [t S0, t S0 + S0) and their ancestors (see wf_select.h).  Every level's
-// coverage scores and score range are loaded at the start (agent-scope
-// loads: other workgroups of the launch wrote them), then each level keeps
-// the k_j best children of the kept parents.  Writes the kept tokens
-// ascending, and with the per-level sinks every level's kept regions.
+// coverage scores and score range are loaded at the start, then a loop over
+// the levels keeps the k_j best children of the kept parents.  The loop body is one copy of the level code, so the
+// instructions a single workgroup runs stay few and, after the first level,
+// cached.  Writes the kept tokens ascending, and with the per-level sinks
+// every level's kept regions.
 // ---------------------------------------------------------------------------
-template <int J> struct IntC { static constexpr int value = J; };
-template <int J, class F>
-__device__ __forceinline__ void for_levels_desc(F&& f) {
-  f(IntC<J>{});
-  if constexpr (J > 0) for_levels_desc<J - 1>(f);
-}
-static_assert(kMaxLevels == 7, "the refinement holds seven levels");
-
 template <int S0, int J> struct Held { static constexpr int N = (S0 >> J) > 0 ? (S0 >> J) : 1; };
 template <int S0> struct HeldScores {
   float s0[Held<S0, 0>::N], s1[Held<S0, 1>::N], s2[Held<S0, 2>::N], s3[Held<S0, 3>::N];
@@ -763,31 +744,62 @@ template <int S0> struct HeldScores {
     else if constexpr (J == 5) return s5;
     else return s6;
   }
+  // level j's slots into a full-width array (slots past the level's count hold 0)
+  __device__ __forceinline__ void level(int j, float (&sc)[S0]) {
+#pragma unroll
+    for (int i = 0; i < S0; ++i) sc[i] = 0.f;
+    switch (j) {
+      case 0: copy<0>(sc); break;
+      case 1: copy<1>(sc); break;
+      case 2: copy<2>(sc); break;
+      case 3: copy<3>(sc); break;
+      case 4: copy<4>(sc); break;
+      case 5: copy<5>(sc); break;
+      default: copy<6>(sc); break;
+    }
+  }
+  template <int J> __device__ __forceinline__ void copy(float (&sc)[S0]) {
+#pragma unroll
+    for (int i = 0; i < Held<S0, J>::N; ++i) sc[i] = get<J>()[i];
+  }
+  template <int J> __device__ __forceinline__ void load(const float* src, int nj, int p0) {
+    auto& s = get<J>();
+    if constexpr (Held<S0, J>::N >= 2) {
+#pragma unroll
+      for (int i = 0; i < Held<S0, J>::N; i += 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src + min(p0 + i, nj - 2));
+        s[i] = v.x;
+        s[i + 1] = v.y;
+      }
+    } else {
+      s[0] = src[min(p0, nj - 1)];
+    }
+  }
 };
+static_assert(kMaxLevels == 7, "the refinement holds seven levels");
 
-template <int S0>
-__device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const int* sel_l, SelShared& sh) {
+template <int NT, int S0>
+__device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const int* sel_l, SelShared<NT>& sh) {
   const int t = threadIdx.x, lane = t & 63;
   const int L = a.levels;
   const int covered = (int)a.covered;
   const float* cov = a.cov + (int64_t)head * a.cov_len;
   // each level's score range: the cover waves' slots (at most 128 per head
-  // here, lanes l and l + 64 of every wave), reduced by every wave.  Loads
-  // are unconditional, from clamped slots; slots past the last wave take the
+  // here, lanes l and l + 64 of wave 0), published to LDS.  Loads are
+  // unconditional, from clamped slots; slots past the last wave take the
   // neutral range by an all-ones mask.
   const int nwav = (covered + 63) >> 6;
   const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
-  uint32_t rmn[kMaxLevels], rmx[kMaxLevels];
-  {
+  if (t < 64) {
     uint32_t x[2][kMaxLevels][2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int v = min(lane + 64 * r, nwav - 1);
 #pragma unroll
       for (int j = 0; j < kMaxLevels; ++j) {
-        const float2 p = load_agent2(reinterpret_cast<const float*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j));
-        x[r][j][0] = __float_as_uint(p.x);
-        x[r][j][1] = __float_as_uint(p.y);
+        const uint2 p = *reinterpret_cast<const uint2*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j);
+        x[r][j][0] = p.x;
+        x[r][j][1] = p.y;
       }
     }
 #pragma unroll
@@ -799,36 +811,28 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const in
         mn = min(mn, x[r][j][0] | off);
         mx = max(mx, x[r][j][1] & ~off);
       }
-      rmn[j] = wave_min_u32(mn);
-      rmx[j] = wave_max_u32(mx);
+      mn = wave_min_u32(mn);
+      mx = wave_max_u32(mx);
+      if (lane == 0) {
+        sh.rmn[j] = mn;
+        sh.rmx[j] = mx;
+      }
     }
   }
   // every live level's scores into registers (clamped positions; slots past
   // a level's end are never valid)
   HeldScores<S0> hs;
-  for_levels_desc<kMaxLevels - 1>([&](auto jc) {
-    constexpr int J = decltype(jc)::value;
-    constexpr int PJ = Held<S0, J>::N;
-    auto& s = hs.template get<J>();
-    if (J < L) {
-      const int nj = covered >> J;
-      const float* src = cov + a.cov_off[J];
-      const int p0 = (t * S0) >> J;
-      if constexpr (PJ >= 2) {
-#pragma unroll
-        for (int i = 0; i < PJ; i += 2) {
-          const float2 v = load_agent2(src + min(p0 + i, nj - 2));
-          s[i] = v.x;
-          s[i + 1] = v.y;
-        }
-      } else {
-        s[0] = load_agent(src + min(p0, nj - 1));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PJ; ++i) s[i] = 0.f;
-    }
-  });
+#define WF_LOAD_LEVEL(J)                                                              \
+  if (J < L) hs.template load<J>(cov + a.cov_off[J], covered >> J, (t * S0) >> J);    \
+  else hs.template copy<J>(hs.s0);
+  WF_LOAD_LEVEL(0)
+  WF_LOAD_LEVEL(1)
+  WF_LOAD_LEVEL(2)
+  WF_LOAD_LEVEL(3)
+  WF_LOAD_LEVEL(4)
+  WF_LOAD_LEVEL(5)
+  WF_LOAD_LEVEL(6)
+#undef WF_LOAD_LEVEL
   sel_init(sh);
   __syncthreads();
 
@@ -839,91 +843,81 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const in
     const int pl = (S0 >> L) > 0 ? (S0 >> L) : 1;
     for (int m = 0; m < pl; ++m) keptp |= (pl0 + m < a.k_top) ? (1u << m) : 0u;
   }
-  uint32_t kmask[kMaxLevels], omask[kMaxLevels];
+  const bool report = a.sel_levels || a.score_levels;
+  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  int off = a.k_top;
   SelCursor cur;
-  for_levels_desc<kMaxLevels - 1>([&](auto jc) {
-    constexpr int J = decltype(jc)::value;
-    constexpr int PJ = Held<S0, J>::N;
-    kmask[J] = 0u;
-    omask[J] = 0u;
-    if (J < L) {
-      const int p0 = (t * S0) >> J, nj = covered >> J;
-      const bool own = PJ > 1 || ((t * S0) & ((1 << J) - 1)) == 0;
-      uint32_t valid = 0u;
-#pragma unroll
-      for (int i = 0; i < PJ; ++i) valid |= ((p0 + i < nj) && ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
-      const uint32_t owned = own ? valid : 0u;
-      const uint32_t kept = select_level<PJ>(hs.template get<J>(), valid, owned, p0, a.budgets[L - J],
-                                             key_to_f32(rmn[J]), key_to_f32(rmx[J]), sh, cur);
-      kmask[J] = kept;
-      omask[J] = own ? kept : 0u;
-      keptp = kept;
-    }
-  });
-
-  // the kept tokens, ascending
-  {
-    const uint32_t k0m = kmask[0];
-    int o = block_excl_scan(__popc(k0m), sh, 1);
-    int32_t* tsel = a.sel_ws + (int64_t)head * a.k0;
-    int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
-    const int mask = (1 << L) - 1;
+  float sc[S0];
+  for (int j = L - 1; j >= 0; --j) {
+    hs.level(j, sc);
+    const int pj = (S0 >> j) > 0 ? (S0 >> j) : 1;
+    const int p0 = (t * S0) >> j, nj = covered >> j;
+    const bool own = pj > 1 || ((t * S0) & ((1 << j) - 1)) == 0;
+    uint32_t valid = 0u;
 #pragma unroll
     for (int i = 0; i < S0; ++i)
-      if ((k0m >> i) & 1u) {
-        const int p = t * S0 + i;
-        const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & mask);
-        if (o < a.k0) {  // exactly k_0 are kept; the bound guards the buffers
-          tsel[o] = tok;
-          if (so) so[o] = tok;
-        }
-        ++o;
-      }
-  }
-  // the kept regions of levels L-1 .. 0 and their scores
-  if (a.sel_levels || a.score_levels) {
-    int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-    float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
-    int off = a.k_top;
-    for_levels_desc<kMaxLevels - 1>([&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      constexpr int PJ = Held<S0, J>::N;
-      if (J < L) {
-        const int kj = a.budgets[L - J];
-        int o = block_excl_scan(__popc(omask[J]), sh, 2 + (J & 1));
-        const int shl = L - J, p0 = (t * S0) >> J;
+      valid |= ((i < pj) & (p0 + i < nj) & ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
+    const uint32_t owned = own ? valid : 0u;
+    const int kj = a.budgets[L - j];
+    const uint32_t kept =
+        select_level<NT, S0>(sc, valid, owned, p0, kj, key_to_f32(sh.rmn[j]), key_to_f32(sh.rmx[j]), sh, cur);
+    if (report) {  // uniform: level j's kept regions, ascending, with their scores
+      const uint32_t km = own ? kept : 0u;
+      int o = block_excl_scan(__popc(km), sh, 2 + (j & 1));
+      const int shl = L - j;
 #pragma unroll
-        for (int i = 0; i < PJ; ++i)
-          if ((omask[J] >> i) & 1u) {
-            const int p = p0 + i;
-            if (o < kj) {
-              if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
-              if (dbg_score) dbg_score[off + o] = hs.template get<J>()[i];
-            }
-            ++o;
+      for (int i = 0; i < S0; ++i)
+        if ((km >> i) & 1u) {
+          const int p = p0 + i;
+          if (o < kj) {
+            if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
+            if (dbg_score) dbg_score[off + o] = sc[i];
           }
-        off += kj;
-      }
-    });
+          ++o;
+        }
+    }
+    off += kj;
+    keptp = kept;
   }
+
+  // the kept tokens, ascending
+  int o = block_excl_scan(__popc(keptp), sh, 1);
+  int32_t* tsel = a.sel_ws + (int64_t)head * a.k0;
+  int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  const int mask = (1 << L) - 1;
+#pragma unroll
+  for (int i = 0; i < S0; ++i)
+    if ((keptp >> i) & 1u) {
+      const int p = t * S0 + i;
+      const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & mask);
+      if (o < a.k0) {  // exactly k_0 are kept; the bound guards the buffers
+        tsel[o] = tok;
+        if (so) so[o] = tok;
+      }
+      ++o;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Cover stage: the kept coarse regions from the coarse launch, the coverage
-// scores of this workgroup's 256 covered positions, then (last workgroup of
-// the head, when the refinement fits in registers) the refinement.
+// Cover stage: the kept coarse regions (the coarse Top-K, computed by every
+// workgroup of the head, or read from the Top-K's own launch), then the
+// coverage scores of this workgroup's 256 covered positions.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int RT, bool MEAN, bool BANDS>
 __device__ __forceinline__ void cover_stage(const StepArgs& a) {
   constexpr int NT = kCoverThreads;
-  static_assert(NT == kSelThreads, "the refinement runs on the cover workgroup");
+  static_assert(NT == kSelThreads, "the coarse Top-K runs on the cover workgroup");
   extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L], ascending
-  __shared__ __align__(16) unsigned char raw[sizeof(SelShared)];
+  __shared__ __align__(16) unsigned char raw[sizeof(SelShared<NT>)];
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   const int head = blockIdx.y;
   int* sel_l = reinterpret_cast<int*>(lds);
   stage_query<T, D, NT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
-  {
+  if (topk_in_cover(a)) {  // uniform: every workgroup of the head computes the same kept regions
+    auto emit = coarse_emitter(a, head, blockIdx.x == 0, [&](int o, int i) { sel_l[o] = i; });
+    coarse_topk_run<false>(a, head, raw, nullptr, emit);
+  } else {  // the Top-K's own launch wrote them
     const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
     for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   }
@@ -931,21 +925,17 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t wave_base = (int64_t)blockIdx.x * 256 + w * 64;
-  if (wave_base < a.covered) {  // wave-uniform
-    Frag<T, D> qf[RT];
-    load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
-    if constexpr (BANDS) cover_from_bands<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
-    else cover_haar<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
-  }
-  if (a.refine_s0 != 16) return;  // uniform: refined in a launch of its own
-  SelShared& sh = *reinterpret_cast<SelShared*>(raw);
-  if (!arrive_last(a.counters + head, gridDim.x, &sh.last)) return;
-  refine_sel<16>(a, head, sel_l, sh);
+  if (wave_base >= a.covered) return;  // no workgroup barrier below
+  Frag<T, D> qf[RT];
+  load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
+  if constexpr (BANDS) cover_from_bands<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
+  else cover_haar<T, D, RT, MEAN>(a, head, sel_l, qf, wave_base, lane, g, l16);
 }
 
 // With one or two query tiles (and bfloat16 rows, or head dim 64) the Haar
-// cover kernel fits 128 registers: four workgroups per compute unit;
-// otherwise it keeps the registers its loads in flight need.
+// cover kernel fits 128 registers without spilling: four workgroups per
+// compute unit, so large launches take fewer rounds; otherwise it keeps the
+// registers its loads in flight need.
 template <typename T, int D>
 constexpr int cover_waves_per_simd(int rt) { return (sizeof(T) == 2 || D == 64) && rt <= 2 ? 4 : 1; }
 template <typename T, int D, int RT>
@@ -1061,24 +1051,27 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
 }
 
 #if !defined(WF_STEP_T)  // one compile unit holds these
-// The coarse Top-K for n_L > 1 024, one workgroup per head.
+// The coarse Top-K in a launch of its own, one workgroup per head (n_L >
+// 1 024, or L = 0).
 __global__ __launch_bounds__(kSelThreads) void coarse_topk_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t keys_l[];  // general path: the keys, when staged
   __shared__ __align__(16) unsigned char raw[kSelRawBytes];
-  coarse_topk_head<true>(a, blockIdx.x, raw, keys_l);
+  const int head = blockIdx.x;
+  coarse_topk_run<true>(a, head, raw, keys_l, coarse_emitter(a, head, true, [](int, int) {}));
 }
 
-// The in-register refinement with 32 level-0 positions per thread (covered
-// sets of 4 097 .. 8 192 positions), one workgroup per head.
-__global__ __launch_bounds__(kSelThreads) void refine_sel_kernel(StepArgs a) {
+// The in-register refinement, one workgroup of 1 024 threads per head, with
+// S0 = 1 .. 8 level-0 positions per thread (covered sets up to 8 192).
+template <int S0>
+__global__ __launch_bounds__(kRefineThreads) void refine_sel_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L]
-  __shared__ __align__(16) SelShared sh;
+  __shared__ __align__(16) SelShared<kRefineThreads> sh;
   const int head = blockIdx.x;
   int* sel_l = reinterpret_cast<int*>(lds);
   const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-  for (int i = threadIdx.x; i < a.k_top; i += kSelThreads) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
+  for (int i = threadIdx.x; i < a.k_top; i += kRefineThreads) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   __syncthreads();
-  refine_sel<32>(a, head, sel_l, sh);
+  refine_sel<kRefineThreads, S0>(a, head, sel_l, sh);
 }
 
 __global__ __launch_bounds__(kSelThreads) void refine_lists_kernel(StepArgs a) {
@@ -1103,8 +1096,7 @@ __global__ __launch_bounds__(kSelThreads) void refine_lists_kernel(StepArgs a) {
 // online softmax per query row in float32; O^T += V^T P^T on MFMA with P
 // split into bf16 hi + lo (float32 MFMA for float32 inputs).  The next
 // chunk's rows are fetched into registers while the current one computes.
-// Writes the split's partial (m, l, O) with agent-scope stores; the head's
-// last split workgroup merges them.
+// Writes the split's partial (m, l, O) to the workspace.
 // ---------------------------------------------------------------------------
 // x of lane l ^ NV: a DPP row rotation by 8 for NV = 8, a lane permute for 16.
 template <int NV>
@@ -1358,77 +1350,69 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
   if (tg == 0 && qvalid) {
     float* pml = a.part_ml + (((int64_t)head * a.n_split + split) * a.n_q + query) * 2;
     float* po = a.part_o + ((int64_t)head * a.n_split + split) * a.n_q * D + (int64_t)query * D;
-    if (g == 0) store_agent2(pml, st.m, st.l);
+    if (g == 0) *reinterpret_cast<float2*>(pml) = make_float2(st.m, st.l);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      store_agent2(po + 16 * dt + 4 * g, st.o[dt][0], st.o[dt][1]);
-      store_agent2(po + 16 * dt + 4 * g + 2, st.o[dt][2], st.o[dt][3]);
-    }
+    for (int dt = 0; dt < D / 16; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of a head's split partials, by its last attention workgroup:
+// Merge of the split partials in a launch of its own:
 // O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s, M = max_s m_s (m in
 // log2 units; an empty split has m = -inf, l = 0).  Thread = one float4 of
-// the output at a time; every split's loads are issued before any is used.
-// The splits are folded in index order, so the result does not depend on
-// which workgroup merges.
+// the output (head, query, 4 columns), so the merge is one round of
+// independent loads spread over the whole chip; the splits are folded in
+// index order.
 // ---------------------------------------------------------------------------
-template <int D, int NT>
-__device__ __forceinline__ void merge_splits(const StepArgs& a, int head) {
-  constexpr int C4 = D / 4;
-  const int ns = a.n_split, nq = a.n_q;
-  const float* ml = a.part_ml + (int64_t)head * ns * nq * 2;
-  const float* po = a.part_o + (int64_t)head * ns * nq * D;
-  float* out = a.out + (int64_t)head * nq * D;
-  for (int e = threadIdx.x; e < nq * C4; e += NT) {
-    const int query = e / C4, c4 = e - query * C4;
-    float mv[kMaxSplit], lv[kMaxSplit];
-    float4 ov[kMaxSplit];
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {
-      mv[sp] = -INFINITY;
-      lv[sp] = 0.f;
-      ov[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (sp < ns) {  // uniform
-        const float2 m2 = load_agent2(ml + ((int64_t)sp * nq + query) * 2);
-        const float* p = po + ((int64_t)sp * nq + query) * D + 4 * c4;
-        const float2 x = load_agent2(p), y = load_agent2(p + 2);
-        mv[sp] = m2.x;
-        lv[sp] = m2.y;
-        ov[sp] = make_float4(x.x, x.y, y.x, y.y);
-      }
-    }
-    float mm = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
-    float den = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplit; ++sp) {
-      const float wv = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - mm);
-      den += wv * lv[sp];
-      acc.x += wv * ov[sp].x;
-      acc.y += wv * ov[sp].y;
-      acc.z += wv * ov[sp].z;
-      acc.w += wv * ov[sp].w;
-    }
-    const float inv = 1.0f / den;
-    *reinterpret_cast<float4*>(out + (int64_t)query * D + 4 * c4) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  }
-}
-
 template <typename T, int D, int NQT>
 __global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  __shared__ int last;
-  const int head = blockIdx.y;
-  attend_split<T, D, NQT>(a, lds, head, blockIdx.x);
-  if (!arrive_last(a.counters + head, a.n_split, &last)) return;
-  merge_splits<D, 64 * NQT * kAttendGroups>(a, head);
+  attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
 }
+
+#if !defined(WF_STEP_T)  // one compile unit holds it
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
+  constexpr int C4 = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_head = (int64_t)a.n_q * C4;
+  if (idx >= per_head * a.heads_total) return;
+  const int head = (int)(idx / per_head);
+  const int rem = (int)(idx - head * per_head);
+  const int query = rem / C4, c4 = rem - query * C4;
+  const int ns = a.n_split;
+  float mv[kMaxSplit], lv[kMaxSplit];
+  float4 ov[kMaxSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {  // every load issued before any is used
+    const bool in = sp < ns;
+    const int64_t row = ((int64_t)head * ns + (in ? sp : 0)) * a.n_q + query;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+    const float4 o = *reinterpret_cast<const float4*>(a.part_o + row * D + 4 * c4);
+    mv[sp] = in ? ml.x : -INFINITY;
+    lv[sp] = in ? ml.y : 0.f;
+    ov[sp] = in ? o : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float mm = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
+  float den = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    const float wv = (mv[sp] == -INFINITY) ? 0.f : exp2f(mv[sp] - mm);
+    den += wv * lv[sp];
+    acc.x += wv * ov[sp].x;
+    acc.y += wv * ov[sp].y;
+    acc.z += wv * ov[sp].z;
+    acc.w += wv * ov[sp].w;
+  }
+  const float inv = 1.0f / den;
+  *reinterpret_cast<float4*>(a.out + ((int64_t)head * a.n_q + query) * D + 4 * c4) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+#endif
 
 // ---------------------------------------------------------------------------
 // Launches.  This file is compiled once per (input type, head dimension,
@@ -1464,12 +1448,14 @@ hipError_t launch_select(const StepArgs& a, const SelectLaunch& L, int stage, hi
   }
   hipError_t e;
   const dim3 cover_grid(P.cover_wg, H);
+  const dim3 blk(kCoverThreads);
+  const int lds = P.cover_lds;
   if (P.stored_bands)
-    e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
-                   : launch_one(cover_bands_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+    e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, blk, lds, s, a)
+                   : launch_one(cover_bands_max_kernel<T, D, RT>, cover_grid, blk, lds, s, a);
   else
-    e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a)
-                   : launch_one(cover_max_kernel<T, D, RT>, cover_grid, dim3(kCoverThreads), P.cover_lds, s, a);
+    e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, blk, lds, s, a)
+                   : launch_one(cover_max_kernel<T, D, RT>, cover_grid, blk, lds, s, a);
   return e;
 }
 
@@ -1521,12 +1507,18 @@ static hipError_t launch_apart(const StepArgs& a, const SelectLaunch& L, int sta
   const SelectPlan& P = L.plan;
   const dim3 grid(P.heads_total), block(kSelThreads);
   if (stage == 0) {  // between the coarse and the cover launches
-    if (P.topk_s >= 1 && P.topk_s <= 4) return hipSuccess;
+    if (P.topk_s >= 1 && P.topk_s <= 4 && P.levels > 0) return hipSuccess;  // the cover workgroups take it
     return launch_one(coarse_topk_kernel, grid, block, P.coarse_lds, s, a);
   }
-  if (P.levels == 0 || P.refine_s0 == 16) return hipSuccess;  // between the cover and the attention launches
-  if (P.refine_s0 == 32) return launch_one(refine_sel_kernel, grid, block, P.cover_lds, s, a);
-  return launch_one(refine_lists_kernel, grid, block, P.refine_lds, s, a);
+  if (P.levels == 0) return hipSuccess;  // between the cover and the attention launches
+  const dim3 rblock(kRefineThreads);
+  switch (P.refine_s0) {
+    case 1: return launch_one(refine_sel_kernel<1>, grid, rblock, P.cover_lds, s, a);
+    case 2: return launch_one(refine_sel_kernel<2>, grid, rblock, P.cover_lds, s, a);
+    case 4: return launch_one(refine_sel_kernel<4>, grid, rblock, P.cover_lds, s, a);
+    case 8: return launch_one(refine_sel_kernel<8>, grid, rblock, P.cover_lds, s, a);
+    default: return launch_one(refine_lists_kernel, grid, block, P.refine_lds, s, a);
+  }
 }
 
 template <typename T, int D>
@@ -1553,7 +1545,6 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.sel_out = L.sel_out;
   a.sel_levels = L.sel_levels;
   a.score_levels = L.score_levels;
-  a.counters = reinterpret_cast<uint32_t*>(L.ws + P.off_counters);
   a.keys_top = reinterpret_cast<uint32_t*>(L.ws + P.off_keys);
   a.sel_top = reinterpret_cast<int32_t*>(L.ws + P.off_sel_top);
   a.cov = reinterpret_cast<float*>(L.ws + P.off_cov);
@@ -1607,8 +1598,13 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
       if ((e = launch_apart(a, L, stage, s)) != hipSuccess) return e;
     }
   }
-  return bf ? (d128 ? launch_rt_attend<bf16_t, 128>(rt, a, L, s) : launch_rt_attend<bf16_t, 64>(rt, a, L, s))
-            : (d128 ? launch_rt_attend<float, 128>(rt, a, L, s) : launch_rt_attend<float, 64>(rt, a, L, s));
+  e = bf ? (d128 ? launch_rt_attend<bf16_t, 128>(rt, a, L, s) : launch_rt_attend<bf16_t, 64>(rt, a, L, s))
+         : (d128 ? launch_rt_attend<float, 128>(rt, a, L, s) : launch_rt_attend<float, 64>(rt, a, L, s));
+  if (e != hipSuccess) return e;
+  const unsigned comb_blocks = (unsigned)(((int64_t)P.heads_total * P.n_q * (P.head_dim / 4) + 255) / 256);
+  if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 #endif
 
