@@ -1,25 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the WaveFilter per-step path on one MI355X.
 
-Workload: the 64K-token layer (32 heads, head dim 128, bfloat16, prompt
-N_p = 65536, generated cache N_g = 512, query block 64, Haar L = 6, budgets
-64, 118, 214, 384, 683, 1195, 2048).  One step is one pass of every stage
-of the path over one synthetic layer: wf_build_pyramid (Haar pyramid of the
-prompt keys) followed by wf_select_attend (coarse scores, coarse Top-K,
-recursive refinement, sparse attention).  Inputs are resident in HBM before
-the timed region; the loop rotates over R device copies of the layer at
-distinct addresses, so no step finds its inputs in the 256 MB last-level
-cache left by the previous one.
+Headline: wf_select_attend calls per second on the 64K-token layer (32 heads,
+head dim 128, bfloat16, prompt N_p = 65536, generated cache N_g = 512, query
+block 64, Haar L = 6, budgets 64, 118, 214, 384, 683, 1195, 2048).  One call
+is one denoising step of the path for the whole layer: coarse scores, coarse
+Top-K, recursive refinement and the sparse attention.  The pyramid is built
+once per cache refresh (wf_build_pyramid) and reused by the calls, as the
+cadence of the method has it; the build and a build + select step are
+reported beside the headline.  Inputs are resident in HBM before the timed
+region; the loop rotates over R device copies of the layer at distinct
+addresses, so no call finds its inputs in the 256 MB last-level cache left by
+the previous one.
 
-Prints one JSON line.  ``value`` is steps/s of the full step; the
-select-attend stage alone (the per-denoising-step cost when the pyramid is
-reused across steps) is reported beside it, as are both stages' HBM
-rooflines and the float64 oracle timed on a bounded sample on the host.
+Prints one JSON line.  Beside the headline: the call's HBM roofline, single
+call latency after a 1 GiB flush, the other workloads' per-layer timings (the
+128K-token sweep with all 32 layers resident), the variants (mean
+aggregation, Daubechies basis, selection reuse, incremental refresh) and the
+float64 oracle timed on the host's cores.
 """
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -30,17 +34,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "wf_select_attend steps/s + achieved HBM GB/s vs peak, 1 MI355X, 64K ctx"
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "pyramid_top_kernel_64k_pmc.txt")
-# the files pyramid_top_kernel is compiled from: counter figures taken on
-# other code are not reported
-KERNEL_SOURCES = [os.path.join(ROOT, "long_context_kv_haar_amd", "csrc", f)
-                  for f in ("wf_pyramid.hip", "wf_pyramid.h", "wf_types.h")]
+CSRC = os.path.join(ROOT, "long_context_kv_haar_amd", "csrc")
+PMC_SELECT = os.path.join(ROOT, "profiles", "select_attend_64k_pmc.txt")
+STATS_SELECT = os.path.join(ROOT, "profiles", "select_attend_64k_kernel_stats.txt")
 
 
 def kernel_source_hash():
+    """Hash of every source the select-attend kernels are compiled from (a
+    counter summary taken on other code is not reported)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:12]
+
+
+def pyramid_source_hash():
+    """Hash of the sources the pyramid build is compiled from."""
+    h = hashlib.sha256()
+    for f in ("wf_pyramid.hip", "wf_pyramid.h", "wf_types.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:12]
 
@@ -73,71 +87,94 @@ def attend_bytes(cfg):
     return BH * (cfg.n_q * d * s + 4 * k0 + 2 * (k0 + cfg.n_gen) * d * s + cfg.n_q * d * 4)
 
 
-def read_pmc_traffic():
-    """HBM bytes per pyramid launch from the committed rocprofv3 counter
-    summary, or None when it is missing or was taken on other kernel code."""
+def read_summary(path, keys, hash_key="kernel_source_sha256_12", hash_fn=kernel_source_hash):
+    """Fields of a committed profile summary, or None when it is missing or
+    was taken on other kernel code."""
     try:
-        text = open(PMC_SUMMARY).read()
+        text = open(path).read()
     except OSError:
         return None
-    m_sha = re.search(r"kernel_source_sha256_12:\s*(\w+)", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != kernel_source_hash():
+    m_sha = re.search(rf"{hash_key}:\s*(\w+)", text)
+    if not m_sha or m_sha.group(1) != hash_fn():
         return None
-    return float(m_b.group(1))
+    out = {}
+    for k in keys:
+        m = re.search(rf"{k}:\s*(\S+)", text)
+        if not m:
+            return None
+        out[k] = m.group(1)
+    return out
 
 
-def time_workload(cfg, dev, launches, warmup):
-    """Per-layer timings of one workload: wf_build_pyramid and wf_select_attend
-    each launched back to back over R device copies of one synthetic layer
-    (R sized so the copies exceed the 256 MB last-level cache where they can),
-    between one pair of HIP events on the launch stream."""
-    import math
+def make_copies(cfg, dev, R):
+    """One synthetic layer and R - 1 device copies of it at other addresses."""
+    import torch
 
+    from workloads.gen import make_layer
+
+    base = make_layer(cfg, 0, device=dev)
+    return [base] + [type(base)(cfg, 0, base.q.clone(), base.k.clone(), base.v.clone(), base.gen_idx.clone(),
+                                base.spans) for _ in range(R - 1)]
+
+
+def timed_loop(fns, launches, warmup, stream):
+    """Average duration (us) of fns[i % len(fns)]() over `launches` calls, one
+    pair of HIP events on the launch stream around them all."""
+    import torch
+
+    R = len(fns)
+    for i in range(warmup):
+        fns[i % R]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(launches):
+        fns[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / launches * 1e3
+
+
+def prepare_steps(copies, cfg, dev, agg="max", flags=0):
     import torch
 
     import long_context_kv_haar_amd as wf
-    from workloads.gen import make_layer
 
-    es = 2 if cfg.dtype == "bf16" else 4
-    BH, d, L, budgets = cfg.batch * cfg.heads, cfg.head_dim, cfg.levels, cfg.budgets
-    per_copy = BH * (2 * cfg.n_tot + cfg.n_q) * d * es
-    R = min(16, max(2, math.ceil((2 << 30) / per_copy)))
-    base = make_layer(cfg, 0, device=dev)
-    copies = [base] + [type(base)(cfg, 0, base.q.clone(), base.k.clone(), base.v.clone(), base.gen_idx.clone(),
-                                  base.spans) for _ in range(R - 1)]
-    pbytes = wf.pyramid_bytes(cfg.batch, cfg.heads, cfg.n_prompt, d, L)
-    builds, steps, ws = [], [], None
+    L, budgets = cfg.levels, cfg.budgets
+    pbytes = wf.pyramid_bytes(cfg.batch, cfg.heads, cfg.n_prompt, cfg.head_dim, L, flags)
+    builds, steps, outs, ws = [], [], [], None
     for c in copies:
-        pb = wf.PreparedBuild(c.k, cfg.n_prompt, L, torch.empty(pbytes, dtype=torch.uint8, device=dev))
+        pb = wf.PreparedBuild(c.k, cfg.n_prompt, L, torch.empty(pbytes, dtype=torch.uint8, device=dev), flags=flags)
         pyr = pb()
         if ws is None:
-            ws = torch.zeros(wf.workspace_bytes(pyr, cfg.n_q, cfg.n_gen, budgets), dtype=torch.uint8, device=dev)
-        out = torch.empty((cfg.batch, cfg.heads, cfg.n_q, d), dtype=torch.float32, device=dev)
+            ws = torch.empty(wf.workspace_bytes(pyr, cfg.n_q, cfg.n_gen, budgets), dtype=torch.uint8, device=dev)
+        out = torch.empty((cfg.batch, cfg.heads, cfg.n_q, cfg.head_dim), dtype=torch.float32, device=dev)
         sel = torch.empty((cfg.batch, cfg.heads, budgets[-1]), dtype=torch.int32, device=dev)
         builds.append(pb)
-        steps.append(wf.PreparedStep(c.q, pyr, c.k, c.v, c.gen_idx, budgets, out, sel, ws))
+        outs.append((out, sel))
+        steps.append(wf.PreparedStep(c.q, pyr, c.k, c.v, c.gen_idx, budgets, out, sel, ws, agg=agg))
+    return builds, steps, outs, ws
+
+
+def time_workload(cfg, dev, launches, warmup):
+    """Per-layer timings of one workload: its build and its select-attend call
+    each launched back to back over R device copies (R sized so the copies
+    exceed 2 GiB where 16 copies can)."""
+    import torch
+
+    es = 2 if cfg.dtype == "bf16" else 4
+    per_copy = cfg.batch * cfg.heads * (2 * cfg.n_tot + cfg.n_q) * cfg.head_dim * es
+    R = min(16, max(2, math.ceil((2 << 30) / per_copy)))
+    copies = make_copies(cfg, dev, R)
+    builds, steps, _, _ = prepare_steps(copies, cfg, dev)
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def timed(fns):
-        for i in range(warmup):
-            fns[i % R]()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(launches):
-            fns[i % R]()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / launches * 1e3  # us
-
-    build_us = timed(builds)
-    sel_us = timed(steps)
+    build_us = timed_loop(builds, launches, warmup, stream)
+    sel_us = timed_loop(steps, launches, warmup, stream)
     pyr_b, sel_b = algorithmic_bytes(cfg)
     rec = {
         "layers_x_batch_x_heads": f"{cfg.layers}x{cfg.batch}x{cfg.heads}",
-        "dtype": cfg.dtype, "n_prompt": cfg.n_prompt, "n_q": cfg.n_q, "levels": L,
-        "budgets": ",".join(map(str, budgets)),
+        "dtype": cfg.dtype, "n_prompt": cfg.n_prompt, "n_q": cfg.n_q, "levels": cfg.levels,
+        "budgets": ",".join(map(str, cfg.budgets)),
         "rotating_copies": R,
         "inputs_fit_in_last_level_cache": R * per_copy < (512 << 20),
         "build_us": round(build_us, 2),
@@ -147,41 +184,149 @@ def time_workload(cfg, dev, launches, warmup):
         "select_attend_GBps": round(sel_b / (sel_us * 1e-6) / 1e9, 1),
         "select_attend_frac_of_hbm_peak": round(sel_b / (sel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
-    if cfg.layers > 1:  # every layer has the same shape: the step of all layers
-        rec["all_layers_select_attend_ms"] = round(cfg.layers * sel_us * 1e-3, 3)
-        rec["all_layers_build_ms"] = round(cfg.layers * build_us * 1e-3, 3)
-    del builds, steps, copies, base, ws
+    del builds, steps, copies
     torch.cuda.empty_cache()
     return rec
 
 
-def cpu_baseline(inp, heads, min_seconds):
-    """The float64 oracle, unchanged, on `heads` heads of one step (one thread),
-    repeated over those heads until at least `min_seconds` of oracle time."""
+def time_sweep(cfg, dev, sweeps, warmup):
+    """The 32-layer sweep with every layer resident at once (each its own
+    seed): one step is wf_select_attend over all layers in turn."""
+    import torch
+
+    from workloads.gen import make_layer
+
+    layers = [make_layer(cfg, layer, device=dev) for layer in range(cfg.layers)]
+    builds, steps, _, _ = prepare_steps(layers, cfg, dev)
+    stream = torch.cuda.current_stream(dev)
+    build_us = timed_loop(builds, cfg.layers, cfg.layers, stream)
+    for _ in range(warmup):
+        for st in steps:
+            st()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(sweeps):
+        for st in steps:
+            st()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sweep_ms = e0.elapsed_time(e1) / sweeps
+    _, sel_b = algorithmic_bytes(cfg)
+    pyr_b, _ = algorithmic_bytes(cfg)
+    rec = {
+        "layers_resident": cfg.layers,
+        "kv_resident_GiB": round(sum(2 * x.k.numel() * x.k.element_size() for x in layers) / 2 ** 30, 1),
+        "sweep_ms": round(sweep_ms, 3),
+        "sweeps_per_s": round(1e3 / sweep_ms, 2),
+        "per_layer_us": round(sweep_ms * 1e3 / cfg.layers, 2),
+        "sweep_GBps": round(cfg.layers * sel_b / (sweep_ms * 1e-3) / 1e9, 1),
+        "sweep_frac_of_hbm_peak": round(cfg.layers * sel_b / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "build_all_layers_ms": round(build_us * cfg.layers * 1e-3, 3),
+        "build_GBps": round(pyr_b / (build_us * 1e-6) / 1e9, 1),
+    }
+    del builds, steps, layers
+    torch.cuda.empty_cache()
+    return rec
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle, as it stands, over every head of one step
+# of the 64K workload, in W worker processes with one BLAS thread each.  Each
+# worker owns a fixed set of heads (head h goes to worker h mod W), receives
+# their stored bits once, widens them to the exact float64 values, and then
+# runs its heads once per step between two barriers; a step ends when the
+# slowest worker is done.
+# ---------------------------------------------------------------------------
+def _decode_bits(arr, dtype):
+    import numpy as np
+
+    if dtype == "bf16":
+        return (np.asarray(arr, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(arr, dtype=np.float32).astype(np.float64)
+
+
+def _oracle_worker(heads, dtype, gen, n_prompt, budgets, levels, barrier, go):
     from threadpoolctl import threadpool_limits
 
     from oracle import select_attend  # the oracle is the CPU baseline
-    from workloads.gen import to_f64
+
+    data = [(_decode_bits(q, dtype), _decode_bits(k, dtype), _decode_bits(v, dtype)) for q, k, v in heads]
+    del heads
+    with threadpool_limits(limits=1):
+        barrier.wait(600)  # ready
+        while True:
+            barrier.wait(600)  # step start
+            if not go.value:
+                break
+            for q, k, v in data:
+                select_attend(q, k, v, n_prompt, gen, budgets, levels)
+            barrier.wait(600)  # step end
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, min_seconds, workers):
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
 
     cfg = inp.cfg
-    gen = inp.gen_idx.cpu().numpy()
-    data = [(to_f64(inp.q[0, h]), to_f64(inp.k[0, h]), to_f64(inp.v[0, h])) for h in heads]
-    times = []
-    with threadpool_limits(limits=1):
-        while not times or sum(times) < min_seconds:
-            for q, k, v in data:
-                t0 = time.perf_counter()
-                select_attend(q, k, v, cfg.n_prompt, gen, cfg.budgets, cfg.levels)
-                times.append(time.perf_counter() - t0)
-    per_head = sum(times) / len(times)
+    H = cfg.heads
+    host_cpus = len(os.sched_getaffinity(0))
+    W = max(1, min(H, workers or min(16, host_cpus)))
+
+    def bits(t):
+        t = t.detach().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    q, k, v = bits(inp.q[0]), bits(inp.k[0]), bits(inp.v[0])
+    gen = inp.gen_idx.cpu().numpy().astype(np.int64)
+    ctx = mp.get_context("spawn")
+    barrier, go = ctx.Barrier(W + 1), ctx.Value("i", 1)
+    procs = []
+    for w in range(W):
+        mine = [(q[h].copy(), k[h].copy(), v[h].copy()) for h in range(w, H, W)]
+        p = ctx.Process(target=_oracle_worker,
+                        args=(mine, cfg.dtype, gen, cfg.n_prompt, list(cfg.budgets), cfg.levels, barrier, go))
+        p.start()
+        procs.append(p)
+    del q, k, v
+    try:
+        barrier.wait(600)  # every worker holds its heads (a worker that died breaks the barrier)
+        steps, t0 = 0, time.perf_counter()
+        while steps == 0 or time.perf_counter() - t0 < min_seconds:
+            barrier.wait(600)
+            barrier.wait(600)
+            steps += 1
+        wall = time.perf_counter() - t0
+        go.value = 0
+        barrier.wait(600)
+    finally:
+        for p in procs:
+            p.join(timeout=60)
+            if p.is_alive():
+                p.terminate()
     return {
-        "value": 1.0 / (per_head * cfg.batch * cfg.heads),
+        "value": steps / wall,
         "unit": "steps/s",
-        "cores": 1,
+        "cores": W,
         "kind": "oracle",
-        "sample": f"{len(times)} head-calls over heads 0..{len(heads) - 1} of one step (Haar pyramid + selection "
-                  f"+ attention per head, float64 numpy, 1 thread), {sum(times):.1f} s; rate scaled to all "
-                  f"{cfg.batch * cfg.heads} heads",
+        "sample": f"{steps} steps of the 64K workload's layer ({H} heads per step: Haar pyramid, selection and "
+                  f"attention per head, float64 numpy), heads spread over {W} processes with one BLAS thread "
+                  f"each, {wall:.1f} s wall",
+        "cpu_model": cpu_model(),
+        "host_cpus": host_cpus,
+        "blas_threads_per_process": 1,
     }
 
 
@@ -191,10 +336,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=16, help="device copies of the layer rotated over")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the CPU-baseline sample (0 = skip)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="minimum oracle time of the CPU-baseline sample")
-    ap.add_argument("--workloads", type=int, default=1,
-                    help="also time every workload's build and select-attend per layer (0 = skip)")
+    ap.add_argument("--latency-calls", type=int, default=40, help="single calls timed after a 1 GiB flush (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="minimum wall time of the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-workers", type=int, default=0, help="CPU baseline processes (0 = every core)")
+    ap.add_argument("--workloads", type=int, default=1, help="also time the other workloads (0 = skip)")
+    ap.add_argument("--variants", type=int, default=1, help="also time the variants (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -208,33 +354,16 @@ def main():
 
     import long_context_kv_haar_amd as wf
     from workloads.configs import CONFIGS
-    from workloads.gen import make_layer
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
     cfg = CONFIGS[4]
-    L, budgets = cfg.levels, cfg.budgets
-    base = make_layer(cfg, 0, device=dev)
     R = max(1, args.rotate)
-    copies = [base] + [type(base)(cfg, 0, base.q.clone(), base.k.clone(), base.v.clone(), base.gen_idx.clone(),
-                                  base.spans) for _ in range(R - 1)]
-    pbytes = wf.pyramid_bytes(cfg.batch, cfg.heads, cfg.n_prompt, cfg.head_dim, L)
-    builds, steps = [], []
-    ws = None
-    outs = []
-    for c in copies:
-        pb = wf.PreparedBuild(c.k, cfg.n_prompt, L, torch.empty(pbytes, dtype=torch.uint8, device=dev))
-        pyr = pb()
-        if ws is None:
-            need = wf.workspace_bytes(pyr, cfg.n_q, cfg.n_gen, budgets)
-            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-        out = torch.empty((cfg.batch, cfg.heads, cfg.n_q, cfg.head_dim), dtype=torch.float32, device=dev)
-        sel = torch.empty((cfg.batch, cfg.heads, budgets[-1]), dtype=torch.int32, device=dev)
-        outs.append((out, sel))
-        builds.append(pb)
-        steps.append(wf.PreparedStep(c.q, pyr, c.k, c.v, c.gen_idx, budgets, out, sel, ws))
+    copies = make_copies(cfg, dev, R)
+    builds, steps, outs, ws = prepare_steps(copies, cfg, dev)
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -245,146 +374,50 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # -- full step: build + select-attend, per-stage HIP events on the launch stream
-    stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
-        builds[i % R]()
-        steps[i % R]()
-    torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
-        builds[i % R]()
-        e1.record(stream)
-        steps[i % R]()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pyr_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / K
-    sel_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / K
-
-    # -- the pyramid build alone, back to back over the copies: the kernel's average
-    #    launch duration (one event pair around all K launches, so no per-launch
-    #    event overhead)
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for i in range(args.warmup):
-        builds[i % R]()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for i in range(K):
-        builds[i % R]()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    pyr_only_ms = s0.elapsed_time(s1) / K
-
-    # -- select-attend alone (pyramids reused), rotating over the copies
-    for i in range(args.warmup):
-        steps[i % R]()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for i in range(K):
-        steps[i % R]()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    sel_only_ms = s0.elapsed_time(s1) / K
-
-    # -- select-attend with the query rows averaged instead of maximised (same bytes)
-    steps_mean = []
-    for c, pb, (out, sel) in zip(copies, builds, outs):
-        steps_mean.append(wf.PreparedStep(c.q, pb.pyramid, c.k, c.v, c.gen_idx, budgets, torch.empty_like(out),
-                                          torch.empty_like(sel), ws, agg="mean"))
-    for i in range(args.warmup):
-        steps_mean[i % R]()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for i in range(K):
-        steps_mean[i % R]()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    mean_ms = s0.elapsed_time(s1) / K
-
-    # -- incremental refresh: every copy (standing in for a layer) rebuilds 64 of its
-    #    1024 level-L blocks, all copies in one call
-    n_top = cfg.n_prompt >> L
-    gref = torch.Generator().manual_seed(7)
-    ref_items = [(c.k, pb.pyramid, torch.randperm(n_top, generator=gref)[:64].to(torch.int32).to(dev))
-                 for c, pb in zip(copies, builds)]
-    refresh = wf.PreparedRefresh(ref_items)
-    for _ in range(args.warmup):
-        refresh()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for _ in range(K):
-        refresh()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    refresh_ms = s0.elapsed_time(s1) / K
-    es = 2 if cfg.dtype == "bf16" else 4
-    refresh_units = R * cfg.batch * cfg.heads * 64
-    refresh_bytes = refresh_units * ((1 << L) * cfg.head_dim * es + cfg.head_dim * 4)
-    # restore every copy's pyramid for what follows
-    for pb in builds:
-        pb()
-    torch.cuda.synchronize()
-
-    # -- the Daubechies four-tap basis: its build stores every band (about 2 GB for this
-    #    layer), so one copy is used; finer levels are scored from the stored bands
-    db2_bytes = wf.pyramid_bytes(cfg.batch, cfg.heads, cfg.n_prompt, cfg.head_dim, L, wf.WF_PYR_DB2)
-    db2_build = wf.PreparedBuild(base.k, cfg.n_prompt, L, torch.empty(db2_bytes, dtype=torch.uint8, device=dev),
-                                 flags=wf.WF_PYR_DB2)
-    db2_build()
-    db2_out = torch.empty_like(outs[0][0])
-    db2_sel = torch.empty_like(outs[0][1])
-    db2_step = wf.PreparedStep(base.q, db2_build.pyramid, base.k, base.v, base.gen_idx, budgets, db2_out, db2_sel, ws)
-    for _ in range(args.warmup):
-        db2_step()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for _ in range(K):
-        db2_step()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    db2_ms = s0.elapsed_time(s1) / K
-    s0.record(stream)
-    db2_build()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    db2_build_ms = s0.elapsed_time(s1)
-    del db2_build, db2_step
-    torch.cuda.empty_cache()
-
-    # -- attention over the selection each copy's last call made (a later step reusing it)
-    reuse = [wf.PreparedAttend(c.q, c.k, c.v, sel, c.gen_idx, torch.empty_like(out), ws)
-             for c, (out, sel) in zip(copies, outs)]
-    for i in range(args.warmup):
-        reuse[i % R]()
-    torch.cuda.synchronize()
-    s0.record(stream)
-    for i in range(K):
-        reuse[i % R]()
-    s1.record(stream)
-    torch.cuda.synchronize()
-    reuse_ms = s0.elapsed_time(s1) / K
-    reuse_bytes = attend_bytes(cfg)
-    reuse_gbs = reuse_bytes / (reuse_ms * 1e-3) / 1e9
-
+    # -- headline: wf_select_attend alone, pyramids reused, rotating over the copies
+    t_wall = time.perf_counter()
+    sel_us = timed_loop(steps, K, args.warmup, stream)
+    t_wall = time.perf_counter() - t_wall
     pyr_bytes, sel_bytes = algorithmic_bytes(cfg)
-    pyr_gbs = pyr_bytes / (pyr_only_ms * 1e-3) / 1e9
-    sel_gbs = sel_bytes / (sel_only_ms * 1e-3) / 1e9
-    traffic = read_pmc_traffic()
+    sel_gbs = sel_bytes / (sel_us * 1e-6) / 1e9
+
+    # -- the pyramid build alone, and a build + select step
+    build_us = timed_loop(builds, K, args.warmup, stream)
+    pairs = [(lambda b=b, s=s: (b(), s())) for b, s in zip(builds, steps)]
+    step_us = timed_loop(pairs, K, args.warmup, stream)
+
+    # -- single-call latency after a 1 GiB flush
+    latency = None
+    if args.latency_calls > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lat = []
+        for i in range(args.latency_calls):
+            flush.fill_(i & 255)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            steps[i % R]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lat.append(e0.elapsed_time(e1) * 1e3)
+        del flush
+        lat.sort()
+        latency = {"calls": len(lat), "flush_bytes": 1 << 30, "p50_us": round(lat[len(lat) // 2], 2),
+                   "p90_us": round(lat[min(len(lat) - 1, (9 * len(lat)) // 10)], 2), "min_us": round(lat[0], 2)}
+
+    stats = read_summary(STATS_SELECT, ["longest_kernel", "longest_kernel_us"])
+    pmc = read_summary(PMC_SELECT, ["hbm_bytes_per_call"])
+    pmc_pyr = read_summary(PMC_SELECT, ["pyramid_hbm_bytes_per_launch"], "pyramid_source_sha256_12",
+                           pyramid_source_hash)
     rec = {
         "metric": METRIC,
-        "value": K / wall,
+        "value": 1e6 / sel_us,
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": wall / K * 1e3,
+        "ms_per_step": sel_us * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -392,66 +425,92 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "llada-64k layer: 1 x 32 heads, d=128, bf16, N_p=65536 (Student-t(4) keys, 8 planted "
-                        "spans), N_g=512, n_q=64, Haar L=6, budgets " + ",".join(map(str, budgets))
-                        + "; step = wf_build_pyramid + wf_select_attend",
+                        "spans), N_g=512, n_q=64, Haar L=6, budgets " + ",".join(map(str, cfg.budgets))
+                        + "; step = one wf_select_attend call (pyramid built once per cache refresh and reused)",
             "rotating_copies": R,
         },
         "roofline": {
-            "kernel": "pyramid_top_kernel (wf_build_pyramid)",
+            "kernel": "wf_select_attend (coarse, cover, refine, attend, combine launches)",
             "bound": "hbm",
-            "achieved": round(pyr_gbs, 1),
+            "achieved": round(sel_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(pyr_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes": pyr_bytes,
-            "avg_launch_us": round(pyr_only_ms * 1e3, 2),
-            "us_in_step": round(pyr_ms * 1e3, 2),
-        },
-        "select_attend": {
-            "calls_per_s": 1e3 / sel_only_ms,
-            "us_per_call": round(sel_only_ms * 1e3, 2),
-            "us_per_call_in_step": round(sel_ms * 1e3, 2),
+            "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
+            "traffic": float(pmc["hbm_bytes_per_call"]) if pmc else None,
             "algorithmic_bytes": sel_bytes,
-            "achieved_GBps": round(sel_gbs, 1),
-            "frac_of_hbm_peak": round(sel_gbs / HBM_PEAK_GBS, 4),
+            "avg_call_us": round(sel_us, 2),
+            "longest_kernel": stats["longest_kernel"] if stats else None,
+            "longest_kernel_us": float(stats["longest_kernel_us"]) if stats else None,
         },
-        "select_attend_mean_rows": {
-            "calls_per_s": 1e3 / mean_ms,
-            "us_per_call": round(mean_ms * 1e3, 2),
-            "achieved_GBps": round(sel_bytes / (mean_ms * 1e-3) / 1e9, 1),
+        "latency_after_flush": latency,
+        "pyramid_build": {
+            "kernel": "pyramid_top_kernel (wf_build_pyramid)",
+            "us_per_call": round(build_us, 2),
+            "algorithmic_bytes": pyr_bytes,
+            "achieved_GBps": round(pyr_bytes / (build_us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(pyr_bytes / (build_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": float(pmc_pyr["pyramid_hbm_bytes_per_launch"]) if pmc_pyr else None,
         },
-        "refresh_pyramids": {
-            "layers": R,
-            "blocks_per_layer": 64,
-            "us_per_call": round(refresh_ms * 1e3, 2),
-            "algorithmic_bytes": refresh_bytes,
-            "achieved_GBps": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9, 1),
-            "frac_of_hbm_peak": round(refresh_bytes / (refresh_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        },
-        "select_attend_db2": {
-            "us_per_call": round(db2_ms * 1e3, 2),
-            "pyramid_build_us": round(db2_build_ms * 1e3, 1),
-            "note": "one copy (the stored bands take about 2 GB), so its inputs may sit in the MALL",
-        },
-        "attend_selected": {
-            "calls_per_s": 1e3 / reuse_ms,
-            "us_per_call": round(reuse_ms * 1e3, 2),
-            "algorithmic_bytes": reuse_bytes,
-            "achieved_GBps": round(reuse_gbs, 1),
-            "frac_of_hbm_peak": round(reuse_gbs / HBM_PEAK_GBS, 4),
+        "build_plus_select": {
+            "us_per_step": round(step_us, 2),
+            "steps_per_s": round(1e6 / step_us, 1),
         },
         "kernel_source_sha256_12": kernel_source_hash(),
+        "timed_region_wall_s": round(t_wall, 4),
     }
+
+    if args.variants:
+        # -- select-attend with the query rows averaged instead of maximised (same bytes)
+        _, steps_mean, _, _ = prepare_steps(copies, cfg, dev, agg="mean")
+        mean_us = timed_loop(steps_mean, K, args.warmup, stream)
+        rec["select_attend_mean_rows"] = {"us_per_call": round(mean_us, 2), "calls_per_s": round(1e6 / mean_us, 1),
+                                          "achieved_GBps": round(sel_bytes / (mean_us * 1e-6) / 1e9, 1)}
+        del steps_mean
+        # -- selection reuse: attention over the kept sets the timed calls returned
+        reuse = [wf.PreparedAttend(c.q, c.k, c.v, sel, c.gen_idx, torch.empty_like(out), ws)
+                 for c, (out, sel) in zip(copies, outs)]
+        reuse_us = timed_loop(reuse, K, args.warmup, stream)
+        rb = attend_bytes(cfg)
+        rec["attend_selected"] = {"us_per_call": round(reuse_us, 2), "calls_per_s": round(1e6 / reuse_us, 1),
+                                  "algorithmic_bytes": rb,
+                                  "achieved_GBps": round(rb / (reuse_us * 1e-6) / 1e9, 1),
+                                  "frac_of_hbm_peak": round(rb / (reuse_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del reuse
+        # -- incremental refresh: every copy (standing in for a layer) rebuilds 64 of its
+        #    1024 level-L blocks, all copies in one call
+        n_top = cfg.n_prompt >> cfg.levels
+        gref = torch.Generator().manual_seed(7)
+        items = [(c.k, pb.pyramid, torch.randperm(n_top, generator=gref)[:64].to(torch.int32).to(dev))
+                 for c, pb in zip(copies, builds)]
+        refresh = wf.PreparedRefresh(items)
+        refresh_us = timed_loop([refresh], K, args.warmup, stream)
+        es = 2 if cfg.dtype == "bf16" else 4
+        refresh_bytes = R * cfg.batch * cfg.heads * 64 * ((1 << cfg.levels) * cfg.head_dim * es + cfg.head_dim * 4)
+        rec["refresh_pyramids"] = {"layers": R, "blocks_per_layer": 64, "us_per_call": round(refresh_us, 2),
+                                   "algorithmic_bytes": refresh_bytes,
+                                   "achieved_GBps": round(refresh_bytes / (refresh_us * 1e-6) / 1e9, 1),
+                                   "frac_of_hbm_peak": round(refresh_bytes / (refresh_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                             4)}
+        del refresh, items
+        # -- the Daubechies four-tap basis: its build stores every band (about 2 GB for
+        #    this layer), so two copies are used; finer levels are scored from the bands
+        b_db2, s_db2, _, _ = prepare_steps(copies[:2], cfg, dev, flags=wf.WF_PYR_DB2)
+        db2_us = timed_loop(s_db2, K, args.warmup, stream)
+        db2_build_us = timed_loop(b_db2, 4, 1, stream)
+        rec["select_attend_db2"] = {"us_per_call": round(db2_us, 2), "pyramid_build_us": round(db2_build_us, 1),
+                                    "rotating_copies": 2}
+        del b_db2, s_db2
+    del builds, steps, outs, ws
+    base = copies[0]
+    del copies
+    torch.cuda.empty_cache()
+
     if args.workloads:
-        # the other workloads (the 1K, 4K, 16K and 128K-sweep layers are parity cases; their
-        # timings are reported here, not as bench lines)
-        del steps, builds, steps_mean, reuse, refresh, ref_items, copies, ws, outs
-        torch.cuda.empty_cache()
-        rec["workloads"] = {CONFIGS[c].name: time_workload(CONFIGS[c], dev, 100 if c < 5 else 40, 10)
-                            for c in sorted(CONFIGS)}
-    if args.cpu_heads > 0:
-        rec["cpu_baseline"] = cpu_baseline(base, list(range(min(args.cpu_heads, cfg.heads))), args.cpu_seconds)
+        # the other workloads are parity cases; their timings are report lines, not bench lines
+        rec["workloads"] = {CONFIGS[c].name: time_workload(CONFIGS[c], dev, 100, 10) for c in (1, 2, 3, 4)}
+        rec["sweep_128k_32_layers"] = time_sweep(CONFIGS[5], dev, 10, 1)
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds, args.cpu_workers)
     print(json.dumps(rec), flush=True)
 
 
