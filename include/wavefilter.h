@@ -20,9 +20,10 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are HIP device memory owned by the caller; the library
- *     never allocates, frees or synchronises, and keeps no mutable global
- *     state.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
- *     stream) and completes asynchronously.
+ *     never allocates, frees or synchronises.  Its only global state is the
+ *     static scratch array of wf_select_attend_noalloc (one per device) and
+ *     that array's looked-up address.  Work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the null stream) and completes asynchronously.
  *   - Arguments are checked on the host before anything is enqueued; on an
  *     error the call returns a negative status and enqueues nothing, and the
  *     outputs are untouched.  A failed kernel launch returns WF_ERR_HIP.
@@ -52,7 +53,7 @@ enum {
     WF_ERR_BUDGET = -5,    /* per-level keep counts infeasible or beyond the supported size */
     WF_ERR_WORKSPACE = -6, /* workspace or pyramid buffer too small */
     WF_ERR_ALIGN = -7,     /* a pointer or stride is not 16-byte aligned */
-    WF_ERR_HIP = -8,       /* a HIP launch failed */
+    WF_ERR_HIP = -8,       /* a HIP launch or runtime call failed */
     WF_ERR_PYRAMID = -9,   /* pyramid descriptor not built by wf_build_pyramid */
     WF_ERR_OPTION = -10    /* an option argument has no defined meaning */
 };
@@ -240,6 +241,33 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
                      int32_t n_q, int32_t aggregation, float* out, int32_t* sel_out,
                      int32_t* sel_levels, float* score_levels, void* workspace, uint64_t ws_bytes,
                      void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * wf_select_attend with the workspace taken from a static device array of
+ * WF_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends.  Arguments, outputs, results and errors are
+ * those of wf_select_attend, and the same kernels run.  The call allocates
+ * and frees nothing; its first call on a device looks up that device's copy
+ * of the array (with the stream's device made current for the lookup, then
+ * restored), so a caller that captures should make one call beforehand.
+ *
+ *   stream       the device of the stream (the current device for the null
+ *                stream) decides whose scratch array is used
+ * Returns WF_ERR_WORKSPACE, before anything is enqueued, when the call's
+ * workspace (wf_select_attend_workspace_bytes) exceeds
+ * WF_NOALLOC_SCRATCH_BYTES; WF_ERR_HIP when the array cannot be located.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind: calls that overlap on one device (on different streams,
+ * or from several host threads onto streams that are not ordered) race and
+ * must be serialised by the caller, e.g. by issuing them on one stream.
+ */
+#define WF_NOALLOC_SCRATCH_BYTES (16u << 20)
+int wf_select_attend_noalloc(const void* q, const wf_pyramid* pyr, const void* k, const void* v,
+                             int32_t n_tot, const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets,
+                             int32_t n_q, int32_t aggregation, float* out, int32_t* sel_out,
+                             int32_t* sel_levels, float* score_levels, void* stream);
 
 /*
  * Bytes of workspace wf_attend_selected needs, or 0 if the arguments are

@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     pyramid_bytes,
     refresh_pyramids,
     select_attend,
+    select_attend_noalloc,
     split_levels,
     status_string,
     version,

@@ -91,6 +91,8 @@ def lib():
         L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p]
         L.wf_select_attend.restype = ctypes.c_int
         L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp, u64, vp]
+        L.wf_select_attend_noalloc.restype = ctypes.c_int
+        L.wf_select_attend_noalloc.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp]
         L.wf_refresh_pyramids.restype = ctypes.c_int
         L.wf_refresh_pyramids.argtypes = [ctypes.POINTER(WfRefreshItem), i32, vp]
         L.wf_attend_selected_workspace_bytes.restype = u64
@@ -386,6 +388,34 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
         res["sel_levels"] = sel_levels
         res["score_levels"] = score_levels
     return res
+
+
+def select_attend_noalloc(q, pyr, k, v, gen_idx, budgets, out, sel_out=None, sel_levels=None, score_levels=None,
+                          agg="max"):
+    """``select_attend`` through ``wf_select_attend_noalloc``: the workspace is
+    the library's static per-device scratch array, and the caller passes
+    every output (``out`` float32 ``[B, H, n_q, d]``; optional ``sel_out``
+    int32 ``[B, H, k_0]``, ``sel_levels`` int32 / ``score_levels`` float32
+    ``[B, H, sum k_j]``), so nothing is allocated by this call.  Calls that
+    overlap on one device race on the scratch array."""
+    agg_code = _agg_code(agg)
+    _need(isinstance(q, torch.Tensor) and q.is_cuda, "q must be a device tensor")
+    _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
+    _need(out is not None, "out must be passed (this call allocates nothing)")
+    budgets = [int(b) for b in budgets]
+    _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out, sel_levels, score_levels)
+    n_q, n_tot = q.shape[2], k.shape[2]
+    n_gen = 0 if gen_idx is None else gen_idx.numel()
+
+    def ptr(t):
+        return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+    st = lib().wf_select_attend_noalloc(ptr(q), ctypes.byref(pyr.desc), ptr(k), ptr(v), n_tot, ptr(gen_idx), n_gen,
+                                        _budget_array(budgets), n_q, agg_code, ptr(out), ptr(sel_out),
+                                        ptr(sel_levels), ptr(score_levels), _stream_handle(q.device))
+    if st != WF_OK:
+        raise WfError(st, "wf_select_attend_noalloc")
+    return {"out": out, "sel": sel_out, "sel_levels": sel_levels, "score_levels": score_levels}
 
 
 def attend_selected_workspace_bytes(batch, heads, head_dim, dtype_code, n_q, k0, n_gen):

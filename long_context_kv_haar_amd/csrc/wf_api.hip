@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/wavefilter.h"
 #include "wf_internal.h"
 
@@ -195,6 +197,46 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
 
 }  // namespace
 
+// Scratch of wf_select_attend_noalloc: one array per device (each GPU holds
+// its own copy at its own address), kept until the process ends.  Host code
+// never uses this name as an address: it uses the pointer that
+// hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) uint8_t scratch[WF_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, looked up once per device
+
+// The device address of `scratch` on the device that owns `stream` (the
+// current device for the null stream), looked up on first use with that
+// device current.
+int device_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return WF_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return WF_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return WF_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return WF_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return WF_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return WF_ERR_HIP;
+    if (e != hipSuccess || !p) return WF_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return WF_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* wf_version(void) { return "wavefilter-gfx950 0.1.0"; }
@@ -209,7 +251,7 @@ const char* wf_status_string(int status) {
     case WF_ERR_BUDGET: return "per-level keep counts infeasible or beyond the supported size";
     case WF_ERR_WORKSPACE: return "workspace or pyramid buffer too small";
     case WF_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
-    case WF_ERR_HIP: return "HIP launch failed";
+    case WF_ERR_HIP: return "HIP launch or runtime call failed";
     case WF_ERR_PYRAMID: return "pyramid descriptor not built by wf_build_pyramid";
     case WF_ERR_OPTION: return "an option argument has no defined meaning";
     default: return "unknown status";
@@ -363,6 +405,22 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
   a.ws = reinterpret_cast<uint8_t*>(workspace);
   if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;
+}
+
+int wf_select_attend_noalloc(const void* q, const wf_pyramid* pyr, const void* k, const void* v, int32_t n_tot,
+                             const int32_t* gen_idx, int32_t n_gen, const int32_t* budgets, int32_t n_q,
+                             int32_t aggregation, float* out, int32_t* sel_out, int32_t* sel_levels,
+                             float* score_levels, void* stream) {
+  if (!q || !pyr || !k || !v || !out || !budgets) return WF_ERR_NULL;
+  wf::SelectPlan P;
+  const int st = make_plan(pyr, n_q, n_gen, budgets, &P);
+  if (st != WF_OK) return st;
+  if (P.total > WF_NOALLOC_SCRATCH_BYTES) return WF_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int sst = device_scratch(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (sst != WF_OK) return sst;
+  return wf_select_attend(q, pyr, k, v, n_tot, gen_idx, n_gen, budgets, n_q, aggregation, out, sel_out, sel_levels,
+                          score_levels, ws, WF_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 uint64_t wf_attend_selected_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype,

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -287,3 +287,42 @@ def test_public_calls_reject_host_tensors_before_the_library():
         wf.select_attend(a["q"], _FakePyr(), a["k"], a["v"], a["gen_idx"], a["budgets"])
     with pytest.raises(ValueError):
         wf.attend_selected(a["q"], a["k"], a["v"], None, a["gen_idx"])
+
+
+def noalloc_scratch_bytes():
+    m = re.search(r"#define\s+WF_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_scratch_holds_every_workload():
+    from workloads.configs import CONFIGS
+    cap = noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    for c in CONFIGS.values():
+        p = fake_pyramid(levels=c.levels, n=c.n_prompt, d=c.head_dim, H=c.batch * c.heads,
+                         dt=wf.WF_BF16 if c.dtype == "bf16" else wf.WF_F32)
+        need = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), c.n_q, c.n_gen, budgets_arr(c.budgets))
+        assert 0 < need <= cap, (c.name, need)
+
+
+def noalloc(p, budgets, n_q=32, n_gen=32, out=FAKE, q=FAKE, agg=wf.WF_AGG_MAX):
+    return lib().wf_select_attend_noalloc(ctypes.c_void_p(q), ctypes.byref(p), ctypes.c_void_p(FAKE),
+                                          ctypes.c_void_p(FAKE), 1 << 20, ctypes.c_void_p(FAKE), n_gen,
+                                          budgets_arr(budgets), n_q, agg, ctypes.c_void_p(out), None, None, None, None)
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch_before_any_device_call():
+    # 2 048 heads of a 1K prompt: the split partials alone exceed the scratch array
+    p = fake_pyramid(levels=3, n=1024, d=64, H=2048)
+    need = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]))
+    assert need > noalloc_scratch_bytes()
+    assert noalloc(p, [8, 16, 32, 64]) == -6                  # WF_ERR_WORKSPACE
+
+
+def test_noalloc_checks_its_arguments_like_the_workspace_call():
+    p = fake_pyramid()
+    assert noalloc(p, [8, 16, 32, 64], q=0) == -1              # WF_ERR_NULL
+    assert noalloc(p, [8, 16, 32, 64], out=0) == -1
+    assert noalloc(p, [8, 17, 32, 64]) == -5                   # k_2 > 2 k_3: WF_ERR_BUDGET
+    assert noalloc(p, [8, 16, 32, 64], n_q=65) == -2           # WF_ERR_SHAPE
+    assert noalloc(fake_pyramid(magic=0), [8, 16, 32, 64]) == -9  # WF_ERR_PYRAMID
