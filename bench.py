@@ -162,6 +162,8 @@ def time_workload(cfg, dev, launches, warmup):
     exceed 2 GiB where 16 copies can)."""
     import torch
 
+    from workloads.configs import budget_reading
+
     es = 2 if cfg.dtype == "bf16" else 4
     per_copy = cfg.batch * cfg.heads * (2 * cfg.n_tot + cfg.n_q) * cfg.head_dim * es
     R = min(16, max(2, math.ceil((2 << 30) / per_copy)))
@@ -175,6 +177,7 @@ def time_workload(cfg, dev, launches, warmup):
         "layers_x_batch_x_heads": f"{cfg.layers}x{cfg.batch}x{cfg.heads}",
         "dtype": cfg.dtype, "n_prompt": cfg.n_prompt, "n_q": cfg.n_q, "levels": cfg.levels,
         "budgets": ",".join(map(str, cfg.budgets)),
+        "budget_reading": budget_reading(cfg),
         "rotating_copies": R,
         "inputs_fit_in_last_level_cache": R * per_copy < (512 << 20),
         "build_us": round(build_us, 2),
@@ -341,6 +344,8 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=0, help="CPU baseline processes (0 = every core)")
     ap.add_argument("--workloads", type=int, default=1, help="also time the other workloads (0 = skip)")
     ap.add_argument("--variants", type=int, default=1, help="also time the variants (0 = skip)")
+    ap.add_argument("--c3-reading", choices=["capped", "full", "both"], default="both",
+                    help="reading(s) of the 16K workload's budgets in the workloads record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -353,7 +358,7 @@ def main():
     import torch
 
     import long_context_kv_haar_amd as wf
-    from workloads.configs import CONFIGS
+    from workloads.configs import C3_READINGS, CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -507,7 +512,9 @@ def main():
 
     if args.workloads:
         # the other workloads are parity cases; their timings are report lines, not bench lines
-        rec["workloads"] = {CONFIGS[c].name: time_workload(CONFIGS[c], dev, 100, 10) for c in (1, 2, 3, 4)}
+        readings = ["capped", "full"] if args.c3_reading == "both" else [args.c3_reading]
+        cfgs = [CONFIGS[1], CONFIGS[2]] + [C3_READINGS[r] for r in readings] + [CONFIGS[4]]
+        rec["workloads"] = {c.name: time_workload(c, dev, 100, 10) for c in cfgs}
         rec["sweep_128k_32_layers"] = time_sweep(CONFIGS[5], dev, 10, 1)
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds, args.cpu_workers)

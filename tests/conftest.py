@@ -8,6 +8,21 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def pytest_addoption(parser):
+    parser.addoption("--c3-reading", choices=["capped", "full", "both"], default="both",
+                     help="reading of the 16K workload's budgets the parity tests run (default: both)")
+
+
+def c3_readings(config):
+    r = config.getoption("--c3-reading")
+    return ["capped", "full"] if r == "both" else [r]
+
+
+def pytest_generate_tests(metafunc):
+    if "c3_reading" in metafunc.fixturenames:
+        metafunc.parametrize("c3_reading", c3_readings(metafunc.config))
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")

@@ -26,6 +26,20 @@ def test_budgets(cid):
     assert check_budgets(cfg.n_prompt, cfg.levels, cfg.budgets)
 
 
+def test_the_16k_workload_has_two_budget_readings():
+    from workloads.configs import C3_READINGS, budget_reading
+    capped, full = C3_READINGS["capped"], C3_READINGS["full"]
+    assert capped is CONFIGS[3] and capped.budgets == EXPECTED_BUDGETS[3]
+    # coarse top-16 dropped: k_L = min(512, 2 ceil(1024 / 32)) = 64, and k_0 reaches B = 1 024
+    assert full.budgets == [64, 116, 205, 359, 615, 1024]
+    assert check_budgets(full.n_prompt, full.levels, full.budgets)
+    assert budget_reading(capped) == "capped" and budget_reading(full) == "full"
+    assert budget_reading(CONFIGS[4]) is None
+    # same inputs under both readings
+    a, b = make_layer(capped, 0), make_layer(full, 0)
+    assert torch.equal(a.k, b.k) and torch.equal(a.q, b.q)
+
+
 def test_budget_rule_edges():
     assert resolve_budgets(64, 0, 16) == [16]
     assert resolve_budgets(64, 6, 64) == [1, 2, 4, 8, 16, 32, 64]

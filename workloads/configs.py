@@ -12,7 +12,7 @@ library.
 This module holds configuration only; it computes nothing of the method.
 """
 
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 import math
 
 
@@ -58,6 +58,28 @@ CONFIGS = {
     5: Config(5, "llada-128k-32layer-b2", 32, 2, 32, 128, "bf16", 32, 131072, 512, 7, 4096, 0,
               16, (32, 32), 2.5, 0.1, "normal"),
 }
+
+
+# The 16K workload names both a coarse Top-K of 16 and a final budget of
+# 1 024, which 16 regions of 32 tokens cannot reach.  Two readings:
+#   "capped": the coarse Top-K is honoured and the final budget is a cap
+#             (k_0 = 512), the default;
+#   "full":   the coarse Top-K is dropped and the default rule picks
+#             k_L = 64, so that k_0 = 1 024 is reached.
+# Both run on the same inputs (same workload id, same seeds); every result
+# names the reading it used.
+C3_READINGS = {
+    "capped": CONFIGS[3],
+    "full": replace(CONFIGS[3], name="llada-16k-full-budget", coarse_k=0),
+}
+
+
+def budget_reading(cfg):
+    """The reading of the 16K workload's budgets that ``cfg`` uses, or None
+    for the other workloads."""
+    if cfg.cid != 3:
+        return None
+    return "full" if cfg.coarse_k == 0 else "capped"
 
 
 def resolve_budgets(n_prompt, levels, final_budget, coarse_k=0):
