@@ -26,7 +26,8 @@ notes): orthonormal Haar filters; the pair (x[2n], x[2n+1]) forms coefficient
 n, so level-j coefficient n covers tokens [n 2^j, (n+1) 2^j) and has exactly
 the children 2n, 2n+1; the score of a region is the maximum over the query
 rows of the scaled dot product with its approximation coefficient (or, as
-the variant "mean", its average over the rows); only the
+the variant "mean", its average over the rows; or the maximum or average of
+the rows' softmax probabilities over the level's candidates); only the
 two children of a selected region become candidates at the next finer level;
 ties go to the lower index; the generated positions are always attended and
 never scored; no mask.
@@ -160,7 +161,7 @@ def haar_reconstruct(a_top, details):
     return x
 
 
-AGGREGATIONS = ("max", "mean")
+AGGREGATIONS = ("max", "mean", "softmax_max", "softmax_mean")
 
 
 def refresh_top(a_top, k_prompt_new, blocks, levels):
@@ -189,6 +190,13 @@ def level_scores(q, coeff_rows, agg="max"):
     keys is the "correlation" of Figure 2 (c); the 1/sqrt(d) factor is the
     one of eq. 3; how the query block is combined is not stated on the
     pages: the maximum is the main reading, the mean a variant.
+
+    The variants "softmax_max" and "softmax_mean" score with attention
+    probabilities instead of logits (section 1 speaks of the attention the
+    queries pay to key regions): each row's logits are normalised by a
+    softmax over the m candidates passed in (the level's candidate set),
+    ``p_i[c] = exp(l_ic) / sum_c' exp(l_ic')``, and ``s[c]`` is the maximum
+    or the mean over i of ``p_i[c]``.
     """
     if agg not in AGGREGATIONS:
         raise ValueError("unknown aggregation")
@@ -196,7 +204,14 @@ def level_scores(q, coeff_rows, agg="max"):
     coeff_rows = np.asarray(coeff_rows, dtype=np.float64)
     d = q.shape[1]
     logits = q @ coeff_rows.T / math.sqrt(d)
-    return logits.max(axis=0) if agg == "max" else logits.mean(axis=0)
+    if agg == "max":
+        return logits.max(axis=0)
+    if agg == "mean":
+        return logits.mean(axis=0)
+    # softmax of every row over the candidates (max-subtracted for range safety)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return p.max(axis=0) if agg == "softmax_max" else p.mean(axis=0)
 
 
 def top_k(candidates, scores, k):

@@ -239,3 +239,81 @@ def test_duplicated_row_moves_the_mean_not_the_max():
     assert np.allclose(level_scores(q_dup, a, "mean"), want, atol=1e-12)
     with pytest.raises(ValueError):
         level_scores(q, a, "median")
+
+
+# -- the softmax-probability aggregations ------------------------------------
+# p_i[c] = exp(l_ic) / sum over the level's candidates c' of exp(l_ic'),
+# l_ic = q_i . a_c / sqrt(d); the score is max_i p_i[c] or mean_i p_i[c].
+
+def test_softmax_scores_are_the_direct_loop():
+    """Both softmax aggregations written out with scalar exp and sums, the
+    normaliser taken over the candidates (columns), not over the rows."""
+    rng = np.random.default_rng(31)
+    n_q, m, d = 4, 6, 8
+    q = rng.standard_normal((n_q, d))
+    a = rng.standard_normal((m, d))
+    p = [[0.0] * m for _ in range(n_q)]
+    for i in range(n_q):
+        logit = [sum(q[i, t] * a[c, t] for t in range(d)) / math.sqrt(d) for c in range(m)]
+        z = sum(math.exp(x) for x in logit)
+        for c in range(m):
+            p[i][c] = math.exp(logit[c]) / z
+    got_max = level_scores(q, a, "softmax_max")
+    got_mean = level_scores(q, a, "softmax_mean")
+    for c in range(m):
+        assert abs(got_max[c] - max(p[i][c] for i in range(n_q))) < 1e-14
+        assert abs(got_mean[c] - sum(p[i][c] for i in range(n_q)) / n_q) < 1e-14
+    # every row's probabilities sum to one, so the mean scores do too
+    assert abs(got_mean.sum() - 1.0) < 1e-12
+
+
+def test_one_row_softmax_max_selects_what_the_logit_max_selects():
+    """With one query row the softmax is a monotone map of the row's logits
+    over the candidates, so both aggregations keep the same regions at every
+    level (the candidates of a level depend only on the previous choice)."""
+    rng = np.random.default_rng(32)
+    for levels, n_p, budgets in [(3, 256, [5, 9, 16, 30]), (4, 512, [6, 10, 17, 30, 50]), (0, 64, [20])]:
+        q = rng.standard_normal((1, 16))
+        kp = rng.standard_normal((n_p, 16))
+        for agg in ("softmax_max", "softmax_mean"):
+            soft = select(q, kp, budgets, levels, agg)
+            hard = select(q, kp, budgets, levels, "max")
+            for j in range(levels + 1):
+                assert list(soft.sel[j]) == list(hard.sel[j])
+
+
+def test_softmax_mean_and_logit_mean_pick_different_regions():
+    """Hand-worked, d = 2, rows q_1 = (1, 0) and q_2 = (0, 1); coefficient
+    c = sqrt2 (x_c, y_c), so the logits are exactly x_c (row 1) and y_c
+    (row 2).  x = (ln 8, 0, 0), y = (0, ln 20, ln 29):
+      row 1 probabilities 8/10, 1/10, 1/10; row 2 1/50, 20/50, 29/50;
+      softmax mean (0.41, 0.25, 0.34) and softmax max (0.8, 0.4, 0.58) keep c0;
+      logit mean (ln 8/2, ln 20/2, ln 29/2) and logit max keep c2."""
+    r2 = math.sqrt(2.0)
+    q = np.array([[1.0, 0.0], [0.0, 1.0]])
+    a = r2 * np.array([[math.log(8), 0.0], [0.0, math.log(20)], [0.0, math.log(29)]])
+    assert np.allclose(level_scores(q, a, "softmax_mean"), [0.41, 0.25, 0.34], atol=1e-14)
+    assert np.allclose(level_scores(q, a, "softmax_max"), [0.8, 0.4, 0.58], atol=1e-14)
+    assert np.allclose(level_scores(q, a, "mean"), [math.log(8) / 2, math.log(20) / 2, math.log(29) / 2])
+    assert list(select(q, a, [1], 0, "softmax_mean").sel[0]) == [0]
+    assert list(select(q, a, [1], 0, "softmax_max").sel[0]) == [0]
+    assert list(select(q, a, [1], 0, "mean").sel[0]) == [2]
+    assert list(select(q, a, [1], 0, "max").sel[0]) == [2]
+
+
+def test_a_constant_added_to_one_rows_logits_changes_nothing():
+    """Shift invariance of each row's softmax: an extra coordinate that is 1
+    in every coefficient and t in one query row adds t/sqrt(d) to that row's
+    logits of every candidate.  The softmax scores do not move (the logit
+    scores do, which shows the change reaches the logits)."""
+    rng = np.random.default_rng(33)
+    n_q, m, d = 5, 7, 9
+    q = rng.standard_normal((n_q, d))
+    q[:, -1] = 0.0
+    a = rng.standard_normal((m, d))
+    a[:, -1] = 1.0
+    q_shift = q.copy()
+    q_shift[2, -1] = 4.0
+    for agg in ("softmax_max", "softmax_mean"):
+        assert np.allclose(level_scores(q_shift, a, agg), level_scores(q, a, agg), rtol=0, atol=1e-14)
+    assert not np.allclose(level_scores(q_shift, a, "mean"), level_scores(q, a, "mean"))
