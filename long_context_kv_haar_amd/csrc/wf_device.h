@@ -14,16 +14,27 @@
 
 namespace wf {
 
-// Round-to-nearest-even float32 -> bfloat16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two float32 values -> a packed bfloat16 pair (a in the low half), rounded
+// to nearest even by the hardware conversion (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// a and b as bfloat16 hi + lo pairs: hi = bf16(x), lo = bf16(x - hi), packed
+// two per word like cvt_pk_bf16 (hi + lo carries 16 significant bits).
+struct Bf16Split {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Bf16Split split_pk_bf16(float a, float b) {
+  const uint32_t hi = cvt_pk_bf16(a, b);
+  return {hi, cvt_pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u))};
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
-
-__device__ __forceinline__ uint32_t pack_bf16(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
 // ---------------------------------------------------------------------------
 // MFMA 16x16 tiles.  D[i][j] += sum_k A[i][k] B[k][j]; lane l supplies row

@@ -103,36 +103,41 @@ template <typename T> struct QueryLds;
 template <> struct QueryLds<bf16_t> { static constexpr int PAD = 8; };
 template <> struct QueryLds<float> { static constexpr int PAD = 4; };
 
-template <typename T, int D, int NT>
-__device__ __forceinline__ void stage_query(const T* qh, int n_q, T* qs) {
-  constexpr int VE = 16 / sizeof(T), NV = D / VE, QS = D + QueryLds<T>::PAD;
-  for (int e = threadIdx.x; e < n_q * NV; e += NT) {
-    const int row = e / NV, cv = e - row * NV;
-    *reinterpret_cast<u32x4*>(qs + row * QS + cv * VE) = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * D + cv * VE);
+// Query rows staged in LDS with every load of a thread issued (clamped in
+// bounds) before the first LDS store: one round trip for the block instead
+// of one per vector.  issue() loads a thread's vectors into registers and
+// store() writes them to LDS, so that other work can run in between while
+// the loads are in flight.
+template <typename T, int D, int NT, int RT>
+struct QueryStage {
+  static constexpr int VE = 16 / sizeof(T), NV = D / VE, QS = D + QueryLds<T>::PAD;
+  static constexpr int IT = (16 * RT * NV + NT - 1) / NT;  // n_q <= 16 RT
+  u32x4 v[IT];
+  __device__ __forceinline__ void issue(const T* qh, int n_q) {
+    const int total = n_q * NV;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int e = min((int)threadIdx.x + i * NT, total - 1);
+      const int row = e / NV, cv = e - row * NV;
+      v[i] = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * D + cv * VE);
+    }
   }
-}
+  __device__ __forceinline__ void store(int n_q, T* qs) const {
+    const int total = n_q * NV;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int e = (int)threadIdx.x + i * NT;
+      const int row = e / NV, cv = e - row * NV;
+      if (e < total) *reinterpret_cast<u32x4*>(qs + row * QS + cv * VE) = v[i];
+    }
+  }
+};
 
-// The same with every load of a thread issued (clamped in bounds) before the
-// first LDS store: one round trip for the block instead of one per vector
-// (the coarse kernel, where nothing else overlaps the staging).
 template <typename T, int D, int NT, int RT>
 __device__ __forceinline__ void stage_query_batched(const T* qh, int n_q, T* qs) {
-  constexpr int VE = 16 / sizeof(T), NV = D / VE, QS = D + QueryLds<T>::PAD;
-  constexpr int IT = (16 * RT * NV + NT - 1) / NT;  // n_q <= 16 RT
-  const int total = n_q * NV;
-  u32x4 v[IT];
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int e = min((int)threadIdx.x + i * NT, total - 1);
-    const int row = e / NV, cv = e - row * NV;
-    v[i] = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * D + cv * VE);
-  }
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int e = (int)threadIdx.x + i * NT;
-    const int row = e / NV, cv = e - row * NV;
-    if (e < total) *reinterpret_cast<u32x4*>(qs + row * QS + cv * VE) = v[i];
-  }
+  QueryStage<T, D, NT, RT> st;
+  st.issue(qh, n_q);
+  st.store(n_q, qs);
 }
 
 // Query fragments as the B operand from the staged rows: lane (l16, g)
@@ -314,17 +319,8 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
       u32x4 hi, lo;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float xs[4] = {x[2 * s + h].x, x[2 * s + h].y, x[2 * s + h].z, x[2 * s + h].w};
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hb[e] = f32_to_bf16(xs[e]);
-          lb[e] = f32_to_bf16(xs[e] - bf16_to_f32(hb[e]));
-        }
-        hi[2 * h] = pack_bf16(hb[0], hb[1]);
-        hi[2 * h + 1] = pack_bf16(hb[2], hb[3]);
-        lo[2 * h] = pack_bf16(lb[0], lb[1]);
-        lo[2 * h + 1] = pack_bf16(lb[2], lb[3]);
+        { const Bf16Split t = split_pk_bf16(x[2 * s + h].x, x[2 * s + h].y); hi[2 * h] = t.hi; lo[2 * h] = t.lo; }
+        { const Bf16Split t = split_pk_bf16(x[2 * s + h].z, x[2 * s + h].w); hi[2 * h + 1] = t.hi; lo[2 * h + 1] = t.lo; }
       }
 #pragma unroll
       for (int qt = 0; qt < RT; ++qt) {
@@ -396,17 +392,8 @@ __device__ __forceinline__ void f32_rows_mma(const float4 (&x)[D / 16], const Fr
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const float4 v = x[2 * s + h];
-        const float xs[4] = {v.x, v.y, v.z, v.w};
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hb[e] = f32_to_bf16(xs[e]);
-          lb[e] = f32_to_bf16(xs[e] - bf16_to_f32(hb[e]));
-        }
-        hi[2 * h] = pack_bf16(hb[0], hb[1]);
-        hi[2 * h + 1] = pack_bf16(hb[2], hb[3]);
-        lo[2 * h] = pack_bf16(lb[0], lb[1]);
-        lo[2 * h + 1] = pack_bf16(lb[2], lb[3]);
+        { const Bf16Split t = split_pk_bf16(v.x, v.y); hi[2 * h] = t.hi; lo[2 * h] = t.lo; }
+        { const Bf16Split t = split_pk_bf16(v.z, v.w); hi[2 * h + 1] = t.hi; lo[2 * h + 1] = t.lo; }
       }
 #pragma unroll
       for (int qt = 0; qt < RT; ++qt) {
@@ -913,7 +900,8 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   const int head = blockIdx.y;
   int* sel_l = reinterpret_cast<int*>(lds);
-  stage_query<T, D, NT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+  QueryStage<T, D, NT, RT> qstage;  // the query block is in flight during the Top-K
+  qstage.issue(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q);
   if (topk_in_cover(a)) {  // uniform: every workgroup of the head computes the same kept regions
     auto emit = coarse_emitter(a, head, blockIdx.x == 0, [&](int o, int i) { sel_l[o] = i; });
     coarse_topk_run<false>(a, head, raw, nullptr, emit);
@@ -921,6 +909,7 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
     const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
     for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   }
+  qstage.store(a.n_q, qs);
   __syncthreads();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
@@ -1250,25 +1239,30 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
         kf.load(Ks + (tg * CW + 16 * t + l16) * KS, g);
         sv[t] = mma_tile<D>(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
       }
+      if (pos0 + CW > t_end) {  // wave-uniform: only a split's last chunk has positions past its end
+#pragma unroll
+        for (int t = 0; t < CW / 16; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (pos0 + 16 * t + 4 * g + r >= t_end) sv[t][r] = -INFINITY;
+      }
       float cmax = -INFINITY;
 #pragma unroll
       for (int t = 0; t < CW / 16; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pos = pos0 + 16 * t + 4 * g + r;
-          const float x = (pos < t_end) ? sv[t][r] * sl2 : -INFINITY;
-          sv[t][r] = x;
-          cmax = fmaxf(cmax, x);
-        }
-      cmax = wave_max_xor_16_32(cmax);
+        for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, sv[t][r]);
+      // the scaled maximum (rounding is monotone: it is the maximum of the scaled scores)
+      cmax = wave_max_xor_16_32(cmax) * sl2;
       const float m_new = fmaxf(st.m, cmax);  // finite: the slice holds a valid token
-      const float alpha = exp2f(st.m - m_new);
+      // p = 2^(s sl2 - m), a single v_exp_f32 each: weights below 2^-126 of the
+      // running maximum flush to zero
+      const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < CW / 16; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(sv[t][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sv[t][r], sl2, -m_new));
           sv[t][r] = p;
           psum += p;
         }
@@ -1283,17 +1277,9 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
           u32x4 ph, pl;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            uint32_t hb[4], lb[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float p = sv[2 * s2 + hh][r];
-              hb[r] = f32_to_bf16(p);
-              lb[r] = f32_to_bf16(p - bf16_to_f32(hb[r]));
-            }
-            ph[2 * hh] = pack_bf16(hb[0], hb[1]);
-            ph[2 * hh + 1] = pack_bf16(hb[2], hb[3]);
-            pl[2 * hh] = pack_bf16(lb[0], lb[1]);
-            pl[2 * hh + 1] = pack_bf16(lb[2], lb[3]);
+            const f32x4 p = sv[2 * s2 + hh];
+            { const Bf16Split t = split_pk_bf16(p[0], p[1]); ph[2 * hh] = t.hi; pl[2 * hh] = t.lo; }
+            { const Bf16Split t = split_pk_bf16(p[2], p[3]); ph[2 * hh + 1] = t.hi; pl[2 * hh + 1] = t.lo; }
           }
           // V^T rows d, tokens tg CW + 32 s2 + 4 g + [0,4) and + 16 (word columns c0, c0 + 8)
           const int c0 = (tg * CW) / 2 + 16 * s2 + 2 * g;
