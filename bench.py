@@ -215,8 +215,18 @@ def time_sweep(cfg, dev, sweeps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     sweep_ms = e0.elapsed_time(e1) / sweeps
-    _, sel_b = algorithmic_bytes(cfg)
-    pyr_b, _ = algorithmic_bytes(cfg)
+    # the same sweep as one batched call over all layers (wf_select_attend_layers)
+    import long_context_kv_haar_amd as wf
+
+    items = [(x.q, b.pyramid, x.k, x.v, torch.empty((cfg.batch, cfg.heads, cfg.n_q, cfg.head_dim),
+                                                     dtype=torch.float32, device=dev),
+              torch.empty((cfg.batch, cfg.heads, cfg.budgets[-1]), dtype=torch.int32, device=dev))
+             for x, b in zip(layers, builds)]
+    lws = torch.empty(wf.layers_workspace_bytes(builds[0].pyramid, cfg.layers, cfg.n_q, cfg.n_gen, cfg.budgets),
+                      dtype=torch.uint8, device=dev)
+    batched = wf.PreparedLayers(items, layers[0].gen_idx, cfg.budgets, lws)
+    batched_ms = timed_loop([batched], sweeps, warmup, stream) * 1e-3
+    pyr_b, sel_b = algorithmic_bytes(cfg)
     rec = {
         "layers_resident": cfg.layers,
         "kv_resident_GiB": round(sum(2 * x.k.numel() * x.k.element_size() for x in layers) / 2 ** 30, 1),
@@ -225,10 +235,14 @@ def time_sweep(cfg, dev, sweeps, warmup):
         "per_layer_us": round(sweep_ms * 1e3 / cfg.layers, 2),
         "sweep_GBps": round(cfg.layers * sel_b / (sweep_ms * 1e-3) / 1e9, 1),
         "sweep_frac_of_hbm_peak": round(cfg.layers * sel_b / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "batched_call_ms": round(batched_ms, 3),
+        "batched_sweeps_per_s": round(1e3 / batched_ms, 2),
+        "batched_GBps": round(cfg.layers * sel_b / (batched_ms * 1e-3) / 1e9, 1),
+        "batched_frac_of_hbm_peak": round(cfg.layers * sel_b / (batched_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "build_all_layers_ms": round(build_us * cfg.layers * 1e-3, 3),
         "build_GBps": round(pyr_b / (build_us * 1e-6) / 1e9, 1),
     }
-    del builds, steps, layers
+    del builds, steps, layers, items, batched, lws
     torch.cuda.empty_cache()
     return rec
 

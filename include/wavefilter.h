@@ -243,6 +243,49 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
                      void* stream);
 
 /*
+ * Several layers in one call: wf_select_attend for every (layer, sequence,
+ * head) of up to WF_MAX_LAYER_ITEMS layers that share one shape, so that the
+ * heads of all layers fill the chip in one chain of launches instead of one
+ * chain per layer (the pyramid of each layer built beforehand, as for
+ * wf_select_attend).  Per layer and head the computation is that of
+ * wf_select_attend; the kept tokens are identical, and O agrees up to the
+ * rounding of the float32 accumulation (the attention is split over more or
+ * fewer workgroups when more heads share the chip).
+ *
+ *   items        host array of n_items descriptors, one per layer:
+ *                  q, k, v, out, sel_out as for wf_select_attend (sel_out may
+ *                  be NULL); pyr built by wf_build_pyramid without
+ *                  WF_PYR_ALL_LEVELS or WF_PYR_DB2, all with the same batch,
+ *                  heads, N_p, head dim, levels and element type
+ *   n_items      1 .. WF_MAX_LAYER_ITEMS
+ *   n_tot, gen_idx, n_gen, budgets, n_q, aggregation
+ *                shared by every layer, as for wf_select_attend
+ *   workspace    device buffer of ws_bytes >=
+ *                wf_select_attend_layers_workspace_bytes; scratch only
+ * Returns WF_ERR_SHAPE when the layers differ in shape or n_items * batch *
+ * heads exceeds WF_MAX_HEADS, WF_ERR_OPTION for a pyramid with stored finer
+ * bands, else the statuses of wf_select_attend, before anything is enqueued.
+ * No per-level outputs (sel_levels / score_levels) in this form.
+ */
+#define WF_MAX_LAYER_ITEMS 32
+typedef struct {
+    const void* q;
+    const wf_pyramid* pyr;
+    const void* k;
+    const void* v;
+    float* out;
+    int32_t* sel_out;
+} wf_layer_item;
+
+/* Bytes of workspace wf_select_attend_layers needs for n_items layers of the
+ * pyramid's shape, or 0 if the arguments are invalid. */
+uint64_t wf_select_attend_layers_workspace_bytes(const wf_pyramid* pyr, int32_t n_items, int32_t n_q,
+                                                 int32_t n_gen, const int32_t* budgets);
+int wf_select_attend_layers(const wf_layer_item* items, int32_t n_items, int32_t n_tot, const int32_t* gen_idx,
+                            int32_t n_gen, const int32_t* budgets, int32_t n_q, int32_t aggregation,
+                            void* workspace, uint64_t ws_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * wf_select_attend with the workspace taken from a static device array of

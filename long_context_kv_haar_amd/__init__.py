@@ -7,6 +7,7 @@ The work runs in ``libwavefilter.so`` (hand-written HIP, C ABI declared in
 from ._lib import (  # noqa: F401
     LIB_PATH,
     MAX_LEVELS,
+    MAX_LAYER_ITEMS,
     MAX_QUERIES,
     WF_AGG_MAX,
     WF_AGG_MEAN,
@@ -17,6 +18,7 @@ from ._lib import (  # noqa: F401
     Pyramid,
     PreparedAttend,
     PreparedBuild,
+    PreparedLayers,
     PreparedRefresh,
     PreparedStep,
     WfError,
@@ -28,6 +30,8 @@ from ._lib import (  # noqa: F401
     pyramid_bytes,
     refresh_pyramids,
     select_attend,
+    select_attend_layers,
+    layers_workspace_bytes,
     select_attend_noalloc,
     split_levels,
     status_string,

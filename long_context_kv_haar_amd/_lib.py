@@ -58,6 +58,20 @@ class WfRefreshItem(ctypes.Structure):
     ]
 
 
+class WfLayerItem(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("pyr", ctypes.POINTER(WfPyramid)),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("sel_out", ctypes.c_void_p),
+    ]
+
+
+MAX_LAYER_ITEMS = 32
+
+
 class WfError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
@@ -93,6 +107,11 @@ def lib():
         L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp, u64, vp]
         L.wf_select_attend_noalloc.restype = ctypes.c_int
         L.wf_select_attend_noalloc.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp]
+        L.wf_select_attend_layers_workspace_bytes.restype = u64
+        L.wf_select_attend_layers_workspace_bytes.argtypes = [pyr_p, i32, i32, i32, i32p]
+        L.wf_select_attend_layers.restype = ctypes.c_int
+        L.wf_select_attend_layers.argtypes = [ctypes.POINTER(WfLayerItem), i32, i32, vp, i32, i32p, i32, i32, vp, u64,
+                                              vp]
         L.wf_refresh_pyramids.restype = ctypes.c_int
         L.wf_refresh_pyramids.argtypes = [ctypes.POINTER(WfRefreshItem), i32, vp]
         L.wf_attend_selected_workspace_bytes.restype = u64
@@ -519,6 +538,91 @@ class PreparedStep:
         st = self._fn(*self._args)
         if st != WF_OK:
             raise WfError(st, "wf_select_attend")
+
+
+def _layer_array(layers, gen_idx, budgets):
+    """Check the layers of a batched call against one another and marshal
+    them: ``layers`` is a list of (q, pyr, k, v, out, sel_out) with sel_out
+    optionally None."""
+    _need(1 <= len(layers) <= MAX_LAYER_ITEMS, f"1 to {MAX_LAYER_ITEMS} layers")
+    q0, p0, k0_, v0 = layers[0][:4]
+    for q, pyr, k, v, out, sel_out in layers:
+        _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out)
+        _need(q.shape == q0.shape and k.shape == k0_.shape and v.shape == v0.shape and q.dtype == q0.dtype,
+              "every layer must have the same shapes and element type")
+        _need(q.device == q0.device, "every layer must be on one device")
+    arr = (WfLayerItem * len(layers))()
+    for i, (q, pyr, k, v, out, sel_out) in enumerate(layers):
+        arr[i] = WfLayerItem(q.data_ptr(), ctypes.pointer(pyr.desc), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             None if sel_out is None else sel_out.data_ptr())
+    return arr
+
+
+def layers_workspace_bytes(pyr, n_items, n_q, n_gen, budgets):
+    return int(lib().wf_select_attend_layers_workspace_bytes(ctypes.byref(pyr.desc), n_items, n_q, n_gen,
+                                                             _budget_array(budgets)))
+
+
+def select_attend_layers(layers, gen_idx, budgets, agg="max", workspace=None):
+    """``select_attend`` for several layers of one shape in one call.
+
+    ``layers`` is a list of (q, pyr, k, v) or (q, pyr, k, v, out, sel_out);
+    missing outputs are allocated.  Returns a list of dicts with ``out`` and
+    ``sel`` per layer."""
+    budgets = [int(b) for b in budgets]
+    full = []
+    for lay in layers:
+        q, pyr, k, v = lay[:4]
+        _need(isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 4, "q must be a 4-d device tensor")
+        out = lay[4] if len(lay) > 4 and lay[4] is not None else torch.empty(q.shape, dtype=torch.float32,
+                                                                             device=q.device)
+        sel = lay[5] if len(lay) > 5 and lay[5] is not None else torch.empty(
+            (q.shape[0], q.shape[1], budgets[-1]), dtype=torch.int32, device=q.device)
+        full.append((q, pyr, k, v, out, sel))
+    arr = _layer_array(full, gen_idx, budgets)
+    q0, p0, k0_ = full[0][:3]
+    n_gen = 0 if gen_idx is None else gen_idx.numel()
+    barr = _budget_array(budgets)
+    need = int(lib().wf_select_attend_layers_workspace_bytes(ctypes.byref(p0.desc), len(full), q0.shape[2], n_gen,
+                                                             barr))
+    if need == 0:
+        raise WfError(-5, "wf_select_attend_layers_workspace_bytes")
+    if workspace is None:
+        workspace = default_workspace(q0.device)
+    ws = workspace.get(need)
+    st = lib().wf_select_attend_layers(arr, len(full), k0_.shape[2],
+                                       ctypes.c_void_p(0 if gen_idx is None else gen_idx.data_ptr()), n_gen, barr,
+                                       q0.shape[2], _agg_code(agg), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                       _stream_handle(q0.device))
+    if st != WF_OK:
+        raise WfError(st, "wf_select_attend_layers")
+    return [{"out": f[4], "sel": f[5]} for f in full]
+
+
+class PreparedLayers:
+    """A batched select-attend call over several layers, marshalled once."""
+
+    def __init__(self, layers, gen_idx, budgets, workspace, agg="max"):
+        budgets = [int(b) for b in budgets]
+        self._arr = _layer_array(layers, gen_idx, budgets)
+        q0, p0, k0_ = layers[0][:3]
+        n_gen = 0 if gen_idx is None else gen_idx.numel()
+        self._barr = _budget_array(budgets)
+        need = int(lib().wf_select_attend_layers_workspace_bytes(ctypes.byref(p0.desc), len(layers), q0.shape[2],
+                                                                 n_gen, self._barr))
+        if need == 0:
+            raise WfError(-5, "PreparedLayers")
+        _check_workspace(workspace, q0.device, need)
+        self._keep = (layers, gen_idx, workspace)
+        self._args = (self._arr, len(layers), k0_.shape[2], ctypes.c_void_p(0 if gen_idx is None else gen_idx.data_ptr()),
+                      n_gen, self._barr, q0.shape[2], _agg_code(agg), ctypes.c_void_p(workspace.data_ptr()),
+                      workspace.numel(), _stream_handle(q0.device))
+        self._fn = lib().wf_select_attend_layers
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != WF_OK:
+            raise WfError(st, "wf_select_attend_layers")
 
 
 class PreparedBuild:

@@ -66,14 +66,18 @@ bool pyramid_ok(const wf_pyramid* p) {
          (p->dtype == WF_F32 || p->dtype == WF_BF16);
 }
 
-// Resolve budgets and the workspace layout; returns a status.
-int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* budgets, wf::SelectPlan* P) {
+// Resolve budgets and the workspace layout for n_items layers of the
+// pyramid's shape; returns a status.
+int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* budgets, wf::SelectPlan* P,
+              int32_t n_items = 1) {
   if (!pyramid_ok(pyr)) return pyr ? WF_ERR_PYRAMID : WF_ERR_NULL;
   if (!budgets) return WF_ERR_NULL;
   if (n_q < 1 || n_q > WF_MAX_QUERIES || n_gen < 0) return WF_ERR_SHAPE;
+  if (n_items < 1 || n_items > WF_MAX_LAYER_ITEMS) return WF_ERR_SHAPE;
+  if ((int64_t)n_items * pyr->batch * pyr->heads > WF_MAX_HEADS) return WF_ERR_SHAPE;
   memset(P, 0, sizeof(*P));
   const int L = pyr->levels;
-  P->heads_total = pyr->batch * pyr->heads;
+  P->heads_total = n_items * pyr->batch * pyr->heads;
   P->n_q = n_q;
   P->n_prompt = pyr->n_prompt;
   P->n_top = pyr->n_prompt >> L;
@@ -390,16 +394,18 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
   if (ws_bytes < P.total) return WF_ERR_WORKSPACE;
   wf::SelectLaunch a;
   a.plan = P;
-  a.q = q;
-  a.a_top = reinterpret_cast<const float*>(pyr->base);
-  a.k = k;
-  a.v = v;
+  a.n_items = 1;
+  a.heads_per_item = P.heads_total;
+  a.q[0] = q;
+  a.a_top[0] = reinterpret_cast<const float*>(pyr->base);
+  a.k[0] = k;
+  a.v[0] = v;
+  a.out[0] = out;
+  a.sel_out[0] = sel_out;
   a.gen_idx = gen_idx;
   a.sel_in = nullptr;
   a.attend_only = 0;
   a.agg_mean = aggregation == WF_AGG_MEAN;
-  a.out = out;
-  a.sel_out = sel_out;
   a.sel_levels = sel_levels;
   a.score_levels = score_levels;
   a.ws = reinterpret_cast<uint8_t*>(workspace);
@@ -421,6 +427,65 @@ int wf_select_attend_noalloc(const void* q, const wf_pyramid* pyr, const void* k
   if (sst != WF_OK) return sst;
   return wf_select_attend(q, pyr, k, v, n_tot, gen_idx, n_gen, budgets, n_q, aggregation, out, sel_out, sel_levels,
                           score_levels, ws, WF_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+uint64_t wf_select_attend_layers_workspace_bytes(const wf_pyramid* pyr, int32_t n_items, int32_t n_q, int32_t n_gen,
+                                                 const int32_t* budgets) {
+  wf::SelectPlan P;
+  if (pyr && (pyr->flags & (WF_PYR_ALL_LEVELS | WF_PYR_DB2))) return 0;
+  if (make_plan(pyr, n_q, n_gen, budgets, &P, n_items) != WF_OK) return 0;
+  return P.total;
+}
+
+int wf_select_attend_layers(const wf_layer_item* items, int32_t n_items, int32_t n_tot, const int32_t* gen_idx,
+                            int32_t n_gen, const int32_t* budgets, int32_t n_q, int32_t aggregation, void* workspace,
+                            uint64_t ws_bytes, void* stream) {
+  if (!items || !workspace || !budgets) return WF_ERR_NULL;
+  if (n_items < 1 || n_items > WF_MAX_LAYER_ITEMS) return WF_ERR_SHAPE;
+  if (n_gen > 0 && !gen_idx) return WF_ERR_NULL;
+  if (aggregation != WF_AGG_MAX && aggregation != WF_AGG_MEAN) return WF_ERR_OPTION;
+  const wf_pyramid* p0 = items[0].pyr;
+  for (int i = 0; i < n_items; ++i) {
+    const wf_layer_item& it = items[i];
+    if (!it.q || !it.pyr || !it.k || !it.v || !it.out) return WF_ERR_NULL;
+    if (!pyramid_ok(it.pyr)) return WF_ERR_PYRAMID;
+    if (it.pyr->flags & (WF_PYR_ALL_LEVELS | WF_PYR_DB2)) return WF_ERR_OPTION;  // A_L-only Haar pyramids
+    if (it.pyr->dtype != p0->dtype) return WF_ERR_DTYPE;
+    if (it.pyr->batch != p0->batch || it.pyr->heads != p0->heads || it.pyr->n_prompt != p0->n_prompt ||
+        it.pyr->head_dim != p0->head_dim || it.pyr->levels != p0->levels)
+      return WF_ERR_SHAPE;
+    if (!aligned16(it.q) || !aligned16(it.k) || !aligned16(it.v) || !aligned16(it.out) || !aligned16(it.pyr->base))
+      return WF_ERR_ALIGN;
+    if (it.sel_out && !aligned4(it.sel_out)) return WF_ERR_ALIGN;
+  }
+  wf::SelectPlan P;
+  const int st = make_plan(p0, n_q, n_gen, budgets, &P, n_items);
+  if (st != WF_OK) return st;
+  if (n_tot < p0->n_prompt || n_tot < 1) return WF_ERR_SHAPE;
+  P.n_tot = n_tot;
+  if (!aligned16(workspace) || (gen_idx && !aligned4(gen_idx))) return WF_ERR_ALIGN;
+  if (ws_bytes < P.total) return WF_ERR_WORKSPACE;
+  wf::SelectLaunch a;
+  a.plan = P;
+  a.n_items = n_items;
+  a.heads_per_item = p0->batch * p0->heads;
+  for (int i = 0; i < n_items; ++i) {
+    a.q[i] = items[i].q;
+    a.a_top[i] = reinterpret_cast<const float*>(items[i].pyr->base);
+    a.k[i] = items[i].k;
+    a.v[i] = items[i].v;
+    a.out[i] = items[i].out;
+    a.sel_out[i] = items[i].sel_out;
+  }
+  a.gen_idx = gen_idx;
+  a.sel_in = nullptr;
+  a.attend_only = 0;
+  a.agg_mean = aggregation == WF_AGG_MEAN;
+  a.sel_levels = nullptr;
+  a.score_levels = nullptr;
+  a.ws = reinterpret_cast<uint8_t*>(workspace);
+  if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  return WF_OK;
 }
 
 uint64_t wf_attend_selected_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype,
@@ -445,16 +510,18 @@ int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batc
   if (ws_bytes < P.total) return WF_ERR_WORKSPACE;
   wf::SelectLaunch a;
   a.plan = P;
-  a.q = q;
-  a.a_top = nullptr;
-  a.k = k;
-  a.v = v;
+  a.n_items = 1;
+  a.heads_per_item = P.heads_total;
+  a.q[0] = q;
+  a.a_top[0] = nullptr;
+  a.k[0] = k;
+  a.v[0] = v;
+  a.out[0] = out;
+  a.sel_out[0] = nullptr;
   a.gen_idx = gen_idx;
   a.sel_in = sel;  // NULL when k0 == 0
   a.attend_only = 1;
   a.agg_mean = 0;
-  a.out = out;
-  a.sel_out = nullptr;
   a.sel_levels = nullptr;
   a.score_levels = nullptr;
   a.ws = reinterpret_cast<uint8_t*>(workspace);

@@ -13,6 +13,7 @@ constexpr int kMaxLevels = WF_MAX_LEVELS;
 static_assert(kMaxLevels == kPyrMaxLevels, "one level limit");
 constexpr int kAttendGroups = 2;          // waves per query tile in the attention workgroup
 constexpr int kMaxSplit = 16;             // attention splits per head
+constexpr int kMaxItems = WF_MAX_LAYER_ITEMS;  // layers of one batched select-attend call
 constexpr int kMaxCoarseLds = 16384;      // general coarse Top-K: keys staged in LDS up to this count
 constexpr int kMaxKeepTop = 16384;        // k_L limit (kept coarse regions live in LDS)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per workgroup on gfx950
@@ -54,16 +55,19 @@ struct SelectPlan {
 
 struct SelectLaunch {
   SelectPlan plan;
-  const void* q;
-  const float* a_top;
-  const void* k;
-  const void* v;
+  // per layer of a batched call (n_items = 1 otherwise); plan.heads_total =
+  // n_items * heads_per_item
+  int n_items, heads_per_item;
+  const void* q[kMaxItems];
+  const float* a_top[kMaxItems];
+  const void* k[kMaxItems];
+  const void* v[kMaxItems];
+  float* out[kMaxItems];
+  int32_t* sel_out[kMaxItems];
   const int32_t* gen_idx;
   const int32_t* sel_in;  // attention only: the kept prompt tokens [heads_total][k0] (NULL if k0 == 0)
   int attend_only;        // 1: skip selection, attend over sel_in and gen_idx
   int agg_mean;           // 1: region scores average the query rows (else their maximum)
-  float* out;
-  int32_t* sel_out;
   int32_t* sel_levels;
   float* score_levels;
   uint8_t* ws;

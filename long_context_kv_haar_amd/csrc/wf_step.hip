@@ -35,15 +35,18 @@ static_assert(wf::kRefineThreads == wf::kRefineThreadsHost, "one refinement work
 namespace wf {
 
 struct StepArgs {
-  const void* q;
-  const float* a_top;
-  const void* k;
-  const void* v;
+  // Per layer (item) of a batched call: the heads of the n_items layers are
+  // stacked, head = item * heads_per_item + its index inside the layer.
+  const void* q[kMaxItems];
+  const float* a_top[kMaxItems];
+  const void* k[kMaxItems];
+  const void* v[kMaxItems];
+  float* out[kMaxItems];
+  int32_t* sel_out[kMaxItems];
+  int n_items, heads_per_item;
   const int32_t* gen_idx;
   const int32_t* sel_in;  // the kept prompt tokens [heads_total][k0] the attention reads (NULL if k0 == 0)
   int32_t* sel_ws;        // where the selection writes them [heads_total][k0]
-  float* out;
-  int32_t* sel_out;
   int32_t* sel_levels;
   float* score_levels;
   uint32_t* keys_top;    // [heads_total][n_top]
@@ -68,6 +71,16 @@ struct StepArgs {
   int stored_bands;                    // score levels 1 .. L-1 from stored A_j (longer bases)
   const float* band_a[kMaxLevels];     // A_j [heads_total][n_prompt >> j][d], when stored
 };
+
+// The layer of a head and the head's index inside that layer.
+struct HeadRef {
+  int item;
+  int64_t local;
+};
+__device__ __forceinline__ HeadRef head_ref(const StepArgs& a, int head) {
+  const int item = a.n_items == 1 ? 0 : head / a.heads_per_item;
+  return {item, (int64_t)(head - item * a.heads_per_item)};
+}
 
 // Max across the 16 lanes of a row; every lane of the row ends with it.
 __device__ __forceinline__ float row_max16(float x) {
@@ -263,7 +276,8 @@ __device__ __forceinline__ auto coarse_emitter(const StepArgs& a, int head, bool
   float* dbg_score = report && a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   // with L = 0 the coarse level is the tokens themselves: these are the kept tokens
   int32_t* tsel = (writer && a.levels == 0) ? a.sel_ws + (int64_t)head * a.k0 : nullptr;
-  int32_t* tout = (writer && a.levels == 0 && a.sel_out) ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  const HeadRef hr = head_ref(a, head);
+  int32_t* tout = (writer && a.levels == 0 && a.sel_out[hr.item]) ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
   return [=](int o, int i, float sc) {
     emit_sel(o, i);
     if (sel_g) sel_g[o] = i;
@@ -297,7 +311,8 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
 
   const int n = blockIdx.x * 64 + w * 16 + l16;  // region supplied by this lane (A operand)
   const bool valid = n < a.n_top;
-  const float* arow = a.a_top + ((int64_t)head * a.n_top + (valid ? n : 0)) * D;
+  const HeadRef hr = head_ref(a, head);
+  const float* arow = a.a_top[hr.item] + (hr.local * a.n_top + (valid ? n : 0)) * D;
   f32x4 acc[RT];
 #pragma unroll
   for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -310,7 +325,7 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
     for (int i = 0; i < 2 * STEPS; ++i)
       x[i] = valid ? p[8 * (i >> 1) + 2 * g + (i & 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
     // Q staged while the coefficient rows are in flight
-    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
@@ -331,7 +346,7 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
   } else {
     Frag<float, D> b;
     if (valid) b.load(arow, g); else b.zero();
-    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q, qs);
+    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
@@ -433,7 +448,8 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
   float* cov = a.cov + (int64_t)head * a.cov_len;
   const int nwav = (int)((a.covered + 63) >> 6);
   uint32_t* lvl = a.lvl_mm + ((int64_t)head * nwav + (wave_base >> 6)) * 2 * kMaxLevels;
-  const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
+  const HeadRef hr = head_ref(a, head);
+  const T* kh = reinterpret_cast<const T*>(a.k[hr.item]) + hr.local * a.n_tot * D;
   for (int j = 0; j < L; ++j) {
     const int64_t nj = a.covered >> j;
     const int sh = L - j;
@@ -515,7 +531,8 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
                                            int64_t wave_base, int lane, int g, int l16) {
   using AG = QueryAgg<MEAN>;
   const int L = a.levels;
-  const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
+  const HeadRef hr = head_ref(a, head);
+  const T* kh = reinterpret_cast<const T*>(a.k[hr.item]) + hr.local * a.n_tot * D;
   Frag<T, D> kf[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -871,7 +888,8 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const in
   // the kept tokens, ascending
   int o = block_excl_scan(__popc(keptp), sh, 1);
   int32_t* tsel = a.sel_ws + (int64_t)head * a.k0;
-  int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  const HeadRef hr = head_ref(a, head);
+  int32_t* so = a.sel_out[hr.item] ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
   const int mask = (1 << L) - 1;
 #pragma unroll
   for (int i = 0; i < S0; ++i)
@@ -901,7 +919,8 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
   const int head = blockIdx.y;
   int* sel_l = reinterpret_cast<int*>(lds);
   QueryStage<T, D, NT, RT> qstage;  // the query block is in flight during the Top-K
-  qstage.issue(reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D, a.n_q);
+  const HeadRef hr = head_ref(a, head);
+  qstage.issue(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q);
   if (topk_in_cover(a)) {  // uniform: every workgroup of the head computes the same kept regions
     auto emit = coarse_emitter(a, head, blockIdx.x == 0, [&](int o, int i) { sel_l[o] = i; });
     coarse_topk_run<false>(a, head, raw, nullptr, emit);
@@ -1030,7 +1049,8 @@ __device__ __forceinline__ void refine_head_lists(const StepArgs& a, int head, u
     kprev = kj;
     dbg_off += kj;
   }
-  int32_t* so = a.sel_out ? a.sel_out + (int64_t)head * a.k0 : nullptr;
+  const HeadRef hr = head_ref(a, head);
+  int32_t* so = a.sel_out[hr.item] ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
   for (int o = threadIdx.x; o < a.k0; o += NT) {
     const int p = cur[o];
     const int tok = (clampi(sel_top[clampi(p >> L, 0, a.k_top - 1)], 0, a.n_top - 1) << L) + (p & ((1 << L) - 1));
@@ -1140,12 +1160,13 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
   const int g = lane >> 4, l16 = lane & 15;
   const int query = 16 * qt + l16;
   const bool qvalid = query < a.n_q;
-  const T* kh = reinterpret_cast<const T*>(a.k) + (int64_t)head * a.n_tot * D;
-  const T* vh = reinterpret_cast<const T*>(a.v) + (int64_t)head * a.n_tot * D;
+  const HeadRef hr = head_ref(a, head);
+  const T* kh = reinterpret_cast<const T*>(a.k[hr.item]) + hr.local * a.n_tot * D;
+  const T* vh = reinterpret_cast<const T*>(a.v[hr.item]) + hr.local * a.n_tot * D;
 
   // this wave's query fragment, in flight while the token list arrives
   Frag<T, D> qf;
-  const T* qh = reinterpret_cast<const T*>(a.q) + (int64_t)head * a.n_q * D;
+  const T* qh = reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D;
   if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
 
   // the attended tokens of this split: T positions [t0, t_end), in nck chunks
@@ -1372,13 +1393,16 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
   float4 ov[kMaxSplit];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplit; ++sp) {  // every load issued before any is used
-    const bool in = sp < ns;
-    const int64_t row = ((int64_t)head * ns + (in ? sp : 0)) * a.n_q + query;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
-    const float4 o = *reinterpret_cast<const float4*>(a.part_o + row * D + 4 * c4);
-    mv[sp] = in ? ml.x : -INFINITY;
-    lv[sp] = in ? ml.y : 0.f;
-    ov[sp] = in ? o : make_float4(0.f, 0.f, 0.f, 0.f);
+    mv[sp] = -INFINITY;
+    lv[sp] = 0.f;
+    ov[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sp < ns) {  // uniform: only the splits that exist are read
+      const int64_t row = ((int64_t)head * ns + sp) * a.n_q + query;
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+      mv[sp] = ml.x;
+      lv[sp] = ml.y;
+      ov[sp] = *reinterpret_cast<const float4*>(a.part_o + row * D + 4 * c4);
+    }
   }
   float mm = -INFINITY;
 #pragma unroll
@@ -1395,7 +1419,8 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
     acc.w += wv * ov[sp].w;
   }
   const float inv = 1.0f / den;
-  *reinterpret_cast<float4*>(a.out + ((int64_t)head * a.n_q + query) * D + 4 * c4) =
+  const HeadRef hr = head_ref(a, head);
+  *reinterpret_cast<float4*>(a.out[hr.item] + (hr.local * a.n_q + query) * D + 4 * c4) =
       make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 #endif
@@ -1520,15 +1545,20 @@ static hipError_t launch_rt_attend(int rt, const StepArgs& a, const SelectLaunch
 hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   const SelectPlan& P = L.plan;
   StepArgs a;
-  a.q = L.q;
-  a.a_top = L.a_top;
-  a.k = L.k;
-  a.v = L.v;
+  a.n_items = L.n_items;
+  a.heads_per_item = L.heads_per_item;
+  for (int i = 0; i < kMaxItems; ++i) {
+    const bool in = i < L.n_items;
+    a.q[i] = in ? L.q[i] : nullptr;
+    a.a_top[i] = in ? L.a_top[i] : nullptr;
+    a.k[i] = in ? L.k[i] : nullptr;
+    a.v[i] = in ? L.v[i] : nullptr;
+    a.out[i] = in ? L.out[i] : nullptr;
+    a.sel_out[i] = in ? L.sel_out[i] : nullptr;
+  }
   a.gen_idx = L.gen_idx;
   a.sel_ws = reinterpret_cast<int32_t*>(L.ws + P.off_sel);
   a.sel_in = L.attend_only ? L.sel_in : a.sel_ws;
-  a.out = L.out;
-  a.sel_out = L.sel_out;
   a.sel_levels = L.sel_levels;
   a.score_levels = L.score_levels;
   a.keys_top = reinterpret_cast<uint32_t*>(L.ws + P.off_keys);
@@ -1568,7 +1598,7 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.stored_bands = P.stored_bands;
   for (int j = 0; j < kMaxLevels; ++j)
     a.band_a[j] = P.stored_bands && j > 0 && j < P.levels
-                      ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top) + P.band_off[j])
+                      ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top[0]) + P.band_off[j])
                       : nullptr;
 
   const int rt = (P.n_q + 15) / 16;

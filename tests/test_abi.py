@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -326,3 +326,50 @@ def test_noalloc_checks_its_arguments_like_the_workspace_call():
     assert noalloc(p, [8, 17, 32, 64]) == -5                   # k_2 > 2 k_3: WF_ERR_BUDGET
     assert noalloc(p, [8, 16, 32, 64], n_q=65) == -2           # WF_ERR_SHAPE
     assert noalloc(fake_pyramid(magic=0), [8, 16, 32, 64]) == -9  # WF_ERR_PYRAMID
+
+
+def _layers(pyrs, q=FAKE):
+    from long_context_kv_haar_amd._lib import WfLayerItem
+    arr = (WfLayerItem * len(pyrs))()
+    for i, p in enumerate(pyrs):
+        arr[i] = WfLayerItem(q, ctypes.pointer(p), FAKE, FAKE, FAKE, None)
+    return arr
+
+
+def layers_call(pyrs, n_items=None, budgets=(8, 16, 32, 64), agg=wf.WF_AGG_MAX, q=FAKE, ws_bytes=1 << 30):
+    arr = _layers(pyrs, q)
+    n = len(pyrs) if n_items is None else n_items
+    return lib().wf_select_attend_layers(arr, n, 1056, ctypes.c_void_p(FAKE), 32, budgets_arr(list(budgets)), 32, agg,
+                                         ctypes.c_void_p(FAKE), ws_bytes, None)
+
+
+def test_layers_workspace_grows_with_the_layers_and_caps_the_heads():
+    q = lib().wf_select_attend_layers_workspace_bytes
+    p = fake_pyramid()
+    one = q(ctypes.byref(p), 1, 32, 32, budgets_arr([8, 16, 32, 64]))
+    assert one == lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]))
+    assert q(ctypes.byref(p), 4, 32, 32, budgets_arr([8, 16, 32, 64])) > one
+    assert q(ctypes.byref(p), 0, 32, 32, budgets_arr([8, 16, 32, 64])) == 0
+    assert q(ctypes.byref(p), 33, 32, 32, budgets_arr([8, 16, 32, 64])) == 0
+    # 32 layers of 2 048 heads exceed the head limit of a launch
+    assert q(ctypes.byref(fake_pyramid(H=2048)), 32, 32, 32, budgets_arr([8, 16, 32, 64])) == 0
+    # pyramids with stored finer bands are not batched
+    db2 = WfPyramid(1, 2, 1024, 64, 3, wf.WF_BF16, wf.WF_PYR_DB2, 0x57465059, FAKE, 1 << 20)
+    assert q(ctypes.byref(db2), 2, 32, 32, budgets_arr([8, 16, 32, 64])) == 0
+
+
+def test_layers_call_checks_its_arguments_before_any_device_call():
+    p = fake_pyramid()
+    assert layers_call([p, fake_pyramid()], n_items=0) == -2            # WF_ERR_SHAPE
+    assert layers_call([p] * 2, n_items=33) == -2
+    assert layers_call([p, fake_pyramid(H=3)]) == -2                    # layers of different shapes
+    assert layers_call([p, fake_pyramid(levels=2)]) == -2
+    assert layers_call([p, fake_pyramid(dt=wf.WF_F32)]) == -3           # WF_ERR_DTYPE
+    assert layers_call([p, fake_pyramid(magic=0)]) == -9                # WF_ERR_PYRAMID
+    assert layers_call([p], q=0) == -1                                  # WF_ERR_NULL
+    assert layers_call([p], q=MISALIGNED) == -7                         # WF_ERR_ALIGN
+    assert layers_call([p], budgets=(8, 17, 32, 64)) == -5              # WF_ERR_BUDGET
+    assert layers_call([p], agg=7) == -10                               # WF_ERR_OPTION
+    assert layers_call([p], ws_bytes=16) == -6                          # WF_ERR_WORKSPACE
+    db2 = WfPyramid(1, 2, 1024, 64, 3, wf.WF_BF16, wf.WF_PYR_DB2, 0x57465059, FAKE, 1 << 20)
+    assert layers_call([p, db2]) == -10

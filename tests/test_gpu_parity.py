@@ -151,9 +151,66 @@ def test_full_size_128k_32_layers():
         say(f"[full size c5] {len(planted)} planted heads exact, {len(extra)} unplanted heads valid "
             f"(least relative margin {worst:.3g})")
         assert torch_attend_all(layers[cfg.layers - 1], results[cfg.layers - 1]) <= TOL["bf16"]
+        say("[full size c5] all 32 layers in one batched call")
+        batched = wf.select_attend_layers([(inp.q, pyrs[i], inp.k, inp.v) for i, inp in enumerate(layers)],
+                                          layers[0].gen_idx, cfg.budgets)
+        torch.cuda.synchronize()
+        for layer in range(cfg.layers):
+            # the same kept tokens for every head; O to float32 rounding (other split sums)
+            assert torch.equal(batched[layer]["sel"], results[layer]["sel"]), layer
+            assert (batched[layer]["out"] - results[layer]["out"]).abs().max().item() <= 1e-5, layer
+        for (layer, (b, h)), o in zip(planted, ora):
+            err = np.abs(batched[layer]["out"][b, h].double().cpu().numpy() - o.out).max()
+            assert err <= TOL["bf16"], (layer, b, h, err)
+        say(f"[full size c5] batched call: every head's kept tokens equal, O within 1e-5 of the per-layer calls")
     finally:
         del layers
         torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("agg", ["max", "mean"])
+def test_batched_layers_match_per_layer_calls(agg):
+    """Three 4K-token layers (own seeds) in one batched call: every head's
+    kept tokens equal the per-layer call's, O agrees to float32 rounding, and
+    one planted head per layer matches the oracle.  A batch of one layer is
+    the per-layer call bit for bit."""
+    cfg = CONFIGS[2]
+    say(f"[batched layers {agg}]")
+    layers = [make_layer(cfg, layer) for layer in range(3)]
+    planted = [(layer, (0, (11 * layer + 3) % cfg.heads)) for layer in range(3)]
+    assert all(plant_many([(layers[layer], bh) for layer, bh in planted], agg=agg))
+    for inp in layers:
+        to_dev(inp)
+    pyrs = [wf.build_pyramid(inp.k, cfg.n_prompt, cfg.levels) for inp in layers]
+    single = [wf.select_attend(inp.q, pyrs[i], inp.k, inp.v, inp.gen_idx, cfg.budgets, agg=agg)
+              for i, inp in enumerate(layers)]
+    batched = wf.select_attend_layers([(inp.q, pyrs[i], inp.k, inp.v) for i, inp in enumerate(layers)],
+                                      layers[0].gen_idx, cfg.budgets, agg=agg)
+    one = wf.select_attend_layers([(layers[1].q, pyrs[1], layers[1].k, layers[1].v)], layers[1].gen_idx,
+                                  cfg.budgets, agg=agg)
+    torch.cuda.synchronize()
+    for layer in range(3):
+        assert torch.equal(batched[layer]["sel"], single[layer]["sel"])
+        assert (batched[layer]["out"] - single[layer]["out"]).abs().max().item() <= 1e-5
+    assert torch.equal(one[0]["sel"], single[1]["sel"])
+    assert torch.equal(one[0]["out"].view(torch.int32), single[1]["out"].view(torch.int32))
+    ora = oracle_many([(layers[layer], bh) for layer, bh in planted], agg=agg)
+    for (layer, (b, h)), o in zip(planted, ora):
+        np.testing.assert_array_equal(batched[layer]["sel"][b, h].cpu().numpy(), o.sel[0])
+        assert np.abs(batched[layer]["out"][b, h].double().cpu().numpy() - o.out).max() <= TOL["bf16"]
+
+
+def test_batched_layers_reject_mismatched_layers():
+    cfg = CONFIGS[1]
+    say("[batched layers reject]")
+    a, b = to_dev(make_layer(cfg, 0)), to_dev(make_layer(cfg, 1))
+    pa = wf.build_pyramid(a.k, cfg.n_prompt, cfg.levels)
+    pb = wf.build_pyramid(b.k, cfg.n_prompt, cfg.levels - 1)  # other level count
+    with pytest.raises((ValueError, wf.WfError)):  # the binding's checks see it first
+        wf.select_attend_layers([(a.q, pa, a.k, a.v), (b.q, pb, b.k, b.v)], a.gen_idx, cfg.budgets)
+    pf = wf.build_pyramid(b.k.bfloat16().contiguous(), cfg.n_prompt, cfg.levels)  # other element type
+    with pytest.raises((ValueError, wf.WfError)):
+        wf.select_attend_layers([(a.q, pa, a.k, a.v), (b.q, pf, b.k, b.v)], a.gen_idx, cfg.budgets)
 
 
 def custom(base, **kw):
