@@ -58,6 +58,37 @@ enum {
     WF_ERR_OPTION = -10    /* an option argument has no defined meaning */
 };
 
+/*
+ * Debug checks (option bit): OR WF_OPT_CHECK into the `aggregation` argument
+ * of wf_select_attend / wf_select_attend_noalloc / wf_select_attend_layers,
+ * or pass it as `options` to wf_attend_selected.  The call then scans its
+ * inputs first and records, in a status word at the start of its workspace,
+ * every precondition they break (bits below; 0 = none).  The selection and
+ * attention kernels still clamp each index they read into its buffer, so an
+ * out-of-range entry never leads to an access outside the buffers; with the
+ * checks on, every such clamp is reported.  Read the word with
+ * wf_check_status after the call.  The scan reads all of q, k, v (rows
+ * [0, n_tot) of every head) and A_L once: a debugging aid, not for the timed
+ * path.
+ */
+#define WF_OPT_CHECK 0x100
+#define WF_CHECK_GEN_INDEX 1u          /* a gen_idx entry outside [0, n_tot) */
+#define WF_CHECK_SEL_INDEX 2u          /* a sel entry outside [0, n_tot) (wf_attend_selected) */
+#define WF_CHECK_NONFINITE_Q 4u        /* a NaN or infinity in q */
+#define WF_CHECK_NONFINITE_K 8u        /* ... in k */
+#define WF_CHECK_NONFINITE_V 16u       /* ... in v */
+#define WF_CHECK_NONFINITE_PYRAMID 32u /* ... in the pyramid's A_L */
+
+/*
+ * The status word the last call with WF_OPT_CHECK left in `workspace` (the
+ * workspace that call was given; NULL: the scratch array of
+ * wf_select_attend_noalloc on the stream's device).  Copies the word to
+ * *status after the work queued on `stream` so far has finished: this call
+ * synchronises the stream and may not be captured into a graph.  Returns
+ * WF_ERR_NULL for a NULL status pointer, WF_ERR_HIP if the copy fails.
+ */
+int wf_check_status(const void* workspace, void* stream, uint32_t* status);
+
 /* How the n_q query rows combine into one region score (Figure 2 (c) scores
  * regions by the queries' correlation with the low-frequency keys and leaves
  * the combination of the rows open): the maximum over the rows, or their
@@ -217,14 +248,16 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  *                the prompt, the rows named by gen_idx the generated positions
  *   gen_idx      device int32 [n_gen], row indices in [0, n_tot) shared by all
  *                heads (normally N_p .. n_tot-1); NULL allowed when n_gen == 0;
- *                out-of-range entries are clamped, not reported
+ *                out-of-range entries are clamped into range, and reported
+ *                in the status word when WF_OPT_CHECK is set
  *   budgets      HOST int32 [levels + 1] = k_L, ..., k_0 with
  *                1 <= k_L <= min(N_p/2^L, WF_MAX_KEEP_TOP) and
  *                1 <= k_j <= min(2 k_{j+1}, N_p/2^j); WF_ERR_BUDGET also when
  *                the refinement state would not fit one workgroup's LDS
  *   n_q          1 .. WF_MAX_QUERIES
- *   aggregation  WF_AGG_MAX or WF_AGG_MEAN (else WF_ERR_OPTION): how the
- *                query rows combine into the scores s_j at every level
+ *   aggregation  WF_AGG_MAX or WF_AGG_MEAN, optionally ORed with
+ *                WF_OPT_CHECK (anything else: WF_ERR_OPTION): how the query
+ *                rows combine into the scores s_j at every level
  *   out          device float32 [batch, heads, n_q, head_dim]
  *   sel_out      NULL, or device int32 [batch, heads, k_0]: kept prompt
  *                tokens, ascending
@@ -333,19 +366,23 @@ uint64_t wf_attend_selected_workspace_bytes(int32_t batch, int32_t heads, int32_
  *   sel          device int32 [batch, heads, k0]: prompt rows per head (any
  *                order; ascending as wf_select_attend returns them); NULL
  *                allowed when k0 == 0; out-of-range entries are clamped
+ *                (reported with WF_OPT_CHECK)
  *   gen_idx      device int32 [n_gen], shared by all heads; NULL allowed when
- *                n_gen == 0; out-of-range entries are clamped
+ *                n_gen == 0; out-of-range entries are clamped (reported with
+ *                WF_OPT_CHECK)
  *   k0 + n_gen   >= 1
+ *   options      0 or WF_OPT_CHECK (else WF_ERR_OPTION)
  *   out          device float32 [batch, heads, n_q, head_dim]
  *   workspace    device buffer of ws_bytes >= wf_attend_selected_workspace_bytes;
  *                scratch only
  * Returns WF_ERR_SHAPE / WF_ERR_DTYPE / WF_ERR_NULL / WF_ERR_ALIGN /
- * WF_ERR_WORKSPACE / WF_ERR_BUDGET (T too long for one workgroup's list) on
- * invalid arguments, before anything is enqueued.
+ * WF_ERR_WORKSPACE / WF_ERR_BUDGET (T too long for one workgroup's list) /
+ * WF_ERR_OPTION on invalid arguments, before anything is enqueued.
  */
 int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batch, int32_t heads, int32_t n_tot,
                        int32_t head_dim, int32_t dtype, const int32_t* sel, int32_t k0, const int32_t* gen_idx,
-                       int32_t n_gen, int32_t n_q, float* out, void* workspace, uint64_t ws_bytes, void* stream);
+                       int32_t n_gen, int32_t n_q, int32_t options, float* out, void* workspace, uint64_t ws_bytes,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     WF_F32,
     WF_PYR_ALL_LEVELS,
     WF_PYR_DB2,
+    WF_OPT_CHECK,
+    CHECK_BITS,
     Pyramid,
     PreparedAttend,
     PreparedBuild,
@@ -26,6 +28,7 @@ from ._lib import (  # noqa: F401
     attend_selected,
     attend_selected_workspace_bytes,
     build_pyramid,
+    check_status,
     lib,
     pyramid_bytes,
     refresh_pyramids,

@@ -21,6 +21,9 @@ WF_AGG_MEAN = 1
 AGGREGATIONS = {"max": WF_AGG_MAX, "mean": WF_AGG_MEAN}
 WF_PYR_ALL_LEVELS = 1
 WF_PYR_DB2 = 2
+WF_OPT_CHECK = 0x100
+CHECK_BITS = {"gen_index": 1, "sel_index": 2, "nonfinite_q": 4, "nonfinite_k": 8, "nonfinite_v": 16,
+              "nonfinite_pyramid": 32}
 MAX_LEVELS = 7
 MAX_QUERIES = 64
 U64_MAX = (1 << 64) - 1
@@ -117,7 +120,10 @@ def lib():
         L.wf_attend_selected_workspace_bytes.restype = u64
         L.wf_attend_selected_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.wf_attend_selected.restype = ctypes.c_int
-        L.wf_attend_selected.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, i32, i32, vp, vp, u64, vp]
+        L.wf_attend_selected.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, i32, vp, i32, i32, i32, vp, vp, u64,
+                                         vp]
+        L.wf_check_status.restype = ctypes.c_int
+        L.wf_check_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
         _LIB = L
     return _LIB
 
@@ -353,22 +359,51 @@ def default_workspace(device):
     return ws
 
 
-def _agg_code(agg):
+def _agg_code(agg, check=False):
     if agg not in AGGREGATIONS:
         raise ValueError("agg must be 'max' or 'mean'")
-    return AGGREGATIONS[agg]
+    return AGGREGATIONS[agg] | (WF_OPT_CHECK if check else 0)
+
+
+def check_status(workspace=None, device=None):
+    """The status word the last call made with ``check=True`` left in its
+    workspace: a ``Workspace``, a uint8 device tensor, None for the default
+    workspace of ``device`` (current device) on the current stream, or the
+    string "noalloc" for the static scratch of ``select_attend_noalloc``.
+    Returns the set of names of ``CHECK_BITS`` that are set (empty: the
+    inputs met every checked precondition).  Synchronises the stream."""
+    if isinstance(workspace, str):
+        _need(workspace == "noalloc", "workspace must be a tensor, a Workspace, None or 'noalloc'")
+        dev = torch.device(device if device is not None else torch.cuda.current_device())
+        ptr = None
+    else:
+        if workspace is None:
+            dev = torch.device(device if device is not None else torch.cuda.current_device())
+            if dev.index is None:
+                dev = torch.device("cuda", torch.cuda.current_device())
+            workspace = default_workspace(dev)
+        buf = workspace.buf if isinstance(workspace, Workspace) else workspace
+        _need(isinstance(buf, torch.Tensor) and buf.is_cuda and buf.numel() >= 4, "no workspace to read")
+        dev = buf.device
+        ptr = buf.data_ptr()
+    word = ctypes.c_uint32(0)
+    st = lib().wf_check_status(ctypes.c_void_p(ptr), _stream_handle(dev), ctypes.byref(word))
+    if st != WF_OK:
+        raise WfError(st, "wf_check_status")
+    return {name for name, bit in CHECK_BITS.items() if word.value & bit}
 
 
 def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels_out=False, workspace=None,
-                  agg="max"):
+                  agg="max", check=False):
     """One step for every (sequence, head).
 
     ``agg`` combines the query rows into region scores: "max" or "mean".
+    ``check`` runs the debug input checks (read with ``check_status``).
     Returns a dict with ``out`` (float32 ``[B, H, n_q, d]``), ``sel``
     (int32 ``[B, H, k_0]``) and, with ``levels_out``, ``sel_levels`` /
     ``score_levels`` (``[B, H, sum k_j]``, level L first).
     """
-    agg_code = _agg_code(agg)
+    agg_code = _agg_code(agg, check)
     _need(isinstance(q, torch.Tensor) and q.is_cuda, "q must be a device tensor")
     _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
     B, H, n_q, d = q.shape
@@ -410,14 +445,15 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
 
 
 def select_attend_noalloc(q, pyr, k, v, gen_idx, budgets, out, sel_out=None, sel_levels=None, score_levels=None,
-                          agg="max"):
+                          agg="max", check=False):
     """``select_attend`` through ``wf_select_attend_noalloc``: the workspace is
     the library's static per-device scratch array, and the caller passes
     every output (``out`` float32 ``[B, H, n_q, d]``; optional ``sel_out``
     int32 ``[B, H, k_0]``, ``sel_levels`` int32 / ``score_levels`` float32
     ``[B, H, sum k_j]``), so nothing is allocated by this call.  Calls that
-    overlap on one device race on the scratch array."""
-    agg_code = _agg_code(agg)
+    overlap on one device race on the scratch array.  ``check``: read the
+    status with ``check_status("noalloc")``."""
+    agg_code = _agg_code(agg, check)
     _need(isinstance(q, torch.Tensor) and q.is_cuda, "q must be a device tensor")
     _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
     _need(out is not None, "out must be passed (this call allocates nothing)")
@@ -441,7 +477,7 @@ def attend_selected_workspace_bytes(batch, heads, head_dim, dtype_code, n_q, k0,
     return int(lib().wf_attend_selected_workspace_bytes(batch, heads, head_dim, dtype_code, n_q, k0, n_gen))
 
 
-def _attend_selected_args(q, k, v, sel, gen_idx, out, ws):
+def _attend_selected_args(q, k, v, sel, gen_idx, out, ws, check=False):
     B, H, n_q, d = q.shape
     k0 = 0 if sel is None else sel.shape[-1]
     n_gen = 0 if gen_idx is None else gen_idx.numel()
@@ -450,13 +486,14 @@ def _attend_selected_args(q, k, v, sel, gen_idx, out, ws):
         return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
     return (ptr(q), ptr(k), ptr(v), B, H, k.shape[2], d, _dtype_code(q), ptr(sel), k0, ptr(gen_idx), n_gen, n_q,
-            ptr(out), ptr(ws), ws.numel(), _stream_handle(q.device))
+            WF_OPT_CHECK if check else 0, ptr(out), ptr(ws), ws.numel(), _stream_handle(q.device))
 
 
-def attend_selected(q, k, v, sel, gen_idx, out=None, workspace=None):
+def attend_selected(q, k, v, sel, gen_idx, out=None, workspace=None, check=False):
     """Attention only over a selection made earlier (``sel``: int32
     ``[B, H, k0]`` prompt rows, e.g. ``select_attend(...)["sel"]``) plus the
-    generated rows ``gen_idx``.  Returns float32 ``[B, H, n_q, d]``."""
+    generated rows ``gen_idx``.  Returns float32 ``[B, H, n_q, d]``.
+    ``check`` runs the debug input checks (read with ``check_status``)."""
     _need(isinstance(q, torch.Tensor) and q.is_cuda, "q must be a device tensor")
     _need(q.dim() == 4, "q must be a 4-d [B, H, n_q, d] tensor")
     B, H, n_q, d = q.shape
@@ -471,7 +508,7 @@ def attend_selected(q, k, v, sel, gen_idx, out=None, workspace=None):
     if workspace is None:
         workspace = default_workspace(q.device)
     ws = workspace.get(need)
-    st = lib().wf_attend_selected(*_attend_selected_args(q, k, v, sel, gen_idx, out, ws))
+    st = lib().wf_attend_selected(*_attend_selected_args(q, k, v, sel, gen_idx, out, ws, check))
     if st != WF_OK:
         raise WfError(st, "wf_attend_selected")
     return out
@@ -480,7 +517,7 @@ def attend_selected(q, k, v, sel, gen_idx, out=None, workspace=None):
 class PreparedAttend:
     """An attend_selected call with its arguments marshalled once."""
 
-    def __init__(self, q, k, v, sel, gen_idx, out, workspace):
+    def __init__(self, q, k, v, sel, gen_idx, out, workspace, check=False):
         _need(isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 4, "q must be a 4-d device tensor")
         _check_attend_args(q, k, v, sel, gen_idx, out)
         B, H, n_q, d = q.shape
@@ -490,7 +527,7 @@ class PreparedAttend:
             raise WfError(-2, "PreparedAttend")
         _check_workspace(workspace, q.device, need)
         self._keep = (q, k, v, sel, gen_idx, out, workspace)
-        self._args = _attend_selected_args(q, k, v, sel, gen_idx, out, workspace)
+        self._args = _attend_selected_args(q, k, v, sel, gen_idx, out, workspace, check)
         self._fn = lib().wf_attend_selected
 
     def __call__(self):
@@ -514,7 +551,7 @@ class PreparedStep:
     loops (benchmarks, serving): calling it only crosses into the library."""
 
     def __init__(self, q, pyr, k, v, gen_idx, budgets, out, sel_out, workspace, sel_levels=None, score_levels=None,
-                 agg="max"):
+                 agg="max", check=False):
         n_gen = 0 if gen_idx is None else gen_idx.numel()
         _need(isinstance(q, torch.Tensor) and q.is_cuda and q.dim() == 4, "q must be a 4-d device tensor")
         budgets = [int(b) for b in budgets]
@@ -530,7 +567,7 @@ class PreparedStep:
             return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
         self._args = (ptr(q), ctypes.byref(pyr.desc), ptr(k), ptr(v), k.shape[2], ptr(gen_idx), n_gen, self._barr,
-                      q.shape[2], _agg_code(agg), ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels),
+                      q.shape[2], _agg_code(agg, check), ptr(out), ptr(sel_out), ptr(sel_levels), ptr(score_levels),
                       ptr(workspace), workspace.numel(), _stream_handle(q.device))
         self._fn = lib().wf_select_attend
 
@@ -563,7 +600,7 @@ def layers_workspace_bytes(pyr, n_items, n_q, n_gen, budgets):
                                                              _budget_array(budgets)))
 
 
-def select_attend_layers(layers, gen_idx, budgets, agg="max", workspace=None):
+def select_attend_layers(layers, gen_idx, budgets, agg="max", workspace=None, check=False):
     """``select_attend`` for several layers of one shape in one call.
 
     ``layers`` is a list of (q, pyr, k, v) or (q, pyr, k, v, out, sel_out);
@@ -592,7 +629,7 @@ def select_attend_layers(layers, gen_idx, budgets, agg="max", workspace=None):
     ws = workspace.get(need)
     st = lib().wf_select_attend_layers(arr, len(full), k0_.shape[2],
                                        ctypes.c_void_p(0 if gen_idx is None else gen_idx.data_ptr()), n_gen, barr,
-                                       q0.shape[2], _agg_code(agg), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                       q0.shape[2], _agg_code(agg, check), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                        _stream_handle(q0.device))
     if st != WF_OK:
         raise WfError(st, "wf_select_attend_layers")
@@ -602,7 +639,7 @@ def select_attend_layers(layers, gen_idx, budgets, agg="max", workspace=None):
 class PreparedLayers:
     """A batched select-attend call over several layers, marshalled once."""
 
-    def __init__(self, layers, gen_idx, budgets, workspace, agg="max"):
+    def __init__(self, layers, gen_idx, budgets, workspace, agg="max", check=False):
         budgets = [int(b) for b in budgets]
         self._arr = _layer_array(layers, gen_idx, budgets)
         q0, p0, k0_ = layers[0][:3]
@@ -615,7 +652,7 @@ class PreparedLayers:
         _check_workspace(workspace, q0.device, need)
         self._keep = (layers, gen_idx, workspace)
         self._args = (self._arr, len(layers), k0_.shape[2], ctypes.c_void_p(0 if gen_idx is None else gen_idx.data_ptr()),
-                      n_gen, self._barr, q0.shape[2], _agg_code(agg), ctypes.c_void_p(workspace.data_ptr()),
+                      n_gen, self._barr, q0.shape[2], _agg_code(agg, check), ctypes.c_void_p(workspace.data_ptr()),
                       workspace.numel(), _stream_handle(q0.device))
         self._fn = lib().wf_select_attend_layers
 

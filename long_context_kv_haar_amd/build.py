@@ -32,7 +32,7 @@ STEP_COMBOS = [(t, d, rt) for t in ("bf16_t", "float") for d in (128, 64) for rt
 
 def _units():
     """(name, source, extra defines) of every compile unit."""
-    units = [("wf_api", "wf_api.hip", []), ("wf_pyramid", "wf_pyramid.hip", []),
+    units = [("wf_api", "wf_api.hip", []), ("wf_pyramid", "wf_pyramid.hip", []), ("wf_check", "wf_check.hip", []),
              ("wf_step_dispatch", "wf_step.hip", [])]
     for t, d, rt in STEP_COMBOS:
         units.append((f"wf_step_{t}_{d}_{rt}", "wf_step.hip",

@@ -157,7 +157,7 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
-  uint64_t w = 0;
+  uint64_t w = wf::kStatusBytes;  // the debug status word comes first
   P->off_keys = w;     w += align_up(H * (uint64_t)P->n_top * 4);
   P->off_sel_top = w;  w += align_up(H * (uint64_t)P->k_top * 4);
   P->off_cov = w;      w += align_up(H * (uint64_t)(P->cov_len > 0 ? P->cov_len : 1) * 4);
@@ -192,11 +192,35 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
   if (buf_bytes > budget) return WF_ERR_BUDGET;
   P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
   const uint64_t H = (uint64_t)P->heads_total;
-  uint64_t w = 0;
+  uint64_t w = wf::kStatusBytes;  // the debug status word comes first
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * head_dim * 4);
   P->total = w;
   return WF_OK;
+}
+
+// The scan of WF_OPT_CHECK over one set of inputs (the status word is
+// cleared by the caller once per call).
+hipError_t check_inputs(const void* q, const void* k, const void* v, const wf_pyramid* pyr, int64_t heads_total,
+                        int n_q, int n_tot, int head_dim, int dtype, const int32_t* gen_idx, int n_gen,
+                        const int32_t* sel, int64_t n_sel, void* workspace, hipStream_t s) {
+  wf::CheckArgs c;
+  const int64_t es = elem_bytes(dtype);
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.a_top = pyr ? reinterpret_cast<const float*>(pyr->base) : nullptr;
+  c.q_bytes = heads_total * n_q * head_dim * es;
+  c.kv_bytes = heads_total * (int64_t)n_tot * head_dim * es;
+  c.a_bytes = pyr ? heads_total * (int64_t)(pyr->n_prompt >> pyr->levels) * head_dim * 4 : 0;
+  c.gen_idx = n_gen > 0 ? gen_idx : nullptr;
+  c.n_gen = n_gen;
+  c.sel = n_sel > 0 ? sel : nullptr;
+  c.n_sel = n_sel;
+  c.n_tot = n_tot;
+  c.bf16 = dtype == WF_BF16;
+  c.status = reinterpret_cast<uint32_t*>(workspace);
+  return wf::launch_check(c, s);
 }
 
 }  // namespace
@@ -379,6 +403,8 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
                      void* workspace, uint64_t ws_bytes, void* stream) {
   if (!q || !pyr || !k || !v || !out || !workspace || !budgets) return WF_ERR_NULL;
   if (n_gen > 0 && !gen_idx) return WF_ERR_NULL;
+  const bool check = (aggregation & WF_OPT_CHECK) != 0;
+  aggregation &= ~WF_OPT_CHECK;
   if (aggregation != WF_AGG_MAX && aggregation != WF_AGG_MEAN) return WF_ERR_OPTION;
   wf::SelectPlan P;
   const int st = make_plan(pyr, n_q, n_gen, budgets, &P);
@@ -409,7 +435,12 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
   a.sel_levels = sel_levels;
   a.score_levels = score_levels;
   a.ws = reinterpret_cast<uint8_t*>(workspace);
-  if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (check && (wf::launch_check_clear(reinterpret_cast<uint32_t*>(workspace), s) != hipSuccess ||
+                check_inputs(q, k, v, pyr, P.heads_total, n_q, n_tot, pyr->head_dim, pyr->dtype, gen_idx, n_gen,
+                             nullptr, 0, workspace, s) != hipSuccess))
+    return WF_ERR_HIP;
+  if (wf::launch_select_attend(a, s) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;
 }
 
@@ -443,6 +474,8 @@ int wf_select_attend_layers(const wf_layer_item* items, int32_t n_items, int32_t
   if (!items || !workspace || !budgets) return WF_ERR_NULL;
   if (n_items < 1 || n_items > WF_MAX_LAYER_ITEMS) return WF_ERR_SHAPE;
   if (n_gen > 0 && !gen_idx) return WF_ERR_NULL;
+  const bool check = (aggregation & WF_OPT_CHECK) != 0;
+  aggregation &= ~WF_OPT_CHECK;
   if (aggregation != WF_AGG_MAX && aggregation != WF_AGG_MEAN) return WF_ERR_OPTION;
   const wf_pyramid* p0 = items[0].pyr;
   for (int i = 0; i < n_items; ++i) {
@@ -484,7 +517,16 @@ int wf_select_attend_layers(const wf_layer_item* items, int32_t n_items, int32_t
   a.sel_levels = nullptr;
   a.score_levels = nullptr;
   a.ws = reinterpret_cast<uint8_t*>(workspace);
-  if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (check) {
+    if (wf::launch_check_clear(reinterpret_cast<uint32_t*>(workspace), s) != hipSuccess) return WF_ERR_HIP;
+    for (int i = 0; i < n_items; ++i)
+      if (check_inputs(items[i].q, items[i].k, items[i].v, items[i].pyr, a.heads_per_item, n_q, n_tot,
+                       p0->head_dim, p0->dtype, i == 0 ? gen_idx : nullptr, i == 0 ? n_gen : 0, nullptr, 0,
+                       workspace, s) != hipSuccess)
+        return WF_ERR_HIP;
+  }
+  if (wf::launch_select_attend(a, s) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;
 }
 
@@ -497,9 +539,11 @@ uint64_t wf_attend_selected_workspace_bytes(int32_t batch, int32_t heads, int32_
 
 int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batch, int32_t heads, int32_t n_tot,
                        int32_t head_dim, int32_t dtype, const int32_t* sel, int32_t k0, const int32_t* gen_idx,
-                       int32_t n_gen, int32_t n_q, float* out, void* workspace, uint64_t ws_bytes, void* stream) {
+                       int32_t n_gen, int32_t n_q, int32_t options, float* out, void* workspace, uint64_t ws_bytes,
+                       void* stream) {
   if (!q || !k || !v || !out || !workspace) return WF_ERR_NULL;
   if ((k0 > 0 && !sel) || (n_gen > 0 && !gen_idx)) return WF_ERR_NULL;
+  if (options & ~WF_OPT_CHECK) return WF_ERR_OPTION;
   wf::SelectPlan P;
   const int st = make_attend_plan(batch, heads, head_dim, dtype, n_q, k0, n_gen, &P);
   if (st != WF_OK) return st;
@@ -525,7 +569,28 @@ int wf_attend_selected(const void* q, const void* k, const void* v, int32_t batc
   a.sel_levels = nullptr;
   a.score_levels = nullptr;
   a.ws = reinterpret_cast<uint8_t*>(workspace);
-  if (wf::launch_select_attend(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return WF_ERR_HIP;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((options & WF_OPT_CHECK) &&
+      (wf::launch_check_clear(reinterpret_cast<uint32_t*>(workspace), s) != hipSuccess ||
+       check_inputs(q, k, v, nullptr, P.heads_total, n_q, n_tot, head_dim, dtype, gen_idx, n_gen, sel,
+                    (int64_t)P.heads_total * k0, workspace, s) != hipSuccess))
+    return WF_ERR_HIP;
+  if (wf::launch_select_attend(a, s) != hipSuccess) return WF_ERR_HIP;
+  return WF_OK;
+}
+
+int wf_check_status(const void* workspace, void* stream, uint32_t* status) {
+  if (!status) return WF_ERR_NULL;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const void* src = workspace;
+  if (!src) {
+    void* p = nullptr;
+    const int st = device_scratch(s, &p);
+    if (st != WF_OK) return st;
+    src = p;
+  }
+  if (hipMemcpyAsync(status, src, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return WF_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return WF_ERR_HIP;
   return WF_OK;
 }
 

@@ -75,6 +75,26 @@ struct SelectLaunch {
 
 hipError_t launch_select_attend(const SelectLaunch& a, hipStream_t s);
 
+// The input checks of WF_OPT_CHECK (wf_check.hip): the status word sits in
+// the first kStatusBytes of every workspace.
+constexpr uint64_t kStatusBytes = 256;
+struct CheckArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* a_top;     // NULL: no pyramid to check
+  int64_t q_bytes, kv_bytes, a_bytes;
+  const int32_t* gen_idx;
+  int64_t n_gen;
+  const int32_t* sel;     // NULL: no selection handed in
+  int64_t n_sel;
+  int n_tot;              // index entries must lie in [0, n_tot)
+  bool bf16;
+  uint32_t* status;
+};
+hipError_t launch_check_clear(uint32_t* status, hipStream_t s);
+hipError_t launch_check(const CheckArgs& c, hipStream_t s);
+
 // Waves per SIMD the attention kernel is compiled for: with two query tiles
 // its 256-thread workgroup fits 256 registers without spilling, so two
 // workgroups share a compute unit; larger workgroups take one each.

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     L = lib()
     for n in names:
         assert hasattr(L, n), n
@@ -116,13 +116,32 @@ def test_select_attend_rejects_bad_arguments():
     assert select(ws_bytes=64) == -6
     assert select(agg=2) == -10
     assert select(agg=-1) == -10
+    assert select(agg=0x200) == -10                                  # an undefined option bit
+    assert select(agg=wf.WF_AGG_MEAN | 0x200) == -10
+    assert select(agg=wf.WF_AGG_MEAN | wf.WF_OPT_CHECK, ws_bytes=64) == -6   # the check bit is accepted
+
+
+def test_check_bits_match_the_header():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define WF_OPT_CHECK (0x[0-9a-fA-F]+)", text).group(1), 16) == wf.WF_OPT_CHECK
+    for name, bit in wf.CHECK_BITS.items():
+        m = re.search(rf"#define WF_CHECK_{name.upper()} (\d+)u", text)
+        assert m and int(m.group(1)) == bit, name
+
+
+def test_workspaces_start_with_the_status_word():
+    # the status word takes the first 256 bytes of every workspace
+    p = fake_pyramid()
+    a = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]))
+    b = lib().wf_attend_selected_workspace_bytes(1, 2, 64, wf.WF_BF16, 32, 64, 32)
+    assert a > 256 and b > 256 and a % 256 == 0 and b % 256 == 0
 
 
 def attend_sel(q=FAKE, k=FAKE, v=FAKE, B=1, H=2, n_tot=1100, d=64, dt=wf.WF_BF16, sel=FAKE, k0=64, gen=FAKE, n_gen=8,
-               n_q=32, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+               n_q=32, options=0, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
     return lib().wf_attend_selected(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), B, H, n_tot, d, dt,
-                                    ctypes.c_void_p(sel), k0, ctypes.c_void_p(gen), n_gen, n_q, ctypes.c_void_p(out),
-                                    ctypes.c_void_p(ws), ws_bytes, None)
+                                    ctypes.c_void_p(sel), k0, ctypes.c_void_p(gen), n_gen, n_q, options,
+                                    ctypes.c_void_p(out), ctypes.c_void_p(ws), ws_bytes, None)
 
 
 def test_attend_selected_rejects_bad_arguments():
@@ -142,6 +161,8 @@ def test_attend_selected_rejects_bad_arguments():
     assert attend_sel(q=MISALIGNED) == -7
     assert attend_sel(sel=FAKE + 2) == -7
     assert attend_sel(ws_bytes=need - 1) == -6
+    assert attend_sel(options=1) == -10            # WF_ERR_OPTION: only WF_OPT_CHECK is defined
+    assert attend_sel(options=wf.WF_OPT_CHECK, q=MISALIGNED) == -7   # the check bit itself is accepted
 
 
 def refresh(items, n=None):
