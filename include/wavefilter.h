@@ -91,9 +91,18 @@ int wf_check_status(const void* workspace, void* stream, uint32_t* status);
 
 /* How the n_q query rows combine into one region score (Figure 2 (c) scores
  * regions by the queries' correlation with the low-frequency keys and leaves
- * the combination of the rows open): the maximum over the rows, or their
- * mean (which equals the score of the averaged query row). */
-enum { WF_AGG_MAX = 0, WF_AGG_MEAN = 1 };
+ * the combination of the rows open): the maximum over the rows of the
+ * scaled logits l_i[c] = q_i . A_j[c] / sqrt(d), or their mean (which equals
+ * the score of the averaged query row); or, with each row's logits turned
+ * into attention probabilities by a softmax over the level's candidate set
+ * (all n_L regions at level L, the children of the kept regions below;
+ * section 1 names the attention mechanism as the measure of relevance),
+ * p_i[c] = exp(l_i[c]) / sum_c' exp(l_i[c']), the maximum or the mean over
+ * the rows of p_i[c].  The softmax variants need a covered set of at most
+ * 8 192 positions (k_L 2^L), one layer per call and a Haar pyramid without
+ * stored bands (else WF_ERR_BUDGET / WF_ERR_OPTION), and a workspace with
+ * every row's logits. */
+enum { WF_AGG_MAX = 0, WF_AGG_MEAN = 1, WF_AGG_SOFTMAX_MAX = 2, WF_AGG_SOFTMAX_MEAN = 3 };
 
 /* Element types of q, k and v. */
 enum { WF_F32 = 0, WF_BF16 = 1 };
@@ -225,7 +234,7 @@ int wf_refresh_pyramids(const wf_refresh_item* items, int32_t n_items, void* str
  * invalid.  `budgets` is the host array k_L, ..., k_0 (levels + 1 entries).
  */
 uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen,
-                                          const int32_t* budgets);
+                                          const int32_t* budgets, int32_t aggregation);
 
 /*
  * One denoising step of WaveFilter for every (sequence, head):
@@ -255,9 +264,10 @@ uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, in
  *                1 <= k_j <= min(2 k_{j+1}, N_p/2^j); WF_ERR_BUDGET also when
  *                the refinement state would not fit one workgroup's LDS
  *   n_q          1 .. WF_MAX_QUERIES
- *   aggregation  WF_AGG_MAX or WF_AGG_MEAN, optionally ORed with
- *                WF_OPT_CHECK (anything else: WF_ERR_OPTION): how the query
- *                rows combine into the scores s_j at every level
+ *   aggregation  WF_AGG_MAX, WF_AGG_MEAN, WF_AGG_SOFTMAX_MAX or
+ *                WF_AGG_SOFTMAX_MEAN, optionally ORed with WF_OPT_CHECK
+ *                (anything else: WF_ERR_OPTION): how the query rows combine
+ *                into the scores s_j at every level
  *   out          device float32 [batch, heads, n_q, head_dim]
  *   sel_out      NULL, or device int32 [batch, heads, k_0]: kept prompt
  *                tokens, ascending

@@ -18,7 +18,10 @@ WF_F32 = 0
 WF_BF16 = 1
 WF_AGG_MAX = 0
 WF_AGG_MEAN = 1
-AGGREGATIONS = {"max": WF_AGG_MAX, "mean": WF_AGG_MEAN}
+WF_AGG_SOFTMAX_MAX = 2
+WF_AGG_SOFTMAX_MEAN = 3
+AGGREGATIONS = {"max": WF_AGG_MAX, "mean": WF_AGG_MEAN, "softmax_max": WF_AGG_SOFTMAX_MAX,
+                "softmax_mean": WF_AGG_SOFTMAX_MEAN}
 WF_PYR_ALL_LEVELS = 1
 WF_PYR_DB2 = 2
 WF_OPT_CHECK = 0x100
@@ -105,7 +108,7 @@ def lib():
         L.wf_build_pyramid.restype = ctypes.c_int
         L.wf_build_pyramid.argtypes = [vp, i64, i32, i32, i32, i32, i32, i32, u32, vp, u64, pyr_p, vp]
         L.wf_select_attend_workspace_bytes.restype = u64
-        L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p]
+        L.wf_select_attend_workspace_bytes.argtypes = [pyr_p, i32, i32, i32p, i32]
         L.wf_select_attend.restype = ctypes.c_int
         L.wf_select_attend.argtypes = [vp, pyr_p, vp, vp, i32, vp, i32, i32p, i32, i32, vp, vp, vp, vp, vp, u64, vp]
         L.wf_select_attend_noalloc.restype = ctypes.c_int
@@ -327,8 +330,9 @@ def _check_workspace(ws, dev, need):
     _need(ws.numel() >= need, f"workspace holds {ws.numel()} bytes, the call needs {need}")
 
 
-def workspace_bytes(pyr, n_q, n_gen, budgets):
-    return int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, _budget_array(budgets)))
+def workspace_bytes(pyr, n_q, n_gen, budgets, agg="max"):
+    return int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, _budget_array(budgets),
+                                                      _agg_code(agg)))
 
 
 class Workspace:
@@ -361,7 +365,7 @@ def default_workspace(device):
 
 def _agg_code(agg, check=False):
     if agg not in AGGREGATIONS:
-        raise ValueError("agg must be 'max' or 'mean'")
+        raise ValueError(f"agg must be one of {sorted(AGGREGATIONS)}")
     return AGGREGATIONS[agg] | (WF_OPT_CHECK if check else 0)
 
 
@@ -422,7 +426,7 @@ def select_attend(q, pyr, k, v, gen_idx, budgets, out=None, sel_out=None, levels
         score_levels = torch.empty((B, H, sum(budgets)), dtype=torch.float32, device=dev)
     _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out, sel_levels, score_levels)
     barr = _budget_array(budgets)
-    ws_need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, barr))
+    ws_need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), n_q, n_gen, barr, agg_code))
     if ws_need == 0:
         raise WfError(-5, "wf_select_attend_workspace_bytes")
     if workspace is None:
@@ -558,7 +562,8 @@ class PreparedStep:
         _check_select_args(q, pyr, k, v, gen_idx, budgets, out, sel_out, sel_levels, score_levels)
         self._keep = (q, pyr, k, v, gen_idx, out, sel_out, workspace, sel_levels, score_levels)
         self._barr = _budget_array(budgets)
-        need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), q.shape[2], n_gen, self._barr))
+        need = int(lib().wf_select_attend_workspace_bytes(ctypes.byref(pyr.desc), q.shape[2], n_gen, self._barr,
+                                                          _agg_code(agg)))
         if need == 0:
             raise WfError(-5, "PreparedStep")
         _check_workspace(workspace, q.device, need)

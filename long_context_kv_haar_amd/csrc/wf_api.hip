@@ -69,15 +69,19 @@ bool pyramid_ok(const wf_pyramid* p) {
 // Resolve budgets and the workspace layout for n_items layers of the
 // pyramid's shape; returns a status.
 int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* budgets, wf::SelectPlan* P,
-              int32_t n_items = 1) {
+              int32_t n_items = 1, int32_t aggregation = WF_AGG_MAX) {
   if (!pyramid_ok(pyr)) return pyr ? WF_ERR_PYRAMID : WF_ERR_NULL;
   if (!budgets) return WF_ERR_NULL;
   if (n_q < 1 || n_q > WF_MAX_QUERIES || n_gen < 0) return WF_ERR_SHAPE;
   if (n_items < 1 || n_items > WF_MAX_LAYER_ITEMS) return WF_ERR_SHAPE;
   if ((int64_t)n_items * pyr->batch * pyr->heads > WF_MAX_HEADS) return WF_ERR_SHAPE;
+  if (aggregation < WF_AGG_MAX || aggregation > WF_AGG_SOFTMAX_MEAN) return WF_ERR_OPTION;
   memset(P, 0, sizeof(*P));
   const int L = pyr->levels;
   P->heads_total = n_items * pyr->batch * pyr->heads;
+  P->soft = aggregation == WF_AGG_SOFTMAX_MAX ? 1 : (aggregation == WF_AGG_SOFTMAX_MEAN ? 2 : 0);
+  // softmax scores: one layer per call, Haar pyramids without stored bands
+  if (P->soft && (n_items != 1 || (pyr->flags & WF_PYR_DB2))) return WF_ERR_OPTION;
   P->n_q = n_q;
   P->n_prompt = pyr->n_prompt;
   P->n_top = pyr->n_prompt >> L;
@@ -165,6 +169,16 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   P->off_sel = w;      w += align_up(H * (uint64_t)(P->k0 > 0 ? P->k0 : 1) * 4);
   P->off_part_ml = w;  w += align_up(H * (uint64_t)P->n_split * 2 * n_q * 4);
   P->off_part_o = w;   w += align_up(H * (uint64_t)P->n_split * n_q * P->head_dim * 4);
+  // softmax scores: every query row's logits, level L [n_q][n_top4] then
+  // levels 0 .. L-1 [n_q][padded level length], per head; and the
+  // refinement's LDS (kept coarse regions, the candidate list, row lse)
+  P->n_top4 = (P->n_top + 3) & ~3;
+  P->off_logits = w;
+  if (P->soft) {
+    if (L > 0 && P->refine_s0 == 0) return WF_ERR_BUDGET;  // covered sets beyond 8 192 positions
+    w += align_up(H * (uint64_t)n_q * ((uint64_t)P->n_top4 + (uint64_t)P->cov_len) * 4);
+    P->refine_soft_lds = (int)(4 * (((int64_t)P->k_top + 3) / 4 * 4 + P->covered + 64));
+  }
   P->total = w;
   return WF_OK;
 }
@@ -391,9 +405,9 @@ int wf_refresh_pyramids(const wf_refresh_item* items, int32_t n_items, void* str
 }
 
 uint64_t wf_select_attend_workspace_bytes(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen,
-                                          const int32_t* budgets) {
+                                          const int32_t* budgets, int32_t aggregation) {
   wf::SelectPlan P;
-  if (make_plan(pyr, n_q, n_gen, budgets, &P) != WF_OK) return 0;
+  if (make_plan(pyr, n_q, n_gen, budgets, &P, 1, aggregation & ~WF_OPT_CHECK) != WF_OK) return 0;
   return P.total;
 }
 
@@ -405,9 +419,9 @@ int wf_select_attend(const void* q, const wf_pyramid* pyr, const void* k, const 
   if (n_gen > 0 && !gen_idx) return WF_ERR_NULL;
   const bool check = (aggregation & WF_OPT_CHECK) != 0;
   aggregation &= ~WF_OPT_CHECK;
-  if (aggregation != WF_AGG_MAX && aggregation != WF_AGG_MEAN) return WF_ERR_OPTION;
+  if (aggregation < WF_AGG_MAX || aggregation > WF_AGG_SOFTMAX_MEAN) return WF_ERR_OPTION;
   wf::SelectPlan P;
-  const int st = make_plan(pyr, n_q, n_gen, budgets, &P);
+  const int st = make_plan(pyr, n_q, n_gen, budgets, &P, 1, aggregation);
   if (st != WF_OK) return st;
   if (n_tot < pyr->n_prompt || n_tot < 1) return WF_ERR_SHAPE;
   P.n_tot = n_tot;
@@ -450,7 +464,7 @@ int wf_select_attend_noalloc(const void* q, const wf_pyramid* pyr, const void* k
                              float* score_levels, void* stream) {
   if (!q || !pyr || !k || !v || !out || !budgets) return WF_ERR_NULL;
   wf::SelectPlan P;
-  const int st = make_plan(pyr, n_q, n_gen, budgets, &P);
+  const int st = make_plan(pyr, n_q, n_gen, budgets, &P, 1, aggregation & ~WF_OPT_CHECK);
   if (st != WF_OK) return st;
   if (P.total > WF_NOALLOC_SCRATCH_BYTES) return WF_ERR_WORKSPACE;
   void* ws = nullptr;

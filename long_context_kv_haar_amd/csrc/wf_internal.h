@@ -46,11 +46,14 @@ struct SelectPlan {
   int refine_cov_in_lds;        // list-based refinement: coverage scores staged in LDS
   int refine_lds;               // list-based refinement workgroup: its state
   int stored_bands;             // levels 1 .. L-1 scored from stored A_j (longer bases)
+  int soft;                     // softmax-probability scores: 0 off, 1 maximum, 2 mean over the query rows
+  int n_top4;                   // n_top rounded up to a multiple of four (the row stride of level-L logits)
+  int refine_soft_lds;          // softmax refinement workgroup: kept coarse regions + candidate list
   uint64_t band_off[kMaxLevels];  // byte offset of A_j inside the pyramid buffer, when stored
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + K/V chunk buffers
   // workspace sections (byte offsets)
-  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, total;
+  uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, off_logits, total;
 };
 
 struct SelectLaunch {

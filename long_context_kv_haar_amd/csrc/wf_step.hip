@@ -69,6 +69,11 @@ struct StepArgs {
   float inv_sqrt_d;
   float inv_nq;  // 1 / n_q, for the mean over query rows
   int stored_bands;                    // score levels 1 .. L-1 from stored A_j (longer bases)
+  // softmax-probability scores (0: off, 1: maximum, 2: mean over the rows):
+  // every row's scaled logits per head, level L [n_q][n_top4], then level j
+  // [n_q][padded level length] at n_q * n_top4 + n_q * cov_off[j]
+  int soft, n_top4;
+  float* logits;
   const float* band_a[kMaxLevels];     // A_j [heads_total][n_prompt >> j][d], when stored
 };
 
@@ -263,7 +268,14 @@ __device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, uns
 // Where the coarse Top-K runs: in every cover workgroup of the head (each
 // computes the same set; n_L <= 1 024 and L > 0), else in a launch of its
 // own, one workgroup per head.
-__device__ __forceinline__ bool topk_in_cover(const StepArgs& a) { return a.topk_s >= 1 && a.topk_s <= 4 && a.levels > 0; }
+__device__ __forceinline__ bool topk_in_cover(const StepArgs& a) {
+  return a.topk_s >= 1 && a.topk_s <= 4 && a.levels > 0 && a.soft == 0;
+}
+
+// The softmax scores' logits of one head (level L first).
+__device__ __forceinline__ float* head_logits(const StepArgs& a, int head) {
+  return a.logits + (int64_t)head * a.n_q * (a.n_top4 + a.cov_len);
+}
 
 // The coarse Top-K's outputs beside emit_sel(o, i): the kept regions
 // (workgroup `writer` of the head only), the level-L sinks, and for L = 0
@@ -282,7 +294,7 @@ __device__ __forceinline__ auto coarse_emitter(const StepArgs& a, int head, bool
     emit_sel(o, i);
     if (sel_g) sel_g[o] = i;
     if (dbg_sel) dbg_sel[o] = i;
-    if (dbg_score) dbg_score[o] = sc;
+    if (dbg_score) dbg_score[o] = a.soft ? expf(sc) : sc;  // softmax scores are ranked as log-probabilities
     if (tsel) {
       tsel[o] = i;
       if (tout) tout[o] = i;
@@ -352,6 +364,19 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
 #pragma unroll
     for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(b, qf[qt], acc[qt]);
+  }
+  if (a.soft) {  // uniform: every query row's scaled logits, for the softmax scores
+    float* lg = head_logits(a, head);
+    const int n0 = blockIdx.x * 64 + w * 16 + 4 * g;
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt) {
+      const int query = 16 * qt + l16;
+      if (query < a.n_q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n0 + r < a.n_top) lg[(int64_t)query * a.n_top4 + n0 + r] = acc[qt][r] * a.inv_sqrt_d;
+    }
+    return;
   }
   float m[4];
 #pragma unroll
@@ -582,6 +607,14 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       lvl[2 * j + 1] = rmx;
     }
   };
+  // softmax scores: every query row's level-j logits (the block sums scaled
+  // by 2^{-j/2} / sqrt(d)), row `query` of level j at lg(j) + query * plen(j)
+  const bool soft = a.soft != 0;
+  float* lgh = soft ? head_logits(a, head) + (int64_t)a.n_q * a.n_top4 : nullptr;
+  auto lgrow = [&](int j, int query) {
+    return lgh + (int64_t)a.n_q * a.cov_off[j] + (int64_t)query * ((((a.covered >> j) + 3) >> 2) << 2);
+  };
+  const float isd_raw = a.inv_sqrt_d;
   // level 0
   rmn = 0xFFFFFFFFu;
   rmx = 0u;
@@ -598,6 +631,12 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
     const int64_t p = tb + 16 * t;
     if (writer && p < a.covered)  // (level arrays are padded to multiples of four)
       *reinterpret_cast<float4*>(cov + a.cov_off[0] + p) = make_float4(m[0], m[1], m[2], m[3]);
+    if (soft && p < a.covered)
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt)
+        if (16 * qt + l16 < a.n_q)
+          *reinterpret_cast<float4*>(lgrow(0, 16 * qt + l16) + p) =
+              make_float4(s[t][qt][0] * isd_raw, s[t][qt][1] * isd_raw, s[t][qt][2] * isd_raw, s[t][qt][3] * isd_raw);
 #pragma unroll
     for (int r = 0; r < 4; ++r) track(writer && p + r < a.covered, m[r]);
   }
@@ -625,6 +664,13 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       }
       const int64_t p = tb + 16 * t;
       if (writer && p < a.covered) *reinterpret_cast<float2*>(cov + a.cov_off[1] + (p >> 1)) = make_float2(m[0], m[1]);
+      if (soft && p < a.covered) {
+        const float f = isd_raw * 0.70710678118654752440f;
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt)
+          if (16 * qt + l16 < a.n_q)
+            *reinterpret_cast<float2*>(lgrow(1, 16 * qt + l16) + (p >> 1)) = make_float2(s[t][qt][0] * f, s[t][qt][2] * f);
+      }
       track(writer && p < a.covered, m[0]);
       track(writer && p + 2 < a.covered, m[1]);
     }
@@ -646,6 +692,10 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
       if (writer && p < a.covered) cov[a.cov_off[2] + (p >> 2)] = x;
+      if (soft && p < a.covered)
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt)
+          if (16 * qt + l16 < a.n_q) lgrow(2, 16 * qt + l16)[p >> 2] = s[t][qt][0] * (isd_raw * 0.5f);
       track(writer && p < a.covered, x);
     }
   }
@@ -666,6 +716,11 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       x = AG::row(x) * sc;
       const int64_t p = tb + 16 * t;
       if (writer && (g & 1) == 0 && p < a.covered) cov[a.cov_off[3] + (p >> 3)] = x;
+      if (soft && (g & 1) == 0 && p < a.covered)
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt)
+          if (16 * qt + l16 < a.n_q)
+            lgrow(3, 16 * qt + l16)[p >> 3] = s[t][qt][0] * (isd_raw * 0.35355339059327376220f);
       track(writer && (g & 1) == 0 && p < a.covered, x);
     }
   }
@@ -686,6 +741,10 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       x = AG::row(x) * sc;
       const int64_t p = wave_base + 16 * t;
       if (writer && g == 0 && p < a.covered) cov[a.cov_off[4] + (p >> 4)] = x;
+      if (soft && g == 0 && p < a.covered)
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt)
+          if (16 * qt + l16 < a.n_q) lgrow(4, 16 * qt + l16)[p >> 4] = s[t][qt][0] * (isd_raw * 0.25f);
       track(writer && g == 0 && p < a.covered, x);
     }
   }
@@ -711,6 +770,16 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
       if (wave_base + 32 < a.covered) cov[a.cov_off[5] + (wave_base >> 5) + 1] = x23;
       if (jmax > 6) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
     }
+    if (soft && g == 0)
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) {
+        const int query = 16 * qt + l16;
+        if (query >= a.n_q) continue;
+        const float a01 = s[0][qt][0] + s[1][qt][0], a23 = s[2][qt][0] + s[3][qt][0];
+        if (wave_base < a.covered) lgrow(5, query)[wave_base >> 5] = a01 * (isd_raw * 0.17677669529663688110f);
+        if (wave_base + 32 < a.covered) lgrow(5, query)[(wave_base >> 5) + 1] = a23 * (isd_raw * 0.17677669529663688110f);
+        if (jmax > 6) lgrow(6, query)[wave_base >> 6] = (a01 + a23) * (isd_raw * 0.125f);
+      }
     rmn = 0xFFFFFFFFu;
     rmx = 0u;
     track(lane == 0 && wave_base < a.covered, x01);
@@ -1067,6 +1136,199 @@ __global__ __launch_bounds__(kSelThreads) void coarse_topk_kernel(StepArgs a) {
   __shared__ __align__(16) unsigned char raw[kSelRawBytes];
   const int head = blockIdx.x;
   coarse_topk_run<true>(a, head, raw, keys_l, coarse_emitter(a, head, true, [](int, int) {}));
+}
+
+// ---------------------------------------------------------------------------
+// Softmax-probability scores.  A query row's probability of candidate c at a
+// level is p_i[c] = exp(l_i[c] - lse_i), lse_i = log sum over the level's
+// candidates c' of exp(l_i[c']), from the per-row logits l_i the coarse and
+// cover launches wrote; the score is max_i p_i[c] or (1/n_q) sum_i p_i[c].
+// Candidates are ranked by the logarithm of that score (a monotone map, so
+// the same ones are kept): probabilities far below the largest (exp(-100)
+// and less) underflow float32 and would tie at zero, their logarithms do
+// not.  The per-level score outputs report the probabilities themselves.
+// ---------------------------------------------------------------------------
+// Online log-sum-exp: (m, s) with s = sum exp(x - m) over the values seen.
+__device__ __forceinline__ void lse_add(float& m, float& s, float x) {
+  if (x > m) {
+    s = s * expf(m - x) + 1.f;
+    m = x;
+  } else {
+    s += expf(x - m);
+  }
+}
+// Merge the state of lane ^ off into this lane's.
+__device__ __forceinline__ void lse_merge(float& m, float& s, int off) {
+  const float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
+  const float mm = fmaxf(m, m2);
+  s = (m == -INFINITY ? 0.f : s * expf(m - mm)) + (m2 == -INFINITY ? 0.f : s2 * expf(m2 - mm));
+  m = mm;
+}
+// The logarithm of one candidate's score from its column of logits (row
+// stride `stride`): max_i (l_i - lse_i), or the log of the mean over the rows
+// of exp(l_i - lse_i) by an online log-sum-exp.
+__device__ __forceinline__ float soft_score(const StepArgs& a, const float* col, int64_t stride, const float* lse) {
+  if (a.soft == 1) {
+    float m = -INFINITY;
+    for (int r = 0; r < a.n_q; ++r) m = fmaxf(m, col[(int64_t)r * stride] - lse[r]);
+    return m;
+  }
+  float m = -INFINITY, sum = 0.f;
+  for (int r = 0; r < a.n_q; ++r) lse_add(m, sum, col[(int64_t)r * stride] - lse[r]);
+  return m + logf(sum * a.inv_nq);
+}
+
+// Level L (every region a candidate): each row's log-sum-exp (four threads
+// per row), then every region's score as an order key for the coarse Top-K
+// launch that follows.
+__global__ __launch_bounds__(kSelThreads) void soft_top_kernel(StepArgs a) {
+  __shared__ float lse[64];
+  const int head = blockIdx.x, t = threadIdx.x;
+  const float* lg = head_logits(a, head);
+  {
+    const int row = t >> 2, part = t & 3;
+    float m = -INFINITY, sum = 0.f;
+    if (row < a.n_q)
+      for (int c = part; c < a.n_top; c += 4) lse_add(m, sum, lg[(int64_t)row * a.n_top4 + c]);
+    lse_merge(m, sum, 1);
+    lse_merge(m, sum, 2);
+    if (part == 0 && row < a.n_q) lse[row] = m + logf(sum);
+  }
+  __syncthreads();
+  uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
+  for (int c = t; c < a.n_top; c += kSelThreads) keys[c] = order_key(soft_score(a, lg + c, a.n_top4, lse));
+}
+
+// The refinement with softmax scores: refine_sel's slot layout and level
+// loop, with each level's scores formed in the loop: the candidates (valid
+// positions) are listed in LDS, each row's log-sum-exp over them is taken by
+// 16 threads per row, then every slot's score from its column of logits and
+// the level's score range for the binning.
+template <int S0>
+__global__ __launch_bounds__(kRefineThreads) void refine_soft_kernel(StepArgs a) {
+  constexpr int NT = kRefineThreads;
+  extern __shared__ __align__(16) uint32_t lds[];  // kept coarse regions [k_L], then the candidate list
+  __shared__ __align__(16) SelShared<NT> sh;
+  __shared__ float lse[64];
+  __shared__ uint32_t smn, smx;
+  const int head = blockIdx.x, t = threadIdx.x, lane = t & 63;
+  const int L = a.levels;
+  const int covered = (int)a.covered;
+  int* sel_l = reinterpret_cast<int*>(lds);
+  int* clist = sel_l + ((a.k_top + 3) & ~3);
+  for (int i = t; i < a.k_top; i += NT) sel_l[i] = clampi(a.sel_top[(int64_t)head * a.k_top + i], 0, a.n_top - 1);
+  sel_init(sh);
+  __syncthreads();
+  const float* lgh = head_logits(a, head) + (int64_t)a.n_q * a.n_top4;
+
+  uint32_t keptp = 0u;  // level L: every kept coarse region
+  {
+    const int pl0 = (t * S0) >> L;
+    const int pl = (S0 >> L) > 0 ? (S0 >> L) : 1;
+    for (int m = 0; m < pl; ++m) keptp |= (pl0 + m < a.k_top) ? (1u << m) : 0u;
+  }
+  const bool report = a.sel_levels || a.score_levels;
+  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  int off = a.k_top;
+  SelCursor cur;
+  for (int j = L - 1; j >= 0; --j) {
+    const int pj = (S0 >> j) > 0 ? (S0 >> j) : 1;
+    const int p0 = (t * S0) >> j, nj = covered >> j;
+    const bool own = pj > 1 || ((t * S0) & ((1 << j) - 1)) == 0;
+    uint32_t valid = 0u;
+#pragma unroll
+    for (int i = 0; i < S0; ++i)
+      valid |= ((i < pj) & (p0 + i < nj) & ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
+    const uint32_t owned = own ? valid : 0u;
+    const int64_t plen = ((nj + 3) >> 2) << 2;
+    const float* lgj = lgh + (int64_t)a.n_q * a.cov_off[j];
+    // 1. the candidates, ascending
+    int nv;
+    {
+      int o = block_excl_scan(__popc(owned), sh, 4 + (j & 1), &nv);
+#pragma unroll
+      for (int i = 0; i < S0; ++i)
+        if ((owned >> i) & 1u) clist[o++] = p0 + i;
+    }
+    if (t == 0) {
+      smn = 0xFFFFFFFFu;
+      smx = 0u;
+    }
+    __syncthreads();
+    // 2. each row's log-sum-exp over the candidates
+    {
+      const int row = t >> 4, part = t & 15;
+      float m = -INFINITY, sum = 0.f;
+      if (row < a.n_q) {
+        const float* lr = lgj + (int64_t)row * plen;
+        for (int e = part; e < nv; e += 16) lse_add(m, sum, lr[clist[e]]);
+      }
+      lse_merge(m, sum, 1);
+      lse_merge(m, sum, 2);
+      lse_merge(m, sum, 4);
+      lse_merge(m, sum, 8);
+      if (part == 0 && row < a.n_q) lse[row] = m + logf(sum);
+    }
+    __syncthreads();
+    // 3. the slots' scores and the level's score range
+    float sc[S0];
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+    for (int i = 0; i < S0; ++i) {
+      sc[i] = 0.f;
+      if ((valid >> i) & 1u) {
+        sc[i] = soft_score(a, lgj + p0 + i, plen, lse);
+        const uint32_t k = order_key(sc[i]);
+        kmn = ((owned >> i) & 1u) ? min(kmn, k) : kmn;
+        kmx = ((owned >> i) & 1u) ? max(kmx, k) : kmx;
+      }
+    }
+    kmn = wave_min_u32(kmn);
+    kmx = wave_max_u32(kmx);
+    if (lane == 0) {
+      atomicMin(&smn, kmn);
+      atomicMax(&smx, kmx);
+    }
+    __syncthreads();
+    const int kj = a.budgets[L - j];
+    const uint32_t kept = select_level<NT, S0>(sc, valid, owned, p0, kj, key_to_f32(smn), key_to_f32(smx), sh, cur);
+    if (report) {  // uniform: level j's kept regions, ascending, with their scores
+      const uint32_t km = own ? kept : 0u;
+      int o = block_excl_scan(__popc(km), sh, 2 + (j & 1));
+      const int shl = L - j;
+#pragma unroll
+      for (int i = 0; i < S0; ++i)
+        if ((km >> i) & 1u) {
+          const int p = p0 + i;
+          if (o < kj) {
+            if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
+            if (dbg_score) dbg_score[off + o] = expf(sc[i]);
+          }
+          ++o;
+        }
+    }
+    off += kj;
+    keptp = kept;
+  }
+
+  // the kept tokens, ascending
+  int o = block_excl_scan(__popc(keptp), sh, 1);
+  int32_t* tsel = a.sel_ws + (int64_t)head * a.k0;
+  const HeadRef hr = head_ref(a, head);
+  int32_t* so = a.sel_out[hr.item] ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
+  const int mask = (1 << L) - 1;
+#pragma unroll
+  for (int i = 0; i < S0; ++i)
+    if ((keptp >> i) & 1u) {
+      const int p = t * S0 + i;
+      const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & mask);
+      if (o < a.k0) {
+        tsel[o] = tok;
+        if (so) so[o] = tok;
+      }
+      ++o;
+    }
 }
 
 // The in-register refinement, one workgroup of 1 024 threads per head, with
@@ -1518,11 +1780,23 @@ static hipError_t launch_apart(const StepArgs& a, const SelectLaunch& L, int sta
   const SelectPlan& P = L.plan;
   const dim3 grid(P.heads_total), block(kSelThreads);
   if (stage == 0) {  // between the coarse and the cover launches
-    if (P.topk_s >= 1 && P.topk_s <= 4 && P.levels > 0) return hipSuccess;  // the cover workgroups take it
+    if (P.topk_s >= 1 && P.topk_s <= 4 && P.levels > 0 && !P.soft) return hipSuccess;  // the cover workgroups take it
+    if (P.soft) {  // the level-L softmax scores first
+      const hipError_t e = launch_one(soft_top_kernel, grid, block, 0, s, a);
+      if (e != hipSuccess) return e;
+    }
     return launch_one(coarse_topk_kernel, grid, block, P.coarse_lds, s, a);
   }
   if (P.levels == 0) return hipSuccess;  // between the cover and the attention launches
   const dim3 rblock(kRefineThreads);
+  if (P.soft) {
+    switch (P.refine_s0) {
+      case 1: return launch_one(refine_soft_kernel<1>, grid, rblock, P.refine_soft_lds, s, a);
+      case 2: return launch_one(refine_soft_kernel<2>, grid, rblock, P.refine_soft_lds, s, a);
+      case 4: return launch_one(refine_soft_kernel<4>, grid, rblock, P.refine_soft_lds, s, a);
+      default: return launch_one(refine_soft_kernel<8>, grid, rblock, P.refine_soft_lds, s, a);
+    }
+  }
   switch (P.refine_s0) {
     case 1: return launch_one(refine_sel_kernel<1>, grid, rblock, P.cover_lds, s, a);
     case 2: return launch_one(refine_sel_kernel<2>, grid, rblock, P.cover_lds, s, a);
@@ -1596,6 +1870,9 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   a.inv_sqrt_d = 1.0f / sqrtf((float)P.head_dim);
   a.inv_nq = 1.0f / (float)P.n_q;
   a.stored_bands = P.stored_bands;
+  a.soft = P.soft;
+  a.n_top4 = P.n_top4;
+  a.logits = reinterpret_cast<float*>(L.ws + P.off_logits);
   for (int j = 0; j < kMaxLevels; ++j)
     a.band_a[j] = P.stored_bands && j > 0 && j < P.levels
                       ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(L.a_top[0]) + P.band_off[j])

@@ -80,7 +80,7 @@ def budgets_arr(b):
 
 def test_workspace_query_and_budget_checks():
     p = fake_pyramid()
-    q = lib().wf_select_attend_workspace_bytes
+    q = lambda *args: lib().wf_select_attend_workspace_bytes(*args, 0)  # noqa: E731
     assert q(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64])) > 0
     assert q(ctypes.byref(p), 32, 32, budgets_arr([8, 17, 32, 64])) == 0   # k_2 > 2 k_3
     assert q(ctypes.byref(p), 32, 32, budgets_arr([0, 1, 1, 1])) == 0      # k_L < 1
@@ -114,7 +114,7 @@ def test_select_attend_rejects_bad_arguments():
     assert select(q=MISALIGNED) == -7
     assert select(sel=FAKE + 2) == -7
     assert select(ws_bytes=64) == -6
-    assert select(agg=2) == -10
+    assert select(agg=4) == -10                                      # not an aggregation
     assert select(agg=-1) == -10
     assert select(agg=0x200) == -10                                  # an undefined option bit
     assert select(agg=wf.WF_AGG_MEAN | 0x200) == -10
@@ -132,7 +132,7 @@ def test_check_bits_match_the_header():
 def test_workspaces_start_with_the_status_word():
     # the status word takes the first 256 bytes of every workspace
     p = fake_pyramid()
-    a = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]))
+    a = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]), 0)
     b = lib().wf_attend_selected_workspace_bytes(1, 2, 64, wf.WF_BF16, 32, 64, 32)
     assert a > 256 and b > 256 and a % 256 == 0 and b % 256 == 0
 
@@ -205,7 +205,7 @@ def test_select_plan_rejects_an_attended_set_beyond_int_range():
     """The kept tokens plus the generated positions must stay within the
     attention's 2^24-entry bound, as for the attention-only call."""
     p = fake_pyramid()
-    q = lib().wf_select_attend_workspace_bytes
+    q = lambda *args: lib().wf_select_attend_workspace_bytes(*args, 0)  # noqa: E731
     assert q(ctypes.byref(p), 32, 5000, budgets_arr([8, 16, 32, 64])) > 0
     assert q(ctypes.byref(p), 32, (1 << 24) - 63, budgets_arr([8, 16, 32, 64])) == 0
     assert q(ctypes.byref(p), 32, 0x7FFFFFF0, budgets_arr([8, 16, 32, 64])) == 0
@@ -322,7 +322,7 @@ def test_noalloc_scratch_holds_every_workload():
     for c in CONFIGS.values():
         p = fake_pyramid(levels=c.levels, n=c.n_prompt, d=c.head_dim, H=c.batch * c.heads,
                          dt=wf.WF_BF16 if c.dtype == "bf16" else wf.WF_F32)
-        need = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), c.n_q, c.n_gen, budgets_arr(c.budgets))
+        need = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), c.n_q, c.n_gen, budgets_arr(c.budgets), 0)
         assert 0 < need <= cap, (c.name, need)
 
 
@@ -335,7 +335,7 @@ def noalloc(p, budgets, n_q=32, n_gen=32, out=FAKE, q=FAKE, agg=wf.WF_AGG_MAX):
 def test_noalloc_rejects_a_workspace_beyond_its_scratch_before_any_device_call():
     # 2 048 heads of a 1K prompt: the split partials alone exceed the scratch array
     p = fake_pyramid(levels=3, n=1024, d=64, H=2048)
-    need = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]))
+    need = lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]), 0)
     assert need > noalloc_scratch_bytes()
     assert noalloc(p, [8, 16, 32, 64]) == -6                  # WF_ERR_WORKSPACE
 
@@ -368,7 +368,7 @@ def test_layers_workspace_grows_with_the_layers_and_caps_the_heads():
     q = lib().wf_select_attend_layers_workspace_bytes
     p = fake_pyramid()
     one = q(ctypes.byref(p), 1, 32, 32, budgets_arr([8, 16, 32, 64]))
-    assert one == lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]))
+    assert one == lib().wf_select_attend_workspace_bytes(ctypes.byref(p), 32, 32, budgets_arr([8, 16, 32, 64]), 0)
     assert q(ctypes.byref(p), 4, 32, 32, budgets_arr([8, 16, 32, 64])) > one
     assert q(ctypes.byref(p), 0, 32, 32, budgets_arr([8, 16, 32, 64])) == 0
     assert q(ctypes.byref(p), 33, 32, 32, budgets_arr([8, 16, 32, 64])) == 0
@@ -394,3 +394,25 @@ def test_layers_call_checks_its_arguments_before_any_device_call():
     assert layers_call([p], ws_bytes=16) == -6                          # WF_ERR_WORKSPACE
     db2 = WfPyramid(1, 2, 1024, 64, 3, wf.WF_BF16, wf.WF_PYR_DB2, 0x57465059, FAKE, 1 << 20)
     assert layers_call([p, db2]) == -10
+
+
+def test_softmax_aggregations_plan_their_logits_and_limits():
+    q = lib().wf_select_attend_workspace_bytes
+    p = fake_pyramid()
+    b = budgets_arr([8, 16, 32, 64])
+    plain = q(ctypes.byref(p), 32, 32, b, wf.WF_AGG_MAX)
+    assert q(ctypes.byref(p), 32, 32, b, wf.WF_AGG_MEAN) == plain
+    # every row's logits: level L (128 regions) and the covered levels 0 .. 2 (64 + 32 + 16 positions)
+    soft = q(ctypes.byref(p), 32, 32, b, wf.WF_AGG_SOFTMAX_MAX)
+    assert soft >= plain + 2 * 32 * (128 + 64 + 32 + 16) * 4
+    assert q(ctypes.byref(p), 32, 32, b, wf.WF_AGG_SOFTMAX_MEAN) == soft
+    assert q(ctypes.byref(p), 32, 32, b, 4) == 0
+    # covered sets beyond 8 192 positions have no softmax refinement
+    big = fake_pyramid(levels=3, n=1 << 16, H=1)
+    assert q(ctypes.byref(big), 32, 0, budgets_arr([1025, 2050, 4100, 8200]), wf.WF_AGG_MAX) > 0
+    assert q(ctypes.byref(big), 32, 0, budgets_arr([1025, 2050, 4100, 8200]), wf.WF_AGG_SOFTMAX_MAX) == 0
+    # not on a pyramid with stored bands, not batched over layers
+    db2 = WfPyramid(1, 2, 1024, 64, 3, wf.WF_BF16, wf.WF_PYR_DB2, 0x57465059, FAKE, 1 << 20)
+    assert q(ctypes.byref(db2), 32, 32, b, wf.WF_AGG_SOFTMAX_MAX) == 0
+    assert select(pyr=db2, agg=wf.WF_AGG_SOFTMAX_MEAN) == -10
+    assert layers_call([p, fake_pyramid()], agg=wf.WF_AGG_SOFTMAX_MAX) == -10

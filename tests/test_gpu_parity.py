@@ -429,6 +429,57 @@ def test_mean_aggregation_matches_oracle(name, cfg, budgets, levels):
         assert check_head(inp, res, b, h, budgets, levels, agg="mean") == 0
 
 
+SOFT_CASES = [
+    ("4k-bf16", CONFIGS[2], None, None),
+    ("ragged-nq20-b2", custom(2, cid=78, batch=2, heads=2, n_q=20, n_prompt=2048, n_gen=7, levels=4),
+     [5, 9, 17, 30, 50], 4),
+    ("1k-f32", CONFIGS[1], None, None),
+    ("dense-L0", custom(2, cid=75, heads=2, n_prompt=512, n_gen=8, levels=0, n_spans=0), [100], 0),
+]
+
+
+@pytest.mark.parametrize("agg", ["softmax_max", "softmax_mean"])
+@pytest.mark.parametrize("name,cfg,budgets,levels", SOFT_CASES, ids=[c[0] for c in SOFT_CASES])
+def test_softmax_aggregations_match_oracle(agg, name, cfg, budgets, levels):
+    """Region scores from attention probabilities: every query row's logits
+    normalised by a softmax over the level's candidates, then the maximum or
+    the mean over the rows.  Planted heads match the oracle exactly at every
+    level, with the kept regions' probabilities to float32 accuracy."""
+    say(f"[{agg} {name}]")
+    inp = make_layer(cfg, 0)
+    budgets = cfg.budgets if budgets is None else budgets
+    levels = cfg.levels if levels is None else levels
+    heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    assert all(plant_many(inp, heads, budgets, levels, agg=agg))
+    to_dev(inp)
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, levels)
+    res = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True, agg=agg)
+    torch.cuda.synchronize()
+    check_structure(res, budgets, levels, cfg.n_prompt)
+    ora = oracle_many(inp, heads, budgets, levels, agg=agg)
+    for (b, h), o in zip(heads, ora):
+        assert check_head(inp, res, b, h, budgets, levels, agg=agg, ora=o) == 0, (b, h)
+
+
+def test_one_query_row_softmax_max_selects_what_max_selects():
+    """With one query row a level's softmax is monotone in the row's logits,
+    so the softmax maximum keeps exactly the regions the logit maximum keeps
+    (margins planted for the logits)."""
+    say("[softmax n_q=1]")
+    cfg = custom(2, cid=74, heads=4, n_q=1, n_prompt=2048, n_gen=8, levels=4)
+    inp = make_layer(cfg, 0)
+    budgets = [8, 15, 28, 50, 90]
+    heads = [(0, h) for h in range(cfg.heads)]
+    assert all(plant_many(inp, heads, budgets, 4, agg="max"))
+    to_dev(inp)
+    pyr = wf.build_pyramid(inp.k, cfg.n_prompt, 4)
+    hard = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True, agg="max")
+    soft = wf.select_attend(inp.q, pyr, inp.k, inp.v, inp.gen_idx, budgets, levels_out=True, agg="softmax_max")
+    torch.cuda.synchronize()
+    assert torch.equal(hard["sel_levels"], soft["sel_levels"])
+    assert torch.equal(hard["out"].view(torch.int32), soft["out"].view(torch.int32))
+
+
 def test_one_query_row_mean_equals_max():
     say("[mean n_q=1]")
     cfg = custom(2, cid=76, heads=2, n_q=1, n_prompt=2048, n_gen=8, levels=4)
