@@ -52,6 +52,10 @@ struct SelectPlan {
   uint64_t band_off[kMaxLevels];  // byte offset of A_j inside the pyramid buffer, when stored
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + K/V chunk buffers
+  // the split plan suits a refinement that shares its launch with the
+  // generated positions' attention splits; level-0 positions per thread of
+  // that refinement when this call does (0: its own launch)
+  int gen_beside, fuse_s0;
   // workspace sections (byte offsets)
   uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, off_logits, total;
 };
@@ -103,28 +107,61 @@ hipError_t launch_check(const CheckArgs& c, hipStream_t s);
 // workgroups share a compute unit; larger workgroups take one each.
 constexpr int attend_waves_per_simd(int nqt) { return nqt == 2 ? 2 : 1; }
 
-// Split plan of the attention over T (fills n_att .. cps_g from k0, n_gen,
-// chunk, n_q and heads_total): about as many splits over all heads as
-// attention workgroups fit the chip at once, at most kMaxSplit per head; the
-// prompt and the generated part share one count of chunks per split.  The
-// selecting call and the attention-only call use this same plan, so over the
-// same T they compute the same thing in the same order.
+// Split plan of the attention over T (fills n_att .. cps_g and gen_beside
+// from k0, n_gen, chunk, n_q and heads_total).  gen_beside: the selecting
+// call may run the generated positions' splits in its refinement's launch
+// (refine_gen_kernel), which holds at most 8 covered positions per
+// attention thread (so k_0 <= covered is at most that) for at most 256 heads,
+// and at least two attention workgroups per head fit the chip at once.  Then
+// the prompt part takes about as many splits per head as fit (they start
+// together once the selection is out, alone in the attention launch) and
+// the generated part splits of as many chunks within kMaxSplit.  Otherwise
+// both parts share one count of chunks per split, about as many splits over
+// all heads as fit the chip.  The decision uses only what the attention-only
+// call also knows: the selecting call and the attention-only call use this
+// same plan, so over the same T they compute the same thing in the same order.
 inline void plan_attention_splits(SelectPlan* P) {
   const int ch = P->chunk;
   P->n_att = P->k0 + P->n_gen;
   const int nc_p = (P->k0 + ch - 1) / ch, nc_g = (P->n_gen + ch - 1) / ch;
-  const int per_cu = attend_waves_per_simd((P->n_q + 15) / 16);  // attention workgroups per compute unit
-  int target = (256 * per_cu + P->heads_total - 1) / P->heads_total;
-  if (target > kMaxSplit) target = kMaxSplit;
-  if (target < 2) target = 2;  // room for a prompt and a generated split
-  int cps = (nc_p + nc_g + target - 1) / target;
-  if (cps < 1) cps = 1;
-  while ((nc_p + cps - 1) / cps + (nc_g + cps - 1) / cps > target) ++cps;
-  P->cps_p = P->cps_g = cps;
-  P->n_split_p = (nc_p + cps - 1) / cps;
-  P->n_split = P->n_split_p + (nc_g + cps - 1) / cps;
-  P->att_t_words = (cps * ch + 3) & ~3;  // one split's part of T
+  const int nqt = (P->n_q + 15) / 16;
+  const int per_cu = attend_waves_per_simd(nqt);  // attention workgroups per compute unit
+  const int slots = 256 * per_cu;
+  P->gen_beside = P->heads_total <= 256 && P->k0 <= 8 * 64 * nqt * kAttendGroups && slots >= 2 * P->heads_total;
+  auto cut = [](int chunks, int splits, int& cps, int& n) {  // chunks over at most `splits` splits
+    if (chunks == 0) {
+      cps = 1;
+      n = 0;
+      return;
+    }
+    cps = (chunks + splits - 1) / splits;
+    n = (chunks + cps - 1) / cps;
+  };
+  if (P->gen_beside) {
+    int tp = slots / P->heads_total;
+    if (tp > kMaxSplit - (nc_g > 0 ? 1 : 0)) tp = kMaxSplit - (nc_g > 0 ? 1 : 0);
+    int n_p, n_g;
+    cut(nc_p, tp, P->cps_p, n_p);
+    const int tg = (nc_g + P->cps_p - 1) / P->cps_p;
+    cut(nc_g, tg < kMaxSplit - n_p ? tg : kMaxSplit - n_p, P->cps_g, n_g);
+    P->n_split_p = n_p;
+    P->n_split = n_p + n_g;
+  } else {
+    int target = (slots + P->heads_total - 1) / P->heads_total;
+    if (target > kMaxSplit) target = kMaxSplit;
+    if (target < 2) target = 2;  // room for a prompt and a generated split
+    int cps = (nc_p + nc_g + target - 1) / target;
+    if (cps < 1) cps = 1;
+    while ((nc_p + cps - 1) / cps + (nc_g + cps - 1) / cps > target) ++cps;
+    P->cps_p = P->cps_g = cps;
+    P->n_split_p = (nc_p + cps - 1) / cps;
+    P->n_split = P->n_split_p + (nc_g + cps - 1) / cps;
+  }
+  const int cps_max = P->cps_p > P->cps_g ? P->cps_p : P->cps_g;
+  P->att_t_words = (cps_max * ch + 3) & ~3;  // one split's part of T
 }
+// Both branches keep n_split <= kMaxSplit: the merge folds at most that many.
+inline bool attention_plan_ok(const SelectPlan* P) { return P->n_split >= 1 && P->n_split <= kMaxSplit; }
 
 // Tokens per attention chunk; each of the kAttendGroups waves of a query
 // tile takes an equal slice.

@@ -1626,6 +1626,39 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
   }
 }
 
+template <typename T, int D, int NQT>
+__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(StepArgs a) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
+}
+
+// The refinement of every head and the generated positions' attention
+// splits in one launch, with the attention's workgroup size: workgroups
+// [0, H) refine head blockIdx.x, the rest take the splits of the generated
+// positions, which need no selection and so run beside the refinement.  The
+// attention launch after it takes only the prompt splits.  No workgroup
+// waits for another.
+template <typename T, int D, int NQT, int S0>
+__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void refine_gen_kernel(StepArgs a) {
+  constexpr int NT = 64 * NQT * kAttendGroups;
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int H = a.heads_total;
+  if ((int)blockIdx.x < H) {
+    const int head = blockIdx.x;
+    int* sel_l = reinterpret_cast<int*>(lds);  // the kept coarse regions [k_L], then the selection state
+    SelShared<NT>& sh = *reinterpret_cast<SelShared<NT>*>(lds + ((a.k_top + 3) & ~3));
+    const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+    for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
+    __syncthreads();
+    refine_sel<NT, S0>(a, head, sel_l, sh);
+    return;
+  }
+  const int ns_g = a.n_split - a.n_split_p;
+  const int r = blockIdx.x - H;
+  const int head = r / ns_g;
+  attend_split<T, D, NQT>(a, lds, head, a.n_split_p + (r - head * ns_g));
+}
+
 // ---------------------------------------------------------------------------
 // Merge of the split partials in a launch of its own:
 // O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s, M = max_s m_s (m in
@@ -1634,12 +1667,6 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
 // independent loads spread over the whole chip; the splits are folded in
 // index order.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int NQT>
-__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(StepArgs a) {
-  extern __shared__ __align__(16) uint32_t lds[];
-  attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
-}
-
 #if !defined(WF_STEP_T)  // one compile unit holds it
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
@@ -1732,26 +1759,48 @@ hipError_t launch_select(const StepArgs& a, const SelectLaunch& L, int stage, hi
   return e;
 }
 
-// The attention stage, for one (T, D, RT).
+// The attention stage, for one (T, D, RT): every split, or only the prompt
+// splits when the refinement's launch took the generated ones.
 template <typename T, int D, int RT>
 hipError_t launch_attend(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
   const SelectPlan& P = L.plan;
-  return launch_one(attend_kernel<T, D, RT>, dim3(P.n_split, P.heads_total), dim3(64 * RT * kAttendGroups),
-                    P.attend_lds, s, a);
+  const bool gen_done = !L.attend_only && P.fuse_s0 > 0;
+  return launch_one(attend_kernel<T, D, RT>, dim3(gen_done ? P.n_split_p : P.n_split, P.heads_total),
+                    dim3(64 * RT * kAttendGroups), P.attend_lds, s, a);
+}
+
+// The refinement with the generated positions' splits (refine_gen_kernel), for one (T, D, RT).
+template <typename T, int D, int RT>
+hipError_t launch_refine_gen(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  const SelectPlan& P = L.plan;
+  constexpr int NT = 64 * RT * kAttendGroups;
+  const int refine_lds = 4 * ((P.k_top + 3) & ~3) + (int)sizeof(SelShared<NT>);
+  const int lds = P.attend_lds > refine_lds ? P.attend_lds : refine_lds;
+  const dim3 grid(P.heads_total * (1 + P.n_split - P.n_split_p));
+  switch (P.fuse_s0) {
+    case 1: return launch_one(refine_gen_kernel<T, D, RT, 1>, grid, dim3(NT), lds, s, a);
+    case 2: return launch_one(refine_gen_kernel<T, D, RT, 2>, grid, dim3(NT), lds, s, a);
+    case 4: return launch_one(refine_gen_kernel<T, D, RT, 4>, grid, dim3(NT), lds, s, a);
+    default: return launch_one(refine_gen_kernel<T, D, RT, 8>, grid, dim3(NT), lds, s, a);
+  }
 }
 
 #if defined(WF_STEP_T)
 template hipError_t launch_select<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&, int,
                                                                     hipStream_t);
 template hipError_t launch_attend<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
+template hipError_t launch_refine_gen<WF_STEP_T, WF_STEP_D, WF_STEP_RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
 #else
 #define WF_EXTERN_SEL(T, D, RT) \
   extern template hipError_t launch_select<T, D, RT>(const StepArgs&, const SelectLaunch&, int, hipStream_t);
 #define WF_EXTERN_ATT(T, D, RT) \
   extern template hipError_t launch_attend<T, D, RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
+#define WF_EXTERN_RG(T, D, RT) \
+  extern template hipError_t launch_refine_gen<T, D, RT>(const StepArgs&, const SelectLaunch&, hipStream_t);
 #define WF_EXTERN_STAGES(T, D)                                                              \
   WF_EXTERN_SEL(T, D, 1) WF_EXTERN_SEL(T, D, 2) WF_EXTERN_SEL(T, D, 3) WF_EXTERN_SEL(T, D, 4) \
-  WF_EXTERN_ATT(T, D, 1) WF_EXTERN_ATT(T, D, 2) WF_EXTERN_ATT(T, D, 3) WF_EXTERN_ATT(T, D, 4)
+  WF_EXTERN_ATT(T, D, 1) WF_EXTERN_ATT(T, D, 2) WF_EXTERN_ATT(T, D, 3) WF_EXTERN_ATT(T, D, 4) \
+  WF_EXTERN_RG(T, D, 1) WF_EXTERN_RG(T, D, 2) WF_EXTERN_RG(T, D, 3) WF_EXTERN_RG(T, D, 4)
 WF_EXTERN_STAGES(bf16_t, 128)
 WF_EXTERN_STAGES(bf16_t, 64)
 WF_EXTERN_STAGES(float, 128)
@@ -1759,6 +1808,7 @@ WF_EXTERN_STAGES(float, 64)
 #undef WF_EXTERN_STAGES
 #undef WF_EXTERN_SEL
 #undef WF_EXTERN_ATT
+#undef WF_EXTERN_RG
 
 template <typename T, int D>
 static hipError_t launch_rt_select(int rt, int stage, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
@@ -1813,6 +1863,16 @@ static hipError_t launch_rt_attend(int rt, const StepArgs& a, const SelectLaunch
     case 2: return launch_attend<T, D, 2>(a, L, s);
     case 3: return launch_attend<T, D, 3>(a, L, s);
     default: return launch_attend<T, D, 4>(a, L, s);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_rt_refine_gen(int rt, const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
+  switch (rt) {
+    case 1: return launch_refine_gen<T, D, 1>(a, L, s);
+    case 2: return launch_refine_gen<T, D, 2>(a, L, s);
+    case 3: return launch_refine_gen<T, D, 3>(a, L, s);
+    default: return launch_refine_gen<T, D, 4>(a, L, s);
   }
 }
 
@@ -1888,7 +1948,12 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
       e = bf ? (d128 ? launch_rt_select<bf16_t, 128>(rt, stage, a, L, s) : launch_rt_select<bf16_t, 64>(rt, stage, a, L, s))
              : (d128 ? launch_rt_select<float, 128>(rt, stage, a, L, s) : launch_rt_select<float, 64>(rt, stage, a, L, s));
       if (e != hipSuccess) return e;
-      if ((e = launch_apart(a, L, stage, s)) != hipSuccess) return e;
+      if (stage == 1 && P.fuse_s0 > 0)  // the refinement with the generated positions' splits
+        e = bf ? (d128 ? launch_rt_refine_gen<bf16_t, 128>(rt, a, L, s) : launch_rt_refine_gen<bf16_t, 64>(rt, a, L, s))
+               : (d128 ? launch_rt_refine_gen<float, 128>(rt, a, L, s) : launch_rt_refine_gen<float, 64>(rt, a, L, s));
+      else
+        e = launch_apart(a, L, stage, s);
+      if (e != hipSuccess) return e;
     }
   }
   e = bf ? (d128 ? launch_rt_attend<bf16_t, 128>(rt, a, L, s) : launch_rt_attend<bf16_t, 64>(rt, a, L, s))
