@@ -852,11 +852,30 @@ template <int S0> struct HeldScores {
 static_assert(kMaxLevels == 7, "the refinement holds seven levels");
 
 template <int NT, int S0>
-__device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const int* sel_l, SelShared<NT>& sh) {
+__device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel_l, SelShared<NT>& sh) {
   const int t = threadIdx.x, lane = t & 63;
   const int L = a.levels;
   const int covered = (int)a.covered;
   const float* cov = a.cov + (int64_t)head * a.cov_len;
+  // Every load of the stage is requested before any is waited for, so the
+  // coverage scores, the level ranges and the kept coarse regions arrive in
+  // one round trip.  First every live level's scores into registers
+  // (clamped positions; slots past a level's end are never valid).
+  HeldScores<S0> hs;
+#define WF_LOAD_LEVEL(J)                                                              \
+  if (J < L) hs.template load<J>(cov + a.cov_off[J], covered >> J, (t * S0) >> J);    \
+  else hs.template copy<J>(hs.s0);
+  WF_LOAD_LEVEL(0)
+  WF_LOAD_LEVEL(1)
+  WF_LOAD_LEVEL(2)
+  WF_LOAD_LEVEL(3)
+  WF_LOAD_LEVEL(4)
+  WF_LOAD_LEVEL(5)
+  WF_LOAD_LEVEL(6)
+#undef WF_LOAD_LEVEL
+  // the kept coarse regions [k_L] (from the cover launch), this thread's first one
+  const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
+  const int sel0 = sel_g[min(t, a.k_top - 1)];
   // each level's score range: the cover waves' slots (at most 128 per head
   // here, lanes l and l + 64 of wave 0), published to LDS.  Loads are
   // unconditional, from clamped slots; slots past the last wave take the
@@ -892,20 +911,9 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, const in
       }
     }
   }
-  // every live level's scores into registers (clamped positions; slots past
-  // a level's end are never valid)
-  HeldScores<S0> hs;
-#define WF_LOAD_LEVEL(J)                                                              \
-  if (J < L) hs.template load<J>(cov + a.cov_off[J], covered >> J, (t * S0) >> J);    \
-  else hs.template copy<J>(hs.s0);
-  WF_LOAD_LEVEL(0)
-  WF_LOAD_LEVEL(1)
-  WF_LOAD_LEVEL(2)
-  WF_LOAD_LEVEL(3)
-  WF_LOAD_LEVEL(4)
-  WF_LOAD_LEVEL(5)
-  WF_LOAD_LEVEL(6)
-#undef WF_LOAD_LEVEL
+  // the kept coarse regions into LDS (more than one per thread only when k_L > NT)
+  if (t < a.k_top) sel_l[t] = clampi(sel0, 0, a.n_top - 1);
+  for (int i = t + NT; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   sel_init(sh);
   __syncthreads();
 
@@ -1338,11 +1346,7 @@ __global__ __launch_bounds__(kRefineThreads) void refine_sel_kernel(StepArgs a) 
   extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L]
   __shared__ __align__(16) SelShared<kRefineThreads> sh;
   const int head = blockIdx.x;
-  int* sel_l = reinterpret_cast<int*>(lds);
-  const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-  for (int i = threadIdx.x; i < a.k_top; i += kRefineThreads) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
-  __syncthreads();
-  refine_sel<kRefineThreads, S0>(a, head, sel_l, sh);
+  refine_sel<kRefineThreads, S0>(a, head, reinterpret_cast<int*>(lds), sh);
 }
 
 __global__ __launch_bounds__(kSelThreads) void refine_lists_kernel(StepArgs a) {
@@ -1645,12 +1649,9 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT
   const int H = a.heads_total;
   if ((int)blockIdx.x < H) {
     const int head = blockIdx.x;
-    int* sel_l = reinterpret_cast<int*>(lds);  // the kept coarse regions [k_L], then the selection state
+    // the kept coarse regions [k_L], then the selection state
     SelShared<NT>& sh = *reinterpret_cast<SelShared<NT>*>(lds + ((a.k_top + 3) & ~3));
-    const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-    for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
-    __syncthreads();
-    refine_sel<NT, S0>(a, head, sel_l, sh);
+    refine_sel<NT, S0>(a, head, reinterpret_cast<int*>(lds), sh);
     return;
   }
   const int ns_g = a.n_split - a.n_split_p;
