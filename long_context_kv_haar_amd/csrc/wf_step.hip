@@ -817,23 +817,29 @@ template <int S0> struct HeldScores {
     else if constexpr (J == 5) return s5;
     else return s6;
   }
-  // level j's slots into a full-width array (slots past the level's count hold 0)
-  __device__ __forceinline__ void level(int j, float (&sc)[S0]) {
+  // a level past the pyramid's top: never read, held at zero
+  template <int J> __device__ __forceinline__ void clear() {
 #pragma unroll
-    for (int i = 0; i < S0; ++i) sc[i] = 0.f;
+    for (int i = 0; i < Held<S0, J>::N; ++i) get<J>()[i] = 0.f;
+  }
+  // level j's first P slots (P is the level's count of held slots)
+  template <int P> __device__ __forceinline__ void first(int j, float (&sc)[P]) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) sc[i] = 0.f;
     switch (j) {
-      case 0: copy<0>(sc); break;
-      case 1: copy<1>(sc); break;
-      case 2: copy<2>(sc); break;
-      case 3: copy<3>(sc); break;
-      case 4: copy<4>(sc); break;
-      case 5: copy<5>(sc); break;
-      default: copy<6>(sc); break;
+      case 0: take<0>(sc); break;
+      case 1: take<1>(sc); break;
+      case 2: take<2>(sc); break;
+      case 3: take<3>(sc); break;
+      case 4: take<4>(sc); break;
+      case 5: take<5>(sc); break;
+      default: take<6>(sc); break;
     }
   }
-  template <int J> __device__ __forceinline__ void copy(float (&sc)[S0]) {
+  template <int J, int P> __device__ __forceinline__ void take(float (&sc)[P]) {
+    constexpr int n = Held<S0, J>::N < P ? Held<S0, J>::N : P;
 #pragma unroll
-    for (int i = 0; i < Held<S0, J>::N; ++i) sc[i] = get<J>()[i];
+    for (int i = 0; i < n; ++i) sc[i] = get<J>()[i];
   }
   template <int J> __device__ __forceinline__ void load(const float* src, int nj, int p0) {
     auto& s = get<J>();
@@ -851,6 +857,48 @@ template <int S0> struct HeldScores {
 };
 static_assert(kMaxLevels == 7, "the refinement holds seven levels");
 
+// One refinement level over the P = max(1, S0 >> j) slots a thread holds at
+// level j (the per-slot work of the level scales with P, not with S0):
+// candidates are the held positions whose parent was kept (keptp, the
+// parent level's slots); returns the kept mask over the P slots and, with
+// the per-level sinks, writes the level's kept regions at off.
+template <int NT, int S0, int P>
+__device__ __forceinline__ uint32_t refine_level(const StepArgs& a, int head, HeldScores<S0>& hs, int j,
+                                                 uint32_t keptp, const int* sel_l, SelShared<NT>& sh, SelCursor& cur,
+                                                 int off) {
+  const int t = threadIdx.x;
+  const int L = a.levels;
+  float sc[P];
+  hs.template first<P>(j, sc);
+  const int p0 = (t * S0) >> j, nj = (int)(a.covered >> j);
+  const bool own = P > 1 || ((t * S0) & ((1 << j) - 1)) == 0;
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int i = 0; i < P; ++i) valid |= ((p0 + i < nj) & ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
+  const uint32_t owned = own ? valid : 0u;
+  const int kj = a.budgets[L - j];
+  const uint32_t kept =
+      select_level<NT, P>(sc, valid, owned, p0, kj, key_to_f32(sh.rmn[j]), key_to_f32(sh.rmx[j]), sh, cur);
+  if (a.sel_levels || a.score_levels) {  // uniform: level j's kept regions, ascending, with their scores
+    int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+    float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+    const uint32_t km = own ? kept : 0u;
+    int o = block_excl_scan(__popc(km), sh, 2 + (j & 1));
+    const int shl = L - j;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      if ((km >> i) & 1u) {
+        const int p = p0 + i;
+        if (o < kj) {
+          if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
+          if (dbg_score) dbg_score[off + o] = sc[i];
+        }
+        ++o;
+      }
+  }
+  return kept;
+}
+
 template <int NT, int S0>
 __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel_l, SelShared<NT>& sh) {
   const int t = threadIdx.x, lane = t & 63;
@@ -864,7 +912,7 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel
   HeldScores<S0> hs;
 #define WF_LOAD_LEVEL(J)                                                              \
   if (J < L) hs.template load<J>(cov + a.cov_off[J], covered >> J, (t * S0) >> J);    \
-  else hs.template copy<J>(hs.s0);
+  else hs.template clear<J>();
   WF_LOAD_LEVEL(0)
   WF_LOAD_LEVEL(1)
   WF_LOAD_LEVEL(2)
@@ -924,41 +972,26 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel
     const int pl = (S0 >> L) > 0 ? (S0 >> L) : 1;
     for (int m = 0; m < pl; ++m) keptp |= (pl0 + m < a.k_top) ? (1u << m) : 0u;
   }
-  const bool report = a.sel_levels || a.score_levels;
-  int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-  float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   int off = a.k_top;
   SelCursor cur;
-  float sc[S0];
-  for (int j = L - 1; j >= 0; --j) {
-    hs.level(j, sc);
+  for (int j = L - 1; j >= 0; --j) {  // each level on its own count of held slots
     const int pj = (S0 >> j) > 0 ? (S0 >> j) : 1;
-    const int p0 = (t * S0) >> j, nj = covered >> j;
-    const bool own = pj > 1 || ((t * S0) & ((1 << j) - 1)) == 0;
-    uint32_t valid = 0u;
-#pragma unroll
-    for (int i = 0; i < S0; ++i)
-      valid |= ((i < pj) & (p0 + i < nj) & ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
-    const uint32_t owned = own ? valid : 0u;
-    const int kj = a.budgets[L - j];
-    const uint32_t kept =
-        select_level<NT, S0>(sc, valid, owned, p0, kj, key_to_f32(sh.rmn[j]), key_to_f32(sh.rmx[j]), sh, cur);
-    if (report) {  // uniform: level j's kept regions, ascending, with their scores
-      const uint32_t km = own ? kept : 0u;
-      int o = block_excl_scan(__popc(km), sh, 2 + (j & 1));
-      const int shl = L - j;
-#pragma unroll
-      for (int i = 0; i < S0; ++i)
-        if ((km >> i) & 1u) {
-          const int p = p0 + i;
-          if (o < kj) {
-            if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
-            if (dbg_score) dbg_score[off + o] = sc[i];
-          }
-          ++o;
-        }
+    uint32_t kept;
+    if (pj == 1) {
+      kept = refine_level<NT, S0, 1>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+    } else if constexpr (S0 >= 2) {
+      if (pj == 2) {
+        kept = refine_level<NT, S0, 2>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+      } else if constexpr (S0 >= 4) {
+        if (pj == 4) kept = refine_level<NT, S0, 4>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+        else kept = refine_level<NT, S0, S0>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+      } else {
+        kept = 0u;  // not reached: pj <= S0
+      }
+    } else {
+      kept = 0u;  // not reached: pj <= S0
     }
-    off += kj;
+    off += a.budgets[L - j];
     keptp = kept;
   }
 
