@@ -141,9 +141,16 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
                    off_d);
     for (int j = 1; j < pyr->levels; ++j) P->band_off[j] = off_a[j];
   }
+  // the refinement shares its launch with the generated positions'
+  // attention splits where it fits (see gen_beside_fits), for the
+  // in-register refinement with at most 8 covered positions per attention
+  // thread and the maximum or mean over the query rows
+  const int nt_att = 64 * ((n_q + 15) / 16) * wf::kAttendGroups;
+  if (wf::gen_beside_fits(P) && L > 0 && !P->soft && P->refine_s0 > 0 && P->covered <= 8 * (int64_t)nt_att)
+    P->fuse_s0 = pow2_at_least((int)((P->covered + nt_att - 1) / nt_att));
   // attention splits
   P->chunk = wf::attend_chunk(pyr->dtype);
-  wf::plan_attention_splits(P);
+  wf::plan_attention_splits(P, P->fuse_s0 > 0);
   if (!wf::attention_plan_ok(P)) return WF_ERR_SHAPE;
   // list-based refinement (one workgroup per head): the kept sets and
   // candidate lists, plus the coverage scores when they fit
@@ -160,13 +167,6 @@ int make_plan(const wf_pyramid* pyr, int32_t n_q, int32_t n_gen, const int32_t* 
   const int64_t buf_bytes = wf::attend_buffer_bytes(pyr->dtype, pyr->head_dim, (n_q + 15) / 16);
   if (buf_bytes > wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words) return WF_ERR_BUDGET;
   P->attend_lds = (int)(4 * (int64_t)P->att_t_words + buf_bytes);
-  // the refinement shares its launch with the generated positions'
-  // attention splits (workgroups of the attention's size) where the split
-  // plan suits it, for the in-register refinement with at most 8 covered
-  // positions per thread and the maximum or mean over the query rows
-  const int nt_att = 64 * ((n_q + 15) / 16) * wf::kAttendGroups;
-  if (P->gen_beside && L > 0 && !P->soft && P->refine_s0 > 0 && P->covered <= 8 * (int64_t)nt_att)
-    P->fuse_s0 = pow2_at_least((int)((P->covered + nt_att - 1) / nt_att));
   // workspace sections
   const uint64_t H = (uint64_t)P->heads_total;
   uint64_t w = wf::kStatusBytes;  // the debug status word comes first
@@ -208,7 +208,7 @@ int make_attend_plan(int32_t batch, int32_t heads, int32_t head_dim, int32_t dty
   P->k0 = k0;
   P->n_gen = n_gen;
   P->chunk = wf::attend_chunk(dtype);
-  wf::plan_attention_splits(P);
+  wf::plan_attention_splits(P, false);
   if (!wf::attention_plan_ok(P)) return WF_ERR_SHAPE;
   const int64_t budget = wf::kLdsLimit - wf::kTopKSharedReserve - 4 * (int64_t)P->att_t_words;
   const int64_t buf_bytes = wf::attend_buffer_bytes(dtype, head_dim, (n_q + 15) / 16);

@@ -52,10 +52,9 @@ struct SelectPlan {
   uint64_t band_off[kMaxLevels];  // byte offset of A_j inside the pyramid buffer, when stored
   int att_t_words;              // words of the attended-set list (T) region
   int attend_lds;               // T list + K/V chunk buffers
-  // the split plan suits a refinement that shares its launch with the
-  // generated positions' attention splits; level-0 positions per thread of
-  // that refinement when this call does (0: its own launch)
-  int gen_beside, fuse_s0;
+  // level-0 positions per thread of the refinement when it shares its launch
+  // with the generated positions' attention splits (0: its own launch)
+  int fuse_s0;
   // workspace sections (byte offsets)
   uint64_t off_keys, off_sel_top, off_cov, off_lvl, off_sel, off_part_ml, off_part_o, off_logits, total;
 };
@@ -107,27 +106,30 @@ hipError_t launch_check(const CheckArgs& c, hipStream_t s);
 // workgroups share a compute unit; larger workgroups take one each.
 constexpr int attend_waves_per_simd(int nqt) { return nqt == 2 ? 2 : 1; }
 
-// Split plan of the attention over T (fills n_att .. cps_g and gen_beside
-// from k0, n_gen, chunk, n_q and heads_total).  gen_beside: the selecting
-// call may run the generated positions' splits in its refinement's launch
-// (refine_gen_kernel), which holds at most 8 covered positions per
-// attention thread (so k_0 <= covered is at most that) for at most 256 heads,
-// and at least two attention workgroups per head fit the chip at once.  Then
-// the prompt part takes about as many splits per head as fit (they start
-// together once the selection is out, alone in the attention launch) and
-// the generated part splits of as many chunks within kMaxSplit.  Otherwise
-// both parts share one count of chunks per split, about as many splits over
-// all heads as fit the chip.  The decision uses only what the attention-only
-// call also knows: the selecting call and the attention-only call use this
-// same plan, so over the same T they compute the same thing in the same order.
-inline void plan_attention_splits(SelectPlan* P) {
+// Whether a selecting call's refinement may share its launch with the
+// generated positions' attention splits (refine_gen_kernel, workgroups of the
+// attention's size): at most 256 heads (one round of refinement workgroups)
+// and at least two attention workgroups per head fitting the chip at once.
+inline bool gen_beside_fits(const SelectPlan* P) {
+  const int per_cu = attend_waves_per_simd((P->n_q + 15) / 16);  // attention workgroups per compute unit
+  return P->heads_total <= 256 && 256 * per_cu >= 2 * P->heads_total;
+}
+
+// Split plan of the attention over T (fills n_att .. cps_g from k0, n_gen,
+// chunk, n_q and heads_total).  beside: the generated positions' splits run
+// in the refinement's launch, so the prompt part takes about as many splits
+// per head as fit the chip (they start together once the selection is out,
+// alone in the attention launch) and the generated part splits of as many
+// chunks within kMaxSplit.  Otherwise (the attention-only call, and
+// selecting calls whose refinement runs apart) both parts share one count
+// of chunks per split, about as many splits over all heads as fit the chip
+// in one round.
+inline void plan_attention_splits(SelectPlan* P, bool beside) {
   const int ch = P->chunk;
   P->n_att = P->k0 + P->n_gen;
   const int nc_p = (P->k0 + ch - 1) / ch, nc_g = (P->n_gen + ch - 1) / ch;
-  const int nqt = (P->n_q + 15) / 16;
-  const int per_cu = attend_waves_per_simd(nqt);  // attention workgroups per compute unit
+  const int per_cu = attend_waves_per_simd((P->n_q + 15) / 16);  // attention workgroups per compute unit
   const int slots = 256 * per_cu;
-  P->gen_beside = P->heads_total <= 256 && P->k0 <= 8 * 64 * nqt * kAttendGroups && slots >= 2 * P->heads_total;
   auto cut = [](int chunks, int splits, int& cps, int& n) {  // chunks over at most `splits` splits
     if (chunks == 0) {
       cps = 1;
@@ -137,7 +139,7 @@ inline void plan_attention_splits(SelectPlan* P) {
     cps = (chunks + splits - 1) / splits;
     n = (chunks + cps - 1) / cps;
   };
-  if (P->gen_beside) {
+  if (beside) {
     int tp = slots / P->heads_total;
     if (tp > kMaxSplit - (nc_g > 0 ? 1 : 0)) tp = kMaxSplit - (nc_g > 0 ? 1 : 0);
     int n_p, n_g;

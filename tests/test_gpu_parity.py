@@ -319,15 +319,17 @@ def oracle_attend_selected_head(q, inp, sel_bh, gen, b, h):
 @pytest.mark.parametrize("cid", [1, 2])
 def test_attend_selected_reuses_a_selection(cid):
     """Attention over a selection made by an earlier call: with the same
-    queries it reproduces that call's output bit for bit; with the queries of
-    a later step it matches the oracle's attention over the same rows."""
+    queries it reproduces that call's output up to float32 rounding (the
+    selecting call may split the attention differently, its generated
+    positions' splits running beside the refinement); with the queries of a
+    later step it matches the oracle's attention over the same rows."""
     say(f"[attend_selected c{cid}]")
     inp = to_dev(make_layer(cid, 0))
     cfg = inp.cfg
     _, res = run(inp)
     again = wf.attend_selected(inp.q, inp.k, inp.v, res["sel"], inp.gen_idx)
     torch.cuda.synchronize()
-    assert torch.equal(again, res["out"])
+    assert torch.allclose(again, res["out"], rtol=1e-5, atol=1e-6), (again - res["out"]).abs().max().item()
     q2 = make_layer(cid, 1).q.to(DEV)          # the queries of another step, same shape
     out2 = wf.attend_selected(q2, inp.k, inp.v, res["sel"], inp.gen_idx)
     torch.cuda.synchronize()
