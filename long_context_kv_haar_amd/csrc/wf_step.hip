@@ -1656,10 +1656,14 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
   if (tg == 0 && qvalid) {
     float* pml = a.part_ml + (((int64_t)head * a.n_split + split) * a.n_q + query) * 2;
     float* po = a.part_o + ((int64_t)head * a.n_split + split) * a.n_q * D + (int64_t)query * D;
-    if (g == 0) *reinterpret_cast<float2*>(pml) = make_float2(st.m, st.l);
+    // non-temporal stores: the merge launch reads the partials (about 10 MB at
+    // 64K) from memory, and they need not sit dirty in this XCD's L2 when the
+    // launch ends (the small hand-offs between the other launches measured
+    // slower this way: their readers then miss the caches)
+    if (g == 0) __builtin_nontemporal_store(f32x2_t{st.m, st.l}, reinterpret_cast<f32x2_t*>(pml));
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(st.o[dt][0], st.o[dt][1], st.o[dt][2], st.o[dt][3]);
+      __builtin_nontemporal_store(st.o[dt], reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g));
   }
 }
 
