@@ -151,13 +151,6 @@ struct QueryStage {
   }
 };
 
-template <typename T, int D, int NT, int RT>
-__device__ __forceinline__ void stage_query_batched(const T* qh, int n_q, T* qs) {
-  QueryStage<T, D, NT, RT> st;
-  st.issue(qh, n_q);
-  st.store(n_q, qs);
-}
-
 // Query fragments as the B operand from the staged rows: lane (l16, g)
 // supplies query row 16 qt + l16; zero beyond n_q.
 template <typename T, int D, int RT>
@@ -187,18 +180,25 @@ template <int NT> struct TopKRaw {
 // registers with S keys per thread (n_L <= 256 S), else by the general
 // Top-K with the keys in LDS (up to kMaxCoarseLds) or read from memory.
 // ---------------------------------------------------------------------------
-template <int S, class Emit>
+template <int S, class Emit, class Pre>
 __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int k, SelShared<kSelThreads>& sh,
-                                                Emit emit) {
+                                                Emit emit, Pre pre) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int pos0 = t * S;
+  uint32_t kv[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) kv[i] = keys[min(pos0 + i, n - 1)];
+  // the caller's own loads go after the keys, which the selection waits for
+  // first, and the selection state is cleared while they are in flight
+  __builtin_amdgcn_sched_barrier(0);
+  pre();
+  sel_init(sh);
   float sc[S];
   uint32_t valid = 0u, mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int i = 0; i < S; ++i) {
-    const int p = pos0 + i;
-    const bool in = p < n;
-    const uint32_t key = keys[min(p, n - 1)];
+    const bool in = pos0 + i < n;
+    const uint32_t key = kv[i];
     sc[i] = key_to_f32(key);
     valid |= in ? (1u << i) : 0u;
     mn = in ? min(mn, key) : mn;
@@ -210,7 +210,6 @@ __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int
     sh.wmn[w] = mn;
     sh.wmx[w] = mx;
   }
-  sel_init(sh);
   __syncthreads();
   mn = 0xFFFFFFFFu;
   mx = 0u;
@@ -232,25 +231,28 @@ __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int
 
 // The in-register coarse Top-K for topk_s in {1, 2, 4} (what a cover
 // workgroup runs), or with LARGE also {8, 16, 32} and the general path (the
-// Top-K's own launch).
-template <bool LARGE, class Emit>
+// Top-K's own launch).  pre() issues the caller's loads that are not needed
+// before the Top-K ends: after the keys' loads where they are in registers,
+// else first.
+template <bool LARGE, class Emit, class Pre>
 __device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, unsigned char* raw, uint32_t* keys_l,
-                                                Emit emit) {
+                                                Emit emit, Pre pre) {
   const uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
   SelShared<kSelThreads>& sh = *reinterpret_cast<SelShared<kSelThreads>*>(raw);
   switch (a.topk_s) {
-    case 1: coarse_topk_sel<1>(keys, a.n_top, a.k_top, sh, emit); return;
-    case 2: coarse_topk_sel<2>(keys, a.n_top, a.k_top, sh, emit); return;
-    case 4: coarse_topk_sel<4>(keys, a.n_top, a.k_top, sh, emit); return;
+    case 1: coarse_topk_sel<1>(keys, a.n_top, a.k_top, sh, emit, pre); return;
+    case 2: coarse_topk_sel<2>(keys, a.n_top, a.k_top, sh, emit, pre); return;
+    case 4: coarse_topk_sel<4>(keys, a.n_top, a.k_top, sh, emit, pre); return;
     default: break;
   }
   if constexpr (LARGE) {
     switch (a.topk_s) {
-      case 8: coarse_topk_sel<8>(keys, a.n_top, a.k_top, sh, emit); return;
-      case 16: coarse_topk_sel<16>(keys, a.n_top, a.k_top, sh, emit); return;
-      case 32: coarse_topk_sel<32>(keys, a.n_top, a.k_top, sh, emit); return;
+      case 8: coarse_topk_sel<8>(keys, a.n_top, a.k_top, sh, emit, pre); return;
+      case 16: coarse_topk_sel<16>(keys, a.n_top, a.k_top, sh, emit, pre); return;
+      case 32: coarse_topk_sel<32>(keys, a.n_top, a.k_top, sh, emit, pre); return;
       default: break;
     }
+    pre();
     auto& fs = *reinterpret_cast<TopKFastShared<kSelThreads>*>(raw);
     auto out = [&](int o, int i) {
       if (o < a.k_top) emit(o, i, key_to_f32(keys[i]));
@@ -328,16 +330,21 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
   f32x4 acc[RT];
 #pragma unroll
   for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the query block is requested first: it goes to LDS while the coefficient
+  // rows are still in flight
+  QueryStage<T, D, 256, RT> qstage;
+  qstage.issue(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q);
   if constexpr (sizeof(T) == 2) {
     constexpr int STEPS = D / 32;
     // step s of lane group g: coefficients [32 s + 8 g, 32 s + 8 g + 8), as Frag<bf16_t>
     const float4* p = reinterpret_cast<const float4*>(arow);
     float4 x[2 * STEPS];
+    // unconditional loads (arow is row 0 for an absent region): a load under
+    // a condition becomes a branch, and the wait for the query block at its
+    // join would then take the rows too
 #pragma unroll
-    for (int i = 0; i < 2 * STEPS; ++i)
-      x[i] = valid ? p[8 * (i >> 1) + 2 * g + (i & 1)] : make_float4(0.f, 0.f, 0.f, 0.f);
-    // Q staged while the coefficient rows are in flight
-    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q, qs);
+    for (int i = 0; i < 2 * STEPS; ++i) x[i] = p[8 * (i >> 1) + 2 * g + (i & 1)];
+    qstage.store(a.n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
@@ -346,8 +353,9 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
       u32x4 hi, lo;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        { const Bf16Split t = split_pk_bf16(x[2 * s + h].x, x[2 * s + h].y); hi[2 * h] = t.hi; lo[2 * h] = t.lo; }
-        { const Bf16Split t = split_pk_bf16(x[2 * s + h].z, x[2 * s + h].w); hi[2 * h + 1] = t.hi; lo[2 * h + 1] = t.lo; }
+        const float4 v = valid ? x[2 * s + h] : make_float4(0.f, 0.f, 0.f, 0.f);
+        { const Bf16Split t = split_pk_bf16(v.x, v.y); hi[2 * h] = t.hi; lo[2 * h] = t.lo; }
+        { const Bf16Split t = split_pk_bf16(v.z, v.w); hi[2 * h + 1] = t.hi; lo[2 * h + 1] = t.lo; }
       }
 #pragma unroll
       for (int qt = 0; qt < RT; ++qt) {
@@ -357,8 +365,9 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
     }
   } else {
     Frag<float, D> b;
-    if (valid) b.load(arow, g); else b.zero();
-    stage_query_batched<T, D, 256, RT>(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q, qs);
+    b.load(arow, g);  // unconditional, as above
+    if (!valid) b.zero();
+    qstage.store(a.n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
     load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
@@ -1030,11 +1039,12 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
   int* sel_l = reinterpret_cast<int*>(lds);
   QueryStage<T, D, NT, RT> qstage;  // the query block is in flight during the Top-K
   const HeadRef hr = head_ref(a, head);
-  qstage.issue(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q);
+  auto issue_q = [&] { qstage.issue(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q); };
   if (topk_in_cover(a)) {  // uniform: every workgroup of the head computes the same kept regions
     auto emit = coarse_emitter(a, head, blockIdx.x == 0, [&](int o, int i) { sel_l[o] = i; });
-    coarse_topk_run<false>(a, head, raw, nullptr, emit);
+    coarse_topk_run<false>(a, head, raw, nullptr, emit, issue_q);
   } else {  // the Top-K's own launch wrote them
+    issue_q();
     const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
     for (int i = threadIdx.x; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
   }
@@ -1176,7 +1186,7 @@ __global__ __launch_bounds__(kSelThreads) void coarse_topk_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t keys_l[];  // general path: the keys, when staged
   __shared__ __align__(16) unsigned char raw[kSelRawBytes];
   const int head = blockIdx.x;
-  coarse_topk_run<true>(a, head, raw, keys_l, coarse_emitter(a, head, true, [](int, int) {}));
+  coarse_topk_run<true>(a, head, raw, keys_l, coarse_emitter(a, head, true, [](int, int) {}), [] {});
 }
 
 // ---------------------------------------------------------------------------
@@ -1463,11 +1473,6 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
   const T* kh = reinterpret_cast<const T*>(a.k[hr.item]) + hr.local * a.n_tot * D;
   const T* vh = reinterpret_cast<const T*>(a.v[hr.item]) + hr.local * a.n_tot * D;
 
-  // this wave's query fragment, in flight while the token list arrives
-  Frag<T, D> qf;
-  const T* qh = reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D;
-  if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
-
   // the attended tokens of this split: T positions [t0, t_end), in nck chunks
   // (prompt splits first, then the generated positions' splits)
   const bool gen_part = split >= a.n_split_p;
@@ -1480,6 +1485,11 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
     const int gi = t0 + i;
     tlist[i] = clampi(gi < a.k0 ? a.sel_in[(int64_t)head * a.k0 + gi] : a.gen_idx[gi - a.k0], 0, a.n_tot - 1);
   }
+  // this wave's query fragment, requested after the token list (which the
+  // gathers wait for) and in flight during the first chunk's gathers
+  Frag<T, D> qf;
+  const T* qh = reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D;
+  if (qvalid) qf.load(qh + (int64_t)query * D, g); else qf.zero();
   __syncthreads();
 
   const float sl2 = a.inv_sqrt_d * 1.44269504088896340736f;  // log2(e)/sqrt(d)
