@@ -25,6 +25,8 @@ FLAGS = [
     "-Wall",
     # keep float32 arithmetic in unpacked VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments in the first 14 dwords arrive in scalar registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
 ]
 
 STEP_COMBOS = [(t, d, rt) for t in ("bf16_t", "float") for d in (128, 64) for rt in (1, 2, 3, 4)]

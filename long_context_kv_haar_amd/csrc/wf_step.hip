@@ -82,10 +82,82 @@ struct HeadRef {
   int item;
   int64_t local;
 };
-__device__ __forceinline__ HeadRef head_ref(const StepArgs& a, int head) {
-  const int item = a.n_items == 1 ? 0 : head / a.heads_per_item;
-  return {item, (int64_t)(head - item * a.heads_per_item)};
+__device__ __forceinline__ HeadRef head_ref(int n_items, int heads_per_item, int head) {
+  const int item = n_items == 1 ? 0 : head / heads_per_item;
+  return {item, (int64_t)(head - item * heads_per_item)};
 }
+__device__ __forceinline__ HeadRef head_ref(const StepArgs& a, int head) {
+  return head_ref(a.n_items, a.heads_per_item, head);
+}
+
+// Leading kernel arguments.  The first 14 dwords of a kernel's arguments are
+// placed in scalar registers before its waves start (kernarg preloading), so
+// what a stage needs for its first loads goes there: the loads then wait for
+// no round trip to the argument segment, and on a single-layer call not for
+// the layer's pointers either.  Each stage states what p[] and i[] hold; the
+// same values are in StepArgs for everything else.
+struct Lead {
+  const void* p[3];
+  int i[8];
+};
+#define WF_LEAD_PARAMS                                                                                      \
+  const void *lead_p0, const void *lead_p1, const void *lead_p2, int lead_i0, int lead_i1, int lead_i2,     \
+      int lead_i3, int lead_i4, int lead_i5, int lead_i6, int lead_i7
+#define WF_LEAD \
+  (Lead{{lead_p0, lead_p1, lead_p2}, {lead_i0, lead_i1, lead_i2, lead_i3, lead_i4, lead_i5, lead_i6, lead_i7}})
+
+// What the cover stage's first loads (the coarse keys) need.
+struct CoverLead {
+  const uint32_t* keys;  // [heads_total][n_top]
+  int n_top, k_top, topk_s, levels, soft, n_items, heads_per_item;
+  __host__ __device__ static CoverLead of(const Lead& l) {
+    return {static_cast<const uint32_t*>(l.p[0]), l.i[0], l.i[1], l.i[2], l.i[3], l.i[4], l.i[5], l.i[6]};
+  }
+  __host__ __device__ Lead lead() const {
+    return {{keys, nullptr, nullptr}, {n_top, k_top, topk_s, levels, soft, n_items, heads_per_item, 0}};
+  }
+};
+// What the refinement's first loads (coverage scores, level ranges, kept
+// coarse regions) need; the level offsets inside a head's scores follow
+// from `covered`.
+struct RefineLead {
+  const float* cov;       // [heads_total][cov_len]
+  const int32_t* sel_top; // [heads_total][k_top]
+  const uint32_t* lvl;    // [heads_total][cover waves][kMaxLevels][2]
+  int covered, levels, k_top, cov_len, n_top, heads_total;
+  __host__ __device__ static RefineLead of(const Lead& l) {
+    return {static_cast<const float*>(l.p[0]), static_cast<const int32_t*>(l.p[1]),
+            static_cast<const uint32_t*>(l.p[2]), l.i[0], l.i[1], l.i[2], l.i[3], l.i[4], l.i[5]};
+  }
+  __host__ __device__ Lead lead() const {
+    return {{cov, sel_top, lvl}, {covered, levels, k_top, cov_len, n_top, heads_total, 0, 0}};
+  }
+};
+// What the attention's first loads (its part of the attended-set list) need.
+struct AttendLead {
+  const int32_t* sel_in;   // kept prompt tokens [heads_total][k0]
+  const int32_t* gen_idx;  // [n_gen]
+  int n_split_p, cps_p, cps_g, k0, n_att, n_tot, n_items, heads_per_item;
+  __host__ __device__ static AttendLead of(const Lead& l) {
+    return {static_cast<const int32_t*>(l.p[0]), static_cast<const int32_t*>(l.p[1]), l.i[0], l.i[1], l.i[2], l.i[3],
+            l.i[4], l.i[5], l.i[6], l.i[7]};
+  }
+  __host__ __device__ Lead lead() const {
+    return {{sel_in, gen_idx, nullptr}, {n_split_p, cps_p, cps_g, k0, n_att, n_tot, n_items, heads_per_item}};
+  }
+};
+// What the split merge's loads need.
+struct CombineLead {
+  const float* part_ml;
+  const float* part_o;
+  int n_q, heads_total, n_split;
+  __host__ __device__ static CombineLead of(const Lead& l) {
+    return {static_cast<const float*>(l.p[0]), static_cast<const float*>(l.p[1]), l.i[0], l.i[1], l.i[2]};
+  }
+  __host__ __device__ Lead lead() const {
+    return {{part_ml, part_o, nullptr}, {n_q, heads_total, n_split, 0, 0, 0, 0, 0}};
+  }
+};
 
 // Max across the 16 lanes of a row; every lane of the row ends with it.
 __device__ __forceinline__ float row_max16(float x) {
@@ -235,34 +307,35 @@ __device__ __forceinline__ void coarse_topk_sel(const uint32_t* keys, int n, int
 // before the Top-K ends: after the keys' loads where they are in registers,
 // else first.
 template <bool LARGE, class Emit, class Pre>
-__device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, unsigned char* raw, uint32_t* keys_l,
-                                                Emit emit, Pre pre) {
-  const uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
+__device__ __forceinline__ void coarse_topk_run(const StepArgs& a, const CoverLead& cl, int head, unsigned char* raw,
+                                                uint32_t* keys_l, Emit emit, Pre pre) {
+  const uint32_t* keys = cl.keys + (int64_t)head * cl.n_top;
+  const int n = cl.n_top, k = cl.k_top;
   SelShared<kSelThreads>& sh = *reinterpret_cast<SelShared<kSelThreads>*>(raw);
-  switch (a.topk_s) {
-    case 1: coarse_topk_sel<1>(keys, a.n_top, a.k_top, sh, emit, pre); return;
-    case 2: coarse_topk_sel<2>(keys, a.n_top, a.k_top, sh, emit, pre); return;
-    case 4: coarse_topk_sel<4>(keys, a.n_top, a.k_top, sh, emit, pre); return;
+  switch (cl.topk_s) {
+    case 1: coarse_topk_sel<1>(keys, n, k, sh, emit, pre); return;
+    case 2: coarse_topk_sel<2>(keys, n, k, sh, emit, pre); return;
+    case 4: coarse_topk_sel<4>(keys, n, k, sh, emit, pre); return;
     default: break;
   }
   if constexpr (LARGE) {
-    switch (a.topk_s) {
-      case 8: coarse_topk_sel<8>(keys, a.n_top, a.k_top, sh, emit, pre); return;
-      case 16: coarse_topk_sel<16>(keys, a.n_top, a.k_top, sh, emit, pre); return;
-      case 32: coarse_topk_sel<32>(keys, a.n_top, a.k_top, sh, emit, pre); return;
+    switch (cl.topk_s) {
+      case 8: coarse_topk_sel<8>(keys, n, k, sh, emit, pre); return;
+      case 16: coarse_topk_sel<16>(keys, n, k, sh, emit, pre); return;
+      case 32: coarse_topk_sel<32>(keys, n, k, sh, emit, pre); return;
       default: break;
     }
     pre();
     auto& fs = *reinterpret_cast<TopKFastShared<kSelThreads>*>(raw);
     auto out = [&](int o, int i) {
-      if (o < a.k_top) emit(o, i, key_to_f32(keys[i]));
+      if (o < k) emit(o, i, key_to_f32(keys[i]));
     };
     if (a.coarse_keys_in_lds) {
-      for (int i = threadIdx.x; i < a.n_top; i += kSelThreads) keys_l[i] = keys[i];
+      for (int i = threadIdx.x; i < n; i += kSelThreads) keys_l[i] = keys[i];
       __syncthreads();
-      topk_fast<kSelThreads>([&](int i) { return keys_l[i]; }, a.n_top, a.k_top, fs, out);
+      topk_fast<kSelThreads>([&](int i) { return keys_l[i]; }, n, k, fs, out);
     } else {
-      topk_fast<kSelThreads>([&](int i) { return keys[i]; }, a.n_top, a.k_top, fs, out);
+      topk_fast<kSelThreads>([&](int i) { return keys[i]; }, n, k, fs, out);
     }
   }
 }
@@ -270,8 +343,20 @@ __device__ __forceinline__ void coarse_topk_run(const StepArgs& a, int head, uns
 // Where the coarse Top-K runs: in every cover workgroup of the head (each
 // computes the same set; n_L <= 1 024 and L > 0), else in a launch of its
 // own, one workgroup per head.
-__device__ __forceinline__ bool topk_in_cover(const StepArgs& a) {
-  return a.topk_s >= 1 && a.topk_s <= 4 && a.levels > 0 && a.soft == 0;
+__host__ __device__ __forceinline__ bool topk_in_cover(const CoverLead& cl) {
+  return cl.topk_s >= 1 && cl.topk_s <= 4 && cl.levels > 0 && cl.soft == 0;
+}
+__host__ __device__ __forceinline__ CoverLead cover_lead(const StepArgs& a) {
+  return {a.keys_top, a.n_top, a.k_top, a.topk_s, a.levels, a.soft, a.n_items, a.heads_per_item};
+}
+__host__ __device__ __forceinline__ AttendLead attend_lead(const StepArgs& a) {
+  return {a.sel_in, a.gen_idx, a.n_split_p, a.cps_p, a.cps_g, a.k0, a.n_att, a.n_tot, a.n_items, a.heads_per_item};
+}
+__host__ __device__ __forceinline__ RefineLead refine_lead(const StepArgs& a) {
+  return {a.cov, a.sel_top, a.lvl_mm, (int)a.covered, a.levels, a.k_top, (int)a.cov_len, a.n_top, a.heads_total};
+}
+__host__ __device__ __forceinline__ CombineLead combine_lead(const StepArgs& a) {
+  return {a.part_ml, a.part_o, a.n_q, a.heads_total, a.n_split};
 }
 
 // The softmax scores' logits of one head (level L first).
@@ -283,14 +368,14 @@ __device__ __forceinline__ float* head_logits(const StepArgs& a, int head) {
 // (workgroup `writer` of the head only), the level-L sinks, and for L = 0
 // the kept tokens.
 template <class F>
-__device__ __forceinline__ auto coarse_emitter(const StepArgs& a, int head, bool writer, F emit_sel) {
+__device__ __forceinline__ auto coarse_emitter(const StepArgs& a, int head, const HeadRef& hr, bool writer,
+                                               F emit_sel) {
   const bool report = writer && (a.sel_levels || a.score_levels);
   int32_t* sel_g = writer ? a.sel_top + (int64_t)head * a.k_top : nullptr;
   int32_t* dbg_sel = report && a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
   float* dbg_score = report && a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
   // with L = 0 the coarse level is the tokens themselves: these are the kept tokens
   int32_t* tsel = (writer && a.levels == 0) ? a.sel_ws + (int64_t)head * a.k0 : nullptr;
-  const HeadRef hr = head_ref(a, head);
   int32_t* tout = (writer && a.levels == 0 && a.sel_out[hr.item]) ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
   return [=](int o, int i, float sc) {
     emit_sel(o, i);
@@ -315,25 +400,29 @@ constexpr size_t kSelRawBytes = cmax(sizeof(SelShared<kSelThreads>), TopKRaw<kSe
 // multiplied exactly, accumulated in float32.  Max over queries: in registers
 // over qt, then across the 16 lanes of a row.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int RT, bool MEAN>
-__device__ __forceinline__ void coarse_stage(const StepArgs& a) {
+template <typename T, int D, int RT, bool MEAN, bool ONE>
+__device__ __forceinline__ void coarse_stage(const StepArgs& a, const Lead& ld) {
   using AG = QueryAgg<MEAN>;
   __shared__ __align__(16) T qs[16 * RT * (D + QueryLds<T>::PAD)];
   const int head = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, l16 = lane & 15;
+  // leading arguments: the layer's A_L and Q (single-layer calls), n_top, n_q
+  const int n_top = ld.i[0], n_q = ld.i[1];
 
   const int n = blockIdx.x * 64 + w * 16 + l16;  // region supplied by this lane (A operand)
-  const bool valid = n < a.n_top;
-  const HeadRef hr = head_ref(a, head);
-  const float* arow = a.a_top[hr.item] + (hr.local * a.n_top + (valid ? n : 0)) * D;
+  const bool valid = n < n_top;
+  const HeadRef hr = ONE ? HeadRef{0, head} : head_ref(a, head);
+  const float* atop = ONE ? static_cast<const float*>(ld.p[0]) : a.a_top[hr.item];
+  const T* qh = (ONE ? static_cast<const T*>(ld.p[1]) : reinterpret_cast<const T*>(a.q[hr.item])) + hr.local * n_q * D;
+  const float* arow = atop + (hr.local * n_top + (valid ? n : 0)) * D;
   f32x4 acc[RT];
 #pragma unroll
   for (int qt = 0; qt < RT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the query block is requested first: it goes to LDS while the coefficient
   // rows are still in flight
   QueryStage<T, D, 256, RT> qstage;
-  qstage.issue(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q);
+  qstage.issue(qh, n_q);
   if constexpr (sizeof(T) == 2) {
     constexpr int STEPS = D / 32;
     // step s of lane group g: coefficients [32 s + 8 g, 32 s + 8 g + 8), as Frag<bf16_t>
@@ -344,10 +433,10 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
     // join would then take the rows too
 #pragma unroll
     for (int i = 0; i < 2 * STEPS; ++i) x[i] = p[8 * (i >> 1) + 2 * g + (i & 1)];
-    qstage.store(a.n_q, qs);
+    qstage.store(n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
-    load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
+    load_query_frags<T, D, RT>(qs, n_q, l16, g, qf);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
       u32x4 hi, lo;
@@ -367,10 +456,10 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
     Frag<float, D> b;
     b.load(arow, g);  // unconditional, as above
     if (!valid) b.zero();
-    qstage.store(a.n_q, qs);
+    qstage.store(n_q, qs);
     __syncthreads();
     Frag<T, D> qf[RT];
-    load_query_frags<T, D, RT>(qs, a.n_q, l16, g, qf);
+    load_query_frags<T, D, RT>(qs, n_q, l16, g, qf);
 #pragma unroll
     for (int qt = 0; qt < RT; ++qt) acc[qt] = mma_tile<D>(b, qf[qt], acc[qt]);
   }
@@ -380,10 +469,10 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
 #pragma unroll
     for (int qt = 0; qt < RT; ++qt) {
       const int query = 16 * qt + l16;
-      if (query < a.n_q)
+      if (query < n_q)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (n0 + r < a.n_top) lg[(int64_t)query * a.n_top4 + n0 + r] = acc[qt][r] * a.inv_sqrt_d;
+          if (n0 + r < n_top) lg[(int64_t)query * a.n_top4 + n0 + r] = acc[qt][r] * a.inv_sqrt_d;
     }
     return;
   }
@@ -393,24 +482,28 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a) {
     float x = acc[0][r];  // query tile 0 always holds a valid row
 #pragma unroll
     for (int qt = 1; qt < RT; ++qt)
-      if (MEAN || 16 * qt + l16 < a.n_q) x = AG::comb(x, acc[qt][r]);  // absent rows: 0 from zero query rows
-    if (!MEAN && l16 >= a.n_q) x = -INFINITY;
+      if (MEAN || 16 * qt + l16 < n_q) x = AG::comb(x, acc[qt][r]);  // absent rows: 0 from zero query rows
+    if (!MEAN && l16 >= n_q) x = -INFINITY;
     m[r] = AG::row(x);
   }
   const float sc = MEAN ? a.inv_sqrt_d * a.inv_nq : a.inv_sqrt_d;
-  uint32_t* keys = a.keys_top + (int64_t)head * a.n_top;
+  uint32_t* keys = a.keys_top + (int64_t)head * n_top;
   const int n0 = blockIdx.x * 64 + w * 16 + 4 * g;  // first region of this row
   if (l16 == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (n0 + r < a.n_top) keys[n0 + r] = order_key(m[r] * sc);
+      if (n0 + r < n_top) keys[n0 + r] = order_key(m[r] * sc);
   }
 }
 
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void coarse_max_kernel(StepArgs a) { coarse_stage<T, D, RT, false>(a); }
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(256) void coarse_mean_kernel(StepArgs a) { coarse_stage<T, D, RT, true>(a); }
+template <typename T, int D, int RT, bool ONE>
+__global__ __launch_bounds__(256) void coarse_max_kernel(WF_LEAD_PARAMS, StepArgs a) {
+  coarse_stage<T, D, RT, false, ONE>(a, WF_LEAD);
+}
+template <typename T, int D, int RT, bool ONE>
+__global__ __launch_bounds__(256) void coarse_mean_kernel(WF_LEAD_PARAMS, StepArgs a) {
+  coarse_stage<T, D, RT, true, ONE>(a, WF_LEAD);
+}
 
 // One 16-row tile of float32 coefficient rows (A operand; lane row l16,
 // k-slice g) against the staged query tiles (B operands): bfloat16 queries
@@ -909,18 +1002,24 @@ __device__ __forceinline__ uint32_t refine_level(const StepArgs& a, int head, He
 }
 
 template <int NT, int S0>
-__device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel_l, SelShared<NT>& sh) {
+__device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& rl, int head, int* sel_l,
+                                           SelShared<NT>& sh) {
   const int t = threadIdx.x, lane = t & 63;
-  const int L = a.levels;
-  const int covered = (int)a.covered;
-  const float* cov = a.cov + (int64_t)head * a.cov_len;
+  const int L = rl.levels;
+  const int covered = rl.covered;
+  const float* cov = rl.cov + (int64_t)head * rl.cov_len;
+  // level j's scores start at sum_{i<j} roundup4(covered >> i) inside the head's slice
+  int coff[kMaxLevels + 1];
+  coff[0] = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxLevels; ++j) coff[j + 1] = coff[j] + (((covered >> j) + 3) & ~3);
   // Every load of the stage is requested before any is waited for, so the
   // coverage scores, the level ranges and the kept coarse regions arrive in
   // one round trip.  First every live level's scores into registers
   // (clamped positions; slots past a level's end are never valid).
   HeldScores<S0> hs;
 #define WF_LOAD_LEVEL(J)                                                              \
-  if (J < L) hs.template load<J>(cov + a.cov_off[J], covered >> J, (t * S0) >> J);    \
+  if (J < L) hs.template load<J>(cov + coff[J], covered >> J, (t * S0) >> J);         \
   else hs.template clear<J>();
   WF_LOAD_LEVEL(0)
   WF_LOAD_LEVEL(1)
@@ -931,14 +1030,14 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel
   WF_LOAD_LEVEL(6)
 #undef WF_LOAD_LEVEL
   // the kept coarse regions [k_L] (from the cover launch), this thread's first one
-  const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
-  const int sel0 = sel_g[min(t, a.k_top - 1)];
+  const int32_t* sel_g = rl.sel_top + (int64_t)head * rl.k_top;
+  const int sel0 = sel_g[min(t, rl.k_top - 1)];
   // each level's score range: the cover waves' slots (at most 128 per head
   // here, lanes l and l + 64 of wave 0), published to LDS.  Loads are
   // unconditional, from clamped slots; slots past the last wave take the
   // neutral range by an all-ones mask.
   const int nwav = (covered + 63) >> 6;
-  const uint32_t* lm = a.lvl_mm + (int64_t)head * nwav * 2 * kMaxLevels;
+  const uint32_t* lm = rl.lvl + (int64_t)head * nwav * 2 * kMaxLevels;
   if (t < 64) {
     uint32_t x[2][kMaxLevels][2];
 #pragma unroll
@@ -969,8 +1068,8 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel
     }
   }
   // the kept coarse regions into LDS (more than one per thread only when k_L > NT)
-  if (t < a.k_top) sel_l[t] = clampi(sel0, 0, a.n_top - 1);
-  for (int i = t + NT; i < a.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, a.n_top - 1);
+  if (t < rl.k_top) sel_l[t] = clampi(sel0, 0, rl.n_top - 1);
+  for (int i = t + NT; i < rl.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, rl.n_top - 1);
   sel_init(sh);
   __syncthreads();
 
@@ -1029,7 +1128,7 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, int head, int* sel
 // coverage scores of this workgroup's 256 covered positions.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int RT, bool MEAN, bool BANDS>
-__device__ __forceinline__ void cover_stage(const StepArgs& a) {
+__device__ __forceinline__ void cover_stage(const StepArgs& a, const CoverLead& cl) {
   constexpr int NT = kCoverThreads;
   static_assert(NT == kSelThreads, "the coarse Top-K runs on the cover workgroup");
   extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L], ascending
@@ -1038,11 +1137,11 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
   const int head = blockIdx.y;
   int* sel_l = reinterpret_cast<int*>(lds);
   QueryStage<T, D, NT, RT> qstage;  // the query block is in flight during the Top-K
-  const HeadRef hr = head_ref(a, head);
+  const HeadRef hr = head_ref(cl.n_items, cl.heads_per_item, head);
   auto issue_q = [&] { qstage.issue(reinterpret_cast<const T*>(a.q[hr.item]) + hr.local * a.n_q * D, a.n_q); };
-  if (topk_in_cover(a)) {  // uniform: every workgroup of the head computes the same kept regions
-    auto emit = coarse_emitter(a, head, blockIdx.x == 0, [&](int o, int i) { sel_l[o] = i; });
-    coarse_topk_run<false>(a, head, raw, nullptr, emit, issue_q);
+  if (topk_in_cover(cl)) {  // uniform: every workgroup of the head computes the same kept regions
+    auto emit = coarse_emitter(a, head, hr, blockIdx.x == 0, [&](int o, int i) { sel_l[o] = i; });
+    coarse_topk_run<false>(a, cl, head, raw, nullptr, emit, issue_q);
   } else {  // the Top-K's own launch wrote them
     issue_q();
     const int32_t* sel_g = a.sel_top + (int64_t)head * a.k_top;
@@ -1067,17 +1166,23 @@ __device__ __forceinline__ void cover_stage(const StepArgs& a) {
 template <typename T, int D>
 constexpr int cover_waves_per_simd(int rt) { return (sizeof(T) == 2 || D == 64) && rt <= 2 ? 4 : 1; }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_max_kernel(StepArgs a) {
-  cover_stage<T, D, RT, false, false>(a);
+__global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_max_kernel(WF_LEAD_PARAMS,
+                                                                                                StepArgs a) {
+  cover_stage<T, D, RT, false, false>(a, CoverLead::of(WF_LEAD));
 }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_mean_kernel(StepArgs a) {
-  cover_stage<T, D, RT, true, false>(a);
+__global__ __launch_bounds__(kCoverThreads, (cover_waves_per_simd<T, D>(RT))) void cover_mean_kernel(WF_LEAD_PARAMS,
+                                                                                                 StepArgs a) {
+  cover_stage<T, D, RT, true, false>(a, CoverLead::of(WF_LEAD));
 }
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_bands_max_kernel(StepArgs a) { cover_stage<T, D, RT, false, true>(a); }
+__global__ __launch_bounds__(kCoverThreads) void cover_bands_max_kernel(WF_LEAD_PARAMS, StepArgs a) {
+  cover_stage<T, D, RT, false, true>(a, CoverLead::of(WF_LEAD));
+}
 template <typename T, int D, int RT>
-__global__ __launch_bounds__(kCoverThreads) void cover_bands_mean_kernel(StepArgs a) { cover_stage<T, D, RT, true, true>(a); }
+__global__ __launch_bounds__(kCoverThreads) void cover_bands_mean_kernel(WF_LEAD_PARAMS, StepArgs a) {
+  cover_stage<T, D, RT, true, true>(a, CoverLead::of(WF_LEAD));
+}
 
 // One refinement level with the candidates in registers (n <= ACT * MAXS):
 // candidate i is child (i & 1) of kept parent cur[i >> 1]; the kept ones go
@@ -1186,7 +1291,8 @@ __global__ __launch_bounds__(kSelThreads) void coarse_topk_kernel(StepArgs a) {
   extern __shared__ __align__(16) uint32_t keys_l[];  // general path: the keys, when staged
   __shared__ __align__(16) unsigned char raw[kSelRawBytes];
   const int head = blockIdx.x;
-  coarse_topk_run<true>(a, head, raw, keys_l, coarse_emitter(a, head, true, [](int, int) {}), [] {});
+  coarse_topk_run<true>(a, cover_lead(a), head, raw, keys_l,
+                        coarse_emitter(a, head, head_ref(a, head), true, [](int, int) {}), [] {});
 }
 
 // ---------------------------------------------------------------------------
@@ -1385,11 +1491,11 @@ __global__ __launch_bounds__(kRefineThreads) void refine_soft_kernel(StepArgs a)
 // The in-register refinement, one workgroup of 1 024 threads per head, with
 // S0 = 1 .. 8 level-0 positions per thread (covered sets up to 8 192).
 template <int S0>
-__global__ __launch_bounds__(kRefineThreads) void refine_sel_kernel(StepArgs a) {
+__global__ __launch_bounds__(kRefineThreads) void refine_sel_kernel(WF_LEAD_PARAMS, StepArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];  // the kept coarse regions [k_L]
   __shared__ __align__(16) SelShared<kRefineThreads> sh;
   const int head = blockIdx.x;
-  refine_sel<kRefineThreads, S0>(a, head, reinterpret_cast<int*>(lds), sh);
+  refine_sel<kRefineThreads, S0>(a, RefineLead::of(WF_LEAD), head, reinterpret_cast<int*>(lds), sh);
 }
 
 __global__ __launch_bounds__(kSelThreads) void refine_lists_kernel(StepArgs a) {
@@ -1448,7 +1554,8 @@ __device__ __forceinline__ void merge_state(SoftmaxState<D>& a, float mb, float 
 }
 
 template <typename T, int D, int NQT>
-__device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, int head, int split) {
+__device__ __forceinline__ void attend_split(const StepArgs& a, const AttendLead& al, uint32_t* lds, int head,
+                                             int split) {
   constexpr int TG = kAttendGroups;
   constexpr int NT = 64 * NQT * TG;
   constexpr int CH = attend_chunk(AttendTraits<T>::DT);
@@ -1469,21 +1576,21 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
   const int g = lane >> 4, l16 = lane & 15;
   const int query = 16 * qt + l16;
   const bool qvalid = query < a.n_q;
-  const HeadRef hr = head_ref(a, head);
-  const T* kh = reinterpret_cast<const T*>(a.k[hr.item]) + hr.local * a.n_tot * D;
-  const T* vh = reinterpret_cast<const T*>(a.v[hr.item]) + hr.local * a.n_tot * D;
+  const HeadRef hr = head_ref(al.n_items, al.heads_per_item, head);
+  const T* kh = reinterpret_cast<const T*>(a.k[hr.item]) + hr.local * al.n_tot * D;
+  const T* vh = reinterpret_cast<const T*>(a.v[hr.item]) + hr.local * al.n_tot * D;
 
   // the attended tokens of this split: T positions [t0, t_end), in nck chunks
   // (prompt splits first, then the generated positions' splits)
-  const bool gen_part = split >= a.n_split_p;
-  const int cps = gen_part ? a.cps_g : a.cps_p;
-  const int t0 = gen_part ? a.k0 + (split - a.n_split_p) * cps * CH : split * cps * CH;
-  const int t_end = min(gen_part ? a.n_att : a.k0, t0 + cps * CH);
+  const bool gen_part = split >= al.n_split_p;
+  const int cps = gen_part ? al.cps_g : al.cps_p;
+  const int t0 = gen_part ? al.k0 + (split - al.n_split_p) * cps * CH : split * cps * CH;
+  const int t_end = min(gen_part ? al.n_att : al.k0, t0 + cps * CH);
   const int tcount = max(0, t_end - t0);
   const int nck = (tcount + CH - 1) / CH;
   for (int i = threadIdx.x; i < tcount; i += NT) {
     const int gi = t0 + i;
-    tlist[i] = clampi(gi < a.k0 ? a.sel_in[(int64_t)head * a.k0 + gi] : a.gen_idx[gi - a.k0], 0, a.n_tot - 1);
+    tlist[i] = clampi(gi < al.k0 ? al.sel_in[(int64_t)head * al.k0 + gi] : al.gen_idx[gi - al.k0], 0, al.n_tot - 1);
   }
   // this wave's query fragment, requested after the token list (which the
   // gathers wait for) and in flight during the first chunk's gathers
@@ -1678,9 +1785,10 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, uint32_t* lds, i
 }
 
 template <typename T, int D, int NQT>
-__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(StepArgs a) {
+__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void attend_kernel(WF_LEAD_PARAMS,
+                                                                                                    StepArgs a) {
   extern __shared__ __align__(16) uint32_t lds[];
-  attend_split<T, D, NQT>(a, lds, blockIdx.y, blockIdx.x);
+  attend_split<T, D, NQT>(a, AttendLead::of(WF_LEAD), lds, blockIdx.y, blockIdx.x);
 }
 
 // The refinement of every head and the generated positions' attention
@@ -1690,21 +1798,23 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT
 // attention launch after it takes only the prompt splits.  No workgroup
 // waits for another.
 template <typename T, int D, int NQT, int S0>
-__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void refine_gen_kernel(StepArgs a) {
+__global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT)) void refine_gen_kernel(
+    WF_LEAD_PARAMS, StepArgs a) {
   constexpr int NT = 64 * NQT * kAttendGroups;
   extern __shared__ __align__(16) uint32_t lds[];
-  const int H = a.heads_total;
+  const RefineLead rl = RefineLead::of(WF_LEAD);
+  const int H = rl.heads_total;
   if ((int)blockIdx.x < H) {
     const int head = blockIdx.x;
     // the kept coarse regions [k_L], then the selection state
-    SelShared<NT>& sh = *reinterpret_cast<SelShared<NT>*>(lds + ((a.k_top + 3) & ~3));
-    refine_sel<NT, S0>(a, head, reinterpret_cast<int*>(lds), sh);
+    SelShared<NT>& sh = *reinterpret_cast<SelShared<NT>*>(lds + ((rl.k_top + 3) & ~3));
+    refine_sel<NT, S0>(a, rl, head, reinterpret_cast<int*>(lds), sh);
     return;
   }
   const int ns_g = a.n_split - a.n_split_p;
   const int r = blockIdx.x - H;
   const int head = r / ns_g;
-  attend_split<T, D, NQT>(a, lds, head, a.n_split_p + (r - head * ns_g));
+  attend_split<T, D, NQT>(a, attend_lead(a), lds, head, a.n_split_p + (r - head * ns_g));
 }
 
 // ---------------------------------------------------------------------------
@@ -1717,15 +1827,16 @@ __global__ __launch_bounds__(64 * NQT * kAttendGroups, attend_waves_per_simd(NQT
 // ---------------------------------------------------------------------------
 #if !defined(WF_STEP_T)  // one compile unit holds it
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(WF_LEAD_PARAMS, StepArgs a) {
   constexpr int C4 = D / 4;
+  const CombineLead cl = CombineLead::of(WF_LEAD);
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_head = (int64_t)a.n_q * C4;
-  if (idx >= per_head * a.heads_total) return;
+  const int64_t per_head = (int64_t)cl.n_q * C4;
+  if (idx >= per_head * cl.heads_total) return;
   const int head = (int)(idx / per_head);
   const int rem = (int)(idx - head * per_head);
   const int query = rem / C4, c4 = rem - query * C4;
-  const int ns = a.n_split;
+  const int ns = cl.n_split;
   float mv[kMaxSplit], lv[kMaxSplit];
   float4 ov[kMaxSplit];
 #pragma unroll
@@ -1734,11 +1845,11 @@ __global__ __launch_bounds__(256) void combine_kernel(StepArgs a) {
     lv[sp] = 0.f;
     ov[sp] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (sp < ns) {  // uniform: only the splits that exist are read
-      const int64_t row = ((int64_t)head * ns + sp) * a.n_q + query;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + row * 2);
+      const int64_t row = ((int64_t)head * ns + sp) * cl.n_q + query;
+      const float2 ml = *reinterpret_cast<const float2*>(cl.part_ml + row * 2);
       mv[sp] = ml.x;
       lv[sp] = ml.y;
-      ov[sp] = *reinterpret_cast<const float4*>(a.part_o + row * D + 4 * c4);
+      ov[sp] = *reinterpret_cast<const float4*>(cl.part_o + row * D + 4 * c4);
     }
   }
   float mm = -INFINITY;
@@ -1783,6 +1894,15 @@ static hipError_t launch_one(K kernel, dim3 grid, dim3 block, int lds, hipStream
   hipLaunchKernelGGL(kernel, grid, block, lds, s, a);
   return hipGetLastError();
 }
+template <class K>
+static hipError_t launch_lead(K kernel, dim3 grid, dim3 block, int lds, hipStream_t s, const Lead& l,
+                              const StepArgs& a) {
+  hipError_t e = allow_lds(kernel, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, l.p[0], l.p[1], l.p[2], l.i[0], l.i[1], l.i[2], l.i[3], l.i[4],
+                     l.i[5], l.i[6], l.i[7], a);
+  return hipGetLastError();
+}
 
 // The coarse and cover stages, for one (T, D, RT).
 template <typename T, int D, int RT>
@@ -1791,19 +1911,24 @@ hipError_t launch_select(const StepArgs& a, const SelectLaunch& L, int stage, hi
   const int H = P.heads_total;
   if (stage == 0) {
     const dim3 coarse_grid(P.coarse_wg, H);
-    return L.agg_mean ? launch_one(coarse_mean_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a)
-                      : launch_one(coarse_max_kernel<T, D, RT>, coarse_grid, dim3(256), 0, s, a);
+    const Lead ld{{a.a_top[0], a.q[0], nullptr}, {P.n_top, P.n_q, 0, 0, 0, 0, 0, 0}};
+    if (L.n_items == 1)
+      return L.agg_mean ? launch_lead(coarse_mean_kernel<T, D, RT, true>, coarse_grid, dim3(256), 0, s, ld, a)
+                        : launch_lead(coarse_max_kernel<T, D, RT, true>, coarse_grid, dim3(256), 0, s, ld, a);
+    return L.agg_mean ? launch_lead(coarse_mean_kernel<T, D, RT, false>, coarse_grid, dim3(256), 0, s, ld, a)
+                      : launch_lead(coarse_max_kernel<T, D, RT, false>, coarse_grid, dim3(256), 0, s, ld, a);
   }
   hipError_t e;
   const dim3 cover_grid(P.cover_wg, H);
   const dim3 blk(kCoverThreads);
   const int lds = P.cover_lds;
+  const Lead ld = cover_lead(a).lead();
   if (P.stored_bands)
-    e = L.agg_mean ? launch_one(cover_bands_mean_kernel<T, D, RT>, cover_grid, blk, lds, s, a)
-                   : launch_one(cover_bands_max_kernel<T, D, RT>, cover_grid, blk, lds, s, a);
+    e = L.agg_mean ? launch_lead(cover_bands_mean_kernel<T, D, RT>, cover_grid, blk, lds, s, ld, a)
+                   : launch_lead(cover_bands_max_kernel<T, D, RT>, cover_grid, blk, lds, s, ld, a);
   else
-    e = L.agg_mean ? launch_one(cover_mean_kernel<T, D, RT>, cover_grid, blk, lds, s, a)
-                   : launch_one(cover_max_kernel<T, D, RT>, cover_grid, blk, lds, s, a);
+    e = L.agg_mean ? launch_lead(cover_mean_kernel<T, D, RT>, cover_grid, blk, lds, s, ld, a)
+                   : launch_lead(cover_max_kernel<T, D, RT>, cover_grid, blk, lds, s, ld, a);
   return e;
 }
 
@@ -1813,8 +1938,8 @@ template <typename T, int D, int RT>
 hipError_t launch_attend(const StepArgs& a, const SelectLaunch& L, hipStream_t s) {
   const SelectPlan& P = L.plan;
   const bool gen_done = !L.attend_only && P.fuse_s0 > 0;
-  return launch_one(attend_kernel<T, D, RT>, dim3(gen_done ? P.n_split_p : P.n_split, P.heads_total),
-                    dim3(64 * RT * kAttendGroups), P.attend_lds, s, a);
+  return launch_lead(attend_kernel<T, D, RT>, dim3(gen_done ? P.n_split_p : P.n_split, P.heads_total),
+                     dim3(64 * RT * kAttendGroups), P.attend_lds, s, attend_lead(a).lead(), a);
 }
 
 // The refinement with the generated positions' splits (refine_gen_kernel), for one (T, D, RT).
@@ -1825,11 +1950,12 @@ hipError_t launch_refine_gen(const StepArgs& a, const SelectLaunch& L, hipStream
   const int refine_lds = 4 * ((P.k_top + 3) & ~3) + (int)sizeof(SelShared<NT>);
   const int lds = P.attend_lds > refine_lds ? P.attend_lds : refine_lds;
   const dim3 grid(P.heads_total * (1 + P.n_split - P.n_split_p));
+  const Lead ld = refine_lead(a).lead();
   switch (P.fuse_s0) {
-    case 1: return launch_one(refine_gen_kernel<T, D, RT, 1>, grid, dim3(NT), lds, s, a);
-    case 2: return launch_one(refine_gen_kernel<T, D, RT, 2>, grid, dim3(NT), lds, s, a);
-    case 4: return launch_one(refine_gen_kernel<T, D, RT, 4>, grid, dim3(NT), lds, s, a);
-    default: return launch_one(refine_gen_kernel<T, D, RT, 8>, grid, dim3(NT), lds, s, a);
+    case 1: return launch_lead(refine_gen_kernel<T, D, RT, 1>, grid, dim3(NT), lds, s, ld, a);
+    case 2: return launch_lead(refine_gen_kernel<T, D, RT, 2>, grid, dim3(NT), lds, s, ld, a);
+    case 4: return launch_lead(refine_gen_kernel<T, D, RT, 4>, grid, dim3(NT), lds, s, ld, a);
+    default: return launch_lead(refine_gen_kernel<T, D, RT, 8>, grid, dim3(NT), lds, s, ld, a);
   }
 }
 
@@ -1896,10 +2022,10 @@ static hipError_t launch_apart(const StepArgs& a, const SelectLaunch& L, int sta
     }
   }
   switch (P.refine_s0) {
-    case 1: return launch_one(refine_sel_kernel<1>, grid, rblock, P.cover_lds, s, a);
-    case 2: return launch_one(refine_sel_kernel<2>, grid, rblock, P.cover_lds, s, a);
-    case 4: return launch_one(refine_sel_kernel<4>, grid, rblock, P.cover_lds, s, a);
-    case 8: return launch_one(refine_sel_kernel<8>, grid, rblock, P.cover_lds, s, a);
+    case 1: return launch_lead(refine_sel_kernel<1>, grid, rblock, P.cover_lds, s, refine_lead(a).lead(), a);
+    case 2: return launch_lead(refine_sel_kernel<2>, grid, rblock, P.cover_lds, s, refine_lead(a).lead(), a);
+    case 4: return launch_lead(refine_sel_kernel<4>, grid, rblock, P.cover_lds, s, refine_lead(a).lead(), a);
+    case 8: return launch_lead(refine_sel_kernel<8>, grid, rblock, P.cover_lds, s, refine_lead(a).lead(), a);
     default: return launch_one(refine_lists_kernel, grid, block, P.refine_lds, s, a);
   }
 }
@@ -2008,9 +2134,9 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
          : (d128 ? launch_rt_attend<float, 128>(rt, a, L, s) : launch_rt_attend<float, 64>(rt, a, L, s));
   if (e != hipSuccess) return e;
   const unsigned comb_blocks = (unsigned)(((int64_t)P.heads_total * P.n_q * (P.head_dim / 4) + 255) / 256);
-  if (d128) hipLaunchKernelGGL(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+  const Lead ld = combine_lead(a).lead();
+  return d128 ? launch_lead(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, ld, a)
+              : launch_lead(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, ld, a);
 }
 #endif
 
