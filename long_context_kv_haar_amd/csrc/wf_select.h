@@ -66,6 +66,13 @@ template <int NT> struct SelShared {
   uint32_t rmn[8], rmx[8];        // the refinement: each level's score range (order keys)
   int bc[4];                      // a level's boundary bin, broadcast by wave 0
   uint64_t tau;                   // a level's threshold pair, broadcast by wave 0
+  // the refinement's per-call values, staged before its first barrier
+  int bud[8];                     // k_L .. k_0
+  int k0;                         // k_0
+  int32_t* tsel;                  // the head's kept tokens (workspace)
+  int32_t* sout;                  // and the caller's copy (or null)
+  int32_t* dsel;                  // the head's per-level kept regions (or null)
+  float* dscore;                  // and their scores (or null)
 };
 
 struct SelCursor {

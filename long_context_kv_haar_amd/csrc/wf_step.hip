@@ -965,25 +965,25 @@ static_assert(kMaxLevels == 7, "the refinement holds seven levels");
 // parent level's slots); returns the kept mask over the P slots and, with
 // the per-level sinks, writes the level's kept regions at off.
 template <int NT, int S0, int P>
-__device__ __forceinline__ uint32_t refine_level(const StepArgs& a, int head, HeldScores<S0>& hs, int j,
-                                                 uint32_t keptp, const int* sel_l, SelShared<NT>& sh, SelCursor& cur,
-                                                 int off) {
+__device__ __forceinline__ uint32_t refine_level(const StepArgs& a, const RefineLead& rl, int head, HeldScores<S0>& hs,
+                                                 int j, uint32_t keptp, const int* sel_l, SelShared<NT>& sh,
+                                                 SelCursor& cur, int off) {
   const int t = threadIdx.x;
-  const int L = a.levels;
+  const int L = rl.levels;
   float sc[P];
   hs.template first<P>(j, sc);
-  const int p0 = (t * S0) >> j, nj = (int)(a.covered >> j);
+  const int p0 = (t * S0) >> j, nj = rl.covered >> j;
   const bool own = P > 1 || ((t * S0) & ((1 << j) - 1)) == 0;
   uint32_t valid = 0u;
 #pragma unroll
   for (int i = 0; i < P; ++i) valid |= ((p0 + i < nj) & ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
   const uint32_t owned = own ? valid : 0u;
-  const int kj = a.budgets[L - j];
+  const int kj = sh.bud[L - j];
   const uint32_t kept =
       select_level<NT, P>(sc, valid, owned, p0, kj, key_to_f32(sh.rmn[j]), key_to_f32(sh.rmx[j]), sh, cur);
-  if (a.sel_levels || a.score_levels) {  // uniform: level j's kept regions, ascending, with their scores
-    int32_t* dbg_sel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
-    float* dbg_score = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+  int32_t* dbg_sel = sh.dsel;
+  float* dbg_score = sh.dscore;
+  if (dbg_sel || dbg_score) {  // uniform: level j's kept regions, ascending, with their scores
     const uint32_t km = own ? kept : 0u;
     int o = block_excl_scan(__popc(km), sh, 2 + (j & 1));
     const int shl = L - j;
@@ -992,7 +992,7 @@ __device__ __forceinline__ uint32_t refine_level(const StepArgs& a, int head, He
       if ((km >> i) & 1u) {
         const int p = p0 + i;
         if (o < kj) {
-          if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, a.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
+          if (dbg_sel) dbg_sel[off + o] = (sel_l[min(p >> shl, rl.k_top - 1)] << shl) + (p & ((1 << shl) - 1));
           if (dbg_score) dbg_score[off + o] = sc[i];
         }
         ++o;
@@ -1070,6 +1070,18 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
   // the kept coarse regions into LDS (more than one per thread only when k_L > NT)
   if (t < rl.k_top) sel_l[t] = clampi(sel0, 0, rl.n_top - 1);
   for (int i = t + NT; i < rl.k_top; i += NT) sel_l[i] = clampi(sel_g[i], 0, rl.n_top - 1);
+  // the level budgets and the output pointers, read while the loads above are
+  // in flight: read after the barrier, each would wait for a trip to memory
+  if (t == 0) {
+#pragma unroll
+    for (int j = 0; j <= kMaxLevels; ++j) sh.bud[j] = a.budgets[j];
+    sh.dsel = a.sel_levels ? a.sel_levels + (int64_t)head * a.sum_k : nullptr;
+    sh.dscore = a.score_levels ? a.score_levels + (int64_t)head * a.sum_k : nullptr;
+    sh.k0 = a.k0;
+    const HeadRef hr = head_ref(a, head);
+    sh.tsel = a.sel_ws + (int64_t)head * a.k0;
+    sh.sout = a.sel_out[hr.item] ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
+  }
   sel_init(sh);
   __syncthreads();
 
@@ -1078,43 +1090,43 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
   {
     const int pl0 = (t * S0) >> L;
     const int pl = (S0 >> L) > 0 ? (S0 >> L) : 1;
-    for (int m = 0; m < pl; ++m) keptp |= (pl0 + m < a.k_top) ? (1u << m) : 0u;
+    for (int m = 0; m < pl; ++m) keptp |= (pl0 + m < rl.k_top) ? (1u << m) : 0u;
   }
-  int off = a.k_top;
+  int off = rl.k_top;
   SelCursor cur;
   for (int j = L - 1; j >= 0; --j) {  // each level on its own count of held slots
     const int pj = (S0 >> j) > 0 ? (S0 >> j) : 1;
     uint32_t kept;
     if (pj == 1) {
-      kept = refine_level<NT, S0, 1>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+      kept = refine_level<NT, S0, 1>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
     } else if constexpr (S0 >= 2) {
       if (pj == 2) {
-        kept = refine_level<NT, S0, 2>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+        kept = refine_level<NT, S0, 2>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
       } else if constexpr (S0 >= 4) {
-        if (pj == 4) kept = refine_level<NT, S0, 4>(a, head, hs, j, keptp, sel_l, sh, cur, off);
-        else kept = refine_level<NT, S0, S0>(a, head, hs, j, keptp, sel_l, sh, cur, off);
+        if (pj == 4) kept = refine_level<NT, S0, 4>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
+        else kept = refine_level<NT, S0, S0>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
       } else {
         kept = 0u;  // not reached: pj <= S0
       }
     } else {
       kept = 0u;  // not reached: pj <= S0
     }
-    off += a.budgets[L - j];
+    off += sh.bud[L - j];
     keptp = kept;
   }
 
   // the kept tokens, ascending
   int o = block_excl_scan(__popc(keptp), sh, 1);
-  int32_t* tsel = a.sel_ws + (int64_t)head * a.k0;
-  const HeadRef hr = head_ref(a, head);
-  int32_t* so = a.sel_out[hr.item] ? a.sel_out[hr.item] + hr.local * a.k0 : nullptr;
+  int32_t* tsel = sh.tsel;
+  int32_t* so = sh.sout;
+  const int k0 = sh.k0;
   const int mask = (1 << L) - 1;
 #pragma unroll
   for (int i = 0; i < S0; ++i)
     if ((keptp >> i) & 1u) {
       const int p = t * S0 + i;
-      const int tok = (sel_l[min(p >> L, a.k_top - 1)] << L) + (p & mask);
-      if (o < a.k0) {  // exactly k_0 are kept; the bound guards the buffers
+      const int tok = (sel_l[min(p >> L, rl.k_top - 1)] << L) + (p & mask);
+      if (o < k0) {  // exactly k_0 are kept; the bound guards the buffers
         tsel[o] = tok;
         if (so) so[o] = tok;
       }
