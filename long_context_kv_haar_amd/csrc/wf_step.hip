@@ -168,6 +168,40 @@ __device__ __forceinline__ float row_max16(float x) {
   return x;
 }
 
+// Max over the 16 lanes of a row of each of M values per lane (M = 1, 2, 4,
+// 8 or 16), left scattered over the row: value k ends in the lanes whose row
+// index, shifted right by log2(16 / M), is k.  Step s pairs every lane with
+// the lane its row index maps to under row mirror, half-row mirror, and the
+// two quad swaps (s = 0..3): each pairing flips bit 3 - s of the index and only
+// lower bits, so a pair always holds the same values, and while more than one
+// value is left, that bit picks the half a lane keeps (the partner keeps the
+// other).  M / 2 + M / 4 + ... + 4 - log2(M) DPP steps instead of 4 per value.
+template <int S> struct ScatterDpp;
+template <> struct ScatterDpp<0> { static constexpr int CTRL = 0x140; };  // row_mirror
+template <> struct ScatterDpp<1> { static constexpr int CTRL = 0x141; };  // row_half_mirror
+template <> struct ScatterDpp<2> { static constexpr int CTRL = 0x4E; };   // quad_perm [2,3,0,1]
+template <> struct ScatterDpp<3> { static constexpr int CTRL = 0xB1; };   // quad_perm [1,0,3,2]
+template <int M, int S = 0>
+__device__ __forceinline__ float row_max_scatter(const float (&v)[M], int l16) {
+  if constexpr (S == 4) {
+    static_assert(M == 1, "16 lanes hold at most 16 values");
+    return v[0];
+  } else if constexpr (M == 1) {
+    const float w[1] = {fmaxf(v[0], dpp_f<ScatterDpp<S>::CTRL>(v[0]))};
+    return row_max_scatter<1, S + 1>(w, l16);
+  } else {
+    const bool up = (l16 >> (3 - S)) & 1;
+    float h[M / 2];
+#pragma unroll
+    for (int k = 0; k < M / 2; ++k) {
+      const float keep = up ? v[M / 2 + k] : v[k];
+      const float give = up ? v[k] : v[M / 2 + k];
+      h[k] = fmaxf(keep, dpp_f<ScatterDpp<S>::CTRL>(give));
+    }
+    return row_max_scatter<M / 2, S + 1>(h, l16);
+  }
+}
+
 // How the query rows of a block combine into a region score: the maximum
 // (rows past n_q are set to -inf) or the mean (rows past n_q hold 0, the sum
 // is scaled by 1/n_q).  comb() folds two rows a lane holds, row() the 16 rows
@@ -640,6 +674,174 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
   }
 }
 
+// The Haar coverage scores of one wave with the maximum over the query rows
+// (cover_haar below sets up s, the per-query token logits of the wave's four
+// tiles): each level sums its blocks in registers or across lane groups, then
+// takes the maximum over the 16 query rows of every block with one scattered
+// row reduction, so that every lane ends with one block's score (or a copy of
+// it) and the stores and the score range take one value per lane.  Level j's
+// value for block k of the wave sits in the lanes of row g with l16 >> (j < 3
+// ? j : 2) == the block's index inside the row's tiles, as worked out below.
+template <int RT, class Track, class Publish>
+__device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4][RT], float* cov, float isd,
+                                                 int64_t wave_base, int lane, int g, int l16, int jmax, Track& track,
+                                                 Publish& publish, uint32_t& rmn, uint32_t& rmx) {
+  const int64_t covered = a.covered;
+  // level 0: value 4 t + r (token 16 t + 4 g + r) ends in lane l16 = 4 t + r
+  {
+    float v[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = s[t][0][r];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][r]);
+        v[4 * t + r] = x;
+      }
+    const float m = row_max_scatter<16>(v, l16) * isd;
+    const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
+    const bool in = p < covered;
+    if (in) cov[a.cov_off[0] + p] = m;
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(in, m);
+    publish(0);
+  }
+  if (jmax <= 1) return;
+  // level 1: token pairs (r = 0,1 and 2,3) summed in place into s[t][qt][0]
+  // and [2]; value 2 t + h ends in lanes l16 = 4 t + 2 h and 4 t + 2 h + 1
+  {
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) {
+        s[t][qt][0] += s[t][qt][1];
+        s[t][qt][2] += s[t][qt][3];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float x = s[t][0][2 * h];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][2 * h]);
+        v[2 * t + h] = x;
+      }
+    }
+    const float m = row_max_scatter<8>(v, l16) * (isd * 0.70710678118654752440f);
+    const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + 2 * ((l16 >> 1) & 1);  // first token of the pair
+    const bool in = p < covered;
+    if (in && (l16 & 1) == 0) cov[a.cov_off[1] + (p >> 1)] = m;
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(in, m);
+    publish(1);
+  }
+  if (jmax <= 2) return;
+  // level 2: 4-token blocks (one per lane group) into s[t][qt][0]; value t
+  // ends in lanes l16 = 4 t .. 4 t + 3
+  {
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += s[t][qt][2];
+      float x = s[t][0][0];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+      v[t] = x;
+    }
+    const float m = row_max_scatter<4>(v, l16) * (isd * 0.5f);
+    const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g;
+    const bool in = p < covered;
+    if (in && (l16 & 3) == 0) cov[a.cov_off[2] + (p >> 2)] = m;
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(in, m);
+    publish(2);
+  }
+  if (jmax <= 3) return;
+  // level 3: 8-token blocks = lane groups {0,1} and {2,3}; as level 2, with
+  // groups g and g ^ 1 holding the same values
+  {
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor16(s[t][qt][0]);
+      float x = s[t][0][0];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+      v[t] = x;
+    }
+    const float m = row_max_scatter<4>(v, l16) * (isd * 0.35355339059327376220f);
+    const int64_t p = wave_base + 16 * (l16 >> 2) + 8 * (g >> 1);
+    const bool in = p < covered;
+    if (in && (l16 & 3) == 0 && (g & 1) == 0) cov[a.cov_off[3] + (p >> 3)] = m;
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(in, m);
+    publish(3);
+  }
+  if (jmax <= 4) return;
+  // level 4: 16-token blocks = whole tiles, every lane group the same
+  {
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor32(s[t][qt][0]);
+      float x = s[t][0][0];
+#pragma unroll
+      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+      v[t] = x;
+    }
+    const float m = row_max_scatter<4>(v, l16) * (isd * 0.25f);
+    const int64_t p = wave_base + 16 * (l16 >> 2);
+    const bool in = p < covered;
+    if (in && (l16 & 3) == 0 && g == 0) cov[a.cov_off[4] + (p >> 4)] = m;
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(in, m);
+    publish(4);
+  }
+  if (jmax <= 5) return;
+  // level 5: tile pairs, value h ends in lanes l16 = 8 h .. 8 h + 7; level 6:
+  // the whole wave
+  {
+    float v[2], xall = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt) {
+        const float pair = s[2 * h][qt][0] + s[2 * h + 1][qt][0];
+        x = fmaxf(x, pair);
+      }
+      v[h] = x;
+    }
+#pragma unroll
+    for (int qt = 0; qt < RT; ++qt)
+      xall = fmaxf(xall, (s[0][qt][0] + s[1][qt][0]) + (s[2][qt][0] + s[3][qt][0]));
+    const float m = row_max_scatter<2>(v, l16) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
+    const int64_t p = wave_base + 32 * (l16 >> 3);
+    const bool in = p < covered;
+    if (in && (l16 & 7) == 0 && g == 0) cov[a.cov_off[5] + (p >> 5)] = m;
+    rmn = 0xFFFFFFFFu;
+    rmx = 0u;
+    track(in, m);
+    publish(5);
+    if (jmax > 6) {
+      xall = row_max16(xall) * (isd * 0.125f);  // 2^{-3}
+      if (lane == 0) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
+      rmn = 0xFFFFFFFFu;
+      rmx = 0u;
+      track(lane == 0, xall);
+      publish(6);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Haar coverage scores of one wave.  The kept coarse regions, ascending,
 // cover positions p = 0 .. k_L 2^L - 1; position p is token
@@ -717,6 +919,12 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
     return lgh + (int64_t)a.n_q * a.cov_off[j] + (int64_t)query * ((((a.covered >> j) + 3) >> 2) << 2);
   };
   const float isd_raw = a.inv_sqrt_d;
+  if constexpr (!MEAN) {
+    if (!soft) {  // uniform
+      cover_levels_max<RT>(a, s, cov, isd, wave_base, lane, g, l16, jmax, track, publish, rmn, rmx);
+      return;
+    }
+  }
   // level 0
   rmn = 0xFFFFFFFFu;
   rmx = 0u;
