@@ -202,6 +202,28 @@ __device__ __forceinline__ float row_max_scatter(const float (&v)[M], int l16) {
   }
 }
 
+// The same for unsigned keys.
+template <int M, int S = 0>
+__device__ __forceinline__ uint32_t row_max_scatter_u(const uint32_t (&v)[M], int l16) {
+  if constexpr (S == 4) {
+    static_assert(M == 1, "16 lanes hold at most 16 values");
+    return v[0];
+  } else if constexpr (M == 1) {
+    const uint32_t w[1] = {max(v[0], dpp_u<ScatterDpp<S>::CTRL>(v[0]))};
+    return row_max_scatter_u<1, S + 1>(w, l16);
+  } else {
+    const bool up = (l16 >> (3 - S)) & 1;
+    uint32_t h[M / 2];
+#pragma unroll
+    for (int k = 0; k < M / 2; ++k) {
+      const uint32_t keep = up ? v[M / 2 + k] : v[k];
+      const uint32_t give = up ? v[k] : v[M / 2 + k];
+      h[k] = max(keep, dpp_u<ScatterDpp<S>::CTRL>(give));
+    }
+    return row_max_scatter_u<M / 2, S + 1>(h, l16);
+  }
+}
+
 // How the query rows of a block combine into a region score: the maximum
 // (rows past n_q are set to -inf) or the mean (rows past n_q hold 0, the sum
 // is scaled by 1/n_q).  comb() folds two rows a lane holds, row() the 16 rows
@@ -518,15 +540,25 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a, const Lead& ld) 
     for (int qt = 1; qt < RT; ++qt)
       if (MEAN || 16 * qt + l16 < n_q) x = AG::comb(x, acc[qt][r]);  // absent rows: 0 from zero query rows
     if (!MEAN && l16 >= n_q) x = -INFINITY;
-    m[r] = AG::row(x);
+    m[r] = x;
   }
   const float sc = MEAN ? a.inv_sqrt_d * a.inv_nq : a.inv_sqrt_d;
   uint32_t* keys = a.keys_top + (int64_t)head * n_top;
   const int n0 = blockIdx.x * 64 + w * 16 + 4 * g;  // first region of this row
-  if (l16 == 0) {
+  if constexpr (!MEAN) {
+    // the four regions' maxima scattered over the row: region n0 + r ends in
+    // lanes l16 = 4 r .. 4 r + 3
+    const int r = l16 >> 2;
+    const float x = row_max_scatter<4>(m, l16);
+    if ((l16 & 3) == 0 && n0 + r < n_top) keys[n0 + r] = order_key(x * sc);
+  } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (n0 + r < n_top) keys[n0 + r] = order_key(m[r] * sc);
+    for (int r = 0; r < 4; ++r) m[r] = AG::row(m[r]);
+    if (l16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n0 + r < n_top) keys[n0 + r] = order_key(m[r] * sc);
+    }
   }
 }
 
@@ -682,164 +714,169 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
 // it) and the stores and the score range take one value per lane.  Level j's
 // value for block k of the wave sits in the lanes of row g with l16 >> (j < 3
 // ? j : 2) == the block's index inside the row's tiles, as worked out below.
-template <int RT, class Track, class Publish>
+template <int RT>
 __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4][RT], float* cov, float isd,
-                                                 int64_t wave_base, int lane, int g, int l16, int jmax, Track& track,
-                                                 Publish& publish, uint32_t& rmn, uint32_t& rmx) {
+                                                 uint32_t* lvl, int64_t wave_base, int lane, int g, int l16,
+                                                 int jmax) {
   const int64_t covered = a.covered;
-  // level 0: value 4 t + r (token 16 t + 4 g + r) ends in lane l16 = 4 t + r
-  {
-    float v[16];
+  // each level's score range over the wave, as order keys: the greatest in
+  // kmx, the least complemented in kmn (so that both reduce by maximum)
+  uint32_t kmn[kMaxLevels], kmx[kMaxLevels];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int j = 0; j < kMaxLevels; ++j) kmn[j] = kmx[j] = 0u;
+  auto track = [&](int j, bool in, float v) {
+    const uint32_t k = order_key(v);
+    kmx[j] = in ? k : 0u;
+    kmn[j] = in ? ~k : 0u;
+  };
+  do {  // the levels; a break skips those past the pyramid's top
+    // level 0: value 4 t + r (token 16 t + 4 g + r) ends in lane l16 = 4 t + r
+    {
+      float v[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = s[t][0][r];
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][r]);
-        v[4 * t + r] = x;
+        for (int r = 0; r < 4; ++r) {
+          float x = s[t][0][r];
+#pragma unroll
+          for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][r]);
+          v[4 * t + r] = x;
+        }
+      const float m = row_max_scatter<16>(v, l16) * isd;
+      const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
+      const bool in = p < covered;
+      if (in) cov[a.cov_off[0] + p] = m;
+      track(0, in, m);
+    }
+    if (jmax <= 1) break;
+    // level 1: token pairs (r = 0,1 and 2,3) summed in place into s[t][qt][0]
+    // and [2]; value 2 t + h ends in lanes l16 = 4 t + 2 h and 4 t + 2 h + 1
+    {
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt) {
+          s[t][qt][0] += s[t][qt][1];
+          s[t][qt][2] += s[t][qt][3];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float x = s[t][0][2 * h];
+#pragma unroll
+          for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][2 * h]);
+          v[2 * t + h] = x;
+        }
       }
-    const float m = row_max_scatter<16>(v, l16) * isd;
-    const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
-    const bool in = p < covered;
-    if (in) cov[a.cov_off[0] + p] = m;
-    rmn = 0xFFFFFFFFu;
-    rmx = 0u;
-    track(in, m);
-    publish(0);
-  }
-  if (jmax <= 1) return;
-  // level 1: token pairs (r = 0,1 and 2,3) summed in place into s[t][qt][0]
-  // and [2]; value 2 t + h ends in lanes l16 = 4 t + 2 h and 4 t + 2 h + 1
-  {
-    float v[8];
+      const float m = row_max_scatter<8>(v, l16) * (isd * 0.70710678118654752440f);
+      const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + 2 * ((l16 >> 1) & 1);  // first token of the pair
+      const bool in = p < covered;
+      if (in && (l16 & 1) == 0) cov[a.cov_off[1] + (p >> 1)] = m;
+      track(1, in, m);
+    }
+    if (jmax <= 2) break;
+    // level 2: 4-token blocks (one per lane group) into s[t][qt][0]; value t
+    // ends in lanes l16 = 4 t .. 4 t + 3
+    {
+      float v[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int qt = 0; qt < RT; ++qt) {
-        s[t][qt][0] += s[t][qt][1];
-        s[t][qt][2] += s[t][qt][3];
+        for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += s[t][qt][2];
+        float x = s[t][0][0];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+        v[t] = x;
       }
+      const float m = row_max_scatter<4>(v, l16) * (isd * 0.5f);
+      const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g;
+      const bool in = p < covered;
+      if (in && (l16 & 3) == 0) cov[a.cov_off[2] + (p >> 2)] = m;
+      track(2, in, m);
+    }
+    if (jmax <= 3) break;
+    // level 3: 8-token blocks = lane groups {0,1} and {2,3}; as level 2, with
+    // groups g and g ^ 1 holding the same values
+    {
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor16(s[t][qt][0]);
+        float x = s[t][0][0];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+        v[t] = x;
+      }
+      const float m = row_max_scatter<4>(v, l16) * (isd * 0.35355339059327376220f);
+      const int64_t p = wave_base + 16 * (l16 >> 2) + 8 * (g >> 1);
+      const bool in = p < covered;
+      if (in && (l16 & 3) == 0 && (g & 1) == 0) cov[a.cov_off[3] + (p >> 3)] = m;
+      track(3, in, m);
+    }
+    if (jmax <= 4) break;
+    // level 4: 16-token blocks = whole tiles, every lane group the same
+    {
+      float v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor32(s[t][qt][0]);
+        float x = s[t][0][0];
+#pragma unroll
+        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+        v[t] = x;
+      }
+      const float m = row_max_scatter<4>(v, l16) * (isd * 0.25f);
+      const int64_t p = wave_base + 16 * (l16 >> 2);
+      const bool in = p < covered;
+      if (in && (l16 & 3) == 0 && g == 0) cov[a.cov_off[4] + (p >> 4)] = m;
+      track(4, in, m);
+    }
+    if (jmax <= 5) break;
+    // level 5: tile pairs, value h ends in lanes l16 = 8 h .. 8 h + 7; level 6:
+    // the whole wave
+    {
+      float v[2], xall = -INFINITY;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        float x = s[t][0][2 * h];
+        float x = -INFINITY;
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][2 * h]);
-        v[2 * t + h] = x;
+        for (int qt = 0; qt < RT; ++qt) {
+          const float pair = s[2 * h][qt][0] + s[2 * h + 1][qt][0];
+          x = fmaxf(x, pair);
+        }
+        v[h] = x;
+      }
+#pragma unroll
+      for (int qt = 0; qt < RT; ++qt)
+        xall = fmaxf(xall, (s[0][qt][0] + s[1][qt][0]) + (s[2][qt][0] + s[3][qt][0]));
+      const float m = row_max_scatter<2>(v, l16) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
+      const int64_t p = wave_base + 32 * (l16 >> 3);
+      const bool in = p < covered;
+      if (in && (l16 & 7) == 0 && g == 0) cov[a.cov_off[5] + (p >> 5)] = m;
+      track(5, in, m);
+      if (jmax > 6) {
+        xall = row_max16(xall) * (isd * 0.125f);  // 2^{-3}
+        if (lane == 0) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
+        track(6, lane == 0, xall);
       }
     }
-    const float m = row_max_scatter<8>(v, l16) * (isd * 0.70710678118654752440f);
-    const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + 2 * ((l16 >> 1) & 1);  // first token of the pair
-    const bool in = p < covered;
-    if (in && (l16 & 1) == 0) cov[a.cov_off[1] + (p >> 1)] = m;
-    rmn = 0xFFFFFFFFu;
-    rmx = 0u;
-    track(in, m);
-    publish(1);
+  } while (false);
+  // the ranges of all levels in one scattered reduction: value l of the row
+  // (l < 8: level l's least key, complemented; l >= 8: level l - 8's greatest)
+  // ends in lane l16 = l, then the four rows combine
+  uint32_t w[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    w[j] = j < kMaxLevels ? kmn[j] : 0u;
+    w[8 + j] = j < kMaxLevels ? kmx[j] : 0u;
   }
-  if (jmax <= 2) return;
-  // level 2: 4-token blocks (one per lane group) into s[t][qt][0]; value t
-  // ends in lanes l16 = 4 t .. 4 t + 3
-  {
-    float v[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += s[t][qt][2];
-      float x = s[t][0][0];
-#pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
-      v[t] = x;
-    }
-    const float m = row_max_scatter<4>(v, l16) * (isd * 0.5f);
-    const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g;
-    const bool in = p < covered;
-    if (in && (l16 & 3) == 0) cov[a.cov_off[2] + (p >> 2)] = m;
-    rmn = 0xFFFFFFFFu;
-    rmx = 0u;
-    track(in, m);
-    publish(2);
-  }
-  if (jmax <= 3) return;
-  // level 3: 8-token blocks = lane groups {0,1} and {2,3}; as level 2, with
-  // groups g and g ^ 1 holding the same values
-  {
-    float v[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor16(s[t][qt][0]);
-      float x = s[t][0][0];
-#pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
-      v[t] = x;
-    }
-    const float m = row_max_scatter<4>(v, l16) * (isd * 0.35355339059327376220f);
-    const int64_t p = wave_base + 16 * (l16 >> 2) + 8 * (g >> 1);
-    const bool in = p < covered;
-    if (in && (l16 & 3) == 0 && (g & 1) == 0) cov[a.cov_off[3] + (p >> 3)] = m;
-    rmn = 0xFFFFFFFFu;
-    rmx = 0u;
-    track(in, m);
-    publish(3);
-  }
-  if (jmax <= 4) return;
-  // level 4: 16-token blocks = whole tiles, every lane group the same
-  {
-    float v[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor32(s[t][qt][0]);
-      float x = s[t][0][0];
-#pragma unroll
-      for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
-      v[t] = x;
-    }
-    const float m = row_max_scatter<4>(v, l16) * (isd * 0.25f);
-    const int64_t p = wave_base + 16 * (l16 >> 2);
-    const bool in = p < covered;
-    if (in && (l16 & 3) == 0 && g == 0) cov[a.cov_off[4] + (p >> 4)] = m;
-    rmn = 0xFFFFFFFFu;
-    rmx = 0u;
-    track(in, m);
-    publish(4);
-  }
-  if (jmax <= 5) return;
-  // level 5: tile pairs, value h ends in lanes l16 = 8 h .. 8 h + 7; level 6:
-  // the whole wave
-  {
-    float v[2], xall = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float x = -INFINITY;
-#pragma unroll
-      for (int qt = 0; qt < RT; ++qt) {
-        const float pair = s[2 * h][qt][0] + s[2 * h + 1][qt][0];
-        x = fmaxf(x, pair);
-      }
-      v[h] = x;
-    }
-#pragma unroll
-    for (int qt = 0; qt < RT; ++qt)
-      xall = fmaxf(xall, (s[0][qt][0] + s[1][qt][0]) + (s[2][qt][0] + s[3][qt][0]));
-    const float m = row_max_scatter<2>(v, l16) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
-    const int64_t p = wave_base + 32 * (l16 >> 3);
-    const bool in = p < covered;
-    if (in && (l16 & 7) == 0 && g == 0) cov[a.cov_off[5] + (p >> 5)] = m;
-    rmn = 0xFFFFFFFFu;
-    rmx = 0u;
-    track(in, m);
-    publish(5);
-    if (jmax > 6) {
-      xall = row_max16(xall) * (isd * 0.125f);  // 2^{-3}
-      if (lane == 0) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
-      rmn = 0xFFFFFFFFu;
-      rmx = 0u;
-      track(lane == 0, xall);
-      publish(6);
-    }
-  }
+  uint32_t r = row_max_scatter_u<16>(w, l16);
+  r = max(r, lane_xor16(r));
+  r = max(r, lane_xor32(r));
+  const int j = lane & 7;
+  if (lane < 16 && j < jmax) lvl[2 * j + (lane >> 3)] = lane < 8 ? ~r : r;
 }
 
 // ---------------------------------------------------------------------------
@@ -921,7 +958,7 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
   const float isd_raw = a.inv_sqrt_d;
   if constexpr (!MEAN) {
     if (!soft) {  // uniform
-      cover_levels_max<RT>(a, s, cov, isd, wave_base, lane, g, l16, jmax, track, publish, rmn, rmx);
+      cover_levels_max<RT>(a, s, cov, isd, lvl, wave_base, lane, g, l16, jmax);
       return;
     }
   }
