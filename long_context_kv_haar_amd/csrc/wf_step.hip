@@ -1295,22 +1295,29 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
         x[r][j][1] = p.y;
       }
     }
+    // all levels' least keys (complemented) and greatest keys in one
+    // scattered reduction: value l (l < 8: level l's least, l >= 8: level
+    // l - 8's greatest) ends in lane l16 = l of every row, then the rows combine
+    uint32_t w[16];
 #pragma unroll
-    for (int j = 0; j < kMaxLevels; ++j) {
-      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int j = 0; j < 8; ++j) {
+      uint32_t mn = 0u, mx = 0u;
+      if (j < kMaxLevels) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint32_t off = (uint32_t)((nwav - 1 - (lane + 64 * r)) >> 31);  // ~0u past the last wave
-        mn = min(mn, x[r][j][0] | off);
-        mx = max(mx, x[r][j][1] & ~off);
+        for (int r = 0; r < 2; ++r) {
+          const uint32_t off = (uint32_t)((nwav - 1 - (lane + 64 * r)) >> 31);  // ~0u past the last wave
+          mn = max(mn, ~(x[r][j][0] | off));
+          mx = max(mx, x[r][j][1] & ~off);
+        }
       }
-      mn = wave_min_u32(mn);
-      mx = wave_max_u32(mx);
-      if (lane == 0) {
-        sh.rmn[j] = mn;
-        sh.rmx[j] = mx;
-      }
+      w[j] = mn;
+      w[8 + j] = mx;
     }
+    uint32_t q = row_max_scatter_u<16>(w, lane & 15);
+    q = max(q, lane_xor16(q));
+    q = max(q, lane_xor32(q));
+    if (lane < kMaxLevels) sh.rmn[lane] = ~q;
+    else if (lane >= 8 && lane < 8 + kMaxLevels) sh.rmx[lane - 8] = q;
   }
   // the kept coarse regions into LDS (more than one per thread only when k_L > NT)
   if (t < rl.k_top) sel_l[t] = clampi(sel0, 0, rl.n_top - 1);
