@@ -181,14 +181,17 @@ template <> struct ScatterDpp<0> { static constexpr int CTRL = 0x140; };  // row
 template <> struct ScatterDpp<1> { static constexpr int CTRL = 0x141; };  // row_half_mirror
 template <> struct ScatterDpp<2> { static constexpr int CTRL = 0x4E; };   // quad_perm [2,3,0,1]
 template <> struct ScatterDpp<3> { static constexpr int CTRL = 0xB1; };   // quad_perm [1,0,3,2]
-template <int M, int S = 0>
-__device__ __forceinline__ float row_max_scatter(const float (&v)[M], int l16) {
+// SUM: the sum over the row instead of the maximum (in another order than a
+// per-value reduction, so it may differ from one in the last bit).
+template <bool SUM, int M, int S = 0>
+__device__ __forceinline__ float row_scatter(const float (&v)[M], int l16) {
   if constexpr (S == 4) {
     static_assert(M == 1, "16 lanes hold at most 16 values");
     return v[0];
   } else if constexpr (M == 1) {
-    const float w[1] = {fmaxf(v[0], dpp_f<ScatterDpp<S>::CTRL>(v[0]))};
-    return row_max_scatter<1, S + 1>(w, l16);
+    const float o = dpp_f<ScatterDpp<S>::CTRL>(v[0]);
+    const float w[1] = {SUM ? v[0] + o : fmaxf(v[0], o)};
+    return row_scatter<SUM, 1, S + 1>(w, l16);
   } else {
     const bool up = (l16 >> (3 - S)) & 1;
     float h[M / 2];
@@ -196,10 +199,15 @@ __device__ __forceinline__ float row_max_scatter(const float (&v)[M], int l16) {
     for (int k = 0; k < M / 2; ++k) {
       const float keep = up ? v[M / 2 + k] : v[k];
       const float give = up ? v[k] : v[M / 2 + k];
-      h[k] = fmaxf(keep, dpp_f<ScatterDpp<S>::CTRL>(give));
+      const float o = dpp_f<ScatterDpp<S>::CTRL>(give);
+      h[k] = SUM ? keep + o : fmaxf(keep, o);
     }
-    return row_max_scatter<M / 2, S + 1>(h, l16);
+    return row_scatter<SUM, M / 2, S + 1>(h, l16);
   }
+}
+template <int M>
+__device__ __forceinline__ float row_max_scatter(const float (&v)[M], int l16) {
+  return row_scatter<false, M>(v, l16);
 }
 
 // The same for unsigned keys.
@@ -545,21 +553,11 @@ __device__ __forceinline__ void coarse_stage(const StepArgs& a, const Lead& ld) 
   const float sc = MEAN ? a.inv_sqrt_d * a.inv_nq : a.inv_sqrt_d;
   uint32_t* keys = a.keys_top + (int64_t)head * n_top;
   const int n0 = blockIdx.x * 64 + w * 16 + 4 * g;  // first region of this row
-  if constexpr (!MEAN) {
-    // the four regions' maxima scattered over the row: region n0 + r ends in
-    // lanes l16 = 4 r .. 4 r + 3
-    const int r = l16 >> 2;
-    const float x = row_max_scatter<4>(m, l16);
-    if ((l16 & 3) == 0 && n0 + r < n_top) keys[n0 + r] = order_key(x * sc);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = AG::row(m[r]);
-    if (l16 == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n0 + r < n_top) keys[n0 + r] = order_key(m[r] * sc);
-    }
-  }
+  // the four regions' row maxima (or sums) scattered over the row: region
+  // n0 + r ends in lanes l16 = 4 r .. 4 r + 3
+  const int r = l16 >> 2;
+  const float x = row_scatter<MEAN, 4>(m, l16);
+  if ((l16 & 3) == 0 && n0 + r < n_top) keys[n0 + r] = order_key(x * sc);
 }
 
 template <typename T, int D, int RT, bool ONE>
@@ -706,18 +704,17 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
   }
 }
 
-// The Haar coverage scores of one wave with the maximum over the query rows
-// (cover_haar below sets up s, the per-query token logits of the wave's four
-// tiles): each level sums its blocks in registers or across lane groups, then
-// takes the maximum over the 16 query rows of every block with one scattered
-// row reduction, so that every lane ends with one block's score (or a copy of
+// The Haar coverage scores of one wave with the maximum (or the mean) over
+// the query rows (cover_haar below sets up s, the per-query token logits of
+// the wave's four tiles): each level sums its blocks in registers or across
+// lane groups, then combines the 16 query rows of every block with one
+// scattered row reduction, so that every lane ends with one block's score (or a copy of
 // it) and the stores and the score range take one value per lane.  Level j's
 // value for block k of the wave sits in the lanes of row g with l16 >> (j < 3
 // ? j : 2) == the block's index inside the row's tiles, as worked out below.
-template <int RT>
-__device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4][RT], float* cov, float isd,
-                                                 uint32_t* lvl, int64_t wave_base, int lane, int g, int l16,
-                                                 int jmax) {
+template <bool MEAN, int RT>
+__device__ __forceinline__ void cover_levels(const StepArgs& a, f32x4 (&s)[4][RT], float* cov, float isd,
+                                             uint32_t* lvl, int64_t wave_base, int lane, int g, int l16, int jmax) {
   const int64_t covered = a.covered;
   // each level's score range over the wave, as order keys: the greatest in
   // kmx, the least complemented in kmn (so that both reduce by maximum)
@@ -739,10 +736,10 @@ __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4
         for (int r = 0; r < 4; ++r) {
           float x = s[t][0][r];
 #pragma unroll
-          for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][r]);
+          for (int qt = 1; qt < RT; ++qt) x = MEAN ? x + s[t][qt][r] : fmaxf(x, s[t][qt][r]);
           v[4 * t + r] = x;
         }
-      const float m = row_max_scatter<16>(v, l16) * isd;
+      const float m = row_scatter<MEAN, 16>(v, l16) * isd;
       const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + (l16 & 3);
       const bool in = p < covered;
       if (in) cov[a.cov_off[0] + p] = m;
@@ -764,11 +761,11 @@ __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4
         for (int h = 0; h < 2; ++h) {
           float x = s[t][0][2 * h];
 #pragma unroll
-          for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][2 * h]);
+          for (int qt = 1; qt < RT; ++qt) x = MEAN ? x + s[t][qt][2 * h] : fmaxf(x, s[t][qt][2 * h]);
           v[2 * t + h] = x;
         }
       }
-      const float m = row_max_scatter<8>(v, l16) * (isd * 0.70710678118654752440f);
+      const float m = row_scatter<MEAN, 8>(v, l16) * (isd * 0.70710678118654752440f);
       const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g + 2 * ((l16 >> 1) & 1);  // first token of the pair
       const bool in = p < covered;
       if (in && (l16 & 1) == 0) cov[a.cov_off[1] + (p >> 1)] = m;
@@ -785,10 +782,10 @@ __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4
         for (int qt = 0; qt < RT; ++qt) s[t][qt][0] += s[t][qt][2];
         float x = s[t][0][0];
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+        for (int qt = 1; qt < RT; ++qt) x = MEAN ? x + s[t][qt][0] : fmaxf(x, s[t][qt][0]);
         v[t] = x;
       }
-      const float m = row_max_scatter<4>(v, l16) * (isd * 0.5f);
+      const float m = row_scatter<MEAN, 4>(v, l16) * (isd * 0.5f);
       const int64_t p = wave_base + 16 * (l16 >> 2) + 4 * g;
       const bool in = p < covered;
       if (in && (l16 & 3) == 0) cov[a.cov_off[2] + (p >> 2)] = m;
@@ -805,10 +802,10 @@ __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4
         for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor16(s[t][qt][0]);
         float x = s[t][0][0];
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+        for (int qt = 1; qt < RT; ++qt) x = MEAN ? x + s[t][qt][0] : fmaxf(x, s[t][qt][0]);
         v[t] = x;
       }
-      const float m = row_max_scatter<4>(v, l16) * (isd * 0.35355339059327376220f);
+      const float m = row_scatter<MEAN, 4>(v, l16) * (isd * 0.35355339059327376220f);
       const int64_t p = wave_base + 16 * (l16 >> 2) + 8 * (g >> 1);
       const bool in = p < covered;
       if (in && (l16 & 3) == 0 && (g & 1) == 0) cov[a.cov_off[3] + (p >> 3)] = m;
@@ -824,10 +821,10 @@ __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4
         for (int qt = 0; qt < RT; ++qt) s[t][qt][0] = sum_xor32(s[t][qt][0]);
         float x = s[t][0][0];
 #pragma unroll
-        for (int qt = 1; qt < RT; ++qt) x = fmaxf(x, s[t][qt][0]);
+        for (int qt = 1; qt < RT; ++qt) x = MEAN ? x + s[t][qt][0] : fmaxf(x, s[t][qt][0]);
         v[t] = x;
       }
-      const float m = row_max_scatter<4>(v, l16) * (isd * 0.25f);
+      const float m = row_scatter<MEAN, 4>(v, l16) * (isd * 0.25f);
       const int64_t p = wave_base + 16 * (l16 >> 2);
       const bool in = p < covered;
       if (in && (l16 & 3) == 0 && g == 0) cov[a.cov_off[4] + (p >> 4)] = m;
@@ -837,27 +834,31 @@ __device__ __forceinline__ void cover_levels_max(const StepArgs& a, f32x4 (&s)[4
     // level 5: tile pairs, value h ends in lanes l16 = 8 h .. 8 h + 7; level 6:
     // the whole wave
     {
-      float v[2], xall = -INFINITY;
+      float v[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        float x = -INFINITY;
+        float x = s[2 * h][0][0] + s[2 * h + 1][0][0];
 #pragma unroll
-        for (int qt = 0; qt < RT; ++qt) {
+        for (int qt = 1; qt < RT; ++qt) {
           const float pair = s[2 * h][qt][0] + s[2 * h + 1][qt][0];
-          x = fmaxf(x, pair);
+          x = MEAN ? x + pair : fmaxf(x, pair);
         }
         v[h] = x;
       }
+      float xall = (s[0][0][0] + s[1][0][0]) + (s[2][0][0] + s[3][0][0]);
 #pragma unroll
-      for (int qt = 0; qt < RT; ++qt)
-        xall = fmaxf(xall, (s[0][qt][0] + s[1][qt][0]) + (s[2][qt][0] + s[3][qt][0]));
-      const float m = row_max_scatter<2>(v, l16) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
+      for (int qt = 1; qt < RT; ++qt) {
+        const float all = (s[0][qt][0] + s[1][qt][0]) + (s[2][qt][0] + s[3][qt][0]);
+        xall = MEAN ? xall + all : fmaxf(xall, all);
+      }
+      const float m = row_scatter<MEAN, 2>(v, l16) * (isd * 0.17677669529663688110f);  // 2^{-5/2}
       const int64_t p = wave_base + 32 * (l16 >> 3);
       const bool in = p < covered;
       if (in && (l16 & 7) == 0 && g == 0) cov[a.cov_off[5] + (p >> 5)] = m;
       track(5, in, m);
       if (jmax > 6) {
-        xall = row_max16(xall) * (isd * 0.125f);  // 2^{-3}
+        const float xw[1] = {xall};
+        xall = row_scatter<MEAN, 1>(xw, l16) * (isd * 0.125f);  // 2^{-3}
         if (lane == 0) cov[a.cov_off[6] + (wave_base >> 6)] = xall;
         track(6, lane == 0, xall);
       }
@@ -956,11 +957,9 @@ __device__ __forceinline__ void cover_haar(const StepArgs& a, int head, const in
     return lgh + (int64_t)a.n_q * a.cov_off[j] + (int64_t)query * ((((a.covered >> j) + 3) >> 2) << 2);
   };
   const float isd_raw = a.inv_sqrt_d;
-  if constexpr (!MEAN) {
-    if (!soft) {  // uniform
-      cover_levels_max<RT>(a, s, cov, isd, lvl, wave_base, lane, g, l16, jmax);
-      return;
-    }
+  if (!soft) {  // uniform
+    cover_levels<MEAN, RT>(a, s, cov, isd, lvl, wave_base, lane, g, l16, jmax);
+    return;
   }
   // level 0
   rmn = 0xFFFFFFFFu;
