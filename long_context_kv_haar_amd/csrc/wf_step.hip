@@ -674,9 +674,11 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
 #pragma unroll
           for (int u = 0; u < 2; ++u) f32_rows_mma<T, D, RT>(xr[u], qf, acc[u]);
         }
+        // the pair's eight positions (4 u + r) in one scattered row reduction:
+        // position 16 (2 tp + u) + 4 g + r ends in lanes l16 = 2 (4 u + r), + 1
+        float v[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int64_t p0 = wave_base + 16 * (2 * tp + u);
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             float x = acc[u][0][r];
@@ -684,15 +686,16 @@ __device__ __forceinline__ void cover_from_bands(const StepArgs& a, int head, co
             for (int qt = 1; qt < RT; ++qt)
               if (MEAN || 16 * qt + l16 < a.n_q) x = AG::comb(x, acc[u][qt][r]);
             if (!MEAN && l16 >= a.n_q) x = -INFINITY;
-            const float m = AG::row(x) * sc;
-            const int64_t pr = p0 + 4 * g + r;
-            const bool in = (l16 == 0) && pr < nj;
-            if (in) cov[a.cov_off[j] + pr] = m;
-            const uint32_t k = order_key(m);
-            rmn = in ? min(rmn, k) : rmn;
-            rmx = in ? max(rmx, k) : rmx;
+            v[4 * u + r] = x;
           }
-        }
+        const float m = row_scatter<MEAN, 8>(v, l16) * sc;
+        const int e = l16 >> 1, u = e >> 2, r = e & 3;
+        const int64_t pr = wave_base + 16 * (2 * tp + u) + 4 * g + r;
+        const bool in = pr < nj;
+        if (in && (l16 & 1) == 0) cov[a.cov_off[j] + pr] = m;
+        const uint32_t k = order_key(m);
+        rmn = in ? min(rmn, k) : rmn;
+        rmx = in ? max(rmx, k) : rmx;
       }
     }
     rmn = wave_min_u32(rmn);
