@@ -91,25 +91,25 @@ __device__ __forceinline__ void sel_init(SelShared<NT>& sh) {
 // float operations, so it never inverts an order.  A degenerate range puts
 // everything in bin 0.
 struct LinBins {
-  float scale, off;
-  bool ok;
+  float scale, off;  // both zero when the range is empty or not finite: every score then takes bin 0
   __device__ __forceinline__ LinBins(float smin, float smax) {
     const float span = smax - smin;
-    scale = __fdividef((float)kSelBins, span);
-    ok = span > 0.f && span < 3.0e38f && scale > 0.f && scale < 3.0e38f;
-    off = -smin * scale;
+    const float sc = (float)kSelBins * __builtin_amdgcn_rcpf(span);  // any monotone map will do: no exact division
+    const bool ok = span > 0.f && span < 3.0e38f && sc > 0.f && sc < 3.0e38f;
+    scale = ok ? sc : 0.f;
+    off = ok ? -smin * sc : 0.f;
   }
   __device__ __forceinline__ int operator()(float s) const {
-    return ok ? min(kSelBins - 1, max(0, (int)fmaf(s, scale, off))) : 0;
+    return min(kSelBins - 1, max(0, (int)fmaf(s, scale, off)));
   }
   // kSelBins sub-bins over bin b's range: another monotone map of the score
   // (it orders only the candidates of bin b, so it need not match the bin
   // edges exactly)
   __device__ __forceinline__ LinBins sub(int b) const {
     LinBins r = *this;
-    r.scale = scale * (float)kSelBins;
-    r.off = (off - (float)b) * (float)kSelBins;
-    r.ok = ok && r.scale < 3.0e38f;
+    const bool ok = scale * (float)kSelBins < 3.0e38f;
+    r.scale = ok ? scale * (float)kSelBins : 0.f;
+    r.off = ok ? (off - (float)b) * (float)kSelBins : 0.f;
     return r;
   }
 };
@@ -126,21 +126,29 @@ __device__ __forceinline__ void find_bin(const int* hist, int want, int& b, int&
   static_assert(kSelBins == 256, "four bins per lane");
   const int lane = threadIdx.x & 63;
   const int4 x = reinterpret_cast<const int4*>(hist)[lane];
-  const int c[4] = {x.x, x.y, x.z, x.w};
-  const int tot = c[0] + c[1] + c[2] + c[3];
-  int all;
-  const int incl = wave_incl_scan(tot, &all);
-  const int above = all - incl;  // entries in the bins of higher lanes
+  const int tot = x.x + x.y + x.z + x.w;
+  // inclusive prefix of the lane totals: within each row of 16 lanes, then
+  // the rows' totals carried to the rows above them by row broadcasts
+  int s = tot;
+  s += dpp_or0<0x111>(s);  // row_shr:1
+  s += dpp_or0<0x112>(s);  // row_shr:2
+  s += dpp_or0<0x114>(s);  // row_shr:4
+  s += dpp_or0<0x118>(s);  // row_shr:8
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
+  const int above = __builtin_amdgcn_readlane(s, 63) - s;  // entries in the bins of higher lanes
   const uint64_t om = __ballot((above < want) & (want <= above + tot));
   const int owner = om ? (int)__ffsll((unsigned long long)om) - 1 : 0;
   // the owner's bins, highest first: suffix counts within the lane
-  const int a3 = above, a2 = a3 + c[3], a1 = a2 + c[2], a0 = a1 + c[1];
-  const int bb = (want <= a2) ? 3 : (want <= a1) ? 2 : (want <= a0) ? 1 : 0;
-  const int ab = bb == 3 ? a3 : bb == 2 ? a2 : bb == 1 ? a1 : a0;
-  const int ct = bb == 3 ? c[3] : bb == 2 ? c[2] : bb == 1 ? c[1] : c[0];
-  b = 4 * owner + __builtin_amdgcn_readlane(bb, owner);
+  const int a2 = above + x.w, a1 = a2 + x.z, a0 = a1 + x.y;
+  const bool h3 = want <= a2, h2 = want <= a1, h1 = want <= a0;
+  const int ab = h3 ? above : h2 ? a2 : h1 ? a1 : a0;
+  const int ct = h3 ? x.w : h2 ? x.z : h1 ? x.y : x.x;
+  const int bb = h3 ? 3 : h2 ? 2 : h1 ? 1 : 0;
+  const uint32_t pk = __builtin_amdgcn_readlane((uint32_t)ct << 2 | (uint32_t)bb, owner);
+  b = 4 * owner + (int)(pk & 3u);
   need = want - __builtin_amdgcn_readlane(ab, owner);
-  cnt = __builtin_amdgcn_readlane(ct, owner);
+  cnt = (int)(pk >> 2);
 }
 
 // Exclusive prefix over the workgroup of one int per thread, in thread
