@@ -63,7 +63,7 @@ template <int NT> struct SelShared {
   int list_n[2];
   uint32_t wmn[NW], wmx[NW];
   int wsum[8][NW];                // per-wave totals of the workgroup scans
-  uint32_t rmn[8], rmx[8];        // the refinement: each level's score range (order keys)
+  float rsc[8], rof[8];           // the refinement: each level's bins over its score range (LinBins)
   int bc[4];                      // a level's boundary bin, broadcast by wave 0
   uint64_t tau;                   // a level's threshold pair, broadcast by wave 0
   // the refinement's per-call values, staged before its first barrier
@@ -92,6 +92,7 @@ __device__ __forceinline__ void sel_init(SelShared<NT>& sh) {
 // everything in bin 0.
 struct LinBins {
   float scale, off;  // both zero when the range is empty or not finite: every score then takes bin 0
+  __device__ __forceinline__ LinBins(float scale_, float off_, bool) : scale(scale_), off(off_) {}
   __device__ __forceinline__ LinBins(float smin, float smax) {
     const float span = smax - smin;
     const float sc = (float)kSelBins * __builtin_amdgcn_rcpf(span);  // any monotone map will do: no exact division
@@ -183,10 +184,9 @@ __device__ __forceinline__ int block_excl_scan(int x, SelShared<NT>& sh, int r, 
 // All threads of the workgroup call it with the same k, smin, smax.
 template <int NT, int S>
 __device__ __forceinline__ uint32_t select_level(const float (&sc)[S], uint32_t valid, uint32_t owned, int pos0, int k,
-                                                 float smin, float smax, SelShared<NT>& sh, SelCursor& cur) {
+                                                 const LinBins bin, SelShared<NT>& sh, SelCursor& cur) {
   const int t = threadIdx.x, lane = t & 63;
   const int trash = kSelBins + lane;  // this lane's bin for slots that do not count
-  const LinBins bin(smin, smax);
   int* hist = sh.hist[cur.hb];
   // 1. histogram of the owned candidates (no branch per slot)
 #pragma unroll
@@ -357,6 +357,13 @@ __device__ __forceinline__ uint32_t select_level(const float (&sc)[S], uint32_t 
   cur.hb = (cur.hb + 1) % 3;
   cur.lb ^= 1;
   return kept;
+}
+
+// The same with the bins built here from the score range.
+template <int NT, int S>
+__device__ __forceinline__ uint32_t select_level(const float (&sc)[S], uint32_t valid, uint32_t owned, int pos0, int k,
+                                                 float smin, float smax, SelShared<NT>& sh, SelCursor& cur) {
+  return select_level<NT, S>(sc, valid, owned, pos0, k, LinBins(smin, smax), sh, cur);
 }
 
 }  // namespace wf

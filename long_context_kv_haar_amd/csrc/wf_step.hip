@@ -1227,7 +1227,7 @@ __device__ __forceinline__ uint32_t refine_level(const StepArgs& a, const Refine
   const uint32_t owned = own ? valid : 0u;
   const int kj = sh.bud[L - j];
   const uint32_t kept =
-      select_level<NT, P>(sc, valid, owned, p0, kj, key_to_f32(sh.rmn[j]), key_to_f32(sh.rmx[j]), sh, cur);
+      select_level<NT, P>(sc, valid, owned, p0, kj, LinBins(sh.rsc[j], sh.rof[j], true), sh, cur);
   int32_t* dbg_sel = sh.dsel;
   float* dbg_score = sh.dscore;
   if (dbg_sel || dbg_score) {  // uniform: level j's kept regions, ascending, with their scores
@@ -1280,7 +1280,8 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
   const int32_t* sel_g = rl.sel_top + (int64_t)head * rl.k_top;
   const int sel0 = sel_g[min(t, rl.k_top - 1)];
   // each level's score range: the cover waves' slots (at most 128 per head
-  // here, lanes l and l + 64 of wave 0), published to LDS.  Loads are
+  // here, lanes l and l + 64 of wave 0), reduced by wave 0, which publishes
+  // the level's bins to LDS.  Loads are
   // unconditional, from clamped slots; slots past the last wave take the
   // neutral range by an all-ones mask.
   const int nwav = (covered + 63) >> 6;
@@ -1318,8 +1319,14 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
     uint32_t q = row_max_scatter_u<16>(w, lane & 15);
     q = max(q, lane_xor16(q));
     q = max(q, lane_xor32(q));
-    if (lane < kMaxLevels) sh.rmn[lane] = ~q;
-    else if (lane >= 8 && lane < 8 + kMaxLevels) sh.rmx[lane - 8] = q;
+    // lane j < 7 takes level j's greatest key from lane j + 8 (row_ror:8) and
+    // publishes the level's bins, built once here rather than in every wave
+    const uint32_t qx = dpp_u<0x128>(q);
+    const LinBins bin(key_to_f32(~q), key_to_f32(qx));
+    if (lane < kMaxLevels) {
+      sh.rsc[lane] = bin.scale;
+      sh.rof[lane] = bin.off;
+    }
   }
   // the kept coarse regions into LDS (more than one per thread only when k_L > NT)
   if (t < rl.k_top) sel_l[t] = clampi(sel0, 0, rl.n_top - 1);
