@@ -1211,10 +1211,16 @@ static_assert(kMaxLevels == 7, "the refinement holds seven levels");
 // candidates are the held positions whose parent was kept (keptp, the
 // parent level's slots); returns the kept mask over the P slots and, with
 // the per-level sinks, writes the level's kept regions at off.
+// A level's bins and budget k_j, read from LDS one level ahead.
+struct LevelPar {
+  float scale, off;
+  int k;
+};
+
 template <int NT, int S0, int P>
 __device__ __forceinline__ uint32_t refine_level(const StepArgs& a, const RefineLead& rl, int head, HeldScores<S0>& hs,
-                                                 int j, uint32_t keptp, const int* sel_l, SelShared<NT>& sh,
-                                                 SelCursor& cur, int off) {
+                                                 int j, const LevelPar& lp, uint32_t keptp, const int* sel_l,
+                                                 SelShared<NT>& sh, SelCursor& cur, int off) {
   const int t = threadIdx.x;
   const int L = rl.levels;
   float sc[P];
@@ -1225,9 +1231,8 @@ __device__ __forceinline__ uint32_t refine_level(const StepArgs& a, const Refine
 #pragma unroll
   for (int i = 0; i < P; ++i) valid |= ((p0 + i < nj) & ((keptp >> (i >> 1)) & 1u)) ? (1u << i) : 0u;
   const uint32_t owned = own ? valid : 0u;
-  const int kj = sh.bud[L - j];
-  const uint32_t kept =
-      select_level<NT, P>(sc, valid, owned, p0, kj, LinBins(sh.rsc[j], sh.rof[j], true), sh, cur);
+  const int kj = lp.k;
+  const uint32_t kept = select_level<NT, P>(sc, valid, owned, p0, kj, LinBins(lp.scale, lp.off, true), sh, cur);
   int32_t* dbg_sel = sh.dsel;
   float* dbg_score = sh.dscore;
   if (dbg_sel || dbg_score) {  // uniform: level j's kept regions, ascending, with their scores
@@ -1355,24 +1360,28 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
   }
   int off = rl.k_top;
   SelCursor cur;
+  LevelPar nxt{sh.rsc[L - 1], sh.rof[L - 1], sh.bud[1]};
   for (int j = L - 1; j >= 0; --j) {  // each level on its own count of held slots
+    const LevelPar lp = nxt;
+    const int jn = j > 0 ? j - 1 : 0;
+    nxt = LevelPar{sh.rsc[jn], sh.rof[jn], sh.bud[L - jn]};  // the next level's, requested before this level waits
     const int pj = (S0 >> j) > 0 ? (S0 >> j) : 1;
     uint32_t kept;
     if (pj == 1) {
-      kept = refine_level<NT, S0, 1>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
+      kept = refine_level<NT, S0, 1>(a, rl, head, hs, j, lp, keptp, sel_l, sh, cur, off);
     } else if constexpr (S0 >= 2) {
       if (pj == 2) {
-        kept = refine_level<NT, S0, 2>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
+        kept = refine_level<NT, S0, 2>(a, rl, head, hs, j, lp, keptp, sel_l, sh, cur, off);
       } else if constexpr (S0 >= 4) {
-        if (pj == 4) kept = refine_level<NT, S0, 4>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
-        else kept = refine_level<NT, S0, S0>(a, rl, head, hs, j, keptp, sel_l, sh, cur, off);
+        if (pj == 4) kept = refine_level<NT, S0, 4>(a, rl, head, hs, j, lp, keptp, sel_l, sh, cur, off);
+        else kept = refine_level<NT, S0, S0>(a, rl, head, hs, j, lp, keptp, sel_l, sh, cur, off);
       } else {
         kept = 0u;  // not reached: pj <= S0
       }
     } else {
       kept = 0u;  // not reached: pj <= S0
     }
-    off += sh.bud[L - j];
+    off += lp.k;
     keptp = kept;
   }
 
@@ -2103,11 +2112,9 @@ template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(WF_LEAD_PARAMS, StepArgs a) {
   constexpr int C4 = D / 4;
   const CombineLead cl = CombineLead::of(WF_LEAD);
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_head = (int64_t)cl.n_q * C4;
-  if (idx >= per_head * cl.heads_total) return;
-  const int head = (int)(idx / per_head);
-  const int rem = (int)(idx - head * per_head);
+  const int head = blockIdx.y;  // the grid's rows are the heads: no division by a run-time size
+  const int rem = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (rem >= cl.n_q * C4) return;
   const int query = rem / C4, c4 = rem - query * C4;
   const int ns = cl.n_split;
   float mv[kMaxSplit], lv[kMaxSplit];
@@ -2406,10 +2413,10 @@ hipError_t launch_select_attend(const SelectLaunch& L, hipStream_t s) {
   e = bf ? (d128 ? launch_rt_attend<bf16_t, 128>(rt, a, L, s) : launch_rt_attend<bf16_t, 64>(rt, a, L, s))
          : (d128 ? launch_rt_attend<float, 128>(rt, a, L, s) : launch_rt_attend<float, 64>(rt, a, L, s));
   if (e != hipSuccess) return e;
-  const unsigned comb_blocks = (unsigned)(((int64_t)P.heads_total * P.n_q * (P.head_dim / 4) + 255) / 256);
+  const dim3 comb_grid((unsigned)((P.n_q * (P.head_dim / 4) + 255) / 256), (unsigned)P.heads_total);
   const Lead ld = combine_lead(a).lead();
-  return d128 ? launch_lead(combine_kernel<128>, dim3(comb_blocks), dim3(256), 0, s, ld, a)
-              : launch_lead(combine_kernel<64>, dim3(comb_blocks), dim3(256), 0, s, ld, a);
+  return d128 ? launch_lead(combine_kernel<128>, comb_grid, dim3(256), 0, s, ld, a)
+              : launch_lead(combine_kernel<64>, comb_grid, dim3(256), 0, s, ld, a);
 }
 #endif
 
