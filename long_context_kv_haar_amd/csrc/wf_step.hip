@@ -2132,6 +2132,11 @@ __global__ __launch_bounds__(256) void combine_kernel(WF_LEAD_PARAMS, StepArgs a
       ov[sp] = *reinterpret_cast<const float4*>(cl.part_o + row * D + 4 * c4);
     }
   }
+  // the head's output rows, read from the arguments while the loads above are
+  // in flight (read after them, the argument read would wait a trip of its own)
+  const HeadRef hr = head_ref(a, head);
+  float* const ob = a.out[hr.item] + (int64_t)hr.local * a.n_q * D;
+  asm volatile("" ::"s"(ob));
   float mm = -INFINITY;
 #pragma unroll
   for (int sp = 0; sp < kMaxSplit; ++sp) mm = fmaxf(mm, mv[sp]);
@@ -2147,9 +2152,7 @@ __global__ __launch_bounds__(256) void combine_kernel(WF_LEAD_PARAMS, StepArgs a
     acc.w += wv * ov[sp].w;
   }
   const float inv = 1.0f / den;
-  const HeadRef hr = head_ref(a, head);
-  *reinterpret_cast<float4*>(a.out[hr.item] + (hr.local * a.n_q + query) * D + 4 * c4) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  *reinterpret_cast<float4*>(ob + query * D + 4 * c4) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 #endif
 
