@@ -1206,17 +1206,17 @@ template <int S0> struct HeldScores {
 };
 static_assert(kMaxLevels == 7, "the refinement holds seven levels");
 
-// One refinement level over the P = max(1, S0 >> j) slots a thread holds at
-// level j (the per-slot work of the level scales with P, not with S0):
-// candidates are the held positions whose parent was kept (keptp, the
-// parent level's slots); returns the kept mask over the P slots and, with
-// the per-level sinks, writes the level's kept regions at off.
 // A level's bins and budget k_j, read from LDS one level ahead.
 struct LevelPar {
   float scale, off;
   int k;
 };
 
+// One refinement level over the P = max(1, S0 >> j) slots a thread holds at
+// level j (the per-slot work of the level scales with P, not with S0):
+// candidates are the held positions whose parent was kept (keptp, the
+// parent level's slots); returns the kept mask over the P slots and, with
+// the per-level sinks, writes the level's kept regions at off.
 template <int NT, int S0, int P>
 __device__ __forceinline__ uint32_t refine_level(const StepArgs& a, const RefineLead& rl, int head, HeldScores<S0>& hs,
                                                  int j, const LevelPar& lp, uint32_t keptp, const int* sel_l,
