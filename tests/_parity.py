@@ -16,8 +16,17 @@ PIN_GAP = 1e-3          # a level is compared bit for bit when the oracle's gap 
 TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 
+# pytest's capture manager (set by conftest): progress lines of the long GPU
+# tests then reach the terminal or log as they happen, not when the test ends
+_capman = None
+
+
 def say(*a):
-    print(*a, flush=True)
+    if _capman is not None:
+        with _capman.global_and_fixture_disabled():
+            print(*a, flush=True)
+    else:
+        print(*a, flush=True)
     sys.stdout.flush()
 
 

@@ -26,6 +26,13 @@ def pytest_generate_tests(metafunc):
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    # the GPU tests' progress lines bypass output capture (a long test then
+    # never looks silent to a watchdog on its output)
+    here = os.path.dirname(os.path.abspath(__file__))
+    if here not in sys.path:
+        sys.path.insert(0, here)
+    import _parity
+    _parity._capman = config.pluginmanager.getplugin("capturemanager")
 
 
 def pytest_collection_modifyitems(config, items):
