@@ -1267,42 +1267,47 @@ __device__ __forceinline__ void refine_sel(const StepArgs& a, const RefineLead& 
   for (int j = 0; j < kMaxLevels; ++j) coff[j + 1] = coff[j] + (((covered >> j) + 3) & ~3);
   // Every load of the stage is requested before any is waited for, so the
   // coverage scores, the level ranges and the kept coarse regions arrive in
-  // one round trip.  First every live level's scores into registers
-  // (clamped positions; slots past a level's end are never valid).
-  HeldScores<S0> hs;
-#define WF_LOAD_LEVEL(J)                                                              \
-  if (J < L) hs.template load<J>(cov + coff[J], covered >> J, (t * S0) >> J);         \
-  else hs.template clear<J>();
-  WF_LOAD_LEVEL(0)
-  WF_LOAD_LEVEL(1)
-  WF_LOAD_LEVEL(2)
-  WF_LOAD_LEVEL(3)
-  WF_LOAD_LEVEL(4)
-  WF_LOAD_LEVEL(5)
-  WF_LOAD_LEVEL(6)
-#undef WF_LOAD_LEVEL
+  // one round trip.  Each level's score range: the cover waves' slots (at most 128 per head
+  // here, lanes l and l + 64 of wave 0), reduced by wave 0, which publishes
+  // the level's bins to LDS.  Loads are unconditional, from clamped slots;
+  // slots past the last wave take the neutral range by an all-ones mask.
+  // They are requested first, then the kept coarse regions, then the scores
+  // (coarsest level first), so that wave 0's reduction and the first barrier
+  // wait only for the first two while the finer levels' scores still arrive.
+  const int nwav = (covered + 63) >> 6;
+  const uint32_t* lm = rl.lvl + (int64_t)head * nwav * 2 * kMaxLevels;
+  // (every wave requests them, so that no branch separates them from the
+  // loads below; only wave 0 reads them)
+  uint32_t x[2][kMaxLevels][2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int v = min(lane + 64 * r, nwav - 1);
+#pragma unroll
+    for (int j = 0; j < kMaxLevels; ++j) {
+      const uint2 p = *reinterpret_cast<const uint2*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j);
+      x[r][j][0] = p.x;
+      x[r][j][1] = p.y;
+    }
+  }
   // the kept coarse regions [k_L] (from the cover launch), this thread's first one
   const int32_t* sel_g = rl.sel_top + (int64_t)head * rl.k_top;
   const int sel0 = sel_g[min(t, rl.k_top - 1)];
-  // each level's score range: the cover waves' slots (at most 128 per head
-  // here, lanes l and l + 64 of wave 0), reduced by wave 0, which publishes
-  // the level's bins to LDS.  Loads are
-  // unconditional, from clamped slots; slots past the last wave take the
-  // neutral range by an all-ones mask.
-  const int nwav = (covered + 63) >> 6;
-  const uint32_t* lm = rl.lvl + (int64_t)head * nwav * 2 * kMaxLevels;
+  __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the score loads
+  // every level's scores into registers (clamped positions; slots past a
+  // level's end are never valid; a level past the pyramid's top loads level
+  // 0's slots and is never read)
+  HeldScores<S0> hs;
+#define WF_LOAD_LEVEL(J) \
+  hs.template load<J>(J < L ? cov + coff[J] : cov, J < L ? covered >> J : covered, (t * S0) >> J);
+  WF_LOAD_LEVEL(6)
+  WF_LOAD_LEVEL(5)
+  WF_LOAD_LEVEL(4)
+  WF_LOAD_LEVEL(3)
+  WF_LOAD_LEVEL(2)
+  WF_LOAD_LEVEL(1)
+  WF_LOAD_LEVEL(0)
+#undef WF_LOAD_LEVEL
   if (t < 64) {
-    uint32_t x[2][kMaxLevels][2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int v = min(lane + 64 * r, nwav - 1);
-#pragma unroll
-      for (int j = 0; j < kMaxLevels; ++j) {
-        const uint2 p = *reinterpret_cast<const uint2*>(lm + (int64_t)v * 2 * kMaxLevels + 2 * j);
-        x[r][j][0] = p.x;
-        x[r][j][1] = p.y;
-      }
-    }
     // all levels' least keys (complemented) and greatest keys in one
     // scattered reduction: value l (l < 8: level l's least, l >= 8: level
     // l - 8's greatest) ends in lane l16 = l of every row, then the rows combine
